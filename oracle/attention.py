@@ -1,0 +1,185 @@
+"""Softmax attention with a mask predicate and score modifications, in fp64.
+Oracle; test infrastructure only.
+
+What is computed, per batch element b, head h and query position q
+(notation: s = score, V_q = set of visible keys of q):
+
+  s_j    = scale * <q, k_j>                      scale = 1/sqrt(D) by default
+  ALiBi:   s_j <- s_j - slope[h] * (q - j)        (tutorial "FlexAttention in
+                                                   PyTorch", Pattern 3)
+  cap:     s_j <- c * tanh(s_j / c)              (same section, c = 30 there)
+  out_q  = sum_{j in V_q} softmax(s)_j v_j        over visible keys only
+  lse_q  = log sum_{j in V_q} exp(s_j)            natural log
+
+The pages fix the mask and score hooks (tutorial, section "The two hooks":
+a score_mod edits the logit after the query-key dot product; a mask_mod
+removes pairs) and the exact, fused softmax attention they feed (speedrun
+notes "FlexAttention", Context paragraph).  Readings taken where they are
+silent: the scale is applied before any score modification; ALiBi comes
+before the soft-cap when both are on; ALiBi uses absolute positions; a query
+with no visible key gives out = 0 and lse = -inf.
+
+Backward, with upstream gradient dO (the pages state that the score
+modifications are differentiable and get a fused backward pass -- tutorial,
+Pattern 3):
+  Delta_q = <dO_q, out_q>
+  p_qj    = exp(s_qj - lse_q) on visible pairs, 0 elsewhere
+  dP_qj   = <dO_q, v_j>
+  g_qj    = p_qj (dP_qj - Delta_q) * (1 - tanh^2(u_qj / c) if capped,
+            u = score before the cap; ALiBi is additive and contributes 1)
+  dQ_q = scale sum_j g_qj k_j,  dK_j = scale sum_q g_qj q_q,
+  dV_j = sum_q p_qj dO_q
+
+Arithmetic columns: by default only keys visible to at least one query of the
+row block take part in the arithmetic; the others would enter the softmax as
+exp(-inf) = 0 exactly (the tutorial notes that a -inf score is numerically the
+same as masking).  restrict=False keeps every column (fully dense), and the
+tests check that both give the same values.
+
+All inputs are per (b, h) float64 arrays [T, D] holding the bf16-rounded
+values the GPU reads.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .predicate import visible
+
+ROW_CHUNK = 128
+
+
+def _scale(D, scale):
+    return 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+
+
+def _scores(Qr, Kc, rows, cols, h, scale, mod):
+    """Returns (u, s): score before the cap and final score, [R, C]."""
+    s = scale * (Qr @ Kc.T)
+    if mod is not None and mod.alibi_slopes is not None:
+        slope = float(mod.alibi_slopes[h])
+        s = s - slope * (rows[:, None] - cols[None, :]).astype(np.float64)
+    u = s
+    if mod is not None and mod.softcap is not None:
+        c = float(mod.softcap)
+        s = c * np.tanh(u / c)
+    return u, s
+
+
+def _row_block(Q, K, V, spec, mod, b, h, rows, scale, restrict):
+    T = K.shape[0]
+    allcols = np.arange(T)
+    m = visible(spec, b, rows[:, None], allcols[None, :])
+    cols = np.nonzero(m.any(axis=0))[0] if restrict else allcols
+    m = m[:, cols]
+    u, s = _scores(Q[rows], K[cols], rows, cols, h, scale, mod)
+    s = np.where(m, s, -np.inf)
+    return cols, m, u, s
+
+
+def forward_rows(Q, K, V, spec, mod, b, h, rows, scale=None, restrict=True):
+    """out [R, D] and lse [R] for the query positions `rows`."""
+    rows = np.asarray(rows, dtype=np.int64)
+    D = Q.shape[1]
+    sc = _scale(D, scale)
+    out = np.zeros((len(rows), V.shape[1]), dtype=np.float64)
+    lse = np.full(len(rows), -np.inf, dtype=np.float64)
+    for a in range(0, len(rows), ROW_CHUNK):
+        r = rows[a:a + ROW_CHUNK]
+        cols, m, _, s = _row_block(Q, K, V, spec, mod, b, h, r, sc, restrict)
+        if len(cols) == 0:
+            continue
+        mx = s.max(axis=1)
+        live = np.isfinite(mx)
+        mx_safe = np.where(live, mx, 0.0)
+        with np.errstate(invalid="ignore"):
+            p = np.exp(s - mx_safe[:, None])
+        p = np.where(m, p, 0.0)
+        ell = p.sum(axis=1)
+        o = p @ V[cols]
+        with np.errstate(invalid="ignore", divide="ignore"):
+            out[a:a + len(r)] = np.where(live[:, None], o / np.where(live, ell, 1.0)[:, None], 0.0)
+            lse[a:a + len(r)] = np.where(live, mx_safe + np.log(np.where(live, ell, 1.0)), -np.inf)
+    return out, lse
+
+
+def forward_dense(Q, K, V, spec, mod, b, h, scale=None, restrict=True):
+    """out [T, D], lse [T] for every query position."""
+    return forward_rows(Q, K, V, spec, mod, b, h, np.arange(Q.shape[0]), scale, restrict)
+
+
+def _grad_block(Q, K, V, dO, spec, mod, b, h, rows, cols_sel, out_r, lse_r, sc):
+    """g [R, C], p [R, C] on rows x cols_sel (visible pairs only)."""
+    m = visible(spec, b, rows[:, None], cols_sel[None, :])
+    u, s = _scores(Q[rows], K[cols_sel], rows, cols_sel, h, sc, mod)
+    live = np.isfinite(lse_r)
+    with np.errstate(invalid="ignore", over="ignore"):
+        p = np.exp(s - np.where(live, lse_r, 0.0)[:, None])
+    p = np.where(m & live[:, None], p, 0.0)
+    delta = np.sum(dO[rows] * out_r, axis=1)
+    dP = dO[rows] @ V[cols_sel].T
+    g = p * (dP - delta[:, None])
+    if mod is not None and mod.softcap is not None:
+        c = float(mod.softcap)
+        g = g * (1.0 - np.tanh(u / c) ** 2)
+    return g, p
+
+
+def backward_dense(Q, K, V, dO, spec, mod, b, h, scale=None):
+    """dQ, dK, dV [T, D] (small T)."""
+    T, D = Q.shape
+    sc = _scale(D, scale)
+    out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    allcols = np.arange(T)
+    for a in range(0, T, ROW_CHUNK):
+        r = np.arange(a, min(T, a + ROW_CHUNK))
+        g, p = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc)
+        dQ[r] = sc * (g @ K)
+        dK += sc * (g.T @ Q[r])
+        dV += p.T @ dO[r]
+    return dQ, dK, dV
+
+
+def backward_dq_rows(Q, K, V, dO, spec, mod, b, h, rows, scale=None):
+    """dQ for the query positions `rows` [R, D]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    T, D = Q.shape
+    sc = _scale(D, scale)
+    out, lse = forward_rows(Q, K, V, spec, mod, b, h, rows, scale)
+    dQ = np.zeros((len(rows), D), dtype=np.float64)
+    for a in range(0, len(rows), ROW_CHUNK):
+        r = rows[a:a + ROW_CHUNK]
+        m = visible(spec, b, r[:, None], np.arange(T)[None, :])
+        cols = np.nonzero(m.any(axis=0))[0]
+        if len(cols) == 0:
+            continue
+        g, _ = _grad_block(Q, K, V, dO, spec, mod, b, h, r, cols,
+                           out[a:a + len(r)], lse[a:a + len(r)], sc)
+        dQ[a:a + len(r)] = sc * (g @ K[cols])
+    return dQ
+
+
+def backward_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None):
+    """dK, dV for the key positions `cols` [C, D]: sums over every query that
+    sees at least one of them, with that query's own forward recomputed."""
+    cols = np.asarray(cols, dtype=np.int64)
+    T, D = Q.shape
+    sc = _scale(D, scale)
+    seen = visible(spec, b, np.arange(T)[:, None], cols[None, :]).any(axis=1)
+    rows = np.nonzero(seen)[0]
+    dK = np.zeros((len(cols), D), dtype=np.float64)
+    dV = np.zeros((len(cols), V.shape[1]), dtype=np.float64)
+    if len(rows) == 0:
+        return dK, dV
+    out, lse = forward_rows(Q, K, V, spec, mod, b, h, rows, scale)
+    for a in range(0, len(rows), ROW_CHUNK):
+        r = rows[a:a + ROW_CHUNK]
+        g, p = _grad_block(Q, K, V, dO, spec, mod, b, h, r, cols,
+                           out[a:a + len(r)], lse[a:a + len(r)], sc)
+        dK += sc * (g.T @ Q[r])
+        dV += p.T @ dO[r]
+    return dK, dV

@@ -1,0 +1,252 @@
+"""Pins for the oracle's fp64 attention forward and backward (CPU only).
+
+Pins used: torch's scaled_dot_product_attention in fp64 (library routine) for
+the unmasked, causal and per-document cases; special cases with closed forms
+(window of 1, a two-key row through the soft-cap); invariants from the pages
+(masking equals a -inf score, tutorial "The two hooks"); the softmax's row
+shift invariance for ALiBi; central finite differences and torch.autograd for
+the backward; sum rules of the gradients.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from workloads import MaskSpecData, ScoreModData, doc_ids_geometric, alibi_slopes
+
+
+def _rand(shape, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+
+
+def _sdpa(Q, K, V, **kw):
+    t = lambda x: torch.from_numpy(x)[None, None]
+    return F.scaled_dot_product_attention(t(Q), t(K), t(V), **kw)[0, 0].numpy()
+
+
+T, D = 384, 32
+
+
+def test_forward_no_mask_matches_sdpa():
+    Q, K, V = (_rand((T, D), s) for s in (1, 2, 3))
+    spec = MaskSpecData(T, causal=False)
+    out, lse = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V), rtol=0, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_forward_causal_matches_sdpa():
+    Q, K, V = (_rand((T, D), s) for s in (4, 5, 6))
+    out, _ = oracle.forward_dense(Q, K, V, MaskSpecData(T, causal=True), None, 0, 0)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, is_causal=True), rtol=0, atol=1e-12)
+
+
+def test_forward_document_equals_independent_documents():
+    """Packed documents (tutorial Pattern 1) = causal attention run on each
+    document alone, concatenated."""
+    Q, K, V = (_rand((T, D), s) for s in (7, 8, 9))
+    docs = doc_ids_geometric(T, 60, np.random.default_rng(3))
+    spec = MaskSpecData(T, causal=True, document=True, doc_ids=docs[None])
+    out, _ = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
+    ref = np.zeros_like(out)
+    for d in np.unique(docs):
+        idx = np.nonzero(docs == d)[0]
+        ref[idx] = _sdpa(Q[idx], K[idx], V[idx], is_causal=True)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_forward_window_one_and_wide():
+    Q, K, V = (_rand((T, D), s) for s in (10, 11, 12))
+    out1, lse1 = oracle.forward_dense(Q, K, V, MaskSpecData(T, causal=True, window=1), None, 0, 0)
+    np.testing.assert_allclose(out1, V, rtol=0, atol=1e-14)
+    s_self = np.einsum("td,td->t", Q, K) / math.sqrt(D)
+    np.testing.assert_allclose(lse1, s_self, rtol=0, atol=1e-12)
+    outw, lsew = oracle.forward_dense(Q, K, V, MaskSpecData(T, causal=True, window=T + 5), None, 0, 0)
+    np.testing.assert_allclose(outw, _sdpa(Q, K, V, is_causal=True), rtol=0, atol=1e-12)
+
+
+def test_forward_sinks_match_explicit_mask():
+    """Tutorial Pattern 2 expressed as an explicit boolean mask in SDPA."""
+    Q, K, V = (_rand((T, D), s) for s in (13, 14, 15))
+    spec = MaskSpecData(T, causal=True, window=50, sinks=4)
+    out, _ = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
+    qi = torch.arange(T)[:, None]
+    ki = torch.arange(T)[None, :]
+    m = (qi >= ki) & (((qi - ki) < 50) | (ki < 4))
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, attn_mask=m), rtol=0, atol=1e-12)
+
+
+def test_alibi_is_a_column_bias():
+    """-slope*(q - kv) = -slope*q + slope*kv: the first term is constant along
+    a row, so the output equals SDPA with a per-column bias +slope*kv, and the
+    lse shifts by -slope*q."""
+    Q, K, V = (_rand((T, D), s) for s in (16, 17, 18))
+    H = 8
+    slopes = alibi_slopes(H)
+    h = 2
+    spec = MaskSpecData(T, causal=True)
+    out, lse = oracle.forward_dense(Q, K, V, spec, ScoreModData(alibi_slopes=slopes), 0, h)
+    sl = float(slopes[h])
+    bias = torch.full((T, T), -math.inf, dtype=torch.float64)
+    qi = torch.arange(T)[:, None]
+    ki = torch.arange(T)[None, :]
+    colb = (sl * ki.double()).expand(T, T)
+    bias = torch.where(qi >= ki, colb, bias)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, attn_mask=bias), rtol=0, atol=1e-12)
+    logits = torch.from_numpy(Q @ K.T / math.sqrt(D)) + bias
+    lse_ref = torch.logsumexp(logits, dim=1).numpy() - sl * np.arange(T)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-10)
+    out0, _ = oracle.forward_dense(Q, K, V, spec, ScoreModData(alibi_slopes=np.zeros(H, np.float32)), 0, h)
+    np.testing.assert_allclose(out0, _sdpa(Q, K, V, is_causal=True), rtol=0, atol=1e-12)
+
+
+def test_softcap_two_key_closed_form():
+    """A row with two visible keys whose raw scores are 0 and c*atanh(1/2):
+    the capped scores are 0 and c/2 (tanh(atanh x) = x), so the softmax
+    weights are 1/(1+e^{c/2}) and e^{c/2}/(1+e^{c/2})."""
+    c = 30.0
+    Dd = 4
+    Tt = 128
+    Q = np.zeros((Tt, Dd))
+    K = np.zeros((Tt, Dd))
+    V = np.arange(Tt * Dd, dtype=np.float64).reshape(Tt, Dd) / 7.0
+    target = c * math.atanh(0.5)
+    # row 1 sees keys 0 and 1 (window 2); score(1, 0) = 0, score(1, 1) = target
+    Q[1, 0] = 1.0
+    K[1, 0] = target * math.sqrt(Dd)
+    spec = MaskSpecData(Tt, causal=True, window=2)
+    out, lse = oracle.forward_rows(Q, K, V, spec, ScoreModData(softcap=c), 0, 0, np.array([1]))
+    w1 = math.exp(c / 2) / (1 + math.exp(c / 2))
+    np.testing.assert_allclose(out[0], (1 - w1) * V[0] + w1 * V[1], rtol=1e-12)
+    np.testing.assert_allclose(lse[0], math.log(1 + math.exp(c / 2)), rtol=1e-12)
+
+
+def test_softcap_bounds_and_limit():
+    Q, K, V = (_rand((T, D), s) for s in (19, 20, 21))
+    Q = Q * 40.0  # large logits so the cap bites
+    spec = MaskSpecData(T, causal=True)
+    out_big, _ = oracle.forward_dense(Q, K, V, spec, ScoreModData(softcap=1e9), 0, 0)
+    np.testing.assert_allclose(out_big, _sdpa(Q, K, V, is_causal=True), rtol=0, atol=1e-9)
+    _, lse_c = oracle.forward_dense(Q, K, V, spec, ScoreModData(softcap=30.0), 0, 0)
+    # every capped score lies in (-30, 30), so lse < 30 + log(#keys)
+    assert np.all(lse_c < 30.0 + np.log(np.arange(1, T + 1)) + 1e-12)
+
+
+def test_restricted_columns_equal_dense_minus_inf():
+    """Skipping keys no query of the block sees = scoring them -inf (tutorial,
+    "The two hooks": a -inf score gives the same numerics as a mask)."""
+    Q, K, V = (_rand((T, D), s) for s in (22, 23, 24))
+    docs = doc_ids_geometric(T, 50, np.random.default_rng(5))
+    spec = MaskSpecData(T, causal=True, document=True, doc_ids=docs[None], window=70)
+    mod = ScoreModData(alibi_slopes=alibi_slopes(4), softcap=30.0)
+    o1, l1 = oracle.forward_dense(Q, K, V, spec, mod, 0, 1, restrict=True)
+    o2, l2 = oracle.forward_dense(Q, K, V, spec, mod, 0, 1, restrict=False)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+def test_empty_rows():
+    Q, K, V = (_rand((128, 8), s) for s in (25, 26, 27))
+    spec = MaskSpecData(128, causal=True, window=0)  # q - kv < 0 with q >= kv: nothing
+    out, lse = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+    dq, dk, dv = oracle.backward_dense(Q, K, V, _rand((128, 8), 28), spec, None, 0, 0)
+    assert not dq.any() and not dk.any() and not dv.any()
+
+
+# ---------------------------------------------------------------- backward
+
+def _specs_for_bwd(Tt):
+    docs = doc_ids_geometric(Tt, 40, np.random.default_rng(9))
+    return [
+        (MaskSpecData(Tt, causal=True), None),
+        (MaskSpecData(Tt, causal=True, document=True, doc_ids=docs[None]),
+         ScoreModData(alibi_slopes=alibi_slopes(2), softcap=30.0)),
+        (MaskSpecData(Tt, causal=True, window=37, sinks=3), ScoreModData(softcap=5.0)),
+        (MaskSpecData(Tt, causal=False, document=True, doc_ids=docs[None]),
+         ScoreModData(alibi_slopes=alibi_slopes(2))),
+    ]
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_backward_finite_differences(case):
+    Tt, Dd = 256, 16
+    spec, mod = _specs_for_bwd(Tt)[case]
+    Q, K, V, dO = (_rand((Tt, Dd), 30 + s) * 1.5 for s in range(4))
+    h = 1
+    dQ, dK, dV = oracle.backward_dense(Q, K, V, dO, spec, mod, 0, h)
+
+    def loss(Qx, Kx, Vx):
+        o, _ = oracle.forward_dense(Qx, Kx, Vx, spec, mod, 0, h)
+        return float(np.sum(o * dO))
+
+    rng = np.random.default_rng(case)
+    eps = 1e-6
+    for which, G in (("q", dQ), ("k", dK), ("v", dV)):
+        for _ in range(4):
+            t, d = int(rng.integers(0, Tt)), int(rng.integers(0, Dd))
+            X = {"q": Q, "k": K, "v": V}
+            Xp = {n: a.copy() for n, a in X.items()}
+            Xm = {n: a.copy() for n, a in X.items()}
+            Xp[which][t, d] += eps
+            Xm[which][t, d] -= eps
+            fd = (loss(Xp["q"], Xp["k"], Xp["v"]) - loss(Xm["q"], Xm["k"], Xm["v"])) / (2 * eps)
+            assert abs(fd - G[t, d]) <= 1e-6 * max(1.0, abs(fd)), (which, t, d, fd, G[t, d])
+
+
+@pytest.mark.parametrize("case", range(4))
+def test_backward_matches_autograd(case):
+    """Autograd through a dense explicit-mask fp64 reference (tutorial, sharp
+    edge 5: check against a dense reference with an explicit mask)."""
+    Tt, Dd = 256, 16
+    spec, mod = _specs_for_bwd(Tt)[case]
+    Q, K, V, dO = (_rand((Tt, Dd), 40 + s) for s in range(4))
+    h = 1
+    dQ, dK, dV = oracle.backward_dense(Q, K, V, dO, spec, mod, 0, h)
+    m = torch.from_numpy(oracle.visible(spec, 0, np.arange(Tt)[:, None], np.arange(Tt)[None, :]))
+    q, k, v = (torch.from_numpy(x).clone().requires_grad_(True) for x in (Q, K, V))
+    s = (q @ k.T) / math.sqrt(Dd)
+    if mod is not None and mod.alibi_slopes is not None:
+        pos = torch.arange(Tt, dtype=torch.float64)
+        s = s - float(mod.alibi_slopes[h]) * (pos[:, None] - pos[None, :])
+    if mod is not None and mod.softcap is not None:
+        s = mod.softcap * torch.tanh(s / mod.softcap)
+    s = s.masked_fill(~m, -math.inf)
+    p = torch.softmax(s, dim=1)
+    p = torch.nan_to_num(p, nan=0.0)
+    o = p @ v
+    o.backward(torch.from_numpy(dO))
+    for a, b_ in ((dQ, q.grad), (dK, k.grad), (dV, v.grad)):
+        np.testing.assert_allclose(a, b_.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_sum_rules():
+    """sum_j dV_j = sum of dO over queries that see something; without a cap,
+    every row of g sums to zero so sum_j dK_j = 0."""
+    Tt, Dd = 256, 16
+    spec, _ = _specs_for_bwd(Tt)[1]
+    mod = ScoreModData(alibi_slopes=alibi_slopes(2))
+    Q, K, V, dO = (_rand((Tt, Dd), 50 + s) for s in range(4))
+    _, dK, dV = oracle.backward_dense(Q, K, V, dO, spec, mod, 0, 0)
+    np.testing.assert_allclose(dV.sum(0), dO.sum(0), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dK.sum(0), np.zeros(Dd), rtol=0, atol=1e-11)
+
+
+def test_sampled_backward_paths_match_dense():
+    Tt, Dd = 512, 16
+    docs = doc_ids_geometric(Tt, 90, np.random.default_rng(2))
+    spec = MaskSpecData(Tt, causal=True, document=True, doc_ids=docs[None], window=200)
+    mod = ScoreModData(alibi_slopes=alibi_slopes(4), softcap=30.0)
+    Q, K, V, dO = (_rand((Tt, Dd), 60 + s) for s in range(4))
+    dQ, dK, dV = oracle.backward_dense(Q, K, V, dO, spec, mod, 0, 3)
+    rows = np.array([0, 5, 127, 128, 300, 511])
+    np.testing.assert_allclose(oracle.backward_dq_rows(Q, K, V, dO, spec, mod, 0, 3, rows), dQ[rows],
+                               rtol=0, atol=1e-12)
+    cols = np.array([0, 1, 130, 255, 256, 400, 511])
+    dk, dv = oracle.backward_dkdv_cols(Q, K, V, dO, spec, mod, 0, 3, cols)
+    np.testing.assert_allclose(dk, dK[cols], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dV[cols], rtol=0, atol=1e-12)

@@ -1,0 +1,194 @@
+"""Pins for the oracle's tile counter and tile lists (CPU only).
+
+Each test checks the oracle against something other than itself: numbers the
+pages print, closed forms derived from the predicate, brute force over pairs
+in pure Python, or an independent dense-mask reduction.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from workloads import MaskSpecData, doc_ids_chunks, make_config
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _spec_by_name(name, T):
+    if name == "causal":
+        return MaskSpecData(T, causal=True)
+    if name == "causal_window_1024":
+        return MaskSpecData(T, causal=True, window=1024)
+    if name == "causal_chunks_1024":
+        return MaskSpecData(T, causal=True, document=True, doc_ids=doc_ids_chunks(T, 1024)[None])
+    raise KeyError(name)
+
+
+def _visible_tiles(spec):
+    return int((oracle.classify(oracle.tile_counts(spec)) > 0).sum())
+
+
+def test_printed_tile_counts_64k():
+    """Speedrun notes, tile-summary paragraph: 131,328 / 4,572 / 2,304."""
+    for name, T, expected in _read_golden("tile_counts_64k.txt"):
+        assert _visible_tiles(_spec_by_name(name, int(T))) == int(expected), name
+
+
+def test_printed_work_ratios_64k():
+    """Speedrun notes, Record #12: ~2x the chunked work; dense causal 57x."""
+    for num, den, ratio, tol in _read_golden("work_ratios_64k.txt"):
+        r = _visible_tiles(_spec_by_name(num, 65536)) / _visible_tiles(_spec_by_name(den, 65536))
+        assert abs(r - float(ratio)) <= float(tol) * float(ratio), (num, den, r)
+
+
+def _window_closed_form(T, w):
+    """causal AND q-kv<w, no documents, n = T/128 tiles per side.
+
+    Tile (i, j) on diagonal d = i - j >= 0 holds differences q - kv from
+    128 d - 127 to 128 d + 127.  It has a visible pair iff its smallest
+    difference is < w, i.e. d <= floor((w + 126) / 128); it is full iff its
+    largest difference is < w and it lies strictly below the diagonal
+    (the diagonal tile has q < kv pairs), i.e. 1 <= d <= floor(w/128) - 1.
+    Diagonal d holds n - d tiles.
+    """
+    n = T // 128
+    dv = min((w + 126) // 128, n - 1)
+    visible = sum(n - d for d in range(0, dv + 1))
+    df = min(w // 128 - 1, n - 1)
+    full = sum(n - d for d in range(1, df + 1)) if df >= 1 else 0
+    return visible, full
+
+
+@pytest.mark.parametrize("w", list(range(64, 1792 + 1, 64)))
+def test_window_sweep_closed_form(w):
+    """The 28-step window schedule (speedrun notes, Record #13) on one
+    65,536-token sequence without documents, against the closed form."""
+    T = 65536
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True, window=w)))
+    vis, full = _window_closed_form(T, w)
+    assert int((cls > 0).sum()) == vis
+    assert int((cls == oracle.FULL).sum()) == full
+
+
+def test_dense_causal_8k_closed_form():
+    """Tutorial quick start shape (S = 8192): 64 tile rows, causal -> the
+    lower triangle with its diagonal: 64*65/2 tiles, 64 of them partial."""
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(8192, causal=True)))
+    assert int((cls > 0).sum()) == 64 * 65 // 2
+    assert int((cls == oracle.PARTIAL).sum()) == 64
+
+
+def test_sinks_32k_closed_form():
+    """Tutorial Pattern 2 (1024 window, 4 sinks) at 32,768 positions.
+
+    Band tiles: diagonals 0..8 (256 - d tiles each); full: diagonals 1..7.
+    Sinks (kv < 4) add tile column 0 for every row beyond the band
+    (i = 9..255), each partial.  ~96.2 % of the full grid is skipped
+    (the tutorial rounds it to ~97 %)."""
+    T = 32768
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True, window=1024, sinks=4)))
+    band = sum(256 - d for d in range(9))
+    full = sum(256 - d for d in range(1, 8))
+    sink_extra = 256 - 9
+    assert int((cls > 0).sum()) == band + sink_extra == 2515
+    assert int((cls == oracle.FULL).sum()) == full == 1764
+    sparsity = 1.0 - (band + sink_extra) / 256 ** 2
+    assert 0.955 < sparsity < 0.975
+
+
+def _pairs_python(spec):
+    """Pure-Python loops over every pair and every tile (tiny T)."""
+    T = spec.T
+    nt = T // 128
+    res = np.zeros((spec.mask_b, nt, nt), dtype=np.int64)
+    for b in range(spec.mask_b):
+        docs = None if spec.doc_ids is None else [int(x) for x in spec.doc_ids[b]]
+        for q in range(T):
+            for kv in range(T):
+                ok = True
+                if spec.causal and not (q >= kv):
+                    ok = False
+                if ok and spec.document and docs[q] != docs[kv]:
+                    ok = False
+                if ok and spec.window is not None:
+                    if not ((q - kv) < spec.window or (spec.sinks and kv < spec.sinks)):
+                        ok = False
+                if ok:
+                    res[b, q // 128, kv // 128] += 1
+    return res
+
+
+def _random_spec(rng, T, allow_nonmono=True):
+    causal = bool(rng.integers(0, 2))
+    document = bool(rng.integers(0, 2))
+    mb = int(rng.integers(1, 3))
+    docs = None
+    if document:
+        if allow_nonmono and rng.integers(0, 3) == 0:
+            docs = rng.integers(0, 3, size=(mb, T)).astype(np.int32)
+        else:
+            docs = np.stack([np.cumsum(rng.random(T) < 1.0 / rng.integers(8, 300)).astype(np.int32)
+                             for _ in range(mb)])
+    window = None
+    sinks = 0
+    if rng.integers(0, 3) > 0:
+        window = int(rng.choice([-3, 0, 1, 2, 64, 127, 128, 129, 200, 255, 256, 257, 700, 5000]))
+        if rng.integers(0, 2):
+            sinks = int(rng.choice([1, 4, 127, 128, 129, 300]))
+    return MaskSpecData(T, causal=causal, document=document, doc_ids=docs,
+                        window=window, sinks=sinks)
+
+
+def test_brute_force_python_tiny():
+    """C counter == pure-Python per-pair loops on tiny random specs."""
+    rng = np.random.default_rng(11)
+    for _ in range(6):
+        spec = _random_spec(rng, 256)
+        assert np.array_equal(oracle.tile_counts(spec), _pairs_python(spec)), spec
+
+
+def test_brute_force_dense_numpy_random():
+    """C counter == dense [T, T] boolean mask reduced per tile, random specs
+    (monotone and non-monotone document ids, windows, sinks, T up to 2048)."""
+    rng = np.random.default_rng(12)
+    for T in (128, 256, 384, 1024, 2048):
+        for _ in range(8):
+            spec = _random_spec(rng, T)
+            assert np.array_equal(oracle.tile_counts(spec), oracle.tile_counts_dense_numpy(spec)), spec
+
+
+def test_lists_from_counts():
+    """Lists: ascending, -1 padded, partial/full split, transposed view."""
+    counts = np.array([[[0, 16384, 5], [16384, 0, 16384], [1, 2, 0]]], dtype=np.int32)
+    bm = oracle.block_mask_lists(counts)
+    assert bm["kv_num_blocks"].tolist() == [[[1, 0, 2]]]
+    assert bm["kv_indices"].tolist() == [[[[2, -1, -1], [-1, -1, -1], [0, 1, -1]]]]
+    assert bm["full_kv_num_blocks"].tolist() == [[[1, 2, 0]]]
+    assert bm["full_kv_indices"].tolist() == [[[[1, -1, -1], [0, 2, -1], [-1, -1, -1]]]]
+    assert bm["q_num_blocks"].tolist() == [[[1, 1, 1]]]
+    assert bm["q_indices"].tolist() == [[[[2, -1, -1], [2, -1, -1], [0, -1, -1]]]]
+    assert bm["full_q_num_blocks"].tolist() == [[[1, 1, 1]]]
+    assert bm["full_q_indices"].tolist() == [[[[1, -1, -1], [0, -1, -1], [1, -1, -1]]]]
+
+
+def test_config_masks_bounded_by_nodoc():
+    """Adding the document term can only remove pairs: per tile the count with
+    documents never exceeds the count without (configs 1, 2 shape at 8K)."""
+    for key, T in ((1, None), (2, 8192)):
+        w = make_config(key, T=T)
+        c_doc = oracle.tile_counts(w.spec)
+        nodoc = MaskSpecData(w.T, causal=True, window=w.spec.window)
+        c_nodoc = oracle.tile_counts(nodoc)
+        assert np.all(c_doc <= c_nodoc)
+        assert int((c_doc > 0).sum()) < int((c_nodoc > 0).sum())
