@@ -1,0 +1,222 @@
+"""Python binding of the block-sparse masked attention library.
+
+Argument marshalling only: every step runs in the HIP kernels of libbsm.so.
+PyTorch provides device memory and the current stream.
+
+    spec = mask_spec(T, causal=True, doc_ids=docs, window=1024)
+    bm   = build_block_mask(spec)                     # once per mask
+    out, lse = flex_attention_fwd(q, k, v, bm, spec, score_mod)
+    dq, dk, dv = flex_attention_bwd(q, k, v, out, lse, dout, bm, spec, score_mod)
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import NamedTuple, Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (BsmBlockMask, BsmMaskSpec, BsmScoreMod, BsmTensor, check, lib,
+                   BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS,
+                   BSM_MOD_ALIBI, BSM_MOD_SOFTCAP)
+
+TILE = 128
+
+
+@dataclasses.dataclass
+class MaskSpec:
+    """Device-side mask description.  `window` is a device int32 tensor of
+    one element so it can change between calls without touching the host."""
+    T: int
+    causal: bool = True
+    doc_ids: Optional[torch.Tensor] = None   # int32 [mask_b, T] on the device
+    window: Optional[torch.Tensor] = None    # int32 [1] on the device
+    sinks: int = 0
+
+    @property
+    def mask_b(self) -> int:
+        return 1 if self.doc_ids is None else int(self.doc_ids.shape[0])
+
+    @property
+    def flags(self) -> int:
+        f = BSM_MASK_CAUSAL if self.causal else 0
+        if self.doc_ids is not None:
+            f |= BSM_MASK_DOCUMENT
+        if self.window is not None:
+            f |= BSM_MASK_WINDOW
+            if self.sinks:
+                f |= BSM_MASK_SINKS
+        return f
+
+    def c_struct(self) -> BsmMaskSpec:
+        return BsmMaskSpec(self.flags, self.T, self.mask_b,
+                           self.doc_ids.data_ptr() if self.doc_ids is not None else None,
+                           self.window.data_ptr() if self.window is not None else None,
+                           int(self.sinks))
+
+    def set_window(self, w: int) -> None:
+        """Writes a new window value on the device (stream-ordered)."""
+        self.window.fill_(int(w))
+
+
+@dataclasses.dataclass
+class ScoreMod:
+    alibi_slopes: Optional[torch.Tensor] = None  # float32 [H] on the device
+    softcap: Optional[float] = None
+
+    def c_struct(self) -> BsmScoreMod:
+        f = 0
+        if self.alibi_slopes is not None:
+            f |= BSM_MOD_ALIBI
+        if self.softcap is not None:
+            f |= BSM_MOD_SOFTCAP
+        return BsmScoreMod(f, self.alibi_slopes.data_ptr() if self.alibi_slopes is not None else None,
+                           float(self.softcap) if self.softcap is not None else 0.0)
+
+
+class BlockMask(NamedTuple):
+    kv_num_blocks: torch.Tensor
+    kv_indices: torch.Tensor
+    full_kv_num_blocks: torch.Tensor
+    full_kv_indices: torch.Tensor
+    q_num_blocks: torch.Tensor
+    q_indices: torch.Tensor
+    full_q_num_blocks: torch.Tensor
+    full_q_indices: torch.Tensor
+
+    def c_struct(self) -> BsmBlockMask:
+        return BsmBlockMask(*[t.data_ptr() for t in self])
+
+    def visible_tiles(self) -> int:
+        """Non-empty tiles (partial + full) over the mask batch."""
+        return int(self.kv_num_blocks.sum().item() + self.full_kv_num_blocks.sum().item())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] = None,
+              sinks: int = 0, device="cuda") -> MaskSpec:
+    """Device mask spec from host values (numpy / torch / int)."""
+    d = None
+    if doc_ids is not None:
+        d = torch.as_tensor(np.asarray(doc_ids), dtype=torch.int32)
+        if d.dim() == 1:
+            d = d[None]
+        d = d.to(device).contiguous()
+    w = None
+    if window is not None:
+        w = torch.tensor([int(window)], dtype=torch.int32, device=device)
+    return MaskSpec(int(T), bool(causal), d, w, int(sinks))
+
+
+def from_spec_data(spec_data, device="cuda") -> MaskSpec:
+    """Device mask spec from a workloads.MaskSpecData."""
+    return mask_spec(spec_data.T, spec_data.causal,
+                     spec_data.doc_ids if spec_data.document else None,
+                     spec_data.window, spec_data.sinks, device)
+
+
+def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda") -> ScoreMod:
+    s = None
+    if alibi_slopes is not None:
+        s = torch.as_tensor(np.asarray(alibi_slopes), dtype=torch.float32).to(device).contiguous()
+    return ScoreMod(s, softcap)
+
+
+def empty_block_mask(T: int, mask_b: int, device="cuda") -> BlockMask:
+    nt = T // TILE
+    mk = lambda *s: torch.empty(s, dtype=torch.int32, device=device)
+    return BlockMask(mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
+                     mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt))
+
+
+def block_mask_workspace(spec: MaskSpec) -> torch.Tensor:
+    n = lib.bsm_block_mask_workspace_bytes(spec.T, spec.mask_b)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=spec.doc_ids.device
+                       if spec.doc_ids is not None else "cuda")
+
+
+def build_block_mask(spec: MaskSpec, out: Optional[BlockMask] = None,
+                     workspace: Optional[torch.Tensor] = None) -> BlockMask:
+    """Runs bsm_build_block_mask on the current stream."""
+    if out is None:
+        out = empty_block_mask(spec.T, spec.mask_b)
+    if workspace is None:
+        workspace = block_mask_workspace(spec)
+    cs = spec.c_struct()
+    cb = out.c_struct()
+    check(lib.bsm_build_block_mask(ctypes.byref(cs), ctypes.byref(cb), workspace.data_ptr(),
+                                   workspace.numel(), _stream()))
+    return out
+
+
+def _tensor(t: torch.Tensor, name: str) -> BsmTensor:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, T, D]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+    sb, sh, st, _ = t.stride()
+    return BsmTensor(t.data_ptr(), sb, sh, st)
+
+
+def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,
+                       mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
+                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Returns (out bf16 [B,H,T,D], lse float32 [B,H,T])."""
+    B, H, T, D = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must have the same shape [B, H, T, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if not lse.is_contiguous() or lse.shape != (B, H, T):
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
+    cb = block_mask.c_struct()
+    cs = spec.c_struct()
+    cm = mod.c_struct() if mod is not None else None
+    check(lib.bsm_flex_attention_fwd(
+        B, H, T, D, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(cb),
+        ctypes.byref(cs), ctypes.byref(cm) if cm is not None else None,
+        float(scale) if scale is not None else 0.0, ctypes.byref(to), lse.data_ptr(), _stream()))
+    return out, lse
+
+
+def bwd_workspace(B: int, H: int, T: int, D: int, device="cuda") -> torch.Tensor:
+    n = lib.bsm_bwd_workspace_bytes(B, H, T, D)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: MaskSpec,
+                       mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
+                       dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None):
+    """Returns (dq, dk, dv), bf16 [B,H,T,D]."""
+    B, H, T, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = bwd_workspace(B, H, T, D, q.device)
+    ts = [_tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"),
+                                     (dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    cb = block_mask.c_struct()
+    cs = spec.c_struct()
+    cm = mod.c_struct() if mod is not None else None
+    check(lib.bsm_flex_attention_bwd(
+        B, H, T, D, *[ctypes.byref(t) for t in ts[:4]], lse.data_ptr(), ctypes.byref(ts[4]),
+        ctypes.byref(cb), ctypes.byref(cs), ctypes.byref(cm) if cm is not None else None,
+        float(scale) if scale is not None else 0.0, *[ctypes.byref(t) for t in ts[5:]],
+        workspace.data_ptr(), workspace.numel(), _stream()))
+    return dq, dk, dv
+
+
+__all__ = ["MaskSpec", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
+           "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
+           "bwd_workspace", "block_mask_workspace", "_lib"]

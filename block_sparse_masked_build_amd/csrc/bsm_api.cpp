@@ -1,0 +1,261 @@
+// C ABI of the block-sparse masked attention library: host-side argument
+// checks, workspace layout and kernel launches.  No call allocates memory or
+// synchronises; every check runs before anything is enqueued.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "bsm_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bsm_status fail(bsm_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bsm_status ok() {
+    g_last_error.clear();
+    return BSM_OK;
+}
+
+constexpr int32_t kMaxT = 1 << 22;
+constexpr uint32_t kMaskFlagsAll = BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS;
+constexpr uint32_t kModFlagsAll = BSM_MOD_ALIBI | BSM_MOD_SOFTCAP;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool bad_T(int64_t T) { return T <= 0 || T % bsm::kTile != 0 || T > kMaxT; }
+
+int32_t n_chunks(int32_t T) { return (T + 255) / 256; }
+
+bsm_status check_spec(const bsm_mask_spec *spec) {
+    if (!spec) return fail(BSM_E_INVALID, "mask spec is NULL");
+    if (spec->flags & ~kMaskFlagsAll) return fail(BSM_E_INVALID, "unknown mask flag bits 0x%x", spec->flags);
+    if (bad_T(spec->seq_len))
+        return fail(BSM_E_INVALID, "seq_len %d must be a positive multiple of 128 and <= %d",
+                    spec->seq_len, kMaxT);
+    if (spec->mask_b < 1) return fail(BSM_E_INVALID, "mask_b %d must be >= 1", spec->mask_b);
+    if ((spec->flags & BSM_MASK_DOCUMENT) && !spec->doc_ids)
+        return fail(BSM_E_INVALID, "DOCUMENT mask without doc_ids");
+    if ((spec->flags & BSM_MASK_WINDOW) && !spec->window)
+        return fail(BSM_E_INVALID, "WINDOW mask without a window pointer");
+    if ((spec->flags & BSM_MASK_SINKS) && spec->num_sinks < 0)
+        return fail(BSM_E_INVALID, "num_sinks %d must be >= 0", spec->num_sinks);
+    return BSM_OK;
+}
+
+bsm_status check_block_mask(const bsm_block_mask *bm, bool need_transposed) {
+    if (!bm) return fail(BSM_E_INVALID, "block mask is NULL");
+    if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
+        return fail(BSM_E_INVALID, "block mask row arrays must be non-NULL");
+    if (need_transposed &&
+        (!bm->q_num_blocks || !bm->q_indices || !bm->full_q_num_blocks || !bm->full_q_indices))
+        return fail(BSM_E_INVALID, "block mask column arrays must be non-NULL");
+    return BSM_OK;
+}
+
+bsm_status check_tensor(const bsm_tensor *t, const char *name) {
+    if (!t || !t->ptr) return fail(BSM_E_INVALID, "tensor %s is NULL", name);
+    if (reinterpret_cast<uintptr_t>(t->ptr) % 16 != 0)
+        return fail(BSM_E_INVALID, "tensor %s must be 16-byte aligned", name);
+    if (t->stride_b % 8 || t->stride_h % 8 || t->stride_t % 8)
+        return fail(BSM_E_INVALID, "tensor %s strides must be multiples of 8 elements", name);
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_t < 0)
+        return fail(BSM_E_INVALID, "tensor %s strides must be non-negative", name);
+    return BSM_OK;
+}
+
+bsm_status check_mod(const bsm_score_mod *mod) {
+    if (!mod) return BSM_OK;
+    if (mod->flags & ~kModFlagsAll) return fail(BSM_E_INVALID, "unknown score-mod flag bits 0x%x", mod->flags);
+    if ((mod->flags & BSM_MOD_ALIBI) && !mod->alibi_slopes)
+        return fail(BSM_E_INVALID, "ALIBI without slopes");
+    if ((mod->flags & BSM_MOD_SOFTCAP) && !(mod->softcap > 0.0f && std::isfinite(mod->softcap)))
+        return fail(BSM_E_INVALID, "SOFTCAP needs a finite cap > 0");
+    return BSM_OK;
+}
+
+bsm_status check_attn_common(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_mask_spec *spec,
+                             const bsm_score_mod *mod) {
+    if (B < 1 || H < 1) return fail(BSM_E_INVALID, "B=%d and H=%d must be >= 1", B, H);
+    if (bad_T(T)) return fail(BSM_E_INVALID, "T %d must be a positive multiple of 128 and <= %d", T, kMaxT);
+    if (D != 64 && D != 128) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64 and 128 are built", D);
+    bsm_status st = check_spec(spec);
+    if (st != BSM_OK) return st;
+    if (spec->seq_len != T) return fail(BSM_E_INVALID, "mask seq_len %d != T %d", spec->seq_len, T);
+    if (spec->mask_b != 1 && spec->mask_b != B)
+        return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
+    if ((int64_t)B * H * (T / bsm::kTile) > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
+    return check_mod(mod);
+}
+
+void fill_tensor(const bsm_tensor *t, const void *&ptr, int64_t &sb, int64_t &sh, int64_t &st) {
+    ptr = t->ptr;
+    sb = t->stride_b;
+    sh = t->stride_h;
+    st = t->stride_t;
+}
+
+void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
+                 const bsm_block_mask *bm, const bsm_mask_spec *spec, const bsm_score_mod *mod,
+                 float scale) {
+    p = bsm::AttnParams{};
+    p.B = B;
+    p.H = H;
+    p.T = T;
+    p.nt = T / bsm::kTile;
+    p.mask_b = spec->mask_b;
+    p.mask_flags = spec->flags;
+    p.sinks = spec->num_sinks;
+    p.doc_ids = spec->doc_ids;
+    p.window = spec->window;
+    p.mod_flags = mod ? mod->flags : 0u;
+    p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
+    p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
+    p.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+    p.kv_num = bm->kv_num_blocks;
+    p.kv_idx = bm->kv_indices;
+    p.full_kv_num = bm->full_kv_num_blocks;
+    p.full_kv_idx = bm->full_kv_indices;
+    p.q_num = bm->q_num_blocks;
+    p.q_idx = bm->q_indices;
+    p.full_q_num = bm->full_q_num_blocks;
+    p.full_q_idx = bm->full_q_indices;
+}
+
+bsm_status hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(BSM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bsm_block_mask_workspace_bytes(int32_t seq_len, int32_t mask_b) {
+    if (bad_T(seq_len) || mask_b < 1) return 0;
+    const int64_t nt = seq_len / bsm::kTile;
+    return align256((size_t)mask_b * n_chunks(seq_len) * sizeof(int32_t)) +
+           align256((size_t)mask_b * nt * nt);
+}
+
+bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask *out,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+    bsm_status st = check_spec(spec);
+    if (st != BSM_OK) return st;
+    st = check_block_mask(out, true);
+    if (st != BSM_OK) return st;
+    const size_t need = bsm_block_mask_workspace_bytes(spec->seq_len, spec->mask_b);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSM_E_WORKSPACE, "block-mask workspace needs %zu bytes, got %zu%s", need,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
+    bsm::MaskBuildParams p{};
+    p.flags = spec->flags;
+    p.T = spec->seq_len;
+    p.nt = spec->seq_len / bsm::kTile;
+    p.mask_b = spec->mask_b;
+    p.nchunks = n_chunks(spec->seq_len);
+    p.sinks = spec->num_sinks;
+    p.doc_ids = spec->doc_ids;
+    p.window = spec->window;
+    p.out = *out;
+    char *ws = static_cast<char *>(workspace);
+    p.nonmono = reinterpret_cast<int32_t *>(ws);
+    p.cls = reinterpret_cast<uint8_t *>(ws + align256((size_t)p.mask_b * p.nchunks * sizeof(int32_t)));
+    return hip_status(bsm::launch_build_block_mask(p, static_cast<hipStream_t>(stream)),
+                      "bsm_build_block_mask launch");
+}
+
+bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_tensor *q,
+                                  const bsm_tensor *k, const bsm_tensor *v, const bsm_block_mask *bm,
+                                  const bsm_mask_spec *spec, const bsm_score_mod *mod, float scale,
+                                  const bsm_tensor *out, float *lse, void *stream) {
+    bsm_status st = check_attn_common(B, H, T, D, spec, mod);
+    if (st != BSM_OK) return st;
+    if ((st = check_block_mask(bm, false)) != BSM_OK) return st;
+    if ((st = check_tensor(q, "q")) != BSM_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSM_OK) return st;
+    if ((st = check_tensor(v, "v")) != BSM_OK) return st;
+    if ((st = check_tensor(out, "out")) != BSM_OK) return st;
+    if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
+    if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
+    bsm::AttnParams p;
+    fill_common(p, B, H, T, D, bm, spec, mod, scale);
+    fill_tensor(q, p.q, p.q_sb, p.q_sh, p.q_st);
+    fill_tensor(k, p.k, p.k_sb, p.k_sh, p.k_st);
+    fill_tensor(v, p.v, p.v_sb, p.v_sh, p.v_st);
+    const void *optr;
+    fill_tensor(out, optr, p.o_sb, p.o_sh, p.o_st);
+    p.o = const_cast<void *>(optr);
+    p.lse = lse;
+    return hip_status(bsm::launch_attn_fwd(p, D, static_cast<hipStream_t>(stream)),
+                      "bsm_flex_attention_fwd launch");
+}
+
+size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D) {
+    if (B < 1 || H < 1 || bad_T(T) || (D != 64 && D != 128)) return 0;
+    return align256((size_t)B * H * T * sizeof(float));
+}
+
+bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_tensor *q,
+                                  const bsm_tensor *k, const bsm_tensor *v, const bsm_tensor *out,
+                                  const float *lse, const bsm_tensor *dout, const bsm_block_mask *bm,
+                                  const bsm_mask_spec *spec, const bsm_score_mod *mod, float scale,
+                                  const bsm_tensor *dq, const bsm_tensor *dk, const bsm_tensor *dv,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    bsm_status st = check_attn_common(B, H, T, D, spec, mod);
+    if (st != BSM_OK) return st;
+    if ((st = check_block_mask(bm, true)) != BSM_OK) return st;
+    if ((st = check_tensor(q, "q")) != BSM_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSM_OK) return st;
+    if ((st = check_tensor(v, "v")) != BSM_OK) return st;
+    if ((st = check_tensor(out, "out")) != BSM_OK) return st;
+    if ((st = check_tensor(dout, "dout")) != BSM_OK) return st;
+    if ((st = check_tensor(dq, "dq")) != BSM_OK) return st;
+    if ((st = check_tensor(dk, "dk")) != BSM_OK) return st;
+    if ((st = check_tensor(dv, "dv")) != BSM_OK) return st;
+    if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
+    if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
+    const size_t need = bsm_bwd_workspace_bytes(B, H, T, D);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSM_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu%s", need,
+                    workspace_bytes, workspace ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
+    bsm::AttnParams p;
+    fill_common(p, B, H, T, D, bm, spec, mod, scale);
+    fill_tensor(q, p.q, p.q_sb, p.q_sh, p.q_st);
+    fill_tensor(k, p.k, p.k_sb, p.k_sh, p.k_st);
+    fill_tensor(v, p.v, p.v_sb, p.v_sh, p.v_st);
+    const void *ptr;
+    fill_tensor(out, ptr, p.o_sb, p.o_sh, p.o_st);
+    p.o = const_cast<void *>(ptr);
+    fill_tensor(dout, p.dout, p.do_sb, p.do_sh, p.do_st);
+    fill_tensor(dq, ptr, p.dq_sb, p.dq_sh, p.dq_st);
+    p.dq = const_cast<void *>(ptr);
+    fill_tensor(dk, ptr, p.dk_sb, p.dk_sh, p.dk_st);
+    p.dk = const_cast<void *>(ptr);
+    fill_tensor(dv, ptr, p.dv_sb, p.dv_sh, p.dv_st);
+    p.dv = const_cast<void *>(ptr);
+    p.lse = const_cast<float *>(lse);
+    p.delta = static_cast<float *>(workspace);
+    return hip_status(bsm::launch_attn_bwd(p, D, static_cast<hipStream_t>(stream)),
+                      "bsm_flex_attention_bwd launch");
+}
+
+const char *bsm_last_error(void) { return g_last_error.c_str(); }
+
+const char *bsm_version(void) { return "bsm 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal parameter blocks and launchers shared by the host shim and the
+// HIP kernels of the block-sparse masked attention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bsm.h"
+
+namespace bsm {
+
+constexpr int kTile = 128;          // mask granularity (query and key tiles)
+constexpr int kTilePairs = kTile * kTile;
+
+// Tile classes in the per-tile class matrix.
+enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
+
+struct MaskBuildParams {
+    uint32_t flags;
+    int32_t T;
+    int32_t nt;          // tiles per side
+    int32_t mask_b;
+    int32_t nchunks;     // 256-position chunks of the monotonicity check
+    int32_t sinks;
+    const int32_t *doc_ids;
+    const int32_t *window;
+    bsm_block_mask out;
+    uint8_t *cls;        // [mask_b, nt, nt]
+    int32_t *nonmono;    // [mask_b, nchunks]
+};
+
+struct AttnParams {
+    int32_t B, H, T, nt;
+    int32_t mask_b;
+    uint32_t mask_flags;
+    uint32_t mod_flags;
+    int32_t sinks;
+    float scale;
+    float softcap;
+    const int32_t *doc_ids;
+    const int32_t *window;
+    const float *alibi_slopes;
+    // block mask
+    const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
+    const int32_t *q_num, *q_idx, *full_q_num, *full_q_idx;
+    // tensors (bf16, strides in elements)
+    const void *q; int64_t q_sb, q_sh, q_st;
+    const void *k; int64_t k_sb, k_sh, k_st;
+    const void *v; int64_t v_sb, v_sh, v_st;
+    void *o; int64_t o_sb, o_sh, o_st;          // forward output / backward input
+    const void *dout; int64_t do_sb, do_sh, do_st;
+    void *dq; int64_t dq_sb, dq_sh, dq_st;
+    void *dk; int64_t dk_sb, dk_sh, dk_st;
+    void *dv; int64_t dv_sb, dv_sh, dv_st;
+    float *lse;      // [B, H, T]
+    float *delta;    // [B, H, T] (backward workspace)
+};
+
+hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);
+hipError_t launch_attn_fwd(const AttnParams &p, int D, hipStream_t stream);
+hipError_t launch_attn_bwd(const AttnParams &p, int D, hipStream_t stream);
+
+}  // namespace bsm

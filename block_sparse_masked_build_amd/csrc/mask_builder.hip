@@ -1,0 +1,259 @@
+// Block-mask builder: exact 128x128 tile classification of a mask predicate
+// and compaction of the non-empty tiles into per-row and per-column lists.
+//
+// What is built (speedrun notes "FlexAttention", tile-summary paragraph;
+// tutorial "FlexAttention in PyTorch", "The two hooks"): for every row of
+// query tiles, the number of tiles that are not fully masked and their
+// column indices, split into partial and full tiles; the same per column of
+// key tiles for the backward pass.  A tile's class follows from the exact
+// count of visible (q, kv) pairs in it.
+//
+// How it is computed on gfx950:
+//  * For non-decreasing document ids (packed documents as the running count of
+//    end-of-text flags, speedrun notes code listing) the visible keys of query
+//    q form at most two intervals: the main one [lo(q), hi(q)] with
+//    lo = max(doc start, q - window + 1) and hi = min(doc end, q or T-1), and
+//    a sink interval [doc start, min(sinks - 1, hi)].  A tile's pair count is
+//    then a sum of 128 interval overlaps -- exact, O(128) per tile.
+//  * Any other document ids take a general path that compares document ids
+//    key by key inside the causal/window intervals (still exact).
+//  * One workgroup per query-tile row; one lane per key tile; wave ballots and
+//    a cross-wave prefix sum compact the partial and full lists in ascending
+//    order.  A per-tile class byte is kept in the workspace and a second
+//    kernel compacts it per key-tile column the same way.
+#include "bsm_internal.hpp"
+
+namespace bsm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+__device__ inline int64_t overlap(int64_t lo, int64_t hi, int64_t k0, int64_t k1) {
+    int64_t a = lo > k0 ? lo : k0;
+    int64_t b = hi < k1 ? hi : k1;
+    return b >= a ? (b - a + 1) : 0;
+}
+
+// First index t in [lo, hi) with doc[t] >= val (doc non-decreasing).
+__device__ inline int lower_bound_doc(const int32_t *doc, int lo, int hi, int32_t val) {
+    while (lo < hi) {
+        int mid = lo + ((hi - lo) >> 1);
+        if (doc[mid] < val) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// First index t in [lo, hi) with doc[t] > val (doc non-decreasing).
+__device__ inline int upper_bound_doc(const int32_t *doc, int lo, int hi, int32_t val) {
+    while (lo < hi) {
+        int mid = lo + ((hi - lo) >> 1);
+        if (doc[mid] <= val) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// nonmono[b][c] = 1 if doc[t] > doc[t + 1] for some t in chunk c.
+__global__ __launch_bounds__(kThreads) void check_monotone_kernel(MaskBuildParams p) {
+    const int b = blockIdx.y;
+    const int t = blockIdx.x * kThreads + threadIdx.x;
+    const int32_t *doc = p.doc_ids + (int64_t)b * p.T;
+    int bad = 0;
+    if (t + 1 < p.T) bad = doc[t] > doc[t + 1];
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) p.nonmono[(int64_t)b * p.nchunks + blockIdx.x] = bad;
+}
+
+// Compacts one chunk of up to 256 class decisions (one per thread, in
+// ascending column order across threads) into the partial / full lists.
+// `run_p`/`run_f` carry the running counts across chunks.
+__device__ inline void compact_chunk(bool is_p, bool is_f, int col, int32_t *idx_p,
+                                     int32_t *idx_f, int &run_p, int &run_f,
+                                     int *s_wp, int *s_wf) {
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const unsigned long long bp = __ballot(is_p);
+    const unsigned long long bf = __ballot(is_f);
+    const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int pp = __popcll(bp & lt);
+    const int pf = __popcll(bf & lt);
+    if (lane == 0) {
+        s_wp[wv] = __popcll(bp);
+        s_wf[wv] = __popcll(bf);
+    }
+    __syncthreads();
+    int off_p = run_p, off_f = run_f, tot_p = 0, tot_f = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wv) {
+            off_p += s_wp[w];
+            off_f += s_wf[w];
+        }
+        tot_p += s_wp[w];
+        tot_f += s_wf[w];
+    }
+    if (is_p) idx_p[off_p + pp] = col;
+    if (is_f) idx_f[off_f + pf] = col;
+    run_p += tot_p;
+    run_f += tot_f;
+    __syncthreads();  // s_wp / s_wf are rewritten by the next chunk
+}
+
+__device__ inline void pad_tail(int32_t *idx, int from, int n) {
+    for (int s = from + (int)threadIdx.x; s < n; s += kThreads) idx[s] = -1;
+}
+
+__global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
+    __shared__ int64_t s_alo[kTile], s_ahi[kTile], s_blo[kTile], s_bhi[kTile];
+    __shared__ int32_t s_docq[kTile];
+    __shared__ int s_wp[kWaves], s_wf[kWaves];
+    __shared__ long long s_amin, s_amax, s_bmin, s_bmax;
+
+    const int i = blockIdx.x;
+    const int b = blockIdx.y;
+    const int T = p.T;
+    const int nt = p.nt;
+    const bool causal = p.flags & BSM_MASK_CAUSAL;
+    const bool document = p.flags & BSM_MASK_DOCUMENT;
+    const bool windowed = p.flags & BSM_MASK_WINDOW;
+    const bool sinks_on = windowed && (p.flags & BSM_MASK_SINKS) && p.sinks > 0;
+    const int32_t *doc = document ? p.doc_ids + (int64_t)b * T : nullptr;
+
+    bool mono = true;
+    if (document) {
+        int bad = 0;
+        for (int c = threadIdx.x; c < p.nchunks; c += kThreads)
+            bad |= p.nonmono[(int64_t)b * p.nchunks + c];
+        mono = !__syncthreads_or(bad);
+    }
+    const bool general = document && !mono;  // per-key document compare
+    const int64_t w = windowed ? (int64_t)(*p.window) : 0;
+
+    if (threadIdx.x == 0) {
+        s_amin = INT64_MAX; s_amax = INT64_MIN;
+        s_bmin = INT64_MAX; s_bmax = INT64_MIN;
+    }
+    __syncthreads();
+    if (threadIdx.x < kTile) {
+        const int r = threadIdx.x;
+        const int q = i * kTile + r;
+        int64_t ds = 0, de = T - 1;
+        if (document) {
+            const int32_t dq = doc[q];
+            s_docq[r] = dq;
+            if (mono) {
+                ds = lower_bound_doc(doc, 0, q + 1, dq);
+                de = upper_bound_doc(doc, q, T, dq) - 1;
+            }
+        }
+        int64_t hi = causal ? (int64_t)q : (int64_t)(T - 1);
+        if (de < hi) hi = de;
+        int64_t lo = ds;
+        if (windowed && q - w + 1 > lo) lo = q - w + 1;
+        int64_t blo = 1, bhi = 0;  // empty
+        if (sinks_on) {
+            blo = ds;
+            bhi = (int64_t)p.sinks - 1 < hi ? (int64_t)p.sinks - 1 : hi;
+        }
+        s_alo[r] = lo; s_ahi[r] = hi;
+        s_blo[r] = blo; s_bhi[r] = bhi;
+        if (lo <= hi) {
+            atomicMin(&s_amin, (long long)lo);
+            atomicMax(&s_amax, (long long)hi);
+        }
+        if (blo <= bhi) {
+            atomicMin(&s_bmin, (long long)blo);
+            atomicMax(&s_bmax, (long long)bhi);
+        }
+    }
+    __syncthreads();
+    const int64_t amin = s_amin, amax = s_amax, bmin = s_bmin, bmax = s_bmax;
+
+    const int64_t row_off = ((int64_t)b * nt + i) * nt;
+    int32_t *idx_p = p.out.kv_indices + row_off;
+    int32_t *idx_f = p.out.full_kv_indices + row_off;
+    uint8_t *cls_row = p.cls + row_off;
+    int run_p = 0, run_f = 0;
+
+    for (int jb = 0; jb < nt; jb += kThreads) {
+        const int j = jb + threadIdx.x;
+        uint8_t c = kEmpty;
+        if (j < nt) {
+            const int64_t k0 = (int64_t)j * kTile, k1 = k0 + kTile - 1;
+            const bool cand = (amin <= k1 && amax >= k0) || (bmin <= k1 && bmax >= k0);
+            if (cand) {
+                int64_t n = 0;
+                if (!general) {
+                    for (int r = 0; r < kTile; ++r) {
+                        const int64_t alo = s_alo[r], ahi = s_ahi[r];
+                        n += overlap(alo, ahi, k0, k1);
+                        if (sinks_on) {
+                            const int64_t blo = s_blo[r], bhi = s_bhi[r];
+                            n += overlap(blo, bhi, k0, k1);
+                            n -= overlap(alo > blo ? alo : blo, ahi < bhi ? ahi : bhi, k0, k1);
+                        }
+                    }
+                } else {
+                    for (int r = 0; r < kTile; ++r) {
+                        const int32_t dq = s_docq[r];
+                        const int64_t alo = s_alo[r], ahi = s_ahi[r];
+                        const int64_t a0 = alo > k0 ? alo : k0, a1 = ahi < k1 ? ahi : k1;
+                        for (int64_t kv = a0; kv <= a1; ++kv) n += (doc[kv] == dq);
+                        if (sinks_on) {
+                            const int64_t blo = s_blo[r], bhi = s_bhi[r];
+                            const int64_t b0 = blo > k0 ? blo : k0, b1 = bhi < k1 ? bhi : k1;
+                            for (int64_t kv = b0; kv <= b1; ++kv)
+                                if (kv < alo || kv > ahi) n += (doc[kv] == dq);
+                        }
+                    }
+                }
+                c = n == 0 ? kEmpty : (n == kTilePairs ? kFull : kPartial);
+            }
+            cls_row[j] = c;
+        }
+        compact_chunk(c == kPartial, c == kFull, j, idx_p, idx_f, run_p, run_f, s_wp, s_wf);
+    }
+    pad_tail(idx_p, run_p, nt);
+    pad_tail(idx_f, run_f, nt);
+    if (threadIdx.x == 0) {
+        p.out.kv_num_blocks[(int64_t)b * nt + i] = run_p;
+        p.out.full_kv_num_blocks[(int64_t)b * nt + i] = run_f;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void cols_kernel(MaskBuildParams p) {
+    __shared__ int s_wp[kWaves], s_wf[kWaves];
+    const int j = blockIdx.x;
+    const int b = blockIdx.y;
+    const int nt = p.nt;
+    const uint8_t *cls = p.cls + (int64_t)b * nt * nt;
+    const int64_t col_off = ((int64_t)b * nt + j) * nt;
+    int32_t *idx_p = p.out.q_indices + col_off;
+    int32_t *idx_f = p.out.full_q_indices + col_off;
+    int run_p = 0, run_f = 0;
+    for (int ib = 0; ib < nt; ib += kThreads) {
+        const int i = ib + threadIdx.x;
+        const uint8_t c = i < nt ? cls[(int64_t)i * nt + j] : kEmpty;
+        compact_chunk(c == kPartial, c == kFull, i, idx_p, idx_f, run_p, run_f, s_wp, s_wf);
+    }
+    pad_tail(idx_p, run_p, nt);
+    pad_tail(idx_f, run_f, nt);
+    if (threadIdx.x == 0) {
+        p.out.q_num_blocks[(int64_t)b * nt + j] = run_p;
+        p.out.full_q_num_blocks[(int64_t)b * nt + j] = run_f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream) {
+    if (p.flags & BSM_MASK_DOCUMENT) {
+        hipLaunchKernelGGL(check_monotone_kernel, dim3(p.nchunks, p.mask_b), dim3(kThreads), 0,
+                           stream, p);
+    }
+    hipLaunchKernelGGL(rows_kernel, dim3(p.nt, p.mask_b), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(cols_kernel, dim3(p.nt, p.mask_b), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace bsm

@@ -1,0 +1,195 @@
+/*
+ * bsm.h -- block-sparse masked attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over three operations:
+ *
+ *   bsm_build_block_mask    mask predicate -> per-tile classes -> tile lists
+ *   bsm_flex_attention_fwd  exact softmax attention over the listed tiles
+ *   bsm_flex_attention_bwd  dQ, dK, dV over the same tile lists
+ *
+ * The operations follow the FlexAttention method as described on three web
+ * pages: speedrun notes "FlexAttention" (sbabichenko.com), the paper record
+ * "FlexAttention: A Programming Model for Generating Optimized Attention
+ * Kernels", and the tutorial "FlexAttention in PyTorch" (intellisensei.com).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library allocates nothing and keeps no pointer after a call returns.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *    null stream) and returns without synchronising.  Nothing that lives in
+ *    device memory (document ids, the window value) is read by the host.
+ *  - Errors: a call returns a bsm_status.  Argument checks run on the host
+ *    before anything is enqueued; on failure nothing is launched and
+ *    bsm_last_error() gives a message (thread-local, valid until the next
+ *    call on the same thread).  BSM_E_HIP reports a launch failure.
+ *  - Sizes: T (sequence length, equal for queries and keys) must be a
+ *    positive multiple of 128 and at most 4,194,304.  Tiles are 128 x 128.
+ *    QT = KT = T / 128.
+ *  - bf16 tensors are [B, H, T, D] with the last dimension contiguous and
+ *    the other three strides given in elements (bsm_tensor).  Base pointers
+ *    must be 16-byte aligned and strides multiples of 8 elements.
+ */
+#ifndef BSM_H
+#define BSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BSM_OK = 0,
+    BSM_E_INVALID = 1,     /* bad argument: null pointer, bad size or stride */
+    BSM_E_UNSUPPORTED = 2, /* valid request this build does not implement   */
+    BSM_E_WORKSPACE = 3,   /* workspace missing or too small                 */
+    BSM_E_HIP = 4          /* HIP runtime reported an error at launch        */
+} bsm_status;
+
+/* Mask predicate terms (bsm_mask_spec.flags).  A (q, kv) pair is visible iff
+ *   (!CAUSAL   || q >= kv)
+ * && (!DOCUMENT || doc_ids[b][q] == doc_ids[b][kv])
+ * && (!WINDOW   || q - kv < *window || (SINKS && kv < num_sinks))
+ * Causal, same-document and window terms: speedrun notes "FlexAttention",
+ * code listing; sinks OR-ed with the window: tutorial "FlexAttention in
+ * PyTorch", Pattern 2.  SINKS without WINDOW has no effect. */
+enum {
+    BSM_MASK_CAUSAL = 1u,
+    BSM_MASK_DOCUMENT = 2u,
+    BSM_MASK_WINDOW = 4u,
+    BSM_MASK_SINKS = 8u
+};
+
+/* Score modifications (bsm_score_mod.flags), applied to s = scale * q.k in
+ * this order (tutorial "FlexAttention in PyTorch", Pattern 3):
+ *   ALIBI:   s <- s - alibi_slopes[h] * (q - kv)     (absolute positions)
+ *   SOFTCAP: s <- softcap * tanh(s / softcap)                           */
+enum {
+    BSM_MOD_ALIBI = 1u,
+    BSM_MOD_SOFTCAP = 2u
+};
+
+typedef struct {
+    uint32_t flags;          /* BSM_MASK_* bits                                    */
+    int32_t seq_len;         /* T                                                  */
+    int32_t mask_b;          /* 1: one mask shared by the whole batch; else = B    */
+    const int32_t *doc_ids;  /* DOCUMENT: device int32 [mask_b, T], any values;
+                                non-decreasing rows take the fast path            */
+    const int32_t *window;   /* WINDOW: device int32 scalar, read by the kernels at
+                                run time (may change between calls, no rebuild of
+                                anything but the block mask)                       */
+    int32_t num_sinks;       /* SINKS: keys kv < num_sinks widen the window        */
+} bsm_mask_spec;
+
+/* A block mask: the tile-level summary of a mask predicate (speedrun notes
+ * "FlexAttention", tile-summary paragraph: per row of query tiles, the number
+ * of tiles that are not fully masked and their column indices; tutorial,
+ * "The two hooks": blocks are empty, partial or full).
+ * Layout, all device int32, head dimension 1 (shared by every head):
+ *   kv_num_blocks       [mask_b, 1, QT]      partial tiles per query-tile row
+ *   kv_indices          [mask_b, 1, QT, KT]  their key-tile indices, ascending,
+ *                                            slots >= count hold -1
+ *   full_kv_num_blocks  [mask_b, 1, QT]      full tiles per row
+ *   full_kv_indices     [mask_b, 1, QT, KT]
+ *   q_num_blocks        [mask_b, 1, KT]      transposed view (per key tile,
+ *   q_indices           [mask_b, 1, KT, QT]   the query tiles), used by the
+ *   full_q_num_blocks   [mask_b, 1, KT]       backward pass
+ *   full_q_indices      [mask_b, 1, KT, QT]
+ * bsm_build_block_mask writes all eight; the forward reads the kv_* four and
+ * the backward reads all eight. */
+typedef struct {
+    int32_t *kv_num_blocks;
+    int32_t *kv_indices;
+    int32_t *full_kv_num_blocks;
+    int32_t *full_kv_indices;
+    int32_t *q_num_blocks;
+    int32_t *q_indices;
+    int32_t *full_q_num_blocks;
+    int32_t *full_q_indices;
+} bsm_block_mask;
+
+typedef struct {
+    uint32_t flags;              /* BSM_MOD_* bits                   */
+    const float *alibi_slopes;   /* ALIBI: device float32 [H]         */
+    float softcap;               /* SOFTCAP: cap value c > 0          */
+} bsm_score_mod;
+
+/* bf16 tensor [B, H, T, D]; element (b,h,t,d) lives at
+ * ptr + b*stride_b + h*stride_h + t*stride_t + d  (strides in elements). */
+typedef struct {
+    void *ptr;
+    int64_t stride_b;
+    int64_t stride_h;
+    int64_t stride_t;
+} bsm_tensor;
+
+/* Bytes of device workspace bsm_build_block_mask needs (per-tile class
+ * bytes and per-chunk monotonicity flags). */
+size_t bsm_block_mask_workspace_bytes(int32_t seq_len, int32_t mask_b);
+
+/* Build the block mask of `spec` (speedrun notes "FlexAttention",
+ * tile-summary paragraph; tutorial "FlexAttention in PyTorch", "The two
+ * hooks").  Every tile's class comes from the exact number of visible pairs
+ * in it: 0 -> empty (not listed), 128*128 -> full, otherwise partial.
+ * The tutorial's advice holds: build once per mask and reuse it across
+ * forward calls; rebuild only when the window or documents change.
+ * workspace: device, >= bsm_block_mask_workspace_bytes(), 256-byte aligned,
+ * contents need not be initialised.  Errors: BSM_E_INVALID (null spec/out
+ * pointers, bad T or mask_b, DOCUMENT without doc_ids, WINDOW without
+ * window), BSM_E_WORKSPACE, BSM_E_HIP. */
+bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask *out,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Forward attention (speedrun notes "FlexAttention", Context: the two
+ * matmuls and the softmax fused in one tiled kernel that never writes the
+ * T x T scores; the kernel visits only listed tiles, applies the elementwise
+ * mask only to partial tiles and the score modifications to every score).
+ *   out[b,h,q,:] = sum_{kv visible} softmax_kv(s)[kv] * v[b,h,kv,:]
+ *   lse[b,h,q]   = log sum_{kv visible} exp(s[kv])   (natural log; -inf and
+ *                  out = 0 for a query with no visible key)
+ * D in {64, 128}.  scale <= 0 selects 1/sqrt(D).  mod may be NULL.
+ * bm must be the block mask of `spec` (as built by bsm_build_block_mask);
+ * the mask batch index is b when spec->mask_b == B, else 0.
+ * lse: device float32 [B, H, T], contiguous.
+ * Errors: BSM_E_INVALID, BSM_E_UNSUPPORTED (D not 64/128), BSM_E_HIP. */
+bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D,
+                                  const bsm_tensor *q, const bsm_tensor *k,
+                                  const bsm_tensor *v, const bsm_block_mask *bm,
+                                  const bsm_mask_spec *spec, const bsm_score_mod *mod,
+                                  float scale, const bsm_tensor *out, float *lse,
+                                  void *stream);
+
+/* Bytes of device workspace bsm_flex_attention_bwd needs. */
+size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D);
+
+/* Backward attention: gradients of sum(out * dout) with respect to q, k, v
+ * through the softmax, the mask and the score modifications (tutorial
+ * "FlexAttention in PyTorch", Pattern 3: differentiable score mods with a
+ * fused backward).  Visits exactly the tiles the block mask lists.
+ * out and lse are the forward's outputs for the same inputs.
+ * dq, dk, dv: bf16 [B, H, T, D], fully overwritten.
+ * workspace: device, >= bsm_bwd_workspace_bytes(), 256-byte aligned.
+ * Errors: as the forward, plus BSM_E_WORKSPACE. */
+bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
+                                  const bsm_tensor *q, const bsm_tensor *k,
+                                  const bsm_tensor *v, const bsm_tensor *out,
+                                  const float *lse, const bsm_tensor *dout,
+                                  const bsm_block_mask *bm, const bsm_mask_spec *spec,
+                                  const bsm_score_mod *mod, float scale,
+                                  const bsm_tensor *dq, const bsm_tensor *dk,
+                                  const bsm_tensor *dv, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *bsm_last_error(void);
+
+/* Library version string. */
+const char *bsm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSM_H */

@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/bsm.h declares, and rejects bad arguments on the host before any
+launch (the fake device pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_masked_build_amd import _lib
+from block_sparse_masked_build_amd._lib import (BsmBlockMask, BsmMaskSpec, BsmScoreMod, BsmTensor,
+                                                lib)
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails host checks
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "bsm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsm_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+
+
+def test_version():
+    assert lib.bsm_version().decode().startswith("bsm ")
+
+
+def _spec(**kw):
+    d = dict(flags=1, seq_len=1024, mask_b=1, doc_ids=None, window=None, num_sinks=0)
+    d.update(kw)
+    return BsmMaskSpec(**d)
+
+
+def _bm(null=None):
+    v = [FAKE] * 8
+    if null is not None:
+        v[null] = None
+    return BsmBlockMask(*v)
+
+
+def _build(spec, bm=None, ws=FAKE, nbytes=1 << 30):
+    bm = bm or _bm()
+    return lib.bsm_build_block_mask(ctypes.byref(spec), ctypes.byref(bm), ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seq_len=1000), _lib.BSM_E_INVALID),
+    (dict(seq_len=0), _lib.BSM_E_INVALID),
+    (dict(seq_len=(1 << 22) + 128), _lib.BSM_E_INVALID),
+    (dict(mask_b=0), _lib.BSM_E_INVALID),
+    (dict(flags=2), _lib.BSM_E_INVALID),          # DOCUMENT without doc_ids
+    (dict(flags=4), _lib.BSM_E_INVALID),          # WINDOW without window
+    (dict(flags=64), _lib.BSM_E_INVALID),         # unknown bit
+    (dict(flags=12, window=FAKE, num_sinks=-1), _lib.BSM_E_INVALID),
+])
+def test_build_rejects_bad_spec(kw, code):
+    assert _build(_spec(**kw)) == code
+    assert lib.bsm_last_error().decode() != ""
+
+
+def test_build_rejects_null_outputs_and_small_workspace():
+    for i in range(8):
+        assert _build(_spec(), _bm(null=i)) == _lib.BSM_E_INVALID
+    need = lib.bsm_block_mask_workspace_bytes(1024, 1)
+    assert need >= 64  # 8x8 class bytes + flags
+    assert _build(_spec(), ws=FAKE, nbytes=need - 1) == _lib.BSM_E_WORKSPACE
+    assert _build(_spec(), ws=None, nbytes=need) == _lib.BSM_E_WORKSPACE
+    assert _build(_spec(), ws=FAKE + 16, nbytes=need) == _lib.BSM_E_WORKSPACE
+    assert b"workspace" in lib.bsm_last_error()
+
+
+def test_workspace_sizes():
+    assert lib.bsm_block_mask_workspace_bytes(100, 1) == 0
+    assert lib.bsm_block_mask_workspace_bytes(65536, 1) >= 512 * 512
+    assert lib.bsm_block_mask_workspace_bytes(65536, 2) >= 2 * 512 * 512
+    assert lib.bsm_bwd_workspace_bytes(2, 16, 16384, 128) >= 2 * 16 * 16384 * 4
+    assert lib.bsm_bwd_workspace_bytes(1, 1, 1024, 96) == 0
+
+
+def _t(ptr=FAKE, sb=8 * 1024 * 64, sh=1024 * 64, st=64):
+    return BsmTensor(ptr, sb, sh, st)
+
+
+def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=None, lse=FAKE,
+         bm=None, scale=0.0):
+    spec = spec or _spec()
+    bm = bm or _bm()
+    q, k, v, o = (x or _t() for x in (q, k, v, o))
+    return lib.bsm_flex_attention_fwd(B, H, T, D, ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                      ctypes.byref(bm), ctypes.byref(spec),
+                                      ctypes.byref(mod) if mod is not None else None, scale,
+                                      ctypes.byref(o), lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), _lib.BSM_E_UNSUPPORTED),
+    (dict(D=256), _lib.BSM_E_UNSUPPORTED),
+    (dict(T=1000), _lib.BSM_E_INVALID),
+    (dict(T=2048), _lib.BSM_E_INVALID),            # != spec seq_len
+    (dict(B=0), _lib.BSM_E_INVALID),
+    (dict(B=3, spec=_spec(flags=3, mask_b=2, doc_ids=FAKE)), _lib.BSM_E_INVALID),
+    (dict(q=_t(ptr=FAKE + 8)), _lib.BSM_E_INVALID),  # misaligned
+    (dict(k=_t(st=60)), _lib.BSM_E_INVALID),        # stride not a multiple of 8
+    (dict(v=_t(ptr=0)), _lib.BSM_E_INVALID),
+    (dict(lse=None), _lib.BSM_E_INVALID),
+    (dict(bm=_bm(null=0)), _lib.BSM_E_INVALID),
+    (dict(mod=BsmScoreMod(1, None, 0.0)), _lib.BSM_E_INVALID),        # ALiBi without slopes
+    (dict(mod=BsmScoreMod(2, None, 0.0)), _lib.BSM_E_INVALID),        # cap must be > 0
+    (dict(mod=BsmScoreMod(2, None, float("inf"))), _lib.BSM_E_INVALID),
+    (dict(mod=BsmScoreMod(8, None, 1.0)), _lib.BSM_E_INVALID),
+    (dict(scale=float("nan")), _lib.BSM_E_INVALID),
+])
+def test_fwd_rejects(kw, code):
+    assert _fwd(**kw) == code
+    assert lib.bsm_last_error().decode() != ""
+
+
+def test_bwd_rejects_small_workspace_and_missing_transposed_lists():
+    spec = _spec()
+    t = _t()
+    need = lib.bsm_bwd_workspace_bytes(1, 1, 1024, 64)
+
+    def call(bm, ws, n):
+        return lib.bsm_flex_attention_bwd(
+            1, 1, 1024, 64, *([ctypes.byref(t)] * 4), FAKE, ctypes.byref(t), ctypes.byref(bm),
+            ctypes.byref(spec), None, 0.0, *([ctypes.byref(t)] * 3), ws, n, None)
+
+    assert call(_bm(), FAKE, need - 4) == _lib.BSM_E_WORKSPACE
+    assert call(_bm(), None, need) == _lib.BSM_E_WORKSPACE
+    for i in range(4, 8):
+        assert call(_bm(null=i), FAKE, need) == _lib.BSM_E_INVALID
