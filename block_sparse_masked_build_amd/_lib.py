@@ -8,6 +8,12 @@ from __future__ import annotations
 import ctypes
 import os
 
+# libbsm.so links libamdhip64 dynamically.  PyTorch ships its own HIP runtime;
+# importing torch first makes the library bind to that one, so that device
+# memory and streams from torch and the kernels launched here share a single
+# runtime in the process.
+import torch  # noqa: F401
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libbsm.so")
 

@@ -16,12 +16,18 @@
 //    score and output accumulators of a query live in one lane pair: the
 //    online softmax (running max m, running sum l, fp32) needs one cross-half
 //    exchange per tile, and the output rescale is lane-local;
-//  * Q stays in registers; K is staged row-major in LDS, V transposed (keys
-//    contiguous, bits 2/3 of the key swapped so each MFMA operand is one
-//    16-byte read); rows padded by 16 bytes against bank conflicts;
-//  * the next listed tile is loaded from HBM into registers while the current
-//    one computes (one LDS buffer, register double-buffering);
-//  * exp via exp2 with log2(e) folded into the score scale.
+//  * Q stays in registers; K and V tiles are copied HBM -> LDS directly
+//    (global_load_lds, 16 bytes per lane, no registers), row-major with
+//    XOR-swizzled 16-byte chunks; the V^T operand comes from transposing LDS
+//    reads (ds_read_tr16_b64), so no tile is ever transposed by hand;
+//  * the copies run asynchronously: the next K tile is requested as soon as
+//    every wave is done with QK^T, the next V tile as soon as PV is done, so
+//    HBM latency hides behind the softmax and the other matrix product;
+//  * two workgroups per CU (at most 256 registers per lane), so one
+//    workgroup's tile loads and softmax overlap the other's matrix products;
+//  * exp via exp2 with log2(e) and the score scale folded into one FMA; the
+//    running maximum is only moved (and the output rescaled) when a score
+//    exceeds it by more than 2^8.
 #include "attn_common.hpp"
 
 namespace bsm {
@@ -29,91 +35,54 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D>
-struct FwdSmem {
-    static constexpr int KS = D + 8;       // K row stride (elements)
-    static constexpr int VS = kTile + 8;   // V^T row stride (elements)
-    __bf16 k[kTile * KS];
-    __bf16 vt[D * VS];
-    int32_t doc[kTile];
-};
-
-template <int D>
-struct TilePrefetch {
-    static constexpr int KCH = kTile * D / 8 / kThreads;  // 16-byte K chunks per thread
-    static constexpr int VU = 32 * (D / 8) / kThreads;     // (4-key group, d-chunk) units per thread
-    uint4 k[KCH];
-    uint4 v[VU][4];
-    int32_t doc;
-};
-
-template <int D>
-__device__ inline void prefetch_tile(TilePrefetch<D> &pf, const __bf16 *kbase, const __bf16 *vbase,
-                                     int64_t k_st, int64_t v_st, const int32_t *doc, int j) {
-    const int tid = threadIdx.x;
-    const int key0 = j * kTile;
-#pragma unroll
-    for (int it = 0; it < TilePrefetch<D>::KCH; ++it) {
-        const int c = it * kThreads + tid;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        pf.k[it] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)(key0 + row) * k_st + col);
-    }
-#pragma unroll
-    for (int it = 0; it < TilePrefetch<D>::VU; ++it) {
-        const int u = it * kThreads + tid;
-        const int g = u / (D / 8), cc = (u % (D / 8)) * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            pf.v[it][e] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)(key0 + 4 * g + e) * v_st + cc);
-    }
-    if (doc != nullptr && tid < kTile) pf.doc = doc[key0 + tid];
-}
-
-__device__ inline uint32_t u16_at(const uint4 &x, int i) {
-    const uint32_t w = (i >> 1) == 0 ? x.x : (i >> 1) == 1 ? x.y : (i >> 1) == 2 ? x.z : x.w;
-    return (i & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-template <int D>
-__device__ inline void store_tile(FwdSmem<D> &sm, const TilePrefetch<D> &pf, bool has_doc) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int it = 0; it < TilePrefetch<D>::KCH; ++it) {
-        const int c = it * kThreads + tid;
-        const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<uint4 *>(&sm.k[row * FwdSmem<D>::KS + col]) = pf.k[it];
-    }
-#pragma unroll
-    for (int it = 0; it < TilePrefetch<D>::VU; ++it) {
-        const int u = it * kThreads + tid;
-        const int g = u / (D / 8), cc = (u % (D / 8)) * 8;
-        const int slot = vt_slot(4 * g);
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-            uint2 w;
-            w.x = u16_at(pf.v[it][0], dd) | (u16_at(pf.v[it][1], dd) << 16);
-            w.y = u16_at(pf.v[it][2], dd) | (u16_at(pf.v[it][3], dd) << 16);
-            *reinterpret_cast<uint2 *>(&sm.vt[(cc + dd) * FwdSmem<D>::VS + slot]) = w;
-        }
-    }
-    if (has_doc && tid < kTile) sm.doc[tid] = pf.doc;
-}
-
 struct RowMask {
     int32_t klo, khi;   // visible window/causal interval of keys
     int32_t sink_end;   // keys < sink_end are visible through the sink term
-    int32_t docq;
-    bool doc_on;
+    int32_t docq;       // document id of the query (0 without the document term)
 };
 
-template <int D, bool ALIBI, bool SOFTCAP, bool MASKED>
-__device__ inline void fwd_tile(const FwdSmem<D> &sm, const bf16x8 (&qf)[D / 16],
-                                f32x16 (&o)[D / 32], float &m, float &l, int j, int qpos,
-                                float scale_log2, float scale, float slope, float cap,
-                                float inv_cap, const RowMask &rm) {
+// Per-query state of the online softmax.  m is the reference maximum (log2
+// domain) the accumulators are scaled to; it is only moved when a new score
+// exceeds it by more than 2^8, so most tiles skip the rescale.  The result
+// stays exact because o and l always share the same reference.
+constexpr float kRescaleThreshold = 8.0f;
+
+// Per-lane LDS byte offsets of the matrix-core operands inside a tile.
+template <int D>
+struct OperandOffsets {
+    int k[D / 16];        // A operand of S^T = K Q^T, per 16-wide d step (row = lane's key in block 0)
+    int v[2][D / 32];     // transposing reads of V, per half (keys +0..3 / +8..11) and d block
+};
+
+template <int D>
+__device__ inline void operand_offsets(OperandOffsets<D> &off) {
+    using L = TileLayout<D>;
     const int lane = threadIdx.x & 63;
     const int n = lane & 31, hl = lane >> 5;
-    f32x16 s[4];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) off.k[st] = n * L::kRowBytes + (((2 * st + hl) ^ L::fk(n)) << 4);
+    // ds_read_tr16_b64: lane j of a 16-lane group G supplies the address of
+    // row K0 + j/4, columns d0 + 4 (j%4) .. +3; lane i then receives rows
+    // K0..K0+3 of column d0 + i.  d0 = 32 db + 16 (G%2); K0 = 4 (G/2) (+8 for
+    // the second half) inside each 16-key group.
+    const int G = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int r = 8 * u + 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int c = db * 4 + 2 * (G & 1) + ((j & 3) >> 1);
+            off.v[u][db] = r * L::kRowBytes + ((c ^ L::fv(r)) << 4) + ((j & 1) << 3);
+        }
+    }
+}
+
+// S^T = K Q^T for one tile: lane (query n, half hl) gets, for key block kb,
+// the 16 scores of keys 32 kb + 8 (r/4) + 4 hl + r%4, r = 0..15.
+template <int D>
+__device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, const bf16x8 (&qf)[D / 16],
+                              f32x16 (&s)[4]) {
+    const char *kbytes = reinterpret_cast<const char *>(sk);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -122,73 +91,105 @@ __device__ inline void fwd_tile(const FwdSmem<D> &sm, const bf16x8 (&qf)[D / 16]
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                &sm.k[(kb * 32 + n) * FwdSmem<D>::KS + st * 16 + hl * 8]);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbytes + kb * 32 * TileLayout<D>::kRowBytes + off.k[st]);
             s[kb] = mfma32(a, qf[st], s[kb]);
         }
     }
-    float mx = -INFINITY;
-    const int kbase = j * kTile;
+    sched_interleave<4 * (D / 16), 4>();
+}
+
+// Score modifications (to the log2 domain) and, on partial tiles, the mask.
+template <bool ALIBI, bool SOFTCAP, bool MASKED>
+__device__ inline void fwd_mod_mask(const int32_t *sdoc, f32x16 (&s)[4], int j, int qpos, float scale, float slope,
+                                    float cap, float inv_cap, const RowMask &rm) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const int hl = (threadIdx.x & 63) >> 5;
+    const int kbase = j * kTile + hl * 4;
+    // Mask bounds relative to this tile.  Kept opaque so that the compiler
+    // compares them with the per-register key offsets inside the loop instead
+    // of hoisting 3 x 64 loop-invariant thresholds into registers.
+    int lo_t = rm.klo - kbase, hi_t = rm.khi - kbase, se_t = rm.sink_end - kbase;
+    if (MASKED) asm volatile("" : "+v"(lo_t), "+v"(hi_t), "+v"(se_t));
+    int rel = qpos - kbase;
+    if (ALIBI) asm volatile("" : "+v"(rel));
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             int4 dk = {0, 0, 0, 0};
-            if (MASKED && rm.doc_on)
-                dk = *reinterpret_cast<const int4 *>(&sm.doc[kb * 32 + g * 8 + hl * 4]);
+            if (MASKED) dk = *reinterpret_cast<const int4 *>(&sdoc[kb * 32 + g * 8 + hl * 4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = g * 4 + e;
-                const int kpos = kbase + kb * 32 + g * 8 + hl * 4 + e;
-                float t;
-                if (!ALIBI && !SOFTCAP) {
-                    t = s[kb][r] * scale_log2;
-                } else {
-                    float y = s[kb][r] * scale;
-                    if (ALIBI) y -= slope * (float)(qpos - kpos);
+                const int c = kb * 32 + g * 8 + e;  // key - kbase
+                float t = s[kb][r];
+                if (kMods) {
+                    float y = t * scale;
+                    if (ALIBI) y -= slope * (float)(rel - c);
                     if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
                     t = y * kLog2e;
                 }
                 if (MASKED) {
-                    bool vis = (kpos >= rm.klo || kpos < rm.sink_end) && kpos <= rm.khi;
-                    if (rm.doc_on) {
-                        const int dkv = e == 0 ? dk.x : e == 1 ? dk.y : e == 2 ? dk.z : dk.w;
-                        vis = vis && (dkv == rm.docq);
-                    }
+                    // Without the document term the staged ids and docq are all 0.
+                    const int dkv = e == 0 ? dk.x : e == 1 ? dk.y : e == 2 ? dk.z : dk.w;
+                    const bool vis = (c >= lo_t || c < se_t) && c <= hi_t && dkv == rm.docq;
                     t = vis ? t : -INFINITY;
                 }
                 s[kb][r] = t;
-                mx = fmaxf(mx, t);
             }
         }
     }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP>
+__device__ inline void fwd_softmax(f32x16 (&s)[4], f32x16 (&o)[D / 32], float &m, float &l, float scale_log2) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    l *= alpha;
+    if (!kMods) mx *= scale_log2;
+    if (__any(mx > m + kRescaleThreshold)) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
+        l *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    m = m_new;
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        m = m_new;
+    }
+    const float m_use = (m == -INFINITY) ? 0.0f : m;
+    const float c_mul = kMods ? 1.0f : scale_log2;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float pv = fast_exp2(__builtin_fmaf(s[kb][r], c_mul, -m_use));
+            l += pv;
+            s[kb][r] = pv;
+        }
+}
+
+template <int D>
+__device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, const f32x16 (&s)[4],
+                              f32x16 (&o)[D / 32]) {
+    const char *vbytes = reinterpret_cast<const char *>(sv);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pv[e] = fast_exp2(s[kb][s2 * 8 + e] - m_use);
-                l += pv[e];
-            }
             bf16x8 pb;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(pv[e]);
+            for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[kb][s2 * 8 + e]);
+            const int rowbase = (kb * 32 + s2 * 16) * TileLayout<D>::kRowBytes;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    &sm.vt[(db * 32 + n) * FwdSmem<D>::VS + kb * 32 + s2 * 16 + hl * 8]);
+                const i16x4 lo = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + off.v[0][db]));
+                const i16x4 hi = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + off.v[1][db]));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[db] = mfma32(a, pb, o[db]);
             }
         }
@@ -196,8 +197,13 @@ __device__ inline void fwd_tile(const FwdSmem<D> &sm, const bf16x8 (&qf)[D / 16]
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
+    // Separate LDS objects so the compiler can tell the copies into one from
+    // reads of another (its wait-count insertion tracks them per object).
+    __shared__ __attribute__((aligned(1024))) __bf16 sk[kTile * D];   // keys, rows swizzled by fk
+    __shared__ __attribute__((aligned(1024))) __bf16 sv[kTile * D];   // values, rows swizzled by fv
+    __shared__ __attribute__((aligned(16))) int32_t sdoc[kTile];      // document ids of the keys
+    constexpr int kInstr = tile_lds_instr<D>();
 
     const int nt = p.nt;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -215,17 +221,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnParams p) {
     const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
     const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
 
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
-
     const int bm = p.mask_b == 1 ? 0 : b;
     const int64_t row = (int64_t)bm * nt + i;
     // Counts and indices are clamped to the grid so that a corrupt block mask
     // gives wrong numbers instead of out-of-bounds reads.
-    const int nfull = min(max(p.full_kv_num[row], 0), nt);
-    const int npart = min(max(p.kv_num[row], 0), nt);
+    const int nfull = min(max(load_uniform(p.full_kv_num + row), 0), nt);
+    const int npart = min(max(load_uniform(p.kv_num + row), 0), nt);
     const int32_t *fidx = p.full_kv_idx + row * nt;
     const int32_t *pidx = p.kv_idx + row * nt;
     const int total = nfull + npart;
@@ -233,7 +234,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnParams p) {
     const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
     const int32_t *doc = doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
     RowMask rm;
-    rm.doc_on = doc_on;
     rm.docq = doc_on ? doc[qpos] : 0;
     rm.khi = (p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1;
     rm.klo = -1;
@@ -244,6 +244,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnParams p) {
         rm.klo = (int32_t)lo;
         if ((p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0) rm.sink_end = p.sinks;
     }
+    if (!doc_on && tid < kTile) sdoc[tid] = 0;  // compared against docq = 0
+    wait_lds_reads();                            // the fill is complete before the first barrier
 
     const float scale = p.scale;
     const float scale_log2 = p.scale * kLog2e;
@@ -251,31 +253,66 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnParams p) {
     const float cap = SOFTCAP ? p.softcap : 1.0f;
     const float inv_cap = 1.0f / cap;
 
+    OperandOffsets<D> off;
+    operand_offsets<D>(off);
+
+    auto tile_at = [&](int it) {
+        return clamp_tile(it < nfull ? load_uniform(fidx + it) : load_uniform(pidx + it - nfull), nt);
+    };
+    // Copies in flight per wave, in issue order: [doc(it), K(it)] then V(it).
+    auto issue_k = [&](int jj) {
+        if (doc_on) issue_ints_to_lds(sdoc, doc + jj * kTile);
+        issue_tile_to_lds<D, false>(sk, kb_ + (int64_t)jj * kTile * p.k_st, p.k_st);
+    };
+    auto issue_v = [&](int jj) { issue_tile_to_lds<D, true>(sv, vb + (int64_t)jj * kTile * p.v_st, p.v_st); };
+
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
+
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m = -INFINITY, l = 0.0f;
+    wait_vmcnt<0>();  // Q and the query's document id are in registers before any tile copy
 
-    TilePrefetch<D> pf;
-    if (total > 0)
-        prefetch_tile<D>(pf, kb_, vb, p.k_st, p.v_st, doc, clamp_tile(nfull > 0 ? fidx[0] : pidx[0], nt));
+    int j = total > 0 ? tile_at(0) : 0;
+    if (total > 0) {
+        issue_k(j);
+        issue_v(j);
+    }
     for (int it = 0; it < total; ++it) {
-        const int j = clamp_tile(it < nfull ? fidx[it] : pidx[it - nfull], nt);
-        __syncthreads();
-        store_tile<D>(sm, pf, doc_on);
-        __syncthreads();
-        if (it + 1 < total) {
-            const int jn = clamp_tile((it + 1) < nfull ? fidx[it + 1] : pidx[it + 1 - nfull], nt);
-            prefetch_tile<D>(pf, kb_, vb, p.k_st, p.v_st, doc, jn);
+        const bool more = it + 1 < total;
+        const int jn = more ? tile_at(it + 1) : 0;
+        // Copies in flight per wave, oldest first: [doc(it)] K(it), V(it).
+        wait_vmcnt<kInstr>();  // doc(it), K(it) landed
+        tile_barrier();        // ... in every wave
+        f32x16 s[4];
+        fwd_qk<D>(sk, off, qf, s);
+        if (it < nfull) {
+            if (ALIBI || SOFTCAP) fwd_mod_mask<ALIBI, SOFTCAP, false>(sdoc, s, j, qpos, scale, slope, cap, inv_cap, rm);
+        } else {
+            fwd_mod_mask<ALIBI, SOFTCAP, true>(sdoc, s, j, qpos, scale, slope, cap, inv_cap, rm);
         }
-        if (it < nfull)
-            fwd_tile<D, ALIBI, SOFTCAP, false>(sm, qf, o, m, l, j, qpos, scale_log2, scale, slope,
-                                               cap, inv_cap, rm);
-        else
-            fwd_tile<D, ALIBI, SOFTCAP, true>(sm, qf, o, m, l, j, qpos, scale_log2, scale, slope,
-                                              cap, inv_cap, rm);
+        wait_lds_reads();
+        tile_barrier();        // every wave is done reading K(it) and doc(it)
+        if (more) issue_k(jn);
+        fwd_softmax<D, ALIBI, SOFTCAP>(s, o, m, l, scale_log2);
+        // In flight now: V(it), then [doc(it+1)] K(it+1).
+        if (more) {
+            if (doc_on) wait_vmcnt<kInstr + 1>(); else wait_vmcnt<kInstr>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        tile_barrier();        // V(it) landed in every wave
+        fwd_pv<D>(sv, off, s, o);
+        wait_lds_reads();
+        tile_barrier();        // every wave is done reading V(it)
+        if (more) issue_v(jn);
+        j = jn;
     }
 
     const float l_tot = l + __shfl_xor(l, 32);
@@ -285,10 +322,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(AttnParams p) {
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            uint2 w;
+            u32x2 w;
             w.x = pack_bf16x2(o[db][g * 4 + 0] * inv, o[db][g * 4 + 1] * inv);
             w.y = pack_bf16x2(o[db][g * 4 + 2] * inv, o[db][g * 4 + 3] * inv);
-            *reinterpret_cast<uint2 *>(ob + db * 32 + g * 8 + hl * 4) = w;
+            *reinterpret_cast<u32x2 *>(ob + db * 32 + g * 8 + hl * 4) = w;
         }
     }
     if (hl == 0) {

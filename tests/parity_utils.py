@@ -1,6 +1,14 @@
 """Helpers shared by the GPU parity tests: run the HIP path and the oracle on
-the same seeded inputs and compare.  Tolerances for bf16 outputs: max-abs
-2e-2 and mean-abs 2e-3 against the fp64 oracle; lse (fp32): max-abs 1e-3."""
+the same seeded inputs and compare.
+
+Tolerances for bf16 outputs against the fp64 oracle:
+  * the five workloads: max-abs 2e-2 and mean-abs 2e-3 (fixed bar);
+  * randomized edge cases, whose outputs can reach |x| ~ 4 and more (tiny
+    windows concentrate the softmax): |err| <= 2e-2 + 2^-8 |ref| per element
+    and mean-abs 2e-3.  Rounding the exact value to bf16 alone costs up to
+    |x| 2^-9, and the bf16 probabilities / score gradients fed to the matrix
+    cores cost about as much again.
+lse (fp32): max-abs 1e-3."""
 import numpy as np
 import pytest
 import torch
@@ -47,14 +55,23 @@ def f64(t):
     return t.detach().float().cpu().double().numpy()
 
 
-def assert_close(gpu, ref, ctx="", max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+EDGE_RTOL = 2.0 ** -8
+
+
+def assert_close(gpu, ref, ctx="", max_abs=MAX_ABS, mean_abs=MEAN_ABS, rtol=0.0):
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (ctx, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{ctx}: non-finite values"
     err = np.abs(gpu - ref)
     mx, mn = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
-    assert mx <= max_abs and mn <= mean_abs, f"{ctx}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+    if rtol == 0.0:
+        assert mx <= max_abs and mn <= mean_abs, f"{ctx}: max-abs {mx:.3e} mean-abs {mn:.3e}"
+    else:
+        excess = err - (max_abs + rtol * np.abs(ref))
+        worst = float(excess.max()) if err.size else -1.0
+        assert worst <= 0.0 and mn <= mean_abs, (
+            f"{ctx}: max-abs {mx:.3e} (bound exceeded by {worst:.3e}) mean-abs {mn:.3e}")
     return mx, mn
 
 
