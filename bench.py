@@ -75,7 +75,7 @@ def measured_traffic():
 
 
 def cpu_baseline(w, tensors, budget_s: float):
-    """Times the oracle (fp64, single thread) on whole query tiles, 64 per
+    """Times the oracle (fp64, single thread) on whole query tiles, 256 per
     head spread over the sequence, head after head, until the time budget is
     used."""
     import numpy as np
@@ -85,7 +85,7 @@ def cpu_baseline(w, tensors, budget_s: float):
     counts = oracle.tile_counts(w.spec)
     vis_per_row = (counts > 0).sum(axis=2)  # [mask_b, QT]
     nt = w.T // TILE
-    order = [int(x) for x in np.linspace(0, nt - 1, num=min(nt, 64)).round()]
+    order = [int(x) for x in np.linspace(0, nt - 1, num=min(nt, 256)).round()]
     done, flops = 0, 0.0
     heads = 0
     t0 = time.perf_counter()

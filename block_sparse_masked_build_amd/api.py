@@ -85,6 +85,7 @@ class BlockMask(NamedTuple):
     q_indices: torch.Tensor
     full_q_num_blocks: torch.Tensor
     full_q_indices: torch.Tensor
+    doc_range: torch.Tensor   # int32 [mask_b, T, 2]: (first, last) position of each position's document
 
     def c_struct(self) -> BsmBlockMask:
         return BsmBlockMask(*[t.data_ptr() for t in self])
@@ -131,7 +132,8 @@ def empty_block_mask(T: int, mask_b: int, device="cuda") -> BlockMask:
     nt = T // TILE
     mk = lambda *s: torch.empty(s, dtype=torch.int32, device=device)
     return BlockMask(mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
-                     mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt))
+                     mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
+                     mk(mask_b, T, 2))
 
 
 def block_mask_workspace(spec: MaskSpec) -> torch.Tensor:

@@ -146,11 +146,12 @@ __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
 // belongs there under the swizzle).  Completion is tracked by vmcnt.
 // Addresses are a wave-uniform base (scalar registers) plus a 32-bit per-lane
 // offset; with the swizzles above only a handful of distinct offsets occur.
-template <int D, bool IS_V>
+template <int D, bool IS_V, int ROWS = kTile>
 __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride) {
     using L = TileLayout<D>;
     constexpr int kRowsPerInstr = 1024 / L::kRowBytes;
-    constexpr int kInstr = kTile / kRowsPerInstr / 4;
+    constexpr int kInstr = ROWS / kRowsPerInstr / 4;
+    static_assert(kInstr >= 1, "at least one copy per wave");
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t row_bytes = row_stride * 2;
     const char *wbase = reinterpret_cast<const char *>(g_row0) + (int64_t)(wv * kInstr * kRowsPerInstr) * row_bytes;
@@ -170,10 +171,12 @@ __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0,
 template <int D>
 constexpr int tile_lds_instr() { return kTile / (1024 / TileLayout<D>::kRowBytes) / 4; }
 
-// 32 of the tile's 128 int32 values (wave w copies entries 32w..32w+31).
+// N int32 values, N/4 per wave (wave w copies entries w N/4 .. (w+1) N/4 - 1).
+template <int N = kTile>
 __device__ inline void issue_ints_to_lds(int32_t *lds, const int32_t *g) {
+    constexpr int kPer = N / 4;
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane < 32) copy4_to_lds(g + wv * 32 + lane, lds_addr(lds + wv * 32));
+    if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds_addr(lds + wv * kPer));
 }
 
 // s_waitcnt on vmcnt only (gfx9 encoding; expcnt and lgkmcnt left at max).
@@ -209,6 +212,21 @@ __device__ inline void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xc07f & ~(
 // tracked by lgkmcnt rather than vmcnt, so it never waits on tile copies.
 __device__ inline int32_t load_uniform(const int32_t *p) {
     return *(const __attribute__((address_space(4))) int32_t *)(p);
+}
+
+// Scheduling pattern for a straight-line block of N_MFMA matrix products
+// whose A operands come from LDS (READS_PER reads each) mixed with
+// independent VALU work: AHEAD reads first, then per product one MFMA, its
+// share of the following reads and VALU_PER vector instructions.
+template <int N_MFMA, int READS_PER, int AHEAD, int VALU_PER>
+__device__ inline void sched_interleave_mfma_valu() {
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+    for (int x = 0; x < N_MFMA; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, READS_PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VALU_PER, 0);
+    }
 }
 
 __device__ inline int clamp_tile(int j, int nt) { return j < 0 ? 0 : (j >= nt ? nt - 1 : j); }

@@ -20,11 +20,15 @@
 //    (global_load_lds, 16 bytes per lane, no registers), row-major with
 //    XOR-swizzled 16-byte chunks; the V^T operand comes from transposing LDS
 //    reads (ds_read_tr16_b64), so no tile is ever transposed by hand;
-//  * the copies run asynchronously: the next K tile is requested as soon as
-//    every wave is done with QK^T, the next V tile as soon as PV is done, so
-//    HBM latency hides behind the softmax and the other matrix product;
+//  * each listed 128-key tile is processed as two 64-key halves through
+//    double-buffered LDS: one barrier per half, and every copy is issued a
+//    whole half-iteration before it is read (K two halves ahead, V one);
+//  * software pipeline inside each wave: the QK^T products of the next half
+//    are interleaved with the exponentials of the current one, and the PV
+//    products of the current half with the masking of the next one, so the
+//    matrix cores and the vector ALU work at the same time;
 //  * two workgroups per CU (at most 256 registers per lane), so one
-//    workgroup's tile loads and softmax overlap the other's matrix products;
+//    workgroup's barrier waits are covered by the other's work;
 //  * exp via exp2 with log2(e) and the score scale folded into one FMA; the
 //    running maximum is only moved (and the output rescaled) when a score
 //    exceeds it by more than 2^8.
@@ -34,24 +38,37 @@ namespace bsm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kHalf = 64;  // keys per pipeline step
+
+// How partial tiles are masked (chosen once per workgroup):
+//   kPlain  -- visible keys of a query form one interval [lo, hi]
+//              (causal, window and, with contiguous documents, the document);
+//   kSinks  -- plus the sink interval [slo, shi];
+//   kGather -- document ids are not contiguous runs: interval terms without
+//              the document, then a per-key document id compare.
+enum MaskMode { kPlain = 0, kSinks = 1, kGather = 2 };
 
 struct RowMask {
-    int32_t klo, khi;   // visible window/causal interval of keys
-    int32_t sink_end;   // keys < sink_end are visible through the sink term
-    int32_t docq;       // document id of the query (0 without the document term)
+    int32_t lo, hi;     // main visible interval of keys (inclusive)
+    int32_t slo, shi;   // sink interval (empty when slo > shi)
+    int32_t docq;       // document id of the query (kGather only)
 };
 
 // Per-query state of the online softmax.  m is the reference maximum (log2
 // domain) the accumulators are scaled to; it is only moved when a new score
-// exceeds it by more than 2^8, so most tiles skip the rescale.  The result
+// exceeds it by more than 2^8, so most steps skip the rescale.  The result
 // stays exact because o and l always share the same reference.
 constexpr float kRescaleThreshold = 8.0f;
 
-// Per-lane LDS byte offsets of the matrix-core operands inside a tile.
+// Per-lane LDS byte offsets of the matrix-core operands inside a half tile.
+// Both patterns are XOR-structured, so one base per role is kept and the
+// offset of each operand is derived where it is used:
+//   K operand of d step st:           k ^ (st << 5)
+//   V operand of d block db, half u:  v + u * 8 rows ^ (db << 6)
 template <int D>
 struct OperandOffsets {
-    int k[D / 16];        // A operand of S^T = K Q^T, per 16-wide d step (row = lane's key in block 0)
-    int v[2][D / 32];     // transposing reads of V, per half (keys +0..3 / +8..11) and d block
+    int k;   // row n of key block 0, chunk hl ^ fk(n)
+    int v;   // transposing-read address of d block 0, keys +0..3
 };
 
 template <int D>
@@ -59,98 +76,138 @@ __device__ inline void operand_offsets(OperandOffsets<D> &off) {
     using L = TileLayout<D>;
     const int lane = threadIdx.x & 63;
     const int n = lane & 31, hl = lane >> 5;
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) off.k[st] = n * L::kRowBytes + (((2 * st + hl) ^ L::fk(n)) << 4);
+    // chunk (2 st + hl) ^ fk(n) = (2 st) ^ (hl ^ fk(n)) since 2 st and hl
+    // occupy different bits; the row part n * kRowBytes is a multiple of 256.
+    off.k = n * L::kRowBytes + ((hl ^ L::fk(n)) << 4);
     // ds_read_tr16_b64: lane j of a 16-lane group G supplies the address of
     // row K0 + j/4, columns d0 + 4 (j%4) .. +3; lane i then receives rows
     // K0..K0+3 of column d0 + i.  d0 = 32 db + 16 (G%2); K0 = 4 (G/2) (+8 for
-    // the second half) inside each 16-key group.
+    // the second half) inside each 16-key group.  fv depends on the row's low
+    // bits only, which the +8 of the second half does not change for either
+    // head dimension, and the d block adds 4 db to the chunk, i.e. XOR
+    // (4 db) ^ ... = (db << 6) in bytes as 4 db stays clear of the other terms'
+    // bits for D = 128 (chunk bits 2-3) and D = 64 (chunk bit 2).
     const int G = lane >> 4, j = lane & 15;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int r = 8 * u + 4 * (G >> 1) + (j >> 2);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const int c = db * 4 + 2 * (G & 1) + ((j & 3) >> 1);
-            off.v[u][db] = r * L::kRowBytes + ((c ^ L::fv(r)) << 4) + ((j & 1) << 3);
-        }
-    }
+    const int r = 4 * (G >> 1) + (j >> 2);
+    const int c = 2 * (G & 1) + ((j & 3) >> 1);
+    off.v = r * L::kRowBytes + ((c ^ L::fv(r)) << 4) + ((j & 1) << 3);
 }
 
-// S^T = K Q^T for one tile: lane (query n, half hl) gets, for key block kb,
-// the 16 scores of keys 32 kb + 8 (r/4) + 4 hl + r%4, r = 0..15.
+template <int D>
+__device__ inline int k_operand_offset(const OperandOffsets<D> &off, int st) {
+    return off.k ^ (st << 5);
+}
+
+template <int D>
+__device__ inline int v_operand_offset(const OperandOffsets<D> &off, int u, int db) {
+    return (off.v ^ (db << 6)) + u * 8 * TileLayout<D>::kRowBytes;
+}
+
+// S^T = K Q^T for one half tile: lane (query n, half hl) gets, for key block
+// kb (32 keys), the 16 scores of keys 32 kb + 8 (r/4) + 4 hl + r%4.
 template <int D>
 __device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, const bf16x8 (&qf)[D / 16],
-                              f32x16 (&s)[4]) {
+                              f32x16 (&s)[2]) {
     const char *kbytes = reinterpret_cast<const char *>(sk);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbytes + kb * 32 * TileLayout<D>::kRowBytes + off.k[st]);
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbytes + kb * 32 * TileLayout<D>::kRowBytes +
+                                                                k_operand_offset(off, st));
             s[kb] = mfma32(a, qf[st], s[kb]);
         }
     }
-    sched_interleave<4 * (D / 16), 4>();
 }
 
-// Score modifications (to the log2 domain) and, on partial tiles, the mask.
-template <bool ALIBI, bool SOFTCAP, bool MASKED>
-__device__ inline void fwd_mod_mask(const int32_t *sdoc, f32x16 (&s)[4], int j, int qpos, float scale, float slope,
-                                    float cap, float inv_cap, const RowMask &rm) {
+// Score modifications (to the log2 domain) and the mask for one half tile
+// whose first key is key0.  Applied to every step: on a full tile every pair
+// is visible, so the mask changes nothing there.
+__device__ inline bool in_range(int c, int lo_t, int span) {
+    return (uint32_t)(c - lo_t) <= (uint32_t)span;  // lo_t <= c <= lo_t + span, span >= 0
+}
+
+template <bool ALIBI, bool SOFTCAP, int MODE>
+__device__ inline void fwd_mod_mask(const int32_t *sdoc, f32x16 (&s)[2], int key0, int qpos, float scale,
+                                    float slope, float cap, float inv_cap, const RowMask &rm, bool partial) {
     constexpr bool kMods = ALIBI || SOFTCAP;
     const int hl = (threadIdx.x & 63) >> 5;
-    const int kbase = j * kTile + hl * 4;
-    // Mask bounds relative to this tile.  Kept opaque so that the compiler
-    // compares them with the per-register key offsets inside the loop instead
-    // of hoisting 3 x 64 loop-invariant thresholds into registers.
-    int lo_t = rm.klo - kbase, hi_t = rm.khi - kbase, se_t = rm.sink_end - kbase;
-    if (MASKED) asm volatile("" : "+v"(lo_t), "+v"(hi_t), "+v"(se_t));
-    int rel = qpos - kbase;
-    if (ALIBI) asm volatile("" : "+v"(rel));
+    const int kbase = key0 + hl * 4;
+    if (kMods) {
+        int rel = qpos - kbase;
+        if (ALIBI) asm volatile("" : "+v"(rel));  // keep per-register offsets from being hoisted
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - kbase
+                float y = s[kb][r] * scale;
+                if (ALIBI) y -= slope * (float)(rel - c);
+                if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
+                s[kb][r] = y * kLog2e;
+            }
+    }
+    if (!partial) return;  // full tile: every pair is visible
+    // Bounds relative to this step, kept opaque so that the compiler compares
+    // them with the per-register key offsets instead of hoisting 64
+    // loop-invariant thresholds into registers.  An empty interval is encoded
+    // as a start beyond every key with span 0, which no offset matches.
+    int lo_t = rm.hi >= rm.lo ? rm.lo - kbase : 1 << 30;
+    const int span = rm.hi >= rm.lo ? rm.hi - rm.lo : 0;
+    int slo_t = rm.shi >= rm.slo ? rm.slo - kbase : 1 << 30;
+    const int sspan = rm.shi >= rm.slo ? rm.shi - rm.slo : 0;
+    asm volatile("" : "+v"(lo_t), "+v"(slo_t));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        // The wave's 32 queries x these 32 keys: skip the elementwise test
+        // when every query sees every key, fill with -inf when none sees any.
+        const int kf = key0 + kb * 32, kl = kf + 31;
+        const bool all_vis = MODE != kGather && rm.lo <= kf && rm.hi >= kl;
+        const bool none_vis = (rm.hi < kf || rm.lo > kl || rm.hi < rm.lo) &&
+                              (MODE == kPlain || rm.shi < kf || rm.slo > kl || rm.shi < rm.slo);
+        if (__all(all_vis)) continue;
+        if (__all(none_vis)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
+            continue;
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             int4 dk = {0, 0, 0, 0};
-            if (MASKED) dk = *reinterpret_cast<const int4 *>(&sdoc[kb * 32 + g * 8 + hl * 4]);
+            if (MODE == kGather) dk = *reinterpret_cast<const int4 *>(&sdoc[kb * 32 + g * 8 + hl * 4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = g * 4 + e;
                 const int c = kb * 32 + g * 8 + e;  // key - kbase
-                float t = s[kb][r];
-                if (kMods) {
-                    float y = t * scale;
-                    if (ALIBI) y -= slope * (float)(rel - c);
-                    if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
-                    t = y * kLog2e;
-                }
-                if (MASKED) {
-                    // Without the document term the staged ids and docq are all 0.
+                bool vis = in_range(c, lo_t, span);
+                if (MODE != kPlain) vis = vis || in_range(c, slo_t, sspan);
+                if (MODE == kGather) {
                     const int dkv = e == 0 ? dk.x : e == 1 ? dk.y : e == 2 ? dk.z : dk.w;
-                    const bool vis = (c >= lo_t || c < se_t) && c <= hi_t && dkv == rm.docq;
-                    t = vis ? t : -INFINITY;
+                    vis = vis && dkv == rm.docq;
                 }
-                s[kb][r] = t;
+                s[kb][r] = vis ? s[kb][r] : -INFINITY;
             }
         }
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP>
-__device__ inline void fwd_softmax(f32x16 (&s)[4], f32x16 (&o)[D / 32], float &m, float &l, float scale_log2) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
+// Running-maximum update for one half tile (and the rescale of o and l when
+// the maximum moved by more than the threshold).  Returns the reference the
+// exponentials use.
+template <int D, bool KMODS>
+__device__ inline float fwd_max_update(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float &m, float &l,
+                                       float scale_log2) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (!kMods) mx *= scale_log2;
+    if (!KMODS) mx *= scale_log2;
     if (__any(mx > m + kRescaleThreshold)) {
         const float m_new = fmaxf(m, mx);
         const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
@@ -161,49 +218,133 @@ __device__ inline void fwd_softmax(f32x16 (&s)[4], f32x16 (&o)[D / 32], float &m
             for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
         m = m_new;
     }
-    const float m_use = (m == -INFINITY) ? 0.0f : m;
-    const float c_mul = kMods ? 1.0f : scale_log2;
+    return (m == -INFINITY) ? 0.0f : m;
+}
+
+// p = 2^(s c - m) as bf16 (the B operand of the PV products), summed into l
+// in fp32 before rounding (so lse keeps fp32 accuracy).
+__device__ inline void fwd_exp(const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float &l, float c_mul, float m_use) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float pv = fast_exp2(__builtin_fmaf(s[kb][r], c_mul, -m_use));
-            l += pv;
-            s[kb][r] = pv;
-        }
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = fast_exp2(__builtin_fmaf(s[kb][s2 * 8 + e], c_mul, -m_use));
+                l += pv;
+                pb[kb][s2][e] = static_cast<__bf16>(pv);
+            }
 }
 
 template <int D>
-__device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, const f32x16 (&s)[4],
+__device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, const bf16x8 (&pb)[2][2],
                               f32x16 (&o)[D / 32]) {
     const char *vbytes = reinterpret_cast<const char *>(sv);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 pb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[kb][s2 * 8 + e]);
             const int rowbase = (kb * 32 + s2 * 16) * TileLayout<D>::kRowBytes;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const i16x4 lo = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + off.v[0][db]));
-                const i16x4 hi = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + off.v[1][db]));
+                const i16x4 lo = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + v_operand_offset(off, 0, db)));
+                const i16x4 hi = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + v_operand_offset(off, 1, db)));
                 const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[db] = mfma32(a, pb, o[db]);
+                o[db] = mfma32(a, pb[kb][s2], o[db]);
             }
         }
     }
 }
 
+struct FwdArgs {
+    const __bf16 *kb, *vb;
+    int64_t k_st, v_st;
+    const int32_t *doc, *fidx, *pidx;
+    int nfull, nt, qpos;
+    float scale, scale_log2, slope, cap, inv_cap;
+};
+
+// The double-buffered, software-pipelined loop over the listed tiles (in
+// 64-key steps).  Step t's scores are computed during step t-1.  At the top
+// of step t the copies issued at the top of step t-1 -- K(t+1) and V(t) --
+// have landed; the barrier also certifies that every wave has finished step
+// t-1, freeing K buffer t%2 (last read for K(t)) and V buffer (t+1)%2 (last
+// read for V(t-1)) for K(t+2) and V(t+1).
+template <int D, bool ALIBI, bool SOFTCAP, int MODE>
+__device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x8 (&qf)[D / 16],
+                                const OperandOffsets<D> &off, __bf16 (&skb)[2][kHalf * D],
+                                __bf16 (&svb)[2][kHalf * D], int32_t (&sdb)[2][kHalf], int nsteps,
+                                f32x16 (&o)[D / 32], float &m, float &l) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const float c_mul = kMods ? 1.0f : a.scale_log2;
+    auto step_key0 = [&](int t) {
+        const int it = t >> 1;
+        const int jj = clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull),
+                                  a.nt);
+        return jj * kTile + (t & 1) * kHalf;
+    };
+    auto issue_k = [&](int t, int key0) {
+        if (MODE == kGather) issue_ints_to_lds<kHalf>(sdb[t & 1], a.doc + key0);
+        issue_tile_to_lds<D, false, kHalf>(skb[t & 1], a.kb + (int64_t)key0 * a.k_st, a.k_st);
+    };
+    auto issue_v = [&](int t, int key0) {
+        issue_tile_to_lds<D, true, kHalf>(svb[t & 1], a.vb + (int64_t)key0 * a.v_st, a.v_st);
+    };
+    if (nsteps <= 0) return;
+
+    f32x16 sc[2];
+    {
+        const int k0 = step_key0(0);
+        issue_k(0, k0);
+        issue_v(0, k0);
+        if (nsteps > 1) issue_k(1, step_key0(1));
+        wait_vmcnt<0>();
+        tile_barrier();
+        fwd_qk<D>(skb[0], off, qf, sc);
+        fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[0], sc, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
+                                           0 >= a.nfull);
+    }
+    for (int t = 0; t + 1 < nsteps; ++t) {
+        wait_vmcnt<0>();
+        tile_barrier();
+        OperandOffsets<D> offt = off;  // opaque per step: derived offsets are not hoisted
+        asm volatile("" : "+v"(offt.k), "+v"(offt.v));
+        const int key_next = step_key0(t + 1);
+        if (t + 2 < nsteps) issue_k(t + 2, step_key0(t + 2));
+        issue_v(t + 1, key_next);
+
+        const float m_use = fwd_max_update<D, kMods>(sc, o, m, l, a.scale_log2);
+        bf16x8 pb[2][2];
+        f32x16 sn[2];
+        // next step's QK^T products, interleaved with this step's exponentials
+        fwd_qk<D>(skb[(t + 1) & 1], offt, qf, sn);
+        fwd_exp(sc, pb, l, c_mul, m_use);
+        // this step's PV products, interleaved with the next step's mask
+        fwd_pv<D>(svb[t & 1], offt, pb, o);
+        fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[(t + 1) & 1], sn, key_next, a.qpos, a.scale, a.slope, a.cap,
+                                           a.inv_cap, rm, ((t + 1) >> 1) >= a.nfull);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
+        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
+    }
+    {
+        wait_vmcnt<0>();
+        tile_barrier();
+        const int t = nsteps - 1;
+        const float m_use = fwd_max_update<D, kMods>(sc, o, m, l, a.scale_log2);
+        bf16x8 pb[2][2];
+        fwd_exp(sc, pb, l, c_mul, m_use);
+        fwd_pv<D>(svb[t & 1], off, pb, o);
+    }
+}
+
 template <int D, bool ALIBI, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
-    // Separate LDS objects so the compiler can tell the copies into one from
-    // reads of another (its wait-count insertion tracks them per object).
-    __shared__ __attribute__((aligned(1024))) __bf16 sk[kTile * D];   // keys, rows swizzled by fk
-    __shared__ __attribute__((aligned(1024))) __bf16 sv[kTile * D];   // values, rows swizzled by fv
-    __shared__ __attribute__((aligned(16))) int32_t sdoc[kTile];      // document ids of the keys
-    constexpr int kInstr = tile_lds_instr<D>();
+    // Double-buffered half tiles.  Separate LDS objects per role so that no
+    // compiler-inserted wait ties reads of one to copies into another.
+    __shared__ __attribute__((aligned(1024))) __bf16 skb[2][kHalf * D];  // keys, rows swizzled by fk
+    __shared__ __attribute__((aligned(1024))) __bf16 svb[2][kHalf * D];  // values, rows swizzled by fv
+    __shared__ __attribute__((aligned(16))) int32_t sdb[2][kHalf];       // document ids of the keys
 
     const int nt = p.nt;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -218,53 +359,62 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
     const int qpos = i * kTile + wv * 32 + n;
 
     const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
-    const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
-    const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
-
     const int bm = p.mask_b == 1 ? 0 : b;
     const int64_t row = (int64_t)bm * nt + i;
+
+    FwdArgs a;
+    a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
+    a.vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
+    a.k_st = p.k_st;
+    a.v_st = p.v_st;
     // Counts and indices are clamped to the grid so that a corrupt block mask
     // gives wrong numbers instead of out-of-bounds reads.
-    const int nfull = min(max(load_uniform(p.full_kv_num + row), 0), nt);
+    a.nfull = min(max(load_uniform(p.full_kv_num + row), 0), nt);
     const int npart = min(max(load_uniform(p.kv_num + row), 0), nt);
-    const int32_t *fidx = p.full_kv_idx + row * nt;
-    const int32_t *pidx = p.kv_idx + row * nt;
-    const int total = nfull + npart;
+    a.fidx = p.full_kv_idx + row * nt;
+    a.pidx = p.kv_idx + row * nt;
+    a.nt = nt;
+    a.qpos = qpos;
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * kLog2e;
+    a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
+    a.cap = SOFTCAP ? p.softcap : 1.0f;
+    a.inv_cap = 1.0f / a.cap;
+    const int nsteps = 2 * (a.nfull + npart);  // 64-key steps
 
+    // Visible keys of this query: [lo, hi] and, with sinks, [slo, shi].
     const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
-    const int32_t *doc = doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
+    a.doc = doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
+    int ds = 0, de = p.T - 1;
     RowMask rm;
-    rm.docq = doc_on ? doc[qpos] : 0;
-    rm.khi = (p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1;
-    rm.klo = -1;
-    rm.sink_end = 0;
-    if (p.mask_flags & BSM_MASK_WINDOW) {
-        int64_t lo = (int64_t)qpos - (int64_t)(*p.window) + 1;
-        lo = lo < -1 ? -1 : (lo > p.T ? p.T : lo);
-        rm.klo = (int32_t)lo;
-        if ((p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0) rm.sink_end = p.sinks;
+    rm.docq = 0;
+    bool gather = false;
+    if (doc_on) {
+        const int32_t *dr = p.doc_range + ((int64_t)bm * p.T + qpos) * 2;
+        ds = dr[0];
+        de = dr[1];
+        gather = ds < 0;  // the whole row is marked, so every lane agrees
+        if (gather) {
+            ds = 0;
+            de = p.T - 1;
+            rm.docq = a.doc[qpos];
+        }
     }
-    if (!doc_on && tid < kTile) sdoc[tid] = 0;  // compared against docq = 0
-    wait_lds_reads();                            // the fill is complete before the first barrier
-
-    const float scale = p.scale;
-    const float scale_log2 = p.scale * kLog2e;
-    const float slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
-    const float cap = SOFTCAP ? p.softcap : 1.0f;
-    const float inv_cap = 1.0f / cap;
+    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1, de);
+    int lo = ds;
+    bool sinks = false;
+    if (p.mask_flags & BSM_MASK_WINDOW) {
+        const int64_t wlo = (int64_t)qpos - (int64_t)(*p.window) + 1;
+        if (wlo > lo) lo = wlo > p.T ? p.T : (int)wlo;
+        sinks = (p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0;
+    }
+    rm.lo = lo;
+    rm.hi = hi;
+    rm.slo = ds;
+    rm.shi = sinks ? min(p.sinks - 1, hi) : ds - 1;
 
     OperandOffsets<D> off;
     operand_offsets<D>(off);
-
-    auto tile_at = [&](int it) {
-        return clamp_tile(it < nfull ? load_uniform(fidx + it) : load_uniform(pidx + it - nfull), nt);
-    };
-    // Copies in flight per wave, in issue order: [doc(it), K(it)] then V(it).
-    auto issue_k = [&](int jj) {
-        if (doc_on) issue_ints_to_lds(sdoc, doc + jj * kTile);
-        issue_tile_to_lds<D, false>(sk, kb_ + (int64_t)jj * kTile * p.k_st, p.k_st);
-    };
-    auto issue_v = [&](int jj) { issue_tile_to_lds<D, true>(sv, vb + (int64_t)jj * kTile * p.v_st, p.v_st); };
 
     bf16x8 qf[D / 16];
 #pragma unroll
@@ -277,43 +427,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m = -INFINITY, l = 0.0f;
-    wait_vmcnt<0>();  // Q and the query's document id are in registers before any tile copy
+    wait_vmcnt<0>();  // Q, the document range and id are in registers before any tile copy
 
-    int j = total > 0 ? tile_at(0) : 0;
-    if (total > 0) {
-        issue_k(j);
-        issue_v(j);
-    }
-    for (int it = 0; it < total; ++it) {
-        const bool more = it + 1 < total;
-        const int jn = more ? tile_at(it + 1) : 0;
-        // Copies in flight per wave, oldest first: [doc(it)] K(it), V(it).
-        wait_vmcnt<kInstr>();  // doc(it), K(it) landed
-        tile_barrier();        // ... in every wave
-        f32x16 s[4];
-        fwd_qk<D>(sk, off, qf, s);
-        if (it < nfull) {
-            if (ALIBI || SOFTCAP) fwd_mod_mask<ALIBI, SOFTCAP, false>(sdoc, s, j, qpos, scale, slope, cap, inv_cap, rm);
-        } else {
-            fwd_mod_mask<ALIBI, SOFTCAP, true>(sdoc, s, j, qpos, scale, slope, cap, inv_cap, rm);
-        }
-        wait_lds_reads();
-        tile_barrier();        // every wave is done reading K(it) and doc(it)
-        if (more) issue_k(jn);
-        fwd_softmax<D, ALIBI, SOFTCAP>(s, o, m, l, scale_log2);
-        // In flight now: V(it), then [doc(it+1)] K(it+1).
-        if (more) {
-            if (doc_on) wait_vmcnt<kInstr + 1>(); else wait_vmcnt<kInstr>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        tile_barrier();        // V(it) landed in every wave
-        fwd_pv<D>(sv, off, s, o);
-        wait_lds_reads();
-        tile_barrier();        // every wave is done reading V(it)
-        if (more) issue_v(jn);
-        j = jn;
-    }
+    if (gather)
+        fwd_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
+    else if (sinks)
+        fwd_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
+    else
+        fwd_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
 
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;

@@ -53,8 +53,10 @@ bsm_status check_spec(const bsm_mask_spec *spec) {
     return BSM_OK;
 }
 
-bsm_status check_block_mask(const bsm_block_mask *bm, bool need_transposed) {
+bsm_status check_block_mask(const bsm_block_mask *bm, bool need_transposed, const bsm_mask_spec *spec) {
     if (!bm) return fail(BSM_E_INVALID, "block mask is NULL");
+    if ((spec->flags & BSM_MASK_DOCUMENT) && !bm->doc_range)
+        return fail(BSM_E_INVALID, "DOCUMENT mask needs the block mask's doc_range array");
     if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
         return fail(BSM_E_INVALID, "block mask row arrays must be non-NULL");
     if (need_transposed &&
@@ -130,6 +132,7 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
     p.q_idx = bm->q_indices;
     p.full_q_num = bm->full_q_num_blocks;
     p.full_q_idx = bm->full_q_indices;
+    p.doc_range = (spec->flags & BSM_MASK_DOCUMENT) ? bm->doc_range : nullptr;
 }
 
 bsm_status hip_status(hipError_t e, const char *what) {
@@ -152,7 +155,7 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
                                 void *workspace, size_t workspace_bytes, void *stream) {
     bsm_status st = check_spec(spec);
     if (st != BSM_OK) return st;
-    st = check_block_mask(out, true);
+    st = check_block_mask(out, true, spec);
     if (st != BSM_OK) return st;
     const size_t need = bsm_block_mask_workspace_bytes(spec->seq_len, spec->mask_b);
     if (!workspace || workspace_bytes < need)
@@ -183,7 +186,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                                   const bsm_tensor *out, float *lse, void *stream) {
     bsm_status st = check_attn_common(B, H, T, D, spec, mod);
     if (st != BSM_OK) return st;
-    if ((st = check_block_mask(bm, false)) != BSM_OK) return st;
+    if ((st = check_block_mask(bm, false, spec)) != BSM_OK) return st;
     if ((st = check_tensor(q, "q")) != BSM_OK) return st;
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;
     if ((st = check_tensor(v, "v")) != BSM_OK) return st;
@@ -216,7 +219,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                                   void *workspace, size_t workspace_bytes, void *stream) {
     bsm_status st = check_attn_common(B, H, T, D, spec, mod);
     if (st != BSM_OK) return st;
-    if ((st = check_block_mask(bm, true)) != BSM_OK) return st;
+    if ((st = check_block_mask(bm, true, spec)) != BSM_OK) return st;
     if ((st = check_tensor(q, "q")) != BSM_OK) return st;
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;
     if ((st = check_tensor(v, "v")) != BSM_OK) return st;

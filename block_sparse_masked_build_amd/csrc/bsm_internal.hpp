@@ -43,6 +43,7 @@ struct AttnParams {
     // block mask
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
     const int32_t *q_num, *q_idx, *full_q_num, *full_q_idx;
+    const int32_t *doc_range;   // [mask_b, T, 2] (first, last) of each position's document, or NULL
     // tensors (bf16, strides in elements)
     const void *q; int64_t q_sb, q_sh, q_st;
     const void *k; int64_t k_sb, k_sh, k_st;

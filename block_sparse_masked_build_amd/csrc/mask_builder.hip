@@ -17,6 +17,10 @@
 //    then a sum of 128 interval overlaps -- exact, O(128) per tile.
 //  * Any other document ids take a general path that compares document ids
 //    key by key inside the causal/window intervals (still exact).
+//  * The document range [start, end] of every position is exported
+//    (doc_range) so the attention kernels can mask partial tiles with two
+//    interval compares per score; (-1, -1) marks rows without contiguous
+//    documents.
 //  * One workgroup per query-tile row; one lane per key tile; wave ballots and
 //    a cross-wave prefix sum compact the partial and full lists in ascending
 //    order.  A per-tile class byte is kept in the workspace and a second
@@ -154,6 +158,11 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
         if (sinks_on) {
             blo = ds;
             bhi = (int64_t)p.sinks - 1 < hi ? (int64_t)p.sinks - 1 : hi;
+        }
+        if (document) {
+            int32_t *dr = p.out.doc_range + ((int64_t)b * T + q) * 2;
+            dr[0] = mono ? (int32_t)ds : -1;
+            dr[1] = mono ? (int32_t)de : -1;
         }
         s_alo[r] = lo; s_ahi[r] = hi;
         s_blo[r] = blo; s_bhi[r] = bhi;

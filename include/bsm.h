@@ -97,8 +97,19 @@ typedef struct {
  *   q_indices           [mask_b, 1, KT, QT]   the query tiles), used by the
  *   full_q_num_blocks   [mask_b, 1, KT]       backward pass
  *   full_q_indices      [mask_b, 1, KT, QT]
- * bsm_build_block_mask writes all eight; the forward reads the kv_* four and
- * the backward reads all eight. */
+ *   doc_range           [mask_b, T, 2]       DOCUMENT only (else may be NULL):
+ *                                            first and last position of the
+ *                                            document holding t when the row's
+ *                                            ids are non-decreasing (documents
+ *                                            are contiguous runs, as for the
+ *                                            running count of end-of-text flags,
+ *                                            speedrun notes code listing);
+ *                                            (-1, -1) for every t of a row whose
+ *                                            ids are not, which makes the
+ *                                            attention kernels compare ids key
+ *                                            by key instead
+ * bsm_build_block_mask writes all nine; the forward reads the kv_* four and
+ * doc_range, the backward reads all nine. */
 typedef struct {
     int32_t *kv_num_blocks;
     int32_t *kv_indices;
@@ -108,6 +119,7 @@ typedef struct {
     int32_t *q_indices;
     int32_t *full_q_num_blocks;
     int32_t *full_q_indices;
+    int32_t *doc_range;
 } bsm_block_mask;
 
 typedef struct {

@@ -16,6 +16,7 @@ from .predicate import visible  # noqa: F401
 from .block_mask import (  # noqa: F401
     tile_counts,
     tile_counts_dense_numpy,
+    document_ranges,
     classify,
     block_mask_lists,
     EMPTY, PARTIAL, FULL, TILE,

@@ -106,6 +106,24 @@ def tile_counts_dense_numpy(spec) -> np.ndarray:
     return np.stack(res)
 
 
+def document_ranges(spec) -> np.ndarray:
+    """int32 [mask_b, T, 2]: first and last position of the document holding
+    each position, for rows whose document ids are non-decreasing (documents
+    are then contiguous runs, as for ids made by counting end-of-text flags --
+    speedrun notes "FlexAttention", code listing); (-1, -1) for every
+    position of any other row."""
+    T = spec.T
+    out = np.full((spec.mask_b, T, 2), -1, dtype=np.int32)
+    for b in range(spec.mask_b):
+        d = np.asarray(spec.doc_ids[b], dtype=np.int64)
+        if np.any(d[1:] < d[:-1]):
+            continue
+        for t in range(T):
+            same = np.nonzero(d == d[t])[0]
+            out[b, t] = (same[0], same[-1])
+    return out
+
+
 def classify(counts: np.ndarray) -> np.ndarray:
     """uint8 class per tile: 0 empty, 1 partial, 2 full."""
     cls = np.full(counts.shape, PARTIAL, dtype=np.uint8)

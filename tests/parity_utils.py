@@ -30,7 +30,10 @@ def log(msg):
 
 
 def oracle_block_mask(spec_data):
-    return oracle.block_mask_lists(oracle.tile_counts(spec_data))
+    ref = oracle.block_mask_lists(oracle.tile_counts(spec_data))
+    if spec_data.document:
+        ref["doc_range"] = oracle.document_ranges(spec_data)
+    return ref
 
 
 def gpu_block_mask(spec_data):
@@ -38,11 +41,12 @@ def gpu_block_mask(spec_data):
     spec = api.from_spec_data(spec_data)
     bm = api.build_block_mask(spec)
     torch.cuda.synchronize()
-    return spec, bm, {n: getattr(bm, n).cpu().numpy() for n in BM_NAMES}
+    names = BM_NAMES + (("doc_range",) if spec_data.document else ())
+    return spec, bm, {n: getattr(bm, n).cpu().numpy() for n in names}
 
 
 def assert_block_masks_equal(gpu, ref, ctx=""):
-    for n in BM_NAMES:
+    for n in ref:
         a, b = gpu[n], ref[n]
         assert a.shape == b.shape, (ctx, n, a.shape, b.shape)
         if not np.array_equal(a, b):

@@ -40,7 +40,7 @@ def _spec(**kw):
 
 
 def _bm(null=None):
-    v = [FAKE] * 8
+    v = [FAKE] * 9
     if null is not None:
         v[null] = None
     return BsmBlockMask(*v)
@@ -69,6 +69,9 @@ def test_build_rejects_bad_spec(kw, code):
 def test_build_rejects_null_outputs_and_small_workspace():
     for i in range(8):
         assert _build(_spec(), _bm(null=i)) == _lib.BSM_E_INVALID
+    # doc_range is required only with the document term
+    assert _build(_spec(flags=3, doc_ids=FAKE), _bm(null=8)) == _lib.BSM_E_INVALID
+    assert b"doc_range" in lib.bsm_last_error()
     need = lib.bsm_block_mask_workspace_bytes(1024, 1)
     assert need >= 64  # 8x8 class bytes + flags
     assert _build(_spec(), ws=FAKE, nbytes=need - 1) == _lib.BSM_E_WORKSPACE

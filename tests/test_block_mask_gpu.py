@@ -71,8 +71,13 @@ def test_config3_window_sweep_all_28():
         torch.cuda.synchronize()
         g = {n: getattr(bm, n).cpu().numpy() for n in bm._fields}
         s = MaskSpecData(w.T, causal=True, document=True, doc_ids=w.spec.doc_ids, window=win)
+        if win != w.windows[0]:
+            g.pop("doc_range")  # compared once; it does not depend on the window
         log(f"[block-mask] config 3 window {win}")
-        assert_block_masks_equal(g, oracle_block_mask(s), f"window {win}")
+        ref = oracle_block_mask(s)
+        if "doc_range" not in g:
+            ref.pop("doc_range")
+        assert_block_masks_equal(g, ref, f"window {win}")
 
 
 def test_config4_and_5():

@@ -192,3 +192,18 @@ def test_config_masks_bounded_by_nodoc():
         c_nodoc = oracle.tile_counts(nodoc)
         assert np.all(c_doc <= c_nodoc)
         assert int((c_doc > 0).sum()) < int((c_nodoc > 0).sum())
+
+
+def test_document_ranges_closed_form_and_sentinel():
+    """Fixed 1000-token chunks: position t lies in [1000 floor(t/1000),
+    min(1000 floor(t/1000) + 999, T - 1)]; ids that go down mark every
+    position of the row with (-1, -1)."""
+    T = 2560
+    docs = doc_ids_chunks(T, 1000)
+    spec = MaskSpecData(T, causal=True, document=True, doc_ids=np.stack([docs, docs[::-1].copy()]))
+    r = oracle.document_ranges(spec)
+    t = np.arange(T)
+    start = 1000 * (t // 1000)
+    assert np.array_equal(r[0, :, 0], start)
+    assert np.array_equal(r[0, :, 1], np.minimum(start + 999, T - 1))
+    assert np.all(r[1] == -1)
