@@ -132,6 +132,23 @@ __device__ inline void copy16_to_lds(const void *g, uint32_t lds_base) {
                  : "memory", "m0");
 }
 
+// Same with the scalar-base address form: 16 bytes from gbase + voff (gbase
+// wave-uniform in scalar registers, voff a 32-bit per-lane offset), so no
+// per-lane 64-bit address arithmetic is needed.
+__device__ inline uint64_t uniform_u64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ inline void copy16_to_lds_s(const void *gbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff),
+                   "s"(uniform_u64((uint64_t)(uintptr_t)gbase))
+                 : "memory", "m0");
+}
+
 // Same, 4 bytes per lane (lanes land at lds_base + 4 * lane).
 __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
@@ -146,13 +163,17 @@ __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
 // belongs there under the swizzle).  Completion is tracked by vmcnt.
 // Addresses are a wave-uniform base (scalar registers) plus a 32-bit per-lane
 // offset; with the swizzles above only a handful of distinct offsets occur.
+// Index of this thread's wave as a scalar (wave-uniform) value, so that the
+// uniform parts of copy addresses are computed by the scalar unit.
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 template <int D, bool IS_V, int ROWS = kTile>
 __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride) {
     using L = TileLayout<D>;
     constexpr int kRowsPerInstr = 1024 / L::kRowBytes;
     constexpr int kInstr = ROWS / kRowsPerInstr / 4;
     static_assert(kInstr >= 1, "at least one copy per wave");
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = wave_id(), lane = threadIdx.x & 63;
     const int64_t row_bytes = row_stride * 2;
     const char *wbase = reinterpret_cast<const char *>(g_row0) + (int64_t)(wv * kInstr * kRowsPerInstr) * row_bytes;
     const int q = lane / L::kChunks;  // row inside the instruction's block
@@ -164,7 +185,7 @@ __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0,
         const int c = (lane % L::kChunks) ^ (IS_V ? L::fv(r16) : L::fk(r16));
         const uint32_t voff = (uint32_t)(q * row_bytes) + (uint32_t)(c * 16);
         const char *xbase = wbase + (int64_t)(x * kRowsPerInstr) * row_bytes;
-        copy16_to_lds(xbase + voff, lds_addr(lds_tile + ((wv * kInstr + x) * kRowsPerInstr) * D));
+        copy16_to_lds_s(xbase, voff, lds_addr(lds_tile + ((wv * kInstr + x) * kRowsPerInstr) * D));
     }
 }
 
@@ -175,7 +196,7 @@ constexpr int tile_lds_instr() { return kTile / (1024 / TileLayout<D>::kRowBytes
 template <int N = kTile>
 __device__ inline void issue_ints_to_lds(int32_t *lds, const int32_t *g) {
     constexpr int kPer = N / 4;
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wv = wave_id(), lane = threadIdx.x & 63;
     if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds_addr(lds + wv * kPer));
 }
 

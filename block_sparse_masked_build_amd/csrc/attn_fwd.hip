@@ -292,7 +292,7 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
     };
     if (nsteps <= 0) return;
 
-    f32x16 sc[2];
+    f32x16 sa[2], sb[2];
     {
         const int k0 = step_key0(0);
         issue_k(0, k0);
@@ -300,11 +300,14 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
         if (nsteps > 1) issue_k(1, step_key0(1));
         wait_vmcnt<0>();
         tile_barrier();
-        fwd_qk<D>(skb[0], off, qf, sc);
-        fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[0], sc, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
+        fwd_qk<D>(skb[0], off, qf, sa);
+        fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[0], sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
                                            0 >= a.nfull);
     }
-    for (int t = 0; t + 1 < nsteps; ++t) {
+    // One pipelined step: exponentials and PV of step t (scores in sc), QK^T
+    // and mask of step t+1 (into sn).  Unrolled by two below so that sc and
+    // sn swap roles without register copies.
+    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t) {
         wait_vmcnt<0>();
         tile_barrier();
         OperandOffsets<D> offt = off;  // opaque per step: derived offsets are not hoisted
@@ -315,7 +318,6 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
 
         const float m_use = fwd_max_update<D, kMods>(sc, o, m, l, a.scale_log2);
         bf16x8 pb[2][2];
-        f32x16 sn[2];
         // next step's QK^T products, interleaved with this step's exponentials
         fwd_qk<D>(skb[(t + 1) & 1], offt, qf, sn);
         fwd_exp(sc, pb, l, c_mul, m_use);
@@ -323,18 +325,26 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
         fwd_pv<D>(svb[t & 1], offt, pb, o);
         fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[(t + 1) & 1], sn, key_next, a.qpos, a.scale, a.slope, a.cap,
                                            a.inv_cap, rm, ((t + 1) >> 1) >= a.nfull);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sc[kb] = sn[kb];
         wait_lds_reads();  // this wave's reads of step t are done before the next barrier
-    }
-    {
+    };
+    auto last = [&](f32x16 (&sc)[2], int t) {
         wait_vmcnt<0>();
         tile_barrier();
-        const int t = nsteps - 1;
         const float m_use = fwd_max_update<D, kMods>(sc, o, m, l, a.scale_log2);
         bf16x8 pb[2][2];
         fwd_exp(sc, pb, l, c_mul, m_use);
         fwd_pv<D>(svb[t & 1], off, pb, o);
+    };
+    int t = 0;
+    for (; t + 2 < nsteps; t += 2) {
+        step(sa, sb, t);
+        step(sb, sa, t + 1);
+    }
+    if (nsteps - t == 2) {
+        step(sa, sb, t);
+        last(sb, t + 1);
+    } else {
+        last(sa, t);
     }
 }
 
