@@ -4,34 +4,47 @@
 // modifications (tutorial "FlexAttention in PyTorch", Pattern 3: ALiBi and
 // soft-cap are differentiable and get a fused backward), visiting only the
 // tiles the block mask lists (speedrun notes "FlexAttention", tile-summary
-// paragraph).  With p = exp(s - lse) recomputed from the forward's lse:
+// paragraph).  With t the log2-domain score (after the modifications) and
+// L = lse log2(e) from the forward, p = 2^(t - L) is recomputed and
 //   Delta_q = <dO_q, out_q>
-//   dS_qk   = p_qk (<dO_q, v_k> - Delta_q) * (1 - (s_qk / c)^2 if capped)
-//   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO
+//   dS_qk   = p_qk (<dO_q, v_k> - Delta_q) * scale * (1 - tanh^2 if capped)
+//   dQ = dS K,  dK = dS^T Q,  dV = P^T dO
+// (dS is the gradient of the raw product q.k, hence the scale factor).
 //
 // Three kernels, no atomics (results are deterministic):
-//  * delta_kernel: Delta per query row (16 lanes per row, 16-byte loads);
-//  * dkdv_kernel: one workgroup per (batch, head, 128-key tile), iterating
-//    the transposed (per key tile) full and partial query-tile lists; lane l
-//    of wave w owns key 32w + l%32, so P and dS come out of the matrix cores
-//    with queries in registers -- exactly the k-operand layout the dV and dK
-//    products need; Q and dO are staged both row-major and transposed in LDS;
+//  * delta_kernel: Delta and L per query row;
+//  * dkdv_kernel: one workgroup of 4 waves per (batch, head, 128-key tile)
+//    over the transposed (per key tile) full and partial query-tile lists.
+//    Lane l of wave w owns key 32w + l%32 and keeps its K and V rows in
+//    registers as the B operands of S = Q K^T and dP = dO V^T, so P and dS
+//    come out of the matrix cores with the queries in registers -- the B
+//    operand layout of dV^T += dO^T P and dK^T += Q^T dS.  Q and dO are
+//    copied HBM -> LDS once per 64-query step and read row-wise (S, dP) and
+//    transposed with ds_read_tr16_b64 (dV, dK) from the same copy.  The two
+//    accumulators take 128 registers per lane at D = 128, so the kernel runs
+//    one workgroup per CU with up to 512 registers per lane;
 //  * dq_kernel: one workgroup per (batch, head, 128-query tile) over the row
-//    lists, lane l owning query 32w + l%32 as in the forward; K is staged
-//    row-major and transposed, V row-major.
+//    lists, lane = query as in the forward: S^T = K Q^T, dP^T = V dO^T,
+//    dQ^T += K^T dS^T, with K and V copied per 64-key step and K read both
+//    ways; two workgroups per CU.
+// Tile copies are asynchronous (global_load_lds) into double-buffered LDS,
+// issued one step ahead, one barrier per step.  On partial tiles, 32 x 32
+// blocks that hold no visible pair are skipped (no products at all), blocks
+// that are entirely visible skip the elementwise test.
 #include "attn_common.hpp"
 
 namespace bsm {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kHalf = 64;  // rows per pipeline step
 
-// ---------------------------------------------------------------- Delta
+// ---------------------------------------------------------------- Delta, L
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel(AttnParams p) {
-    constexpr int LPR = D / 8;                 // lanes per row
-    constexpr int RPB = kThreads / LPR;        // rows per block
+    constexpr int LPR = D / 8;           // lanes per row
+    constexpr int RPB = kThreads / LPR;  // rows per block
     const int64_t rows = (int64_t)p.B * p.H * p.T;
     const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     const int c = (threadIdx.x % LPR) * 8;
@@ -52,433 +65,446 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (r < rows && threadIdx.x % LPR == 0) p.delta[r] = acc;
-}
-
-// ------------------------------------------------------- shared helpers
-
-// Log2-domain score of one (query, key) pair and, through y, the final
-// natural-domain score (needed for the soft-cap derivative).  Same arithmetic
-// as the forward kernel.
-template <bool ALIBI, bool SOFTCAP>
-__device__ inline float score_log2(float raw, int qpos, int kpos, float scale_log2, float scale,
-                                   float slope, float cap, float inv_cap, float &y) {
-    if (!ALIBI && !SOFTCAP) {
-        y = 0.0f;
-        return raw * scale_log2;
-    }
-    float v = raw * scale;
-    if (ALIBI) v -= slope * (float)(qpos - kpos);
-    if (SOFTCAP) v = cap * tanh_exp2(v * inv_cap);
-    y = v;
-    return v * kLog2e;
-}
-
-// 128 rows x D of a bf16 [T, D] matrix, loaded as (4-row group, 8-column
-// chunk) units so that each unit can be written row-major and transposed.
-template <int D>
-struct RowsUnits {
-    static constexpr int U = 32 * (D / 8) / kThreads;
-    u32x4 v[U][4];
-};
-
-template <int D>
-__device__ inline void load_rows(RowsUnits<D> &ru, const __bf16 *base, int64_t st, int row0) {
-#pragma unroll
-    for (int it = 0; it < RowsUnits<D>::U; ++it) {
-        const int u = it * kThreads + threadIdx.x;
-        const int g = u / (D / 8), cc = (u % (D / 8)) * 8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            ru.v[it][e] = *reinterpret_cast<const u32x4 *>(base + (int64_t)(row0 + 4 * g + e) * st + cc);
+    if (r < rows && threadIdx.x % LPR == 0) {
+        p.delta[r] = acc;
+        const float lse = p.lse[r];  // lse is [B, H, T] contiguous: same flat index
+        p.lse2[r] = lse == -INFINITY ? 0.0f : lse * kLog2e;
     }
 }
 
-template <int D>
-__device__ inline void store_rows(const RowsUnits<D> &ru, __bf16 *rowmajor, int ld_rm, __bf16 *transposed,
-                                  int ld_t) {
-#pragma unroll
-    for (int it = 0; it < RowsUnits<D>::U; ++it) {
-        const int u = it * kThreads + threadIdx.x;
-        const int g = u / (D / 8), cc = (u % (D / 8)) * 8;
-        if (rowmajor != nullptr) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                *reinterpret_cast<u32x4 *>(&rowmajor[(4 * g + e) * ld_rm + cc]) = ru.v[it][e];
-        }
-        if (transposed != nullptr) store_transposed_4x8(transposed, ld_t, 4 * g, cc, ru.v[it]);
-    }
-}
-
-// Writes a D^T-layout accumulator block (lane = row of dst, registers =
-// 16 columns col0 + 8*(r/4) + 4*half + r%4) as bf16.
-__device__ inline void store_acc_rows(__bf16 *dst, const f32x16 &acc, int col0, int hl, float mul) {
+// Writes a transposed accumulator block (lane = row of dst; register r holds
+// column col0 + 8 (r/4) + 4 hl + r%4) as bf16.
+__device__ inline void store_acc_rows(__bf16 *dst, const f32x16 &acc, int col0, int hl) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         u32x2 w;
-        w.x = pack_bf16x2(acc[g * 4 + 0] * mul, acc[g * 4 + 1] * mul);
-        w.y = pack_bf16x2(acc[g * 4 + 2] * mul, acc[g * 4 + 3] * mul);
+        w.x = pack_bf16x2(acc[g * 4 + 0], acc[g * 4 + 1]);
+        w.y = pack_bf16x2(acc[g * 4 + 2], acc[g * 4 + 3]);
         *reinterpret_cast<u32x2 *>(dst + col0 + g * 8 + hl * 4) = w;
     }
 }
 
+// Soft-cap derivative from the log2-domain capped score t = cap tanh(.) log2 e:
+// 1 - tanh^2, with tanh clamped so that masked scores (-inf) give 0.
+__device__ inline float softcap_grad(float t, float inv_cap) {
+    const float th = __builtin_amdgcn_fmed3f(t * (kLn2 * inv_cap), -1.0f, 1.0f);
+    return 1.0f - th * th;
+}
+
+// Start of pipeline step t (64 rows): step t covers half t%2 of listed tile
+// t/2 (full tiles first, then partial ones).
+__device__ inline int step_row0(int t, int nfull, const int32_t *fidx, const int32_t *pidx, int nt) {
+    const int it = t >> 1;
+    const int jj = clamp_tile(it < nfull ? load_uniform(fidx + it) : load_uniform(pidx + it - nfull), nt);
+    return jj * kTile + (t & 1) * kHalf;
+}
+
+// ---------------------------------------------------------------- dQ
+
+struct DqArgs {
+    const __bf16 *kb, *vb;
+    int64_t k_st, v_st;
+    const int32_t *fidx, *pidx, *doc;
+    int nfull, nt, qpos;
+    float scale, scale_log2, slope, cap, inv_cap;
+    float l2, delta;  // this lane's query
+};
+
+template <int D, bool ALIBI, bool SOFTCAP, int MODE>
+__device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 (&qf)[D / 16],
+                               const bf16x8 (&gf)[D / 16], const KvOffsets &off, __bf16 (&skb)[2][kHalf * D],
+                               __bf16 (&svb)[2][kHalf * D], int32_t (&sdb)[2][kHalf], int nsteps,
+                               f32x16 (&dq)[D / 32]) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    auto issue = [&](int t, int key0) {
+        if (MODE == kGather) issue_ints_to_lds<kHalf>(sdb[t & 1], a.doc + key0);
+        issue_tile_to_lds<D, kSwzKV, kHalf>(skb[t & 1], a.kb + (int64_t)key0 * a.k_st, a.k_st);
+        issue_tile_to_lds<D, kSwzKV, kHalf>(svb[t & 1], a.vb + (int64_t)key0 * a.v_st, a.v_st);
+    };
+    if (nsteps <= 0) return;
+    int key0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt);
+    issue(0, key0);
+#pragma unroll 1
+    for (int t = 0; t < nsteps; ++t) {
+        wait_vmcnt<0>();
+        tile_barrier();  // step t's tiles are visible; every wave is done with step t-1's buffers
+        int key_next = 0;
+        if (t + 1 < nsteps) {
+            key_next = step_row0(t + 1, a.nfull, a.fidx, a.pidx, a.nt);
+            issue(t + 1, key_next);
+        }
+        const __bf16 *sk = skb[t & 1], *sv = svb[t & 1];
+        KvOffsets offt = off;  // opaque per step: derived offsets are not hoisted
+        asm volatile("" : "+v"(offt.row), "+v"(offt.tr));
+        const bool partial = (t >> 1) >= a.nfull;
+        bool skip[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            skip[kb] = partial && block_none_visible<MODE>(rm, key0 + kb * 32, key0 + kb * 32 + 31);
+
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s[kb][r] = 0.0f;
+                dp[kb][r] = 0.0f;
+            }
+            if (skip[kb]) continue;
+#pragma unroll
+            for (int st = 0; st < D / 16; ++st) {
+                s[kb] = mfma32(read_rows_operand<D>(sk, offt, kb, st), qf[st], s[kb]);
+                dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, st), gf[st], dp[kb]);
+            }
+        }
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[t & 1], s, key0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
+                                           partial);
+        bf16x8 dsb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float tl = s[kb][r];
+                const float pv = fast_exp2(kMods ? tl - a.l2 : __builtin_fmaf(tl, a.scale_log2, -a.l2));
+                float ds = pv * (dp[kb][r] - a.delta) * a.scale;
+                if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
+                dsb[kb][r >> 3][r & 7] = static_cast<__bf16>(ds);
+            }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if (skip[kb]) continue;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    dq[db] = mfma32(read_cols_operand<D>(sk, offt, kb * 2 + s2, db), dsb[kb][s2], dq[db]);
+        }
+        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
+        key0 = key_next;
+    }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) __bf16 skb[2][kHalf * D];  // keys (fkv swizzle)
+    __shared__ __attribute__((aligned(1024))) __bf16 svb[2][kHalf * D];  // values (fkv swizzle)
+    __shared__ __attribute__((aligned(16))) int32_t sdb[2][kHalf];       // document ids of the keys
+
+    const int nt = p.nt;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = wg / nt;
+    const int i = nt - 1 - (wg % nt);  // later query tiles first (more tiles under a causal mask)
+    const int b = bh / p.H, h = bh % p.H;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int n = lane & 31, hl = lane >> 5;
+    const int qpos = i * kTile + wv * 32 + n;
+
+    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
+    const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    const int bm = p.mask_b == 1 ? 0 : b;
+    const int64_t row = (int64_t)bm * nt + i;
+
+    DqArgs a;
+    a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
+    a.vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
+    a.k_st = p.k_st;
+    a.v_st = p.v_st;
+    a.nfull = min(max(load_uniform(p.full_kv_num + row), 0), nt);
+    const int npart = min(max(load_uniform(p.kv_num + row), 0), nt);
+    a.fidx = p.full_kv_idx + row * nt;
+    a.pidx = p.kv_idx + row * nt;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.T : nullptr;
+    a.nt = nt;
+    a.qpos = qpos;
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * kLog2e;
+    a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
+    a.cap = SOFTCAP ? p.softcap : 1.0f;
+    a.inv_cap = 1.0f / a.cap;
+    const int64_t row_bh = ((int64_t)b * p.H + h) * p.T + qpos;
+    a.l2 = p.lse2[row_bh];
+    a.delta = p.delta[row_bh];
+    const int nsteps = 2 * (a.nfull + npart);
+
+    RowMask rm;
+    const int mode = make_row_mask(p, bm, qpos, rm);
+    KvOffsets off;
+    kv_offsets<D>(off);
+
+    bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
+        gf[st] = *reinterpret_cast<const bf16x8 *>(gb + (int64_t)qpos * p.do_st + st * 16 + hl * 8);
+    }
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
+    wait_vmcnt<0>();  // row operands and per-query values are in registers before any tile copy
+
+    if (mode == kGather)
+        dq_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, gf, off, skb, svb, sdb, nsteps, dq);
+    else if (mode == kSinks)
+        dq_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, gf, off, skb, svb, sdb, nsteps, dq);
+    else
+        dq_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, gf, off, skb, svb, sdb, nsteps, dq);
+
+    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qpos * p.dq_st;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) store_acc_rows(dqp, dq[db], db * 32, hl);
+}
+
 // ---------------------------------------------------------------- dK, dV
+
+// Column view of the mask for one key: the visible queries form [lo, hi]
+// (causal: q >= key; window: q <= key + w - 1 unless the key is a sink; the
+// key's document).  Sinks only lift the window bound, so one interval always
+// suffices.  In gather mode (documents not contiguous runs) the document is
+// left out of the interval and dock holds the key's id for a per-query
+// compare.
+struct ColMask {
+    int32_t lo, hi, dock;
+};
+
+__device__ inline bool make_col_mask(const AttnParams &p, int bm, int kpos, ColMask &cm) {
+    int ds = 0, de = p.T - 1;
+    bool gather = false;
+    cm.dock = 0;
+    if (p.mask_flags & BSM_MASK_DOCUMENT) {
+        const int32_t *dr = p.doc_range + ((int64_t)bm * p.T + kpos) * 2;
+        ds = dr[0];
+        de = dr[1];
+        gather = ds < 0;  // whole row flagged: every lane agrees
+        if (gather) {
+            ds = 0;
+            de = p.T - 1;
+            cm.dock = p.doc_ids[(int64_t)bm * p.T + kpos];
+        }
+    }
+    cm.lo = max((p.mask_flags & BSM_MASK_CAUSAL) ? kpos : 0, ds);
+    int hi = de;
+    if (p.mask_flags & BSM_MASK_WINDOW) {
+        const bool sink = (p.mask_flags & BSM_MASK_SINKS) && kpos < p.sinks;
+        if (!sink) {
+            int64_t whi = (int64_t)kpos + (int64_t)(*p.window) - 1;
+            whi = whi < -1 ? -1 : (whi > p.T - 1 ? p.T - 1 : whi);
+            hi = min(hi, (int)whi);
+        }
+    }
+    cm.hi = hi;
+    return gather;
+}
+
+struct DkdvArgs {
+    const __bf16 *qb, *gb;
+    int64_t q_st, do_st;
+    const float *l2, *delta;  // this (batch, head)
+    const int32_t *fidx, *pidx, *doc;
+    int nfull, nt, kpos;
+    float scale, scale_log2, slope, cap, inv_cap;
+};
 
 template <int D>
 struct DkdvSmem {
-    static constexpr int RS = D + 8;       // row-major stride
-    static constexpr int TS = kTile + 8;   // transposed stride
-    __bf16 q[kTile * RS];
-    __bf16 qt[D * TS];
-    __bf16 dout[kTile * RS];
-    __bf16 doutt[D * TS];
-    float lse2[kTile];
-    float delta[kTile];
-    int32_t doc[kTile];
+    __bf16 q[2][kHalf * D];   // queries (fkv swizzle)
+    __bf16 g[2][kHalf * D];   // output gradients (fkv swizzle)
+    float l2[2][kHalf];
+    float delta[2][kHalf];
+    int32_t doc[2][kHalf];
 };
 
-// One listed query tile for the wave's 32 keys, one 32-query block at a time
-// (keeps 32 score registers live instead of 128).
-template <int D, bool ALIBI, bool SOFTCAP, bool MASKED>
-__device__ inline void dkdv_tile(const DkdvSmem<D> &sm, const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16],
-                                 f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], int i, int kpos, int qlo, int qhi,
-                                 int dockey, bool doc_on, float scale_log2, float scale, float slope,
-                                 float cap, float inv_cap) {
-    const int lane = threadIdx.x & 63;
-    const int n = lane & 31, hl = lane >> 5;
-    const int qbase = i * kTile;
-#pragma unroll 1
-    for (int qb = 0; qb < 4; ++qb) {
-        f32x16 s, dp;
+// One 32-query block (queries q0.. q0+31 of the step, rows 32 qb.. of the LDS
+// tiles) against the wave's 32 keys.
+template <int D, bool ALIBI, bool SOFTCAP, bool GATHER>
+__device__ inline void dkdv_block(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
+                                  const bf16x8 (&vf)[D / 16], const KvOffsets &off, const __bf16 *sq,
+                                  const __bf16 *sg, const float *sl2, const float *sdl, const int32_t *sdoc,
+                                  int qb, int q0, bool partial, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const int hl = (threadIdx.x & 63) >> 5;
+    const int qf = q0 + qb * 32, ql = qf + 31;
+    if (partial && __all(cm.hi < qf || cm.lo > ql || cm.hi < cm.lo)) return;  // nothing visible
+    const bool masked = partial && !__all(!GATHER && cm.lo <= qf && cm.hi >= ql);
+
+    f32x16 s, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[r] = 0.0f;
-            dp[r] = 0.0f;
-        }
+    for (int r = 0; r < 16; ++r) {
+        s[r] = 0.0f;
+        dp[r] = 0.0f;
+    }
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const int off = (qb * 32 + n) * DkdvSmem<D>::RS + st * 16 + hl * 8;
-            s = mfma32(*reinterpret_cast<const bf16x8 *>(&sm.q[off]), kf[st], s);
-            dp = mfma32(*reinterpret_cast<const bf16x8 *>(&sm.dout[off]), vf[st], dp);
-        }
+    for (int st = 0; st < D / 16; ++st) {
+        s = mfma32(read_rows_operand<D>(sq, off, qb, st), kf[st], s);
+        dp = mfma32(read_rows_operand<D>(sg, off, qb, st), vf[st], dp);
+    }
+    // Register r holds query qf + 4 hl + c with c = 8 (r/4) + r%4.
+    const int qbase = qf + 4 * hl;
+    int lo_t = cm.hi >= cm.lo ? cm.lo - qbase : 1 << 30;  // empty interval: no offset matches
+    const int span = cm.hi >= cm.lo ? cm.hi - cm.lo : 0;
+    int rel = qbase - a.kpos;
+    asm volatile("" : "+v"(lo_t), "+v"(rel));
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int ql = qb * 32 + g * 8 + hl * 4;
-            const float4 L = *reinterpret_cast<const float4 *>(&sm.lse2[ql]);
-            const float4 Dl = *reinterpret_cast<const float4 *>(&sm.delta[ql]);
-            int4 dq4 = {0, 0, 0, 0};
-            if (MASKED && doc_on) dq4 = *reinterpret_cast<const int4 *>(&sm.doc[ql]);
+    for (int g = 0; g < 4; ++g) {
+        const int ql4 = qb * 32 + g * 8 + hl * 4;
+        const f32x4 L = *reinterpret_cast<const f32x4 *>(sl2 + ql4);
+        const f32x4 Dl = *reinterpret_cast<const f32x4 *>(sdl + ql4);
+        int4 dq4 = {0, 0, 0, 0};
+        if (GATHER && masked) dq4 = *reinterpret_cast<const int4 *>(sdoc + ql4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = g * 4 + e;
-                const int qpos = qbase + ql + e;
-                float y;
-                const float t = score_log2<ALIBI, SOFTCAP>(s[r], qpos, kpos, scale_log2, scale, slope, cap,
-                                                           inv_cap, y);
-                const float le = e == 0 ? L.x : e == 1 ? L.y : e == 2 ? L.z : L.w;
-                const float de = e == 0 ? Dl.x : e == 1 ? Dl.y : e == 2 ? Dl.z : Dl.w;
-                float pv = fast_exp2(t - le);
-                if (MASKED) {
-                    bool vis = qpos >= qlo && qpos <= qhi;
-                    if (doc_on) {
-                        const int dq = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
-                        vis = vis && dq == dockey;
-                    }
-                    pv = vis ? pv : 0.0f;
+        for (int e = 0; e < 4; ++e) {
+            const int r = g * 4 + e;
+            const int c = g * 8 + e;
+            float tl;
+            if (kMods) {
+                float y = s[r] * a.scale;
+                if (ALIBI) y -= a.slope * (float)(rel + c);
+                if (SOFTCAP) y = a.cap * tanh_exp2(y * a.inv_cap);
+                tl = y * kLog2e;
+            } else {
+                tl = s[r] * a.scale_log2;
+            }
+            float pv = fast_exp2(tl - L[e]);
+            if (masked) {
+                bool vis = (uint32_t)(c - lo_t) <= (uint32_t)span;
+                if (GATHER) {
+                    const int dqv = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
+                    vis = vis && dqv == cm.dock;
                 }
-                float ds = pv * (dp[r] - de) * scale;
-                if (SOFTCAP) ds *= 1.0f - (y * inv_cap) * (y * inv_cap);
-                s[r] = pv;
-                dp[r] = ds;
+                pv = vis ? pv : 0.0f;
             }
+            float ds = pv * (dp[r] - Dl[e]) * a.scale;
+            if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
+            s[r] = pv;
+            dp[r] = ds;
+        }
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pb[s2][e] = static_cast<__bf16>(s[s2 * 8 + e]);
+            dsb[s2][e] = static_cast<__bf16>(dp[s2 * 8 + e]);
         }
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 pb, db16;
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pb[e] = static_cast<__bf16>(s[s2 * 8 + e]);
-                db16[e] = static_cast<__bf16>(dp[s2 * 8 + e]);
-            }
-#pragma unroll
-            for (int dbk = 0; dbk < D / 32; ++dbk) {
-                const int off = (dbk * 32 + n) * DkdvSmem<D>::TS + qb * 32 + s2 * 16 + hl * 8;
-                dv[dbk] = mfma32(*reinterpret_cast<const bf16x8 *>(&sm.doutt[off]), pb, dv[dbk]);
-                dk[dbk] = mfma32(*reinterpret_cast<const bf16x8 *>(&sm.qt[off]), db16, dk[dbk]);
-            }
+        for (int db = 0; db < D / 32; ++db) {
+            dv[db] = mfma32(read_cols_operand<D>(sg, off, qb * 2 + s2, db), pb[s2], dv[db]);
+            dk[db] = mfma32(read_cols_operand<D>(sq, off, qb * 2 + s2, db), dsb[s2], dk[db]);
         }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP, bool GATHER>
+__device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
+                                 const bf16x8 (&vf)[D / 16], const KvOffsets &off, DkdvSmem<D> &sm, int nsteps,
+                                 f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    auto issue = [&](int t, int q0) {
+        const int bf = t & 1;
+        issue_words_to_lds<kHalf>(sm.l2[bf], a.l2 + q0);
+        issue_words_to_lds<kHalf>(sm.delta[bf], a.delta + q0);
+        if (GATHER) issue_ints_to_lds<kHalf>(sm.doc[bf], a.doc + q0);
+        issue_tile_to_lds<D, kSwzKV, kHalf>(sm.q[bf], a.qb + (int64_t)q0 * a.q_st, a.q_st);
+        issue_tile_to_lds<D, kSwzKV, kHalf>(sm.g[bf], a.gb + (int64_t)q0 * a.do_st, a.do_st);
+    };
+    if (nsteps <= 0) return;
+    int q0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt);
+    issue(0, q0);
+#pragma unroll 1
+    for (int t = 0; t < nsteps; ++t) {
+        wait_vmcnt<0>();
+        tile_barrier();  // step t's tiles are visible; every wave is done with step t-1's buffers
+        int q_next = 0;
+        if (t + 1 < nsteps) {
+            q_next = step_row0(t + 1, a.nfull, a.fidx, a.pidx, a.nt);
+            issue(t + 1, q_next);
+        }
+        KvOffsets offt = off;  // opaque per step: derived offsets are not hoisted
+        asm volatile("" : "+v"(offt.row), "+v"(offt.tr));
+        const bool partial = (t >> 1) >= a.nfull;
+        const int bf = t & 1;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+            dkdv_block<D, ALIBI, SOFTCAP, GATHER>(a, cm, kf, vf, offt, sm.q[bf], sm.g[bf], sm.l2[bf],
+                                                  sm.delta[bf], sm.doc[bf], qb, q0, partial, dk, dv);
+        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
+        q0 = q_next;
     }
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) DkdvSmem<D> sm;
+    __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
     const int nt = p.nt;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = wg / nt;
     const int j = wg % nt;  // early key tiles first: under a causal mask they carry the most tiles
     const int b = bh / p.H, h = bh % p.H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 31, hl = lane >> 5;
     const int kpos = j * kTile + wv * 32 + n;
 
-    const __bf16 *qb_ = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
-    const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
-    const __bf16 *vb_ = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
-    const __bf16 *gb_ = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    const __bf16 *kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
+    const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
+    const int bm = p.mask_b == 1 ? 0 : b;
+    const int64_t col = (int64_t)bm * nt + j;
+
+    DkdvArgs a;
+    a.qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
+    a.gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    a.q_st = p.q_st;
+    a.do_st = p.do_st;
+    a.l2 = p.lse2 + ((int64_t)b * p.H + h) * p.T;
+    a.delta = p.delta + ((int64_t)b * p.H + h) * p.T;
+    a.nfull = min(max(load_uniform(p.full_q_num + col), 0), nt);
+    const int npart = min(max(load_uniform(p.q_num + col), 0), nt);
+    a.fidx = p.full_q_idx + col * nt;
+    a.pidx = p.q_idx + col * nt;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.T : nullptr;
+    a.nt = nt;
+    a.kpos = kpos;
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * kLog2e;
+    a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
+    a.cap = SOFTCAP ? p.softcap : 1.0f;
+    a.inv_cap = 1.0f / a.cap;
+    const int nsteps = 2 * (a.nfull + npart);
+
+    ColMask cm;
+    const bool gather = make_col_mask(p, bm, kpos, cm);
+    KvOffsets off;
+    kv_offsets<D>(off);
 
     bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        kf[st] = *reinterpret_cast<const bf16x8 *>(kb_ + (int64_t)kpos * p.k_st + st * 16 + hl * 8);
-        vf[st] = *reinterpret_cast<const bf16x8 *>(vb_ + (int64_t)kpos * p.v_st + st * 16 + hl * 8);
+        kf[st] = *reinterpret_cast<const bf16x8 *>(kb + (int64_t)kpos * p.k_st + st * 16 + hl * 8);
+        vf[st] = *reinterpret_cast<const bf16x8 *>(vb + (int64_t)kpos * p.v_st + st * 16 + hl * 8);
     }
-
-    const int bm = p.mask_b == 1 ? 0 : b;
-    const int64_t col = (int64_t)bm * nt + j;
-    const int nfull = min(max(p.full_q_num[col], 0), nt);
-    const int npart = min(max(p.q_num[col], 0), nt);
-    const int32_t *fidx = p.full_q_idx + col * nt;
-    const int32_t *pidx = p.q_idx + col * nt;
-    const int total = nfull + npart;
-
-    // Visible queries of this key: qlo <= q <= qhi (causal / window / sink),
-    // and the same document.
-    const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
-    const int32_t *doc = doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
-    const int dockey = doc_on ? doc[kpos] : 0;
-    const int qlo = (p.mask_flags & BSM_MASK_CAUSAL) ? kpos : 0;
-    int qhi = p.T - 1;
-    if (p.mask_flags & BSM_MASK_WINDOW) {
-        const bool sink = (p.mask_flags & BSM_MASK_SINKS) && kpos < p.sinks;
-        if (!sink) {
-            int64_t hi = (int64_t)kpos + (int64_t)(*p.window) - 1;
-            hi = hi < -1 ? -1 : (hi > p.T - 1 ? p.T - 1 : hi);
-            qhi = (int)hi;
-        }
-    }
-
-    const float scale = p.scale;
-    const float scale_log2 = p.scale * kLog2e;
-    const float slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
-    const float cap = SOFTCAP ? p.softcap : 1.0f;
-    const float inv_cap = 1.0f / cap;
-    const float *lse_bh = p.lse + ((int64_t)b * p.H + h) * p.T;
-    const float *delta_bh = p.delta + ((int64_t)b * p.H + h) * p.T;
-
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            dk[d][r] = 0.0f;
-            dv[d][r] = 0.0f;
+            dk[db][r] = 0.0f;
+            dv[db][r] = 0.0f;
         }
+    wait_vmcnt<0>();  // key rows and the mask bounds are in registers before any tile copy
 
-    for (int it = 0; it < total; ++it) {
-        const int i = clamp_tile(it < nfull ? fidx[it] : pidx[it - nfull], nt);
-        // Q and dO staged one after the other: one set of staging registers.
-        RowsUnits<D> ur;
-        load_rows<D>(ur, qb_, p.q_st, i * kTile);
-        float l2 = 0.0f, dl = 0.0f;
-        int dq = 0;
-        if (tid < kTile) {
-            const float lse = lse_bh[i * kTile + tid];
-            l2 = lse == -INFINITY ? 0.0f : lse * kLog2e;
-            dl = delta_bh[i * kTile + tid];
-            if (doc_on) dq = doc[i * kTile + tid];
-        }
-        __syncthreads();
-        store_rows<D>(ur, sm.q, DkdvSmem<D>::RS, sm.qt, DkdvSmem<D>::TS);
-        load_rows<D>(ur, gb_, p.do_st, i * kTile);
-        store_rows<D>(ur, sm.dout, DkdvSmem<D>::RS, sm.doutt, DkdvSmem<D>::TS);
-        if (tid < kTile) {
-            sm.lse2[tid] = l2;
-            sm.delta[tid] = dl;
-            sm.doc[tid] = dq;
-        }
-        __syncthreads();
-        if (it < nfull)
-            dkdv_tile<D, ALIBI, SOFTCAP, false>(sm, kf, vf, dk, dv, i, kpos, qlo, qhi, dockey, doc_on,
-                                                scale_log2, scale, slope, cap, inv_cap);
-        else
-            dkdv_tile<D, ALIBI, SOFTCAP, true>(sm, kf, vf, dk, dv, i, kpos, qlo, qhi, dockey, doc_on,
-                                               scale_log2, scale, slope, cap, inv_cap);
-    }
+    if (gather)
+        dkdv_main<D, ALIBI, SOFTCAP, true>(a, cm, kf, vf, off, sm, nsteps, dk, dv);
+    else
+        dkdv_main<D, ALIBI, SOFTCAP, false>(a, cm, kf, vf, off, sm, nsteps, dk, dv);
 
     __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)kpos * p.dk_st;
     __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)kpos * p.dv_st;
 #pragma unroll
-    for (int d = 0; d < D / 32; ++d) {
-        store_acc_rows(dkp, dk[d], d * 32, hl, 1.0f);
-        store_acc_rows(dvp, dv[d], d * 32, hl, 1.0f);
+    for (int db = 0; db < D / 32; ++db) {
+        store_acc_rows(dkp, dk[db], db * 32, hl);
+        store_acc_rows(dvp, dv[db], db * 32, hl);
     }
-}
-
-// ---------------------------------------------------------------- dQ
-
-template <int D>
-struct DqSmem {
-    static constexpr int RS = D + 8;
-    static constexpr int TS = kTile + 8;
-    __bf16 k[kTile * RS];
-    __bf16 kt[D * TS];
-    __bf16 v[kTile * RS];
-    int32_t doc[kTile];
-};
-
-struct QueryMask {
-    int32_t klo, khi, sink_end, docq;
-    bool doc_on;
-};
-
-// One listed key tile for the wave's 32 queries, one 32-key block at a time.
-template <int D, bool ALIBI, bool SOFTCAP, bool MASKED>
-__device__ inline void dq_tile(const DqSmem<D> &sm, const bf16x8 (&qf)[D / 16], const bf16x8 (&gf)[D / 16],
-                               f32x16 (&dq)[D / 32], int j, int qpos, float L, float Dl, const QueryMask &qm,
-                               float scale_log2, float scale, float slope, float cap, float inv_cap) {
-    const int lane = threadIdx.x & 63;
-    const int n = lane & 31, hl = lane >> 5;
-    const int kbase = j * kTile;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        f32x16 s, dp;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            s[r] = 0.0f;
-            dp[r] = 0.0f;
-        }
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-            const int off = (kb * 32 + n) * DqSmem<D>::RS + st * 16 + hl * 8;
-            s = mfma32(*reinterpret_cast<const bf16x8 *>(&sm.k[off]), qf[st], s);
-            dp = mfma32(*reinterpret_cast<const bf16x8 *>(&sm.v[off]), gf[st], dp);
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            int4 dk4 = {0, 0, 0, 0};
-            if (MASKED && qm.doc_on) dk4 = *reinterpret_cast<const int4 *>(&sm.doc[kb * 32 + g * 8 + hl * 4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = g * 4 + e;
-                const int kpos = kbase + kb * 32 + g * 8 + hl * 4 + e;
-                float y;
-                const float t = score_log2<ALIBI, SOFTCAP>(s[r], qpos, kpos, scale_log2, scale, slope, cap,
-                                                           inv_cap, y);
-                float pv = fast_exp2(t - L);
-                if (MASKED) {
-                    bool vis = (kpos >= qm.klo || kpos < qm.sink_end) && kpos <= qm.khi;
-                    if (qm.doc_on) {
-                        const int dkv = e == 0 ? dk4.x : e == 1 ? dk4.y : e == 2 ? dk4.z : dk4.w;
-                        vis = vis && dkv == qm.docq;
-                    }
-                    pv = vis ? pv : 0.0f;
-                }
-                float ds = pv * (dp[r] - Dl) * scale;
-                if (SOFTCAP) ds *= 1.0f - (y * inv_cap) * (y * inv_cap);
-                s[r] = ds;
-            }
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            bf16x8 db16;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) db16[e] = static_cast<__bf16>(s[s2 * 8 + e]);
-#pragma unroll
-            for (int d = 0; d < D / 32; ++d) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
-                    &sm.kt[(d * 32 + n) * DqSmem<D>::TS + kb * 32 + s2 * 16 + hl * 8]);
-                dq[d] = mfma32(a, db16, dq[d]);
-            }
-        }
-    }
-}
-
-template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 1) void dq_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
-    const int nt = p.nt;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / nt;
-    const int i = nt - 1 - (wg % nt);
-    const int b = bh / p.H, h = bh % p.H;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int n = lane & 31, hl = lane >> 5;
-    const int qpos = i * kTile + wv * 32 + n;
-
-    const __bf16 *qb_ = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
-    const __bf16 *kb_ = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
-    const __bf16 *vb_ = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
-    const __bf16 *gb_ = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
-
-    bf16x8 qf[D / 16], gf[D / 16];
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-        qf[st] = *reinterpret_cast<const bf16x8 *>(qb_ + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
-        gf[st] = *reinterpret_cast<const bf16x8 *>(gb_ + (int64_t)qpos * p.do_st + st * 16 + hl * 8);
-    }
-    const int64_t row_bh = ((int64_t)b * p.H + h) * p.T + qpos;
-    const float lse = p.lse[row_bh];
-    const float L = lse == -INFINITY ? 0.0f : lse * kLog2e;
-    const float Dl = p.delta[row_bh];
-
-    const int bm = p.mask_b == 1 ? 0 : b;
-    const int64_t row = (int64_t)bm * nt + i;
-    const int nfull = min(max(p.full_kv_num[row], 0), nt);
-    const int npart = min(max(p.kv_num[row], 0), nt);
-    const int32_t *fidx = p.full_kv_idx + row * nt;
-    const int32_t *pidx = p.kv_idx + row * nt;
-    const int total = nfull + npart;
-
-    QueryMask qm;
-    qm.doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
-    const int32_t *doc = qm.doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
-    qm.docq = qm.doc_on ? doc[qpos] : 0;
-    qm.khi = (p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1;
-    qm.klo = -1;
-    qm.sink_end = 0;
-    if (p.mask_flags & BSM_MASK_WINDOW) {
-        int64_t lo = (int64_t)qpos - (int64_t)(*p.window) + 1;
-        lo = lo < -1 ? -1 : (lo > p.T ? p.T : lo);
-        qm.klo = (int32_t)lo;
-        if ((p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0) qm.sink_end = p.sinks;
-    }
-
-    const float scale = p.scale;
-    const float scale_log2 = p.scale * kLog2e;
-    const float slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
-    const float cap = SOFTCAP ? p.softcap : 1.0f;
-    const float inv_cap = 1.0f / cap;
-
-    f32x16 dq[D / 32];
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dq[d][r] = 0.0f;
-
-    for (int it = 0; it < total; ++it) {
-        const int j = clamp_tile(it < nfull ? fidx[it] : pidx[it - nfull], nt);
-        RowsUnits<D> uk, uv;
-        load_rows<D>(uk, kb_, p.k_st, j * kTile);
-        load_rows<D>(uv, vb_, p.v_st, j * kTile);
-        int dk = 0;
-        if (qm.doc_on && tid < kTile) dk = doc[j * kTile + tid];
-        __syncthreads();
-        store_rows<D>(uk, sm.k, DqSmem<D>::RS, sm.kt, DqSmem<D>::TS);
-        store_rows<D>(uv, sm.v, DqSmem<D>::RS, nullptr, 0);
-        if (tid < kTile) sm.doc[tid] = dk;
-        __syncthreads();
-        if (it < nfull)
-            dq_tile<D, ALIBI, SOFTCAP, false>(sm, qf, gf, dq, j, qpos, L, Dl, qm, scale_log2, scale, slope, cap,
-                                              inv_cap);
-        else
-            dq_tile<D, ALIBI, SOFTCAP, true>(sm, qf, gf, dq, j, qpos, L, Dl, qm, scale_log2, scale, slope, cap,
-                                             inv_cap);
-    }
-
-    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qpos * p.dq_st;
-#pragma unroll
-    for (int d = 0; d < D / 32; ++d) store_acc_rows(dqp, dq[d], d * 32, hl, 1.0f);
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>

@@ -86,14 +86,20 @@ __device__ inline void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------
-// Tiles in LDS.  A 128 x D bf16 tile is stored row-major without padding; the
-// 16-byte chunks of row r are permuted by XOR with a row-dependent value so
-// that the two read patterns below hit distinct banks:
-//   * 16-byte reads of one chunk column by 32 consecutive rows (the A operand
-//     of S^T = K Q^T): f_K spreads 16 consecutive rows over 16 bank groups;
-//   * transposing 8-byte reads (ds_read_tr16_b64) of 4 chunks by 8
-//     consecutive rows (the A operand of O^T += V^T P^T): f_V spreads 4
-//     consecutive rows x 4 chunks over 16 bank groups.
+// Tiles in LDS.  A tile of rows x D bf16 is stored row-major without padding;
+// the 16-byte chunks of row r are permuted by XOR with a row-dependent value
+// so that the read patterns used on the tile hit distinct banks:
+//   * row reads: 16-byte reads of one chunk column by 32 consecutive rows (a
+//     matrix-core operand taken row by row) -- fk spreads 16 consecutive rows
+//     over 16 bank groups;
+//   * transposing reads: 8-byte ds_read_tr16_b64 of 4 chunks by 8
+//     consecutive rows (an operand taken column by column) -- fv spreads 4
+//     consecutive rows x 4 chunks over 16 bank groups;
+//   * both patterns on one tile: fkv has fv's low-row bits in chunk bits 2-3
+//     (so transposing reads stay conflict-free) and row bits 2-3 in chunk
+//     bits 0-1 (so 16 consecutive rows still get 16 distinct chunks).
+enum TileSwizzle { kSwzK = 0, kSwzV = 1, kSwzKV = 2 };
+
 template <int D>
 struct TileLayout;
 
@@ -103,6 +109,7 @@ struct TileLayout<128> {
     static constexpr int kChunks = 16;
     __device__ static int fk(int r) { return r & 15; }
     __device__ static int fv(int r) { return (r & 3) << 2; }
+    __device__ static int fkv(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 };
 
 template <>
@@ -111,7 +118,14 @@ struct TileLayout<64> {
     static constexpr int kChunks = 8;
     __device__ static int fk(int r) { return (r >> 1) & 7; }
     __device__ static int fv(int r) { return ((r >> 1) & 1) << 2; }
+    __device__ static int fkv(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 };
+
+template <int D, int SWZ>
+__device__ inline int tile_swizzle(int r) {
+    using L = TileLayout<D>;
+    return SWZ == kSwzK ? L::fk(r) : SWZ == kSwzV ? L::fv(r) : L::fkv(r);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -167,7 +181,7 @@ __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
 // uniform parts of copy addresses are computed by the scalar unit.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-template <int D, bool IS_V, int ROWS = kTile>
+template <int D, int SWZ, int ROWS>
 __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride) {
     using L = TileLayout<D>;
     constexpr int kRowsPerInstr = 1024 / L::kRowBytes;
@@ -182,15 +196,12 @@ __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0,
         // (wv * kInstr + x) * kRowsPerInstr is a multiple of 16 plus a
         // function of x only, so the swizzle depends on (x, q) alone.
         const int r16 = (x * kRowsPerInstr + q) & 15;
-        const int c = (lane % L::kChunks) ^ (IS_V ? L::fv(r16) : L::fk(r16));
+        const int c = (lane % L::kChunks) ^ tile_swizzle<D, SWZ>(r16);
         const uint32_t voff = (uint32_t)(q * row_bytes) + (uint32_t)(c * 16);
         const char *xbase = wbase + (int64_t)(x * kRowsPerInstr) * row_bytes;
         copy16_to_lds_s(xbase, voff, lds_addr(lds_tile + ((wv * kInstr + x) * kRowsPerInstr) * D));
     }
 }
-
-template <int D>
-constexpr int tile_lds_instr() { return kTile / (1024 / TileLayout<D>::kRowBytes) / 4; }
 
 // N int32 values, N/4 per wave (wave w copies entries w N/4 .. (w+1) N/4 - 1).
 template <int N = kTile>
@@ -198,6 +209,12 @@ __device__ inline void issue_ints_to_lds(int32_t *lds, const int32_t *g) {
     constexpr int kPer = N / 4;
     const int wv = wave_id(), lane = threadIdx.x & 63;
     if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds_addr(lds + wv * kPer));
+}
+
+// Same for N 4-byte words of any type.
+template <int N>
+__device__ inline void issue_words_to_lds(void *lds, const void *g) {
+    issue_ints_to_lds<N>(static_cast<int32_t *>(lds), static_cast<const int32_t *>(g));
 }
 
 // s_waitcnt on vmcnt only (gfx9 encoding; expcnt and lgkmcnt left at max).
@@ -250,6 +267,60 @@ __device__ inline void sched_interleave_mfma_valu() {
     }
 }
 
+// Per-lane LDS byte offsets of matrix-core operands read from a tile stored
+// with the fkv swizzle (read both ways).  Both patterns are XOR-structured,
+// so one base per pattern is kept and each operand's offset is derived where
+// it is used (row-block offsets are added as immediates):
+//   row read (A operand [32 rows][16 columns], lane = row):
+//       row ^ (st << 5)                           st = 16-column step
+//   transposing read (A operand [32 columns][16 rows] of the tile transposed):
+//       (tr ^ (db << 6) ^ (u << 5)) + 8 u rows    db = 32-column block,
+//                                                 u = rows +0..3 / +8..11 of a 16-row group
+struct KvOffsets {
+    int row;
+    int tr;
+};
+
+template <int D>
+__device__ inline void kv_offsets(KvOffsets &off) {
+    using L = TileLayout<D>;
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 31, hl = lane >> 5;
+    // chunk (2 st + hl) ^ fkv(n) = (2 st) ^ (hl ^ fkv(n)): 2 st and hl occupy
+    // different bits; n * kRowBytes is a multiple of 128.
+    off.row = n * L::kRowBytes + ((hl ^ L::fkv(n)) << 4);
+    // ds_read_tr16_b64: lane j of a 16-lane group G supplies the address of
+    // row R0 + j/4, columns c0 + 4 (j%4) .. +3; lane i then receives rows
+    // R0..R0+3 of column c0 + i.  c0 = 32 db + 16 (G%2), R0 = 4 (G/2) (+8
+    // for u = 1) inside each 16-row group.  The column block adds 4 db to the
+    // chunk index (an XOR, as the chunk's own low bits stay below bit 2), and
+    // the 8 extra rows of u = 1 flip bit 1 of fkv.
+    const int G = lane >> 4, j = lane & 15;
+    const int r = 4 * (G >> 1) + (j >> 2);
+    const int c = 2 * (G & 1) + ((j & 3) >> 1);
+    off.tr = r * L::kRowBytes + ((c ^ L::fkv(r)) << 4) + ((j & 1) << 3);
+}
+
+// A operand [32 rows][16 columns] at row block rb, column step st of an fkv
+// tile (lane = row, 8 consecutive columns).
+template <int D>
+__device__ inline bf16x8 read_rows_operand(const __bf16 *tile, const KvOffsets &off, int rb, int st) {
+    return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(tile) + rb * 32 * TileLayout<D>::kRowBytes +
+                                             (off.row ^ (st << 5)));
+}
+
+// A operand [32 columns][16 rows] of an fkv tile transposed: columns
+// 32 db + lane%32, rows 16 g16 + {4 hl..4 hl+3, 8+4 hl..8+4 hl+3} with hl the
+// lane half (the k-slot order of a 32x32 score block's registers).
+template <int D>
+__device__ inline bf16x8 read_cols_operand(const __bf16 *tile, const KvOffsets &off, int g16, int db) {
+    const char *base = reinterpret_cast<const char *>(tile) + g16 * 16 * TileLayout<D>::kRowBytes;
+    const i16x4 lo = ds_read_tr16(reinterpret_cast<const __bf16 *>(base + (off.tr ^ (db << 6))));
+    const i16x4 hi = ds_read_tr16(
+        reinterpret_cast<const __bf16 *>(base + 8 * TileLayout<D>::kRowBytes + (off.tr ^ ((db << 6) | 32))));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 __device__ inline int clamp_tile(int j, int nt) { return j < 0 ? 0 : (j >= nt ? nt - 1 : j); }
 
 // Key slot inside a 16-key group of the transposed value tile: bits 2 and 3
@@ -279,6 +350,140 @@ __device__ inline void store_transposed_4x8(__bf16 *dst, int ld, int r0, int c0,
         w.y = u16_at(v[2], dd) | (u16_at(v[3], dd) << 16);
         *reinterpret_cast<u32x2 *>(&dst[(c0 + dd) * ld + slot]) = w;
     }
+}
+
+// ---------------------------------------------------------------------------
+// How partial tiles are masked (chosen once per workgroup):
+//   kPlain  -- visible keys of a query form one interval [lo, hi]
+//              (causal, window and, with contiguous documents, the document);
+//   kSinks  -- plus the sink interval [slo, shi];
+//   kGather -- document ids are not contiguous runs: interval terms without
+//              the document, then a per-key document id compare.
+enum MaskMode { kPlain = 0, kSinks = 1, kGather = 2 };
+
+struct RowMask {
+    int32_t lo, hi;     // main visible interval of keys (inclusive)
+    int32_t slo, shi;   // sink interval (empty when slo > shi)
+    int32_t docq;       // document id of the query (kGather only)
+};
+
+// Row view (lane = query, S^T = K Q^T layout: lane (query n, half hl) holds
+// for key block kb the keys 32 kb + 8 (r/4) + 4 hl + r%4 of a 64-key step).
+// Score modifications (to the log2 domain) and the mask for the step whose
+// first key is key0.  Applied to every step: on a full tile every pair
+// is visible, so the mask changes nothing there.
+__device__ inline bool in_range(int c, int lo_t, int span) {
+    return (uint32_t)(c - lo_t) <= (uint32_t)span;  // lo_t <= c <= lo_t + span, span >= 0
+}
+
+template <bool ALIBI, bool SOFTCAP, int MODE>
+__device__ inline void row_mod_mask(const int32_t *sdoc, f32x16 (&s)[2], int key0, int qpos, float scale,
+                                    float slope, float cap, float inv_cap, const RowMask &rm, bool partial) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const int hl = (threadIdx.x & 63) >> 5;
+    const int kbase = key0 + hl * 4;
+    if (kMods) {
+        int rel = qpos - kbase;
+        if (ALIBI) asm volatile("" : "+v"(rel));  // keep per-register offsets from being hoisted
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - kbase
+                float y = s[kb][r] * scale;
+                if (ALIBI) y -= slope * (float)(rel - c);
+                if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
+                s[kb][r] = y * kLog2e;
+            }
+    }
+    if (!partial) return;  // full tile: every pair is visible
+    // Bounds relative to this step, kept opaque so that the compiler compares
+    // them with the per-register key offsets instead of hoisting 64
+    // loop-invariant thresholds into registers.  An empty interval is encoded
+    // as a start beyond every key with span 0, which no offset matches.
+    int lo_t = rm.hi >= rm.lo ? rm.lo - kbase : 1 << 30;
+    const int span = rm.hi >= rm.lo ? rm.hi - rm.lo : 0;
+    int slo_t = rm.shi >= rm.slo ? rm.slo - kbase : 1 << 30;
+    const int sspan = rm.shi >= rm.slo ? rm.shi - rm.slo : 0;
+    asm volatile("" : "+v"(lo_t), "+v"(slo_t));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        // The wave's 32 queries x these 32 keys: skip the elementwise test
+        // when every query sees every key, fill with -inf when none sees any.
+        const int kf = key0 + kb * 32, kl = kf + 31;
+        const bool all_vis = MODE != kGather && rm.lo <= kf && rm.hi >= kl;
+        const bool none_vis = (rm.hi < kf || rm.lo > kl || rm.hi < rm.lo) &&
+                              (MODE == kPlain || rm.shi < kf || rm.slo > kl || rm.shi < rm.slo);
+        if (__all(all_vis)) continue;
+        if (__all(none_vis)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
+            continue;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            int4 dk = {0, 0, 0, 0};
+            if (MODE == kGather) dk = *reinterpret_cast<const int4 *>(&sdoc[kb * 32 + g * 8 + hl * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = g * 4 + e;
+                const int c = kb * 32 + g * 8 + e;  // key - kbase
+                bool vis = in_range(c, lo_t, span);
+                if (MODE != kPlain) vis = vis || in_range(c, slo_t, sspan);
+                if (MODE == kGather) {
+                    const int dkv = e == 0 ? dk.x : e == 1 ? dk.y : e == 2 ? dk.z : dk.w;
+                    vis = vis && dkv == rm.docq;
+                }
+                s[kb][r] = vis ? s[kb][r] : -INFINITY;
+            }
+        }
+    }
+}
+
+// Row view of the mask for query qpos (mask batch row bm): visible keys form
+// [lo, hi] plus, with sinks, [slo, shi] (empty when slo > shi).  With
+// contiguous documents the document bounds come from the exported document
+// range; a row whose documents are not contiguous is flagged (-1) there, and
+// then the interval terms exclude the document and docq holds the query's id
+// for a per-key compare.  Returns the mode the row needs.
+__device__ inline int make_row_mask(const AttnParams &p, int bm, int qpos, RowMask &rm) {
+    const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
+    int ds = 0, de = p.T - 1;
+    rm.docq = 0;
+    bool gather = false;
+    if (doc_on) {
+        const int32_t *dr = p.doc_range + ((int64_t)bm * p.T + qpos) * 2;
+        ds = dr[0];
+        de = dr[1];
+        gather = ds < 0;  // the whole row is marked, so every lane agrees
+        if (gather) {
+            ds = 0;
+            de = p.T - 1;
+            rm.docq = p.doc_ids[(int64_t)bm * p.T + qpos];
+        }
+    }
+    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1, de);
+    int lo = ds;
+    bool sinks = false;
+    if (p.mask_flags & BSM_MASK_WINDOW) {
+        const int64_t wlo = (int64_t)qpos - (int64_t)(*p.window) + 1;
+        if (wlo > lo) lo = wlo > p.T ? p.T : (int)wlo;
+        sinks = (p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0;
+    }
+    rm.lo = lo;
+    rm.hi = hi;
+    rm.slo = ds;
+    rm.shi = sinks ? min(p.sinks - 1, hi) : ds - 1;
+    return gather ? kGather : sinks ? kSinks : kPlain;
+}
+
+// Whether no (query, key) pair of the wave's 32 queries and keys kf..kl is
+// visible in the row view (wave-uniform).
+template <int MODE>
+__device__ inline bool block_none_visible(const RowMask &rm, int kf, int kl) {
+    const bool none = (rm.hi < kf || rm.lo > kl || rm.hi < rm.lo) &&
+                      (MODE == kPlain || rm.shi < kf || rm.slo > kl || rm.shi < rm.slo);
+    return __all(none);
 }
 
 }  // namespace bsm

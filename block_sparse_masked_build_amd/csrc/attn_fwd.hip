@@ -40,20 +40,6 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kHalf = 64;  // keys per pipeline step
 
-// How partial tiles are masked (chosen once per workgroup):
-//   kPlain  -- visible keys of a query form one interval [lo, hi]
-//              (causal, window and, with contiguous documents, the document);
-//   kSinks  -- plus the sink interval [slo, shi];
-//   kGather -- document ids are not contiguous runs: interval terms without
-//              the document, then a per-key document id compare.
-enum MaskMode { kPlain = 0, kSinks = 1, kGather = 2 };
-
-struct RowMask {
-    int32_t lo, hi;     // main visible interval of keys (inclusive)
-    int32_t slo, shi;   // sink interval (empty when slo > shi)
-    int32_t docq;       // document id of the query (kGather only)
-};
-
 // Per-query state of the online softmax.  m is the reference maximum (log2
 // domain) the accumulators are scaled to; it is only moved when a new score
 // exceeds it by more than 2^8, so most steps skip the rescale.  The result
@@ -120,77 +106,6 @@ __device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, co
             const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbytes + kb * 32 * TileLayout<D>::kRowBytes +
                                                                 k_operand_offset(off, st));
             s[kb] = mfma32(a, qf[st], s[kb]);
-        }
-    }
-}
-
-// Score modifications (to the log2 domain) and the mask for one half tile
-// whose first key is key0.  Applied to every step: on a full tile every pair
-// is visible, so the mask changes nothing there.
-__device__ inline bool in_range(int c, int lo_t, int span) {
-    return (uint32_t)(c - lo_t) <= (uint32_t)span;  // lo_t <= c <= lo_t + span, span >= 0
-}
-
-template <bool ALIBI, bool SOFTCAP, int MODE>
-__device__ inline void fwd_mod_mask(const int32_t *sdoc, f32x16 (&s)[2], int key0, int qpos, float scale,
-                                    float slope, float cap, float inv_cap, const RowMask &rm, bool partial) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
-    const int hl = (threadIdx.x & 63) >> 5;
-    const int kbase = key0 + hl * 4;
-    if (kMods) {
-        int rel = qpos - kbase;
-        if (ALIBI) asm volatile("" : "+v"(rel));  // keep per-register offsets from being hoisted
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - kbase
-                float y = s[kb][r] * scale;
-                if (ALIBI) y -= slope * (float)(rel - c);
-                if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
-                s[kb][r] = y * kLog2e;
-            }
-    }
-    if (!partial) return;  // full tile: every pair is visible
-    // Bounds relative to this step, kept opaque so that the compiler compares
-    // them with the per-register key offsets instead of hoisting 64
-    // loop-invariant thresholds into registers.  An empty interval is encoded
-    // as a start beyond every key with span 0, which no offset matches.
-    int lo_t = rm.hi >= rm.lo ? rm.lo - kbase : 1 << 30;
-    const int span = rm.hi >= rm.lo ? rm.hi - rm.lo : 0;
-    int slo_t = rm.shi >= rm.slo ? rm.slo - kbase : 1 << 30;
-    const int sspan = rm.shi >= rm.slo ? rm.shi - rm.slo : 0;
-    asm volatile("" : "+v"(lo_t), "+v"(slo_t));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        // The wave's 32 queries x these 32 keys: skip the elementwise test
-        // when every query sees every key, fill with -inf when none sees any.
-        const int kf = key0 + kb * 32, kl = kf + 31;
-        const bool all_vis = MODE != kGather && rm.lo <= kf && rm.hi >= kl;
-        const bool none_vis = (rm.hi < kf || rm.lo > kl || rm.hi < rm.lo) &&
-                              (MODE == kPlain || rm.shi < kf || rm.slo > kl || rm.shi < rm.slo);
-        if (__all(all_vis)) continue;
-        if (__all(none_vis)) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = -INFINITY;
-            continue;
-        }
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            int4 dk = {0, 0, 0, 0};
-            if (MODE == kGather) dk = *reinterpret_cast<const int4 *>(&sdoc[kb * 32 + g * 8 + hl * 4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = g * 4 + e;
-                const int c = kb * 32 + g * 8 + e;  // key - kbase
-                bool vis = in_range(c, lo_t, span);
-                if (MODE != kPlain) vis = vis || in_range(c, slo_t, sspan);
-                if (MODE == kGather) {
-                    const int dkv = e == 0 ? dk.x : e == 1 ? dk.y : e == 2 ? dk.z : dk.w;
-                    vis = vis && dkv == rm.docq;
-                }
-                s[kb][r] = vis ? s[kb][r] : -INFINITY;
-            }
         }
     }
 }
@@ -285,10 +200,10 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
     };
     auto issue_k = [&](int t, int key0) {
         if (MODE == kGather) issue_ints_to_lds<kHalf>(sdb[t & 1], a.doc + key0);
-        issue_tile_to_lds<D, false, kHalf>(skb[t & 1], a.kb + (int64_t)key0 * a.k_st, a.k_st);
+        issue_tile_to_lds<D, kSwzK, kHalf>(skb[t & 1], a.kb + (int64_t)key0 * a.k_st, a.k_st);
     };
     auto issue_v = [&](int t, int key0) {
-        issue_tile_to_lds<D, true, kHalf>(svb[t & 1], a.vb + (int64_t)key0 * a.v_st, a.v_st);
+        issue_tile_to_lds<D, kSwzV, kHalf>(svb[t & 1], a.vb + (int64_t)key0 * a.v_st, a.v_st);
     };
     if (nsteps <= 0) return;
 
@@ -301,7 +216,7 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
         wait_vmcnt<0>();
         tile_barrier();
         fwd_qk<D>(skb[0], off, qf, sa);
-        fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[0], sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[0], sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
                                            0 >= a.nfull);
     }
     // One pipelined step: exponentials and PV of step t (scores in sc), QK^T
@@ -323,7 +238,7 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
         fwd_exp(sc, pb, l, c_mul, m_use);
         // this step's PV products, interleaved with the next step's mask
         fwd_pv<D>(svb[t & 1], offt, pb, o);
-        fwd_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[(t + 1) & 1], sn, key_next, a.qpos, a.scale, a.slope, a.cap,
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[(t + 1) & 1], sn, key_next, a.qpos, a.scale, a.slope, a.cap,
                                            a.inv_cap, rm, ((t + 1) >> 1) >= a.nfull);
         wait_lds_reads();  // this wave's reads of step t are done before the next barrier
     };
@@ -392,36 +307,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
     a.inv_cap = 1.0f / a.cap;
     const int nsteps = 2 * (a.nfull + npart);  // 64-key steps
 
-    // Visible keys of this query: [lo, hi] and, with sinks, [slo, shi].
     const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
     a.doc = doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
-    int ds = 0, de = p.T - 1;
     RowMask rm;
-    rm.docq = 0;
-    bool gather = false;
-    if (doc_on) {
-        const int32_t *dr = p.doc_range + ((int64_t)bm * p.T + qpos) * 2;
-        ds = dr[0];
-        de = dr[1];
-        gather = ds < 0;  // the whole row is marked, so every lane agrees
-        if (gather) {
-            ds = 0;
-            de = p.T - 1;
-            rm.docq = a.doc[qpos];
-        }
-    }
-    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1, de);
-    int lo = ds;
-    bool sinks = false;
-    if (p.mask_flags & BSM_MASK_WINDOW) {
-        const int64_t wlo = (int64_t)qpos - (int64_t)(*p.window) + 1;
-        if (wlo > lo) lo = wlo > p.T ? p.T : (int)wlo;
-        sinks = (p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0;
-    }
-    rm.lo = lo;
-    rm.hi = hi;
-    rm.slo = ds;
-    rm.shi = sinks ? min(p.sinks - 1, hi) : ds - 1;
+    const int mode = make_row_mask(p, bm, qpos, rm);
 
     OperandOffsets<D> off;
     operand_offsets<D>(off);
@@ -439,9 +328,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
     float m = -INFINITY, l = 0.0f;
     wait_vmcnt<0>();  // Q, the document range and id are in registers before any tile copy
 
-    if (gather)
+    if (mode == kGather)
         fwd_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
-    else if (sinks)
+    else if (mode == kSinks)
         fwd_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
     else
         fwd_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);

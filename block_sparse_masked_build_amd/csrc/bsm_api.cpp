@@ -208,7 +208,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
 
 size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D) {
     if (B < 1 || H < 1 || bad_T(T) || (D != 64 && D != 128)) return 0;
-    return align256((size_t)B * H * T * sizeof(float));
+    return 2 * align256((size_t)B * H * T * sizeof(float));
 }
 
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_tensor *q,
@@ -253,6 +253,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     p.dv = const_cast<void *>(ptr);
     p.lse = const_cast<float *>(lse);
     p.delta = static_cast<float *>(workspace);
+    p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)B * H * T * sizeof(float)));
     return hip_status(bsm::launch_attn_bwd(p, D, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_bwd launch");
 }

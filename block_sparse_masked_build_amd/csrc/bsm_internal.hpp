@@ -54,7 +54,8 @@ struct AttnParams {
     void *dk; int64_t dk_sb, dk_sh, dk_st;
     void *dv; int64_t dv_sb, dv_sh, dv_st;
     float *lse;      // [B, H, T]
-    float *delta;    // [B, H, T] (backward workspace)
+    float *delta;    // [B, H, T] (backward workspace): <dO, out> per query
+    float *lse2;     // [B, H, T] (backward workspace): lse * log2(e), 0 where lse = -inf
 };
 
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);

@@ -84,7 +84,7 @@ def test_workspace_sizes():
     assert lib.bsm_block_mask_workspace_bytes(100, 1) == 0
     assert lib.bsm_block_mask_workspace_bytes(65536, 1) >= 512 * 512
     assert lib.bsm_block_mask_workspace_bytes(65536, 2) >= 2 * 512 * 512
-    assert lib.bsm_bwd_workspace_bytes(2, 16, 16384, 128) >= 2 * 16 * 16384 * 4
+    assert lib.bsm_bwd_workspace_bytes(2, 16, 16384, 128) >= 2 * (2 * 16 * 16384 * 4)  # Delta and L per row
     assert lib.bsm_bwd_workspace_bytes(1, 1, 1024, 96) == 0
 
 
