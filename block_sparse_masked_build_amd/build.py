@@ -4,7 +4,8 @@
 
 Every source is compiled with hipcc for gfx950 only.  Packed fp32 VALU
 instructions are disabled for device code (-packed-fp32-ops); the host pass
-warns that it does not know the feature, which is harmless.
+warns that it does not know the feature, which is harmless.  The machine-code
+verifier runs on every build.
 """
 from __future__ import annotations
 
@@ -33,6 +34,9 @@ def hipcc() -> str:
 def compile_flags():
     return [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # run the machine-code verifier: an instruction the backend builds
+            # with an illegal operand is a build error, not silent bad code
+            "-mllvm", "-verify-machineinstrs",
             "-I", os.path.join(HERE, "..", "include")]
 
 

@@ -31,6 +31,8 @@
 // issued one step ahead, one barrier per step.  On partial tiles, 32 x 32
 // blocks that hold no visible pair are skipped (no products at all), blocks
 // that are entirely visible skip the elementwise test.
+#include <type_traits>
+
 #include "attn_common.hpp"
 
 namespace bsm {
@@ -110,16 +112,32 @@ struct DqArgs {
     float l2, delta;  // this lane's query
 };
 
+// LDS of dq_kernel: double-buffered 64-key halves of K and V and the keys'
+// document ids, addressed by byte address from the shared object.
+template <int D>
+struct DqSmem {
+    __bf16 k[2][kHalf * D];  // fkv swizzle
+    __bf16 v[2][kHalf * D];  // fkv swizzle
+    int32_t doc[2][kHalf];
+};
+
+template <int D>
+struct DqLds {
+    static constexpr uint32_t kTileBytes = kHalf * D * 2;
+    uint32_t k, v, doc;  // buffer 0; buffer 1 follows
+};
+
 template <int D, bool ALIBI, bool SOFTCAP, int MODE>
 __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 (&qf)[D / 16],
-                               const bf16x8 (&gf)[D / 16], const KvOffsets &off, __bf16 (&skb)[2][kHalf * D],
-                               __bf16 (&svb)[2][kHalf * D], int32_t (&sdb)[2][kHalf], int nsteps,
+                               const bf16x8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
                                f32x16 (&dq)[D / 32]) {
     constexpr bool kMods = ALIBI || SOFTCAP;
+    constexpr uint32_t kTB = DqLds<D>::kTileBytes;
     auto issue = [&](int t, int key0) {
-        if (MODE == kGather) issue_ints_to_lds<kHalf>(sdb[t & 1], a.doc + key0);
-        issue_tile_to_lds<D, kSwzKV, kHalf>(skb[t & 1], a.kb + (int64_t)key0 * a.k_st, a.k_st);
-        issue_tile_to_lds<D, kSwzKV, kHalf>(svb[t & 1], a.vb + (int64_t)key0 * a.v_st, a.v_st);
+        const uint32_t bf = t & 1;
+        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0);
+        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st);
+        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st);
     };
     if (nsteps <= 0) return;
     int key0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt);
@@ -133,7 +151,8 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
             key_next = step_row0(t + 1, a.nfull, a.fidx, a.pidx, a.nt);
             issue(t + 1, key_next);
         }
-        const __bf16 *sk = skb[t & 1], *sv = svb[t & 1];
+        const uint32_t bf = t & 1;
+        const uint32_t sk = lds.k + bf * kTB, sv = lds.v + bf * kTB;
         KvOffsets offt = off;  // opaque per step: derived offsets are not hoisted
         asm volatile("" : "+v"(offt.row), "+v"(offt.tr));
         const bool partial = (t >> 1) >= a.nfull;
@@ -157,8 +176,8 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
                 dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, st), gf[st], dp[kb]);
             }
         }
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[t & 1], s, key0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
-                                           partial);
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.scale, a.slope, a.cap,
+                                           a.inv_cap, rm, partial);
         bf16x8 dsb[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -166,7 +185,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
             for (int r = 0; r < 16; ++r) {
                 const float tl = s[kb][r];
                 const float pv = fast_exp2(kMods ? tl - a.l2 : __builtin_fmaf(tl, a.scale_log2, -a.l2));
-                float ds = pv * (dp[kb][r] - a.delta) * a.scale;
+                float ds = pv * (dp[kb][r] - a.delta);
                 if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
                 dsb[kb][r >> 3][r & 7] = static_cast<__bf16>(ds);
             }
@@ -186,9 +205,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
 
 template <int D, bool ALIBI, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(1024))) __bf16 skb[2][kHalf * D];  // keys (fkv swizzle)
-    __shared__ __attribute__((aligned(1024))) __bf16 svb[2][kHalf * D];  // values (fkv swizzle)
-    __shared__ __attribute__((aligned(16))) int32_t sdb[2][kHalf];       // document ids of the keys
+    __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
     const int nt = p.nt;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -230,6 +247,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
     const int mode = make_row_mask(p, bm, qpos, rm);
     KvOffsets off;
     kv_offsets<D>(off);
+    DqLds<D> lds;
+    lds.k = lds_addr(&sm.k[0][0]);
+    lds.v = lds_addr(&sm.v[0][0]);
+    lds.doc = lds_addr(&sm.doc[0][0]);
 
     bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -245,15 +266,15 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
     wait_vmcnt<0>();  // row operands and per-query values are in registers before any tile copy
 
     if (mode == kGather)
-        dq_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, gf, off, skb, svb, sdb, nsteps, dq);
+        dq_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, gf, off, lds, nsteps, dq);
     else if (mode == kSinks)
-        dq_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, gf, off, skb, svb, sdb, nsteps, dq);
+        dq_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, gf, off, lds, nsteps, dq);
     else
-        dq_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, gf, off, skb, svb, sdb, nsteps, dq);
+        dq_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, gf, off, lds, nsteps, dq);
 
     __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qpos * p.dq_st;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) store_acc_rows(dqp, dq[db], db * 32, hl);
+    for (int db = 0; db < D / 32; ++db) store_acc_rows(dqp, dq[db] * p.scale, db * 32, hl);  // dS without the scale
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -306,29 +327,37 @@ struct DkdvArgs {
     float scale, scale_log2, slope, cap, inv_cap;
 };
 
+// One pipeline step of dkdv is one listed 128-query tile.
 template <int D>
 struct DkdvSmem {
-    __bf16 q[2][kHalf * D];   // queries (fkv swizzle)
-    __bf16 g[2][kHalf * D];   // output gradients (fkv swizzle)
-    float l2[2][kHalf];
-    float delta[2][kHalf];
-    int32_t doc[2][kHalf];
+    __bf16 q[2][kTile * D];   // queries (fkv swizzle)
+    __bf16 g[2][kTile * D];   // output gradients (fkv swizzle)
+    float l2[2][kTile];
+    float delta[2][kTile];
+    int32_t doc[2][kTile];
 };
 
-// One 32-query block (queries q0.. q0+31 of the step, rows 32 qb.. of the LDS
-// tiles) against the wave's 32 keys.
-template <int D, bool ALIBI, bool SOFTCAP, bool GATHER>
-__device__ inline void dkdv_block(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
-                                  const bf16x8 (&vf)[D / 16], const KvOffsets &off, const __bf16 *sq,
-                                  const __bf16 *sg, const float *sl2, const float *sdl, const int32_t *sdoc,
-                                  int qb, int q0, bool partial, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
-    const int hl = (threadIdx.x & 63) >> 5;
-    const int qf = q0 + qb * 32, ql = qf + 31;
-    if (partial && __all(cm.hi < qf || cm.lo > ql || cm.hi < cm.lo)) return;  // nothing visible
-    const bool masked = partial && !__all(!GATHER && cm.lo <= qf && cm.hi >= ql);
+// Byte addresses of buffer 0 of each DkdvSmem field (buffer 1 follows).
+template <int D>
+struct DkdvLds {
+    static constexpr uint32_t kTileBytes = kTile * D * 2;
+    uint32_t q, g, l2, delta, doc;
+};
 
-    f32x16 s, dp;
+// Row operands (A of S = Q K^T and dP = dO V^T) of query block b.
+template <int D>
+__device__ inline void dkdv_read_rows(uint32_t sq, uint32_t sg, const KvOffsets &off, int b,
+                                      bf16x8 (&rq)[D / 16], bf16x8 (&rg)[D / 16]) {
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+        rq[st] = read_rows_operand<D>(sq, off, b, st);
+        rg[st] = read_rows_operand<D>(sg, off, b, st);
+    }
+}
+
+template <int D>
+__device__ inline void dkdv_sdp(const bf16x8 (&rq)[D / 16], const bf16x8 (&rg)[D / 16], const bf16x8 (&kf)[D / 16],
+                                const bf16x8 (&vf)[D / 16], f32x16 &s, f32x16 &dp) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         s[r] = 0.0f;
@@ -336,37 +365,46 @@ __device__ inline void dkdv_block(const DkdvArgs &a, const ColMask &cm, const bf
     }
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        s = mfma32(read_rows_operand<D>(sq, off, qb, st), kf[st], s);
-        dp = mfma32(read_rows_operand<D>(sg, off, qb, st), vf[st], dp);
+        s = mfma32(rq[st], kf[st], s);
+        dp = mfma32(rg[st], vf[st], dp);
     }
-    // Register r holds query qf + 4 hl + c with c = 8 (r/4) + r%4.
-    const int qbase = qf + 4 * hl;
+}
+
+// p and dS / scale of query block b (queries q0 + 32 b + 4 hl + 8 (r/4) + r%4
+// in register r) as the bf16 B operands of the dV and dK products.
+template <bool ALIBI, bool SOFTCAP, bool GATHER, bool MASKED>
+__device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t sl2, uint32_t sdl,
+                                  uint32_t sdoc, int b, int q0, const f32x16 &s, const f32x16 &dp,
+                                  bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const int hl = (threadIdx.x & 63) >> 5;
+    const int qbase = q0 + b * 32 + 4 * hl;
     int lo_t = cm.hi >= cm.lo ? cm.lo - qbase : 1 << 30;  // empty interval: no offset matches
     const int span = cm.hi >= cm.lo ? cm.hi - cm.lo : 0;
     int rel = qbase - a.kpos;
     asm volatile("" : "+v"(lo_t), "+v"(rel));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        const int ql4 = qb * 32 + g * 8 + hl * 4;
-        const f32x4 L = *reinterpret_cast<const f32x4 *>(sl2 + ql4);
-        const f32x4 Dl = *reinterpret_cast<const f32x4 *>(sdl + ql4);
-        int4 dq4 = {0, 0, 0, 0};
-        if (GATHER && masked) dq4 = *reinterpret_cast<const int4 *>(sdoc + ql4);
+        const int ql4 = b * 32 + g * 8 + hl * 4;
+        const f32x4 L = lds_load<f32x4>(sl2 + 4 * ql4);
+        const f32x4 Dl = lds_load<f32x4>(sdl + 4 * ql4);
+        i32x4 dq4 = {0, 0, 0, 0};
+        if (GATHER && MASKED) dq4 = lds_load<i32x4>(sdoc + 4 * ql4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = g * 4 + e;
             const int c = g * 8 + e;
-            float tl;
+            float pv, tl = 0.0f;
             if (kMods) {
                 float y = s[r] * a.scale;
                 if (ALIBI) y -= a.slope * (float)(rel + c);
                 if (SOFTCAP) y = a.cap * tanh_exp2(y * a.inv_cap);
                 tl = y * kLog2e;
+                pv = fast_exp2(tl - L[e]);
             } else {
-                tl = s[r] * a.scale_log2;
+                pv = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -L[e]));
             }
-            float pv = fast_exp2(tl - L[e]);
-            if (masked) {
+            if (MASKED) {
                 bool vis = (uint32_t)(c - lo_t) <= (uint32_t)span;
                 if (GATHER) {
                     const int dqv = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
@@ -374,64 +412,112 @@ __device__ inline void dkdv_block(const DkdvArgs &a, const ColMask &cm, const bf
                 }
                 pv = vis ? pv : 0.0f;
             }
-            float ds = pv * (dp[r] - Dl[e]) * a.scale;
+            float ds = pv * (dp[r] - Dl[e]);
             if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
-            s[r] = pv;
-            dp[r] = ds;
+            pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
+            dsb[r >> 3][r & 7] = static_cast<__bf16>(ds);
         }
     }
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pb[s2][e] = static_cast<__bf16>(s[s2 * 8 + e]);
-            dsb[s2][e] = static_cast<__bf16>(dp[s2 * 8 + e]);
-        }
+}
+
+// Transposed operands (A of dV^T += dO^T P and dK^T += Q^T dS) of block b.
+template <int D>
+__device__ inline void dkdv_read_cols(uint32_t sq, uint32_t sg, const KvOffsets &off, int b,
+                                      bf16x8 (&tq)[2][D / 32], bf16x8 (&tg)[2][D / 32]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            dv[db] = mfma32(read_cols_operand<D>(sg, off, qb * 2 + s2, db), pb[s2], dv[db]);
-            dk[db] = mfma32(read_cols_operand<D>(sq, off, qb * 2 + s2, db), dsb[s2], dk[db]);
+            tg[s2][db] = read_cols_operand<D>(sg, off, b * 2 + s2, db);
+            tq[s2][db] = read_cols_operand<D>(sq, off, b * 2 + s2, db);
         }
+}
+
+template <int D>
+__device__ inline void dkdv_acc(const bf16x8 (&tq)[2][D / 32], const bf16x8 (&tg)[2][D / 32], const bf16x8 (&pb)[2],
+                                const bf16x8 (&dsb)[2], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            dv[db] = mfma32(tg[s2][db], pb[s2], dv[db]);
+            dk[db] = mfma32(tq[s2][db], dsb[s2], dk[db]);
+        }
+}
+
+// One 128-query tile against the wave's 32 keys, software-pipelined over its
+// four 32-query blocks: the S / dP products of block b+1 are issued next to
+// the gradient arithmetic of block b, and the row operands of block b+2 are
+// read during the dV / dK products of block b.
+template <int D, bool ALIBI, bool SOFTCAP, bool GATHER, bool MASKED>
+__device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
+                                 const bf16x8 (&vf)[D / 16], const KvOffsets &off, uint32_t sq, uint32_t sg,
+                                 uint32_t sl2, uint32_t sdl, uint32_t sdoc, int q0,
+                                 f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    constexpr int NB = kTile / 32;
+    bf16x8 rq[D / 16], rg[D / 16];
+    f32x16 s[2], dp[2];
+    dkdv_read_rows<D>(sq, sg, off, 0, rq, rg);
+    dkdv_sdp<D>(rq, rg, kf, vf, s[0], dp[0]);
+    dkdv_read_rows<D>(sq, sg, off, 1, rq, rg);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int cur = b & 1;
+        if (b + 1 < NB) dkdv_sdp<D>(rq, rg, kf, vf, s[cur ^ 1], dp[cur ^ 1]);
+        bf16x8 pb[2], dsb[2];
+        dkdv_grads<ALIBI, SOFTCAP, GATHER, MASKED>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb);
+        bf16x8 tq[2][D / 32], tg[2][D / 32];
+        dkdv_read_cols<D>(sq, sg, off, b, tq, tg);
+        if (b + 2 < NB) dkdv_read_rows<D>(sq, sg, off, b + 2, rq, rg);
+        dkdv_acc<D>(tq, tg, pb, dsb, dk, dv);
+        __builtin_amdgcn_sched_barrier(0);  // keep each block's reads and products in their own window
+    }
 }
 
 template <int D, bool ALIBI, bool SOFTCAP, bool GATHER>
 __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
-                                 const bf16x8 (&vf)[D / 16], const KvOffsets &off, DkdvSmem<D> &sm, int nsteps,
-                                 f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
-    auto issue = [&](int t, int q0) {
-        const int bf = t & 1;
-        issue_words_to_lds<kHalf>(sm.l2[bf], a.l2 + q0);
-        issue_words_to_lds<kHalf>(sm.delta[bf], a.delta + q0);
-        if (GATHER) issue_ints_to_lds<kHalf>(sm.doc[bf], a.doc + q0);
-        issue_tile_to_lds<D, kSwzKV, kHalf>(sm.q[bf], a.qb + (int64_t)q0 * a.q_st, a.q_st);
-        issue_tile_to_lds<D, kSwzKV, kHalf>(sm.g[bf], a.gb + (int64_t)q0 * a.do_st, a.do_st);
+                                 const bf16x8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
+                                 int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+    constexpr uint32_t kTB = DkdvLds<D>::kTileBytes, kWB = kTile * 4;
+    auto tile_q0 = [&](int it) {
+        return clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull), a.nt) *
+               kTile;
     };
-    if (nsteps <= 0) return;
-    int q0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt);
+    auto issue = [&](int t, int q0) {
+        const uint32_t bf = t & 1;
+        issue_ints_to_lds_at<kTile>(lds.l2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0));
+        issue_ints_to_lds_at<kTile>(lds.delta + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0));
+        if (GATHER) issue_ints_to_lds_at<kTile>(lds.doc + bf * kWB, a.doc + q0);
+        issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.q + bf * kTB, a.qb + (int64_t)q0 * a.q_st, a.q_st);
+        issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.g + bf * kTB, a.gb + (int64_t)q0 * a.do_st, a.do_st);
+    };
+    if (ntiles <= 0) return;
+    int q0 = tile_q0(0);
     issue(0, q0);
-#pragma unroll 1
-    for (int t = 0; t < nsteps; ++t) {
+    // One step per listed tile.  Full tiles and partial tiles run in two
+    // loops of straight-line code, so that the accumulators never pass
+    // through a branch merge (which makes the register allocator copy them).
+    auto step = [&](int t, auto masked) {
         wait_vmcnt<0>();
-        tile_barrier();  // step t's tiles are visible; every wave is done with step t-1's buffers
+        tile_barrier();  // tile t is visible; every wave is done with tile t-1's buffers
         int q_next = 0;
-        if (t + 1 < nsteps) {
-            q_next = step_row0(t + 1, a.nfull, a.fidx, a.pidx, a.nt);
+        if (t + 1 < ntiles) {
+            q_next = tile_q0(t + 1);
             issue(t + 1, q_next);
         }
         KvOffsets offt = off;  // opaque per step: derived offsets are not hoisted
         asm volatile("" : "+v"(offt.row), "+v"(offt.tr));
-        const bool partial = (t >> 1) >= a.nfull;
-        const int bf = t & 1;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-            dkdv_block<D, ALIBI, SOFTCAP, GATHER>(a, cm, kf, vf, offt, sm.q[bf], sm.g[bf], sm.l2[bf],
-                                                  sm.delta[bf], sm.doc[bf], qb, q0, partial, dk, dv);
-        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
+        const uint32_t bf = t & 1;
+        dkdv_tile<D, ALIBI, SOFTCAP, GATHER, decltype(masked)::value>(
+            a, cm, kf, vf, offt, lds.q + bf * kTB, lds.g + bf * kTB, lds.l2 + bf * kWB, lds.delta + bf * kWB,
+            lds.doc + bf * kWB, q0, dk, dv);
+        wait_lds_reads();  // this wave's reads of tile t are done before the next barrier
         q0 = q_next;
-    }
+    };
+#pragma unroll 1
+    for (int t = 0; t < a.nfull; ++t) step(t, std::false_type());
+#pragma unroll 1
+    for (int t = a.nfull; t < ntiles; ++t) step(t, std::true_type());
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>
@@ -470,10 +556,17 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
     a.cap = SOFTCAP ? p.softcap : 1.0f;
     a.inv_cap = 1.0f / a.cap;
-    const int nsteps = 2 * (a.nfull + npart);
+    const int ntiles = a.nfull + npart;
 
     ColMask cm;
     const bool gather = make_col_mask(p, bm, kpos, cm);
+    // LDS is addressed by byte address, taken here from the shared object.
+    DkdvLds<D> lds;
+    lds.q = lds_addr(&sm.q[0][0]);
+    lds.g = lds_addr(&sm.g[0][0]);
+    lds.l2 = lds_addr(&sm.l2[0][0]);
+    lds.delta = lds_addr(&sm.delta[0][0]);
+    lds.doc = lds_addr(&sm.doc[0][0]);
     KvOffsets off;
     kv_offsets<D>(off);
 
@@ -494,15 +587,15 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
     wait_vmcnt<0>();  // key rows and the mask bounds are in registers before any tile copy
 
     if (gather)
-        dkdv_main<D, ALIBI, SOFTCAP, true>(a, cm, kf, vf, off, sm, nsteps, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, true>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
     else
-        dkdv_main<D, ALIBI, SOFTCAP, false>(a, cm, kf, vf, off, sm, nsteps, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, false>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
 
     __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)kpos * p.dk_st;
     __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)kpos * p.dv_st;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-        store_acc_rows(dkp, dk[db], db * 32, hl);
+        store_acc_rows(dkp, dk[db] * p.scale, db * 32, hl);  // dS was accumulated without the scale
         store_acc_rows(dvp, dv[db], db * 32, hl);
     }
 }

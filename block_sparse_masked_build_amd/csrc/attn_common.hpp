@@ -11,6 +11,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -182,7 +183,7 @@ __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <int D, int SWZ, int ROWS>
-__device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride) {
+__device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_row0, int64_t row_stride) {
     using L = TileLayout<D>;
     constexpr int kRowsPerInstr = 1024 / L::kRowBytes;
     constexpr int kInstr = ROWS / kRowsPerInstr / 4;
@@ -199,8 +200,13 @@ __device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0,
         const int c = (lane % L::kChunks) ^ tile_swizzle<D, SWZ>(r16);
         const uint32_t voff = (uint32_t)(q * row_bytes) + (uint32_t)(c * 16);
         const char *xbase = wbase + (int64_t)(x * kRowsPerInstr) * row_bytes;
-        copy16_to_lds_s(xbase, voff, lds_addr(lds_tile + ((wv * kInstr + x) * kRowsPerInstr) * D));
+        copy16_to_lds_s(xbase, voff, lds_tile + (uint32_t)((wv * kInstr + x) * kRowsPerInstr * L::kRowBytes));
     }
+}
+
+template <int D, int SWZ, int ROWS>
+__device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride) {
+    issue_tile_to_lds_at<D, SWZ, ROWS>(lds_addr(lds_tile), g_row0, row_stride);
 }
 
 // N int32 values, N/4 per wave (wave w copies entries w N/4 .. (w+1) N/4 - 1).
@@ -209,6 +215,20 @@ __device__ inline void issue_ints_to_lds(int32_t *lds, const int32_t *g) {
     constexpr int kPer = N / 4;
     const int wv = wave_id(), lane = threadIdx.x & 63;
     if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds_addr(lds + wv * kPer));
+}
+
+// Same with the LDS destination given as a byte address.
+template <int N>
+__device__ inline void issue_ints_to_lds_at(uint32_t lds, const int32_t *g) {
+    constexpr int kPer = N / 4;
+    const int wv = wave_id(), lane = threadIdx.x & 63;
+    if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds + 4 * wv * kPer);
+}
+
+// Load of a T from an LDS byte address.
+template <typename T>
+__device__ inline T lds_load(uint32_t addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) T *>((uintptr_t)addr);
 }
 
 // Same for N 4-byte words of any type.
@@ -228,6 +248,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline i16x4 ds_read_tr16(const __bf16 *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
+}
+
+__device__ inline i16x4 ds_read_tr16_at(uint32_t addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)((uintptr_t)addr));
 }
 
 // Barrier for the asynchronous tile copies.  A fenced __syncthreads would
@@ -302,22 +326,20 @@ __device__ inline void kv_offsets(KvOffsets &off) {
 }
 
 // A operand [32 rows][16 columns] at row block rb, column step st of an fkv
-// tile (lane = row, 8 consecutive columns).
+// tile at LDS byte address `tile` (lane = row, 8 consecutive columns).
 template <int D>
-__device__ inline bf16x8 read_rows_operand(const __bf16 *tile, const KvOffsets &off, int rb, int st) {
-    return *reinterpret_cast<const bf16x8 *>(reinterpret_cast<const char *>(tile) + rb * 32 * TileLayout<D>::kRowBytes +
-                                             (off.row ^ (st << 5)));
+__device__ inline bf16x8 read_rows_operand(uint32_t tile, const KvOffsets &off, int rb, int st) {
+    return lds_load<bf16x8>(tile + rb * 32 * TileLayout<D>::kRowBytes + (off.row ^ (st << 5)));
 }
 
 // A operand [32 columns][16 rows] of an fkv tile transposed: columns
 // 32 db + lane%32, rows 16 g16 + {4 hl..4 hl+3, 8+4 hl..8+4 hl+3} with hl the
 // lane half (the k-slot order of a 32x32 score block's registers).
 template <int D>
-__device__ inline bf16x8 read_cols_operand(const __bf16 *tile, const KvOffsets &off, int g16, int db) {
-    const char *base = reinterpret_cast<const char *>(tile) + g16 * 16 * TileLayout<D>::kRowBytes;
-    const i16x4 lo = ds_read_tr16(reinterpret_cast<const __bf16 *>(base + (off.tr ^ (db << 6))));
-    const i16x4 hi = ds_read_tr16(
-        reinterpret_cast<const __bf16 *>(base + 8 * TileLayout<D>::kRowBytes + (off.tr ^ ((db << 6) | 32))));
+__device__ inline bf16x8 read_cols_operand(uint32_t tile, const KvOffsets &off, int g16, int db) {
+    const uint32_t base = tile + g16 * 16 * TileLayout<D>::kRowBytes;
+    const i16x4 lo = ds_read_tr16_at(base + (off.tr ^ (db << 6)));
+    const i16x4 hi = ds_read_tr16_at(base + 8 * TileLayout<D>::kRowBytes + (off.tr ^ ((db << 6) | 32)));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -370,14 +392,15 @@ struct RowMask {
 // Row view (lane = query, S^T = K Q^T layout: lane (query n, half hl) holds
 // for key block kb the keys 32 kb + 8 (r/4) + 4 hl + r%4 of a 64-key step).
 // Score modifications (to the log2 domain) and the mask for the step whose
-// first key is key0.  Applied to every step: on a full tile every pair
-// is visible, so the mask changes nothing there.
+// first key is key0; sdoc is the LDS byte address of the step's key document
+// ids (gather mode).  Applied to every step: on a full tile every pair is
+// visible, so the mask changes nothing there.
 __device__ inline bool in_range(int c, int lo_t, int span) {
     return (uint32_t)(c - lo_t) <= (uint32_t)span;  // lo_t <= c <= lo_t + span, span >= 0
 }
 
 template <bool ALIBI, bool SOFTCAP, int MODE>
-__device__ inline void row_mod_mask(const int32_t *sdoc, f32x16 (&s)[2], int key0, int qpos, float scale,
+__device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int qpos, float scale,
                                     float slope, float cap, float inv_cap, const RowMask &rm, bool partial) {
     constexpr bool kMods = ALIBI || SOFTCAP;
     const int hl = (threadIdx.x & 63) >> 5;
@@ -422,8 +445,8 @@ __device__ inline void row_mod_mask(const int32_t *sdoc, f32x16 (&s)[2], int key
         }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            int4 dk = {0, 0, 0, 0};
-            if (MODE == kGather) dk = *reinterpret_cast<const int4 *>(&sdoc[kb * 32 + g * 8 + hl * 4]);
+            i32x4 dk = {0, 0, 0, 0};
+            if (MODE == kGather) dk = lds_load<i32x4>(sdoc + 4 * (kb * 32 + g * 8 + hl * 4));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = g * 4 + e;

@@ -216,7 +216,7 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
         wait_vmcnt<0>();
         tile_barrier();
         fwd_qk<D>(skb[0], off, qf, sa);
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[0], sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds_addr(sdb[0]), sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
                                            0 >= a.nfull);
     }
     // One pipelined step: exponentials and PV of step t (scores in sc), QK^T
@@ -238,7 +238,7 @@ __device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x
         fwd_exp(sc, pb, l, c_mul, m_use);
         // this step's PV products, interleaved with the next step's mask
         fwd_pv<D>(svb[t & 1], offt, pb, o);
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(sdb[(t + 1) & 1], sn, key_next, a.qpos, a.scale, a.slope, a.cap,
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds_addr(sdb[(t + 1) & 1]), sn, key_next, a.qpos, a.scale, a.slope, a.cap,
                                            a.inv_cap, rm, ((t + 1) >> 1) >= a.nfull);
         wait_lds_reads();  // this wave's reads of step t are done before the next barrier
     };
