@@ -34,7 +34,8 @@ class BsmMaskSpec(ctypes.Structure):
 class BsmBlockMask(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices",
-        "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices", "doc_range")]
+        "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices", "doc_range",
+        "kv_order", "q_order")]
 
 
 class BsmScoreMod(ctypes.Structure):

@@ -86,6 +86,8 @@ class BlockMask(NamedTuple):
     full_q_num_blocks: torch.Tensor
     full_q_indices: torch.Tensor
     doc_range: torch.Tensor   # int32 [mask_b, T, 2]: (first, last) position of each position's document
+    kv_order: torch.Tensor    # int32 [mask_b * QT, 4]: rows, most tiles first (row, full, partial, first tile)
+    q_order: torch.Tensor     # int32 [mask_b * KT, 4]: columns, most tiles first (same layout)
 
     def c_struct(self) -> BsmBlockMask:
         return BsmBlockMask(*[t.data_ptr() for t in self])
@@ -133,7 +135,7 @@ def empty_block_mask(T: int, mask_b: int, device="cuda") -> BlockMask:
     mk = lambda *s: torch.empty(s, dtype=torch.int32, device=device)
     return BlockMask(mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
                      mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
-                     mk(mask_b, T, 2))
+                     mk(mask_b, T, 2), mk(mask_b * nt, 4), mk(mask_b * nt, 4))
 
 
 def block_mask_workspace(spec: MaskSpec) -> torch.Tensor:

@@ -130,9 +130,12 @@ __device__ inline int tile_swizzle(int r) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ inline uint32_t lds_addr(const void *p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)(p);
-}
+// LDS byte address of a pointer into LDS.  A generic address of LDS is the
+// shared aperture base (zero low half) plus the LDS offset, so the low 32
+// bits are the offset; taking them directly avoids a generic-to-LDS cast,
+// whose null test the backend can emit as an illegal compare against the
+// aperture register.
+__device__ inline uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
 // One asynchronous HBM -> LDS copy per lane: 16 bytes from `g` land at LDS
 // byte lds_base + 16 * lane (lds_base wave-uniform, passed through M0).
@@ -229,6 +232,12 @@ __device__ inline void issue_ints_to_lds_at(uint32_t lds, const int32_t *g) {
 template <typename T>
 __device__ inline T lds_load(uint32_t addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) T *>((uintptr_t)addr);
+}
+
+// Store of a T to an LDS byte address.
+template <typename T>
+__device__ inline void lds_store(uint32_t addr, T v) {
+    *reinterpret_cast<__attribute__((address_space(3))) T *>((uintptr_t)addr) = v;
 }
 
 // Same for N 4-byte words of any type.
@@ -461,6 +470,83 @@ __device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int
             }
         }
     }
+}
+
+// Score modifications alone (row view, step starting at key0): the scores
+// leave in the log2 domain.  Without modifications nothing is done here; the
+// scale is folded into the exponential instead.
+template <bool ALIBI, bool SOFTCAP>
+__device__ inline void row_mods(f32x16 (&s)[2], int key0, int qpos, float scale, float slope, float cap,
+                                float inv_cap) {
+    if (!(ALIBI || SOFTCAP)) return;
+    const int hl = (threadIdx.x & 63) >> 5;
+    int rel = qpos - (key0 + hl * 4);
+    if (ALIBI) asm volatile("" : "+v"(rel));  // keep per-register offsets from being hoisted
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - (key0 + 4 hl)
+            float y = s[kb][r] * scale;
+            if (ALIBI) y -= slope * (float)(rel - c);
+            if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
+            s[kb][r] = y * kLog2e;
+        }
+}
+
+// Elementwise mask of a partial tile's step (row view), without branches:
+// every score is tested, hidden ones become -inf.  sdoc is the LDS byte
+// address of the step's key document ids (kGather only).
+template <int MODE>
+__device__ inline void row_mask_flat(uint32_t sdoc, f32x16 (&s)[2], int key0, const RowMask &rm) {
+    const int hl = (threadIdx.x & 63) >> 5;
+    const int kbase = key0 + hl * 4;
+    // Bounds relative to this lane's first key, opaque so that the compiler
+    // compares them with the per-register key offsets instead of hoisting 64
+    // loop-invariant thresholds.  An empty interval starts beyond every key.
+    int lo_t = rm.hi >= rm.lo ? rm.lo - kbase : 1 << 30;
+    const int span = rm.hi >= rm.lo ? rm.hi - rm.lo : 0;
+    int slo_t = rm.shi >= rm.slo ? rm.slo - kbase : 1 << 30;
+    const int sspan = rm.shi >= rm.slo ? rm.shi - rm.slo : 0;
+    asm volatile("" : "+v"(lo_t), "+v"(slo_t));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            i32x4 dk = {0, 0, 0, 0};
+            if (MODE == kGather) dk = lds_load<i32x4>(sdoc + 4 * (kb * 32 + g * 8 + hl * 4));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = g * 4 + e;
+                const int c = kb * 32 + g * 8 + e;  // key - kbase
+                bool vis = in_range(c, lo_t, span);
+                if (MODE != kPlain) vis = vis || in_range(c, slo_t, sspan);
+                if (MODE == kGather) {
+                    const int dkv = e == 0 ? dk.x : e == 1 ? dk.y : e == 2 ? dk.z : dk.w;
+                    vis = vis && dkv == rm.docq;
+                }
+                s[kb][r] = vis ? s[kb][r] : -INFINITY;
+            }
+        }
+}
+
+// Maximum over a row-view step (32 scores per lane, both lane halves of a
+// query combined): four independent chains, then the lane-half exchange as
+// one cross-lane swap (no LDS round trip).
+__device__ inline float row_max(const f32x16 (&s)[2]) {
+    float c[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int kb = x >> 1, r0 = (x & 1) * 8;
+        float v = fmaxf(fmaxf(s[kb][r0], s[kb][r0 + 1]), s[kb][r0 + 2]);
+        v = fmaxf(fmaxf(v, s[kb][r0 + 3]), s[kb][r0 + 4]);
+        v = fmaxf(fmaxf(v, s[kb][r0 + 5]), s[kb][r0 + 6]);
+        c[x] = fmaxf(v, s[kb][r0 + 7]);
+    }
+    const float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+    const uint32_t u = __builtin_bit_cast(uint32_t, mx);
+    const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
 }
 
 // Row view of the mask for query qpos (mask batch row bm): visible keys form

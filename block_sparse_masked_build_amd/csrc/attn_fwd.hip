@@ -32,6 +32,10 @@
 //  * exp via exp2 with log2(e) and the score scale folded into one FMA; the
 //    running maximum is only moved (and the output rescaled) when a score
 //    exceeds it by more than 2^8.
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
 #include "attn_common.hpp"
 
 namespace bsm {
@@ -110,32 +114,6 @@ __device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, co
     }
 }
 
-// Running-maximum update for one half tile (and the rescale of o and l when
-// the maximum moved by more than the threshold).  Returns the reference the
-// exponentials use.
-template <int D, bool KMODS>
-__device__ inline float fwd_max_update(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float &m, float &l,
-                                       float scale_log2) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (!KMODS) mx *= scale_log2;
-    if (__any(mx > m + kRescaleThreshold)) {
-        const float m_new = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        m = m_new;
-    }
-    return (m == -INFINITY) ? 0.0f : m;
-}
-
 // p = 2^(s c - m) as bf16 (the B operand of the PV products), summed into l
 // in fp32 before rounding (so lse keeps fp32 accuracy).
 __device__ inline void fwd_exp(const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float &l, float c_mul, float m_use) {
@@ -171,173 +149,219 @@ __device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, co
     }
 }
 
+// ---------------------------------------------------------------- schedule
+// One workgroup per item -- one (batch, head, query tile) row of the block
+// mask.  The hardware dispatcher hands workgroups to free slots in blockIdx
+// order, so the order of blockIdx is the order of work: the block mask's
+// work order (rows with the most listed tiles first, so short rows fill the
+// end of the launch), arranged so that the rows running at the same time on
+// one XCD share key and value tiles (see ItemOrder).
+
+// One work-order record: (flat row, full tiles, partial tiles, first tile).
+struct WorkRec {
+    int packed, nfull, npart, first;
+};
+
+__device__ inline WorkRec load_rec(const int32_t *order, int e) {
+    const i32x4 r = *(const __attribute__((address_space(4))) i32x4 *)(order + 4 * (int64_t)e);
+    return {r.x, r.y, r.z, r.w};
+}
+
+// Wave-uniform values of the item being worked on.
 struct FwdArgs {
     const __bf16 *kb, *vb;
-    int64_t k_st, v_st;
     const int32_t *doc, *fidx, *pidx;
-    int nfull, nt, qpos;
+    int b, h, bm, row;
+    int nfull, ntiles, nt, qpos, first;
     float scale, scale_log2, slope, cap, inv_cap;
 };
 
-// The double-buffered, software-pipelined loop over the listed tiles (in
-// 64-key steps).  Step t's scores are computed during step t-1.  At the top
-// of step t the copies issued at the top of step t-1 -- K(t+1) and V(t) --
-// have landed; the barrier also certifies that every wave has finished step
-// t-1, freeing K buffer t%2 (last read for K(t)) and V buffer (t+1)%2 (last
-// read for V(t-1)) for K(t+2) and V(t+1).
-template <int D, bool ALIBI, bool SOFTCAP, int MODE>
-__device__ inline void fwd_main(const FwdArgs &a, const RowMask &rm, const bf16x8 (&qf)[D / 16],
-                                const OperandOffsets<D> &off, __bf16 (&skb)[2][kHalf * D],
-                                __bf16 (&svb)[2][kHalf * D], int32_t (&sdb)[2][kHalf], int nsteps,
-                                f32x16 (&o)[D / 32], float &m, float &l) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
-    const float c_mul = kMods ? 1.0f : a.scale_log2;
-    auto step_key0 = [&](int t) {
-        const int it = t >> 1;
-        const int jj = clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull),
-                                  a.nt);
-        return jj * kTile + (t & 1) * kHalf;
-    };
-    auto issue_k = [&](int t, int key0) {
-        if (MODE == kGather) issue_ints_to_lds<kHalf>(sdb[t & 1], a.doc + key0);
-        issue_tile_to_lds<D, kSwzK, kHalf>(skb[t & 1], a.kb + (int64_t)key0 * a.k_st, a.k_st);
-    };
-    auto issue_v = [&](int t, int key0) {
-        issue_tile_to_lds<D, kSwzV, kHalf>(svb[t & 1], a.vb + (int64_t)key0 * a.v_st, a.v_st);
-    };
-    if (nsteps <= 0) return;
+// Item order.  Item k is work-order entry e for head (and, with a shared
+// mask, batch entry) rem.  Items come in chunks of 2^ord_chunk_log2
+// consecutive entries of one head -- rows that mostly share key and value
+// tiles -- and chunk c is served by queue c % Q: workgroup b takes the
+// (b / Q)-th item of queue b % Q.  Workgroups are dispatched round-robin
+// over the XCDs, so with Q = 8 each queue runs on one XCD and the rows
+// running at the same time there share tiles through its L2; items leave
+// each queue in work order.  The host picks the chunk so that every queue
+// gets several chunks.
+constexpr int kQueues = 8;
 
-    f32x16 sa[2], sb[2];
-    {
-        const int k0 = step_key0(0);
-        issue_k(0, k0);
-        issue_v(0, k0);
-        if (nsteps > 1) issue_k(1, step_key0(1));
-        wait_vmcnt<0>();
-        tile_barrier();
-        fwd_qk<D>(skb[0], off, qf, sa);
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds_addr(sdb[0]), sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap, rm,
-                                           0 >= a.nfull);
-    }
-    // One pipelined step: exponentials and PV of step t (scores in sc), QK^T
-    // and mask of step t+1 (into sn).  Unrolled by two below so that sc and
-    // sn swap roles without register copies.
-    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t) {
-        wait_vmcnt<0>();
-        tile_barrier();
-        OperandOffsets<D> offt = off;  // opaque per step: derived offsets are not hoisted
-        asm volatile("" : "+v"(offt.k), "+v"(offt.v));
-        const int key_next = step_key0(t + 1);
-        if (t + 2 < nsteps) issue_k(t + 2, step_key0(t + 2));
-        issue_v(t + 1, key_next);
+// Quotient k / d for 0 <= k < 2^31 and d >= 1, with m = ceil(2^32 / d)
+// computed on the host (d >= 2; d = 1 is passed through): the estimate is
+// q or q + 1.
+__device__ inline int div_by(int k, int d, uint32_t m) {
+    if (d == 1) return k;
+    int q = (int)(((uint64_t)(uint32_t)k * m) >> 32);
+    if ((int64_t)q * d > k) --q;
+    return q;
+}
 
-        const float m_use = fwd_max_update<D, kMods>(sc, o, m, l, a.scale_log2);
-        bf16x8 pb[2][2];
-        // next step's QK^T products, interleaved with this step's exponentials
-        fwd_qk<D>(skb[(t + 1) & 1], offt, qf, sn);
-        fwd_exp(sc, pb, l, c_mul, m_use);
-        // this step's PV products, interleaved with the next step's mask
-        fwd_pv<D>(svb[t & 1], offt, pb, o);
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds_addr(sdb[(t + 1) & 1]), sn, key_next, a.qpos, a.scale, a.slope, a.cap,
-                                           a.inv_cap, rm, ((t + 1) >> 1) >= a.nfull);
-        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
-    };
-    auto last = [&](f32x16 (&sc)[2], int t) {
-        wait_vmcnt<0>();
-        tile_barrier();
-        const float m_use = fwd_max_update<D, kMods>(sc, o, m, l, a.scale_log2);
-        bf16x8 pb[2][2];
-        fwd_exp(sc, pb, l, c_mul, m_use);
-        fwd_pv<D>(svb[t & 1], off, pb, o);
-    };
-    int t = 0;
-    for (; t + 2 < nsteps; t += 2) {
-        step(sa, sb, t);
-        step(sb, sa, t + 1);
+struct ItemOrder {
+    int nitems;  // B * H * QT, within int32 (checked on the host)
+    int Q, queue, cl;
+    const AttnParams &p;
+
+    __device__ ItemOrder(const AttnParams &p_, int G) : p(p_) {
+        nitems = p.mask_b * p.nt * p.ord_r;
+        Q = G < kQueues ? G : kQueues;
+        queue = blockIdx.x % Q;
+        cl = p.ord_chunk_log2;
     }
-    if (nsteps - t == 2) {
-        step(sa, sb, t);
-        last(sb, t + 1);
-    } else {
-        last(sa, t);
+    // Item of this queue's i-th grab (>= nitems: the queue is empty).
+    __device__ int item(int i) const {
+        const int64_t k = (((int64_t)queue + (int64_t)Q * (i >> cl)) << cl) + (i & ((1 << cl) - 1));
+        return k < nitems ? (int)k : nitems;
+    }
+    // Blocks of 2^cl entries times R heads, head-major inside a block; the
+    // last block holds the remaining P entries.
+    __device__ void decode(int k, int &e, int &rem) const {
+        const int cr = p.ord_r << cl;
+        const int full_items = p.ord_nblk * cr;
+        if (k < full_items) {
+            const int blk = div_by(k, cr, p.ord_m_cr), w = k - blk * cr;
+            rem = w >> cl;
+            e = (blk << cl) + (w & ((1 << cl) - 1));
+        } else {
+            const int w = k - full_items;
+            rem = div_by(w, p.ord_p, p.ord_m_p);
+            e = (p.ord_nblk << cl) + (w - rem * p.ord_p);
+        }
+    }
+};
+
+template <bool ALIBI, bool SOFTCAP>
+__device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &rec, FwdArgs &a) {
+    const int nt = p.nt;
+    const int packed = min(max(rec.packed, 0), p.mask_b * nt - 1);
+    a.bm = packed / nt;
+    a.row = packed - a.bm * nt;
+    a.b = p.mask_b == 1 ? rem / p.H : a.bm;
+    a.h = p.mask_b == 1 ? rem % p.H : rem;
+    a.kb = static_cast<const __bf16 *>(p.k) + a.b * p.k_sb + a.h * p.k_sh;
+    a.vb = static_cast<const __bf16 *>(p.v) + a.b * p.v_sb + a.h * p.v_sh;
+    a.fidx = p.full_kv_idx + (int64_t)packed * nt;
+    a.pidx = p.kv_idx + (int64_t)packed * nt;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)a.bm * p.T : nullptr;
+    a.nfull = min(max(rec.nfull, 0), nt);
+    a.ntiles = a.nfull + min(max(rec.npart, 0), nt);
+    a.first = clamp_tile(rec.first, nt);
+    a.nt = nt;
+    a.qpos = a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * kLog2e;
+    a.slope = ALIBI ? p.alibi_slopes[a.h] : 0.0f;
+    a.cap = SOFTCAP ? p.softcap : 1.0f;
+    a.inv_cap = 1.0f / a.cap;
+}
+
+// Entries 0..127 of the query-tile row's tile list (full tiles first, then
+// partial ones), one per lane in two registers, so that a step finds its key
+// tile with one cross-lane read instead of a dependent memory load.  Longer
+// lists (beyond 128 visible tiles in one row) read the rest from memory.
+struct TileList {
+    int lo, hi;  // entries lane and 64 + lane
+};
+
+__device__ inline int list_entry(const FwdArgs &a, int e) {
+    int v = 0;
+    if (e < a.nfull)
+        v = a.fidx[e];
+    else if (e < a.ntiles)
+        v = a.pidx[e - a.nfull];
+    return clamp_tile(v, a.nt);
+}
+
+__device__ inline int tile_at(const TileList &tl, const FwdArgs &a, int it) {
+    if (it >= 128)
+        return clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull), a.nt);
+    return __builtin_amdgcn_readlane(it < 64 ? tl.lo : tl.hi, it & 63);
+}
+
+// Per-lane row data loaded at the start of an item: the query's document
+// range and id.
+struct RowLoad {
+    int ds, de, docq;
+};
+
+// Row view of the mask (see make_row_mask) from the loaded row data; returns
+// the mode the row needs (uniform over the workgroup: the document-range
+// sentinel marks whole mask rows).
+__device__ inline int finish_row_mask(const AttnParams &p, int qpos, const RowLoad &rl, int window, RowMask &rm) {
+    int ds = rl.ds, de = rl.de;
+    const bool gather = ds < 0;
+    if (gather) {
+        ds = 0;
+        de = p.T - 1;
+    }
+    rm.docq = rl.docq;
+    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1, de);
+    int lo = ds;
+    bool sinks = false;
+    if (p.mask_flags & BSM_MASK_WINDOW) {
+        const int64_t wlo = (int64_t)qpos - (int64_t)window + 1;
+        if (wlo > lo) lo = wlo > p.T ? p.T : (int)wlo;
+        sinks = (p.mask_flags & BSM_MASK_SINKS) && p.sinks > 0;
+    }
+    rm.lo = lo;
+    rm.hi = hi;
+    rm.slo = ds;
+    rm.shi = sinks ? min(p.sinks - 1, hi) : ds - 1;
+    return __builtin_amdgcn_readfirstlane(gather ? kGather : sinks ? kSinks : kPlain);
+}
+
+// LDS of the forward: double-buffered 64-key halves of K and V and the
+// keys' document ids.
+template <int D>
+struct FwdSmem {
+    __bf16 k[2][kHalf * D];  // keys, rows swizzled by fk
+    __bf16 v[2][kHalf * D];  // values, rows swizzled by fv
+    int32_t doc[2][kHalf];   // document ids of the keys
+};
+
+// Starts an item: copies of K and V of step 0 and K of step 1 (the two
+// halves of the first listed tile) into buffers 0 / 0 / 1, and loads of the
+// query rows, the tile list and the row data.  Every item has an even
+// number of steps, so each item starts on buffer 0.
+template <int D>
+__device__ inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, bf16x8 (&qf)[D / 16],
+                                  TileList &tl, RowLoad &rl) {
+    if (a.ntiles > 0) {
+        const int k0 = a.first * kTile;
+        if (a.doc) {
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0);
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k0 + kHalf);
+        }
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st);
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)(k0 + kHalf) * p.k_st, p.k_st);
+    }
+    const int hl = (threadIdx.x & 63) >> 5;
+    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + a.b * p.q_sb + a.h * p.q_sh + (int64_t)a.qpos * p.q_st;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qrow + st * 16 + hl * 8);
+    const int lane = threadIdx.x & 63;
+    tl.lo = list_entry(a, lane);
+    tl.hi = a.ntiles > 64 ? list_entry(a, 64 + lane) : 0;
+    rl.ds = 0;
+    rl.de = p.T - 1;
+    rl.docq = 0;
+    if (a.doc) {
+        const int32_t *dr = p.doc_range + ((int64_t)a.bm * p.T + a.qpos) * 2;
+        rl.ds = dr[0];
+        rl.de = dr[1];
+        rl.docq = a.doc[a.qpos];
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
-    // Double-buffered half tiles.  Separate LDS objects per role so that no
-    // compiler-inserted wait ties reads of one to copies into another.
-    __shared__ __attribute__((aligned(1024))) __bf16 skb[2][kHalf * D];  // keys, rows swizzled by fk
-    __shared__ __attribute__((aligned(1024))) __bf16 svb[2][kHalf * D];  // values, rows swizzled by fv
-    __shared__ __attribute__((aligned(16))) int32_t sdb[2][kHalf];       // document ids of the keys
-
-    const int nt = p.nt;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / nt;
-    const int i = nt - 1 - (wg % nt);  // later query tiles first: under a causal
-                                       // mask they carry the most tiles
-    const int b = bh / p.H, h = bh % p.H;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
-    const int n = lane & 31, hl = lane >> 5;
-    const int qpos = i * kTile + wv * 32 + n;
-
-    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
-    const int bm = p.mask_b == 1 ? 0 : b;
-    const int64_t row = (int64_t)bm * nt + i;
-
-    FwdArgs a;
-    a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
-    a.vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
-    a.k_st = p.k_st;
-    a.v_st = p.v_st;
-    // Counts and indices are clamped to the grid so that a corrupt block mask
-    // gives wrong numbers instead of out-of-bounds reads.
-    a.nfull = min(max(load_uniform(p.full_kv_num + row), 0), nt);
-    const int npart = min(max(load_uniform(p.kv_num + row), 0), nt);
-    a.fidx = p.full_kv_idx + row * nt;
-    a.pidx = p.kv_idx + row * nt;
-    a.nt = nt;
-    a.qpos = qpos;
-    a.scale = p.scale;
-    a.scale_log2 = p.scale * kLog2e;
-    a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
-    a.cap = SOFTCAP ? p.softcap : 1.0f;
-    a.inv_cap = 1.0f / a.cap;
-    const int nsteps = 2 * (a.nfull + npart);  // 64-key steps
-
-    const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
-    a.doc = doc_on ? p.doc_ids + (int64_t)bm * p.T : nullptr;
-    RowMask rm;
-    const int mode = make_row_mask(p, bm, qpos, rm);
-
-    OperandOffsets<D> off;
-    operand_offsets<D>(off);
-
-    bf16x8 qf[D / 16];
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
-        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
-
-    f32x16 o[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float m = -INFINITY, l = 0.0f;
-    wait_vmcnt<0>();  // Q, the document range and id are in registers before any tile copy
-
-    if (mode == kGather)
-        fwd_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
-    else if (mode == kSinks)
-        fwd_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
-    else
-        fwd_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, off, skb, svb, sdb, nsteps, o, m, l);
-
+// Output of a finished item: out = o / l as bf16, lse = (m + log2 l) ln 2.
+template <int D>
+__device__ inline void store_item(const AttnParams &p, const FwdArgs &a, const f32x16 (&o)[D / 32], float m,
+                                  float l) {
+    const int hl = (threadIdx.x & 63) >> 5;
     const float l_tot = l + __shfl_xor(l, 32);
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    __bf16 *ob = static_cast<__bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qpos * p.o_st;
+    const float inv = l_tot > 0.0f ? fast_rcp(l_tot) : 0.0f;
+    __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh + (int64_t)a.qpos * p.o_st;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -348,25 +372,209 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
             *reinterpret_cast<u32x2 *>(ob + db * 32 + g * 8 + hl * 4) = w;
         }
     }
-    if (hl == 0) {
-        const float lse = l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
-        p.lse[((int64_t)b * p.H + h) * p.T + qpos] = lse;
-    }
+    if (hl == 0)
+        p.lse[((int64_t)a.b * p.H + a.h) * p.T + a.qpos] =
+            l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
+
+// The double-buffered, software-pipelined loop over one item's listed tiles
+// (in 64-key steps); the caller has waited for the item's first copies and
+// loads and passed a workgroup barrier.  Step t's scores (modified, masked)
+// and their row maximum are computed during step t-1.  At the top of step t
+// the copies issued at the top of step t-1 -- K(t+1) and V(t) -- have
+// landed; the barrier also certifies that every wave has finished step t-1,
+// freeing K buffer t%2 (last read for K(t)) and V buffer (t+1)%2 (last read
+// for V(t-1)) for K(t+2) and V(t+1).
+//
+// A step first settles the online-softmax reference (moving it, and
+// rescaling o and l, only when the new maximum exceeds it by more than the
+// threshold), then runs one branch-free block: QK^T products of step t+1,
+// exponentials and PV products of step t, score modifications, mask and row
+// maximum of step t+1 -- so the compiler can interleave matrix-core products
+// with all of the step's vector work.  Steps whose next tile is full and
+// steps whose next tile is partial run in separate loops (the tile list
+// holds full tiles first), so the elementwise mask needs no branch.
+//
+// The item's output is written at its end.
+template <int D, bool ALIBI, bool SOFTCAP, int MODE>
+__device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
+                                const bf16x8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
+                                f32x16 (&o)[D / 32], float &m, float &l) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const float c_mul = kMods ? 1.0f : a.scale_log2;
+    const int nsteps = 2 * a.ntiles;
+    auto reset = [&]() {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+        m = -INFINITY;
+        l = 0.0f;
+    };
+    if (nsteps == 0) {  // nothing visible: out = 0, lse = -inf
+        reset();
+        store_item<D>(p, a, o, m, l);
+        return;
+    }
+    auto step_key0 = [&](int t) { return tile_at(tl, a, t >> 1) * kTile + (t & 1) * kHalf; };
+    auto issue_k = [&](int t, int key0) {
+        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st);
+    };
+    auto issue_v = [&](int t, int key0) {
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[t & 1], a.vb + (int64_t)key0 * p.v_st, p.v_st);
+    };
+    // Row maximum of a step in the log2 domain (without score modifications
+    // the scale is applied here and folded into the exponentials).
+    auto step_max = [&](const f32x16 (&s)[2]) {
+        const float mx = row_max(s);
+        return kMods ? mx : mx * a.scale_log2;
+    };
+    // Moves the reference to the step maximum mx when it grew by more than
+    // the threshold anywhere in the wave (o and l follow); returns the
+    // reference the exponentials subtract.
+    auto settle = [&](float mx) {
+        if (__any(mx > m + kRescaleThreshold)) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2(m - (m_new == -INFINITY ? 0.0f : m_new));
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            m = m_new;
+        }
+        return (m == -INFINITY) ? 0.0f : m;
+    };
+
+    f32x16 sa[2], sb[2];
+    float mx;  // row maximum of the current step's scores
+    const int k0 = a.first * kTile;
+    int key_ahead = k0 + kHalf;  // first key of step t+1 at the top of step t
+    fwd_qk<D>(sm.k[0], off, qf, sa);
+    row_mods<ALIBI, SOFTCAP>(sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap);
+    if (a.nfull == 0) row_mask_flat<MODE>(lds_addr(sm.doc[0]), sa, k0, rm);
+    mx = step_max(sa);
+
+    auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t, auto next_masked, auto first_step) {
+        wait_vmcnt<0>();
+        tile_barrier();
+        OperandOffsets<D> offt = off;  // opaque per step: derived offsets are not hoisted
+        asm volatile("" : "+v"(offt.k), "+v"(offt.v));
+        // first keys of steps t+1 (carried from the previous step) and t+2
+        const int key_next = key_ahead;
+        key_ahead = ((t + 2) & 1) ? key_ahead + kHalf : (t + 2 < nsteps ? step_key0(t + 2) : 0);
+        if (t + 2 < nsteps) issue_k(t + 2, key_ahead);
+        issue_v(t + 1, key_next);
+        if (decltype(first_step)::value) reset();
+        const float m_use = settle(mx);
+
+        bf16x8 pb[2][2];
+        fwd_qk<D>(sm.k[(t + 1) & 1], offt, qf, sn);
+        fwd_exp(sc, pb, l, c_mul, m_use);
+        fwd_pv<D>(sm.v[t & 1], offt, pb, o);
+        row_mods<ALIBI, SOFTCAP>(sn, key_next, a.qpos, a.scale, a.slope, a.cap, a.inv_cap);
+        if (decltype(next_masked)::value) row_mask_flat<MODE>(lds_addr(sm.doc[(t + 1) & 1]), sn, key_next, rm);
+        mx = step_max(sn);
+        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
+    };
+    // step 0; its next step is the second half of the first tile
+    if (a.nfull > 0)
+        step(sa, sb, 0, std::false_type(), std::true_type());
+    else
+        step(sa, sb, 0, std::true_type(), std::true_type());
+    sa[0] = sb[0];  // the current scores live in sa between loops
+    sa[1] = sb[1];
+    // Steps t < t_switch have a full next tile.
+    const int t_switch = min(max(2 * a.nfull - 1, 1), nsteps - 1);
+    int t = 1;
+    auto phase = [&](int t_end, auto next_masked) {
+        for (; t + 1 < t_end; t += 2) {
+            step(sa, sb, t, next_masked, std::false_type());
+            step(sb, sa, t + 1, next_masked, std::false_type());
+        }
+        if (t < t_end) {
+            step(sa, sb, t, next_masked, std::false_type());
+            sa[0] = sb[0];
+            sa[1] = sb[1];
+            ++t;
+        }
+    };
+    phase(t_switch, std::false_type());
+    phase(nsteps - 1, std::true_type());
+    // last step (t = nsteps - 1)
+    wait_vmcnt<0>();
+    tile_barrier();
+    const float m_use = settle(mx);
+    bf16x8 pb[2][2];
+    fwd_exp(sa, pb, l, c_mul, m_use);
+    fwd_pv<D>(sm.v[1], off, pb, o);
+    store_item<D>(p, a, o, m, l);
+}
+
+// One item per workgroup (workgroups past the last item exit at once).
+template <int D, bool ALIBI, bool SOFTCAP>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
+    const ItemOrder ord(p, kQueues);
+    const int k = ord.item(blockIdx.x / ord.Q);
+    if (k >= ord.nitems) return;
+    const int window = (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0;
+    int e, rem;
+    ord.decode(k, e, rem);
+    FwdArgs cur;
+    item_args<ALIBI, SOFTCAP>(p, rem, load_rec(p.kv_order, e), cur);
+    OperandOffsets<D> off;
+    operand_offsets<D>(off);
+    bf16x8 qf[D / 16];
+    TileList tl;
+    RowLoad rl;
+    item_start<D>(p, sm, cur, qf, tl, rl);
+    f32x16 o[D / 32];
+    float m = -INFINITY, l = 0.0f;
+    wait_vmcnt<0>();  // the item's first tiles, query rows, tile list and row data
+    tile_barrier();
+    RowMask rm;
+    const int mode = finish_row_mask(p, cur.qpos, rl, window, rm);
+    if (mode == kGather)
+        item_run<D, ALIBI, SOFTCAP, kGather>(p, cur, tl, rm, qf, off, sm, o, m, l);
+    else if (mode == kSinks)
+        item_run<D, ALIBI, SOFTCAP, kSinks>(p, cur, tl, rm, qf, off, sm, o, m, l);
+    else
+        item_run<D, ALIBI, SOFTCAP, kPlain>(p, cur, tl, rm, qf, off, sm, o, m, l);
+}
+
+
+// ceil(2^32 / d) for d >= 1.
+uint32_t div_magic(int64_t d) { return d <= 1 ? 0xffffffffu : (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d); }
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
-    const dim3 grid(p.B * p.H * p.nt), block(kThreads);
+    const int64_t nitems = (int64_t)p.B * p.H * p.nt;
+    AttnParams q = p;
+    q.ord_r = p.mask_b == 1 ? p.B * p.H : p.H;
+    // chunks of up to 16 entries, at least four per queue
+    int cl = 4;
+    while (cl > 0 && ((int64_t)1 << cl) * 4 * kQueues > nitems) --cl;
+    q.ord_chunk_log2 = cl;
+    const int nrows = p.mask_b * p.nt;
+    q.ord_nblk = nrows >> cl;
+    q.ord_p = nrows - (q.ord_nblk << cl);
+    q.ord_m_cr = div_magic((int64_t)q.ord_r << cl);
+    q.ord_m_p = div_magic(q.ord_p);
+    // one workgroup per (queue, grab index) pair; see fwd_kernel
+    const int64_t nchunks = (nitems + (1 << cl) - 1) >> cl;
+    const dim3 grid((unsigned)((kQueues * ((nchunks + kQueues - 1) / kQueues)) << cl)), block(kThreads);
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
     if (alibi && cap)
-        hipLaunchKernelGGL((fwd_kernel<D, true, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, true, true>), grid, block, 0, stream, q);
     else if (alibi)
-        hipLaunchKernelGGL((fwd_kernel<D, true, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, true, false>), grid, block, 0, stream, q);
     else if (cap)
-        hipLaunchKernelGGL((fwd_kernel<D, false, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, false, true>), grid, block, 0, stream, q);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, false, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((fwd_kernel<D, false, false>), grid, block, 0, stream, q);
     return hipGetLastError();
 }
 

@@ -37,6 +37,11 @@ bool bad_T(int64_t T) { return T <= 0 || T % bsm::kTile != 0 || T > kMaxT; }
 
 int32_t n_chunks(int32_t T) { return (T + 255) / 256; }
 
+// Blocks of the work orders (kOrderBlock rows of one mask batch each).
+int64_t order_blocks(int32_t T, int32_t mask_b) {
+    return (int64_t)mask_b * ((T / bsm::kTile + bsm::kOrderBlock - 1) / bsm::kOrderBlock);
+}
+
 bsm_status check_spec(const bsm_mask_spec *spec) {
     if (!spec) return fail(BSM_E_INVALID, "mask spec is NULL");
     if (spec->flags & ~kMaskFlagsAll) return fail(BSM_E_INVALID, "unknown mask flag bits 0x%x", spec->flags);
@@ -57,10 +62,14 @@ bsm_status check_block_mask(const bsm_block_mask *bm, bool need_transposed, cons
     if (!bm) return fail(BSM_E_INVALID, "block mask is NULL");
     if ((spec->flags & BSM_MASK_DOCUMENT) && !bm->doc_range)
         return fail(BSM_E_INVALID, "DOCUMENT mask needs the block mask's doc_range array");
-    if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
+    if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices ||
+        !bm->kv_order)
         return fail(BSM_E_INVALID, "block mask row arrays must be non-NULL");
-    if (need_transposed &&
-        (!bm->q_num_blocks || !bm->q_indices || !bm->full_q_num_blocks || !bm->full_q_indices))
+    if (reinterpret_cast<uintptr_t>(bm->kv_order) % 16 != 0 ||
+        (need_transposed && reinterpret_cast<uintptr_t>(bm->q_order) % 16 != 0))
+        return fail(BSM_E_INVALID, "block mask work orders must be 16-byte aligned");
+    if (need_transposed && (!bm->q_num_blocks || !bm->q_indices || !bm->full_q_num_blocks ||
+                            !bm->full_q_indices || !bm->q_order))
         return fail(BSM_E_INVALID, "block mask column arrays must be non-NULL");
     return BSM_OK;
 }
@@ -133,6 +142,8 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
     p.full_q_num = bm->full_q_num_blocks;
     p.full_q_idx = bm->full_q_indices;
     p.doc_range = (spec->flags & BSM_MASK_DOCUMENT) ? bm->doc_range : nullptr;
+    p.kv_order = bm->kv_order;
+    p.q_order = bm->q_order;
 }
 
 bsm_status hip_status(hipError_t e, const char *what) {
@@ -148,7 +159,7 @@ size_t bsm_block_mask_workspace_bytes(int32_t seq_len, int32_t mask_b) {
     if (bad_T(seq_len) || mask_b < 1) return 0;
     const int64_t nt = seq_len / bsm::kTile;
     return align256((size_t)mask_b * n_chunks(seq_len) * sizeof(int32_t)) +
-           align256((size_t)mask_b * nt * nt);
+           align256((size_t)mask_b * nt * nt) + 2 * align256((size_t)order_blocks(seq_len, mask_b) * sizeof(int32_t));
 }
 
 bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask *out,
@@ -157,6 +168,8 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     if (st != BSM_OK) return st;
     st = check_block_mask(out, true, spec);
     if (st != BSM_OK) return st;
+    if ((int64_t)spec->mask_b * (spec->seq_len / bsm::kTile) > INT32_MAX)
+        return fail(BSM_E_INVALID, "mask_b * T/128 exceeds the int32 work-order range");
     const size_t need = bsm_block_mask_workspace_bytes(spec->seq_len, spec->mask_b);
     if (!workspace || workspace_bytes < need)
         return fail(BSM_E_WORKSPACE, "block-mask workspace needs %zu bytes, got %zu%s", need,
@@ -175,7 +188,12 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     p.out = *out;
     char *ws = static_cast<char *>(workspace);
     p.nonmono = reinterpret_cast<int32_t *>(ws);
-    p.cls = reinterpret_cast<uint8_t *>(ws + align256((size_t)p.mask_b * p.nchunks * sizeof(int32_t)));
+    const size_t off_cls = align256((size_t)p.mask_b * p.nchunks * sizeof(int32_t));
+    p.cls = reinterpret_cast<uint8_t *>(ws + off_cls);
+    const size_t off_order = off_cls + align256((size_t)p.mask_b * p.nt * p.nt);
+    p.order_ws = reinterpret_cast<int32_t *>(ws + off_order);
+    p.order_ws_stride =
+        (int32_t)(align256((size_t)order_blocks(spec->seq_len, spec->mask_b) * sizeof(int32_t)) / sizeof(int32_t));
     return hip_status(bsm::launch_build_block_mask(p, static_cast<hipStream_t>(stream)),
                       "bsm_build_block_mask launch");
 }

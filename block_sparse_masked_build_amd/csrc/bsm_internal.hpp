@@ -12,6 +12,11 @@ namespace bsm {
 constexpr int kTile = 128;          // mask granularity (query and key tiles)
 constexpr int kTilePairs = kTile * kTile;
 
+// Work orders: rows (columns) are ordered in blocks of kOrderBlock; distinct
+// sort keys of the blocks (longer blocks share the last key).
+constexpr int kOrderBlock = 16;
+constexpr int kOrderKeys = 8192;
+
 // Tile classes in the per-tile class matrix.
 enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
 
@@ -27,6 +32,8 @@ struct MaskBuildParams {
     bsm_block_mask out;
     uint8_t *cls;        // [mask_b, nt, nt]
     int32_t *nonmono;    // [mask_b, nchunks]
+    int32_t *order_ws;   // two arrays of order_ws_stride ints: sorted blocks of the row / column orders
+    int32_t order_ws_stride;
 };
 
 struct AttnParams {
@@ -44,6 +51,7 @@ struct AttnParams {
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
     const int32_t *q_num, *q_idx, *full_q_num, *full_q_idx;
     const int32_t *doc_range;   // [mask_b, T, 2] (first, last) of each position's document, or NULL
+    const int32_t *kv_order, *q_order;  // work orders [mask_b * nt, 4]: longest rows / columns first
     // tensors (bf16, strides in elements)
     const void *q; int64_t q_sb, q_sh, q_st;
     const void *k; int64_t k_sb, k_sh, k_st;
@@ -56,6 +64,10 @@ struct AttnParams {
     float *lse;      // [B, H, T]
     float *delta;    // [B, H, T] (backward workspace): <dO, out> per query
     float *lse2;     // [B, H, T] (backward workspace): lse * log2(e), 0 where lse = -inf
+    // forward item order: items per work-order entry, full blocks, entries in
+    // the last block, and division magic numbers (set by the launcher)
+    int32_t ord_r, ord_chunk_log2, ord_nblk, ord_p;
+    uint32_t ord_m_cr, ord_m_p;
 };
 
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);

@@ -253,6 +253,136 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(MaskBuildParams p) {
     }
 }
 
+// Work orders: the query-tile rows (block 0) and key-tile columns (block 1)
+// of every mask batch in the order the attention kernels take them.  Rows
+// are grouped in blocks of kOrderBlock consecutive rows of one mask batch
+// (the last block of a batch may be shorter) -- neighbouring rows read
+// mostly the same key and value tiles.  Blocks go by decreasing key
+// min(visible tiles of the block, kOrderKeys - 1), ties in ascending block
+// index, rows inside a block in ascending order: the longest work starts
+// first and short blocks fill the end of a launch.  Entry e of kv_order is
+// the record (bm * nt + i, full tiles, partial tiles, first listed tile) of
+// the e-th row in this order, so a kernel starts a row with one load.
+//
+// A counting sort of the blocks: histogram of the keys in LDS, exclusive
+// scan from the largest key down, one wave places the blocks in index order
+// (for each key present in a chunk of 64 blocks, the lanes holding it get
+// consecutive slots in lane order), then a scan of the block sizes gives
+// each block its first entry.
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderPer = kOrderKeys / kOrderThreads;
+
+// Exclusive prefix sum of one value per thread over the workgroup; returns
+// this thread's prefix and sets total.
+__device__ inline int block_exclusive_scan(int v, int *s_wsum, int &total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int up = __shfl_up(incl, d);
+        if (lane >= d) incl += up;
+    }
+    __syncthreads();  // s_wsum free from any previous use
+    if (lane == 63) s_wsum[wv] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+    for (int w = 0; w < kOrderThreads / 64; ++w) {
+        if (w < wv) before += s_wsum[w];
+        total += s_wsum[w];
+    }
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(MaskBuildParams p) {
+    __shared__ int s_hist[kOrderKeys];
+    __shared__ int s_wsum[kOrderThreads / 64];
+    const bool cols = blockIdx.x == 1;
+    const int32_t *num = cols ? p.out.q_num_blocks : p.out.kv_num_blocks;
+    const int32_t *fnum = cols ? p.out.full_q_num_blocks : p.out.full_kv_num_blocks;
+    const int32_t *idx = cols ? p.out.q_indices : p.out.kv_indices;
+    const int32_t *fidx = cols ? p.out.full_q_indices : p.out.full_kv_indices;
+    int32_t *order = cols ? p.out.q_order : p.out.kv_order;
+    int32_t *sorted = p.order_ws + (cols ? p.order_ws_stride : 0);  // block at each sorted position
+    const int nt = p.nt;
+    const int bpb = (nt + kOrderBlock - 1) / kOrderBlock;  // blocks per mask batch
+    const int nb = p.mask_b * bpb;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    auto block_rows = [&](int g, int &r0, int &n) {
+        const int bm = g / bpb, j = g - bm * bpb;
+        r0 = bm * nt + j * kOrderBlock;
+        n = min(kOrderBlock, nt - j * kOrderBlock);
+    };
+    auto key_of = [&](int g) {
+        int r0, n;
+        block_rows(g, r0, n);
+        int tot = 0;
+        for (int r = r0; r < r0 + n; ++r) tot += num[r] + fnum[r];
+        return min(tot, kOrderKeys - 1);
+    };
+
+    for (int x = tid; x < kOrderKeys; x += kOrderThreads) s_hist[x] = 0;
+    __syncthreads();
+    for (int g = tid; g < nb; g += kOrderThreads) atomicAdd(&s_hist[key_of(g)], 1);
+    __syncthreads();
+    // Thread t owns keys kOrderKeys-1-kOrderPer*t down to kOrderKeys-kOrderPer*(t+1).
+    int v[kOrderPer], sum = 0;
+#pragma unroll
+    for (int x = 0; x < kOrderPer; ++x) {
+        v[x] = s_hist[kOrderKeys - 1 - (kOrderPer * tid + x)];
+        sum += v[x];
+    }
+    int total;
+    int start = block_exclusive_scan(sum, s_wsum, total);
+#pragma unroll
+    for (int x = 0; x < kOrderPer; ++x) {
+        s_hist[kOrderKeys - 1 - (kOrderPer * tid + x)] = start;  // first slot of the key
+        start += v[x];
+    }
+    __syncthreads();
+    if (wv == 0) {
+        for (int g0 = 0; g0 < nb; g0 += 64) {
+            const int g = g0 + lane;
+            const int key = g < nb ? key_of(g) : -1;
+            unsigned long long todo = __ballot(g < nb);
+            while (todo) {
+                const int src = __builtin_ctzll(todo);
+                const int kk = __shfl(key, src);
+                const unsigned long long same = __ballot(key == kk);
+                const int base = s_hist[kk];
+                if (key == kk) sorted[base + __builtin_popcountll(same & ((1ull << lane) - 1))] = g;
+                __builtin_amdgcn_wave_barrier();
+                if (lane == src) s_hist[kk] = base + __builtin_popcountll(same);
+                __builtin_amdgcn_wave_barrier();
+                todo &= ~same;
+            }
+        }
+    }
+    __threadfence_block();
+    __syncthreads();
+    // Entries of the rows of each block, in sorted block order.
+    int run = 0;  // entries before the current chunk of sorted positions
+    for (int pos0 = 0; pos0 < nb; pos0 += kOrderThreads) {
+        const int pos = pos0 + tid;
+        int r0 = 0, n = 0;
+        if (pos < nb) block_rows(sorted[pos], r0, n);
+        int chunk_total;
+        const int first = run + block_exclusive_scan(n, s_wsum, chunk_total);
+        for (int x = 0; x < n; ++x) {
+            const int e = r0 + x;
+            const int nf = fnum[e], np = num[e];
+            const int ft = nf > 0 ? fidx[(int64_t)e * nt] : (np > 0 ? idx[(int64_t)e * nt] : 0);
+            int4 rec;
+            rec.x = e;
+            rec.y = nf;
+            rec.z = np;
+            rec.w = ft;
+            reinterpret_cast<int4 *>(order)[first + x] = rec;
+        }
+        run += chunk_total;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream) {
@@ -262,6 +392,7 @@ hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream)
     }
     hipLaunchKernelGGL(rows_kernel, dim3(p.nt, p.mask_b), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(cols_kernel, dim3(p.nt, p.mask_b), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(order_kernel, dim3(2), dim3(kOrderThreads), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -108,8 +108,24 @@ typedef struct {
  *                                            ids are not, which makes the
  *                                            attention kernels compare ids key
  *                                            by key instead
- * bsm_build_block_mask writes all nine; the forward reads the kv_* four and
- * doc_range, the backward reads all nine. */
+ *   kv_order            [mask_b * QT, 4]     (16-byte aligned) work order of the
+ *                                            query-tile rows:
+ *                                            entry e describes the row (bm, i)
+ *                                            with the e-th largest
+ *                                            min(kv_num + full_kv_num, 8191),
+ *                                            ties in ascending bm * QT + i, as
+ *                                            (bm * QT + i, full_kv_num,
+ *                                            kv_num, first listed key tile:
+ *                                            the first full one if any, else
+ *                                            the first partial one, else 0)
+ *   q_order             [mask_b * KT, 4]     the same for the key-tile columns
+ *                                            (q_num + full_q_num; first listed
+ *                                            query tile)
+ * The work orders are a schedule, not part of the mask: the attention
+ * kernels start the rows (columns) with the most tiles first, so that the
+ * short ones fill the end of the launch.
+ * bsm_build_block_mask writes all eleven; the forward reads the kv_* five
+ * and doc_range, the backward reads all eleven. */
 typedef struct {
     int32_t *kv_num_blocks;
     int32_t *kv_indices;
@@ -120,6 +136,8 @@ typedef struct {
     int32_t *full_q_num_blocks;
     int32_t *full_q_indices;
     int32_t *doc_range;
+    int32_t *kv_order;
+    int32_t *q_order;
 } bsm_block_mask;
 
 typedef struct {

@@ -19,6 +19,7 @@ from .block_mask import (  # noqa: F401
     document_ranges,
     classify,
     block_mask_lists,
+    work_order,
     EMPTY, PARTIAL, FULL, TILE,
 )
 from .attention import (  # noqa: F401

@@ -20,7 +20,8 @@ MEAN_ABS = 2e-3
 LSE_MAX_ABS = 1e-3
 
 BM_NAMES = ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices",
-            "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices")
+            "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices",
+            "kv_order", "q_order")
 
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU visible")
 

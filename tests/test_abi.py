@@ -40,7 +40,7 @@ def _spec(**kw):
 
 
 def _bm(null=None):
-    v = [FAKE] * 9
+    v = [FAKE] * 11
     if null is not None:
         v[null] = None
     return BsmBlockMask(*v)
@@ -67,7 +67,7 @@ def test_build_rejects_bad_spec(kw, code):
 
 
 def test_build_rejects_null_outputs_and_small_workspace():
-    for i in range(8):
+    for i in list(range(8)) + [9, 10]:  # tile lists and work orders
         assert _build(_spec(), _bm(null=i)) == _lib.BSM_E_INVALID
     # doc_range is required only with the document term
     assert _build(_spec(flags=3, doc_ids=FAKE), _bm(null=8)) == _lib.BSM_E_INVALID
@@ -115,6 +115,7 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
     (dict(v=_t(ptr=0)), _lib.BSM_E_INVALID),
     (dict(lse=None), _lib.BSM_E_INVALID),
     (dict(bm=_bm(null=0)), _lib.BSM_E_INVALID),
+    (dict(bm=_bm(null=9)), _lib.BSM_E_INVALID),     # work order
     (dict(mod=BsmScoreMod(1, None, 0.0)), _lib.BSM_E_INVALID),        # ALiBi without slopes
     (dict(mod=BsmScoreMod(2, None, 0.0)), _lib.BSM_E_INVALID),        # cap must be > 0
     (dict(mod=BsmScoreMod(2, None, float("inf"))), _lib.BSM_E_INVALID),
