@@ -196,54 +196,6 @@ def work_records(num, idx, fnum, fidx) -> np.ndarray:
     return rec
 
 
-def block_mask_lists(counts: np.ndarray) -> dict:
-    """The eight tile-list arrays of a block mask, shaped [mask_b, 1, ...]
-    (head dim 1: one mask shared by all heads), and the two work orders,
-    flat [mask_b * n]."""
-    cls = classify(counts)
-    names = {}
-    out = {k: [] for k in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
-                           "full_kv_indices", "q_num_blocks", "q_indices",
-                           "full_q_num_blocks", "full_q_indices")}
-    for b in range(cls.shape[0]):
-        c = cls[b]
-        n, i = _lists(c, PARTIAL)
-        out["kv_num_blocks"].append(n)
-        out["kv_indices"].append(i)
-        n, i = _lists(c, FULL)
-        out["full_kv_num_blocks"].append(n)
-        out["full_kv_indices"].append(i)
-        n, i = _lists(c.T, PARTIAL)
-        out["q_num_blocks"].append(n)
-        out["q_indices"].append(i)
-        n, i = _lists(c.T, FULL)
-        out["full_q_num_blocks"].append(n)
-        out["full_q_indices"].append(i)
-    for k, v in out.items():
-        names[k] = np.stack(v)[:, None]
-    names["kv_order"] = work_records(names["kv_num_blocks"], names["kv_indices"],
-                                     names["full_kv_num_blocks"], names["full_kv_indices"])
-    names["q_order"] = work_records(names["q_num_blocks"], names["q_indices"],
-                                    names["full_q_num_blocks"], names["full_q_indices"])
-    return names
-
-
-def work_records(num, idx, fnum, fidx) -> np.ndarray:
-    """The work order as records: per entry (flat row index, full count,
-    partial count, first listed tile -- the first full one if any, else the
-    first partial one, else 0), int32 [mask_b * n, 4]."""
-    num = num.reshape(-1)
-    fnum = fnum.reshape(-1)
-    idx = idx.reshape(num.size, -1)
-    fidx = fidx.reshape(num.size, -1)
-    order = work_order(num + fnum)
-    rec = np.zeros((num.size, 4), dtype=np.int32)
-    for e, r in enumerate(order):
-        first = fidx[r, 0] if fnum[r] > 0 else (idx[r, 0] if num[r] > 0 else 0)
-        rec[e] = (r, fnum[r], num[r], first)
-    return rec
-
-
 # Work orders group rows in blocks of ORDER_BLOCK consecutive rows of one
 # mask batch; block sort keys are capped so that very long blocks tie.
 ORDER_BLOCK = 16

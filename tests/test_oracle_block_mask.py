@@ -202,6 +202,14 @@ def test_work_order_worked_examples():
     # two mask batches of 2 rows: batch 0's block (6 tiles) before batch 1's (5)
     assert oracle.work_order(np.array([[1, 5], [5, 0]])).tolist() == [0, 1, 2, 3]
     assert oracle.work_order(np.array([[1, 3], [5, 0]])).tolist() == [2, 3, 0, 1]
+    # block_mask_lists keeps the blocks of two mask batches apart: T = 1024
+    # (8 rows each), batch 0 one 128-token document per tile (the diagonal,
+    # 8 tiles), batch 1 one document (causal, 36 tiles): batch 1 goes first
+    docs = np.stack([np.repeat(np.arange(8), 128), np.zeros(1024, dtype=np.int64)])
+    bm = oracle.block_mask_lists(oracle.tile_counts(
+        MaskSpecData(1024, causal=True, document=True, doc_ids=docs.astype(np.int32))))
+    assert bm["kv_order"][:, 0].tolist() == list(range(8, 16)) + list(range(8))
+    assert bm["kv_order"][:, 1].tolist() == [0, 1, 2, 3, 4, 5, 6, 7] + [0] * 8
 
 
 def test_work_order_properties_random():
