@@ -13,18 +13,25 @@
 //    end-of-text flags, speedrun notes code listing) the visible keys of query
 //    q form at most two intervals: the main one [lo(q), hi(q)] with
 //    lo = max(doc start, q - window + 1) and hi = min(doc end, q or T-1), and
-//    a sink interval [doc start, min(sinks - 1, hi)].  A tile's pair count is
-//    then a sum of 128 interval overlaps -- exact, O(128) per tile.
+//    a sink interval [doc start, min(sinks - 1, hi)].  Merged when they touch,
+//    they are disjoint with a gap, so a tile is fully visible to a query only
+//    when one interval covers it and empty only when neither meets it: exact
+//    classes from two interval tests per (query, tile).
+//  * Document boundaries: one 64-way wave search from the tile's first query
+//    back to its document start and one from its last query on to its
+//    document end; every other document of the tile starts or ends inside it
+//    and is found in LDS.
 //  * Any other document ids take a general path that compares document ids
 //    key by key inside the causal/window intervals (still exact).
 //  * The document range [start, end] of every position is exported
 //    (doc_range) so the attention kernels can mask partial tiles with two
 //    interval compares per score; (-1, -1) marks rows without contiguous
 //    documents.
-//  * One workgroup per query-tile row; one lane per key tile; wave ballots and
-//    a cross-wave prefix sum compact the partial and full lists in ascending
-//    order.  A per-tile class byte is kept in the workspace and a second
-//    kernel compacts it per key-tile column the same way.
+//  * One workgroup per query-tile row; only the tiles between the row's lowest
+//    and highest visible key are classified, 64 at a time; wave ballots merge
+//    the four waves' row quarters and compact the partial and full lists in
+//    ascending order.  A per-tile class byte is kept in the workspace and a
+//    second kernel compacts it per key-tile column.
 #include "bsm_internal.hpp"
 
 namespace bsm {
@@ -33,26 +40,52 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-__device__ inline int64_t overlap(int64_t lo, int64_t hi, int64_t k0, int64_t k1) {
-    int64_t a = lo > k0 ? lo : k0;
-    int64_t b = hi < k1 ? hi : k1;
-    return b >= a ? (b - a + 1) : 0;
-}
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// First index t in [lo, hi) with doc[t] >= val (doc non-decreasing).
-__device__ inline int lower_bound_doc(const int32_t *doc, int lo, int hi, int32_t val) {
-    while (lo < hi) {
-        int mid = lo + ((hi - lo) >> 1);
-        if (doc[mid] < val) lo = mid + 1; else hi = mid;
+// First t in [lo, hi) with doc[t] > val (ABOVE) or doc[t] >= val (!ABOVE), or
+// hi if there is none; doc is non-decreasing on [lo, hi).  All 64 lanes of a
+// wave call it with the same arguments.  Each round probes 64 evenly spaced
+// positions and keeps the gap in which the predicate turns true, so n
+// positions take about log64(n) + 1 rounds of loads rather than log2(n)
+// dependent ones.
+template <bool ABOVE>
+__device__ inline int wave_search_doc(const int32_t *doc, int lo, int hi, int32_t val) {
+    const int lane = threadIdx.x & 63;
+    while (hi - lo > 64) {
+        const int step = (hi - lo + 63) >> 6;  // 64 probes cover [lo, hi)
+        const int t = lo + lane * step;
+        bool hit = true;                       // probes at or past hi count as hits
+        if (t < hi) {
+            const int32_t d = doc[t];
+            hit = ABOVE ? d > val : d >= val;
+        }
+        const unsigned long long m = __ballot(hit);
+        if (m == 0) {                          // every probe is below hi and misses
+            lo += 63 * step + 1;
+        } else {
+            const int f = __builtin_ctzll(m);
+            if (f == 0) return lo;
+            const int nhi = lo + f * step;     // a hit, or past hi
+            lo += (f - 1) * step + 1;          // probe f - 1 missed
+            hi = nhi < hi ? nhi : hi;
+        }
     }
-    return lo;
+    const int t = lo + lane;
+    bool hit = true;
+    if (t < hi) {
+        const int32_t d = doc[t];
+        hit = ABOVE ? d > val : d >= val;
+    }
+    const unsigned long long m = __ballot(hit);
+    return m ? lo + __builtin_ctzll(m) : hi;
 }
 
-// First index t in [lo, hi) with doc[t] > val (doc non-decreasing).
-__device__ inline int upper_bound_doc(const int32_t *doc, int lo, int hi, int32_t val) {
+// Same searches over a short array in LDS, one lane at a time.
+template <bool ABOVE>
+__device__ inline int lds_search_doc(const int32_t *a, int lo, int hi, int32_t val) {
     while (lo < hi) {
-        int mid = lo + ((hi - lo) >> 1);
-        if (doc[mid] <= val) lo = mid + 1; else hi = mid;
+        const int mid = lo + ((hi - lo) >> 1);
+        if (ABOVE ? a[mid] > val : a[mid] >= val) hi = mid; else lo = mid + 1;
     }
     return lo;
 }
@@ -107,120 +140,199 @@ __device__ inline void pad_tail(int32_t *idx, int from, int n) {
     for (int s = from + (int)threadIdx.x; s < n; s += kThreads) idx[s] = -1;
 }
 
+constexpr int kNone = 0x7fffffff;       // lower end of an empty interval (upper end -1)
+constexpr int kRowsPerWave = kTile / kWaves;  // 32
+
+// One workgroup per query-tile row.  The 128 rows' visible keys are reduced
+// to intervals in LDS; the tiles between the lowest and highest visible key
+// are then classified 64 at a time, lane = tile, each wave testing a quarter
+// of the rows, and wave ballots merge the quarters and compact the lists.
 __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
-    __shared__ int64_t s_alo[kTile], s_ahi[kTile], s_blo[kTile], s_bhi[kTile];
+    __shared__ i32x4 s_iv[kTile];
     __shared__ int32_t s_docq[kTile];
-    __shared__ int s_wp[kWaves], s_wf[kWaves];
-    __shared__ long long s_amin, s_amax, s_bmin, s_bmax;
+    __shared__ int s_ds0, s_deN;
+    __shared__ i32x4 s_ext[kTile / 64];
+    __shared__ unsigned long long s_any[2][kWaves], s_all[2][kWaves];
 
     const int i = blockIdx.x;
     const int b = blockIdx.y;
     const int T = p.T;
     const int nt = p.nt;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const bool causal = p.flags & BSM_MASK_CAUSAL;
     const bool document = p.flags & BSM_MASK_DOCUMENT;
     const bool windowed = p.flags & BSM_MASK_WINDOW;
     const bool sinks_on = windowed && (p.flags & BSM_MASK_SINKS) && p.sinks > 0;
     const int32_t *doc = document ? p.doc_ids + (int64_t)b * T : nullptr;
+    const int64_t w = windowed ? (int64_t)(*p.window) : 0;
+    const int q0 = i * kTile;
 
-    bool mono = true;
+    int bad = 0;
+    int32_t dq = 0;
     if (document) {
-        int bad = 0;
         for (int c = threadIdx.x; c < p.nchunks; c += kThreads)
             bad |= p.nonmono[(int64_t)b * p.nchunks + c];
-        mono = !__syncthreads_or(bad);
+        if (threadIdx.x < kTile) {
+            dq = doc[q0 + threadIdx.x];
+            s_docq[threadIdx.x] = dq;
+        }
+        // Document of the tile's first and last query, searched before the
+        // monotonicity verdict is known (in bounds either way; unused if the
+        // ids are not monotone).
+        if (wv == 0) {
+            const int v = wave_search_doc<false>(doc, 0, q0 + 1, __shfl(dq, 0));
+            if (lane == 0) s_ds0 = v;
+        } else if (wv == 1) {
+            const int v = wave_search_doc<true>(doc, q0 + kTile - 1, T, __shfl(dq, 63)) - 1;
+            if (lane == 0) s_deN = v;
+        }
     }
+    const bool mono = !__syncthreads_or(bad);
     const bool general = document && !mono;  // per-key document compare
-    const int64_t w = windowed ? (int64_t)(*p.window) : 0;
 
-    if (threadIdx.x == 0) {
-        s_amin = INT64_MAX; s_amax = INT64_MIN;
-        s_bmin = INT64_MAX; s_bmax = INT64_MIN;
-    }
-    __syncthreads();
     if (threadIdx.x < kTile) {
         const int r = threadIdx.x;
-        const int q = i * kTile + r;
-        int64_t ds = 0, de = T - 1;
-        if (document) {
-            const int32_t dq = doc[q];
-            s_docq[r] = dq;
-            if (mono) {
-                ds = lower_bound_doc(doc, 0, q + 1, dq);
-                de = upper_bound_doc(doc, q, T, dq) - 1;
-            }
+        const int q = q0 + r;
+        int ds = 0, de = T - 1;
+        if (document && mono) {
+            // Rows sharing the first (last) query's document share its start
+            // (end); any other document starts (ends) inside the tile.
+            ds = dq == s_docq[0] ? s_ds0 : q0 + lds_search_doc<false>(s_docq, 1, r, dq);
+            de = dq == s_docq[kTile - 1]
+                     ? s_deN
+                     : q0 + lds_search_doc<true>(s_docq, r + 1, kTile - 1, dq) - 1;
         }
-        int64_t hi = causal ? (int64_t)q : (int64_t)(T - 1);
+        int hi = causal ? q : T - 1;
         if (de < hi) hi = de;
-        int64_t lo = ds;
-        if (windowed && q - w + 1 > lo) lo = q - w + 1;
-        int64_t blo = 1, bhi = 0;  // empty
+        int64_t lo64 = ds;
+        if (windowed && (int64_t)q - w + 1 > lo64) lo64 = (int64_t)q - w + 1;
+        int lo = lo64 < T ? (int)lo64 : T;
+        int blo = kNone, bhi = -1;
         if (sinks_on) {
             blo = ds;
-            bhi = (int64_t)p.sinks - 1 < hi ? (int64_t)p.sinks - 1 : hi;
+            bhi = p.sinks - 1 < hi ? p.sinks - 1 : hi;
         }
+        if (lo > hi) { lo = kNone; hi = -1; }
+        if (blo > bhi) { blo = kNone; bhi = -1; }
         if (document) {
             int32_t *dr = p.out.doc_range + ((int64_t)b * T + q) * 2;
-            dr[0] = mono ? (int32_t)ds : -1;
-            dr[1] = mono ? (int32_t)de : -1;
+            dr[0] = mono ? ds : -1;
+            dr[1] = mono ? de : -1;
         }
-        s_alo[r] = lo; s_ahi[r] = hi;
-        s_blo[r] = blo; s_bhi[r] = bhi;
-        if (lo <= hi) {
-            atomicMin(&s_amin, (long long)lo);
-            atomicMax(&s_amax, (long long)hi);
+        // Extents of the main and sink intervals over the wave's rows (empty
+        // intervals are (kNone, -1) and drop out of both).
+        int e0 = lo, e1 = hi, e2 = blo, e3 = bhi;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            e0 = min(e0, __shfl_xor(e0, d));
+            e1 = max(e1, __shfl_xor(e1, d));
+            e2 = min(e2, __shfl_xor(e2, d));
+            e3 = max(e3, __shfl_xor(e3, d));
         }
-        if (blo <= bhi) {
-            atomicMin(&s_bmin, (long long)blo);
-            atomicMax(&s_bmax, (long long)bhi);
+        if (lane == 0) s_ext[wv] = i32x4{e0, e1, e2, e3};
+        // Without per-key document tests a row sees the union of two
+        // intervals; overlapping or touching ones are merged so that a tile
+        // is covered by the union only when one interval covers it.
+        if (!general && lo <= hi && blo <= bhi &&
+            (lo > blo ? lo : blo) <= (hi < bhi ? hi : bhi) + 1) {
+            lo = lo < blo ? lo : blo;
+            hi = hi > bhi ? hi : bhi;
+            blo = kNone;
+            bhi = -1;
         }
+        s_iv[r] = i32x4{lo, hi, blo, bhi};
     }
     __syncthreads();
-    const int64_t amin = s_amin, amax = s_amax, bmin = s_bmin, bmax = s_bmax;
+    const i32x4 x0 = s_ext[0], x1 = s_ext[1];
+    const int amin = min(x0.x, x1.x), amax = max(x0.y, x1.y);
+    const int bmin = min(x0.z, x1.z), bmax = max(x0.w, x1.w);
+    int jlo = nt, jhi = -1;  // tiles that can hold a visible pair
+    if (amin <= amax) {
+        jlo = amin / kTile;
+        jhi = amax / kTile;
+    }
+    if (bmin <= bmax) {
+        jlo = bmin / kTile < jlo ? bmin / kTile : jlo;
+        jhi = bmax / kTile > jhi ? bmax / kTile : jhi;
+    }
 
     const int64_t row_off = ((int64_t)b * nt + i) * nt;
     int32_t *idx_p = p.out.kv_indices + row_off;
     int32_t *idx_f = p.out.full_kv_indices + row_off;
     uint8_t *cls_row = p.cls + row_off;
-    int run_p = 0, run_f = 0;
+    for (int j = threadIdx.x; j < nt; j += kThreads)
+        if (j < jlo || j > jhi) cls_row[j] = kEmpty;
 
-    for (int jb = 0; jb < nt; jb += kThreads) {
-        const int j = jb + threadIdx.x;
-        uint8_t c = kEmpty;
-        if (j < nt) {
-            const int64_t k0 = (int64_t)j * kTile, k1 = k0 + kTile - 1;
-            const bool cand = (amin <= k1 && amax >= k0) || (bmin <= k1 && bmax >= k0);
-            if (cand) {
-                int64_t n = 0;
-                if (!general) {
-                    for (int r = 0; r < kTile; ++r) {
-                        const int64_t alo = s_alo[r], ahi = s_ahi[r];
-                        n += overlap(alo, ahi, k0, k1);
-                        if (sinks_on) {
-                            const int64_t blo = s_blo[r], bhi = s_bhi[r];
-                            n += overlap(blo, bhi, k0, k1);
-                            n -= overlap(alo > blo ? alo : blo, ahi < bhi ? ahi : bhi, k0, k1);
-                        }
-                    }
-                } else {
-                    for (int r = 0; r < kTile; ++r) {
-                        const int32_t dq = s_docq[r];
-                        const int64_t alo = s_alo[r], ahi = s_ahi[r];
-                        const int64_t a0 = alo > k0 ? alo : k0, a1 = ahi < k1 ? ahi : k1;
-                        for (int64_t kv = a0; kv <= a1; ++kv) n += (doc[kv] == dq);
-                        if (sinks_on) {
-                            const int64_t blo = s_blo[r], bhi = s_bhi[r];
-                            const int64_t b0 = blo > k0 ? blo : k0, b1 = bhi < k1 ? bhi : k1;
-                            for (int64_t kv = b0; kv <= b1; ++kv)
-                                if (kv < alo || kv > ahi) n += (doc[kv] == dq);
-                        }
-                    }
+    // Lane = (row group, tile): W tiles per pass and 64 / W groups splitting
+    // the wave's rows, W the smallest power of two (>= 8) covering the
+    // candidate tiles, at most 64.
+    const int hull = jhi - jlo + 1;
+    int W = 64;
+    while (W > 8 && W / 2 >= hull) W >>= 1;
+    const int rows_per = kRowsPerWave * W / 64;
+    const int tl = lane & (W - 1);
+    const int rb = wv * kRowsPerWave + (lane / W) * rows_per;
+    const unsigned long long low = W == 64 ? ~0ull : (1ull << W) - 1;
+    int run_p = 0, run_f = 0, buf = 0;
+    for (int jc = jlo; jc <= jhi; jc += W, buf ^= 1) {
+        const int j = jc + tl;
+        const int k0 = j * kTile, k1 = k0 + kTile - 1;
+        bool any = false, all = false;
+        if (j <= jhi && ((amin <= k1 && amax >= k0) || (bmin <= k1 && bmax >= k0))) {
+            if (!general) {
+                // Sign bits: x <= k1 <=> x - k1 - 1 < 0, and so on; the two
+                // tests of one interval are ANDed, the intervals ORed.
+                int acc_any = 0, acc_all = -1;
+#pragma unroll 4
+                for (int r = rb; r < rb + rows_per; ++r) {
+                    const i32x4 v = s_iv[r];
+                    acc_any |= ((v.x - k1 - 1) & (k0 - 1 - v.y)) | ((v.z - k1 - 1) & (k0 - 1 - v.w));
+                    acc_all &= ((v.x - k0 - 1) & (k1 - 1 - v.y)) | ((v.z - k0 - 1) & (k1 - 1 - v.w));
                 }
-                c = n == 0 ? kEmpty : (n == kTilePairs ? kFull : kPartial);
+                any = acc_any < 0;
+                all = acc_all < 0;
+            } else {
+                all = true;
+                for (int r = rb; r < rb + rows_per; ++r) {
+                    const i32x4 v = s_iv[r];
+                    const int32_t d = s_docq[r];
+                    int n = 0;
+                    const int a0 = v.x > k0 ? v.x : k0, a1 = v.y < k1 ? v.y : k1;
+                    for (int kv = a0; kv <= a1; ++kv) n += doc[kv] == d;
+                    const int c0 = v.z > k0 ? v.z : k0, c1 = v.w < k1 ? v.w : k1;
+                    for (int kv = c0; kv <= c1; ++kv)
+                        if (kv < v.x || kv > v.y) n += doc[kv] == d;
+                    any |= n > 0;
+                    all &= n == kTile;
+                }
             }
-            cls_row[j] = c;
         }
-        compact_chunk(c == kPartial, c == kFull, j, idx_p, idx_f, run_p, run_f, s_wp, s_wf);
+        unsigned long long ba = __ballot(any), bf = __ballot(all);
+        for (int sh = W; sh < 64; sh <<= 1) {  // fold the row groups onto lanes 0..W-1
+            ba |= ba >> sh;
+            bf &= bf >> sh;
+        }
+        if (lane == 0) {
+            s_any[buf][wv] = ba & low;
+            s_all[buf][wv] = bf & low;
+        }
+        __syncthreads();  // the other buffer is rewritten only after the next barrier
+        unsigned long long ma = 0, mf = ~0ull;
+#pragma unroll
+        for (int x = 0; x < kWaves; ++x) {
+            ma |= s_any[buf][x];
+            mf &= s_all[buf][x];
+        }
+        mf &= low;
+        const unsigned long long mp = ma & ~mf;  // some pair visible, not all
+        if (wv == 0 && lane < W && j <= jhi) {
+            const unsigned long long bit = 1ull << lane, lt = bit - 1;
+            if (mp & bit) idx_p[run_p + __popcll(mp & lt)] = j;
+            if (mf & bit) idx_f[run_f + __popcll(mf & lt)] = j;
+            cls_row[j] = (mf & bit) ? kFull : ((mp & bit) ? kPartial : kEmpty);
+        }
+        run_p += __popcll(mp);
+        run_f += __popcll(mf);
     }
     pad_tail(idx_p, run_p, nt);
     pad_tail(idx_f, run_f, nt);
@@ -264,11 +376,12 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(MaskBuildParams p) {
 // the record (bm * nt + i, full tiles, partial tiles, first listed tile) of
 // the e-th row in this order, so a kernel starts a row with one load.
 //
-// A counting sort of the blocks: histogram of the keys in LDS, exclusive
-// scan from the largest key down, one wave places the blocks in index order
-// (for each key present in a chunk of 64 blocks, the lanes holding it get
-// consecutive slots in lane order), then a scan of the block sizes gives
-// each block its first entry.
+// Up to 1024 blocks each thread ranks one block against all keys in LDS.
+// Beyond that, a counting sort: histogram of the keys in LDS, exclusive scan
+// from the largest key down, one wave places the blocks in index order (for
+// each key present in a chunk of 64 blocks, the lanes holding it get
+// consecutive slots in lane order).  A scan of the block sizes in sorted
+// order then gives each block its first entry.
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderPer = kOrderKeys / kOrderThreads;
 
@@ -313,71 +426,115 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(MaskBuildParams p)
         r0 = bm * nt + j * kOrderBlock;
         n = min(kOrderBlock, nt - j * kOrderBlock);
     };
+    // Loads of all rows of a block are independent and issued together
+    // (clamped to the block's last row, which every block has).
     auto key_of = [&](int g) {
         int r0, n;
         block_rows(g, r0, n);
         int tot = 0;
-        for (int r = r0; r < r0 + n; ++r) tot += num[r] + fnum[r];
+#pragma unroll
+        for (int x = 0; x < kOrderBlock; ++x) {
+            const int e = r0 + (x < n ? x : n - 1);
+            const int v = num[e] + fnum[e];
+            tot += x < n ? v : 0;
+        }
         return min(tot, kOrderKeys - 1);
     };
 
-    for (int x = tid; x < kOrderKeys; x += kOrderThreads) s_hist[x] = 0;
-    __syncthreads();
-    for (int g = tid; g < nb; g += kOrderThreads) atomicAdd(&s_hist[key_of(g)], 1);
-    __syncthreads();
-    // Thread t owns keys kOrderKeys-1-kOrderPer*t down to kOrderKeys-kOrderPer*(t+1).
-    int v[kOrderPer], sum = 0;
+    const int *srt;  // block at each sorted position
+    if (nb <= kOrderThreads) {
+        // Few blocks: each takes its rank from one pass over all keys in LDS.
+        int *s_key = s_hist, *s_sorted = s_hist + kOrderThreads;
+        int key = 0;
+        if (tid < nb) {
+            key = key_of(tid);
+            s_key[tid] = key;
+        }
+        __syncthreads();
+        if (tid < nb) {
+            int pos = 0;
+#pragma unroll 8
+            for (int g = 0; g < nb; ++g) {
+                const int kg = s_key[g];
+                pos += (kg > key) | ((kg == key) & (g < tid));
+            }
+            s_sorted[pos] = tid;
+        }
+        __syncthreads();
+        srt = s_sorted;
+    } else {
+        // Counting sort: histogram of the keys, exclusive scan from the
+        // largest key down, one wave places the blocks in index order.
+        for (int x = tid; x < kOrderKeys; x += kOrderThreads) s_hist[x] = 0;
+        __syncthreads();
+        for (int g = tid; g < nb; g += kOrderThreads) atomicAdd(&s_hist[key_of(g)], 1);
+        __syncthreads();
+        // Thread t owns keys kOrderKeys-1-kOrderPer*t down to kOrderKeys-kOrderPer*(t+1).
+        int v[kOrderPer], sum = 0;
 #pragma unroll
-    for (int x = 0; x < kOrderPer; ++x) {
-        v[x] = s_hist[kOrderKeys - 1 - (kOrderPer * tid + x)];
-        sum += v[x];
-    }
-    int total;
-    int start = block_exclusive_scan(sum, s_wsum, total);
+        for (int x = 0; x < kOrderPer; ++x) {
+            v[x] = s_hist[kOrderKeys - 1 - (kOrderPer * tid + x)];
+            sum += v[x];
+        }
+        int total;
+        int start = block_exclusive_scan(sum, s_wsum, total);
 #pragma unroll
-    for (int x = 0; x < kOrderPer; ++x) {
-        s_hist[kOrderKeys - 1 - (kOrderPer * tid + x)] = start;  // first slot of the key
-        start += v[x];
-    }
-    __syncthreads();
-    if (wv == 0) {
-        for (int g0 = 0; g0 < nb; g0 += 64) {
-            const int g = g0 + lane;
-            const int key = g < nb ? key_of(g) : -1;
-            unsigned long long todo = __ballot(g < nb);
-            while (todo) {
-                const int src = __builtin_ctzll(todo);
-                const int kk = __shfl(key, src);
-                const unsigned long long same = __ballot(key == kk);
-                const int base = s_hist[kk];
-                if (key == kk) sorted[base + __builtin_popcountll(same & ((1ull << lane) - 1))] = g;
-                __builtin_amdgcn_wave_barrier();
-                if (lane == src) s_hist[kk] = base + __builtin_popcountll(same);
-                __builtin_amdgcn_wave_barrier();
-                todo &= ~same;
+        for (int x = 0; x < kOrderPer; ++x) {
+            s_hist[kOrderKeys - 1 - (kOrderPer * tid + x)] = start;  // first slot of the key
+            start += v[x];
+        }
+        __syncthreads();
+        if (wv == 0) {
+            for (int g0 = 0; g0 < nb; g0 += 64) {
+                const int g = g0 + lane;
+                const int key = g < nb ? key_of(g) : -1;
+                unsigned long long todo = __ballot(g < nb);
+                while (todo) {
+                    const int src = __builtin_ctzll(todo);
+                    const int kk = __shfl(key, src);
+                    const unsigned long long same = __ballot(key == kk);
+                    const int base = s_hist[kk];
+                    if (key == kk) sorted[base + __builtin_popcountll(same & ((1ull << lane) - 1))] = g;
+                    __builtin_amdgcn_wave_barrier();
+                    if (lane == src) s_hist[kk] = base + __builtin_popcountll(same);
+                    __builtin_amdgcn_wave_barrier();
+                    todo &= ~same;
+                }
             }
         }
+        __threadfence_block();
+        __syncthreads();
+        srt = sorted;
     }
-    __threadfence_block();
-    __syncthreads();
     // Entries of the rows of each block, in sorted block order.
     int run = 0;  // entries before the current chunk of sorted positions
     for (int pos0 = 0; pos0 < nb; pos0 += kOrderThreads) {
         const int pos = pos0 + tid;
         int r0 = 0, n = 0;
-        if (pos < nb) block_rows(sorted[pos], r0, n);
+        if (pos < nb) block_rows(srt[pos], r0, n);
         int chunk_total;
         const int first = run + block_exclusive_scan(n, s_wsum, chunk_total);
-        for (int x = 0; x < n; ++x) {
-            const int e = r0 + x;
-            const int nf = fnum[e], np = num[e];
-            const int ft = nf > 0 ? fidx[(int64_t)e * nt] : (np > 0 ? idx[(int64_t)e * nt] : 0);
-            int4 rec;
-            rec.x = e;
-            rec.y = nf;
-            rec.z = np;
-            rec.w = ft;
-            reinterpret_cast<int4 *>(order)[first + x] = rec;
+        if (n > 0) {
+            // Every load of the block before the first store: the record
+            // stores could alias the lists as far as the compiler knows.
+            int nf[kOrderBlock], np[kOrderBlock], fi[kOrderBlock], pi[kOrderBlock];
+#pragma unroll
+            for (int x = 0; x < kOrderBlock; ++x) {
+                const int e = r0 + (x < n ? x : n - 1);
+                nf[x] = fnum[e];
+                np[x] = num[e];
+                fi[x] = fidx[(int64_t)e * nt];
+                pi[x] = idx[(int64_t)e * nt];
+            }
+#pragma unroll
+            for (int x = 0; x < kOrderBlock; ++x) {
+                int4 rec;
+                rec.x = r0 + x;
+                rec.y = nf[x];
+                rec.z = np[x];
+                rec.w = nf[x] > 0 ? fi[x] : (np[x] > 0 ? pi[x] : 0);
+                if (x < n) reinterpret_cast<int4 *>(order)[first + x] = rec;
+            }
         }
         run += chunk_total;
     }

@@ -43,6 +43,16 @@ def test_random_small_specs():
         _check(_random_spec(rng, T), f"random#{it}")
 
 
+def test_many_mask_batches():
+    """1030 mask batches of T = 1024 (one row block each): more blocks than
+    the work-order kernel ranks directly, so its counting-sort path runs."""
+    rng = np.random.default_rng(77)
+    T, mb = 1024, 1030
+    docs = np.stack([np.cumsum(rng.random(T) < 1.0 / rng.integers(4, 600)).astype(np.int32)
+                     for _ in range(mb)])
+    _check(MaskSpecData(T, causal=True, document=True, doc_ids=docs), "1030 batches")
+
+
 def test_config1_tiny():
     _check(make_config(1).spec, "config 1")
 
