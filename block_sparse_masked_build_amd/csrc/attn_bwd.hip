@@ -109,6 +109,7 @@ struct DqArgs {
     const int32_t *fidx, *pidx, *doc;
     int nfull, nt, qpos;
     float scale, scale_log2, slope, cap, inv_cap;
+    ModK mk;          // folded score-modification constants
     float l2, delta;  // this lane's query
 };
 
@@ -176,8 +177,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
                 dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, st), gf[st], dp[kb]);
             }
         }
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.scale, a.slope, a.cap,
-                                           a.inv_cap, rm, partial);
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial);
         bf16x8 dsb[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -238,6 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
     a.cap = SOFTCAP ? p.softcap : 1.0f;
     a.inv_cap = 1.0f / a.cap;
+    a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
     const int64_t row_bh = ((int64_t)b * p.H + h) * p.T + qpos;
     a.l2 = p.lse2[row_bh];
     a.delta = p.delta[row_bh];
@@ -325,6 +326,7 @@ struct DkdvArgs {
     const int32_t *fidx, *pidx, *doc;
     int nfull, nt, kpos;
     float scale, scale_log2, slope, cap, inv_cap;
+    ModK mk;  // folded score-modification constants
 };
 
 // One pipeline step of dkdv is one listed 128-query tile.
@@ -381,8 +383,11 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
     const int qbase = q0 + b * 32 + 4 * hl;
     int lo_t = cm.hi >= cm.lo ? cm.lo - qbase : 1 << 30;  // empty interval: no offset matches
     const int span = cm.hi >= cm.lo ? cm.hi - cm.lo : 0;
-    int rel = qbase - a.kpos;
-    asm volatile("" : "+v"(lo_t), "+v"(rel));
+    // ALiBi term of the score at query offset c: -slope_f (q - kpos) =
+    // c ns + n with ns = -slope_f and n = ns (qbase - kpos).
+    float ns = -a.mk.slope_f;
+    float n = ALIBI ? ns * (float)(qbase - a.kpos) : 0.0f;
+    asm volatile("" : "+v"(lo_t), "+v"(n), "+v"(ns));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int ql4 = b * 32 + g * 8 + hl * 4;
@@ -396,10 +401,8 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
             const int c = g * 8 + e;
             float pv, tl = 0.0f;
             if (kMods) {
-                float y = s[r] * a.scale;
-                if (ALIBI) y -= a.slope * (float)(rel + c);
-                if (SOFTCAP) y = a.cap * tanh_exp2(y * a.inv_cap);
-                tl = y * kLog2e;
+                const float bias = ALIBI ? __builtin_fmaf((float)c, ns, n) : 0.0f;
+                tl = mod_apply<ALIBI, SOFTCAP>(s[r], bias, a.mk);
                 pv = fast_exp2(tl - L[e]);
             } else {
                 pv = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -L[e]));
@@ -556,6 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
     a.cap = SOFTCAP ? p.softcap : 1.0f;
     a.inv_cap = 1.0f / a.cap;
+    a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
     const int ntiles = a.nfull + npart;
 
     ColMask cm;

@@ -27,11 +27,33 @@ __device__ inline f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// tanh(x) = 1 - 2 / (exp(2x) + 1), with exp(2x) = 2^(2x log2 e).
-// Saturates to +-1 for large |x| (2^inf = inf -> rcp = 0; 2^-inf = 0).
-__device__ inline float tanh_exp2(float x) {
-    const float e = fast_exp2(x * (2.0f * kLog2e));
-    return 1.0f - 2.0f * fast_rcp(e + 1.0f);
+// Score modifications with their constants folded once per item.  The
+// modified score leaves in the log2 domain:
+//   plain / ALiBi:  t = (s scale - slope (q - kv)) log2 e = s a + b
+//   soft-capped:    t = cap tanh(z) log2 e with z = (s scale - slope (q - kv)) / cap,
+//                   tanh z = 1 - 2 / (e^{2z} + 1), e^{2z} = 2^u, u = s a + b,
+//                   so t = c1 - c2 / (2^u + 1)
+// with a = scale f, b = -slope f (q - kv) and f = log2 e (plain) or
+// 2 log2 e / cap (soft-capped), c1 = cap log2 e, c2 = 2 cap log2 e.  The
+// ALiBi term b of each score is one fused multiply-add of its key offset.
+// Saturation: 2^u = inf gives t = c1, 2^u = 0 gives t = c1 - c2 = -cap log2 e.
+struct ModK {
+    float a, slope_f;  // score multiplier, slope in the same domain
+    float c1, c2;      // soft-cap constants
+};
+
+template <bool SOFTCAP>
+__device__ inline ModK mod_k(float scale, float slope, float cap) {
+    const float f = SOFTCAP ? 2.0f * kLog2e / cap : kLog2e;
+    return {scale * f, slope * f, cap * kLog2e, 2.0f * cap * kLog2e};
+}
+
+// t from a raw score s and its ALiBi term b (ignored without ALiBi).
+template <bool ALIBI, bool SOFTCAP>
+__device__ inline float mod_apply(float s, float b, const ModK &k) {
+    const float u = ALIBI ? __builtin_fmaf(s, k.a, b) : s * k.a;
+    if (!SOFTCAP) return u;
+    return __builtin_fmaf(-k.c2, fast_rcp(fast_exp2(u) + 1.0f), k.c1);
 }
 
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
@@ -408,26 +430,36 @@ __device__ inline bool in_range(int c, int lo_t, int span) {
     return (uint32_t)(c - lo_t) <= (uint32_t)span;  // lo_t <= c <= lo_t + span, span >= 0
 }
 
+// Score modifications alone (row view, step starting at key0): the scores
+// leave in the log2 domain.  Without modifications nothing is done here; the
+// scale is folded into the exponential instead.  The ALiBi term of the
+// score at key offset c (key - key0 - 4 hl) is slope_f c + n with
+// n = -slope_f (q - key0 - 4 hl).
+template <bool ALIBI, bool SOFTCAP>
+__device__ inline void row_mods(f32x16 (&s)[2], int key0, int qpos, const ModK &mk) {
+    if (!(ALIBI || SOFTCAP)) return;
+    const int hl = (threadIdx.x & 63) >> 5;
+    float n = 0.0f, sf = mk.slope_f;
+    if (ALIBI) {
+        n = -mk.slope_f * (float)(qpos - (key0 + hl * 4));
+        asm volatile("" : "+v"(n), "+v"(sf));  // per step: keeps the per-register terms from being hoisted
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+            const float b = ALIBI ? __builtin_fmaf((float)c, sf, n) : 0.0f;
+            s[kb][r] = mod_apply<ALIBI, SOFTCAP>(s[kb][r], b, mk);
+        }
+}
+
 template <bool ALIBI, bool SOFTCAP, int MODE>
-__device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int qpos, float scale,
-                                    float slope, float cap, float inv_cap, const RowMask &rm, bool partial) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
+__device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int qpos, const ModK &mk,
+                                    const RowMask &rm, bool partial) {
     const int hl = (threadIdx.x & 63) >> 5;
     const int kbase = key0 + hl * 4;
-    if (kMods) {
-        int rel = qpos - kbase;
-        if (ALIBI) asm volatile("" : "+v"(rel));  // keep per-register offsets from being hoisted
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - kbase
-                float y = s[kb][r] * scale;
-                if (ALIBI) y -= slope * (float)(rel - c);
-                if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
-                s[kb][r] = y * kLog2e;
-            }
-    }
+    row_mods<ALIBI, SOFTCAP>(s, key0, qpos, mk);
     if (!partial) return;  // full tile: every pair is visible
     // Bounds relative to this step, kept opaque so that the compiler compares
     // them with the per-register key offsets instead of hoisting 64
@@ -470,28 +502,6 @@ __device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int
             }
         }
     }
-}
-
-// Score modifications alone (row view, step starting at key0): the scores
-// leave in the log2 domain.  Without modifications nothing is done here; the
-// scale is folded into the exponential instead.
-template <bool ALIBI, bool SOFTCAP>
-__device__ inline void row_mods(f32x16 (&s)[2], int key0, int qpos, float scale, float slope, float cap,
-                                float inv_cap) {
-    if (!(ALIBI || SOFTCAP)) return;
-    const int hl = (threadIdx.x & 63) >> 5;
-    int rel = qpos - (key0 + hl * 4);
-    if (ALIBI) asm volatile("" : "+v"(rel));  // keep per-register offsets from being hoisted
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int c = kb * 32 + (r >> 2) * 8 + (r & 3);  // key - (key0 + 4 hl)
-            float y = s[kb][r] * scale;
-            if (ALIBI) y -= slope * (float)(rel - c);
-            if (SOFTCAP) y = cap * tanh_exp2(y * inv_cap);
-            s[kb][r] = y * kLog2e;
-        }
 }
 
 // Elementwise mask of a partial tile's step (row view), without branches:

@@ -174,6 +174,7 @@ struct FwdArgs {
     int b, h, bm, row;
     int nfull, ntiles, nt, qpos, first;
     float scale, scale_log2, slope, cap, inv_cap;
+    ModK mk;  // folded score-modification constants
 };
 
 // Item order.  Item k is work-order entry e for head (and, with a shared
@@ -253,6 +254,7 @@ __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &re
     a.slope = ALIBI ? p.alibi_slopes[a.h] : 0.0f;
     a.cap = SOFTCAP ? p.softcap : 1.0f;
     a.inv_cap = 1.0f / a.cap;
+    a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
 }
 
 // Entries 0..127 of the query-tile row's tile list (full tiles first, then
@@ -452,7 +454,7 @@ __device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const Til
     const int k0 = a.first * kTile;
     int key_ahead = k0 + kHalf;  // first key of step t+1 at the top of step t
     fwd_qk<D>(sm.k[0], off, qf, sa);
-    row_mods<ALIBI, SOFTCAP>(sa, k0, a.qpos, a.scale, a.slope, a.cap, a.inv_cap);
+    row_mods<ALIBI, SOFTCAP>(sa, k0, a.qpos, a.mk);
     if (a.nfull == 0) row_mask_flat<MODE>(lds_addr(sm.doc[0]), sa, k0, rm);
     mx = step_max(sa);
 
@@ -473,7 +475,7 @@ __device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const Til
         fwd_qk<D>(sm.k[(t + 1) & 1], offt, qf, sn);
         fwd_exp(sc, pb, l, c_mul, m_use);
         fwd_pv<D>(sm.v[t & 1], offt, pb, o);
-        row_mods<ALIBI, SOFTCAP>(sn, key_next, a.qpos, a.scale, a.slope, a.cap, a.inv_cap);
+        row_mods<ALIBI, SOFTCAP>(sn, key_next, a.qpos, a.mk);
         if (decltype(next_masked)::value) row_mask_flat<MODE>(lds_addr(sm.doc[(t + 1) & 1]), sn, key_next, rm);
         mx = step_max(sn);
         wait_lds_reads();  // this wave's reads of step t are done before the next barrier
