@@ -357,22 +357,37 @@ __device__ inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const Fwd
 }
 
 // Output of a finished item: out = o / l as bf16, lse = (m + log2 l) ln 2.
+// Each wave passes its 32 output rows through its own 32 x D slice of LDS at
+// `stage` (16-byte chunks of a row XOR-swizzled by the row, so neither side
+// conflicts), then stores whole rows: 16 bytes per lane, 2 D contiguous
+// bytes per row, instead of 16-byte pieces of 32 rows per instruction.  The
+// exchange stays inside the wave, whose LDS accesses execute in order.
 template <int D>
 __device__ inline void store_item(const AttnParams &p, const FwdArgs &a, const f32x16 (&o)[D / 32], float m,
-                                  float l) {
-    const int hl = (threadIdx.x & 63) >> 5;
+                                  float l, uint32_t stage) {
+    constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kRowsPerRead = 64 / kChunks;
+    const int lane = threadIdx.x & 63, n = lane & 31, hl = lane >> 5, wv = wave_id();
+    const uint32_t base = stage + (uint32_t)(wv * 32 * kRowBytes);
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.0f ? fast_rcp(l_tot) : 0.0f;
-    __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh + (int64_t)a.qpos * p.o_st;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
+            // d = 32 db + 8 g + 4 hl + 0..3: chunk 4 db + g, half hl
             u32x2 w;
             w.x = pack_bf16x2(o[db][g * 4 + 0] * inv, o[db][g * 4 + 1] * inv);
             w.y = pack_bf16x2(o[db][g * 4 + 2] * inv, o[db][g * 4 + 3] * inv);
-            *reinterpret_cast<u32x2 *>(ob + db * 32 + g * 8 + hl * 4) = w;
+            lds_store<u32x2>(base + n * kRowBytes + (((db * 4 + g) ^ (n % kChunks)) * 16) + hl * 8, w);
         }
+    }
+    __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh +
+                 (int64_t)(a.row * kTile + wv * 32) * p.o_st;
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPerRead; ++i) {
+        const int r = i * kRowsPerRead + lane / kChunks, c = lane % kChunks;
+        const u32x4 v = lds_load<u32x4>(base + r * kRowBytes + ((c ^ (r % kChunks)) * 16));
+        *reinterpret_cast<u32x4 *>(ob + (int64_t)r * p.o_st + c * 8) = v;
     }
     if (hl == 0)
         p.lse[((int64_t)a.b * p.H + a.h) * p.T + a.qpos] =
@@ -397,12 +412,14 @@ __device__ inline void store_item(const AttnParams &p, const FwdArgs &a, const f
 // steps whose next tile is partial run in separate loops (the tile list
 // holds full tiles first), so the elementwise mask needs no branch.
 //
-// The item's output is written at its end.
+// The item's output is written at its end, staged through the K buffers,
+// which no wave reads during the last step.
 template <int D, bool ALIBI, bool SOFTCAP, int MODE>
 __device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
                                 const bf16x8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
                                 f32x16 (&o)[D / 32], float &m, float &l) {
     constexpr bool kMods = ALIBI || SOFTCAP;
+    static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "output staging fits the K buffers");
     const float c_mul = kMods ? 1.0f : a.scale_log2;
     const int nsteps = 2 * a.ntiles;
     auto reset = [&]() {
@@ -415,7 +432,7 @@ __device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const Til
     };
     if (nsteps == 0) {  // nothing visible: out = 0, lse = -inf
         reset();
-        store_item<D>(p, a, o, m, l);
+        store_item<D>(p, a, o, m, l, lds_addr(sm.k[0]));
         return;
     }
     auto step_key0 = [&](int t) { return tile_at(tl, a, t >> 1) * kTile + (t & 1) * kHalf; };
@@ -511,7 +528,7 @@ __device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const Til
     bf16x8 pb[2][2];
     fwd_exp(sa, pb, l, c_mul, m_use);
     fwd_pv<D>(sm.v[1], off, pb, o);
-    store_item<D>(p, a, o, m, l);
+    store_item<D>(p, a, o, m, l, lds_addr(sm.k[0]));
 }
 
 // One item per workgroup (workgroups past the last item exit at once).
