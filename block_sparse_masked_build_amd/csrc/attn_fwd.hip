@@ -326,7 +326,7 @@ struct FwdSmem {
 // query rows, the tile list and the row data.  Every item has an even
 // number of steps, so each item starts on buffer 0.
 template <int D>
-__device__ inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, bf16x8 (&qf)[D / 16],
+__device__ __attribute__((always_inline)) inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, bf16x8 (&qf)[D / 16],
                                   TileList &tl, RowLoad &rl) {
     if (a.ntiles > 0) {
         const int k0 = a.first * kTile;
@@ -363,7 +363,7 @@ __device__ inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const Fwd
 // bytes per row, instead of 16-byte pieces of 32 rows per instruction.  The
 // exchange stays inside the wave, whose LDS accesses execute in order.
 template <int D>
-__device__ inline void store_item(const AttnParams &p, const FwdArgs &a, const f32x16 (&o)[D / 32], float m,
+__device__ __attribute__((always_inline)) inline void store_item(const AttnParams &p, const FwdArgs &a, const f32x16 (&o)[D / 32], float m,
                                   float l, uint32_t stage) {
     constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kRowsPerRead = 64 / kChunks;
     const int lane = threadIdx.x & 63, n = lane & 31, hl = lane >> 5, wv = wave_id();
@@ -415,7 +415,7 @@ __device__ inline void store_item(const AttnParams &p, const FwdArgs &a, const f
 // The item's output is written at its end, staged through the K buffers,
 // which no wave reads during the last step.
 template <int D, bool ALIBI, bool SOFTCAP, int MODE>
-__device__ inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
+__device__ __attribute__((always_inline)) inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
                                 const bf16x8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
                                 f32x16 (&o)[D / 32], float &m, float &l) {
     constexpr bool kMods = ALIBI || SOFTCAP;
