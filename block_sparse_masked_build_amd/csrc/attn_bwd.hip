@@ -74,18 +74,6 @@ __global__ __launch_bounds__(kThreads) void delta_kernel(AttnParams p) {
     }
 }
 
-// Writes a transposed accumulator block (lane = row of dst; register r holds
-// column col0 + 8 (r/4) + 4 hl + r%4) as bf16.
-__device__ inline void store_acc_rows(__bf16 *dst, const f32x16 &acc, int col0, int hl) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        u32x2 w;
-        w.x = pack_bf16x2(acc[g * 4 + 0], acc[g * 4 + 1]);
-        w.y = pack_bf16x2(acc[g * 4 + 2], acc[g * 4 + 3]);
-        *reinterpret_cast<u32x2 *>(dst + col0 + g * 8 + hl * 4) = w;
-    }
-}
-
 // Soft-cap derivative from the log2-domain capped score t = cap tanh(.) log2 e:
 // 1 - tanh^2, with tanh clamped so that masked scores (-inf) give 0.
 __device__ inline float softcap_grad(float t, float inv_cap) {
@@ -273,9 +261,12 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
     else
         dq_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, gf, off, lds, nsteps, dq);
 
-    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)qpos * p.dq_st;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) store_acc_rows(dqp, dq[db] * p.scale, db * 32, hl);  // dS without the scale
+    // dQ rows of the wave, staged through the K buffers once every wave is
+    // done with them (dS was accumulated without the scale).
+    static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "dQ staging fits the K buffers");
+    tile_barrier();
+    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)(qpos - n) * p.dq_st;
+    store_rows_staged<D>(dqp, p.dq_st, dq, p.scale, lds.k + (uint32_t)(wv * 32 * 2 * D));
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -595,13 +586,17 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
     else
         dkdv_main<D, ALIBI, SOFTCAP, false>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
 
-    __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)kpos * p.dk_st;
-    __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)kpos * p.dv_st;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        store_acc_rows(dkp, dk[db] * p.scale, db * 32, hl);  // dS was accumulated without the scale
-        store_acc_rows(dvp, dv[db], db * 32, hl);
-    }
+    // dK and dV rows of the wave, staged through the query and output-gradient
+    // buffers once every wave is done with them (dS was accumulated without
+    // the scale).
+    static_assert(sizeof(sm.q) >= (kThreads / 64) * 32 * 2 * D, "dK staging fits the query buffers");
+    static_assert(sizeof(sm.g) >= (kThreads / 64) * 32 * 2 * D, "dV staging fits the gradient buffers");
+    tile_barrier();
+    const uint32_t slice = (uint32_t)(wv * 32 * 2 * D);
+    __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)(kpos - n) * p.dk_st;
+    __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)(kpos - n) * p.dv_st;
+    store_rows_staged<D>(dkp, p.dk_st, dk, p.scale, lds.q + slice);
+    store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice);
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>

@@ -420,6 +420,39 @@ struct RowMask {
     int32_t docq;       // document id of the query (kGather only)
 };
 
+// Stores a wave's 32 x D block of fp32 accumulators as bf16 rows, times mul
+// (per lane, i.e. per row).  Accumulator layout: lane (row n, half hl) holds
+// for column block db the columns 32 db + 8 g + 4 hl + e in register 4 g + e.
+// The block passes through this wave's own 32 x 2D-byte LDS slice at
+// `stage` (16-byte chunks of a row XOR-swizzled by the row, so neither side
+// conflicts), then each store writes 16 bytes per lane and whole 2D-byte
+// rows, instead of 16-byte pieces of 32 rows.  The exchange stays inside the
+// wave, whose LDS accesses execute in order; the caller makes sure no other
+// wave uses the slice.  dst is row 0 of the block, ld its row stride.
+template <int D>
+__device__ __attribute__((always_inline)) inline void store_rows_staged(__bf16 *dst, int64_t ld,
+                                                                        const f32x16 (&acc)[D / 32], float mul,
+                                                                        uint32_t stage) {
+    constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kRowsPerRead = 64 / kChunks;
+    const int lane = threadIdx.x & 63, n = lane & 31, hl = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x2 w;  // columns 32 db + 8 g + 4 hl + 0..3: chunk 4 db + g, half hl
+            w.x = pack_bf16x2(acc[db][g * 4 + 0] * mul, acc[db][g * 4 + 1] * mul);
+            w.y = pack_bf16x2(acc[db][g * 4 + 2] * mul, acc[db][g * 4 + 3] * mul);
+            lds_store<u32x2>(stage + n * kRowBytes + (((db * 4 + g) ^ (n % kChunks)) * 16) + hl * 8, w);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 32 / kRowsPerRead; ++i) {
+        const int r = i * kRowsPerRead + lane / kChunks, c = lane % kChunks;
+        const u32x4 v = lds_load<u32x4>(stage + r * kRowBytes + ((c ^ (r % kChunks)) * 16));
+        *reinterpret_cast<u32x4 *>(dst + (int64_t)r * ld + c * 8) = v;
+    }
+}
+
 // Row view (lane = query, S^T = K Q^T layout: lane (query n, half hl) holds
 // for key block kb the keys 32 kb + 8 (r/4) + 4 hl + r%4 of a 64-key step).
 // Score modifications (to the log2 domain) and the mask for the step whose

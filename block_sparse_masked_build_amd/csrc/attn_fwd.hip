@@ -357,38 +357,18 @@ __device__ __attribute__((always_inline)) inline void item_start(const AttnParam
 }
 
 // Output of a finished item: out = o / l as bf16, lse = (m + log2 l) ln 2.
-// Each wave passes its 32 output rows through its own 32 x D slice of LDS at
-// `stage` (16-byte chunks of a row XOR-swizzled by the row, so neither side
-// conflicts), then stores whole rows: 16 bytes per lane, 2 D contiguous
-// bytes per row, instead of 16-byte pieces of 32 rows per instruction.  The
-// exchange stays inside the wave, whose LDS accesses execute in order.
+// Each wave's 32 rows go through its own 32 x D slice of LDS at `stage`
+// and are stored as whole rows.
 template <int D>
-__device__ __attribute__((always_inline)) inline void store_item(const AttnParams &p, const FwdArgs &a, const f32x16 (&o)[D / 32], float m,
-                                  float l, uint32_t stage) {
-    constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kRowsPerRead = 64 / kChunks;
-    const int lane = threadIdx.x & 63, n = lane & 31, hl = lane >> 5, wv = wave_id();
-    const uint32_t base = stage + (uint32_t)(wv * 32 * kRowBytes);
+__device__ __attribute__((always_inline)) inline void store_item(const AttnParams &p, const FwdArgs &a,
+                                                                 const f32x16 (&o)[D / 32], float m, float l,
+                                                                 uint32_t stage) {
+    const int hl = (threadIdx.x & 63) >> 5, wv = wave_id();
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.0f ? fast_rcp(l_tot) : 0.0f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            // d = 32 db + 8 g + 4 hl + 0..3: chunk 4 db + g, half hl
-            u32x2 w;
-            w.x = pack_bf16x2(o[db][g * 4 + 0] * inv, o[db][g * 4 + 1] * inv);
-            w.y = pack_bf16x2(o[db][g * 4 + 2] * inv, o[db][g * 4 + 3] * inv);
-            lds_store<u32x2>(base + n * kRowBytes + (((db * 4 + g) ^ (n % kChunks)) * 16) + hl * 8, w);
-        }
-    }
     __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh +
                  (int64_t)(a.row * kTile + wv * 32) * p.o_st;
-#pragma unroll
-    for (int i = 0; i < 32 / kRowsPerRead; ++i) {
-        const int r = i * kRowsPerRead + lane / kChunks, c = lane % kChunks;
-        const u32x4 v = lds_load<u32x4>(base + r * kRowBytes + ((c ^ (r % kChunks)) * 16));
-        *reinterpret_cast<u32x4 *>(ob + (int64_t)r * p.o_st + c * 8) = v;
-    }
+    store_rows_staged<D>(ob, p.o_st, o, inv, stage + (uint32_t)(wv * 32 * 2 * D));
     if (hl == 0)
         p.lse[((int64_t)a.b * p.H + a.h) * p.T + a.qpos] =
             l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
