@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
             s_docq[threadIdx.x] = dq;
         }
         // Document of the tile's first and last query, searched before the
-        // monotonicity verdict is known (in bounds either way; unused if the
+        // monotonicity result is known (in bounds either way; unused if the
         // ids are not monotone).
         if (wv == 0) {
             const int v = wave_search_doc<false>(doc, 0, q0 + 1, __shfl(dq, 0));

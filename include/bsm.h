@@ -43,7 +43,7 @@ extern "C" {
 typedef enum {
     BSM_OK = 0,
     BSM_E_INVALID = 1,     /* bad argument: null pointer, bad size or stride */
-    BSM_E_UNSUPPORTED = 2, /* valid request this build does not implement   */
+    BSM_E_UNSUPPORTED = 2, /* valid request outside what the library covers  */
     BSM_E_WORKSPACE = 3,   /* workspace missing or too small                 */
     BSM_E_HIP = 4          /* HIP runtime reported an error at launch        */
 } bsm_status;
