@@ -13,7 +13,7 @@ from workloads import MaskSpecData, ScoreModData, alibi_slopes, make_config, ran
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
-def _run(tensors, spec_data, mod_data, scale=None):
+def _run(tensors, spec_data, mod_data, scale=None, layout="bhtd"):
     from block_sparse_masked_build_amd import api
     spec = api.from_spec_data(spec_data)
     mod = None
@@ -21,14 +21,16 @@ def _run(tensors, spec_data, mod_data, scale=None):
         mod = api.score_mod(mod_data.alibi_slopes, mod_data.softcap)
     bm = api.build_block_mask(spec)
     q, k, v, do = (tensors[n].cuda() for n in ("q", "k", "v", "dout"))
+    if layout == "bthd":  # same values, [B, T, H, D] memory viewed as [B, H, T, D]
+        q, k, v, do = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v, do))
     out, lse = api.flex_attention_fwd(q, k, v, bm, spec, mod, scale)
     dq, dk, dv = api.flex_attention_bwd(q, k, v, out, lse, do, bm, spec, mod, scale)
     torch.cuda.synchronize()
     return dq.cpu(), dk.cpu(), dv.cpu()
 
 
-def _full(tensors, spec, mod, B, H, T, ctx, scale=None, rtol=0.0):
-    dq, dk, dv = _run(tensors, spec, mod, scale)
+def _full(tensors, spec, mod, B, H, T, ctx, scale=None, rtol=0.0, layout="bhtd"):
+    dq, dk, dv = _run(tensors, spec, mod, scale, layout)
     for b in range(B):
         for h in range(H):
             Q, K, V, dO = (per_head_f64(tensors[n], b, h) for n in ("q", "k", "v", "dout"))
@@ -72,6 +74,23 @@ def test_random_small_cases_every_element():
                f"w={spec.window} s={spec.sinks} alibi={mod.alibi_slopes is not None} cap={mod.softcap}")
         log(f"[bwd] {ctx}")
         _full(tensors, spec, mod, B, H, T, ctx, rtol=EDGE_RTOL)
+
+
+def test_strided_layout_every_element():
+    """[B, T, H, D] memory for every input, so that out, dQ, dK and dV (made
+    like the inputs) have row strides H * D: both the row loads and the row
+    stores of the kernels follow the strides.  D = 128 and D = 64."""
+    rng = np.random.default_rng(7)
+    for D in (128, 64):
+        B, H, T = 2, 3, 384
+        docs = np.cumsum(rng.random((1, T)) < 0.01, axis=1).astype(np.int32)
+        spec = MaskSpecData(T, causal=True, document=True, doc_ids=docs, window=200)
+        mod = ScoreModData(alibi_slopes=alibi_slopes(H), softcap=20.0)
+        g = torch.Generator("cpu").manual_seed(77 + D)
+        tensors = {n: random_bf16((B, H, T, D), g) for n in ("q", "k", "v", "dout")}
+        ctx = f"strided B{B} H{H} T{T} D{D}"
+        log(f"[bwd] {ctx}")
+        _full(tensors, spec, mod, B, H, T, ctx, rtol=EDGE_RTOL, layout="bthd")
 
 
 def test_config1_every_element():
