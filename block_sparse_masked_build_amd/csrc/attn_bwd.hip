@@ -43,34 +43,49 @@ constexpr int kHalf = 64;  // rows per pipeline step
 
 // ---------------------------------------------------------------- Delta, L
 
+// Workgroups of one (batch, head) take kDeltaRows consecutive query rows;
+// a thread reads 16 bytes of out and dO for each of its kDeltaPasses rows,
+// all loads issued before the first use.
+constexpr int kDeltaPasses = 4;
+
+template <int D>
+constexpr int delta_rows() { return kThreads / (D / 8) * kDeltaPasses; }
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void delta_kernel(AttnParams p) {
     constexpr int LPR = D / 8;           // lanes per row
-    constexpr int RPB = kThreads / LPR;  // rows per block
-    const int64_t rows = (int64_t)p.B * p.H * p.T;
-    const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+    constexpr int RPI = kThreads / LPR;  // rows per pass
+    const int per_bh = p.T / delta_rows<D>();  // T is a multiple of 128, delta_rows<D>() divides it
+    const int bh = blockIdx.x / per_bh;
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int t0 = (blockIdx.x - bh * per_bh) * delta_rows<D>() + threadIdx.x / LPR;
     const int c = (threadIdx.x % LPR) * 8;
-    float acc = 0.0f;
-    if (r < rows) {
-        const int64_t t = r % p.T, bh = r / p.T;
-        const int64_t b = bh / p.H, h = bh % p.H;
-        const u32x4 o = *reinterpret_cast<const u32x4 *>(static_cast<const __bf16 *>(p.o) + b * p.o_sb +
-                                                          h * p.o_sh + t * p.o_st + c);
-        const u32x4 g = *reinterpret_cast<const u32x4 *>(static_cast<const __bf16 *>(p.dout) + b * p.do_sb +
-                                                          h * p.do_sh + t * p.do_st + c);
+    const __bf16 *ob = static_cast<const __bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + c;
+    const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh + c;
+    u32x4 o[kDeltaPasses], g[kDeltaPasses];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float ov = __builtin_bit_cast(float, u16_at(o, e) << 16);
-            const float gv = __builtin_bit_cast(float, u16_at(g, e) << 16);
-            acc += ov * gv;
-        }
+    for (int k = 0; k < kDeltaPasses; ++k) {
+        const int64_t t = t0 + k * RPI;
+        o[k] = *reinterpret_cast<const u32x4 *>(ob + t * p.o_st);
+        g[k] = *reinterpret_cast<const u32x4 *>(gb + t * p.do_st);
     }
 #pragma unroll
-    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-    if (r < rows && threadIdx.x % LPR == 0) {
-        p.delta[r] = acc;
-        const float lse = p.lse[r];  // lse is [B, H, T] contiguous: same flat index
-        p.lse2[r] = lse == -INFINITY ? 0.0f : lse * kLog2e;
+    for (int k = 0; k < kDeltaPasses; ++k) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float ov = __builtin_bit_cast(float, u16_at(o[k], e) << 16);
+            const float gv = __builtin_bit_cast(float, u16_at(g[k], e) << 16);
+            acc += ov * gv;
+        }
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+        if (threadIdx.x % LPR == 0) {
+            const int64_t r = (int64_t)bh * p.T + t0 + k * RPI;  // [B, H, T] contiguous
+            p.delta[r] = acc;
+            const float lse = p.lse[r];
+            p.lse2[r] = lse == -INFINITY ? 0.0f : lse * kLog2e;
+        }
     }
 }
 
@@ -608,9 +623,9 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
-    constexpr int RPB = kThreads / (D / 8);
-    const int64_t rows = (int64_t)p.B * p.H * p.T;
-    hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), 0, stream, p);
+    static_assert(kTile % delta_rows<D>() == 0, "delta workgroups tile every query tile");
+    const int64_t blocks = (int64_t)p.B * p.H * (p.T / delta_rows<D>());
+    hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
     if (alibi && cap)
