@@ -267,7 +267,10 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dq[db][r] = 0.0f;
-    wait_vmcnt<0>();  // row operands and per-query values are in registers before any tile copy
+    // No wait here: the first tile copies are issued while the row operands
+    // load.  Loads complete in order, so the compiler's waits before their
+    // uses only become more conservative with copies in flight, and the
+    // first pipeline step waits for everything.
 
     if (mode == kGather)
         dq_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, gf, off, lds, nsteps, dq);
@@ -594,7 +597,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
             dk[db][r] = 0.0f;
             dv[db][r] = 0.0f;
         }
-    wait_vmcnt<0>();  // key rows and the mask bounds are in registers before any tile copy
+    // No wait here: the first tile copies are issued while the key rows
+    // load (see dq_kernel).
 
     if (gather)
         dkdv_main<D, ALIBI, SOFTCAP, true>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
