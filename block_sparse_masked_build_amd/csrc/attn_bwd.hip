@@ -211,26 +211,32 @@ __global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
     const int nt = p.nt;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = wg / nt;
-    const int i = nt - 1 - (wg % nt);  // later query tiles first (more tiles under a causal mask)
-    const int b = bh / p.H, h = bh % p.H;
+    // Item: a query-tile row of the row work order (longest first) and a
+    // head index, in the forward's item order.
+    const ItemOrder ord(p, kQueues);
+    const int k = ord.item(blockIdx.x / ord.Q);
+    if (k >= ord.nitems) return;
+    int e, rem;
+    ord.decode(k, e, rem);
+    const WorkRec rec = load_rec(p.kv_order, e);
+    const int64_t row = min(max(rec.packed, 0), p.mask_b * nt - 1);
+    const int bm = (int)(row / nt), i = (int)(row - (int64_t)bm * nt);
+    int b, h;
+    head_of(p, rem, bm, b, h);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 31, hl = lane >> 5;
     const int qpos = i * kTile + wv * 32 + n;
 
     const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
     const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
-    const int bm = p.mask_b == 1 ? 0 : b;
-    const int64_t row = (int64_t)bm * nt + i;
 
     DqArgs a;
     a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
     a.vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
     a.k_st = p.k_st;
     a.v_st = p.v_st;
-    a.nfull = min(max(load_uniform(p.full_kv_num + row), 0), nt);
-    const int npart = min(max(load_uniform(p.kv_num + row), 0), nt);
+    a.nfull = min(max(rec.nfull, 0), nt);
+    const int npart = min(max(rec.npart, 0), nt);
     a.fidx = p.full_kv_idx + row * nt;
     a.pidx = p.kv_idx + row * nt;
     a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.T : nullptr;
@@ -618,11 +624,18 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
     store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice);
 }
 
+// dq_kernel runs the rows in the forward's item order (longest rows first,
+// neighbouring rows of a head together on an XCD); dkdv_kernel runs one
+// workgroup per (batch, head, key tile), early key tiles first.  Measured on
+// the 64K doc+window, causal-in-chunks and ALiBi + soft-cap workloads, the
+// column work order gained for dK/dV only with soft-capped documents and lost
+// elsewhere, while the row order for dQ gained or held everywhere.
 template <int D, bool ALIBI, bool SOFTCAP>
 void launch_main(const AttnParams &p, hipStream_t stream) {
-    const dim3 grid(p.B * p.H * p.nt), block(kThreads);
-    hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP>), grid, block, 0, stream, p);
-    hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP>), grid, block, 0, stream, p);
+    AttnParams q = p;
+    const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
+    hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP>), dkdv_grid, block, 0, stream, q);
+    hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP>), dq_grid, block, 0, stream, q);
 }
 
 template <int D>

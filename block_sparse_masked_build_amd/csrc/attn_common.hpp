@@ -638,4 +638,104 @@ __device__ inline bool block_none_visible(const RowMask &rm, int kf, int kl) {
     return __all(none);
 }
 
+// ---------------------------------------------------------------- item order
+// Both attention directions run one workgroup per item: a row (forward, dQ)
+// or a column (dK/dV) of tiles of the block mask, for one head index.  The
+// block mask's work orders list rows / columns longest first, as records
+// that let a workgroup start with one scalar load.
+
+// One work-order record: (flat row, full tiles, partial tiles, first tile).
+struct WorkRec {
+    int packed, nfull, npart, first;
+};
+
+__device__ inline WorkRec load_rec(const int32_t *order, int e) {
+    const i32x4 r = *(const __attribute__((address_space(4))) i32x4 *)(order + 4 * (int64_t)e);
+    return {r.x, r.y, r.z, r.w};
+}
+
+// Item order.  Item k is work-order entry e for head (and, with a shared
+// mask, batch entry) rem.  Items come in chunks of 2^ord_chunk_log2
+// consecutive entries of one head -- rows that mostly share key and value
+// tiles -- and chunk c is served by queue c % Q: workgroup b takes the
+// (b / Q)-th item of queue b % Q.  Workgroups are dispatched round-robin
+// over the XCDs, so with Q = 8 each queue runs on one XCD and the rows
+// running at the same time there share tiles through its L2; items leave
+// each queue in work order.  The host picks the chunk so that every queue
+// gets several chunks.
+constexpr int kQueues = 8;
+
+// Quotient k / d for 0 <= k < 2^31 and d >= 1, with m = ceil(2^32 / d)
+// computed on the host (d >= 2; d = 1 is passed through): the estimate is
+// q or q + 1.
+__device__ inline int div_by(int k, int d, uint32_t m) {
+    if (d == 1) return k;
+    int q = (int)(((uint64_t)(uint32_t)k * m) >> 32);
+    if ((int64_t)q * d > k) --q;
+    return q;
+}
+
+struct ItemOrder {
+    int nitems;  // B * H * QT, within int32 (checked on the host)
+    int Q, queue, cl;
+    const AttnParams &p;
+
+    __device__ ItemOrder(const AttnParams &p_, int G) : p(p_) {
+        nitems = p.mask_b * p.nt * p.ord_r;
+        Q = G < kQueues ? G : kQueues;
+        queue = blockIdx.x % Q;
+        cl = p.ord_chunk_log2;
+    }
+    // Item of this queue's i-th grab (>= nitems: the queue is empty).
+    __device__ int item(int i) const {
+        const int64_t k = (((int64_t)queue + (int64_t)Q * (i >> cl)) << cl) + (i & ((1 << cl) - 1));
+        return k < nitems ? (int)k : nitems;
+    }
+    // Blocks of 2^cl entries times R heads, head-major inside a block; the
+    // last block holds the remaining P entries.
+    __device__ void decode(int k, int &e, int &rem) const {
+        const int cr = p.ord_r << cl;
+        const int full_items = p.ord_nblk * cr;
+        if (k < full_items) {
+            const int blk = div_by(k, cr, p.ord_m_cr), w = k - blk * cr;
+            rem = w >> cl;
+            e = (blk << cl) + (w & ((1 << cl) - 1));
+        } else {
+            const int w = k - full_items;
+            rem = div_by(w, p.ord_p, p.ord_m_p);
+            e = (p.ord_nblk << cl) + (w - rem * p.ord_p);
+        }
+    }
+};
+
+// Batch and head of head index rem of an entry of mask batch bm (with one
+// shared mask, rem runs over all batches and heads).
+__device__ inline void head_of(const AttnParams &p, int rem, int bm, int &b, int &h) {
+    b = p.mask_b == 1 ? rem / p.H : bm;
+    h = p.mask_b == 1 ? rem % p.H : rem;
+}
+
+// ceil(2^32 / d) for d >= 2 (host side; d <= 1 passes k through).
+inline uint32_t div_magic(int64_t d) {
+    return d <= 1 ? 0xffffffffu : (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d);
+}
+
+// Fills q's item-order fields and returns the grid size: head indices per
+// entry (every batch and head with one shared mask, the heads of the entry's
+// batch otherwise), chunks of up to 16 entries, at least four per queue.
+inline unsigned item_order(AttnParams &q) {
+    q.ord_r = q.mask_b == 1 ? q.B * q.H : q.H;
+    const int64_t nitems = (int64_t)q.mask_b * q.nt * q.ord_r;
+    int cl = 4;
+    while (cl > 0 && ((int64_t)1 << cl) * 4 * kQueues > nitems) --cl;
+    q.ord_chunk_log2 = cl;
+    const int nrows = q.mask_b * q.nt;
+    q.ord_nblk = nrows >> cl;
+    q.ord_p = nrows - (q.ord_nblk << cl);
+    q.ord_m_cr = div_magic((int64_t)q.ord_r << cl);
+    q.ord_m_p = div_magic(q.ord_p);
+    const int64_t nchunks = (nitems + (1 << cl) - 1) >> cl;
+    return (unsigned)((kQueues * ((nchunks + kQueues - 1) / kQueues)) << cl);
+}
+
 }  // namespace bsm

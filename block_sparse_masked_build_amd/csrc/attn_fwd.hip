@@ -157,16 +157,6 @@ __device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, co
 // end of the launch), arranged so that the rows running at the same time on
 // one XCD share key and value tiles (see ItemOrder).
 
-// One work-order record: (flat row, full tiles, partial tiles, first tile).
-struct WorkRec {
-    int packed, nfull, npart, first;
-};
-
-__device__ inline WorkRec load_rec(const int32_t *order, int e) {
-    const i32x4 r = *(const __attribute__((address_space(4))) i32x4 *)(order + 4 * (int64_t)e);
-    return {r.x, r.y, r.z, r.w};
-}
-
 // Wave-uniform values of the item being worked on.
 struct FwdArgs {
     const __bf16 *kb, *vb;
@@ -177,68 +167,13 @@ struct FwdArgs {
     ModK mk;  // folded score-modification constants
 };
 
-// Item order.  Item k is work-order entry e for head (and, with a shared
-// mask, batch entry) rem.  Items come in chunks of 2^ord_chunk_log2
-// consecutive entries of one head -- rows that mostly share key and value
-// tiles -- and chunk c is served by queue c % Q: workgroup b takes the
-// (b / Q)-th item of queue b % Q.  Workgroups are dispatched round-robin
-// over the XCDs, so with Q = 8 each queue runs on one XCD and the rows
-// running at the same time there share tiles through its L2; items leave
-// each queue in work order.  The host picks the chunk so that every queue
-// gets several chunks.
-constexpr int kQueues = 8;
-
-// Quotient k / d for 0 <= k < 2^31 and d >= 1, with m = ceil(2^32 / d)
-// computed on the host (d >= 2; d = 1 is passed through): the estimate is
-// q or q + 1.
-__device__ inline int div_by(int k, int d, uint32_t m) {
-    if (d == 1) return k;
-    int q = (int)(((uint64_t)(uint32_t)k * m) >> 32);
-    if ((int64_t)q * d > k) --q;
-    return q;
-}
-
-struct ItemOrder {
-    int nitems;  // B * H * QT, within int32 (checked on the host)
-    int Q, queue, cl;
-    const AttnParams &p;
-
-    __device__ ItemOrder(const AttnParams &p_, int G) : p(p_) {
-        nitems = p.mask_b * p.nt * p.ord_r;
-        Q = G < kQueues ? G : kQueues;
-        queue = blockIdx.x % Q;
-        cl = p.ord_chunk_log2;
-    }
-    // Item of this queue's i-th grab (>= nitems: the queue is empty).
-    __device__ int item(int i) const {
-        const int64_t k = (((int64_t)queue + (int64_t)Q * (i >> cl)) << cl) + (i & ((1 << cl) - 1));
-        return k < nitems ? (int)k : nitems;
-    }
-    // Blocks of 2^cl entries times R heads, head-major inside a block; the
-    // last block holds the remaining P entries.
-    __device__ void decode(int k, int &e, int &rem) const {
-        const int cr = p.ord_r << cl;
-        const int full_items = p.ord_nblk * cr;
-        if (k < full_items) {
-            const int blk = div_by(k, cr, p.ord_m_cr), w = k - blk * cr;
-            rem = w >> cl;
-            e = (blk << cl) + (w & ((1 << cl) - 1));
-        } else {
-            const int w = k - full_items;
-            rem = div_by(w, p.ord_p, p.ord_m_p);
-            e = (p.ord_nblk << cl) + (w - rem * p.ord_p);
-        }
-    }
-};
-
 template <bool ALIBI, bool SOFTCAP>
 __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &rec, FwdArgs &a) {
     const int nt = p.nt;
     const int packed = min(max(rec.packed, 0), p.mask_b * nt - 1);
     a.bm = packed / nt;
     a.row = packed - a.bm * nt;
-    a.b = p.mask_b == 1 ? rem / p.H : a.bm;
-    a.h = p.mask_b == 1 ? rem % p.H : rem;
+    head_of(p, rem, a.bm, a.b, a.h);
     a.kb = static_cast<const __bf16 *>(p.k) + a.b * p.k_sb + a.h * p.k_sh;
     a.vb = static_cast<const __bf16 *>(p.v) + a.b * p.v_sb + a.h * p.v_sh;
     a.fidx = p.full_kv_idx + (int64_t)packed * nt;
@@ -545,25 +480,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
 
 
 // ceil(2^32 / d) for d >= 1.
-uint32_t div_magic(int64_t d) { return d <= 1 ? 0xffffffffu : (uint32_t)(((1ull << 32) + (uint64_t)d - 1) / (uint64_t)d); }
-
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
-    const int64_t nitems = (int64_t)p.B * p.H * p.nt;
     AttnParams q = p;
-    q.ord_r = p.mask_b == 1 ? p.B * p.H : p.H;
-    // chunks of up to 16 entries, at least four per queue
-    int cl = 4;
-    while (cl > 0 && ((int64_t)1 << cl) * 4 * kQueues > nitems) --cl;
-    q.ord_chunk_log2 = cl;
-    const int nrows = p.mask_b * p.nt;
-    q.ord_nblk = nrows >> cl;
-    q.ord_p = nrows - (q.ord_nblk << cl);
-    q.ord_m_cr = div_magic((int64_t)q.ord_r << cl);
-    q.ord_m_p = div_magic(q.ord_p);
-    // one workgroup per (queue, grab index) pair; see fwd_kernel
-    const int64_t nchunks = (nitems + (1 << cl) - 1) >> cl;
-    const dim3 grid((unsigned)((kQueues * ((nchunks + kQueues - 1) / kQueues)) << cl)), block(kThreads);
+    const dim3 grid(item_order(q)), block(kThreads);  // one workgroup per (queue, grab index) pair
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
     if (alibi && cap)
