@@ -478,8 +478,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
         item_run<D, ALIBI, SOFTCAP, kPlain>(p, cur, tl, rm, qf, off, sm, o, m, l);
 }
 
-
-// ceil(2^32 / d) for d >= 1.
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
     AttnParams q = p;
