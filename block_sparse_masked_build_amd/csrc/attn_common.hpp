@@ -189,6 +189,15 @@ __device__ inline void copy16_to_lds_s(const void *gbase, uint32_t voff, uint32_
                  : "memory", "m0");
 }
 
+// Same with a base that is already wave-uniform (from uniform_u64), so the
+// per-copy offsets added to it stay scalar arithmetic.
+__device__ inline void copy16_to_lds_u(uint64_t gbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(gbase)
+                 : "memory", "m0");
+}
+
 // Same, 4 bytes per lane (lanes land at lds_base + 4 * lane).
 __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
@@ -215,7 +224,10 @@ __device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_r
     static_assert(kInstr >= 1, "at least one copy per wave");
     const int wv = wave_id(), lane = threadIdx.x & 63;
     const int64_t row_bytes = row_stride * 2;
-    const char *wbase = reinterpret_cast<const char *>(g_row0) + (int64_t)(wv * kInstr * kRowsPerInstr) * row_bytes;
+    // The wave's base goes to scalar registers once; the instructions'
+    // bases below it are scalar adds.
+    const uint64_t wbase = uniform_u64((uint64_t)(uintptr_t)(reinterpret_cast<const char *>(g_row0) +
+                                                             (int64_t)(wv * kInstr * kRowsPerInstr) * row_bytes));
     const int q = lane / L::kChunks;  // row inside the instruction's block
 #pragma unroll
     for (int x = 0; x < kInstr; ++x) {
@@ -224,8 +236,8 @@ __device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_r
         const int r16 = (x * kRowsPerInstr + q) & 15;
         const int c = (lane % L::kChunks) ^ tile_swizzle<D, SWZ>(r16);
         const uint32_t voff = (uint32_t)(q * row_bytes) + (uint32_t)(c * 16);
-        const char *xbase = wbase + (int64_t)(x * kRowsPerInstr) * row_bytes;
-        copy16_to_lds_s(xbase, voff, lds_tile + (uint32_t)((wv * kInstr + x) * kRowsPerInstr * L::kRowBytes));
+        const uint64_t xbase = wbase + (uint64_t)((int64_t)(x * kRowsPerInstr) * row_bytes);
+        copy16_to_lds_u(xbase, voff, lds_tile + (uint32_t)((wv * kInstr + x) * kRowsPerInstr * L::kRowBytes));
     }
 }
 
