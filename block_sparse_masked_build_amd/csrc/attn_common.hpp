@@ -588,20 +588,35 @@ __device__ inline void row_mask_flat(uint32_t sdoc, f32x16 (&s)[2], int key0, co
 // Maximum over a row-view step (32 scores per lane, both lane halves of a
 // query combined): four independent chains, then the lane-half exchange as
 // one cross-lane swap (no LDS round trip).
+// Maxima of scores, which are never NaN, as single v_max_f32 / v_max3_f32:
+// fmaxf first quiets inputs it cannot prove canonical (IEEE mode), up to
+// three instructions for one two-input maximum.
+__device__ inline float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+__device__ inline float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ inline float row_max(const f32x16 (&s)[2]) {
     float c[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int kb = x >> 1, r0 = (x & 1) * 8;
-        float v = fmaxf(fmaxf(s[kb][r0], s[kb][r0 + 1]), s[kb][r0 + 2]);
-        v = fmaxf(fmaxf(v, s[kb][r0 + 3]), s[kb][r0 + 4]);
-        v = fmaxf(fmaxf(v, s[kb][r0 + 5]), s[kb][r0 + 6]);
-        c[x] = fmaxf(v, s[kb][r0 + 7]);
+        float v = max3(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2]);
+        v = max3(v, s[kb][r0 + 3], s[kb][r0 + 4]);
+        v = max3(v, s[kb][r0 + 5], s[kb][r0 + 6]);
+        c[x] = max2(v, s[kb][r0 + 7]);
     }
-    const float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+    const float mx = max2(max3(c[0], c[1], c[2]), c[3]);
     const uint32_t u = __builtin_bit_cast(uint32_t, mx);
     const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    return max2(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
 }
 
 // Row view of the mask for query qpos (mask batch row bm): visible keys form
