@@ -96,6 +96,19 @@ __device__ inline float softcap_grad(float t, float inv_cap) {
     return 1.0f - th * th;
 }
 
+// Lane offsets of one pipeline step: those of a tile at LDS byte 0 moved by
+// `base` (a tile base and buffer).  The swizzles XOR bits 5-7 of an offset,
+// so adding a multiple of 256 before the XOR gives the same address as after
+// it.  The result is opaque, so derived addresses are formed per step
+// instead of being held in registers across the loop.
+__device__ inline KvOffsets step_offsets(const KvOffsets &off, uint32_t base) {
+    KvOffsets o;
+    o.row = off.row + (int)base;
+    o.tr = off.tr + (int)base;
+    asm volatile("" : "+v"(o.row), "+v"(o.tr));
+    return o;
+}
+
 // Start of pipeline step t (64 rows): step t covers half t%2 of listed tile
 // t/2 (full tiles first, then partial ones).
 __device__ inline int step_row0(int t, int nfull, const int32_t *fidx, const int32_t *pidx, int nt) {
@@ -137,6 +150,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
                                f32x16 (&dq)[D / 32]) {
     constexpr bool kMods = ALIBI || SOFTCAP;
     constexpr uint32_t kTB = DqLds<D>::kTileBytes;
+    static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto issue = [&](int t, int key0) {
         const uint32_t bf = t & 1;
         if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0);
@@ -156,26 +170,37 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
             issue(t + 1, key_next);
         }
         const uint32_t bf = t & 1;
-        const uint32_t sk = lds.k + bf * kTB, sv = lds.v + bf * kTB;
-        KvOffsets offt = off;  // opaque per step: derived offsets are not hoisted
-        asm volatile("" : "+v"(offt.row), "+v"(offt.tr));
+        // The buffer enters through the lane offsets, so that every read
+        // addresses a fixed tile base plus one swizzled offset (the base
+        // folds into the instruction's offset field).
+        const uint32_t sk = lds.k, sv = lds.v;
+        const KvOffsets offt = step_offsets(off, bf * kTB);
         const bool partial = (t >> 1) >= a.nfull;
         bool skip[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             skip[kb] = partial && block_none_visible<MODE>(rm, key0 + kb * 32, key0 + kb * 32 + 31);
 
+        // A skipped block takes scores of -inf (its probabilities are 0) and
+        // dP of 0; the others start their sums from the first product.  The
+        // fills are opaque so that the compiler keeps them on the skip branch
+        // instead of writing them ahead of every step's products.
         f32x16 s[2], dp[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (skip[kb]) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                s[kb][r] = 0.0f;
-                dp[kb][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) {
+                    asm volatile("v_mov_b32 %0, 0xff800000" : "=v"(s[kb][r]));  // -inf
+                    asm volatile("v_mov_b32 %0, 0" : "=v"(dp[kb][r]));
+                }
+                continue;
             }
-            if (skip[kb]) continue;
+            const f32x16 zero = {};
+            s[kb] = mfma32(read_rows_operand<D>(sk, offt, kb, 0), qf[0], zero);
+            dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, 0), gf[0], zero);
 #pragma unroll
-            for (int st = 0; st < D / 16; ++st) {
+            for (int st = 1; st < D / 16; ++st) {
                 s[kb] = mfma32(read_rows_operand<D>(sk, offt, kb, st), qf[st], s[kb]);
                 dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, st), gf[st], dp[kb]);
             }
@@ -363,12 +388,12 @@ struct DkdvLds {
 
 // Row operands (A of S = Q K^T and dP = dO V^T) of query block b.
 template <int D>
-__device__ inline void dkdv_read_rows(uint32_t sq, uint32_t sg, const KvOffsets &off, int b,
-                                      bf16x8 (&rq)[D / 16], bf16x8 (&rg)[D / 16]) {
+__device__ inline void dkdv_read_rows(const KvOffsets &oq, const KvOffsets &og, int b, bf16x8 (&rq)[D / 16],
+                                      bf16x8 (&rg)[D / 16]) {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        rq[st] = read_rows_operand<D>(sq, off, b, st);
-        rg[st] = read_rows_operand<D>(sg, off, b, st);
+        rq[st] = read_rows_operand<D>(0, oq, b, st);
+        rg[st] = read_rows_operand<D>(0, og, b, st);
     }
 }
 
@@ -440,14 +465,14 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
 
 // Transposed operands (A of dV^T += dO^T P and dK^T += Q^T dS) of block b.
 template <int D>
-__device__ inline void dkdv_read_cols(uint32_t sq, uint32_t sg, const KvOffsets &off, int b,
-                                      bf16x8 (&tq)[2][D / 32], bf16x8 (&tg)[2][D / 32]) {
+__device__ inline void dkdv_read_cols(const KvOffsets &oq, const KvOffsets &og, int b, bf16x8 (&tq)[2][D / 32],
+                                      bf16x8 (&tg)[2][D / 32]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            tg[s2][db] = read_cols_operand<D>(sg, off, b * 2 + s2, db);
-            tq[s2][db] = read_cols_operand<D>(sq, off, b * 2 + s2, db);
+            tg[s2][db] = read_cols_operand<D>(0, og, b * 2 + s2, db);
+            tq[s2][db] = read_cols_operand<D>(0, oq, b * 2 + s2, db);
         }
 }
 
@@ -469,15 +494,15 @@ __device__ inline void dkdv_acc(const bf16x8 (&tq)[2][D / 32], const bf16x8 (&tg
 // read during the dV / dK products of block b.
 template <int D, bool ALIBI, bool SOFTCAP, bool GATHER, bool MASKED>
 __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
-                                 const bf16x8 (&vf)[D / 16], const KvOffsets &off, uint32_t sq, uint32_t sg,
+                                 const bf16x8 (&vf)[D / 16], const KvOffsets &oq, const KvOffsets &og,
                                  uint32_t sl2, uint32_t sdl, uint32_t sdoc, int q0,
                                  f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
     constexpr int NB = kTile / 32;
     bf16x8 rq[D / 16], rg[D / 16];
     f32x16 s[2], dp[2];
-    dkdv_read_rows<D>(sq, sg, off, 0, rq, rg);
+    dkdv_read_rows<D>(oq, og, 0, rq, rg);
     dkdv_sdp<D>(rq, rg, kf, vf, s[0], dp[0]);
-    dkdv_read_rows<D>(sq, sg, off, 1, rq, rg);
+    dkdv_read_rows<D>(oq, og, 1, rq, rg);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int cur = b & 1;
@@ -485,8 +510,8 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf1
         bf16x8 pb[2], dsb[2];
         dkdv_grads<ALIBI, SOFTCAP, GATHER, MASKED>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb);
         bf16x8 tq[2][D / 32], tg[2][D / 32];
-        dkdv_read_cols<D>(sq, sg, off, b, tq, tg);
-        if (b + 2 < NB) dkdv_read_rows<D>(sq, sg, off, b + 2, rq, rg);
+        dkdv_read_cols<D>(oq, og, b, tq, tg);
+        if (b + 2 < NB) dkdv_read_rows<D>(oq, og, b + 2, rq, rg);
         dkdv_acc<D>(tq, tg, pb, dsb, dk, dv);
         __builtin_amdgcn_sched_barrier(0);  // keep each block's reads and products in their own window
     }
@@ -497,6 +522,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf1
                                  const bf16x8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
                                  int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
     constexpr uint32_t kTB = DkdvLds<D>::kTileBytes, kWB = kTile * 4;
+    static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto tile_q0 = [&](int it) {
         return clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull), a.nt) *
                kTile;
@@ -523,12 +549,12 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf1
             q_next = tile_q0(t + 1);
             issue(t + 1, q_next);
         }
-        KvOffsets offt = off;  // opaque per step: derived offsets are not hoisted
-        asm volatile("" : "+v"(offt.row), "+v"(offt.tr));
         const uint32_t bf = t & 1;
+        // Tile base and buffer enter through the lane offsets (see dq_main):
+        // the second tile's base lies beyond a read's 16-bit offset field.
+        const KvOffsets oq = step_offsets(off, lds.q + bf * kTB), og = step_offsets(off, lds.g + bf * kTB);
         dkdv_tile<D, ALIBI, SOFTCAP, GATHER, decltype(masked)::value>(
-            a, cm, kf, vf, offt, lds.q + bf * kTB, lds.g + bf * kTB, lds.l2 + bf * kWB, lds.delta + bf * kWB,
-            lds.doc + bf * kWB, q0, dk, dv);
+            a, cm, kf, vf, oq, og, lds.l2 + bf * kWB, lds.delta + bf * kWB, lds.doc + bf * kWB, q0, dk, dv);
         wait_lds_reads();  // this wave's reads of tile t are done before the next barrier
         q0 = q_next;
     };
