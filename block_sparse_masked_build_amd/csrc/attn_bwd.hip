@@ -232,7 +232,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void dq_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
     const int nt = p.nt;

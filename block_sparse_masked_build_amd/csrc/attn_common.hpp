@@ -692,6 +692,14 @@ __device__ inline WorkRec load_rec(const int32_t *order, int e) {
 // gets several chunks.
 constexpr int kQueues = 8;
 
+// Workgroups per CU that the row kernels (forward, dQ) are compiled for.
+// Both fit 66 KB of LDS and 256 registers per lane at two per CU.  At D = 64
+// without score modifications the loops fit 168 registers with no spill
+// inside them, and the LDS (33 KB) allows three: 12 waves per CU instead of
+// 8.  With score modifications at 168 registers the loops would spill.
+template <int D, bool MODS>
+constexpr int kWgPerCu = (D == 64 && !MODS) ? 3 : 2;
+
 // Quotient k / d for 0 <= k < 2^31 and d >= 1, with m = ceil(2^32 / d)
 // computed on the host (d >= 2; d = 1 is passed through): the estimate is
 // q or q + 1.

@@ -448,7 +448,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
 
 // One item per workgroup (workgroups past the last item exit at once).
 template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
     const ItemOrder ord(p, kQueues);
     const int k = ord.item(blockIdx.x / ord.Q);
