@@ -22,7 +22,8 @@
 //    copied HBM -> LDS once per 64-query step and read row-wise (S, dP) and
 //    transposed with ds_read_tr16_b64 (dV, dK) from the same copy.  The two
 //    accumulators take 128 registers per lane at D = 128, so the kernel runs
-//    one workgroup per CU with up to 512 registers per lane;
+//    one workgroup per CU with up to 512 registers per lane; at D = 64 it
+//    fits 256 registers (no spill in its loops) and runs two;
 //  * dq_kernel: one workgroup per (batch, head, 128-query tile) over the row
 //    lists, lane = query as in the forward: S^T = K Q^T, dP^T = V dO^T,
 //    dQ^T += K^T dS^T, with K and V copied per 64-key step and K read both
@@ -565,7 +566,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf1
 }
 
 template <int D, bool ALIBI, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
     const int nt = p.nt;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
