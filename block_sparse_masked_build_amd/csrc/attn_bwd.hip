@@ -11,8 +11,7 @@
 //   dQ = dS K,  dK = dS^T Q,  dV = P^T dO
 // (dS is the gradient of the raw product q.k, hence the scale factor).
 //
-// Three kernels, no atomics (results are deterministic):
-//  * delta_kernel: Delta and L per query row;
+// Two kernels, no atomics (results are deterministic):
 //  * dkdv_kernel: one workgroup of 4 waves per (batch, head, 128-key tile)
 //    over the transposed (per key tile) full and partial query-tile lists.
 //    Lane l of wave w owns key 32w + l%32 and keeps its K and V rows in
@@ -27,7 +26,9 @@
 //  * dq_kernel: one workgroup per (batch, head, 128-query tile) over the row
 //    lists, lane = query as in the forward: S^T = K Q^T, dP^T = V dO^T,
 //    dQ^T += K^T dS^T, with K and V copied per 64-key step and K read both
-//    ways; two workgroups per CU.
+//    ways; two workgroups per CU.  It runs first and also computes Delta
+//    and L of its rows from the row operands it loads anyway (plus the
+//    output rows), writing them to the workspace that dkdv_kernel reads.
 // Tile copies are asynchronous (global_load_lds) into double-buffered LDS,
 // issued one step ahead, one barrier per step.  On partial tiles, 32 x 32
 // blocks that hold no visible pair are skipped (no products at all), blocks
@@ -41,54 +42,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kHalf = 64;  // rows per pipeline step
-
-// ---------------------------------------------------------------- Delta, L
-
-// Workgroups of one (batch, head) take kDeltaRows consecutive query rows;
-// a thread reads 16 bytes of out and dO for each of its kDeltaPasses rows,
-// all loads issued before the first use.
-constexpr int kDeltaPasses = 4;
-
-template <int D>
-constexpr int delta_rows() { return kThreads / (D / 8) * kDeltaPasses; }
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void delta_kernel(AttnParams p) {
-    constexpr int LPR = D / 8;           // lanes per row
-    constexpr int RPI = kThreads / LPR;  // rows per pass
-    const int per_bh = p.T / delta_rows<D>();  // T is a multiple of 128, delta_rows<D>() divides it
-    const int bh = blockIdx.x / per_bh;
-    const int b = bh / p.H, h = bh - b * p.H;
-    const int t0 = (blockIdx.x - bh * per_bh) * delta_rows<D>() + threadIdx.x / LPR;
-    const int c = (threadIdx.x % LPR) * 8;
-    const __bf16 *ob = static_cast<const __bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + c;
-    const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh + c;
-    u32x4 o[kDeltaPasses], g[kDeltaPasses];
-#pragma unroll
-    for (int k = 0; k < kDeltaPasses; ++k) {
-        const int64_t t = t0 + k * RPI;
-        o[k] = *reinterpret_cast<const u32x4 *>(ob + t * p.o_st);
-        g[k] = *reinterpret_cast<const u32x4 *>(gb + t * p.do_st);
-    }
-#pragma unroll
-    for (int k = 0; k < kDeltaPasses; ++k) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float ov = __builtin_bit_cast(float, u16_at(o[k], e) << 16);
-            const float gv = __builtin_bit_cast(float, u16_at(g[k], e) << 16);
-            acc += ov * gv;
-        }
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (threadIdx.x % LPR == 0) {
-            const int64_t r = (int64_t)bh * p.T + t0 + k * RPI;  // [B, H, T] contiguous
-            p.delta[r] = acc;
-            const float lse = p.lse[r];
-            p.lse2[r] = lse == -INFINITY ? 0.0f : lse * kLog2e;
-        }
-    }
-}
 
 // Soft-cap derivative from the log2-domain capped score t = cap tanh(.) log2 e:
 // 1 - tanh^2, with tanh clamped so that masked scores (-inf) give 0.
@@ -255,6 +208,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
 
     const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
     const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    const __bf16 *obr = static_cast<const __bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qpos * p.o_st;
 
     DqArgs a;
     a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -275,8 +229,8 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     a.inv_cap = 1.0f / a.cap;
     a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
     const int64_t row_bh = ((int64_t)b * p.H + h) * p.T + qpos;
-    a.l2 = p.lse2[row_bh];
-    a.delta = p.delta[row_bh];
+    const float lse = p.lse[row_bh];
+    a.l2 = lse == -INFINITY ? 0.0f : lse * kLog2e;
     const int nsteps = 2 * (a.nfull + npart);
 
     RowMask rm;
@@ -289,10 +243,27 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     lds.doc = lds_addr(&sm.doc[0][0]);
 
     bf16x8 qf[D / 16], gf[D / 16];
+    u32x4 of[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
         qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
         gf[st] = *reinterpret_cast<const bf16x8 *>(gb + (int64_t)qpos * p.do_st + st * 16 + hl * 8);
+        of[st] = *reinterpret_cast<const u32x4 *>(obr + st * 16 + hl * 8);
+    }
+    // Delta = <dO, out> of this lane's query: each lane half holds half of
+    // the row's columns.  Delta and L go to the workspace for dkdv_kernel.
+    {
+        float acc = 0.0f;
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc += __builtin_bit_cast(float, u16_at(of[st], e) << 16) * static_cast<float>(gf[st][e]);
+        a.delta = acc + __shfl_xor(acc, 32);
+        if (hl == 0) {
+            p.delta[row_bh] = a.delta;
+            p.lse2[row_bh] = a.l2;
+        }
     }
     f32x16 dq[D / 32];
 #pragma unroll
@@ -661,15 +632,14 @@ template <int D, bool ALIBI, bool SOFTCAP>
 void launch_main(const AttnParams &p, hipStream_t stream) {
     AttnParams q = p;
     const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
-    hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP>), dkdv_grid, block, 0, stream, q);
+    // dq_kernel writes Delta and L of every query row (every row is one of
+    // its items), which dkdv_kernel reads.
     hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP>), dq_grid, block, 0, stream, q);
+    hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP>), dkdv_grid, block, 0, stream, q);
 }
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
-    static_assert(kTile % delta_rows<D>() == 0, "delta workgroups tile every query tile");
-    const int64_t blocks = (int64_t)p.B * p.H * (p.T / delta_rows<D>());
-    hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
     if (alibi && cap)
