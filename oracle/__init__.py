@@ -10,7 +10,8 @@ Modules:
   block_mask  -- per-tile visible-pair counts (brute force, C with a numpy
                  check path), tile classes and the compacted tile lists
   attention   -- fp64 softmax attention forward and backward, per row and per
-                 key column, with the ALiBi and soft-cap score modifications
+                 key column, with the ALiBi and soft-cap score modifications,
+                 and the gradient with respect to the ALiBi slopes
 """
 from .predicate import visible  # noqa: F401
 from .block_mask import (  # noqa: F401
@@ -28,4 +29,5 @@ from .attention import (  # noqa: F401
     backward_dense,
     backward_dq_rows,
     backward_dkdv_cols,
+    slope_grad_dense,
 )

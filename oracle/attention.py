@@ -30,6 +30,13 @@ Pattern 3):
   dQ_q = scale sum_j g_qj k_j,  dK_j = scale sum_q g_qj q_q,
   dV_j = sum_q p_qj dO_q
 
+Gradient of the same loss with respect to the ALiBi slope of head h (the
+pages: a learned relative-position bias trains through the fused backward --
+tutorial, Pattern 3).  The slope enters every visible score through
+u_qj = ... - slope[h] (q - j), so
+  dL/dslope[h] = sum over b and visible (q, j) of g_qj (j - q)
+with g as above (the gradient with respect to u).
+
 Arithmetic columns: by default only keys visible to at least one query of the
 row block take part in the arithmetic; the others would enter the softmax as
 exp(-inf) = 0 exactly (the tutorial notes that a -inf score is numerically the
@@ -183,3 +190,22 @@ def backward_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None):
         dK += sc * (g.T @ Q[r])
         dV += p.T @ dO[r]
     return dK, dV
+
+
+def slope_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None):
+    """(dL/dslope[h] for batch element b, sum of |g_qj (j - q)|) over every
+    visible pair (small T).  The second value bounds the sum's conditioning:
+    the rows of g sum to zero without a cap, so the terms cancel heavily."""
+    T, D = Q.shape
+    sc = _scale(D, scale)
+    out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
+    allcols = np.arange(T)
+    total = 0.0
+    mass = 0.0
+    for a in range(0, T, ROW_CHUNK):
+        r = np.arange(a, min(T, a + ROW_CHUNK))
+        g, _ = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc)
+        term = g * (allcols[None, :] - r[:, None]).astype(np.float64)
+        total += float(term.sum())
+        mass += float(np.abs(term).sum())
+    return total, mass

@@ -250,3 +250,49 @@ def test_sampled_backward_paths_match_dense():
     dk, dv = oracle.backward_dkdv_cols(Q, K, V, dO, spec, mod, 0, 3, cols)
     np.testing.assert_allclose(dk, dK[cols], rtol=0, atol=1e-12)
     np.testing.assert_allclose(dv, dV[cols], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", [1, 3])
+def test_slope_gradient_finite_differences(case):
+    """dL/dslope[h] against central differences of the fp64 forward in the
+    slope (cases with ALiBi; case 1 also has the soft-cap)."""
+    Tt, Dd = 256, 16
+    spec, mod = _specs_for_bwd(Tt)[case]
+    Q, K, V, dO = (_rand((Tt, Dd), 70 + s) for s in range(4))
+    h = 1
+    gs, mass = oracle.slope_grad_dense(Q, K, V, dO, spec, mod, 0, h)
+    assert mass > 0
+
+    def loss(slope):
+        sl = np.array(mod.alibi_slopes, dtype=np.float64).copy()
+        sl[h] = slope
+        m2 = ScoreModData(alibi_slopes=sl, softcap=mod.softcap)
+        o, _ = oracle.forward_dense(Q, K, V, spec, m2, 0, h)
+        return float(np.sum(o * dO))
+
+    s0 = float(mod.alibi_slopes[h])
+    eps = 1e-7
+    fd = (loss(s0 + eps) - loss(s0 - eps)) / (2 * eps)
+    assert abs(fd - gs) <= 1e-6 * max(1.0, abs(fd)), (fd, gs)
+
+
+@pytest.mark.parametrize("case", [1, 3])
+def test_slope_gradient_matches_autograd(case):
+    """The same gradient through torch.autograd on a dense explicit-mask fp64
+    reference with the slope as a leaf tensor."""
+    Tt, Dd = 256, 16
+    spec, mod = _specs_for_bwd(Tt)[case]
+    Q, K, V, dO = (_rand((Tt, Dd), 80 + s) for s in range(4))
+    h = 0
+    gs, _ = oracle.slope_grad_dense(Q, K, V, dO, spec, mod, 0, h)
+    m = torch.from_numpy(oracle.visible(spec, 0, np.arange(Tt)[:, None], np.arange(Tt)[None, :]))
+    slope = torch.tensor(float(mod.alibi_slopes[h]), dtype=torch.float64, requires_grad=True)
+    q, k, v = (torch.from_numpy(x) for x in (Q, K, V))
+    pos = torch.arange(Tt, dtype=torch.float64)
+    s = (q @ k.T) / math.sqrt(Dd) - slope * (pos[:, None] - pos[None, :])
+    if mod.softcap is not None:
+        s = mod.softcap * torch.tanh(s / mod.softcap)
+    s = s.masked_fill(~m, -math.inf)
+    p = torch.nan_to_num(torch.softmax(s, dim=1), nan=0.0)
+    (p @ v).backward(torch.from_numpy(dO))
+    assert abs(slope.grad.item() - gs) <= 1e-9 * max(1.0, abs(gs)), (slope.grad.item(), gs)
