@@ -40,7 +40,7 @@ class BsmBlockMask(ctypes.Structure):
 
 class BsmScoreMod(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("alibi_slopes", ctypes.c_void_p),
-                ("softcap", ctypes.c_float)]
+                ("softcap", ctypes.c_float), ("alibi_slopes_grad", ctypes.c_void_p)]
 
 
 class BsmTensor(ctypes.Structure):

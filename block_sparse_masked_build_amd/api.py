@@ -73,7 +73,7 @@ class ScoreMod:
         if self.softcap is not None:
             f |= BSM_MOD_SOFTCAP
         return BsmScoreMod(f, self.alibi_slopes.data_ptr() if self.alibi_slopes is not None else None,
-                           float(self.softcap) if self.softcap is not None else 0.0)
+                           float(self.softcap) if self.softcap is not None else 0.0, None)
 
 
 class BlockMask(NamedTuple):
@@ -200,8 +200,11 @@ def bwd_workspace(B: int, H: int, T: int, D: int, device="cuda") -> torch.Tensor
 
 def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: MaskSpec,
                        mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
-                       dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None):
-    """Returns (dq, dk, dv), bf16 [B,H,T,D]."""
+                       dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
+                       dslopes: Optional[torch.Tensor] = None):
+    """Returns (dq, dk, dv), bf16 [B,H,T,D].  With ALiBi, a float32 [H]
+    device tensor passed as dslopes receives dL/dslope (summed over the
+    batch)."""
     B, H, T, D = q.shape
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -213,6 +216,12 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
     cb = block_mask.c_struct()
     cs = spec.c_struct()
     cm = mod.c_struct() if mod is not None else None
+    if dslopes is not None:
+        if cm is None or mod.alibi_slopes is None:
+            raise ValueError("dslopes needs a score_mod with ALiBi slopes")
+        if dslopes.dtype != torch.float32 or dslopes.numel() != H or not dslopes.is_contiguous():
+            raise ValueError("dslopes must be a contiguous float32 tensor of H elements")
+        cm.alibi_slopes_grad = dslopes.data_ptr()
     check(lib.bsm_flex_attention_bwd(
         B, H, T, D, *[ctypes.byref(t) for t in ts[:4]], lse.data_ptr(), ctypes.byref(ts[4]),
         ctypes.byref(cb), ctypes.byref(cs), ctypes.byref(cm) if cm is not None else None,

@@ -90,6 +90,7 @@ struct DqSmem {
     __bf16 k[2][kHalf * D];  // fkv swizzle
     __bf16 v[2][kHalf * D];  // fkv swizzle
     int32_t doc[2][kHalf];
+    float red[kThreads / 64];  // per-wave sums of the slope gradient
 };
 
 template <int D>
@@ -98,10 +99,16 @@ struct DqLds {
     uint32_t k, v, doc;  // buffer 0; buffer 1 follows
 };
 
-template <int D, bool ALIBI, bool SOFTCAP, int MODE>
+// SGRAD (with ALiBi only): also sums g_qk (k - q) over the visible keys of
+// this lane's query into sg, the lane's share of dL/dslope[h] (g is dS
+// before the scale, the gradient with respect to the score the ALiBi term
+// is added to).  Per step, with the score at key key0 + 4 hl + c:
+//   sum g (k - q) = sum g c + (key0 + 4 hl - q) sum g.
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE>
 __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 (&qf)[D / 16],
                                const bf16x8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
-                               f32x16 (&dq)[D / 32]) {
+                               f32x16 (&dq)[D / 32], float &sg) {
+    static_assert(!SGRAD || ALIBI, "the slope gradient needs the ALiBi term");
     constexpr bool kMods = ALIBI || SOFTCAP;
     constexpr uint32_t kTB = DqLds<D>::kTileBytes;
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
@@ -161,6 +168,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
         }
         row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial);
         bf16x8 dsb[2][2];
+        float sg_c = 0.0f, sg_s = 0.0f;  // SGRAD: sum ds c and sum ds over the step
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -170,7 +178,15 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
                 float ds = pv * (dp[kb][r] - a.delta);
                 if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
                 dsb[kb][r >> 3][r & 7] = static_cast<__bf16>(ds);
+                if (SGRAD) {
+                    sg_c = __builtin_fmaf(ds, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), sg_c);
+                    sg_s += ds;
+                }
             }
+        if (SGRAD) {
+            const int hl = (threadIdx.x & 63) >> 5;
+            sg = __builtin_fmaf((float)(key0 + 4 * hl - a.qpos), sg_s, sg + sg_c);
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (skip[kb]) continue;
@@ -185,7 +201,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP>
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
@@ -275,12 +291,24 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     // uses only become more conservative with copies in flight, and the
     // first pipeline step waits for everything.
 
+    float sg = 0.0f;
     if (mode == kGather)
-        dq_main<D, ALIBI, SOFTCAP, kGather>(a, rm, qf, gf, off, lds, nsteps, dq);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else if (mode == kSinks)
-        dq_main<D, ALIBI, SOFTCAP, kSinks>(a, rm, qf, gf, off, lds, nsteps, dq);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else
-        dq_main<D, ALIBI, SOFTCAP, kPlain>(a, rm, qf, gf, off, lds, nsteps, dq);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+
+    // Slope gradient of the item: wave sums by a fixed butterfly, then the
+    // four waves in order, one partial per (batch, head, query tile).
+    if (SGRAD) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sg += __shfl_xor(sg, o);
+        if (lane == 0) sm.red[wv] = sg;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            p.dslope_part[((int64_t)b * p.H + h) * nt + i] = ((sm.red[0] + sm.red[1]) + sm.red[2]) + sm.red[3];
+    }
 
     // dQ rows of the wave, staged through the K buffers once every wave is
     // done with them (dS was accumulated without the scale).
@@ -622,6 +650,27 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice);
 }
 
+// dL/dslope[h]: the per-(batch, head, query tile) partials of dq_kernel
+// summed over the batch and the query tiles in a fixed order (strided
+// per-thread sums, then a fixed tree), so the result is deterministic.
+__global__ __launch_bounds__(kThreads) void slope_reduce_kernel(const float *part, float *dslopes, int B, int H,
+                                                                  int nt) {
+    __shared__ float red[kThreads];
+    const int h = blockIdx.x, n = B * nt;
+    float acc = 0.0f;
+    for (int j = threadIdx.x; j < n; j += kThreads) {
+        const int b = j / nt, i = j - b * nt;
+        acc += part[((int64_t)b * H + h) * nt + i];
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) dslopes[h] = red[0];
+}
+
 // dq_kernel runs the rows in the forward's item order (longest rows first,
 // neighbouring rows of a head together on an XCD); dkdv_kernel runs one
 // workgroup per (batch, head, key tile), early key tiles first.  Measured on
@@ -634,7 +683,13 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
     const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
     // dq_kernel writes Delta and L of every query row (every row is one of
     // its items), which dkdv_kernel reads.
-    hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP>), dq_grid, block, 0, stream, q);
+    if (ALIBI && p.dslopes) {
+        hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI>), dq_grid, block, 0, stream, q);
+        hipLaunchKernelGGL(slope_reduce_kernel, dim3(p.H), block, 0, stream, p.dslope_part, p.dslopes, p.B, p.H,
+                           p.nt);
+    } else {
+        hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false>), dq_grid, block, 0, stream, q);
+    }
     hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP>), dkdv_grid, block, 0, stream, q);
 }
 

@@ -92,6 +92,8 @@ bsm_status check_mod(const bsm_score_mod *mod) {
         return fail(BSM_E_INVALID, "ALIBI without slopes");
     if ((mod->flags & BSM_MOD_SOFTCAP) && !(mod->softcap > 0.0f && std::isfinite(mod->softcap)))
         return fail(BSM_E_INVALID, "SOFTCAP needs a finite cap > 0");
+    if (mod->alibi_slopes_grad && !(mod->flags & BSM_MOD_ALIBI))
+        return fail(BSM_E_INVALID, "alibi_slopes_grad given without ALIBI");
     return BSM_OK;
 }
 
@@ -131,6 +133,8 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
     p.window = spec->window;
     p.mod_flags = mod ? mod->flags : 0u;
     p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
+    p.dslopes = nullptr;  // set by the backward only
+    p.dslope_part = nullptr;
     p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
     p.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
     p.kv_num = bm->kv_num_blocks;
@@ -226,7 +230,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
 
 size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D) {
     if (B < 1 || H < 1 || bad_T(T) || (D != 64 && D != 128)) return 0;
-    return 2 * align256((size_t)B * H * T * sizeof(float));
+    return 2 * align256((size_t)B * H * T * sizeof(float)) + align256((size_t)B * H * (T / 128) * sizeof(float));
 }
 
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_tensor *q,
@@ -272,6 +276,9 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     p.lse = const_cast<float *>(lse);
     p.delta = static_cast<float *>(workspace);
     p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)B * H * T * sizeof(float)));
+    p.dslope_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                              2 * align256((size_t)B * H * T * sizeof(float)));
+    p.dslopes = (mod && (mod->flags & BSM_MOD_ALIBI)) ? mod->alibi_slopes_grad : nullptr;
     return hip_status(bsm::launch_attn_bwd(p, D, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_bwd launch");
 }

@@ -64,6 +64,8 @@ struct AttnParams {
     float *lse;      // [B, H, T]
     float *delta;    // [B, H, T] (backward workspace): <dO, out> per query
     float *lse2;     // [B, H, T] (backward workspace): lse * log2(e), 0 where lse = -inf
+    float *dslope_part;  // [B, H, nt] (backward workspace): slope-gradient partial per query tile
+    float *dslopes;      // [H] backward output dL/dslope, or NULL (not computed)
     // forward item order: items per work-order entry, full blocks, entries in
     // the last block, and division magic numbers (set by the launcher)
     int32_t ord_r, ord_chunk_log2, ord_nblk, ord_p;

@@ -144,6 +144,14 @@ typedef struct {
     uint32_t flags;              /* BSM_MOD_* bits                   */
     const float *alibi_slopes;   /* ALIBI: device float32 [H]         */
     float softcap;               /* SOFTCAP: cap value c > 0          */
+    float *alibi_slopes_grad;    /* ALIBI, backward only: NULL, or device
+                                    float32 [H] that bsm_flex_attention_bwd
+                                    overwrites with dL/dslope[h], summed over
+                                    the batch (a learned bias trains through the
+                                    fused backward: tutorial "FlexAttention in
+                                    PyTorch", Pattern 3).  Non-NULL without
+                                    ALIBI is BSM_E_INVALID; the forward
+                                    ignores it.                        */
 } bsm_score_mod;
 
 /* bf16 tensor [B, H, T, D]; element (b,h,t,d) lives at
@@ -191,7 +199,9 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   float scale, const bsm_tensor *out, float *lse,
                                   void *stream);
 
-/* Bytes of device workspace bsm_flex_attention_bwd needs. */
+/* Bytes of device workspace bsm_flex_attention_bwd needs: Delta and
+ * lse log2(e) per query (2 x B*H*T floats) and one slope-gradient partial per
+ * (batch, head, query tile), each part rounded up to 256 bytes. */
 size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D);
 
 /* Backward attention: gradients of sum(out * dout) with respect to q, k, v
@@ -200,6 +210,9 @@ size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D);
  * fused backward).  Visits exactly the tiles the block mask lists.
  * out and lse are the forward's outputs for the same inputs.
  * dq, dk, dv: bf16 [B, H, T, D], fully overwritten.
+ * mod->alibi_slopes_grad (optional, ALIBI): dL/dslope[h] = sum over the batch
+ * and the visible pairs of g_qk (k - q), with g the gradient with respect to
+ * the score the ALiBi term is added to; deterministic (fixed-order sums).
  * workspace: device, >= bsm_bwd_workspace_bytes(), 256-byte aligned.
  * Errors: as the forward, plus BSM_E_WORKSPACE. */
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,

@@ -192,13 +192,17 @@ def backward_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None):
     return dK, dV
 
 
-def slope_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None):
+def slope_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=None):
     """(dL/dslope[h] for batch element b, sum of |g_qj (j - q)|) over every
     visible pair (small T).  The second value bounds the sum's conditioning:
-    the rows of g sum to zero without a cap, so the terms cancel heavily."""
+    the rows of g sum to zero without a cap, so the terms cancel heavily.
+    out, lse: the forward's outputs as a backward receives them (its inputs
+    Delta = <dO, out> and p = exp(s - lse) are formed from them); by default
+    they are computed here in fp64."""
     T, D = Q.shape
     sc = _scale(D, scale)
-    out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
+    if out is None or lse is None:
+        out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
     allcols = np.arange(T)
     total = 0.0
     mass = 0.0

@@ -120,6 +120,7 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
     (dict(mod=BsmScoreMod(2, None, 0.0)), _lib.BSM_E_INVALID),        # cap must be > 0
     (dict(mod=BsmScoreMod(2, None, float("inf"))), _lib.BSM_E_INVALID),
     (dict(mod=BsmScoreMod(8, None, 1.0)), _lib.BSM_E_INVALID),
+    (dict(mod=BsmScoreMod(2, None, 1.0, FAKE)), _lib.BSM_E_INVALID),  # slope gradient without ALiBi
     (dict(scale=float("nan")), _lib.BSM_E_INVALID),
 ])
 def test_fwd_rejects(kw, code):
@@ -137,7 +138,20 @@ def test_bwd_rejects_small_workspace_and_missing_transposed_lists():
             1, 1, 1024, 64, *([ctypes.byref(t)] * 4), FAKE, ctypes.byref(t), ctypes.byref(bm),
             ctypes.byref(spec), None, 0.0, *([ctypes.byref(t)] * 3), ws, n, None)
 
+    assert need == 2 * 4096 + 256  # Delta and lse log2 e per query, one slope partial per query tile
     assert call(_bm(), FAKE, need - 4) == _lib.BSM_E_WORKSPACE
     assert call(_bm(), None, need) == _lib.BSM_E_WORKSPACE
     for i in range(4, 8):
         assert call(_bm(null=i), FAKE, need) == _lib.BSM_E_INVALID
+
+
+def test_bwd_rejects_slope_gradient_without_alibi():
+    spec = _spec()
+    t = _t()
+    need = lib.bsm_bwd_workspace_bytes(1, 1, 1024, 64)
+    mod = BsmScoreMod(2, None, 30.0, FAKE)
+    rc = lib.bsm_flex_attention_bwd(
+        1, 1, 1024, 64, *([ctypes.byref(t)] * 4), FAKE, ctypes.byref(t), ctypes.byref(_bm()),
+        ctypes.byref(spec), ctypes.byref(mod), 0.0, *([ctypes.byref(t)] * 3), FAKE, need, None)
+    assert rc == _lib.BSM_E_INVALID
+    assert "alibi_slopes_grad" in lib.bsm_last_error().decode()

@@ -296,3 +296,20 @@ def test_slope_gradient_matches_autograd(case):
     p = torch.nan_to_num(torch.softmax(s, dim=1), nan=0.0)
     (p @ v).backward(torch.from_numpy(dO))
     assert abs(slope.grad.item() - gs) <= 1e-9 * max(1.0, abs(gs)), (slope.grad.item(), gs)
+
+
+def test_slope_gradient_takes_the_backward_inputs():
+    """Passing the forward's own fp64 out and lse reproduces the default
+    exactly, and rounding out to bf16 moves the result by no more than the
+    Delta change it causes: |dDelta_q| * sum_j p_qj |j - q| <= |dDelta_q| * T."""
+    Tt, Dd = 256, 16
+    spec, mod = _specs_for_bwd(Tt)[1]
+    Q, K, V, dO = (_rand((Tt, Dd), 90 + s) for s in range(4))
+    gs, mass = oracle.slope_grad_dense(Q, K, V, dO, spec, mod, 0, 1)
+    out, lse = oracle.forward_dense(Q, K, V, spec, mod, 0, 1)
+    gs2, mass2 = oracle.slope_grad_dense(Q, K, V, dO, spec, mod, 0, 1, out=out, lse=lse)
+    assert gs2 == gs and mass2 == mass
+    out_b = torch.from_numpy(out).to(torch.bfloat16).double().numpy()
+    gs3, _ = oracle.slope_grad_dense(Q, K, V, dO, spec, mod, 0, 1, out=out_b, lse=lse)
+    bound = float(np.sum(np.abs(np.sum(dO * (out_b - out), axis=1)))) * Tt
+    assert gs3 != gs and abs(gs3 - gs) <= bound
