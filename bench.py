@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="2",
                     help="1, 2, 2-causal, 2-window, 2-chunks, 3, 4a, 4b, 5")
     ap.add_argument("--fwd-only", action="store_true", help="leave the backward out of the step")
+    ap.add_argument("--slopes", action="store_true",
+                    help="the backward also returns dL/dslope (workloads with ALiBi)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="time budget of the oracle sample")
@@ -140,9 +142,14 @@ def main():
     ws = api.block_mask_workspace(spec)
     out = torch.empty_like(dev["q"])
     lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
+    dslopes = None
     if backward:
         dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
         bws = api.bwd_workspace(w.B, w.H, w.T, w.D)
+        if args.slopes:
+            if mod is None or mod.alibi_slopes is None:
+                sys.exit("--slopes needs a workload with ALiBi (5)")
+            dslopes = torch.empty(w.H, dtype=torch.float32, device="cuda")
     windows = w.windows or [None]
 
     def step(s):
@@ -157,7 +164,7 @@ def main():
         ev[2].record()
         if backward:
             api.flex_attention_bwd(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], bm, spec, mod,
-                                   dq=dq, dk=dk, dv=dv, workspace=bws)
+                                   dq=dq, dk=dk, dv=dv, workspace=bws, dslopes=dslopes)
         ev[3].record()
         return ev, win
 
@@ -211,6 +218,7 @@ def main():
         bwd_flops = fwd_flops * 2.5
         extra["bwd_us_median"] = float(np.median(bwd_ms) * 1e3)
         extra["bwd_tflops"] = float(bwd_flops.sum() / (bwd_ms.sum() * 1e-3) / 1e12)
+        extra["bwd_slope_grad"] = dslopes is not None
     line = {
         "metric": METRIC,
         "value": round(float(achieved), 3),
@@ -232,7 +240,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(float(achieved / PEAK_BF16_TFLOPS), 4),
             "traffic": measured_traffic() if args.workload == "2" else None,
-            "kernel": "fwd_kernel<128,false,false>" if w.D == 128 else "fwd_kernel<64,...>",
+            "kernel": "fwd_kernel<%d,%s,%s>" % (w.D, str(w.mod.alibi_slopes is not None).lower(),
+                                                str(w.mod.softcap is not None).lower()),
         },
         "detail": extra,
     }
