@@ -49,13 +49,14 @@ def build_c(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            build_c()
+        src = os.path.join(os.path.dirname(_LIB_PATH), "tile_counts.c")
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+            build_c(force=True)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_tile_counts.restype = ctypes.c_int
         lib.oracle_tile_counts.argtypes = [
             ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -70,6 +71,8 @@ def _flags(spec) -> int:
         f |= 4
         if spec.sinks:
             f |= 8
+    if spec.causal and getattr(spec, "prefix", 0):
+        f |= 16
     return f
 
 
@@ -88,7 +91,7 @@ def tile_counts(spec) -> np.ndarray:
         T, mb, _flags(spec),
         docs.ctypes.data if docs is not None else None,
         int(spec.window) if spec.window is not None else 0,
-        int(spec.sinks), out.ctypes.data)
+        int(spec.sinks), int(getattr(spec, "prefix", 0)), out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_tile_counts rejected the spec")
     return out

@@ -12,7 +12,9 @@
  * The predicate is evaluated for every single pair, exactly as written on the
  * pages: causal (q >= kv), same document (docs[q] == docs[kv]), window
  * (q - kv < window), sinks (kv < SINKS) OR-ed with the window
- * (speedrun notes, code listing; tutorial, Patterns 1 and 2).
+ * (speedrun notes, code listing; tutorial, Patterns 1 and 2), prefix
+ * (kv < PREFIX) OR-ed with the causal term (prefix-LM masking, named in the
+ * tutorial's introduction).
  *
  * No shortcut, no interval reasoning, no pruning: O(T^2) work per mask.
  * Only tests/, the smoke check and the benchmark's CPU baseline use this.
@@ -22,14 +24,18 @@
 
 #define ORACLE_TILE 128
 
-/* flags: bit0 causal, bit1 document, bit2 window, bit3 sinks */
+/* flags: bit0 causal, bit1 document, bit2 window, bit3 sinks, bit4 prefix */
 static inline int visible_pair(int64_t q, int64_t kv, int flags,
                                const int32_t *docs, int64_t window,
-                               int64_t sinks)
+                               int64_t sinks, int64_t prefix)
 {
     int ok = 1;
-    if (flags & 1)
-        ok = ok && (q >= kv);
+    if (flags & 1) {
+        int c = q >= kv;
+        if (flags & 16)
+            c = c || (kv < prefix);
+        ok = ok && c;
+    }
     if (flags & 2)
         ok = ok && (docs[q] == docs[kv]);
     if (flags & 4) {
@@ -48,7 +54,8 @@ static inline int visible_pair(int64_t q, int64_t kv, int flags,
  * Returns 0 on success, -1 if T is not a positive multiple of 128.
  */
 int oracle_tile_counts(int64_t T, int mask_b, int flags, const int32_t *docs,
-                       int64_t window, int64_t sinks, int32_t *counts)
+                       int64_t window, int64_t sinks, int64_t prefix,
+                       int32_t *counts)
 {
     if (T <= 0 || T % ORACLE_TILE != 0 || mask_b <= 0)
         return -1;
@@ -62,7 +69,7 @@ int oracle_tile_counts(int64_t T, int mask_b, int flags, const int32_t *docs,
                 int32_t n = 0;
                 for (int64_t q = i * ORACLE_TILE; q < (i + 1) * ORACLE_TILE; ++q)
                     for (int64_t kv = j * ORACLE_TILE; kv < (j + 1) * ORACLE_TILE; ++kv)
-                        n += visible_pair(q, kv, flags, d, window, sinks);
+                        n += visible_pair(q, kv, flags, d, window, sinks, prefix);
                 c[i * nt + j] = n;
             }
         }

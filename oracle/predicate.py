@@ -7,11 +7,17 @@ Follows:
     (docs[q] == docs[kv]) and inside the window (q - kv < window);
   * tutorial "FlexAttention in PyTorch", Pattern 1 (document mask, causal and
     same document) and Pattern 2 (causal AND (in window OR sink), sink being
-    kv < SINKS).
+    kv < SINKS);
+  * prefix-LM masking, which the tutorial's introduction lists among the
+    variants: the keys of a prefix are seen by every query (bidirectional
+    inside the prefix), the rest causally.
 
-Reading taken where the pages leave it open: the sink term only widens the
+Readings taken where the pages leave it open: the sink term only widens the
 window term (without a window there is nothing for it to widen), and it is
-AND-ed with causality and the document term like every other term.
+AND-ed with causality and the document term like every other term.  The
+prefix term kv < PREFIX likewise only widens the causal term (q >= kv OR
+kv < PREFIX; without causality every key is already allowed) and is AND-ed
+with the document and window terms.
 """
 from __future__ import annotations
 
@@ -30,7 +36,10 @@ def visible(spec, b, q_idx, kv_idx) -> np.ndarray:
     kv = np.asarray(kv_idx, dtype=np.int64)
     ok = np.ones(np.broadcast_shapes(q.shape, kv.shape), dtype=bool)
     if spec.causal:
-        ok &= q >= kv
+        causal_ok = q >= kv
+        if getattr(spec, "prefix", 0):
+            causal_ok = causal_ok | (kv < spec.prefix)
+        ok &= causal_ok
     if spec.document:
         docs = spec.doc_ids[b if spec.doc_ids.shape[0] > 1 else 0].astype(np.int64)
         ok &= docs[q] == docs[kv]

@@ -313,3 +313,15 @@ def test_slope_gradient_takes_the_backward_inputs():
     gs3, _ = oracle.slope_grad_dense(Q, K, V, dO, spec, mod, 0, 1, out=out_b, lse=lse)
     bound = float(np.sum(np.abs(np.sum(dO * (out_b - out), axis=1)))) * Tt
     assert gs3 != gs and abs(gs3 - gs) <= bound
+
+
+@pytest.mark.parametrize("P", [1, 100, 256, T])
+def test_forward_prefix_lm_matches_sdpa(P):
+    """Prefix-LM (tutorial introduction): a query inside the prefix sees
+    exactly the prefix keys, so its row is unmasked attention over K[:P];
+    a query after it sees keys 0..q, so its row is the causal row."""
+    Q, K, V = (_rand((T, D), s) for s in (31, 32, 33))
+    spec = MaskSpecData(T, causal=True, prefix=P)
+    out, _ = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
+    np.testing.assert_allclose(out[:P], _sdpa(Q[:P], K[:P], V[:P]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(out[P:], _sdpa(Q, K, V, is_causal=True)[P:], rtol=0, atol=1e-12)

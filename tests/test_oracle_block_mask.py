@@ -117,7 +117,7 @@ def _pairs_python(spec):
         for q in range(T):
             for kv in range(T):
                 ok = True
-                if spec.causal and not (q >= kv):
+                if spec.causal and not (q >= kv or (spec.prefix and kv < spec.prefix)):
                     ok = False
                 if ok and spec.document and docs[q] != docs[kv]:
                     ok = False
@@ -264,3 +264,38 @@ def test_document_ranges_closed_form_and_sentinel():
     assert np.array_equal(r[0, :, 0], start)
     assert np.array_equal(r[0, :, 1], np.minimum(start + 999, T - 1))
     assert np.all(r[1] == -1)
+
+
+@pytest.mark.parametrize("P", [0, 1, 640, 677, 8192])
+def test_prefix_lm_closed_form(P):
+    """Causal with a prefix of P = 128 p + r positions every query sees
+    (prefix-LM masking, tutorial introduction), T = 8192: the causal triangle
+    plus, above the diagonal, the p (p - 1) / 2 tiles inside the prefix
+    (full) and, when r > 0, tile column p for the rows before it (partial).
+    The diagonal tiles inside the prefix are full."""
+    T = 8192
+    nt, p, r = T // 128, P // 128, P % 128
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True, prefix=P)))
+    visible = nt * (nt + 1) // 2 + p * (p - 1) // 2 + (p if r else 0)
+    full = nt * (nt - 1) // 2 + p * (p + 1) // 2
+    assert int((cls > 0).sum()) == visible
+    assert int((cls == oracle.FULL).sum()) == full
+
+
+def _random_prefix_spec(rng, T):
+    spec = _random_spec(rng, T)
+    spec.prefix = int(rng.choice([1, 37, 128, 129, 300, T]))
+    return spec
+
+
+def test_prefix_brute_force():
+    """With the prefix term: C counter == pure-Python per-pair loops (T = 256)
+    and == the dense [T, T] mask reduction (T up to 1024), random specs."""
+    rng = np.random.default_rng(13)
+    for _ in range(4):
+        spec = _random_prefix_spec(rng, 256)
+        assert np.array_equal(oracle.tile_counts(spec), _pairs_python(spec)), spec
+    for T in (128, 384, 1024):
+        for _ in range(6):
+            spec = _random_prefix_spec(rng, T)
+            assert np.array_equal(oracle.tile_counts(spec), oracle.tile_counts_dense_numpy(spec)), spec

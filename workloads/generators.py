@@ -35,6 +35,8 @@ class MaskSpecData:
     document    -- doc_ids[b, q] == doc_ids[b, kv]; doc_ids has shape [mask_b, T]
     window      -- q - kv < window   (None: no window term)
     sinks       -- kv < sinks, OR-ed with the window term (0: none)
+    prefix      -- kv < prefix, OR-ed with the causal term (prefix-LM: the
+                   first `prefix` positions are seen by every query; 0: none)
     """
     T: int
     causal: bool = True
@@ -42,6 +44,7 @@ class MaskSpecData:
     doc_ids: Optional[np.ndarray] = None  # int32 [mask_b, T]
     window: Optional[int] = None
     sinks: int = 0
+    prefix: int = 0
 
     @property
     def mask_b(self) -> int:
