@@ -588,9 +588,19 @@ __device__ inline void row_mask_flat(uint32_t sdoc, f32x16 (&s)[2], int key0, co
 // Maximum over a row-view step (32 scores per lane, both lane halves of a
 // query combined): four independent chains, then the lane-half exchange as
 // one cross-lane swap (no LDS round trip).
-// Maxima of scores, which are never NaN, as single v_max_f32 / v_max3_f32:
-// fmaxf first quiets inputs it cannot prove canonical (IEEE mode), up to
-// three instructions for one two-input maximum.
+// Maxima of scores, which are never NaN: fmaxf would first quiet inputs it
+// cannot prove canonical (IEEE mode), up to three instructions for one
+// two-input maximum, so the chains use v_max3_f32 / v_max_f32 from inline
+// assembly.  The compiler inserts no hazard wait states before inline
+// assembly, and the hardware does not interlock a vector read of a register
+// that a matrix-core product is still writing.  So no inline-assembly
+// instruction may read a product's result first.  Each chain therefore
+// starts from ready(), a canonicalisation (one v_max_f32 x, x) the compiler
+// emits itself and so waits for the product before.  The chain's
+// inline-assembly steps depend on its result, and the chain's other scores
+// come from the same product, complete by then.
+__device__ inline float ready(float a) { return __builtin_canonicalizef(a); }
+
 __device__ inline float max2(float a, float b) {
     float r;
     asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -608,7 +618,7 @@ __device__ inline float row_max(const f32x16 (&s)[2]) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int kb = x >> 1, r0 = (x & 1) * 8;
-        float v = max3(s[kb][r0], s[kb][r0 + 1], s[kb][r0 + 2]);
+        float v = max3(ready(s[kb][r0]), s[kb][r0 + 1], s[kb][r0 + 2]);
         v = max3(v, s[kb][r0 + 3], s[kb][r0 + 4]);
         v = max3(v, s[kb][r0 + 5], s[kb][r0 + 6]);
         c[x] = max2(v, s[kb][r0 + 7]);
@@ -616,7 +626,8 @@ __device__ inline float row_max(const f32x16 (&s)[2]) {
     const float mx = max2(max3(c[0], c[1], c[2]), c[3]);
     const uint32_t u = __builtin_bit_cast(uint32_t, mx);
     const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return max2(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    // the swap's results, too, are first read by a compiled instruction
+    return max2(ready(__builtin_bit_cast(float, (uint32_t)sw[0])), __builtin_bit_cast(float, (uint32_t)sw[1]));
 }
 
 // Row view of the mask for query qpos (mask batch row bm): visible keys form
