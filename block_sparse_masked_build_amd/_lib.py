@@ -21,14 +21,15 @@ BSM_OK, BSM_E_INVALID, BSM_E_UNSUPPORTED, BSM_E_WORKSPACE, BSM_E_HIP = range(5)
 STATUS_NAMES = {0: "BSM_OK", 1: "BSM_E_INVALID", 2: "BSM_E_UNSUPPORTED",
                 3: "BSM_E_WORKSPACE", 4: "BSM_E_HIP"}
 
-BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS = 1, 2, 4, 8
+BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX = 1, 2, 4, 8, 16
 BSM_MOD_ALIBI, BSM_MOD_SOFTCAP = 1, 2
 
 
 class BsmMaskSpec(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("seq_len", ctypes.c_int32),
                 ("mask_b", ctypes.c_int32), ("doc_ids", ctypes.c_void_p),
-                ("window", ctypes.c_void_p), ("num_sinks", ctypes.c_int32)]
+                ("window", ctypes.c_void_p), ("num_sinks", ctypes.c_int32),
+                ("prefix_len", ctypes.c_int32)]
 
 
 class BsmBlockMask(ctypes.Structure):

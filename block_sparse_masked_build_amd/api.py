@@ -19,7 +19,7 @@ import torch
 
 from . import _lib
 from ._lib import (BsmBlockMask, BsmMaskSpec, BsmScoreMod, BsmTensor, check, lib,
-                   BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS,
+                   BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX,
                    BSM_MOD_ALIBI, BSM_MOD_SOFTCAP)
 
 TILE = 128
@@ -34,6 +34,7 @@ class MaskSpec:
     doc_ids: Optional[torch.Tensor] = None   # int32 [mask_b, T] on the device
     window: Optional[torch.Tensor] = None    # int32 [1] on the device
     sinks: int = 0
+    prefix: int = 0                          # prefix-LM: keys < prefix seen by every query
 
     @property
     def mask_b(self) -> int:
@@ -42,6 +43,8 @@ class MaskSpec:
     @property
     def flags(self) -> int:
         f = BSM_MASK_CAUSAL if self.causal else 0
+        if self.prefix:
+            f |= BSM_MASK_PREFIX
         if self.doc_ids is not None:
             f |= BSM_MASK_DOCUMENT
         if self.window is not None:
@@ -54,7 +57,7 @@ class MaskSpec:
         return BsmMaskSpec(self.flags, self.T, self.mask_b,
                            self.doc_ids.data_ptr() if self.doc_ids is not None else None,
                            self.window.data_ptr() if self.window is not None else None,
-                           int(self.sinks))
+                           int(self.sinks), int(self.prefix))
 
     def set_window(self, w: int) -> None:
         """Writes a new window value on the device (stream-ordered)."""
@@ -102,7 +105,7 @@ def _stream() -> int:
 
 
 def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] = None,
-              sinks: int = 0, device="cuda") -> MaskSpec:
+              sinks: int = 0, device="cuda", prefix: int = 0) -> MaskSpec:
     """Device mask spec from host values (numpy / torch / int)."""
     d = None
     if doc_ids is not None:
@@ -113,14 +116,14 @@ def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] =
     w = None
     if window is not None:
         w = torch.tensor([int(window)], dtype=torch.int32, device=device)
-    return MaskSpec(int(T), bool(causal), d, w, int(sinks))
+    return MaskSpec(int(T), bool(causal), d, w, int(sinks), int(prefix))
 
 
 def from_spec_data(spec_data, device="cuda") -> MaskSpec:
     """Device mask spec from a workloads.MaskSpecData."""
     return mask_spec(spec_data.T, spec_data.causal,
                      spec_data.doc_ids if spec_data.document else None,
-                     spec_data.window, spec_data.sinks, device)
+                     spec_data.window, spec_data.sinks, device, getattr(spec_data, "prefix", 0))
 
 
 def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda") -> ScoreMod:

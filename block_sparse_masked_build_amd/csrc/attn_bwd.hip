@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
 // ---------------------------------------------------------------- dK, dV
 
 // Column view of the mask for one key: the visible queries form [lo, hi]
-// (causal: q >= key; window: q <= key + w - 1 unless the key is a sink; the
+// (causal: q >= key unless the key is in the prefix; window: q <= key + w - 1
+// unless the key is a sink; the
 // key's document).  Sinks only lift the window bound, so one interval always
 // suffices.  In gather mode (documents not contiguous runs) the document is
 // left out of the interval and dock holds the key's id for a per-query
@@ -345,7 +346,9 @@ __device__ inline bool make_col_mask(const AttnParams &p, int bm, int kpos, ColM
             cm.dock = p.doc_ids[(int64_t)bm * p.T + kpos];
         }
     }
-    cm.lo = max((p.mask_flags & BSM_MASK_CAUSAL) ? kpos : 0, ds);
+    // causal: queries from the key on, except for prefix keys, which every
+    // query sees
+    cm.lo = max(((p.mask_flags & BSM_MASK_CAUSAL) && kpos >= p.prefix) ? kpos : 0, ds);
     int hi = de;
     if (p.mask_flags & BSM_MASK_WINDOW) {
         const bool sink = (p.mask_flags & BSM_MASK_SINKS) && kpos < p.sinks;

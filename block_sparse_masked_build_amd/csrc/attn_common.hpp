@@ -652,7 +652,7 @@ __device__ inline int make_row_mask(const AttnParams &p, int bm, int qpos, RowMa
             rm.docq = p.doc_ids[(int64_t)bm * p.T + qpos];
         }
     }
-    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1, de);
+    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? max(qpos, p.prefix - 1) : p.T - 1, de);
     int lo = ds;
     bool sinks = false;
     if (p.mask_flags & BSM_MASK_WINDOW) {

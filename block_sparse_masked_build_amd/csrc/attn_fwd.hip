@@ -232,7 +232,7 @@ __device__ inline int finish_row_mask(const AttnParams &p, int qpos, const RowLo
         de = p.T - 1;
     }
     rm.docq = rl.docq;
-    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? qpos : p.T - 1, de);
+    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? max(qpos, p.prefix - 1) : p.T - 1, de);
     int lo = ds;
     bool sinks = false;
     if (p.mask_flags & BSM_MASK_WINDOW) {

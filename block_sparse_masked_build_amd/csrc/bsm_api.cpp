@@ -28,7 +28,15 @@ bsm_status ok() {
 }
 
 constexpr int32_t kMaxT = 1 << 22;
-constexpr uint32_t kMaskFlagsAll = BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS;
+constexpr uint32_t kMaskFlagsAll =
+    BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS | BSM_MASK_PREFIX;
+
+// The widened causal bound kv < prefix the kernels use: 0 when the term is
+// off (no PREFIX, or no causal term for it to widen), at most T.
+int32_t effective_prefix(const bsm_mask_spec *spec) {
+    if (!(spec->flags & BSM_MASK_CAUSAL) || !(spec->flags & BSM_MASK_PREFIX)) return 0;
+    return spec->prefix_len < spec->seq_len ? spec->prefix_len : spec->seq_len;
+}
 constexpr uint32_t kModFlagsAll = BSM_MOD_ALIBI | BSM_MOD_SOFTCAP;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -55,6 +63,8 @@ bsm_status check_spec(const bsm_mask_spec *spec) {
         return fail(BSM_E_INVALID, "WINDOW mask without a window pointer");
     if ((spec->flags & BSM_MASK_SINKS) && spec->num_sinks < 0)
         return fail(BSM_E_INVALID, "num_sinks %d must be >= 0", spec->num_sinks);
+    if ((spec->flags & BSM_MASK_PREFIX) && spec->prefix_len < 0)
+        return fail(BSM_E_INVALID, "prefix_len %d must be >= 0", spec->prefix_len);
     return BSM_OK;
 }
 
@@ -129,6 +139,7 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
     p.mask_b = spec->mask_b;
     p.mask_flags = spec->flags;
     p.sinks = spec->num_sinks;
+    p.prefix = effective_prefix(spec);
     p.doc_ids = spec->doc_ids;
     p.window = spec->window;
     p.mod_flags = mod ? mod->flags : 0u;
@@ -187,6 +198,7 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     p.mask_b = spec->mask_b;
     p.nchunks = n_chunks(spec->seq_len);
     p.sinks = spec->num_sinks;
+    p.prefix = effective_prefix(spec);
     p.doc_ids = spec->doc_ids;
     p.window = spec->window;
     p.out = *out;

@@ -27,6 +27,7 @@ struct MaskBuildParams {
     int32_t mask_b;
     int32_t nchunks;     // 256-position chunks of the monotonicity check
     int32_t sinks;
+    int32_t prefix;      // causal term widened to kv < prefix (0: plain causal or no causal term)
     const int32_t *doc_ids;
     const int32_t *window;
     bsm_block_mask out;
@@ -42,6 +43,7 @@ struct AttnParams {
     uint32_t mask_flags;
     uint32_t mod_flags;
     int32_t sinks;
+    int32_t prefix;      // causal term widened to kv < prefix (0: plain causal or no causal term)
     float scale;
     float softcap;
     const int32_t *doc_ids;

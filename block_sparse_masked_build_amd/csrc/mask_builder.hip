@@ -12,7 +12,8 @@
 //  * For non-decreasing document ids (packed documents as the running count of
 //    end-of-text flags, speedrun notes code listing) the visible keys of query
 //    q form at most two intervals: the main one [lo(q), hi(q)] with
-//    lo = max(doc start, q - window + 1) and hi = min(doc end, q or T-1), and
+//    lo = max(doc start, q - window + 1) and hi = min(doc end, max(q, prefix - 1)
+//    or T-1), and
 //    a sink interval [doc start, min(sinks - 1, hi)].  Merged when they touch,
 //    they are disjoint with a gap, so a tile is fully visible to a query only
 //    when one interval covers it and empty only when neither meets it: exact
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
                      ? s_deN
                      : q0 + lds_search_doc<true>(s_docq, r + 1, kTile - 1, dq) - 1;
         }
-        int hi = causal ? q : T - 1;
+        int hi = causal ? (q > p.prefix - 1 ? q : p.prefix - 1) : T - 1;
         if (de < hi) hi = de;
         int64_t lo64 = ds;
         if (windowed && (int64_t)q - w + 1 > lo64) lo64 = (int64_t)q - w + 1;

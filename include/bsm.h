@@ -49,17 +49,20 @@ typedef enum {
 } bsm_status;
 
 /* Mask predicate terms (bsm_mask_spec.flags).  A (q, kv) pair is visible iff
- *   (!CAUSAL   || q >= kv)
+ *   (!CAUSAL   || q >= kv || (PREFIX && kv < prefix_len))
  * && (!DOCUMENT || doc_ids[b][q] == doc_ids[b][kv])
  * && (!WINDOW   || q - kv < *window || (SINKS && kv < num_sinks))
  * Causal, same-document and window terms: speedrun notes "FlexAttention",
  * code listing; sinks OR-ed with the window: tutorial "FlexAttention in
- * PyTorch", Pattern 2.  SINKS without WINDOW has no effect. */
+ * PyTorch", Pattern 2; a prefix every query sees (prefix-LM masking, named
+ * in that tutorial's introduction) OR-ed with the causal term.  SINKS
+ * without WINDOW and PREFIX without CAUSAL have no effect. */
 enum {
     BSM_MASK_CAUSAL = 1u,
     BSM_MASK_DOCUMENT = 2u,
     BSM_MASK_WINDOW = 4u,
-    BSM_MASK_SINKS = 8u
+    BSM_MASK_SINKS = 8u,
+    BSM_MASK_PREFIX = 16u
 };
 
 /* Score modifications (bsm_score_mod.flags), applied to s = scale * q.k in
@@ -81,6 +84,8 @@ typedef struct {
                                 run time (may change between calls, no rebuild of
                                 anything but the block mask)                       */
     int32_t num_sinks;       /* SINKS: keys kv < num_sinks widen the window        */
+    int32_t prefix_len;      /* PREFIX: keys kv < prefix_len widen the causal term
+                                (host value, >= 0; values above T act as T)        */
 } bsm_mask_spec;
 
 /* A block mask: the tile-level summary of a mask predicate (speedrun notes

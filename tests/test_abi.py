@@ -122,6 +122,8 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
     (dict(mod=BsmScoreMod(8, None, 1.0)), _lib.BSM_E_INVALID),
     (dict(mod=BsmScoreMod(2, None, 1.0, FAKE)), _lib.BSM_E_INVALID),  # slope gradient without ALiBi
     (dict(scale=float("nan")), _lib.BSM_E_INVALID),
+    (dict(spec=_spec(flags=1 | 16, prefix_len=-1)), _lib.BSM_E_INVALID),  # negative prefix
+    (dict(spec=_spec(flags=32)), _lib.BSM_E_INVALID),                     # unknown mask flag
 ])
 def test_fwd_rejects(kw, code):
     assert _fwd(**kw) == code

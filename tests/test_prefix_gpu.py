@@ -1,0 +1,153 @@
+"""GPU parity of prefix-LM masking (keys before PREFIX are seen by every
+query; the tutorial's introduction names prefix-LM among the variants): the
+block-mask integers bit for bit, the forward and the backward against the
+fp64 oracle on the same bf16-rounded inputs (max-abs 2e-2, mean-abs 2e-3;
+randomized edge cases with the per-element relative term of the other
+random-case tests)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_utils import (EDGE_RTOL, assert_block_masks_equal, assert_close, assert_lse_close, f64,
+                          gpu_block_mask, log, needs_gpu, oracle_block_mask, per_head_f64)
+from workloads import MaskSpecData, ScoreModData, alibi_slopes, random_bf16
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _random_spec(rng, T, B=2):
+    """Random predicate with a prefix; the mask batch is 1 or B."""
+    docs = None
+    if rng.integers(0, 2):
+        mb = B if rng.integers(0, 2) else 1
+        if rng.integers(0, 4) == 0:  # ids that are not contiguous runs
+            docs = rng.integers(0, 3, size=(mb, T)).astype(np.int32)
+        else:
+            docs = np.stack([np.cumsum(rng.random(T) < 1.0 / rng.integers(8, 300)).astype(np.int32)
+                             for _ in range(mb)])
+    window, sinks = None, 0
+    if rng.integers(0, 2):
+        window = int(rng.choice([1, 17, 128, 129, 300, 5000]))
+        if rng.integers(0, 2):
+            sinks = int(rng.choice([1, 4, 130]))
+    prefix = int(rng.choice([1, 37, 128, 129, 300, T // 2, T, T + 50]))
+    return MaskSpecData(T, causal=bool(rng.integers(0, 5) > 0), document=docs is not None, doc_ids=docs,
+                        window=window, sinks=sinks, prefix=prefix)
+
+
+def _api_objects(spec_data, mod_data):
+    from block_sparse_masked_build_amd import api
+    spec = api.from_spec_data(spec_data)
+    mod = None
+    if mod_data is not None and (mod_data.alibi_slopes is not None or mod_data.softcap is not None):
+        mod = api.score_mod(mod_data.alibi_slopes, mod_data.softcap)
+    return api, spec, mod, api.build_block_mask(spec)
+
+
+def test_block_mask_random_prefix_specs():
+    rng = np.random.default_rng(41)
+    for T in (128, 256, 1024, 4096):
+        for it in range(6):
+            spec = _random_spec(rng, T)
+            ctx = f"prefix {spec.prefix} causal {spec.causal} window {spec.window} sinks {spec.sinks}"
+            log(f"[prefix] block mask T={T} {ctx}")
+            _, _, g = gpu_block_mask(spec)
+            assert_block_masks_equal(g, oracle_block_mask(spec), ctx)
+
+
+def test_block_mask_64k_closed_form():
+    """T = 65,536, causal + prefix 10,000 = 128 * 78 + 16: the causal
+    triangle plus 78 * 77 / 2 full tiles above the diagonal and tile column
+    78 for rows 0..77 (partial); the lists equal the oracle's."""
+    T, P = 65536, 10000
+    spec = MaskSpecData(T, causal=True, prefix=P)
+    log("[prefix] block mask 64K, prefix 10000")
+    _, _, g = gpu_block_mask(spec)
+    nt, p = T // 128, P // 128
+    assert int(g["kv_num_blocks"].sum() + g["full_kv_num_blocks"].sum()) == nt * (nt + 1) // 2 + p * (p - 1) // 2 + p
+    assert int(g["full_kv_num_blocks"].sum()) == nt * (nt - 1) // 2 + p * (p + 1) // 2
+    assert_block_masks_equal(g, oracle_block_mask(spec), "64K prefix")
+
+
+def _random_case(rng, it, backward):
+    T = int(rng.choice([128, 256, 384, 512]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    D = int(rng.choice([64, 128]))
+    spec = _random_spec(rng, T, B)
+    mod = ScoreModData(alibi_slopes=alibi_slopes(H) if rng.integers(0, 2) else None,
+                       softcap=float(rng.choice([30.0, 5.0])) if rng.integers(0, 2) else None)
+    g = torch.Generator("cpu").manual_seed(4000 + it)
+    names = ("q", "k", "v", "dout") if backward else ("q", "k", "v")
+    tensors = {n: random_bf16((B, H, T, D), g) for n in names}
+    return B, H, T, D, spec, mod, tensors
+
+
+def test_forward_random_prefix_cases_every_element():
+    rng = np.random.default_rng(42)
+    for it in range(10):
+        B, H, T, D, spec, mod, tensors = _random_case(rng, it, backward=False)
+        ctx = f"case {it}: B{B} H{H} T{T} D{D} prefix {spec.prefix} causal {spec.causal}"
+        log(f"[prefix] fwd {ctx}")
+        api, s, m, bm = _api_objects(spec, mod)
+        out, lse = api.flex_attention_fwd(*(tensors[n].cuda() for n in ("q", "k", "v")), bm, s, m)
+        out, lse = out.cpu(), lse.cpu()
+        for b in range(B):
+            for h in range(H):
+                Q, K, V = (per_head_f64(tensors[n], b, h) for n in ("q", "k", "v"))
+                ro, rl = oracle.forward_dense(Q, K, V, spec, mod, b, h)
+                assert_close(f64(out[b, h]), ro, f"{ctx} b{b} h{h}", rtol=EDGE_RTOL)
+                assert_lse_close(lse[b, h].double().numpy(), rl, f"{ctx} b{b} h{h}")
+
+
+def test_backward_random_prefix_cases_every_element():
+    rng = np.random.default_rng(43)
+    for it in range(8):
+        B, H, T, D, spec, mod, tensors = _random_case(rng, it, backward=True)
+        ctx = f"case {it}: B{B} H{H} T{T} D{D} prefix {spec.prefix} causal {spec.causal}"
+        log(f"[prefix] bwd {ctx}")
+        api, s, m, bm = _api_objects(spec, mod)
+        q, k, v, do = (tensors[n].cuda() for n in ("q", "k", "v", "dout"))
+        out, lse = api.flex_attention_fwd(q, k, v, bm, s, m)
+        dq, dk, dv = (x.cpu() for x in api.flex_attention_bwd(q, k, v, out, lse, do, bm, s, m))
+        for b in range(B):
+            for h in range(H):
+                Q, K, V, dO = (per_head_f64(tensors[n], b, h) for n in ("q", "k", "v", "dout"))
+                rq, rk, rv = oracle.backward_dense(Q, K, V, dO, spec, mod, b, h)
+                for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+                    assert_close(f64(got[b, h]), ref, f"{ctx} b{b} h{h} {name}", rtol=EDGE_RTOL)
+
+
+def test_prefix_lm_8k_sampled():
+    """B1 H4 T8192 D128, causal + prefix 3000 (plain prefix-LM): whole
+    sampled query tiles (forward, dQ) and key tiles (dK, dV) on two heads,
+    strict bound.  ALiBi with a prefix is covered by the small random cases;
+    at this length it makes every prefix query attend almost only to the
+    last prefix key (-slope (q - kv) is positive for later keys), whose dK
+    is then a sum of about 3000 bf16 dS terms and misses the absolute bound
+    by bf16 operand rounding alone."""
+    T, H, D, P = 8192, 4, 128, 3000
+    spec = MaskSpecData(T, causal=True, prefix=P)
+    mod = None
+    g = torch.Generator("cpu").manual_seed(44)
+    tensors = {n: random_bf16((1, H, T, D), g) for n in ("q", "k", "v", "dout")}
+    log("[prefix] B1 H4 T8192 D128 prefix 3000")
+    api, s, m, bm = _api_objects(spec, mod)
+    q, k, v, do = (tensors[n].cuda() for n in ("q", "k", "v", "dout"))
+    out, lse = api.flex_attention_fwd(q, k, v, bm, s, m)
+    dq, dk, dv = (x.cpu() for x in api.flex_attention_bwd(q, k, v, out, lse, do, bm, s, m))
+    out, lse = out.cpu(), lse.cpu()
+    tiles = [0, 23, 24, 63]  # inside the prefix, the tile holding its end, the last
+    idx = np.concatenate([np.arange(t * 128, t * 128 + 128) for t in tiles])
+    for h in (0, 3):
+        Q, K, V, dO = (per_head_f64(tensors[n], 0, h) for n in ("q", "k", "v", "dout"))
+        ro, rl = oracle.forward_rows(Q, K, V, spec, mod, 0, h, idx)
+        mx, mn = assert_close(f64(out[0, h])[idx], ro, f"h{h} out")
+        assert_lse_close(lse[0, h].double().numpy()[idx], rl, f"h{h} lse")
+        log(f"  h{h} out: max-abs {mx:.2e} mean-abs {mn:.2e}")
+        rq = oracle.backward_dq_rows(Q, K, V, dO, spec, mod, 0, h, idx)
+        assert_close(f64(dq[0, h])[idx], rq, f"h{h} dq")
+        rk, rv = oracle.backward_dkdv_cols(Q, K, V, dO, spec, mod, 0, h, idx)
+        mx, mn = assert_close(f64(dk[0, h])[idx], rk, f"h{h} dk")
+        assert_close(f64(dv[0, h])[idx], rv, f"h{h} dv")
+        log(f"  h{h} dk: max-abs {mx:.2e} mean-abs {mn:.2e}")
