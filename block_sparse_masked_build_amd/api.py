@@ -233,6 +233,28 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
     return dq, dk, dv
 
 
+def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = None,
+                          scale: Optional[float] = None, out=None, lse=None,
+                          workspace: Optional[torch.Tensor] = None):
+    """One decoding step: q [B, H, 1, D] at position kv_len - 1 against the
+    cache k, v [B, H, kv_len, D].  Returns (out [B, H, 1, D] bf16, lse [B, H])."""
+    B, H, T, D = k.shape
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        workspace = torch.empty(max(lib.bsm_decode_workspace_bytes(B, H, T, D), 256), dtype=torch.uint8,
+                                device=q.device)
+    ts = [_tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    cs = spec.c_struct()
+    cm = mod.c_struct() if mod is not None else None
+    check(lib.bsm_flex_attention_decode(
+        B, H, T, D, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]), ctypes.byref(cs),
+        ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
+        ctypes.byref(ts[3]), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
+    return out, lse
+
+
 __all__ = ["MaskSpec", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
+           "flex_attention_decode",
            "bwd_workspace", "block_mask_workspace", "_lib"]

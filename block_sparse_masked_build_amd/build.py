@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbsm.so")
 
-SOURCES = ["mask_builder.hip", "attn_fwd.hip", "attn_bwd.hip", "bsm_api.cpp"]
+SOURCES = ["mask_builder.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "bsm_api.cpp"]
 ARCH = "gfx950"
 
 

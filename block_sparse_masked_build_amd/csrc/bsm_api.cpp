@@ -295,6 +295,57 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                       "bsm_flex_attention_bwd launch");
 }
 
+size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t kv_len, int32_t D) {
+    if (B < 1 || H < 1 || bad_T(kv_len) || (D != 64 && D != 128)) return 0;
+    return align256((size_t)B * H * bsm::decode_splits(kv_len) * (D + 2) * sizeof(float));
+}
+
+bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t kv_len, int32_t D, const bsm_tensor *q,
+                                     const bsm_tensor *k, const bsm_tensor *v, const bsm_mask_spec *spec,
+                                     const bsm_score_mod *mod, float scale, const bsm_tensor *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream) {
+    bsm_status st = check_attn_common(B, H, kv_len, D, spec, mod);
+    if (st != BSM_OK) return st;
+    if (spec->mask_b != 1 && spec->mask_b != B)
+        return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
+    if ((st = check_tensor(q, "q")) != BSM_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSM_OK) return st;
+    if ((st = check_tensor(v, "v")) != BSM_OK) return st;
+    if ((st = check_tensor(out, "out")) != BSM_OK) return st;
+    if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
+    if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
+    const size_t need = bsm_decode_workspace_bytes(B, H, kv_len, D);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSM_E_WORKSPACE, "decode workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
+    bsm::AttnParams p{};
+    p.B = B;
+    p.H = H;
+    p.T = kv_len;
+    p.nt = kv_len / bsm::kTile;
+    p.mask_b = spec->mask_b;
+    p.mask_flags = spec->flags;
+    p.sinks = spec->num_sinks;
+    p.prefix = effective_prefix(spec);
+    p.doc_ids = spec->doc_ids;
+    p.window = spec->window;
+    p.mod_flags = mod ? mod->flags : 0u;
+    p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
+    p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
+    p.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+    fill_tensor(q, p.q, p.q_sb, p.q_sh, p.q_st);
+    fill_tensor(k, p.k, p.k_sb, p.k_sh, p.k_st);
+    fill_tensor(v, p.v, p.v_sb, p.v_sh, p.v_st);
+    const void *optr;
+    fill_tensor(out, optr, p.o_sb, p.o_sh, p.o_st);
+    p.o = const_cast<void *>(optr);
+    p.lse = lse;
+    return hip_status(bsm::launch_attn_decode(p, D, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
+                      "bsm_flex_attention_decode launch");
+}
+
 const char *bsm_last_error(void) { return g_last_error.c_str(); }
 
 const char *bsm_version(void) { return "bsm 0.1.0 gfx950"; }

@@ -77,5 +77,8 @@ struct AttnParams {
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnParams &p, int D, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnParams &p, int D, hipStream_t stream);
+// decode: one query per (b, h) at position T - 1; part = B*H*splits*(D + 2) floats
+int decode_splits(int kv_len);
+hipError_t launch_attn_decode(const AttnParams &p, int D, float *part, hipStream_t stream);
 
 }  // namespace bsm

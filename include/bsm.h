@@ -230,6 +230,27 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *dv, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* Bytes of device workspace bsm_flex_attention_decode needs: per (batch,
+ * head) and 512-key chunk of the cache, D + 2 floats (the chunk's
+ * unnormalised output, running maximum and sum). */
+size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t kv_len, int32_t D);
+
+/* Decoding step (tutorial "FlexAttention in PyTorch", "Decoding and paged
+ * KV caches": the query length is 1 and the mask is taken against the current
+ * key length).  One query per (batch, head) at position kv_len - 1 attends to
+ * the cache k, v [B, H, kv_len, D] under the mask predicate (spec->seq_len ==
+ * kv_len; no block mask is needed: each key's visibility is tested directly)
+ * and the score modifications, as the forward does.
+ * q, out: bf16 [B, H, 1, D] (stride_t unused); lse: fp32 [B, H], natural
+ * log, -inf (with out = 0) when no key is visible.
+ * workspace: device, >= bsm_decode_workspace_bytes(), 256-byte aligned.
+ * Errors: as the forward, plus BSM_E_WORKSPACE. */
+bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t kv_len, int32_t D,
+                                     const bsm_tensor *q, const bsm_tensor *k, const bsm_tensor *v,
+                                     const bsm_mask_spec *spec, const bsm_score_mod *mod, float scale,
+                                     const bsm_tensor *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *bsm_last_error(void);
 

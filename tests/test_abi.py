@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -157,3 +157,20 @@ def test_bwd_rejects_slope_gradient_without_alibi():
         ctypes.byref(spec), ctypes.byref(mod), 0.0, *([ctypes.byref(t)] * 3), FAKE, need, None)
     assert rc == _lib.BSM_E_INVALID
     assert "alibi_slopes_grad" in lib.bsm_last_error().decode()
+
+
+def test_decode_rejects_bad_arguments():
+    spec = _spec()
+    t = _t()
+    need = lib.bsm_decode_workspace_bytes(1, 1, 1024, 64)
+    assert need == 2 * (64 + 2) * 4 + 256 - (2 * (64 + 2) * 4) % 256  # two 512-key chunks, 256-byte rounded
+
+    def call(D=64, ws=FAKE, n=need, s=spec, lse=FAKE):
+        return lib.bsm_flex_attention_decode(1, 1, 1024, D, *([ctypes.byref(t)] * 3), ctypes.byref(s), None, 0.0,
+                                             ctypes.byref(t), lse, ws, n, None)
+
+    assert call(D=96) == _lib.BSM_E_UNSUPPORTED
+    assert call(n=need - 4) == _lib.BSM_E_WORKSPACE
+    assert call(ws=None) == _lib.BSM_E_WORKSPACE
+    assert call(lse=None) == _lib.BSM_E_INVALID
+    assert call(s=_spec(seq_len=2048)) == _lib.BSM_E_INVALID
