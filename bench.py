@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="2",
-                    help="1, 2, 2-causal, 2-window, 2-chunks, 3, 4a, 4b, 5")
+                    help="1, 2, 2-causal, 2-window, 2-chunks, 3, 4a, 4b, 5, decode")
     ap.add_argument("--fwd-only", action="store_true", help="leave the backward out of the step")
     ap.add_argument("--slopes", action="store_true",
                     help="the backward also returns dL/dslope (workloads with ALiBi)")
@@ -111,6 +111,48 @@ def cpu_baseline(w, tensors, budget_s: float):
                        f"thread; {dt:.1f} s; visible-tile FLOPs counted as for the GPU")}
 
 
+def decode_bench(args, w):
+    """Decoding step: one query per (b, h) at the last cache position against
+    the whole K/V cache; HBM-bound, so the roofline is bytes of K and V of the
+    visible keys (every key under the causal mask) over the kernel time."""
+    import torch
+    from block_sparse_masked_build_amd import api
+    t = w.tensors()
+    q = t["q"][:, :, -1:].contiguous().cuda()
+    k, v = t["k"].cuda(), t["v"].cuda()
+    spec = api.from_spec_data(w.spec)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.lib.bsm_decode_workspace_bytes(w.B, w.H, w.T, w.D), dtype=torch.uint8, device="cuda")
+    for _ in range(args.warmup):
+        api.flex_attention_decode(q, k, v, spec, None, out=out, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        api.flex_attention_decode(q, k, v, spec, None, out=out, lse=lse, workspace=ws)
+        e[1].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)[len(evs) // 2]
+    kv_bytes = 2 * w.B * w.H * w.T * w.D * 2
+    gbs = kv_bytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "decode K/V GB/s (one query per batch and head, whole cache)", "value": round(gbs, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_partial_kernel<%d> + decode_combine_kernel" % w.D},
+        "detail": {"decode_us_median": us, "kv_bytes": kv_bytes}}))
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -129,6 +171,8 @@ def main():
         return 1
 
     w = make_config(args.workload)
+    if str(args.workload) == "decode":
+        return decode_bench(args, w)
     backward = w.backward or (str(args.workload) == "2" and not args.fwd_only)
     if args.fwd_only:
         backward = False
