@@ -210,11 +210,13 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams P) {
     const int bh = blockIdx.x, lane = threadIdx.x;
     const int b = bh / P.H, h = bh - b * P.H;
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < P.nsplit; ++s) M = fmaxf(M, P.part_ml[((int64_t)bh * P.nsplit + s) * 2]);
     float L = 0.0f, acc[kDimsPerLane];
 #pragma unroll
     for (int i = 0; i < kDimsPerLane; ++i) acc[i] = 0.0f;
-    for (int s = 0; s < P.nsplit; ++s) {
+#pragma unroll 8
+    for (int s = 0; s < P.nsplit; ++s) {  // independent loads, unrolled so they overlap
         const int64_t slot = (int64_t)bh * P.nsplit + s;
         const float f = (M == -INFINITY) ? 0.0f : __expf(P.part_ml[slot * 2] - M);
         L += P.part_ml[slot * 2 + 1] * f;
