@@ -35,6 +35,8 @@ TILE = 128
 FWD_KERNEL_SOURCES = ["block_sparse_masked_build_amd/csrc/attn_fwd.hip",
                       "block_sparse_masked_build_amd/csrc/attn_common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_64k_doc_window_traffic.json")
+DECODE_SOURCES = ["block_sparse_masked_build_amd/csrc/attn_decode.hip"]
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b8h32_32k_traffic.json")
 
 
 def parse():
@@ -61,6 +63,27 @@ def fwd_source_hash() -> str:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_traffic():
+    """HBM bytes per decoding step from the committed counter summary, or
+    None when the decode kernels have changed since."""
+    try:
+        with open(DECODE_TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_source_hash") != source_hash(DECODE_SOURCES):
+        return None
+    return t.get("bytes_per_launch")
 
 
 def measured_traffic():
@@ -147,9 +170,16 @@ def decode_bench(args, w):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": decode_traffic(),
                      "kernel": "decode_partial_kernel<%d> + decode_combine_kernel" % w.D},
-        "detail": {"decode_us_median": us, "kv_bytes": kv_bytes}}))
+        "detail": {"decode_us_median": us, "kv_bytes": kv_bytes}}), flush=True)
+    if args.copy_calibration_mib:  # one device copy of known size for the HBM counters
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
     return 0
 
 
