@@ -11,7 +11,7 @@
 // Mapping to CDNA4: a single query has no matrix-product shape, and the
 // work is a stream of K and V read once, so the path is HBM-bound and runs on
 // the vector units:
-//  * decode_partial_kernel: one workgroup of 4 waves per (chunk of 512 keys,
+//  * decode_partial_kernel: one workgroup of 4 waves per (chunk of 1024 keys,
 //    batch x head).  Lane = key for the scores (the query row is broadcast
 //    from LDS), then lane = head dimension for the value sum (each key's
 //    value row read as one coalesced 256-byte line).  fp32 online softmax per
@@ -70,7 +70,7 @@ __device__ inline bool dec_visible(const DecodeParams &P, int b, int p, int kv, 
 
 template <int D>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
-    constexpr int kChunk = 512;           // keys per workgroup
+    constexpr int kChunk = 1024;          // keys per workgroup
     constexpr int kPerWave = kChunk / kDecWaves;
     constexpr int kDimsPerLane = D / 64;  // output dims per lane: lane * kDimsPerLane + i
     __shared__ float sq[D];               // the query row, fp32
@@ -239,7 +239,7 @@ hipError_t launch_d(const DecodeParams &P, hipStream_t stream) {
 
 }  // namespace
 
-int decode_splits(int kv_len) { return (kv_len + 511) / 512; }
+int decode_splits(int kv_len) { return (kv_len + 1023) / 1024; }
 
 hipError_t launch_attn_decode(const AttnParams &a, int D, float *part, hipStream_t stream) {
     DecodeParams P{};

@@ -231,7 +231,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace bsm_flex_attention_decode needs: per (batch,
- * head) and 512-key chunk of the cache, D + 2 floats (the chunk's
+ * head) and 1024-key chunk of the cache, D + 2 floats (the chunk's
  * unnormalised output, running maximum and sum). */
 size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t kv_len, int32_t D);
 

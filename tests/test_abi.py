@@ -163,7 +163,7 @@ def test_decode_rejects_bad_arguments():
     spec = _spec()
     t = _t()
     need = lib.bsm_decode_workspace_bytes(1, 1, 1024, 64)
-    assert need == 2 * (64 + 2) * 4 + 256 - (2 * (64 + 2) * 4) % 256  # two 512-key chunks, 256-byte rounded
+    assert need == 512  # one 1024-key chunk: (64 + 2) floats = 264 bytes, rounded up to a multiple of 256
 
     def call(D=64, ws=FAKE, n=need, s=spec, lse=FAKE):
         return lib.bsm_flex_attention_decode(1, 1, 1024, D, *([ctypes.byref(t)] * 3), ctypes.byref(s), None, 0.0,
