@@ -5,15 +5,19 @@
 
 One step = one pass of the whole path over one batch already resident in HBM:
 build the block mask, run the forward, and (when the workload has it, or by
-default on the 64K packed-document workload) the backward.  Each kernel call
-is bracketed by HIP events on the stream it is launched on; the reported
-value is the forward throughput counted over visible tiles:
+default on the 64K packed-document workload) the backward.  Each call is
+bracketed by HIP events on the stream it is launched on, and each is preceded
+(outside its events) by a 512 MiB device write that evicts the L2 and the
+256 MiB last-level cache, so every call starts cold.  The reported value is
+the forward throughput counted over visible tiles at the median cold time:
 
     TFLOP/s = sum_{b,h} visible_tiles(b) * 4 * 128 * 128 * D / t_fwd
 
-(4*128*128*D = the two 128x128xD products of one tile; a partial tile counts
-in full, as the speedrun notes state a tile with one visible score costs a
-full tile).  Prints one JSON line.
+(4*128*128*D = the two 128x128xD products of one tile; a partial tile costs
+as much as a full one -- speedrun notes, tile-summary paragraph).  The
+minimum and a warm back-to-back median go to `detail`, with every other
+workload of the suite timed the same way (`detail.configs`).  Prints one
+JSON line.
 """
 from __future__ import annotations
 
@@ -54,7 +58,43 @@ def parse():
                     help="time budget of the oracle sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="leave out the timing of the other workloads (detail.configs)")
+    ap.add_argument("--config-reps", type=int, default=8, help="cold reps per other workload")
     return ap.parse_args()
+
+
+FLUSH_BYTES = 512 << 20
+_flush_buf = None
+
+
+def flush_caches():
+    """Writes 512 MiB on the current stream: larger than the 8 x 4 MiB of L2
+    and the 256 MiB last-level cache, so the next call reads its inputs from
+    HBM."""
+    import torch
+    global _flush_buf
+    if _flush_buf is None:
+        _flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    _flush_buf.fill_(1)
+
+
+def timed(fn, flush=True):
+    """(start, end) events around fn() on the current stream, after a cache
+    flush outside them."""
+    import torch
+    if flush:
+        flush_caches()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    return e0, e1
+
+
+def us(evs):
+    import numpy as np
+    return np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
 
 
 def fwd_source_hash() -> str:
@@ -100,13 +140,20 @@ def measured_traffic():
 
 
 def cpu_baseline(w, tensors, budget_s: float):
-    """Times the oracle (fp64, single thread) on whole query tiles, 256 per
-    head spread over the sequence, head after head, until the time budget is
-    used."""
+    """Times the oracle (fp64 numpy, mode R: the predicate over every pair of
+    a row block, arithmetic on the columns some row of the block sees) on
+    whole query tiles, 256 per head spread over the sequence, head after
+    head, until the time budget is used; BLAS may use every core the process
+    is allowed on.  The full-workload time is extrapolated from the sampled
+    visible-tile FLOPs."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
+    host_cpus = os.cpu_count()
+    allowed = len(os.sched_getaffinity(0))
+    # the box's CPU share is set through OMP_NUM_THREADS there
+    threads = min(allowed, int(os.environ.get("OMP_NUM_THREADS", allowed) or allowed))
     counts = oracle.tile_counts(w.spec)
     vis_per_row = (counts > 0).sum(axis=2)  # [mask_b, QT]
     nt = w.T // TILE
@@ -114,7 +161,8 @@ def cpu_baseline(w, tensors, budget_s: float):
     done, flops = 0, 0.0
     heads = 0
     t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
         for h in range(w.H):
             Q, K, V = (tensors[n][0, h].double().numpy() for n in ("q", "k", "v"))
             heads += 1
@@ -128,10 +176,16 @@ def cpu_baseline(w, tensors, budget_s: float):
             if time.perf_counter() - t0 > budget_s:
                 break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    rate = flops / dt
+    total = float(sum(int(vis_per_row[b if w.spec.mask_b > 1 else 0].sum()) for b in range(w.B))) * w.H \
+        * 4 * TILE * TILE * w.D
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": blas_threads, "kind": "oracle",
+            "host_cpu_count": host_cpus, "affinity_cpus": allowed, "blas_threads": blas_threads,
+            "mode": "R", "extrapolated_full_forward_s": round(total / rate, 1),
             "sample": (f"{done} query tiles (128 rows each) over {heads} head(s) of batch 0, "
-                       f"{len(order)} per head spread over the sequence; fp64 numpy on one "
-                       f"thread; {dt:.1f} s; visible-tile FLOPs counted as for the GPU")}
+                       f"{len(order)} per head spread over the sequence; fp64 numpy, mode R, "
+                       f"BLAS on up to {blas_threads} threads; {dt:.1f} s; visible-tile FLOPs "
+                       f"counted as for the GPU")}
 
 
 def decode_bench(args, w):
@@ -150,19 +204,20 @@ def decode_bench(args, w):
     for _ in range(args.warmup):
         api.flex_attention_decode(q, k, v, spec, None, out=out, lse=lse, workspace=ws)
     torch.cuda.synchronize()
-    evs = []
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record()
+    import numpy as np
+
+    def call():
         api.flex_attention_decode(q, k, v, spec, None, out=out, lse=lse, workspace=ws)
-        e[1].record()
-        evs.append(e)
+
+    t0 = time.perf_counter()
+    evs = [timed(call) for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)[len(evs) // 2]
+    warm = [timed(call, flush=False) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_us = float(np.median(us(evs)))
     kv_bytes = 2 * w.B * w.H * w.T * w.D * 2
-    gbs = kv_bytes / (us * 1e-6) / 1e9
+    gbs = kv_bytes / (t_us * 1e-6) / 1e9
     print(json.dumps({
         "metric": "decode K/V GB/s (one query per batch and head, whole cache)", "value": round(gbs, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -172,7 +227,10 @@ def decode_bench(args, w):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": decode_traffic(),
                      "kernel": "decode_partial_kernel<%d> + decode_combine_kernel" % w.D},
-        "detail": {"decode_us_median": us, "kv_bytes": kv_bytes}}), flush=True)
+        "detail": {"decode_us_median_cold": t_us, "decode_us_min_cold": float(us(evs).min()),
+                   "decode_us_median_warm": float(np.median(us(warm))), "kv_bytes": kv_bytes,
+                   "timing": "HIP events per call, 512 MiB device write before each (outside the events)"}}),
+          flush=True)
     if args.copy_calibration_mib:  # one device copy of known size for the HBM counters
         n = args.copy_calibration_mib * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
@@ -181,6 +239,108 @@ def decode_bench(args, w):
         dst.copy_(src)
         torch.cuda.synchronize()
     return 0
+
+
+def tiles_per_bh(api, spec, bm, ws, w, win=None):
+    """Visible tiles summed over (b, h), full and partial tiles of the mask
+    (read once, outside any timed region)."""
+    import torch
+    if win is not None:
+        spec.set_window(win)
+    api.build_block_mask(spec, out=bm, workspace=ws)
+    torch.cuda.synchronize()
+    per_b = (bm.kv_num_blocks + bm.full_kv_num_blocks).sum(dim=(1, 2)).cpu().numpy()
+    full = int(bm.full_kv_num_blocks.sum().item())
+    part = int(bm.kv_num_blocks.sum().item())
+    return sum(int(per_b[b if spec.mask_b > 1 else 0]) for b in range(w.B)) * w.H, full, part
+
+
+class Path:
+    """Device buffers of one workload and its three calls."""
+
+    def __init__(self, api, w, backward, slopes=False):
+        import torch
+        self.api, self.w, self.backward = api, w, backward
+        t = w.tensors(with_dout=backward)
+        self.dev = {k: v.cuda() for k, v in t.items()}
+        self.host = t
+        self.spec = api.from_spec_data(w.spec)
+        self.mod = None
+        if w.mod.alibi_slopes is not None or w.mod.softcap is not None:
+            self.mod = api.score_mod(w.mod.alibi_slopes, w.mod.softcap)
+        self.bm = api.empty_block_mask(w.T, self.spec.mask_b)
+        self.ws = api.block_mask_workspace(self.spec)
+        self.out = torch.empty_like(self.dev["q"])
+        self.lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
+        self.dslopes = None
+        if backward:
+            self.grads = [torch.empty_like(self.dev["q"]) for _ in range(3)]
+            self.bws = api.bwd_workspace(w.B, w.H, w.T, w.D)
+            if slopes:
+                self.dslopes = torch.empty(w.H, dtype=torch.float32, device="cuda")
+
+    def build(self):
+        self.api.build_block_mask(self.spec, out=self.bm, workspace=self.ws)
+
+    def fwd(self):
+        d = self.dev
+        self.api.flex_attention_fwd(d["q"], d["k"], d["v"], self.bm, self.spec, self.mod, out=self.out,
+                                    lse=self.lse)
+
+    def bwd(self):
+        d = self.dev
+        dq, dk, dv = self.grads
+        self.api.flex_attention_bwd(d["q"], d["k"], d["v"], self.out, self.lse, d["dout"], self.bm, self.spec,
+                                    self.mod, dq=dq, dk=dk, dv=dv, workspace=self.bws, dslopes=self.dslopes)
+
+
+def config_detail(api, key, reps):
+    """Cold timings of one other workload: mask build, forward and (with a
+    backward) backward medians, and the throughput over visible tiles."""
+    import numpy as np
+    import torch
+    from workloads import make_config
+    w = make_config(key)
+    path = Path(api, w, w.backward)
+    windows = w.windows or [None]
+    res = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D, "mask_b": path.spec.mask_b}
+    per_win = {}
+    for win in windows:
+        vis, full, part = tiles_per_bh(api, path.spec, path.bm, path.ws, w, win)
+        path.fwd()
+        if w.backward:
+            path.bwd()
+        ev = {"mask": [], "fwd": [], "bwd": []}
+        for _ in range(reps):
+            ev["mask"].append(timed(path.build))
+            ev["fwd"].append(timed(path.fwd))
+            if w.backward:
+                ev["bwd"].append(timed(path.bwd))
+        torch.cuda.synchronize()
+        fl = vis * 4 * TILE * TILE * w.D
+        r = {"visible_tiles_per_head": vis // w.H, "full_tiles": full, "partial_tiles": part,
+             "mask_build_us": round(float(np.median(us(ev["mask"]))), 1),
+             "fwd_us": round(float(np.median(us(ev["fwd"]))), 1)}
+        r["fwd_tflops"] = round(fl / (r["fwd_us"] * 1e-6) / 1e12, 1)
+        r["fwd_pct_bf16_peak"] = round(100 * r["fwd_tflops"] / PEAK_BF16_TFLOPS, 1)
+        if w.backward:
+            r["bwd_us"] = round(float(np.median(us(ev["bwd"]))), 1)
+            r["bwd_tflops"] = round(2.5 * fl / (r["bwd_us"] * 1e-6) / 1e12, 1)
+            r["bwd_pct_bf16_peak"] = round(100 * r["bwd_tflops"] / PEAK_BF16_TFLOPS, 1)
+        per_win[win] = r
+    if w.windows:
+        res["per_window"] = {str(k): v for k, v in per_win.items()}
+        fwd_tot = sum(v["fwd_us"] for v in per_win.values())
+        fl_tot = sum(v["visible_tiles_per_head"] * w.H * 4 * TILE * TILE * w.D for v in per_win.values())
+        res["sweep_fwd_us_total"] = round(fwd_tot, 1)
+        res["sweep_mask_build_us_total"] = round(sum(v["mask_build_us"] for v in per_win.values()), 1)
+        res["sweep_fwd_tflops"] = round(fl_tot / (fwd_tot * 1e-6) / 1e12, 1)
+        res["sweep_fwd_pct_bf16_peak"] = round(100 * res["sweep_fwd_tflops"] / PEAK_BF16_TFLOPS, 1)
+    else:
+        res.update(per_win[None])
+    del path
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -206,54 +366,20 @@ def main():
     backward = w.backward or (str(args.workload) == "2" and not args.fwd_only)
     if args.fwd_only:
         backward = False
-    tensors = w.tensors(with_dout=backward)
-    dev = {k: v.cuda() for k, v in tensors.items()}
-    spec = api.from_spec_data(w.spec)
-    mod = None
-    if w.mod.alibi_slopes is not None or w.mod.softcap is not None:
-        mod = api.score_mod(w.mod.alibi_slopes, w.mod.softcap)
-    bm = api.empty_block_mask(w.T, spec.mask_b)
-    ws = api.block_mask_workspace(spec)
-    out = torch.empty_like(dev["q"])
-    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
-    dslopes = None
-    if backward:
-        dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
-        bws = api.bwd_workspace(w.B, w.H, w.T, w.D)
-        if args.slopes:
-            if mod is None or mod.alibi_slopes is None:
-                sys.exit("--slopes needs a workload with ALiBi (5)")
-            dslopes = torch.empty(w.H, dtype=torch.float32, device="cuda")
+    if args.slopes and (w.mod.alibi_slopes is None):
+        sys.exit("--slopes needs a workload with ALiBi (5)")
+    path = Path(api, w, backward, args.slopes)
     windows = w.windows or [None]
+    vis = {win: tiles_per_bh(api, path.spec, path.bm, path.ws, w, win) for win in windows}
 
-    def step(s):
+    def step(s, flush=True):
         win = windows[s % len(windows)]
         if win is not None:
-            spec.set_window(win)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        ev[0].record()
-        api.build_block_mask(spec, out=bm, workspace=ws)
-        ev[1].record()
-        api.flex_attention_fwd(dev["q"], dev["k"], dev["v"], bm, spec, mod, out=out, lse=lse)
-        ev[2].record()
+            path.spec.set_window(win)
+        ev = [timed(path.build, flush), timed(path.fwd, flush)]
         if backward:
-            api.flex_attention_bwd(dev["q"], dev["k"], dev["v"], out, lse, dev["dout"], bm, spec, mod,
-                                   dq=dq, dk=dk, dv=dv, workspace=bws, dslopes=dslopes)
-        ev[3].record()
+            ev.append(timed(path.bwd, flush))
         return ev, win
-
-    # visible tiles per window (read once, outside the timed region)
-    vis = {}
-    for win in windows:
-        if win is not None:
-            spec.set_window(win)
-        api.build_block_mask(spec, out=bm, workspace=ws)
-        torch.cuda.synchronize()
-        per_b = (bm.kv_num_blocks + bm.full_kv_num_blocks).sum(dim=(1, 2)).cpu().numpy()
-        full = int(bm.full_kv_num_blocks.sum().item())
-        part = int(bm.kv_num_blocks.sum().item())
-        tiles_bh = sum(int(per_b[b if spec.mask_b > 1 else 0]) for b in range(w.B)) * w.H
-        vis[win] = (tiles_bh, full, part)
 
     for s in range(args.warmup):
         step(s)
@@ -262,16 +388,27 @@ def main():
     recs = [step(s) for s in range(args.steps)]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # warm reference: the same forward calls back to back, no flush
+    warm = []
+    for s in range(args.steps):
+        win = windows[s % len(windows)]
+        if win is not None:
+            path.spec.set_window(win)
+            path.build()
+        warm.append((timed(path.fwd, flush=False), win))
+    torch.cuda.synchronize()
 
-    mask_ms = np.array([r[0][0].elapsed_time(r[0][1]) for r in recs])
-    fwd_ms = np.array([r[0][1].elapsed_time(r[0][2]) for r in recs])
-    bwd_ms = np.array([r[0][2].elapsed_time(r[0][3]) for r in recs]) if backward else None
-    fwd_flops = np.array([vis[r[1]][0] * 4 * TILE * TILE * w.D for r in recs], dtype=np.float64)
-    fwd_tflops_total = fwd_flops.sum() / (fwd_ms.sum() * 1e-3) / 1e12
-    achieved = fwd_tflops_total
+    mask_us = us([r[0][0] for r in recs])
+    fwd_us = us([r[0][1] for r in recs])
+    bwd_us = us([r[0][2] for r in recs]) if backward else None
+    warm_us = us([r[0] for r in warm])
+    fl = np.array([vis[r[1]][0] * 4 * TILE * TILE * w.D for r in recs], dtype=np.float64)
+    tflops = fl / (fwd_us * 1e-6) / 1e12          # per cold call
+    warm_tflops = np.array([vis[r[1]][0] * 4 * TILE * TILE * w.D for r in warm]) / (warm_us * 1e-6) / 1e12
+    achieved = float(np.median(tflops))           # the median cold call
     cfg = {
         "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D,
-        "mask_b": spec.mask_b,
+        "mask_b": path.spec.mask_b,
         "visible_tiles_per_head": vis[windows[0]][0] // w.H,
         "full_tiles": vis[windows[0]][1], "partial_tiles": vis[windows[0]][2],
         "tiles_per_side": w.T // TILE,
@@ -280,22 +417,27 @@ def main():
     }
     if w.windows:
         cfg["windows"] = f"{w.windows[0]}..{w.windows[-1]} step {w.windows[1] - w.windows[0]}"
-        cfg["per_window"] = {str(win): {"visible_tiles_per_head": vis[win][0] // w.H}
-                             for win in w.windows}
     extra = {
-        "mask_build_us_median": float(np.median(mask_ms) * 1e3),
-        "fwd_us_median": float(np.median(fwd_ms) * 1e3),
-        "fwd_us_mean": float(fwd_ms.mean() * 1e3),
+        "timing": "HIP events per call; 512 MiB device write before each call (outside the events); "
+                  "value = median cold call",
+        "mask_build_us_median": float(np.median(mask_us)),
+        "fwd_us_median_cold": float(np.median(fwd_us)),
+        "fwd_us_min_cold": float(fwd_us.min()),
+        "fwd_us_median_warm": float(np.median(warm_us)),
+        "fwd_tflops_median_cold": achieved,
+        "fwd_tflops_best_cold": float(tflops.max()),
+        "fwd_tflops_median_warm": float(np.median(warm_tflops)),
         "pct_bf16_peak": 100.0 * achieved / PEAK_BF16_TFLOPS,
+        "ms_per_step_includes": "three 512 MiB cache flushes per step",
     }
     if backward:
-        bwd_flops = fwd_flops * 2.5
-        extra["bwd_us_median"] = float(np.median(bwd_ms) * 1e3)
-        extra["bwd_tflops"] = float(bwd_flops.sum() / (bwd_ms.sum() * 1e-3) / 1e12)
-        extra["bwd_slope_grad"] = dslopes is not None
+        extra["bwd_us_median_cold"] = float(np.median(bwd_us))
+        extra["bwd_tflops_median_cold"] = float(np.median(2.5 * fl / (bwd_us * 1e-6) / 1e12))
+        extra["bwd_pct_bf16_peak"] = 100.0 * extra["bwd_tflops_median_cold"] / PEAK_BF16_TFLOPS
+        extra["bwd_slope_grad"] = path.dslopes is not None
     line = {
         "metric": METRIC,
-        "value": round(float(achieved), 3),
+        "value": round(achieved, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -309,10 +451,10 @@ def main():
         "config": cfg,
         "roofline": {
             "bound": "mfma",
-            "achieved": round(float(achieved), 3),
+            "achieved": round(achieved, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(float(achieved / PEAK_BF16_TFLOPS), 4),
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic() if args.workload == "2" else None,
             "kernel": "fwd_kernel<%d,%s,%s>" % (w.D, str(w.mod.alibi_slopes is not None).lower(),
                                                 str(w.mod.softcap is not None).lower()),
@@ -327,8 +469,18 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         line["detail"]["copy_calibration_bytes"] = n
+    host = path.host
+    del path
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        confs = {}
+        for key in ("1", "2", "2-causal", "2-window", "2-chunks", "3", "4a", "4b", "5"):
+            print(f"[bench] timing workload {key}", file=sys.stderr, flush=True)
+            confs[key] = config_detail(api, key, args.config_reps)
+        line["detail"]["configs"] = confs
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, tensors, args.cpu_seconds)
+        print("[bench] oracle baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -17,10 +17,8 @@ from .predicate import visible  # noqa: F401
 from .block_mask import (  # noqa: F401
     tile_counts,
     tile_counts_dense_numpy,
-    document_ranges,
     classify,
     block_mask_lists,
-    work_order,
     EMPTY, PARTIAL, FULL, TILE,
 )
 from .attention import (  # noqa: F401

@@ -37,6 +37,20 @@ u_qj = ... - slope[h] (q - j), so
   dL/dslope[h] = sum over b and visible (q, j) of g_qj (j - q)
 with g as above (the gradient with respect to u).
 
+Operand masses (for the parity bound of a bf16 implementation).  Each
+output element is a sum of products; its "mass" is the same sum with every
+factor replaced by its absolute value -- the size of the sum that rounding
+its operands to bf16 (unit roundoff u = 2^-8) can disturb, to first order:
+  out_qd:  sum_j w_qj |v_jd|                     w = p / l, the softmax weights
+  A_q:     sum_d |dO_qd| (|out_qd| + Mout_qd)    Delta_q's error from out in bf16
+  Mg_qj:   |g_qj| + p_qj c'_qj A_q               c' = cap derivative (1 uncapped)
+  dQ_qd:   scale sum_j Mg_qj |k_jd|
+  dK_jd:   scale sum_q Mg_qj |q_qd|
+  dV_jd:   sum_q p_qj |dO_qd|
+so |computed - exact| <= u * mass + the output's own rounding.  The masses
+are sums of absolute values (triangle inequality): mass >= |value|, with
+equality when every term has one sign.
+
 Arithmetic columns: by default only keys visible to at least one query of the
 row block take part in the arithmetic; the others would enter the softmax as
 exp(-inf) = 0 exactly (the tutorial notes that a -inf score is numerically the
@@ -85,12 +99,14 @@ def _row_block(Q, K, V, spec, mod, b, h, rows, scale, restrict):
     return cols, m, u, s
 
 
-def forward_rows(Q, K, V, spec, mod, b, h, rows, scale=None, restrict=True):
-    """out [R, D] and lse [R] for the query positions `rows`."""
+def forward_rows(Q, K, V, spec, mod, b, h, rows, scale=None, restrict=True, with_mass=False):
+    """out [R, D] and lse [R] for the query positions `rows` (and the
+    operand mass of out, [R, D], with with_mass)."""
     rows = np.asarray(rows, dtype=np.int64)
     D = Q.shape[1]
     sc = _scale(D, scale)
     out = np.zeros((len(rows), V.shape[1]), dtype=np.float64)
+    mass = np.zeros_like(out)
     lse = np.full(len(rows), -np.inf, dtype=np.float64)
     for a in range(0, len(rows), ROW_CHUNK):
         r = rows[a:a + ROW_CHUNK]
@@ -105,19 +121,25 @@ def forward_rows(Q, K, V, spec, mod, b, h, rows, scale=None, restrict=True):
         p = np.where(m, p, 0.0)
         ell = p.sum(axis=1)
         o = p @ V[cols]
+        ell_safe = np.where(live, ell, 1.0)[:, None]
         with np.errstate(invalid="ignore", divide="ignore"):
-            out[a:a + len(r)] = np.where(live[:, None], o / np.where(live, ell, 1.0)[:, None], 0.0)
+            out[a:a + len(r)] = np.where(live[:, None], o / ell_safe, 0.0)
             lse[a:a + len(r)] = np.where(live, mx_safe + np.log(np.where(live, ell, 1.0)), -np.inf)
+        if with_mass:
+            mass[a:a + len(r)] = np.where(live[:, None], (p @ np.abs(V[cols])) / ell_safe, 0.0)
+    if with_mass:
+        return out, lse, mass
     return out, lse
 
 
-def forward_dense(Q, K, V, spec, mod, b, h, scale=None, restrict=True):
-    """out [T, D], lse [T] for every query position."""
-    return forward_rows(Q, K, V, spec, mod, b, h, np.arange(Q.shape[0]), scale, restrict)
+def forward_dense(Q, K, V, spec, mod, b, h, scale=None, restrict=True, with_mass=False):
+    """out [T, D], lse [T] for every query position (and out's operand mass)."""
+    return forward_rows(Q, K, V, spec, mod, b, h, np.arange(Q.shape[0]), scale, restrict, with_mass)
 
 
-def _grad_block(Q, K, V, dO, spec, mod, b, h, rows, cols_sel, out_r, lse_r, sc):
-    """g [R, C], p [R, C] on rows x cols_sel (visible pairs only)."""
+def _grad_block(Q, K, V, dO, spec, mod, b, h, rows, cols_sel, out_r, lse_r, sc, with_cap=False):
+    """g [R, C], p [R, C] on rows x cols_sel (visible pairs only), and with
+    with_cap the cap derivative c' [R, C] (ones without a cap)."""
     m = visible(spec, b, rows[:, None], cols_sel[None, :])
     u, s = _scores(Q[rows], K[cols_sel], rows, cols_sel, h, sc, mod)
     live = np.isfinite(lse_r)
@@ -127,68 +149,104 @@ def _grad_block(Q, K, V, dO, spec, mod, b, h, rows, cols_sel, out_r, lse_r, sc):
     delta = np.sum(dO[rows] * out_r, axis=1)
     dP = dO[rows] @ V[cols_sel].T
     g = p * (dP - delta[:, None])
+    cprime = np.ones_like(g)
     if mod is not None and mod.softcap is not None:
         c = float(mod.softcap)
-        g = g * (1.0 - np.tanh(u / c) ** 2)
+        cprime = 1.0 - np.tanh(u / c) ** 2
+        g = g * cprime
+    if with_cap:
+        return g, p, cprime
     return g, p
 
 
-def backward_dense(Q, K, V, dO, spec, mod, b, h, scale=None):
-    """dQ, dK, dV [T, D] (small T)."""
+def _delta_mass(dO_r, out_r, mout_r):
+    """A_q = sum_d |dO_qd| (|out_qd| + Mout_qd): what rounding out to bf16
+    (and its own operand error) can move Delta_q, over u."""
+    return np.sum(np.abs(dO_r) * (np.abs(out_r) + mout_r), axis=1)
+
+
+def _mg(g, p, cprime, A_r):
+    """Mg_qj = |g_qj| + p_qj c'_qj A_q."""
+    return np.abs(g) + p * cprime * A_r[:, None]
+
+
+def backward_dense(Q, K, V, dO, spec, mod, b, h, scale=None, with_mass=False):
+    """dQ, dK, dV [T, D] (small T); with with_mass also their operand masses
+    (mass_dQ, mass_dK, mass_dV)."""
     T, D = Q.shape
     sc = _scale(D, scale)
-    out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
+    out, lse, mout = forward_dense(Q, K, V, spec, mod, b, h, scale, with_mass=True)
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
+    mQ, mK, mV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
     allcols = np.arange(T)
     for a in range(0, T, ROW_CHUNK):
         r = np.arange(a, min(T, a + ROW_CHUNK))
-        g, p = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc)
+        g, p, cp = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc, with_cap=True)
         dQ[r] = sc * (g @ K)
         dK += sc * (g.T @ Q[r])
         dV += p.T @ dO[r]
+        if with_mass:
+            mg = _mg(g, p, cp, _delta_mass(dO[r], out[r], mout[r]))
+            mQ[r] = sc * (mg @ np.abs(K))
+            mK += sc * (mg.T @ np.abs(Q[r]))
+            mV += p.T @ np.abs(dO[r])
+    if with_mass:
+        return dQ, dK, dV, mQ, mK, mV
     return dQ, dK, dV
 
 
-def backward_dq_rows(Q, K, V, dO, spec, mod, b, h, rows, scale=None):
-    """dQ for the query positions `rows` [R, D]."""
+def backward_dq_rows(Q, K, V, dO, spec, mod, b, h, rows, scale=None, with_mass=False):
+    """dQ for the query positions `rows` [R, D] (and its operand mass)."""
     rows = np.asarray(rows, dtype=np.int64)
     T, D = Q.shape
     sc = _scale(D, scale)
-    out, lse = forward_rows(Q, K, V, spec, mod, b, h, rows, scale)
+    out, lse, mout = forward_rows(Q, K, V, spec, mod, b, h, rows, scale, with_mass=True)
     dQ = np.zeros((len(rows), D), dtype=np.float64)
+    mQ = np.zeros_like(dQ)
     for a in range(0, len(rows), ROW_CHUNK):
         r = rows[a:a + ROW_CHUNK]
         m = visible(spec, b, r[:, None], np.arange(T)[None, :])
         cols = np.nonzero(m.any(axis=0))[0]
         if len(cols) == 0:
             continue
-        g, _ = _grad_block(Q, K, V, dO, spec, mod, b, h, r, cols,
-                           out[a:a + len(r)], lse[a:a + len(r)], sc)
-        dQ[a:a + len(r)] = sc * (g @ K[cols])
+        sl = slice(a, a + len(r))
+        g, p, cp = _grad_block(Q, K, V, dO, spec, mod, b, h, r, cols, out[sl], lse[sl], sc, with_cap=True)
+        dQ[sl] = sc * (g @ K[cols])
+        if with_mass:
+            mQ[sl] = sc * (_mg(g, p, cp, _delta_mass(dO[r], out[sl], mout[sl])) @ np.abs(K[cols]))
+    if with_mass:
+        return dQ, mQ
     return dQ
 
 
-def backward_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None):
+def backward_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None, with_mass=False):
     """dK, dV for the key positions `cols` [C, D]: sums over every query that
-    sees at least one of them, with that query's own forward recomputed."""
+    sees at least one of them, with that query's own forward recomputed (and
+    their operand masses with with_mass)."""
     cols = np.asarray(cols, dtype=np.int64)
     T, D = Q.shape
     sc = _scale(D, scale)
-    seen = visible(spec, b, np.arange(T)[:, None], cols[None, :]).any(axis=1)
+    seen = visible(spec, b, np.arange(Q.shape[0])[:, None], cols[None, :]).any(axis=1)
     rows = np.nonzero(seen)[0]
     dK = np.zeros((len(cols), D), dtype=np.float64)
     dV = np.zeros((len(cols), V.shape[1]), dtype=np.float64)
+    mK, mV = np.zeros_like(dK), np.zeros_like(dV)
     if len(rows) == 0:
-        return dK, dV
-    out, lse = forward_rows(Q, K, V, spec, mod, b, h, rows, scale)
+        return (dK, dV, mK, mV) if with_mass else (dK, dV)
+    out, lse, mout = forward_rows(Q, K, V, spec, mod, b, h, rows, scale, with_mass=True)
     for a in range(0, len(rows), ROW_CHUNK):
         r = rows[a:a + ROW_CHUNK]
-        g, p = _grad_block(Q, K, V, dO, spec, mod, b, h, r, cols,
-                           out[a:a + len(r)], lse[a:a + len(r)], sc)
+        sl = slice(a, a + len(r))
+        g, p, cp = _grad_block(Q, K, V, dO, spec, mod, b, h, r, cols, out[sl], lse[sl], sc, with_cap=True)
         dK += sc * (g.T @ Q[r])
         dV += p.T @ dO[r]
+        if with_mass:
+            mK += sc * (_mg(g, p, cp, _delta_mass(dO[r], out[sl], mout[sl])).T @ np.abs(Q[r]))
+            mV += p.T @ np.abs(dO[r])
+    if with_mass:
+        return dK, dV, mK, mV
     return dK, dV
 
 

@@ -109,24 +109,6 @@ def tile_counts_dense_numpy(spec) -> np.ndarray:
     return np.stack(res)
 
 
-def document_ranges(spec) -> np.ndarray:
-    """int32 [mask_b, T, 2]: first and last position of the document holding
-    each position, for rows whose document ids are non-decreasing (documents
-    are then contiguous runs, as for ids made by counting end-of-text flags --
-    speedrun notes "FlexAttention", code listing); (-1, -1) for every
-    position of any other row."""
-    T = spec.T
-    out = np.full((spec.mask_b, T, 2), -1, dtype=np.int32)
-    for b in range(spec.mask_b):
-        d = np.asarray(spec.doc_ids[b], dtype=np.int64)
-        if np.any(d[1:] < d[:-1]):
-            continue
-        for t in range(T):
-            same = np.nonzero(d == d[t])[0]
-            out[b, t] = (same[0], same[-1])
-    return out
-
-
 def classify(counts: np.ndarray) -> np.ndarray:
     """uint8 class per tile: 0 empty, 1 partial, 2 full."""
     cls = np.full(counts.shape, PARTIAL, dtype=np.uint8)
@@ -150,8 +132,7 @@ def _lists(cls2d: np.ndarray, want: int):
 
 def block_mask_lists(counts: np.ndarray) -> dict:
     """The eight tile-list arrays of a block mask, shaped [mask_b, 1, ...]
-    (head dim 1: one mask shared by all heads), and the two work orders,
-    flat [mask_b * n]."""
+    (head dim 1: one mask shared by all heads)."""
     cls = classify(counts)
     names = {}
     out = {k: [] for k in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
@@ -173,57 +154,4 @@ def block_mask_lists(counts: np.ndarray) -> dict:
         out["full_q_indices"].append(i)
     for k, v in out.items():
         names[k] = np.stack(v)[:, None]
-    names["kv_order"] = work_records(names["kv_num_blocks"], names["kv_indices"],
-                                     names["full_kv_num_blocks"], names["full_kv_indices"])
-    names["q_order"] = work_records(names["q_num_blocks"], names["q_indices"],
-                                    names["full_q_num_blocks"], names["full_q_indices"])
     return names
-
-
-def work_records(num, idx, fnum, fidx) -> np.ndarray:
-    """The work order as records: per entry (flat row index, full count,
-    partial count, first listed tile -- the first full one if any, else the
-    first partial one, else 0), int32 [mask_b * n, 4]."""
-    mask_b, n = num.shape[0], num.shape[-1]
-    num = num.reshape(mask_b, n)
-    fnum = fnum.reshape(mask_b, n)
-    order = work_order(num + fnum)
-    num = num.reshape(-1)
-    fnum = fnum.reshape(-1)
-    idx = idx.reshape(num.size, -1)
-    fidx = fidx.reshape(num.size, -1)
-    rec = np.zeros((num.size, 4), dtype=np.int32)
-    for e, r in enumerate(order):
-        first = fidx[r, 0] if fnum[r] > 0 else (idx[r, 0] if num[r] > 0 else 0)
-        rec[e] = (r, fnum[r], num[r], first)
-    return rec
-
-
-# Work orders group rows in blocks of ORDER_BLOCK consecutive rows of one
-# mask batch; block sort keys are capped so that very long blocks tie.
-ORDER_BLOCK = 16
-ORDER_KEY_CAP = 8191
-
-
-def work_order(tiles: np.ndarray) -> np.ndarray:
-    """A work order over the rows (or columns) of every mask batch, tiles
-    [mask_b, n] visible tiles per row: rows are grouped in blocks of
-    ORDER_BLOCK consecutive rows of one batch (the last block of a batch may
-    be shorter); blocks go by min(visible tiles of the block, ORDER_KEY_CAP),
-    largest first, equal keys in ascending block order; rows inside a block
-    ascending.  Returns the flat row indices bm * n + i in that order.  This
-    is scheduling data carried by the block mask, not part of the mask: the
-    longest work starts first and neighbouring rows, which share key and
-    value tiles, run together."""
-    tiles = np.asarray(tiles, dtype=np.int64)
-    if tiles.ndim == 1:
-        tiles = tiles[None]
-    mask_b, n = tiles.shape
-    blocks = []  # (key, block index, rows)
-    for bm in range(mask_b):
-        for j0 in range(0, n, ORDER_BLOCK):
-            rows = list(range(bm * n + j0, bm * n + min(j0 + ORDER_BLOCK, n)))
-            key = min(int(tiles[bm, j0:j0 + ORDER_BLOCK].sum()), ORDER_KEY_CAP)
-            blocks.append((key, len(blocks), rows))
-    blocks.sort(key=lambda b: (-b[0], b[1]))
-    return np.array([r for b in blocks for r in b[2]], dtype=np.int32)

@@ -2,26 +2,33 @@
 the same seeded inputs and compare.
 
 Tolerances for bf16 outputs against the fp64 oracle:
-  * the five workloads: max-abs 2e-2 and mean-abs 2e-3 (fixed bar);
-  * randomized edge cases, whose outputs can reach |x| ~ 4 and more (tiny
-    windows concentrate the softmax): |err| <= 2e-2 + 2^-8 |ref| per element
-    and mean-abs 2e-3.  Rounding the exact value to bf16 alone costs up to
-    |x| 2^-9, and the bf16 probabilities / score gradients fed to the matrix
-    cores cost about as much again.
+  * the five workloads: max-abs 2e-2 and mean-abs 2e-3 (the fixed bar);
+  * other cases (randomized edge cases, long prefixes with ALiBi), whose
+    outputs can be large or sums of thousands of terms: per element
+        |err| <= 2e-2 + half_ulp_bf16(|ref|) + 2^-8 * mass
+    and mean-abs 2e-3, where half_ulp_bf16 is the rounding of the exact value
+    to the bf16 output and mass is the oracle's operand mass of the element
+    (the sum it is made of, with absolute values): the first-order worst case
+    of rounding the matrix-core operands P and dS, and the forward output
+    that Delta is formed from, to bf16 (unit roundoff 2^-8).
 lse (fp32): max-abs 1e-3."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from schedule_checks import check_schedule
 
 MAX_ABS = 2e-2
 MEAN_ABS = 2e-3
 LSE_MAX_ABS = 1e-3
 
+# The eight tile-list arrays: compared bit for bit with the oracle.
 BM_NAMES = ("kv_num_blocks", "kv_indices", "full_kv_num_blocks", "full_kv_indices",
-            "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices",
-            "kv_order", "q_order")
+            "q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices")
+# Scheduling data exported with them: checked by its properties
+# (schedule_checks), not against the oracle.
+SCHEDULE_NAMES = ("kv_order", "q_order", "doc_range")
 
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="no GPU visible")
 
@@ -31,10 +38,7 @@ def log(msg):
 
 
 def oracle_block_mask(spec_data):
-    ref = oracle.block_mask_lists(oracle.tile_counts(spec_data))
-    if spec_data.document:
-        ref["doc_range"] = oracle.document_ranges(spec_data)
-    return ref
+    return oracle.block_mask_lists(oracle.tile_counts(spec_data))
 
 
 def gpu_block_mask(spec_data):
@@ -42,41 +46,71 @@ def gpu_block_mask(spec_data):
     spec = api.from_spec_data(spec_data)
     bm = api.build_block_mask(spec)
     torch.cuda.synchronize()
-    names = BM_NAMES + (("doc_range",) if spec_data.document else ())
+    names = BM_NAMES + SCHEDULE_NAMES[:2] + (("doc_range",) if spec_data.document else ())
     return spec, bm, {n: getattr(bm, n).cpu().numpy() for n in names}
 
 
-def assert_block_masks_equal(gpu, ref, ctx=""):
-    for n in ref:
+def assert_block_masks_equal(gpu, ref, ctx="", spec=None):
+    """The tile lists bit for bit against the oracle's, then the exported
+    schedule (work orders, document ranges) by its properties."""
+    for n in BM_NAMES:
         a, b = gpu[n], ref[n]
         assert a.shape == b.shape, (ctx, n, a.shape, b.shape)
         if not np.array_equal(a, b):
             bad = np.argwhere(a != b)[:5]
             raise AssertionError(f"{ctx} {n} differs at {bad.tolist()}: "
                                  f"gpu {[a[tuple(x)] for x in bad]} oracle {[b[tuple(x)] for x in bad]}")
+    if "kv_order" in gpu:
+        docs = spec.doc_ids if spec is not None and spec.document else None
+        check_schedule(gpu, docs, ctx)
 
 
 def f64(t):
     return t.detach().float().cpu().double().numpy()
 
 
-EDGE_RTOL = 2.0 ** -8
+BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to nearest)
 
 
-def assert_close(gpu, ref, ctx="", max_abs=MAX_ABS, mean_abs=MEAN_ABS, rtol=0.0):
+def half_ulp_bf16(x):
+    """Half the bf16 spacing at |x|: 2^(e - 8) for |x| in [2^e, 2^(e+1))."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, E = np.frexp(x)  # x = m 2^E, m in [0.5, 1)
+    return np.where(x > 0, np.ldexp(1.0, E - 9), 0.0)
+
+
+def operand_bound(ref, mass, max_abs=MAX_ABS):
+    """Per-element bound: max_abs + half_ulp_bf16(|ref|) + u * mass."""
+    return max_abs + half_ulp_bf16(ref) + BF16_U * np.asarray(mass, dtype=np.float64)
+
+
+def assert_within_bound(gpu, ref, mass, ctx="", mean_abs=MEAN_ABS):
+    """Every element within operand_bound, and mean-abs <= mean_abs."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape == np.shape(mass), (ctx, gpu.shape, ref.shape, np.shape(mass))
+    assert np.all(np.isfinite(gpu)), f"{ctx}: non-finite values"
+    err = np.abs(gpu - ref)
+    if not err.size:
+        return 0.0, 0.0
+    bound = operand_bound(ref, mass)
+    worst = int(np.argmax(err - bound))
+    mx, mn = float(err.max()), float(err.mean())
+    assert err.flat[worst] <= bound.flat[worst] and mn <= mean_abs, (
+        f"{ctx}: max-abs {mx:.3e}; worst element {worst} err {err.flat[worst]:.3e} > bound "
+        f"{bound.flat[worst]:.3e} (ref {ref.flat[worst]:.3e}); mean-abs {mn:.3e}")
+    return mx, mn
+
+
+def assert_close(gpu, ref, ctx="", max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    """The fixed bar: max-abs <= max_abs and mean-abs <= mean_abs."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape, (ctx, gpu.shape, ref.shape)
     assert np.all(np.isfinite(gpu)), f"{ctx}: non-finite values"
     err = np.abs(gpu - ref)
     mx, mn = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
-    if rtol == 0.0:
-        assert mx <= max_abs and mn <= mean_abs, f"{ctx}: max-abs {mx:.3e} mean-abs {mn:.3e}"
-    else:
-        excess = err - (max_abs + rtol * np.abs(ref))
-        worst = float(excess.max()) if err.size else -1.0
-        assert worst <= 0.0 and mn <= mean_abs, (
-            f"{ctx}: max-abs {mx:.3e} (bound exceeded by {worst:.3e}) mean-abs {mn:.3e}")
+    assert mx <= max_abs and mn <= mean_abs, f"{ctx}: max-abs {mx:.3e} mean-abs {mn:.3e}"
     return mx, mn
 
 

@@ -182,63 +182,6 @@ def test_lists_from_counts():
     assert bm["full_q_indices"].tolist() == [[[[1, -1, -1], [0, -1, -1], [1, -1, -1]]]]
 
 
-def test_work_order_worked_examples():
-    """Work orders, worked by hand.  Causal T = 512 (4 tiles per side) has
-    1, 2, 3, 4 tiles in rows 0..3 and 4, 3, 2, 1 in columns 0..3: one block
-    each, so rows and columns keep their order; the records carry (row, full
-    tiles, partial tiles, first listed tile).  The 3 x 3 list example is one
-    block too."""
-    bm = oracle.block_mask_lists(oracle.tile_counts(MaskSpecData(512, causal=True)))
-    assert bm["kv_order"].tolist() == [[0, 0, 1, 0], [1, 1, 1, 0], [2, 2, 1, 0], [3, 3, 1, 0]]
-    assert bm["q_order"].tolist() == [[0, 3, 1, 1], [1, 2, 1, 2], [2, 1, 1, 3], [3, 0, 1, 3]]
-    counts = np.array([[[0, 16384, 5], [16384, 0, 16384], [1, 2, 0]]], dtype=np.int32)
-    bm = oracle.block_mask_lists(counts)
-    assert bm["kv_order"].tolist() == [[0, 1, 1, 1], [1, 2, 0, 0], [2, 0, 2, 0]]
-    assert bm["q_order"].tolist() == [[0, 1, 1, 1], [1, 1, 1, 0], [2, 1, 1, 1]]
-    # 40 rows: blocks of rows 0-15 (total 16), 16-31 (32) and 32-39 (40, the
-    # short last block) go last, second and first
-    tiles = np.array([1] * 16 + [2] * 16 + [5] * 8)
-    assert oracle.work_order(tiles[None]).tolist() == list(range(32, 40)) + list(range(16, 32)) + list(range(16))
-    # two mask batches of 2 rows: batch 0's block (6 tiles) before batch 1's (5)
-    assert oracle.work_order(np.array([[1, 5], [5, 0]])).tolist() == [0, 1, 2, 3]
-    assert oracle.work_order(np.array([[1, 3], [5, 0]])).tolist() == [2, 3, 0, 1]
-    # block_mask_lists keeps the blocks of two mask batches apart: T = 1024
-    # (8 rows each), batch 0 one 128-token document per tile (the diagonal,
-    # 8 tiles), batch 1 one document (causal, 36 tiles): batch 1 goes first
-    docs = np.stack([np.repeat(np.arange(8), 128), np.zeros(1024, dtype=np.int64)])
-    bm = oracle.block_mask_lists(oracle.tile_counts(
-        MaskSpecData(1024, causal=True, document=True, doc_ids=docs.astype(np.int32))))
-    assert bm["kv_order"][:, 0].tolist() == list(range(8, 16)) + list(range(8))
-    assert bm["kv_order"][:, 1].tolist() == [0, 1, 2, 3, 4, 5, 6, 7] + [0] * 8
-
-
-def test_work_order_properties_random():
-    """A permutation; rows of a block stay together and ascending; block keys
-    never increase and equal keys keep block order; keys are capped."""
-    rng = np.random.default_rng(5)
-    B = oracle.block_mask.ORDER_BLOCK
-    for mask_b, n in ((1, 1), (1, 7), (2, 64), (3, 65), (1, 1000)):
-        tiles = rng.integers(0, 20, size=(mask_b, n))
-        order = oracle.work_order(tiles)
-        assert sorted(order.tolist()) == list(range(mask_b * n))
-        blk = [(r // n) * ((n + B - 1) // B) + (r % n) // B for r in order]
-        runs = [blk[0]] + [b for a, b in zip(blk[:-1], blk[1:]) if a != b]
-        assert len(runs) == len(set(runs))  # each block appears as one run
-        for a, b in zip(order[:-1], order[1:]):
-            if blk[list(order).index(a)] == blk[list(order).index(b)]:
-                assert b == a + 1
-        flat = tiles.reshape(-1)
-        keys = [min(int(sum(flat[r] for r in order if (r // n) * ((n + B - 1) // B) + (r % n) // B == g)), 8191)
-                for g in runs]
-        assert all(k1 >= k2 for k1, k2 in zip(keys[:-1], keys[1:]))
-        for (g1, k1), (g2, k2) in zip(zip(runs[:-1], keys[:-1]), zip(runs[1:], keys[1:])):
-            if k1 == k2:
-                assert g1 < g2
-    cap = oracle.block_mask.ORDER_KEY_CAP
-    big = np.array([[cap] * 16 + [cap + 100] * 16 + [3] * 16])
-    assert oracle.work_order(big).tolist() == list(range(48))  # both long blocks tie at the cap
-
-
 def test_config_masks_bounded_by_nodoc():
     """Adding the document term can only remove pairs: per tile the count with
     documents never exceeds the count without (configs 1, 2 shape at 8K)."""
@@ -249,21 +192,6 @@ def test_config_masks_bounded_by_nodoc():
         c_nodoc = oracle.tile_counts(nodoc)
         assert np.all(c_doc <= c_nodoc)
         assert int((c_doc > 0).sum()) < int((c_nodoc > 0).sum())
-
-
-def test_document_ranges_closed_form_and_sentinel():
-    """Fixed 1000-token chunks: position t lies in [1000 floor(t/1000),
-    min(1000 floor(t/1000) + 999, T - 1)]; ids that go down mark every
-    position of the row with (-1, -1)."""
-    T = 2560
-    docs = doc_ids_chunks(T, 1000)
-    spec = MaskSpecData(T, causal=True, document=True, doc_ids=np.stack([docs, docs[::-1].copy()]))
-    r = oracle.document_ranges(spec)
-    t = np.arange(T)
-    start = 1000 * (t // 1000)
-    assert np.array_equal(r[0, :, 0], start)
-    assert np.array_equal(r[0, :, 1], np.minimum(start + 999, T - 1))
-    assert np.all(r[1] == -1)
 
 
 @pytest.mark.parametrize("P", [0, 1, 640, 677, 8192])

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from parity_utils import (EDGE_RTOL, assert_block_masks_equal, assert_close, assert_lse_close, f64,
+from parity_utils import (assert_block_masks_equal, assert_close, assert_lse_close, assert_within_bound, f64,
                           gpu_block_mask, log, needs_gpu, oracle_block_mask, per_head_f64)
 from workloads import MaskSpecData, ScoreModData, alibi_slopes, random_bf16
 
@@ -53,7 +53,7 @@ def test_block_mask_random_prefix_specs():
             ctx = f"prefix {spec.prefix} causal {spec.causal} window {spec.window} sinks {spec.sinks}"
             log(f"[prefix] block mask T={T} {ctx}")
             _, _, g = gpu_block_mask(spec)
-            assert_block_masks_equal(g, oracle_block_mask(spec), ctx)
+            assert_block_masks_equal(g, oracle_block_mask(spec), ctx, spec)
 
 
 def test_block_mask_64k_closed_form():
@@ -67,7 +67,7 @@ def test_block_mask_64k_closed_form():
     nt, p = T // 128, P // 128
     assert int(g["kv_num_blocks"].sum() + g["full_kv_num_blocks"].sum()) == nt * (nt + 1) // 2 + p * (p - 1) // 2 + p
     assert int(g["full_kv_num_blocks"].sum()) == nt * (nt - 1) // 2 + p * (p + 1) // 2
-    assert_block_masks_equal(g, oracle_block_mask(spec), "64K prefix")
+    assert_block_masks_equal(g, oracle_block_mask(spec), "64K prefix", spec)
 
 
 def _random_case(rng, it, backward):
@@ -95,8 +95,8 @@ def test_forward_random_prefix_cases_every_element():
         for b in range(B):
             for h in range(H):
                 Q, K, V = (per_head_f64(tensors[n], b, h) for n in ("q", "k", "v"))
-                ro, rl = oracle.forward_dense(Q, K, V, spec, mod, b, h)
-                assert_close(f64(out[b, h]), ro, f"{ctx} b{b} h{h}", rtol=EDGE_RTOL)
+                ro, rl, rm = oracle.forward_dense(Q, K, V, spec, mod, b, h, with_mass=True)
+                assert_within_bound(f64(out[b, h]), ro, rm, f"{ctx} b{b} h{h}")
                 assert_lse_close(lse[b, h].double().numpy(), rl, f"{ctx} b{b} h{h}")
 
 
@@ -113,25 +113,27 @@ def test_backward_random_prefix_cases_every_element():
         for b in range(B):
             for h in range(H):
                 Q, K, V, dO = (per_head_f64(tensors[n], b, h) for n in ("q", "k", "v", "dout"))
-                rq, rk, rv = oracle.backward_dense(Q, K, V, dO, spec, mod, b, h)
-                for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
-                    assert_close(f64(got[b, h]), ref, f"{ctx} b{b} h{h} {name}", rtol=EDGE_RTOL)
+                rq, rk, rv, mq, mk, mv = oracle.backward_dense(Q, K, V, dO, spec, mod, b, h, with_mass=True)
+                for name, got, ref, mass in (("dq", dq, rq, mq), ("dk", dk, rk, mk), ("dv", dv, rv, mv)):
+                    assert_within_bound(f64(got[b, h]), ref, mass, f"{ctx} b{b} h{h} {name}")
 
 
-def test_prefix_lm_8k_sampled():
-    """B1 H4 T8192 D128, causal + prefix 3000 (plain prefix-LM): whole
-    sampled query tiles (forward, dQ) and key tiles (dK, dV) on two heads,
-    strict bound.  ALiBi with a prefix is covered by the small random cases;
-    at this length it makes every prefix query attend almost only to the
-    last prefix key (-slope (q - kv) is positive for later keys), whose dK
-    is then a sum of about 3000 bf16 dS terms and misses the absolute bound
-    by bf16 operand rounding alone."""
+@pytest.mark.parametrize("alibi", [False, True])
+def test_prefix_lm_8k_sampled(alibi):
+    """B1 H4 T8192 D128, causal + prefix 3000: whole sampled query tiles
+    (forward, dQ) and key tiles (dK, dV) on two heads.  Plain prefix-LM is
+    held to the fixed bar.  With ALiBi every prefix query attends almost only
+    to the last prefix keys (-slope (q - kv) is positive for later keys), so
+    their dK (|x| up to ~30) is a sum of thousands of bf16 dS terms: the
+    numpy emulation of the bf16 rounding points (tests/test_error_model.py)
+    misses 2e-2 there by itself, so this case is held to the derived operand
+    bound."""
     T, H, D, P = 8192, 4, 128, 3000
     spec = MaskSpecData(T, causal=True, prefix=P)
-    mod = None
+    mod = ScoreModData(alibi_slopes=alibi_slopes(H)) if alibi else None
     g = torch.Generator("cpu").manual_seed(44)
     tensors = {n: random_bf16((1, H, T, D), g) for n in ("q", "k", "v", "dout")}
-    log("[prefix] B1 H4 T8192 D128 prefix 3000")
+    log(f"[prefix] B1 H4 T8192 D128 prefix 3000 alibi={alibi}")
     api, s, m, bm = _api_objects(spec, mod)
     q, k, v, do = (tensors[n].cuda() for n in ("q", "k", "v", "dout"))
     out, lse = api.flex_attention_fwd(q, k, v, bm, s, m)
@@ -139,15 +141,21 @@ def test_prefix_lm_8k_sampled():
     out, lse = out.cpu(), lse.cpu()
     tiles = [0, 23, 24, 63]  # inside the prefix, the tile holding its end, the last
     idx = np.concatenate([np.arange(t * 128, t * 128 + 128) for t in tiles])
+
+    def check(got, ref, mass, ctx):
+        if alibi:
+            return assert_within_bound(got, ref, mass, ctx)
+        return assert_close(got, ref, ctx)
+
     for h in (0, 3):
         Q, K, V, dO = (per_head_f64(tensors[n], 0, h) for n in ("q", "k", "v", "dout"))
-        ro, rl = oracle.forward_rows(Q, K, V, spec, mod, 0, h, idx)
-        mx, mn = assert_close(f64(out[0, h])[idx], ro, f"h{h} out")
+        ro, rl, mo = oracle.forward_rows(Q, K, V, spec, mod, 0, h, idx, with_mass=True)
+        mx, mn = check(f64(out[0, h])[idx], ro, mo, f"h{h} out")
         assert_lse_close(lse[0, h].double().numpy()[idx], rl, f"h{h} lse")
         log(f"  h{h} out: max-abs {mx:.2e} mean-abs {mn:.2e}")
-        rq = oracle.backward_dq_rows(Q, K, V, dO, spec, mod, 0, h, idx)
-        assert_close(f64(dq[0, h])[idx], rq, f"h{h} dq")
-        rk, rv = oracle.backward_dkdv_cols(Q, K, V, dO, spec, mod, 0, h, idx)
-        mx, mn = assert_close(f64(dk[0, h])[idx], rk, f"h{h} dk")
-        assert_close(f64(dv[0, h])[idx], rv, f"h{h} dv")
+        rq, mq = oracle.backward_dq_rows(Q, K, V, dO, spec, mod, 0, h, idx, with_mass=True)
+        check(f64(dq[0, h])[idx], rq, mq, f"h{h} dq")
+        rk, rv, mk, mv = oracle.backward_dkdv_cols(Q, K, V, dO, spec, mod, 0, h, idx, with_mass=True)
+        mx, mn = check(f64(dk[0, h])[idx], rk, mk, f"h{h} dk")
+        check(f64(dv[0, h])[idx], rv, mv, f"h{h} dv")
         log(f"  h{h} dk: max-abs {mx:.2e} mean-abs {mn:.2e}")
