@@ -200,14 +200,16 @@ def decode_bench(args, w):
     spec = api.from_spec_data(w.spec)
     out = torch.empty_like(q)
     lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
-    ws = torch.empty(api.lib.bsm_decode_workspace_bytes(w.B, w.H, w.T, w.D), dtype=torch.uint8, device="cuda")
-    for _ in range(args.warmup):
-        api.flex_attention_decode(q, k, v, spec, None, out=out, lse=lse, workspace=ws)
-    torch.cuda.synchronize()
+    ws = api.decode_workspace(w.B, w.H, w.T, w.D)
+    kvl = torch.tensor([w.T], dtype=torch.int32, device="cuda")  # live length: the whole cache
     import numpy as np
 
     def call():
-        api.flex_attention_decode(q, k, v, spec, None, out=out, lse=lse, workspace=ws)
+        api.flex_attention_decode(q, k, v, spec, None, kv_len=kvl, out=out, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     evs = [timed(call) for _ in range(args.steps)]

@@ -68,9 +68,9 @@ SIGNATURES = {
         ctypes.c_void_p]),
     "bsm_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 4),
     "bsm_flex_attention_decode": (ctypes.c_int, [
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), _P(BsmMaskSpec), _P(BsmScoreMod), ctypes.c_float,
-        _P(BsmTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+        _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), _P(BsmMaskSpec), _P(BsmBlockMask), _P(BsmScoreMod),
+        ctypes.c_float, _P(BsmTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "bsm_last_error": (ctypes.c_char_p, []),
     "bsm_version": (ctypes.c_char_p, []),
 }

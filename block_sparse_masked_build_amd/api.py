@@ -183,8 +183,9 @@ def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if not lse.is_contiguous() or lse.shape != (B, H, T):
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, T):
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    _check_mod(mod, H)
     tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
     cb = block_mask.c_struct()
     cs = spec.c_struct()
@@ -209,6 +210,12 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
     device tensor passed as dslopes receives dL/dslope (summed over the
     batch)."""
     B, H, T, D = q.shape
+    for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if x.shape != q.shape:
+            raise ValueError(f"{name} {tuple(x.shape)} must have the shape of q {tuple(q.shape)}")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, T):
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    _check_mod(mod, H)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -233,22 +240,73 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
     return dq, dk, dv
 
 
+def _check_mod(mod: Optional[ScoreMod], H: int) -> None:
+    """The slopes tensor the kernels read H entries of."""
+    if mod is not None and mod.alibi_slopes is not None:
+        sl = mod.alibi_slopes
+        if sl.dtype != torch.float32 or not sl.is_contiguous() or sl.numel() < H:
+            raise ValueError(f"alibi_slopes must be a contiguous float32 tensor of at least H={H} elements")
+
+
+def _kv_len_tensor(kv_len, B: int, capacity: int, device) -> tuple:
+    """(device int32 tensor, stride): one live length for the batch or one per
+    batch element."""
+    if kv_len is None:
+        kv_len = capacity
+    if isinstance(kv_len, int):
+        if not 0 <= kv_len <= capacity:
+            raise ValueError(f"kv_len {kv_len} must be in [0, capacity={capacity}]")
+        kv_len = torch.tensor([kv_len], dtype=torch.int32, device=device)
+    if not isinstance(kv_len, torch.Tensor) or kv_len.dtype != torch.int32 or not kv_len.is_contiguous():
+        raise ValueError("kv_len must be an int or a contiguous int32 device tensor")
+    if kv_len.numel() == 1:
+        return kv_len, 0
+    if kv_len.numel() == B:
+        return kv_len, 1
+    raise ValueError(f"kv_len must hold 1 or B={B} values, got {kv_len.numel()}")
+
+
+def decode_workspace(B: int, H: int, capacity: int, D: int, device="cuda") -> torch.Tensor:
+    n = lib.bsm_decode_workspace_bytes(B, H, capacity, D)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = None,
-                          scale: Optional[float] = None, out=None, lse=None,
+                          scale: Optional[float] = None, kv_len=None,
+                          block_mask: Optional[BlockMask] = None, out=None, lse=None,
                           workspace: Optional[torch.Tensor] = None):
     """One decoding step: q [B, H, 1, D] at position kv_len - 1 against the
-    cache k, v [B, H, kv_len, D].  Returns (out [B, H, 1, D] bf16, lse [B, H])."""
-    B, H, T, D = k.shape
+    cache k, v [B, H, capacity, D] of which the first kv_len positions are
+    live.  kv_len: an int, or a device int32 tensor of 1 or B values (read
+    by the kernels, so a captured step replays as the cache grows); default
+    the whole capacity.  block_mask: optional mask of spec built once for the
+    capacity; the step then reads only the key tiles its row lists.
+    Returns (out [B, H, 1, D] bf16, lse [B, H] float32)."""
+    B, H, capacity, D = k.shape
+    if v.shape != k.shape:
+        raise ValueError(f"v {tuple(v.shape)} must have the shape of k {tuple(k.shape)}")
+    if q.shape != (B, H, 1, D):
+        raise ValueError(f"q must be [B, H, 1, D] = {(B, H, 1, D)}, got {tuple(q.shape)}")
+    if spec.T != capacity:
+        raise ValueError(f"mask spec length {spec.T} != cache capacity {capacity}")
+    _check_mod(mod, H)
     out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    if out.shape != (B, H, 1, D):
+        raise ValueError(f"out must be [B, H, 1, D] = {(B, H, 1, D)}")
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H):
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    kvl, stride = _kv_len_tensor(kv_len, B, capacity, q.device)
     if workspace is None:
-        workspace = torch.empty(max(lib.bsm_decode_workspace_bytes(B, H, T, D), 256), dtype=torch.uint8,
-                                device=q.device)
+        workspace = decode_workspace(B, H, capacity, D, q.device)
     ts = [_tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
     cs = spec.c_struct()
+    cb = block_mask.c_struct() if block_mask is not None else None
     cm = mod.c_struct() if mod is not None else None
     check(lib.bsm_flex_attention_decode(
-        B, H, T, D, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]), ctypes.byref(cs),
+        B, H, capacity, D, kvl.data_ptr(), stride, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
+        ctypes.byref(cs), ctypes.byref(cb) if cb is not None else None,
         ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
         ctypes.byref(ts[3]), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
     return out, lse
@@ -256,5 +314,5 @@ def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = Non
 
 __all__ = ["MaskSpec", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
-           "flex_attention_decode",
+           "flex_attention_decode", "decode_workspace",
            "bwd_workspace", "block_mask_workspace", "_lib"]

@@ -1,29 +1,43 @@
 // Block-sparse masked attention for decoding: one query per (batch, head)
-// at the last position of the key/value cache, for gfx950.
+// at the last live position of a key/value cache, for gfx950.
 //
-// Method (tutorial "FlexAttention in PyTorch", "Decoding and paged KV
-// caches": during generation the query length is 1 and the mask is taken
-// against the current key length; a dedicated path serves short queries).
-// The query sits at position p = kv_len - 1 and sees key kv when the mask
-// predicate holds for (p, kv); its scores go through the same score
-// modifications as the forward's.
+// Method (tutorial "FlexAttention in PyTorch", section "Decoding and paged
+// KV caches"): while generating, a single query attends to a cache whose
+// length grows by one per step, so the mask must follow the live length;
+// the tutorial buckets the cache allocation (e.g. to multiples of 1024) and
+// either rebuilds the block mask against the current length or derives the
+// key blocks from an existing one.  Here the allocation ("capacity") is what
+// the launch is sized by, and the live length is a device value read by the
+// kernels, so one launch configuration serves every step of a bucket.  The
+// query of batch element b sits at position p = kv_len[b] - 1 and sees key kv
+// when kv < kv_len[b] and the mask predicate holds for (p, kv); its scores go
+// through the score modifications in the forward's own formulation
+// (mod_apply: ALiBi, then the exp2-based tanh soft-cap).
 //
-// Mapping to CDNA4: a single query has no matrix-product shape, and the
-// work is a stream of K and V read once, so the path is HBM-bound and runs on
-// the vector units:
-//  * decode_partial_kernel: one workgroup of 4 waves per (chunk of 1024 keys,
-//    batch x head).  Lane = key for the scores (the query row is broadcast
-//    from LDS), then lane = head dimension for the value sum (each key's
-//    value row read as one coalesced 256-byte line).  fp32 online softmax per
-//    wave, waves merged through LDS; the chunk's (max, sum, unnormalised
-//    output) go to the workspace.  Chunks holding no visible key skip their
-//    loads.
-//  * decode_combine_kernel: one workgroup per (batch, head) merges the chunks
+// Which keys are read:
+//  * with a block mask (built once for the whole capacity, square), the
+//    row of query tiles holding p lists every key tile any query of that
+//    row can see -- a superset of the query's own -- so only those tiles are
+//    read (a document-masked decode reads its document's tiles only); the
+//    mask needs no rebuild while the cache grows inside the capacity;
+//  * without one, every 1024-key chunk below the live length is read,
+//    except chunks wholly before the window that hold no sink.
+//
+// Mapping to CDNA4: a single query has no matrix-product shape, and K and V
+// are streamed once, so the path is HBM-bound and runs on the vector units:
+//  * decode_partial_kernel: one workgroup of 4 waves per (slot of up to
+//    eight 128-key tiles, batch x head).  Each wave takes two tiles, in
+//    64-key blocks: lane = key for the scores (the query row is broadcast
+//    from LDS), then lane = head dimension for the value sum (value rows
+//    read as coalesced lines, 16 rows in flight).  fp32 online softmax in
+//    the log2 domain per wave, waves merged through LDS; the slot's (max,
+//    sum, unnormalised output) go to the workspace.
+//  * decode_combine_kernel: one workgroup per (batch, head) merges the slots
 //    through their log-sum-exps and writes out (bf16) and lse (fp32, natural
-//    log).
+//    log; -inf and out = 0 when no key is visible).
 #include <cmath>
 
-#include "bsm_internal.hpp"
+#include "attn_common.hpp"
 
 namespace bsm {
 namespace {
@@ -32,34 +46,41 @@ typedef __bf16 dec_bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kSlotTiles = 8;                      // 128-key tiles per workgroup
+constexpr int kWaveTiles = kSlotTiles / kDecWaves; // 2 per wave
 
 struct DecodeParams {
-    int32_t B, H, kv_len, D, nsplit;
-    uint32_t mask_flags, mod_flags;
+    int32_t B, H, capacity, D, nslot, nt;
+    const int32_t *kv_len;       // device: live length(s)
+    int32_t kv_len_stride;       // 0: one value for the batch; 1: one per batch element
+    uint32_t mask_flags;
     int32_t sinks, prefix;
     float scale, softcap;
-    const int32_t *doc_ids;      // [mask_b, kv_len] or NULL
+    const int32_t *doc_ids;      // [mask_b, capacity] or NULL
     const int32_t *window;       // device scalar or NULL
     int32_t mask_b;
     const float *alibi_slopes;   // [H] or NULL
+    // block mask rows (NULL kv_num: no block mask)
+    const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
     const __bf16 *q; int64_t q_sb, q_sh;
     const __bf16 *k; int64_t k_sb, k_sh, k_st;
     const __bf16 *v; int64_t v_sb, v_sh, v_st;
     __bf16 *o; int64_t o_sb, o_sh;
     float *lse;                  // [B, H]
-    float *part_o;               // [B*H, nsplit, D]
-    float *part_ml;              // [B*H, nsplit, 2]: running max and sum
+    float *part_o;               // [B*H, nslot, D]
+    float *part_ml;              // [B*H, nslot, 2]: running max (log2 domain) and sum
 };
 
-// Visibility of key kv for the query at p (the mask predicate written out;
-// with the query last, the causal term and its prefix widening admit every
-// key at or before p).
-__device__ inline bool dec_visible(const DecodeParams &P, int b, int p, int kv, int window, int docq) {
+// Live length of batch element b, clamped to [0, capacity].
+__device__ inline int live_len(const DecodeParams &P, int b) {
+    const int L = P.kv_len[P.kv_len_stride ? b : 0];
+    return L < 0 ? 0 : (L > P.capacity ? P.capacity : L);
+}
+
+// The mask predicate for the query at p and key kv < live length.
+__device__ inline bool dec_visible(const DecodeParams &P, int bm, int p, int kv, int window, int docq) {
     if ((P.mask_flags & BSM_MASK_CAUSAL) && kv > p && !(kv < P.prefix)) return false;
-    if (P.mask_flags & BSM_MASK_DOCUMENT) {
-        const int bm = P.mask_b == 1 ? 0 : b;
-        if (P.doc_ids[(int64_t)bm * P.kv_len + kv] != docq) return false;
-    }
+    if ((P.mask_flags & BSM_MASK_DOCUMENT) && P.doc_ids[(int64_t)bm * P.capacity + kv] != docq) return false;
     if (P.mask_flags & BSM_MASK_WINDOW) {
         const bool in_win = (int64_t)p - kv < window;
         const bool sink = (P.mask_flags & BSM_MASK_SINKS) && kv < P.sinks;
@@ -69,41 +90,64 @@ __device__ inline bool dec_visible(const DecodeParams &P, int b, int p, int kv, 
 }
 
 template <int D>
+__device__ inline void write_empty_slot(const DecodeParams &P, int64_t slot) {
+    for (int d = threadIdx.x; d < D; d += kDecThreads) P.part_o[slot * D + d] = 0.0f;
+    if (threadIdx.x == 0) {
+        P.part_ml[slot * 2] = -INFINITY;
+        P.part_ml[slot * 2 + 1] = 0.0f;
+    }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP, bool LISTED>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
-    constexpr int kChunk = 1024;          // keys per workgroup
-    constexpr int kPerWave = kChunk / kDecWaves;
     constexpr int kDimsPerLane = D / 64;  // output dims per lane: lane * kDimsPerLane + i
     __shared__ float sq[D];               // the query row, fp32
     __shared__ float sp[kDecWaves][64];   // probabilities of a wave's 64 keys
     __shared__ float sm[kDecWaves], sl[kDecWaves];
     __shared__ float so[kDecWaves][D];
 
-    const int split = blockIdx.x, bh = blockIdx.y;
+    const int slot_i = blockIdx.x, bh = blockIdx.y;
     const int b = bh / P.H, h = bh - b * P.H;
+    const int bm = P.mask_b == 1 ? 0 : b;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int p = P.kv_len - 1;
+    const int64_t slot = (int64_t)bh * P.nslot + slot_i;
+    const int L = live_len(P, b);
+    const int p = L - 1;
     const int window = (P.mask_flags & BSM_MASK_WINDOW) ? *P.window : 0;
-    int docq = 0;
-    if (P.mask_flags & BSM_MASK_DOCUMENT) docq = P.doc_ids[(int64_t)(P.mask_b == 1 ? 0 : b) * P.kv_len + p];
-    const float slope = (P.mod_flags & BSM_MOD_ALIBI) ? P.alibi_slopes[h] : 0.0f;
-    const bool capped = P.mod_flags & BSM_MOD_SOFTCAP;
 
-    // A chunk wholly before the window (and holding no sink) sees nothing:
-    // its partial is (-inf, 0, 0) without touching K or V.
-    if (P.mask_flags & BSM_MASK_WINDOW) {
-        const int64_t c0 = (int64_t)split * kChunk, c1 = min((int64_t)(split + 1) * kChunk, (int64_t)P.kv_len);
-        const bool before = (int64_t)p - (c1 - 1) >= window;
-        const bool sink = (P.mask_flags & BSM_MASK_SINKS) && c0 < P.sinks;
-        if (before && !sink) {
-            const int64_t slot = (int64_t)bh * P.nsplit + split;
-            for (int d = threadIdx.x; d < D; d += kDecThreads) P.part_o[slot * D + d] = 0.0f;
-            if (threadIdx.x == 0) {
-                P.part_ml[slot * 2] = -INFINITY;
-                P.part_ml[slot * 2 + 1] = 0.0f;
-            }
+    // Tiles of this slot: listed ones (block mask row of p), or the slot's
+    // eight consecutive tiles.  ntl = number of tiles the slot covers.
+    int row = 0, nfull = 0, nlist = 0;
+    if (L == 0) {
+        write_empty_slot<D>(P, slot);
+        return;
+    }
+    if (LISTED) {
+        row = bm * P.nt + p / kTile;
+        // counts clamped to the row length, so indices stay inside the lists
+        nfull = min(max(P.full_kv_num[row], 0), P.nt);
+        nlist = nfull + min(max(P.kv_num[row], 0), P.nt - nfull);
+        if (kSlotTiles * slot_i >= nlist) {
+            write_empty_slot<D>(P, slot);
+            return;
+        }
+    } else {
+        const int64_t c0 = (int64_t)slot_i * kSlotTiles * kTile;
+        const int64_t c1 = min(c0 + kSlotTiles * kTile, (int64_t)L);  // keys [c0, c1)
+        bool skip = c0 >= L;
+        // wholly before the window and holding no sink
+        if (!skip && (P.mask_flags & BSM_MASK_WINDOW))
+            skip = (int64_t)p - (c1 - 1) >= window && !((P.mask_flags & BSM_MASK_SINKS) && c0 < P.sinks);
+        if (skip) {
+            write_empty_slot<D>(P, slot);
             return;
         }
     }
+
+    int docq = 0;
+    if (P.mask_flags & BSM_MASK_DOCUMENT) docq = P.doc_ids[(int64_t)bm * P.capacity + p];
+    const float slope = ALIBI ? P.alibi_slopes[h] : 0.0f;
+    const ModK mk = mod_k<SOFTCAP>(P.scale, slope, SOFTCAP ? P.softcap : 1.0f);
 
     const __bf16 *qrow = P.q + b * P.q_sb + h * P.q_sh;
     for (int d = threadIdx.x; d < D; d += kDecThreads) sq[d] = static_cast<float>(qrow[d]);
@@ -116,12 +160,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 #pragma unroll
     for (int i = 0; i < kDimsPerLane; ++i) o[i] = 0.0f;
 
-    const int k_begin = split * kChunk + wv * kPerWave;
 #pragma unroll 1
-    for (int sub = 0; sub < kPerWave; sub += 64) {
-        const int kv = k_begin + sub + lane;
-        float s = -INFINITY;
-        if (kv < P.kv_len && dec_visible(P, b, p, kv, window, docq)) {
+    for (int sub = 0; sub < 2 * kWaveTiles; ++sub) {
+        // first key of this 64-key block (-1: no block)
+        const int te = kSlotTiles * slot_i + kWaveTiles * wv + (sub >> 1);
+        int key0 = -1;
+        if (LISTED) {
+            if (te < nlist) {
+                const int j = te < nfull ? P.full_kv_idx[(int64_t)row * P.nt + te]
+                                         : P.kv_idx[(int64_t)row * P.nt + te - nfull];
+                key0 = clamp_tile(j, P.nt) * kTile + (sub & 1) * 64;
+            }
+        } else {
+            key0 = te * kTile + (sub & 1) * 64;
+        }
+        if (key0 < 0 || key0 >= L) continue;  // wave-uniform
+        const int kv = key0 + lane;
+        float t = -INFINITY;
+        if (kv < L && dec_visible(P, bm, p, kv, window, docq)) {
             const __bf16 *krow = kb + (int64_t)kv * P.k_st;
             float acc = 0.0f;
 #pragma unroll
@@ -130,17 +186,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(sq[d0 + e], static_cast<float>(kk[e]), acc);
             }
-            s = acc * P.scale;
-            if (P.mod_flags & BSM_MOD_ALIBI) s -= slope * (float)(p - kv);
-            if (capped) s = P.softcap * tanhf(s / P.softcap);
+            // log2-domain modified score, as in the forward
+            t = mod_apply<ALIBI, SOFTCAP>(acc, -mk.slope_f * (float)(p - kv), mk);
         }
-        // online softmax over this wave's 64 keys
-        float mx = s;
+        // online softmax over this wave's 64 keys (log2 domain)
+        float mx = t;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
         const float m_new = fmaxf(m, mx);
-        const float pk = m_new == -INFINITY ? 0.0f : __expf(s - m_new);
-        const float alpha = m_new == -INFINITY ? 1.0f : __expf(m - m_new);
+        const float pk = m_new == -INFINITY ? 0.0f : fast_exp2(t - m_new);
+        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m - m_new);
         float ps = pk;
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
@@ -149,18 +204,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         sp[wv][lane] = pk;  // read back by every lane of this wave (LDS operations stay in order)
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; ++i) o[i] *= alpha;
-        const int nk = min(64, P.kv_len - (k_begin + sub));
         if (mx != -INFINITY) {
-            // value rows of the wave's keys, 16 at a time with their loads
-            // issued together (keys past the cache end contribute p = 0 and
-            // read the last row instead)
+            // value rows of the block's keys, 16 at a time with their loads
+            // issued together (keys past the live length have p = 0 and read
+            // a row inside the cache instead)
+            const int nk = min(64, L - key0);
             const __bf16 *vbase = vb + lane * kDimsPerLane;
 #pragma unroll 1
             for (int j0 = 0; j0 < 64; j0 += 16) {
                 float vv[16][kDimsPerLane];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int key = min(k_begin + sub + j0 + j, P.kv_len - 1);
+                    const int key = min(key0 + j0 + j, L - 1);
                     const __bf16 *vrow = vbase + (int64_t)key * P.v_st;
 #pragma unroll
                     for (int i = 0; i < kDimsPerLane; ++i) vv[j][i] = static_cast<float>(vrow[i]);
@@ -185,21 +240,20 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     if (wv == 0) {
         float M = sm[0];
         for (int w = 1; w < kDecWaves; ++w) M = fmaxf(M, sm[w]);
-        float L = 0.0f, acc[kDimsPerLane];
+        float Ls = 0.0f, acc[kDimsPerLane];
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; ++i) acc[i] = 0.0f;
         for (int w = 0; w < kDecWaves; ++w) {
-            const float f = (M == -INFINITY) ? 0.0f : __expf(sm[w] - M);
-            L += sl[w] * f;
+            const float f = (M == -INFINITY) ? 0.0f : fast_exp2(sm[w] - M);
+            Ls += sl[w] * f;
 #pragma unroll
             for (int i = 0; i < kDimsPerLane; ++i) acc[i] += so[w][lane * kDimsPerLane + i] * f;
         }
-        const int64_t slot = (int64_t)bh * P.nsplit + split;
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; ++i) P.part_o[slot * D + lane * kDimsPerLane + i] = acc[i];
         if (lane == 0) {
             P.part_ml[slot * 2] = M;
-            P.part_ml[slot * 2 + 1] = L;
+            P.part_ml[slot * 2 + 1] = Ls;
         }
     }
 }
@@ -211,45 +265,65 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams P) {
     const int b = bh / P.H, h = bh - b * P.H;
     float M = -INFINITY;
 #pragma unroll 8
-    for (int s = 0; s < P.nsplit; ++s) M = fmaxf(M, P.part_ml[((int64_t)bh * P.nsplit + s) * 2]);
-    float L = 0.0f, acc[kDimsPerLane];
+    for (int s = 0; s < P.nslot; ++s) M = fmaxf(M, P.part_ml[((int64_t)bh * P.nslot + s) * 2]);
+    float Ls = 0.0f, acc[kDimsPerLane];
 #pragma unroll
     for (int i = 0; i < kDimsPerLane; ++i) acc[i] = 0.0f;
 #pragma unroll 8
-    for (int s = 0; s < P.nsplit; ++s) {  // independent loads, unrolled so they overlap
-        const int64_t slot = (int64_t)bh * P.nsplit + s;
-        const float f = (M == -INFINITY) ? 0.0f : __expf(P.part_ml[slot * 2] - M);
-        L += P.part_ml[slot * 2 + 1] * f;
+    for (int s = 0; s < P.nslot; ++s) {  // independent loads, unrolled so they overlap
+        const int64_t slot = (int64_t)bh * P.nslot + s;
+        const float f = (M == -INFINITY) ? 0.0f : fast_exp2(P.part_ml[slot * 2] - M);
+        Ls += P.part_ml[slot * 2 + 1] * f;
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; ++i) acc[i] += P.part_o[slot * D + lane * kDimsPerLane + i] * f;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
     __bf16 *orow = P.o + b * P.o_sb + h * P.o_sh;
 #pragma unroll
     for (int i = 0; i < kDimsPerLane; ++i) orow[lane * kDimsPerLane + i] = static_cast<__bf16>(acc[i] * inv);
-    if (lane == 0) P.lse[bh] = L > 0.0f ? M + logf(L) : -INFINITY;
+    if (lane == 0) P.lse[bh] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+template <int D, bool ALIBI, bool SOFTCAP>
+void launch_mods(const DecodeParams &P, hipStream_t stream) {
+    const dim3 grid(P.nslot, P.B * P.H), block(kDecThreads);
+    if (P.kv_num)
+        hipLaunchKernelGGL((decode_partial_kernel<D, ALIBI, SOFTCAP, true>), grid, block, 0, stream, P);
+    else
+        hipLaunchKernelGGL((decode_partial_kernel<D, ALIBI, SOFTCAP, false>), grid, block, 0, stream, P);
 }
 
 template <int D>
-hipError_t launch_d(const DecodeParams &P, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_partial_kernel<D>), dim3(P.nsplit, P.B * P.H), dim3(kDecThreads), 0, stream, P);
+hipError_t launch_d(const DecodeParams &P, uint32_t mod_flags, hipStream_t stream) {
+    const bool alibi = mod_flags & BSM_MOD_ALIBI, cap = mod_flags & BSM_MOD_SOFTCAP;
+    if (alibi && cap)
+        launch_mods<D, true, true>(P, stream);
+    else if (alibi)
+        launch_mods<D, true, false>(P, stream);
+    else if (cap)
+        launch_mods<D, false, true>(P, stream);
+    else
+        launch_mods<D, false, false>(P, stream);
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(P.B * P.H), dim3(64), 0, stream, P);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int decode_splits(int kv_len) { return (kv_len + 1023) / 1024; }
+int decode_slots(int capacity) { return (capacity + kSlotTiles * kTile - 1) / (kSlotTiles * kTile); }
 
-hipError_t launch_attn_decode(const AttnParams &a, int D, float *part, hipStream_t stream) {
+hipError_t launch_attn_decode(const DecodeLaunch &d, float *part, hipStream_t stream) {
+    const AttnParams &a = d.a;
     DecodeParams P{};
     P.B = a.B;
     P.H = a.H;
-    P.kv_len = a.T;
-    P.D = D;
-    P.nsplit = decode_splits(a.T);
+    P.capacity = a.T;
+    P.D = d.D;
+    P.nslot = decode_slots(a.T);
+    P.nt = (a.T + kTile - 1) / kTile;
+    P.kv_len = d.kv_len;
+    P.kv_len_stride = d.kv_len_stride;
     P.mask_flags = a.mask_flags;
-    P.mod_flags = a.mod_flags;
     P.sinks = a.sinks;
     P.prefix = a.prefix;
     P.scale = a.scale;
@@ -258,6 +332,10 @@ hipError_t launch_attn_decode(const AttnParams &a, int D, float *part, hipStream
     P.window = a.window;
     P.mask_b = a.mask_b;
     P.alibi_slopes = a.alibi_slopes;
+    P.kv_num = a.kv_num;
+    P.kv_idx = a.kv_idx;
+    P.full_kv_num = a.full_kv_num;
+    P.full_kv_idx = a.full_kv_idx;
     P.q = static_cast<const __bf16 *>(a.q);
     P.q_sb = a.q_sb;
     P.q_sh = a.q_sh;
@@ -274,9 +352,9 @@ hipError_t launch_attn_decode(const AttnParams &a, int D, float *part, hipStream
     P.o_sh = a.o_sh;
     P.lse = a.lse;
     P.part_o = part;
-    P.part_ml = part + (int64_t)a.B * a.H * P.nsplit * D;
-    if (D == 64) return launch_d<64>(P, stream);
-    return launch_d<128>(P, stream);
+    P.part_ml = part + (int64_t)a.B * a.H * P.nslot * d.D;
+    if (d.D == 64) return launch_d<64>(P, a.mod_flags, stream);
+    return launch_d<128>(P, a.mod_flags, stream);
 }
 
 }  // namespace bsm

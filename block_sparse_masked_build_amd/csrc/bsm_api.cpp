@@ -166,6 +166,91 @@ bsm_status hip_status(hipError_t e, const char *what) {
     return ok();
 }
 
+size_t decode_part_bytes(int32_t B, int32_t H, int32_t capacity, int32_t D) {
+    return align256((size_t)B * H * bsm::decode_slots(capacity) * (D + 2) * sizeof(float));
+}
+
+// Host checks and parameter block of a decoding step (both decode entry
+// points).  The cache holds `capacity` positions; kv_len is a device value.
+bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, const int32_t *kv_len,
+                          int32_t kv_len_stride, const bsm_tensor *q, const bsm_tensor *k, const bsm_tensor *v,
+                          const bsm_mask_spec *spec, const bsm_block_mask *bm, const bsm_score_mod *mod,
+                          float scale, const bsm_tensor *out, float *lse, bsm::DecodeLaunch &d) {
+    if (B < 1 || H < 1) return fail(BSM_E_INVALID, "B=%d and H=%d must be >= 1", B, H);
+    if (capacity < 1 || capacity > kMaxT)
+        return fail(BSM_E_INVALID, "capacity %d must be in [1, %d]", capacity, kMaxT);
+    if (D != 64 && D != 128) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64 and 128 are built", D);
+    if (!spec) return fail(BSM_E_INVALID, "mask spec is NULL");
+    if (spec->seq_len != capacity)
+        return fail(BSM_E_INVALID, "mask seq_len %d != cache capacity %d", spec->seq_len, capacity);
+    if (bm) {  // a block mask is built for the whole capacity, square
+        bsm_status st = check_spec(spec);
+        if (st != BSM_OK) return st;
+        if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
+            return fail(BSM_E_INVALID, "block mask row arrays must be non-NULL");
+    } else {
+        if (spec->flags & ~kMaskFlagsAll) return fail(BSM_E_INVALID, "unknown mask flag bits 0x%x", spec->flags);
+        if (spec->mask_b < 1) return fail(BSM_E_INVALID, "mask_b %d must be >= 1", spec->mask_b);
+        if ((spec->flags & BSM_MASK_DOCUMENT) && !spec->doc_ids)
+            return fail(BSM_E_INVALID, "DOCUMENT mask without doc_ids");
+        if ((spec->flags & BSM_MASK_WINDOW) && !spec->window)
+            return fail(BSM_E_INVALID, "WINDOW mask without a window pointer");
+        if ((spec->flags & BSM_MASK_SINKS) && spec->num_sinks < 0)
+            return fail(BSM_E_INVALID, "num_sinks %d must be >= 0", spec->num_sinks);
+        if ((spec->flags & BSM_MASK_PREFIX) && spec->prefix_len < 0)
+            return fail(BSM_E_INVALID, "prefix_len %d must be >= 0", spec->prefix_len);
+    }
+    if (spec->mask_b != 1 && spec->mask_b != B)
+        return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
+    if (!kv_len) return fail(BSM_E_INVALID, "kv_len is NULL");
+    if (kv_len_stride != 0 && kv_len_stride != 1)
+        return fail(BSM_E_INVALID, "kv_len_stride %d must be 0 or 1", kv_len_stride);
+    bsm_status st = check_mod(mod);
+    if (st != BSM_OK) return st;
+    if (mod && mod->alibi_slopes_grad) return fail(BSM_E_INVALID, "alibi_slopes_grad is a backward output");
+    if ((st = check_tensor(q, "q")) != BSM_OK) return st;
+    if ((st = check_tensor(k, "k")) != BSM_OK) return st;
+    if ((st = check_tensor(v, "v")) != BSM_OK) return st;
+    if ((st = check_tensor(out, "out")) != BSM_OK) return st;
+    if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
+    if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
+    bsm::AttnParams &p = d.a;
+    p = bsm::AttnParams{};
+    p.B = B;
+    p.H = H;
+    p.T = capacity;
+    p.nt = (capacity + bsm::kTile - 1) / bsm::kTile;
+    p.mask_b = spec->mask_b;
+    p.mask_flags = spec->flags;
+    p.sinks = spec->num_sinks;
+    p.prefix = (spec->flags & BSM_MASK_CAUSAL) && (spec->flags & BSM_MASK_PREFIX)
+                   ? (spec->prefix_len < capacity ? spec->prefix_len : capacity)
+                   : 0;
+    p.doc_ids = spec->doc_ids;
+    p.window = spec->window;
+    p.mod_flags = mod ? mod->flags : 0u;
+    p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
+    p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
+    p.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
+    if (bm) {
+        p.kv_num = bm->kv_num_blocks;
+        p.kv_idx = bm->kv_indices;
+        p.full_kv_num = bm->full_kv_num_blocks;
+        p.full_kv_idx = bm->full_kv_indices;
+    }
+    fill_tensor(q, p.q, p.q_sb, p.q_sh, p.q_st);
+    fill_tensor(k, p.k, p.k_sb, p.k_sh, p.k_st);
+    fill_tensor(v, p.v, p.v_sb, p.v_sh, p.v_st);
+    const void *optr;
+    fill_tensor(out, optr, p.o_sb, p.o_sh, p.o_st);
+    p.o = const_cast<void *>(optr);
+    p.lse = lse;
+    d.D = D;
+    d.kv_len = kv_len;
+    d.kv_len_stride = kv_len_stride;
+    return BSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,54 +380,27 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                       "bsm_flex_attention_bwd launch");
 }
 
-size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t kv_len, int32_t D) {
-    if (B < 1 || H < 1 || bad_T(kv_len) || (D != 64 && D != 128)) return 0;
-    return align256((size_t)B * H * bsm::decode_splits(kv_len) * (D + 2) * sizeof(float));
+size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t capacity, int32_t D) {
+    if (B < 1 || H < 1 || capacity < 1 || capacity > kMaxT || (D != 64 && D != 128)) return 0;
+    return decode_part_bytes(B, H, capacity, D);
 }
 
-bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t kv_len, int32_t D, const bsm_tensor *q,
-                                     const bsm_tensor *k, const bsm_tensor *v, const bsm_mask_spec *spec,
+bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, const int32_t *kv_len,
+                                     int32_t kv_len_stride, const bsm_tensor *q, const bsm_tensor *k,
+                                     const bsm_tensor *v, const bsm_mask_spec *spec, const bsm_block_mask *bm,
                                      const bsm_score_mod *mod, float scale, const bsm_tensor *out, float *lse,
                                      void *workspace, size_t workspace_bytes, void *stream) {
-    bsm_status st = check_attn_common(B, H, kv_len, D, spec, mod);
+    bsm::DecodeLaunch d;
+    bsm_status st = prepare_decode(B, H, capacity, D, kv_len, kv_len_stride, q, k, v, spec, bm, mod, scale, out,
+                                   lse, d);
     if (st != BSM_OK) return st;
-    if (spec->mask_b != 1 && spec->mask_b != B)
-        return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
-    if ((st = check_tensor(q, "q")) != BSM_OK) return st;
-    if ((st = check_tensor(k, "k")) != BSM_OK) return st;
-    if ((st = check_tensor(v, "v")) != BSM_OK) return st;
-    if ((st = check_tensor(out, "out")) != BSM_OK) return st;
-    if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
-    if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
-    const size_t need = bsm_decode_workspace_bytes(B, H, kv_len, D);
+    const size_t need = decode_part_bytes(B, H, capacity, D);
     if (!workspace || workspace_bytes < need)
         return fail(BSM_E_WORKSPACE, "decode workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
                     workspace ? "" : " (NULL)");
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
-    bsm::AttnParams p{};
-    p.B = B;
-    p.H = H;
-    p.T = kv_len;
-    p.nt = kv_len / bsm::kTile;
-    p.mask_b = spec->mask_b;
-    p.mask_flags = spec->flags;
-    p.sinks = spec->num_sinks;
-    p.prefix = effective_prefix(spec);
-    p.doc_ids = spec->doc_ids;
-    p.window = spec->window;
-    p.mod_flags = mod ? mod->flags : 0u;
-    p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
-    p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
-    p.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
-    fill_tensor(q, p.q, p.q_sb, p.q_sh, p.q_st);
-    fill_tensor(k, p.k, p.k_sb, p.k_sh, p.k_st);
-    fill_tensor(v, p.v, p.v_sb, p.v_sh, p.v_st);
-    const void *optr;
-    fill_tensor(out, optr, p.o_sb, p.o_sh, p.o_st);
-    p.o = const_cast<void *>(optr);
-    p.lse = lse;
-    return hip_status(bsm::launch_attn_decode(p, D, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
+    return hip_status(bsm::launch_attn_decode(d, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_decode launch");
 }
 

@@ -77,8 +77,16 @@ struct AttnParams {
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);
 hipError_t launch_attn_fwd(const AttnParams &p, int D, hipStream_t stream);
 hipError_t launch_attn_bwd(const AttnParams &p, int D, hipStream_t stream);
-// decode: one query per (b, h) at position T - 1; part = B*H*splits*(D + 2) floats
-int decode_splits(int kv_len);
-hipError_t launch_attn_decode(const AttnParams &p, int D, float *part, hipStream_t stream);
+// Decoding step: one query per (b, h) at the last live position of a cache
+// of p.T (capacity) positions; the block-mask row arrays of `a` are the
+// optional block mask (kv_num NULL: none).  part = B*H*slots*(D + 2) floats.
+struct DecodeLaunch {
+    AttnParams a;
+    int D;
+    const int32_t *kv_len;   // device live length(s)
+    int32_t kv_len_stride;   // 0: one value; 1: one per batch element
+};
+int decode_slots(int capacity);
+hipError_t launch_attn_decode(const DecodeLaunch &d, float *part, hipStream_t stream);
 
 }  // namespace bsm

@@ -231,23 +231,38 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace bsm_flex_attention_decode needs: per (batch,
- * head) and 1024-key chunk of the cache, D + 2 floats (the chunk's
- * unnormalised output, running maximum and sum). */
-size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t kv_len, int32_t D);
+ * head) and slot of eight 128-key tiles of the capacity, D + 2 floats (the
+ * slot's unnormalised output, running maximum and sum). */
+size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t capacity, int32_t D);
 
-/* Decoding step (tutorial "FlexAttention in PyTorch", "Decoding and paged
- * KV caches": the query length is 1 and the mask is taken against the current
- * key length).  One query per (batch, head) at position kv_len - 1 attends to
- * the cache k, v [B, H, kv_len, D] under the mask predicate (spec->seq_len ==
- * kv_len; no block mask is needed: each key's visibility is tested directly)
- * and the score modifications, as the forward does.
- * q, out: bf16 [B, H, 1, D] (stride_t unused); lse: fp32 [B, H], natural
- * log, -inf (with out = 0) when no key is visible.
+/* Decoding step (tutorial "FlexAttention in PyTorch", section "Decoding and
+ * paged KV caches": one query per step against a cache that grows; the
+ * allocation is bucketed and the mask follows the current length).
+ * The cache k, v is [B, H, capacity, D] (any capacity >= 1); its live length
+ * is a DEVICE int32 value read by the kernels -- kv_len[0] for every batch
+ * element (kv_len_stride 0) or kv_len[b] (kv_len_stride 1) -- so a step
+ * needs no host value and one launch configuration serves a whole bucket.
+ * Values are clamped to [0, capacity]; 0 gives out = 0, lse = -inf.
+ * The query of batch element b (q: [B, H, 1, D], stride_t unused) sits at
+ * position kv_len[b] - 1 and sees key kv < kv_len[b] when the mask predicate
+ * of spec (seq_len == capacity, doc_ids [mask_b, capacity]) holds for
+ * (kv_len[b] - 1, kv); its scores take the score modifications of the
+ * forward.
+ * bm (optional, may be NULL): the block mask of spec built once for the
+ * whole capacity (so capacity is then a multiple of 128).  The step reads
+ * only the key tiles listed in the row of query tiles holding the query
+ * (every tile some query of that row sees), so a document-masked step reads
+ * its document's tiles only; the mask stays valid while the cache grows
+ * within the capacity.  Without it every key below the live length is
+ * visited, except 1024-key chunks wholly before the window.
+ * out: bf16 [B, H, 1, D] (stride_t unused); lse: fp32 [B, H], natural log.
  * workspace: device, >= bsm_decode_workspace_bytes(), 256-byte aligned.
- * Errors: as the forward, plus BSM_E_WORKSPACE. */
-bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t kv_len, int32_t D,
+ * Errors: BSM_E_INVALID, BSM_E_UNSUPPORTED (D), BSM_E_WORKSPACE, BSM_E_HIP. */
+bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int32_t D,
+                                     const int32_t *kv_len, int32_t kv_len_stride,
                                      const bsm_tensor *q, const bsm_tensor *k, const bsm_tensor *v,
-                                     const bsm_mask_spec *spec, const bsm_score_mod *mod, float scale,
+                                     const bsm_mask_spec *spec, const bsm_block_mask *bm,
+                                     const bsm_score_mod *mod, float scale,
                                      const bsm_tensor *out, float *lse, void *workspace,
                                      size_t workspace_bytes, void *stream);
 

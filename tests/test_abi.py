@@ -163,14 +163,77 @@ def test_decode_rejects_bad_arguments():
     spec = _spec()
     t = _t()
     need = lib.bsm_decode_workspace_bytes(1, 1, 1024, 64)
-    assert need == 512  # one 1024-key chunk: (64 + 2) floats = 264 bytes, rounded up to a multiple of 256
+    assert need == 512  # one slot of 8 tiles: (64 + 2) floats = 264 bytes, rounded up to a multiple of 256
+    assert lib.bsm_decode_workspace_bytes(1, 1, 1000, 64) == 512  # any capacity
+    assert lib.bsm_decode_workspace_bytes(2, 3, 1025, 128) == 6400  # 2 x 3 x 2 slots x 130 floats x 4 B, to 256
 
-    def call(D=64, ws=FAKE, n=need, s=spec, lse=FAKE):
-        return lib.bsm_flex_attention_decode(1, 1, 1024, D, *([ctypes.byref(t)] * 3), ctypes.byref(s), None, 0.0,
-                                             ctypes.byref(t), lse, ws, n, None)
+    def call(D=64, ws=FAKE, n=need, s=spec, lse=FAKE, kvl=FAKE, stride=0, cap=1024, bm=None):
+        return lib.bsm_flex_attention_decode(1, 1, cap, D, kvl, stride, *([ctypes.byref(t)] * 3),
+                                             ctypes.byref(s), ctypes.byref(bm) if bm is not None else None, None,
+                                             0.0, ctypes.byref(t), lse, ws, n, None)
 
     assert call(D=96) == _lib.BSM_E_UNSUPPORTED
     assert call(n=need - 4) == _lib.BSM_E_WORKSPACE
     assert call(ws=None) == _lib.BSM_E_WORKSPACE
     assert call(lse=None) == _lib.BSM_E_INVALID
-    assert call(s=_spec(seq_len=2048)) == _lib.BSM_E_INVALID
+    assert call(kvl=None) == _lib.BSM_E_INVALID
+    assert call(stride=2) == _lib.BSM_E_INVALID
+    assert call(cap=0) == _lib.BSM_E_INVALID
+    assert call(s=_spec(seq_len=2048)) == _lib.BSM_E_INVALID   # seq_len must equal the capacity
+    assert call(bm=_bm(null=0)) == _lib.BSM_E_INVALID           # block mask row arrays
+    # a capacity that is not a multiple of 128 is fine without a block mask
+    # (fails only at the workspace check here), not with one
+    assert call(cap=1000, s=_spec(seq_len=1000), ws=None) == _lib.BSM_E_WORKSPACE
+    assert call(cap=1000, s=_spec(seq_len=1000), bm=_bm()) == _lib.BSM_E_INVALID
+
+
+def _cpu(shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_python_decode_checks_shapes_before_launch():
+    """The binding rejects shapes the C ABI cannot see (CPU tensors: nothing
+    reaches the library)."""
+    import torch
+    from block_sparse_masked_build_amd import api
+    B, H, T, D = 2, 3, 256, 64
+    k, v = _cpu((B, H, T, D)), _cpu((B, H, T, D))
+    spec = api.MaskSpec(T)
+    with pytest.raises(ValueError, match="q must be"):
+        api.flex_attention_decode(_cpu((B, H, T, D)), k, v, spec)       # a full-length q
+    with pytest.raises(ValueError, match="q must be"):
+        api.flex_attention_decode(_cpu((B, H, 1, 32)), k, v, spec)      # smaller D
+    with pytest.raises(ValueError, match="v "):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), k, _cpu((B, H, T - 128, D)), spec)
+    with pytest.raises(ValueError, match="lse"):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), k, v, spec, lse=_cpu((B, H + 1), torch.float32))
+    with pytest.raises(ValueError, match="lse"):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), k, v, spec, lse=_cpu((H, B), torch.float32).t())
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), k, v, spec,
+                                  api.ScoreMod(alibi_slopes=_cpu((H - 1,), torch.float32)))
+    with pytest.raises(ValueError, match="kv_len"):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), k, v, spec, kv_len=T + 1)
+    with pytest.raises(ValueError, match="kv_len"):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), k, v, spec, kv_len=torch.ones(B + 1, dtype=torch.int32))
+
+
+def test_python_fwd_bwd_check_slopes_and_lse():
+    import torch
+    from block_sparse_masked_build_amd import api
+    B, H, T, D = 1, 4, 256, 64
+    q = _cpu((B, H, T, D))
+    spec = api.MaskSpec(T)
+    bm = None
+    short = api.ScoreMod(alibi_slopes=_cpu((H - 1,), torch.float32))
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        api.flex_attention_fwd(q, q, q, bm, spec, short)
+    lse = _cpu((B, H, T), torch.float32)
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        api.flex_attention_bwd(q, q, q, q, lse, q, bm, spec, short)
+    with pytest.raises(ValueError, match="lse"):
+        api.flex_attention_bwd(q, q, q, q, _cpu((B, H, T), torch.bfloat16), q, bm, spec, None)
+    with pytest.raises(ValueError, match="dout"):
+        api.flex_attention_bwd(q, q, q, q, lse, _cpu((B, H, T, 32)), bm, spec, None)
+
