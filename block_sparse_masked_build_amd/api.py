@@ -312,7 +312,40 @@ def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = Non
     return out, lse
 
 
+def flex_attention_decode_static(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod], scale: Optional[float],
+                                 kv_len: torch.Tensor, block_mask: Optional[BlockMask], out: torch.Tensor,
+                                 lse: torch.Tensor):
+    """The decoding step of flex_attention_decode through the allocation-free
+    entry point: nothing is allocated, here or in the library (its partials
+    live in the library's static device scratch).  Every buffer is the
+    caller's: kv_len a device int32 tensor of 1 or B values, out [B, H, 1, D]
+    bf16, lse [B, H] float32.  Calls that overlap on one GPU race."""
+    B, H, capacity, D = k.shape
+    if v.shape != k.shape:
+        raise ValueError(f"v {tuple(v.shape)} must have the shape of k {tuple(k.shape)}")
+    if q.shape != (B, H, 1, D) or out.shape != (B, H, 1, D):
+        raise ValueError(f"q and out must be [B, H, 1, D] = {(B, H, 1, D)}")
+    if spec.T != capacity:
+        raise ValueError(f"mask spec length {spec.T} != cache capacity {capacity}")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H):
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    if not isinstance(kv_len, torch.Tensor):
+        raise ValueError("kv_len must be a device int32 tensor (the static entry point allocates nothing)")
+    _check_mod(mod, H)
+    kvl, stride = _kv_len_tensor(kv_len, B, capacity, q.device)
+    ts = [_tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+    cs = spec.c_struct()
+    cb = block_mask.c_struct() if block_mask is not None else None
+    cm = mod.c_struct() if mod is not None else None
+    check(lib.bsm_flex_attention_decode_static(
+        B, H, capacity, D, kvl.data_ptr(), stride, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
+        ctypes.byref(cs), ctypes.byref(cb) if cb is not None else None,
+        ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
+        ctypes.byref(ts[3]), lse.data_ptr(), _stream()))
+    return out, lse
+
+
 __all__ = ["MaskSpec", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
-           "flex_attention_decode", "decode_workspace",
+           "flex_attention_decode", "decode_workspace", "flex_attention_decode_static",
            "bwd_workspace", "block_mask_workspace", "_lib"]

@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "bsm_internal.hpp"
@@ -251,6 +252,47 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     return BSM_OK;
 }
 
+// ------------------------------------------------------------ static scratch
+// Device memory of the allocation-free decoding entry point: one array per
+// GPU, in the library's code object, held until the process ends.  Host code
+// never uses the array's name as an address: the address on each device comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+// Address of this device's scratch array (the current device, which must be
+// the stream's), looked up on the first call on the device.
+bsm_status scratch_address(void *stream, void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BSM_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(BSM_E_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return fail(BSM_E_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev) return fail(BSM_E_INVALID, "stream is on device %d, current device is %d", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(BSM_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return BSM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,6 +444,31 @@ bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int
         return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
     return hip_status(bsm::launch_attn_decode(d, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_decode launch");
+}
+
+size_t bsm_decode_static_max_bytes(void) { return kScratchBytes; }
+
+bsm_status bsm_flex_attention_decode_static(int32_t B, int32_t H, int32_t capacity, int32_t D,
+                                            const int32_t *kv_len, int32_t kv_len_stride, const bsm_tensor *q,
+                                            const bsm_tensor *k, const bsm_tensor *v, const bsm_mask_spec *spec,
+                                            const bsm_block_mask *bm, const bsm_score_mod *mod, float scale,
+                                            const bsm_tensor *out, float *lse, void *stream) {
+    bsm::DecodeLaunch d;
+    bsm_status st = prepare_decode(B, H, capacity, D, kv_len, kv_len_stride, q, k, v, spec, bm, mod, scale, out,
+                                   lse, d);
+    if (st != BSM_OK) return st;
+    const size_t need = decode_part_bytes(B, H, capacity, D);
+    if (need > kScratchBytes)
+        return fail(BSM_E_WORKSPACE,
+                    "decode partials need %zu bytes, beyond the %zu-byte static scratch (B * H * ceil(capacity / "
+                    "1024) * (D + 2) * 4 bytes); use bsm_flex_attention_decode with a workspace",
+                    need, kScratchBytes);
+    void *ptr = nullptr;
+    if ((st = scratch_address(stream, &ptr)) != BSM_OK) return st;
+    // Every slot of the partials is written before the combine reads it, so
+    // nothing in the scratch needs clearing.
+    return hip_status(bsm::launch_attn_decode(d, static_cast<float *>(ptr), static_cast<hipStream_t>(stream)),
+                      "bsm_flex_attention_decode_static launch");
 }
 
 const char *bsm_last_error(void) { return g_last_error.c_str(); }

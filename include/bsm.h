@@ -266,6 +266,26 @@ bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int
                                      const bsm_tensor *out, float *lse, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* Allocation-free decoding step, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  The same step as bsm_flex_attention_decode, with the
+ * partials kept in a static device array of bsm_decode_static_max_bytes()
+ * (16 MiB) that the library holds on each GPU it runs on until the process
+ * ends, instead of a caller workspace.  Requests whose partials,
+ * B * H * ceil(capacity / 1024) * (D + 2) * 4 bytes, exceed it return
+ * BSM_E_WORKSPACE.  The call allocates nothing; stream must belong to the
+ * current device (BSM_E_INVALID otherwise).  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (different streams, or host
+ * threads) race and give wrong results; calls ordered on one stream are
+ * safe.  Errors: as bsm_flex_attention_decode. */
+size_t bsm_decode_static_max_bytes(void);
+bsm_status bsm_flex_attention_decode_static(int32_t B, int32_t H, int32_t capacity, int32_t D,
+                                            const int32_t *kv_len, int32_t kv_len_stride,
+                                            const bsm_tensor *q, const bsm_tensor *k, const bsm_tensor *v,
+                                            const bsm_mask_spec *spec, const bsm_block_mask *bm,
+                                            const bsm_score_mod *mod, float scale,
+                                            const bsm_tensor *out, float *lse, void *stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *bsm_last_error(void);
 

@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -237,3 +237,14 @@ def test_python_fwd_bwd_check_slopes_and_lse():
     with pytest.raises(ValueError, match="dout"):
         api.flex_attention_bwd(q, q, q, q, lse, _cpu((B, H, T, 32)), bm, spec, None)
 
+
+def test_static_decode_rejects_oversize_on_the_host():
+    """The allocation-free decoding entry point checks the size of its
+    partials against the static scratch before touching the device."""
+    assert lib.bsm_decode_static_max_bytes() == 16 << 20
+    t = _t()
+    spec = _spec(seq_len=32768)
+    rc = lib.bsm_flex_attention_decode_static(64, 32, 32768, 128, FAKE, 0, *([ctypes.byref(t)] * 3),
+                                              ctypes.byref(spec), None, None, 0.0, ctypes.byref(t), FAKE, None)
+    assert rc == _lib.BSM_E_WORKSPACE
+    assert b"static scratch" in lib.bsm_last_error()
