@@ -79,14 +79,27 @@ the block that follows it."""
     return bad
 
 
+_ASM = {}
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    """Device assembly of a source, compiled once per test module."""
+    def get(src):
+        if src not in _ASM:
+            out = tmp_path_factory.mktemp("isa") / (src + ".s")
+            cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                   "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
+                   "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
+            subprocess.run(cmd, check=True, capture_output=True)
+            _ASM[src] = out.read_text()
+        return _ASM[src]
+    return get
+
+
 @pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip"])
-def test_no_inline_assembly_reads_of_pending_matrix_results(src, tmp_path):
-    out = tmp_path / "k.s"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
-           "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True)
-    text = out.read_text()
+def test_no_inline_assembly_reads_of_pending_matrix_results(src, asm):
+    text = asm(src)
     kernels = re.findall(r"^(_Z\S*kernel\S*):", text, re.M)
     assert kernels
     problems = {}
@@ -97,3 +110,32 @@ def test_no_inline_assembly_reads_of_pending_matrix_results(src, tmp_path):
         if bad:
             problems[k] = bad[:3]
     assert not problems, problems
+
+
+
+@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip", "mask_builder.hip", "attn_decode.hip"])
+def test_m0_is_only_written_by_the_lds_copies(src, asm):
+    """The asynchronous LDS copies set M0 (the LDS destination) in inline
+    assembly and list it as clobbered, but M0 is a register the compiler
+    reserves, and it does not promise to preserve a value of its own in M0
+    across such a block.  So the compiled code must not use M0 at all: no
+    instruction outside inline assembly may read or write it, and there is
+    no dynamic VGPR indexing (which keeps its index in M0) and no call."""
+    text = asm(src)
+    bad, in_asm = [], False
+    for raw in text.split("\n"):
+        if ";;#ASMSTART" in raw:
+            in_asm = True
+            continue
+        if ";;#ASMEND" in raw:
+            in_asm = False
+            continue
+        line = raw.split(";")[0].strip()
+        if not line or line.startswith(".") or line.endswith(":"):
+            continue
+        op = line.split()[0]
+        if in_asm:
+            continue
+        if re.search(r"\bm0\b", line) or "gpr_idx" in op or "movrel" in op or op == "s_swappc_b64":
+            bad.append(line)
+    assert not bad, bad[:5]
