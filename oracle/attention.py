@@ -6,7 +6,9 @@ What is computed, per batch element b, head h and query position q
 
   s_j    = scale * <q, k_j>                      scale = 1/sqrt(D) by default
   ALiBi:   s_j <- s_j - slope[h] * (q - j)        (tutorial "FlexAttention in
-                                                   PyTorch", Pattern 3)
+                                                   PyTorch", Pattern 3; q the
+                                                   query's absolute position,
+                                                   q_offset + its index)
   cap:     s_j <- c * tanh(s_j / c)              (same section, c = 30 there)
   out_q  = sum_{j in V_q} softmax(s)_j v_j        over visible keys only
   lse_q  = log sum_{j in V_q} exp(s_j)            natural log
@@ -71,16 +73,21 @@ from .predicate import visible
 ROW_CHUNK = 128
 
 
+def _qoff(spec):
+    return int(getattr(spec, "q_offset", 0))
+
+
 def _scale(D, scale):
     return 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
 
 
-def _scores(Qr, Kc, rows, cols, h, scale, mod):
-    """Returns (u, s): score before the cap and final score, [R, C]."""
+def _scores(Qr, Kc, rows, cols, h, scale, mod, q_offset=0):
+    """Returns (u, s): score before the cap and final score, [R, C]; rows are
+    query indices (absolute position q_offset + row), cols key positions."""
     s = scale * (Qr @ Kc.T)
     if mod is not None and mod.alibi_slopes is not None:
         slope = float(mod.alibi_slopes[h])
-        s = s - slope * (rows[:, None] - cols[None, :]).astype(np.float64)
+        s = s - slope * ((rows[:, None] + q_offset) - cols[None, :]).astype(np.float64)
     u = s
     if mod is not None and mod.softcap is not None:
         c = float(mod.softcap)
@@ -94,7 +101,7 @@ def _row_block(Q, K, V, spec, mod, b, h, rows, scale, restrict):
     m = visible(spec, b, rows[:, None], allcols[None, :])
     cols = np.nonzero(m.any(axis=0))[0] if restrict else allcols
     m = m[:, cols]
-    u, s = _scores(Q[rows], K[cols], rows, cols, h, scale, mod)
+    u, s = _scores(Q[rows], K[cols], rows, cols, h, scale, mod, _qoff(spec))
     s = np.where(m, s, -np.inf)
     return cols, m, u, s
 
@@ -141,7 +148,7 @@ def _grad_block(Q, K, V, dO, spec, mod, b, h, rows, cols_sel, out_r, lse_r, sc, 
     """g [R, C], p [R, C] on rows x cols_sel (visible pairs only), and with
     with_cap the cap derivative c' [R, C] (ones without a cap)."""
     m = visible(spec, b, rows[:, None], cols_sel[None, :])
-    u, s = _scores(Q[rows], K[cols_sel], rows, cols_sel, h, sc, mod)
+    u, s = _scores(Q[rows], K[cols_sel], rows, cols_sel, h, sc, mod, _qoff(spec))
     live = np.isfinite(lse_r)
     with np.errstate(invalid="ignore", over="ignore"):
         p = np.exp(s - np.where(live, lse_r, 0.0)[:, None])
@@ -180,7 +187,7 @@ def backward_dense(Q, K, V, dO, spec, mod, b, h, scale=None, with_mass=False):
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
     mQ, mK, mV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
-    allcols = np.arange(T)
+    allcols = np.arange(K.shape[0])
     for a in range(0, T, ROW_CHUNK):
         r = np.arange(a, min(T, a + ROW_CHUNK))
         g, p, cp = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc, with_cap=True)
@@ -207,7 +214,7 @@ def backward_dq_rows(Q, K, V, dO, spec, mod, b, h, rows, scale=None, with_mass=F
     mQ = np.zeros_like(dQ)
     for a in range(0, len(rows), ROW_CHUNK):
         r = rows[a:a + ROW_CHUNK]
-        m = visible(spec, b, r[:, None], np.arange(T)[None, :])
+        m = visible(spec, b, r[:, None], np.arange(K.shape[0])[None, :])
         cols = np.nonzero(m.any(axis=0))[0]
         if len(cols) == 0:
             continue
@@ -261,13 +268,13 @@ def slope_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=Non
     sc = _scale(D, scale)
     if out is None or lse is None:
         out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
-    allcols = np.arange(T)
+    allcols = np.arange(K.shape[0])
     total = 0.0
     mass = 0.0
     for a in range(0, T, ROW_CHUNK):
         r = np.arange(a, min(T, a + ROW_CHUNK))
         g, _ = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc)
-        term = g * (allcols[None, :] - r[:, None]).astype(np.float64)
+        term = g * (allcols[None, :] - (r[:, None] + _qoff(spec))).astype(np.float64)
         total += float(term.sum())
         mass += float(np.abs(term).sum())
     return total, mass

@@ -10,7 +10,8 @@ Follows:
 
 Readings taken where the pages are silent:
   * classes come from the exact number of visible pairs in the tile
-    (0 -> empty, 128*128 -> full, otherwise partial);
+    (0 -> empty, 128*128 -> full, otherwise partial), so a tile at the end
+    of a length that is not a multiple of 128 is never full;
   * partial and full tiles are listed separately, each in ascending column
     order, padded with -1 after the count; counts are int32;
   * for the backward pass the same lists are also given per key tile
@@ -55,8 +56,8 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.oracle_tile_counts.restype = ctypes.c_int
         lib.oracle_tile_counts.argtypes = [
-            ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -69,43 +70,54 @@ def _flags(spec) -> int:
         f |= 2
     if spec.window is not None:
         f |= 4
-        if spec.sinks:
-            f |= 8
-    if spec.causal and getattr(spec, "prefix", 0):
+    if spec.sinks:
+        f |= 8
+    if getattr(spec, "prefix", 0):
         f |= 16
+    if getattr(spec, "table", None) is not None:
+        f |= 32
     return f
 
 
+def _q_len(spec):
+    q = getattr(spec, "q_len", None)
+    return spec.T if q is None else int(q)
+
+
 def tile_counts(spec) -> np.ndarray:
-    """int32 [mask_b, T/128, T/128]: visible pairs per tile (brute force)."""
-    T = spec.T
-    if T % TILE:
-        raise ValueError("T must be a multiple of 128")
+    """int32 [mask_b, ceil(Q_LEN/128), ceil(KV_LEN/128)]: visible pairs per
+    tile (brute force)."""
+    kv_len, q_len, q_off = spec.T, _q_len(spec), int(getattr(spec, "q_offset", 0))
     mb = spec.mask_b
-    nt = T // TILE
-    out = np.zeros((mb, nt, nt), dtype=np.int32)
-    docs = None
+    nq, nk = -(-q_len // TILE), -(-kv_len // TILE)
+    out = np.zeros((mb, nq, nk), dtype=np.int32)
+    docs, npos = None, max(kv_len, q_off + q_len)
     if spec.document:
         docs = np.ascontiguousarray(spec.doc_ids, dtype=np.int32)
+        if docs.shape[1] < npos:
+            raise ValueError(f"doc_ids cover {docs.shape[1]} positions, need {npos}")
+        npos = docs.shape[1]
     rc = _load().oracle_tile_counts(
-        T, mb, _flags(spec),
-        docs.ctypes.data if docs is not None else None,
+        kv_len, q_len, q_off, mb, _flags(spec),
+        docs.ctypes.data if docs is not None else None, npos,
         int(spec.window) if spec.window is not None else 0,
-        int(spec.sinks), int(getattr(spec, "prefix", 0)), out.ctypes.data)
+        int(spec.sinks), int(getattr(spec, "prefix", 0)),
+        int(getattr(spec, "table", None) or 0) & 0xFFFFFFFF, out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_tile_counts rejected the spec")
     return out
 
 
 def tile_counts_dense_numpy(spec) -> np.ndarray:
-    """Same counts from a dense [T, T] boolean mask (small T only)."""
-    T = spec.T
-    nt = T // TILE
-    ar = np.arange(T)
+    """Same counts from a dense [Q_LEN, KV_LEN] boolean mask, padded with
+    False to whole tiles (small sizes only)."""
+    kv_len, q_len = spec.T, _q_len(spec)
+    nq, nk = -(-q_len // TILE), -(-kv_len // TILE)
     res = []
     for b in range(spec.mask_b):
-        m = visible(spec, b, ar[:, None], ar[None, :])
-        res.append(m.reshape(nt, TILE, nt, TILE).sum(axis=(1, 3)).astype(np.int32))
+        m = np.zeros((nq * TILE, nk * TILE), dtype=bool)
+        m[:q_len, :kv_len] = visible(spec, b, np.arange(q_len)[:, None], np.arange(kv_len)[None, :])
+        res.append(m.reshape(nq, TILE, nk, TILE).sum(axis=(1, 3)).astype(np.int32))
     return np.stack(res)
 
 

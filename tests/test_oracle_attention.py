@@ -325,3 +325,138 @@ def test_forward_prefix_lm_matches_sdpa(P):
     out, _ = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
     np.testing.assert_allclose(out[:P], _sdpa(Q[:P], K[:P], V[:P]), rtol=0, atol=1e-12)
     np.testing.assert_allclose(out[P:], _sdpa(Q, K, V, is_causal=True)[P:], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------- Q_LEN != KV_LEN,
+# ragged lengths, composed masks
+
+def _rect_case(Tk, Lq, seed):
+    docs = doc_ids_geometric(Tk, 70, np.random.default_rng(seed))
+    sq = MaskSpecData(Tk, causal=True, document=True, doc_ids=docs[None], window=150, sinks=3, prefix=20)
+    rect = MaskSpecData(Tk, causal=True, document=True, doc_ids=docs[None], window=150, sinks=3, prefix=20,
+                        q_len=Lq, q_offset=Tk - Lq)
+    mod = ScoreModData(alibi_slopes=alibi_slopes(2), softcap=20.0)
+    return sq, rect, mod
+
+
+@pytest.mark.parametrize("Tk,Lq", [(300, 1), (300, 77), (384, 384), (257, 130)])
+def test_rectangular_is_a_slice_of_the_square_problem(Tk, Lq):
+    """Queries at the end of the keys (q_offset = KV_LEN - Q_LEN): the forward
+    equals rows q_offset.. of the square problem, and the backward equals the
+    square backward with dO zero on the first q_offset rows (dQ on the last
+    rows, dK and dV everywhere) -- with documents, window, sinks, prefix,
+    ALiBi and soft-cap on, so every term sees absolute positions."""
+    sq, rect, mod = _rect_case(Tk, Lq, 5)
+    off = Tk - Lq
+    Q, K, V, dO = (_rand((Tk, 16), 70 + s) for s in range(4))
+    o_sq, l_sq = oracle.forward_dense(Q, K, V, sq, mod, 0, 1)
+    o_r, l_r = oracle.forward_dense(Q[off:], K, V, rect, mod, 0, 1)
+    np.testing.assert_allclose(o_r, o_sq[off:], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_r, l_sq[off:], rtol=0, atol=1e-12)
+    dO_sq = dO.copy()
+    dO_sq[:off] = 0.0
+    dq_sq, dk_sq, dv_sq = oracle.backward_dense(Q, K, V, dO_sq, sq, mod, 0, 1)
+    dq, dk, dv = oracle.backward_dense(Q[off:], K, V, dO[off:], rect, mod, 0, 1)
+    np.testing.assert_allclose(dq, dq_sq[off:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_sq, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_sq, rtol=0, atol=1e-12)
+    # the sampled paths agree with the dense one
+    rows = np.array([0, Lq - 1])
+    np.testing.assert_allclose(oracle.backward_dq_rows(Q[off:], K, V, dO[off:], rect, mod, 0, 1, rows), dq[rows],
+                               rtol=0, atol=1e-12)
+    cols = np.array([0, Tk // 2, Tk - 1])
+    dkc, dvc = oracle.backward_dkdv_cols(Q[off:], K, V, dO[off:], rect, mod, 0, 1, cols)
+    np.testing.assert_allclose(dkc, dk[cols], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dvc, dv[cols], rtol=0, atol=1e-12)
+
+
+def test_ragged_length_matches_sdpa():
+    """T = 1000 (not a multiple of 128), causal: torch's SDPA in fp64."""
+    Q, K, V = (_rand((1000, D), s) for s in (81, 82, 83))
+    out, _ = oracle.forward_dense(Q, K, V, MaskSpecData(1000, causal=True), None, 0, 0)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V, is_causal=True), rtol=0, atol=1e-12)
+
+
+def test_cross_lengths_without_causal_match_sdpa():
+    """Q_LEN = 100 queries over KV_LEN = 300 keys, no mask: SDPA fp64."""
+    Q, K, V = _rand((100, D), 84), _rand((300, D), 85), _rand((300, D), 86)
+    out, _ = oracle.forward_dense(Q, K, V, MaskSpecData(300, causal=False, q_len=100), None, 0, 0)
+    np.testing.assert_allclose(out, _sdpa(Q, K, V), rtol=0, atol=1e-12)
+
+
+def test_table_of_the_standard_combination_gives_the_same_attention():
+    """The standard combination written as a truth table gives the same
+    outputs and gradients (documents, window, sinks, prefix, mods)."""
+    Tt = 256
+    docs = doc_ids_geometric(Tt, 50, np.random.default_rng(8))
+    spec = MaskSpecData(Tt, causal=True, document=True, doc_ids=docs[None], window=60, sinks=5, prefix=9)
+    t = 0
+    for idx in range(32):
+        c, d, w, s, p = (bool(idx & k) for k in (1, 2, 4, 8, 16))
+        t |= int((c or p) and d and (w or s)) << idx
+    tab = MaskSpecData(Tt, causal=True, document=True, doc_ids=docs[None], window=60, sinks=5, prefix=9, table=t)
+    mod = ScoreModData(alibi_slopes=alibi_slopes(2), softcap=30.0)
+    Q, K, V, dO = (_rand((Tt, 16), 90 + s) for s in range(4))
+    for a, b_ in zip(oracle.forward_dense(Q, K, V, spec, mod, 0, 0), oracle.forward_dense(Q, K, V, tab, mod, 0, 0)):
+        np.testing.assert_array_equal(a, b_)
+    for a, b_ in zip(oracle.backward_dense(Q, K, V, dO, spec, mod, 0, 0),
+                     oracle.backward_dense(Q, K, V, dO, tab, mod, 0, 0)):
+        np.testing.assert_array_equal(a, b_)
+
+
+def test_or_of_masks_matches_explicit_mask_sdpa():
+    """A composed mask (causal AND window) OR (NOT causal AND same document)
+    as a truth table equals SDPA with the same mask written out densely."""
+    Tt = 256
+    docs = doc_ids_geometric(Tt, 40, np.random.default_rng(9))
+    T_C, T_D, T_W = 0xAAAAAAAA, 0xCCCCCCCC, 0xF0F0F0F0
+    table = (T_C & T_W) | ((0xFFFFFFFF ^ T_C) & T_D)
+    spec = MaskSpecData(Tt, document=True, doc_ids=docs[None], window=30, table=table)
+    Q, K, V = (_rand((Tt, D), 95 + s) for s in range(3))
+    q, k = np.arange(Tt)[:, None], np.arange(Tt)[None, :]
+    m = ((q >= k) & ((q - k) < 30)) | ((q < k) & (docs[q] == docs[k]))
+    out, _ = oracle.forward_dense(Q, K, V, spec, None, 0, 0)
+    ref = _sdpa(Q, K, V, attn_mask=torch.from_numpy(m)[None, None])
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_rectangular_backward_finite_differences():
+    """Central differences of the rectangular forward (8 queries at the end
+    of 200 keys, documents, ALiBi + soft-cap)."""
+    sq, rect, mod = _rect_case(200, 8, 6)
+    Q, K, V, dO = (_rand(sh, 100 + s) * 1.5 for s, sh in enumerate([(8, 16), (200, 16), (200, 16), (8, 16)]))
+    dQ, dK, dV = oracle.backward_dense(Q, K, V, dO, rect, mod, 0, 1)
+
+    def loss(Qx, Kx, Vx):
+        o, _ = oracle.forward_dense(Qx, Kx, Vx, rect, mod, 0, 1)
+        return float(np.sum(o * dO))
+
+    rng = np.random.default_rng(3)
+    eps = 1e-6
+    for which, G in (("q", dQ), ("k", dK), ("v", dV)):
+        X = {"q": Q, "k": K, "v": V}
+        for _ in range(4):
+            t, d = int(rng.integers(0, X[which].shape[0])), int(rng.integers(0, 16))
+            Xp = {n: a.copy() for n, a in X.items()}
+            Xm = {n: a.copy() for n, a in X.items()}
+            Xp[which][t, d] += eps
+            Xm[which][t, d] -= eps
+            fd = (loss(Xp["q"], Xp["k"], Xp["v"]) - loss(Xm["q"], Xm["k"], Xm["v"])) / (2 * eps)
+            assert abs(fd - G[t, d]) <= 1e-6 * max(1.0, abs(fd)), (which, t, d, fd, G[t, d])
+
+
+def test_rectangular_slope_gradient_finite_differences():
+    """dL/dslope with absolute query positions (q_offset > 0)."""
+    sq, rect, mod = _rect_case(200, 40, 7)
+    Q, K, V, dO = (_rand(sh, 110 + s) for s, sh in enumerate([(40, 16), (200, 16), (200, 16), (40, 16)]))
+    g, _ = oracle.slope_grad_dense(Q, K, V, dO, rect, mod, 0, 1)
+    eps = 1e-6
+
+    def loss(delta):
+        sl = mod.alibi_slopes.astype(np.float64).copy()
+        sl[1] += delta
+        o, _ = oracle.forward_dense(Q, K, V, rect, ScoreModData(alibi_slopes=sl, softcap=mod.softcap), 0, 1)
+        return float(np.sum(o * dO))
+
+    fd = (loss(eps) - loss(-eps)) / (2 * eps)
+    assert abs(fd - g) <= 1e-6 * max(1.0, abs(fd)), (fd, g)

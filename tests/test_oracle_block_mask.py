@@ -227,3 +227,148 @@ def test_prefix_brute_force():
         for _ in range(6):
             spec = _random_prefix_spec(rng, T)
             assert np.array_equal(oracle.tile_counts(spec), oracle.tile_counts_dense_numpy(spec)), spec
+
+
+# ---------------------------------------------------------- Q_LEN != KV_LEN,
+# lengths that are not multiples of 128, composed masks
+
+# Truth tables of the five terms alone: bit `idx` of a term's table is set
+# when the term's own bit is set in idx (C 1, Dc 2, W 4, S 8, P 16).
+T_C, T_D, T_W, T_S, T_P = 0xAAAAAAAA, 0xCCCCCCCC, 0xF0F0F0F0, 0xFF00FF00, 0xFFFF0000
+ALL = 0xFFFFFFFF
+
+
+def _pairs_python_general(spec):
+    """Pure-Python loops over every (query index, key) pair (tiny sizes),
+    with absolute query positions and, when given, the truth table."""
+    kv_len, q_len, off = spec.T, spec.Q, spec.q_offset
+    nq, nk = -(-q_len // 128), -(-kv_len // 128)
+    res = np.zeros((spec.mask_b, nq, nk), dtype=np.int64)
+    for b in range(spec.mask_b):
+        docs = None if spec.doc_ids is None else [int(x) for x in spec.doc_ids[b]]
+        for qi in range(q_len):
+            q = off + qi
+            for kv in range(kv_len):
+                c = q >= kv
+                d = spec.document and docs[q] == docs[kv]
+                w = spec.window is not None and (q - kv) < spec.window
+                s = bool(spec.sinks) and kv < spec.sinks
+                p = bool(spec.prefix) and kv < spec.prefix
+                if spec.table is not None:
+                    ok = (spec.table >> (c + 2 * d + 4 * w + 8 * s + 16 * p)) & 1
+                else:
+                    ok = ((not spec.causal) or c or p) and ((not spec.document) or d) and \
+                         (spec.window is None or w or s)
+                if ok:
+                    res[b, qi // 128, kv // 128] += 1
+    return res
+
+
+@pytest.mark.parametrize("T", [1000, 129, 383, 65535])
+def test_ragged_causal_closed_form(T):
+    """Causal with T = 128 n + r, 0 < r < 128: ceil(T/128) = n + 1 tiles per
+    side; the (n+1)(n+2)/2 tiles on or below the diagonal are visible; full
+    are only the n(n-1)/2 strictly below it among whole tiles -- the last
+    row and column hold r < 128 positions, so no tile of theirs is full."""
+    n = T // 128
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True)))
+    assert cls.shape == (1, n + 1, n + 1)
+    assert int((cls > 0).sum()) == (n + 1) * (n + 2) // 2
+    assert int((cls == oracle.FULL).sum()) == n * (n - 1) // 2
+
+
+@pytest.mark.parametrize("a,c", [(2, 6), (1, 0), (3, 5), (8, 504)])
+def test_rectangular_bottom_right_causal_closed_form(a, c):
+    """Q_LEN = 128 a queries at the end of KV_LEN = 128 (c + a) keys
+    (q_offset = 128 c), causal: query-tile row i sees key tiles 0 .. c + i,
+    all full but the diagonal one, so c a + a (a + 1) / 2 visible and
+    c a + a (a - 1) / 2 full."""
+    spec = MaskSpecData(128 * (c + a), causal=True, q_len=128 * a, q_offset=128 * c)
+    cls = oracle.classify(oracle.tile_counts(spec))
+    assert cls.shape == (1, a, c + a)
+    assert int((cls > 0).sum()) == c * a + a * (a + 1) // 2
+    assert int((cls == oracle.FULL).sum()) == c * a + a * (a - 1) // 2
+
+
+def test_single_query_rows_are_partial():
+    """One query (the decoding shape: Q_LEN 1 at position KV_LEN - 1), causal:
+    every key tile holds a visible pair and none can be full."""
+    for L in (1, 127, 128, 129, 1000, 4096):
+        cls = oracle.classify(oracle.tile_counts(MaskSpecData(L, causal=True, q_len=1, q_offset=L - 1)))
+        assert cls.shape == (1, 1, -(-L // 128))
+        assert np.all(cls == oracle.PARTIAL)
+
+
+def test_composed_closed_forms_64k():
+    """Truth tables at T = 65,536 (512 tiles per side):
+      * NOT causal (kv > q): the 130,816 tiles above the diagonal, full, and
+        the 512 diagonal tiles, partial;
+      * the window alone, no causal term (q - kv < 1024): every tile on or
+        above the diagonal is full (q - kv <= 127 < 1024 there) and below it
+        diagonal d holds differences 128 d - 127 .. 128 d + 127, so diagonals
+        1..8 are visible and 1..7 full (128 * 7 + 127 = 1023 < 1024);
+      * causal AND (window OR sink) written as a table equals Pattern 2 at
+        32K (2,515 tiles, 1,764 full)."""
+    T, n = 65536, 512
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, table=ALL ^ T_C)))
+    assert int((cls > 0).sum()) == n * (n + 1) // 2 and int((cls == oracle.FULL).sum()) == n * (n - 1) // 2
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, window=1024, table=T_W)))
+    upper = n * (n + 1) // 2
+    assert int((cls > 0).sum()) == upper + sum(n - d for d in range(1, 9))
+    assert int((cls == oracle.FULL).sum()) == upper + sum(n - d for d in range(1, 8))
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(32768, window=1024, sinks=4, table=T_C & (T_W | T_S))))
+    assert int((cls > 0).sum()) == 2515 and int((cls == oracle.FULL).sum()) == 1764
+
+
+def _equivalent_table(spec):
+    """The standard combination of the spec's terms as a truth table,
+    enumerated over the 32 term combinations."""
+    t = 0
+    for idx in range(32):
+        c, d, w, s, p = (bool(idx & k) for k in (1, 2, 4, 8, 16))
+        ok = ((not spec.causal) or c or p) and ((not spec.document) or d) and (spec.window is None or w or s)
+        t |= int(ok) << idx
+    return t
+
+
+def _random_general_spec(rng, table=False):
+    kv_len = int(rng.choice([1, 77, 128, 129, 300, 384, 700]))
+    q_len = int(rng.choice([1, 5, 128, 200, kv_len]))
+    q_off = int(rng.choice([0, max(0, kv_len - q_len), 3, 130]))
+    npos = max(kv_len, q_off + q_len)
+    spec = _random_spec(rng, npos)
+    spec.T, spec.q_len, spec.q_offset = kv_len, q_len, q_off
+    spec.prefix = int(rng.choice([0, 0, 40, 129]))
+    if table:
+        spec.table = int(rng.integers(0, 2 ** 32))
+    return spec
+
+
+def test_general_brute_force_python_tiny():
+    """C counter == pure-Python per-pair loops on random rectangular, ragged
+    and composed specs."""
+    rng = np.random.default_rng(21)
+    for it in range(10):
+        spec = _random_general_spec(rng, table=bool(it % 2))
+        assert np.array_equal(oracle.tile_counts(spec), _pairs_python_general(spec)), spec
+
+
+def test_general_brute_force_dense_numpy():
+    """C counter == the dense-mask reduction (numpy predicate) on random
+    rectangular, ragged and composed specs."""
+    rng = np.random.default_rng(22)
+    for it in range(40):
+        spec = _random_general_spec(rng, table=bool(it % 2))
+        assert np.array_equal(oracle.tile_counts(spec), oracle.tile_counts_dense_numpy(spec)), spec
+
+
+def test_table_of_the_standard_combination_gives_the_same_counts():
+    """A truth table written out from the standard combination (causal OR
+    prefix) AND document AND (window OR sink) classifies every tile as the
+    standard path does, on random square and rectangular specs."""
+    rng = np.random.default_rng(23)
+    for it in range(30):
+        spec = _random_general_spec(rng) if it % 2 else _random_spec(rng, int(rng.choice([256, 384, 1024])))
+        ref = oracle.tile_counts(spec)
+        spec.table = _equivalent_table(spec)
+        assert np.array_equal(oracle.tile_counts(spec), ref), spec

@@ -31,24 +31,48 @@ import torch
 class MaskSpecData:
     """Plain description of a mask predicate.
 
+    T           -- number of key positions (KV_LEN)
+    q_len       -- number of queries (Q_LEN; None: T); query i sits at
+                   absolute position q_offset + i
     causal      -- q >= kv
-    document    -- doc_ids[b, q] == doc_ids[b, kv]; doc_ids has shape [mask_b, T]
+    document    -- doc_ids[b, q] == doc_ids[b, kv]; doc_ids has shape
+                   [mask_b, positions], positions = max(T, q_offset + q_len)
     window      -- q - kv < window   (None: no window term)
     sinks       -- kv < sinks, OR-ed with the window term (0: none)
     prefix      -- kv < prefix, OR-ed with the causal term (prefix-LM: the
                    first `prefix` positions are seen by every query; 0: none)
+    table       -- None: the terms combine as above.  Otherwise a 32-bit truth
+                   table over the five terms: the pair is visible iff bit
+                   (C + 2 Dc + 4 W + 8 S + 16 P) of it is set, with C = q >= kv,
+                   Dc = same document, W = q - kv < window, S = kv < sinks,
+                   P = kv < prefix (a term whose data is absent -- no document
+                   ids, no window -- is 0; the flags above are then unused
+                   except to say which data exist)
     """
     T: int
     causal: bool = True
     document: bool = False
-    doc_ids: Optional[np.ndarray] = None  # int32 [mask_b, T]
+    doc_ids: Optional[np.ndarray] = None  # int32 [mask_b, positions]
     window: Optional[int] = None
     sinks: int = 0
     prefix: int = 0
+    q_len: Optional[int] = None
+    q_offset: int = 0
+    table: Optional[int] = None
 
     @property
     def mask_b(self) -> int:
         return 1 if self.doc_ids is None else int(self.doc_ids.shape[0])
+
+    @property
+    def Q(self) -> int:
+        """Number of queries."""
+        return self.T if self.q_len is None else int(self.q_len)
+
+    @property
+    def positions(self) -> int:
+        """Positions covered by the document ids: keys and queries."""
+        return max(self.T, self.q_offset + self.Q)
 
 
 @dataclasses.dataclass
