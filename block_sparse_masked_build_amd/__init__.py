@@ -5,9 +5,11 @@ first use; importing the package alone does not, so that `build` can run
 before the library exists.  There is no fallback: a missing library raises
 ImportError.
 """
-_API_NAMES = {"MaskSpec", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
+_API_NAMES = {"MaskSpec", "MaskTerm", "CAUSAL", "SAME_DOC", "IN_WINDOW", "SINK", "PREFIX",
+              "and_masks", "or_masks", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
               "empty_block_mask", "build_block_mask", "flex_attention_fwd",
-              "flex_attention_bwd", "bwd_workspace", "block_mask_workspace"}
+              "flex_attention_bwd", "bwd_workspace", "block_mask_workspace",
+              "flex_attention_decode", "flex_attention_decode_static", "decode_workspace"}
 
 
 def __getattr__(name):

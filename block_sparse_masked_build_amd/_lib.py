@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "BSM_OK", 1: "BSM_E_INVALID", 2: "BSM_E_UNSUPPORTED",
                 3: "BSM_E_WORKSPACE", 4: "BSM_E_HIP"}
 
 BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX = 1, 2, 4, 8, 16
+BSM_MASK_TABLE = 32
 BSM_MOD_ALIBI, BSM_MOD_SOFTCAP = 1, 2
 
 
@@ -29,7 +30,8 @@ class BsmMaskSpec(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("seq_len", ctypes.c_int32),
                 ("mask_b", ctypes.c_int32), ("doc_ids", ctypes.c_void_p),
                 ("window", ctypes.c_void_p), ("num_sinks", ctypes.c_int32),
-                ("prefix_len", ctypes.c_int32)]
+                ("prefix_len", ctypes.c_int32), ("q_len", ctypes.c_int32),
+                ("q_offset", ctypes.c_int32), ("table", ctypes.c_uint32)]
 
 
 class BsmBlockMask(ctypes.Structure):
@@ -52,7 +54,7 @@ class BsmTensor(ctypes.Structure):
 # Every symbol include/bsm.h declares, with its ctypes signature.
 _P = ctypes.POINTER
 SIGNATURES = {
-    "bsm_block_mask_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "bsm_block_mask_workspace_bytes": (ctypes.c_size_t, [_P(BsmMaskSpec)]),
     "bsm_build_block_mask": (ctypes.c_int, [_P(BsmMaskSpec), _P(BsmBlockMask), ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
     "bsm_flex_attention_fwd": (ctypes.c_int, [

@@ -7,6 +7,12 @@ PyTorch provides device memory and the current stream.
     bm   = build_block_mask(spec)                     # once per mask
     out, lse = flex_attention_fwd(q, k, v, bm, spec, score_mod)
     dq, dk, dv = flex_attention_bwd(q, k, v, out, lse, dout, bm, spec, score_mod)
+
+Queries and keys may differ in number: mask_spec(KV_LEN, q_len=Q_LEN,
+q_offset=o) puts query i at absolute position o + i (the last Q_LEN positions
+of a cache when o = KV_LEN - Q_LEN).  Masks composed with and_masks /
+or_masks / ~ over the terms CAUSAL, SAME_DOC, IN_WINDOW, SINK and PREFIX are
+passed as mask_spec(..., composed=expr).
 """
 from __future__ import annotations
 
@@ -20,21 +26,97 @@ import torch
 from . import _lib
 from ._lib import (BsmBlockMask, BsmMaskSpec, BsmScoreMod, BsmTensor, check, lib,
                    BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX,
-                   BSM_MOD_ALIBI, BSM_MOD_SOFTCAP)
+                   BSM_MASK_TABLE, BSM_MOD_ALIBI, BSM_MOD_SOFTCAP)
 
 TILE = 128
+
+
+class MaskTerm:
+    """A boolean function of the five mask terms -- causal (q >= kv), same
+    document, in window (q - kv < window), sink (kv < sinks), prefix
+    (kv < prefix) -- held as its 32-entry truth table: bit
+    (C + 2 Dc + 4 W + 8 S + 16 P) is the value when those terms hold.
+    Combined with & (and_masks), | (or_masks) and ~ (tutorial "FlexAttention
+    in PyTorch", Pattern 3)."""
+
+    __slots__ = ("table",)
+
+    def __init__(self, table: int):
+        self.table = int(table) & 0xFFFFFFFF
+
+    def __and__(self, other: "MaskTerm") -> "MaskTerm":
+        return MaskTerm(self.table & other.table)
+
+    def __or__(self, other: "MaskTerm") -> "MaskTerm":
+        return MaskTerm(self.table | other.table)
+
+    def __invert__(self) -> "MaskTerm":
+        return MaskTerm(~self.table)
+
+    def __eq__(self, other) -> bool:
+        return isinstance(other, MaskTerm) and other.table == self.table
+
+    def __hash__(self) -> int:
+        return hash(self.table)
+
+    def __repr__(self) -> str:
+        return f"MaskTerm(0x{self.table:08X})"
+
+
+CAUSAL = MaskTerm(0xAAAAAAAA)
+SAME_DOC = MaskTerm(0xCCCCCCCC)
+IN_WINDOW = MaskTerm(0xF0F0F0F0)
+SINK = MaskTerm(0xFF00FF00)
+PREFIX = MaskTerm(0xFFFF0000)
+ALL = MaskTerm(0xFFFFFFFF)
+NONE = MaskTerm(0)
+
+
+def and_masks(*terms: MaskTerm) -> MaskTerm:
+    out = ALL
+    for t in terms:
+        out = out & t
+    return out
+
+
+def or_masks(*terms: MaskTerm) -> MaskTerm:
+    out = NONE
+    for t in terms:
+        out = out | t
+    return out
 
 
 @dataclasses.dataclass
 class MaskSpec:
     """Device-side mask description.  `window` is a device int32 tensor of
-    one element so it can change between calls without touching the host."""
+    one element so it can change between calls without touching the host.
+    T is KV_LEN; Q_LEN = q_len (0: T) queries sit at absolute positions
+    q_offset + i."""
     T: int
     causal: bool = True
-    doc_ids: Optional[torch.Tensor] = None   # int32 [mask_b, T] on the device
+    doc_ids: Optional[torch.Tensor] = None   # int32 [mask_b, positions] on the device
     window: Optional[torch.Tensor] = None    # int32 [1] on the device
     sinks: int = 0
     prefix: int = 0                          # prefix-LM: keys < prefix seen by every query
+    q_len: int = 0
+    q_offset: int = 0
+    composed: Optional[MaskTerm] = None      # replaces the standard combination of the terms
+
+    @property
+    def Q(self) -> int:
+        return self.q_len if self.q_len else self.T
+
+    @property
+    def positions(self) -> int:
+        return max(self.T, self.q_offset + self.Q)
+
+    @property
+    def QT(self) -> int:
+        return -(-self.Q // TILE)
+
+    @property
+    def KT(self) -> int:
+        return -(-self.T // TILE)
 
     @property
     def mask_b(self) -> int:
@@ -49,15 +131,18 @@ class MaskSpec:
             f |= BSM_MASK_DOCUMENT
         if self.window is not None:
             f |= BSM_MASK_WINDOW
-            if self.sinks:
-                f |= BSM_MASK_SINKS
+        if self.sinks and (self.window is not None or self.composed is not None):
+            f |= BSM_MASK_SINKS
+        if self.composed is not None:
+            f |= BSM_MASK_TABLE
         return f
 
     def c_struct(self) -> BsmMaskSpec:
         return BsmMaskSpec(self.flags, self.T, self.mask_b,
                            self.doc_ids.data_ptr() if self.doc_ids is not None else None,
                            self.window.data_ptr() if self.window is not None else None,
-                           int(self.sinks), int(self.prefix))
+                           int(self.sinks), int(self.prefix), int(self.q_len), int(self.q_offset),
+                           self.composed.table if self.composed is not None else 0)
 
     def set_window(self, w: int) -> None:
         """Writes a new window value on the device (stream-ordered)."""
@@ -88,7 +173,7 @@ class BlockMask(NamedTuple):
     q_indices: torch.Tensor
     full_q_num_blocks: torch.Tensor
     full_q_indices: torch.Tensor
-    doc_range: torch.Tensor   # int32 [mask_b, T, 2]: (first, last) position of each position's document
+    doc_range: torch.Tensor   # int32 [mask_b, positions, 2]: (first, last) position of each position's document
     kv_order: torch.Tensor    # int32 [mask_b * QT, 4]: rows, most tiles first (row, full, partial, first tile)
     q_order: torch.Tensor     # int32 [mask_b * KT, 4]: columns, most tiles first (same layout)
 
@@ -105,8 +190,10 @@ def _stream() -> int:
 
 
 def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] = None,
-              sinks: int = 0, device="cuda", prefix: int = 0) -> MaskSpec:
-    """Device mask spec from host values (numpy / torch / int)."""
+              sinks: int = 0, device="cuda", prefix: int = 0, q_len: int = 0, q_offset: int = 0,
+              composed: Optional[MaskTerm] = None) -> MaskSpec:
+    """Device mask spec from host values (numpy / torch / int).  T is KV_LEN;
+    doc_ids has one id per absolute position (max(T, q_offset + Q_LEN))."""
     d = None
     if doc_ids is not None:
         d = torch.as_tensor(np.asarray(doc_ids), dtype=torch.int32)
@@ -116,14 +203,20 @@ def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] =
     w = None
     if window is not None:
         w = torch.tensor([int(window)], dtype=torch.int32, device=device)
-    return MaskSpec(int(T), bool(causal), d, w, int(sinks), int(prefix))
+    if composed is not None and not isinstance(composed, MaskTerm):
+        composed = MaskTerm(composed)
+    return MaskSpec(int(T), bool(causal), d, w, int(sinks), int(prefix), int(q_len), int(q_offset), composed)
 
 
 def from_spec_data(spec_data, device="cuda") -> MaskSpec:
     """Device mask spec from a workloads.MaskSpecData."""
+    table = getattr(spec_data, "table", None)
+    q_len = getattr(spec_data, "q_len", None)
     return mask_spec(spec_data.T, spec_data.causal,
                      spec_data.doc_ids if spec_data.document else None,
-                     spec_data.window, spec_data.sinks, device, getattr(spec_data, "prefix", 0))
+                     spec_data.window, spec_data.sinks, device, getattr(spec_data, "prefix", 0),
+                     q_len=int(q_len) if q_len else 0, q_offset=int(getattr(spec_data, "q_offset", 0)),
+                     composed=MaskTerm(table) if table is not None else None)
 
 
 def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda") -> ScoreMod:
@@ -133,16 +226,27 @@ def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda")
     return ScoreMod(s, softcap)
 
 
-def empty_block_mask(T: int, mask_b: int, device="cuda") -> BlockMask:
-    nt = T // TILE
+def empty_block_mask(spec, mask_b: Optional[int] = None, device="cuda") -> BlockMask:
+    """Uninitialised block-mask arrays for a MaskSpec (or for a square mask
+    of length T = spec and mask_b batch rows)."""
+    if isinstance(spec, MaskSpec):
+        Q, T, npos = spec.Q, spec.T, spec.positions
+        mask_b = spec.mask_b if mask_b is None else mask_b
+    else:
+        Q = T = npos = int(spec)
+        mask_b = 1 if mask_b is None else mask_b
+    qt, kt = -(-Q // TILE), -(-T // TILE)
     mk = lambda *s: torch.empty(s, dtype=torch.int32, device=device)
-    return BlockMask(mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
-                     mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt), mk(mask_b, 1, nt), mk(mask_b, 1, nt, nt),
-                     mk(mask_b, T, 2), mk(mask_b * nt, 4), mk(mask_b * nt, 4))
+    return BlockMask(mk(mask_b, 1, qt), mk(mask_b, 1, qt, kt), mk(mask_b, 1, qt), mk(mask_b, 1, qt, kt),
+                     mk(mask_b, 1, kt), mk(mask_b, 1, kt, qt), mk(mask_b, 1, kt), mk(mask_b, 1, kt, qt),
+                     mk(mask_b, npos, 2), mk(mask_b * qt, 4), mk(mask_b * kt, 4))
 
 
 def block_mask_workspace(spec: MaskSpec) -> torch.Tensor:
-    n = lib.bsm_block_mask_workspace_bytes(spec.T, spec.mask_b)
+    cs = spec.c_struct()
+    n = lib.bsm_block_mask_workspace_bytes(ctypes.byref(cs))
+    if n == 0:
+        check(lib.bsm_build_block_mask(ctypes.byref(cs), None, None, 0, None))  # raises with the reason
     return torch.empty(max(n, 256), dtype=torch.uint8, device=spec.doc_ids.device
                        if spec.doc_ids is not None else "cuda")
 
@@ -151,7 +255,7 @@ def build_block_mask(spec: MaskSpec, out: Optional[BlockMask] = None,
                      workspace: Optional[torch.Tensor] = None) -> BlockMask:
     """Runs bsm_build_block_mask on the current stream."""
     if out is None:
-        out = empty_block_mask(spec.T, spec.mask_b)
+        out = empty_block_mask(spec)
     if workspace is None:
         workspace = block_mask_workspace(spec)
     cs = spec.c_struct()
@@ -175,16 +279,17 @@ def _tensor(t: torch.Tensor, name: str) -> BsmTensor:
 def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,
                        mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
-    """Returns (out bf16 [B,H,T,D], lse float32 [B,H,T])."""
-    B, H, T, D = q.shape
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must have the same shape [B, H, T, D]")
+    """q [B, H, Q_LEN, D], k and v [B, H, KV_LEN, D].  Returns (out bf16
+    [B, H, Q_LEN, D], lse float32 [B, H, Q_LEN])."""
+    B, H, Q, D, T = _shapes(q, k, v, spec)
     if out is None:
         out = torch.empty_like(q)
+    if out.shape != q.shape:
+        raise ValueError(f"out {tuple(out.shape)} must have the shape of q {tuple(q.shape)}")
     if lse is None:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, T):
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+        lse = torch.empty((B, H, Q), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Q):
+        raise ValueError("lse must be a contiguous float32 [B, H, Q_LEN] tensor")
     _check_mod(mod, H)
     tq, tk, tv, to = _tensor(q, "q"), _tensor(k, "k"), _tensor(v, "v"), _tensor(out, "out")
     cb = block_mask.c_struct()
@@ -197,8 +302,23 @@ def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,
     return out, lse
 
 
-def bwd_workspace(B: int, H: int, T: int, D: int, device="cuda") -> torch.Tensor:
-    n = lib.bsm_bwd_workspace_bytes(B, H, T, D)
+def _shapes(q, k, v, spec: MaskSpec):
+    """(B, H, Q_LEN, D, KV_LEN) after checking q against Q_LEN and k, v
+    against KV_LEN."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, length, D]")
+    B, H, Q, D = q.shape
+    T = k.shape[2]
+    if k.shape != (B, H, T, D) or v.shape != k.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must be [B, H, KV_LEN, D] with B, H, D of q")
+    if T != spec.T or Q != spec.Q:
+        raise ValueError(f"q has {Q} queries and k {T} keys; the mask spec has Q_LEN {spec.Q}, KV_LEN {spec.T}")
+    return B, H, Q, D, T
+
+
+def bwd_workspace(B: int, H: int, Q: int, D: int, device="cuda") -> torch.Tensor:
+    """Workspace of the backward for Q = Q_LEN queries."""
+    n = lib.bsm_bwd_workspace_bytes(B, H, Q, D)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -206,21 +326,24 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
                        mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
                        dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
                        dslopes: Optional[torch.Tensor] = None):
-    """Returns (dq, dk, dv), bf16 [B,H,T,D].  With ALiBi, a float32 [H]
-    device tensor passed as dslopes receives dL/dslope (summed over the
-    batch)."""
-    B, H, T, D = q.shape
-    for name, x in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+    """Returns (dq bf16 [B, H, Q_LEN, D], dk and dv bf16 [B, H, KV_LEN, D]).
+    With ALiBi, a float32 [H] device tensor passed as dslopes receives
+    dL/dslope (summed over the batch)."""
+    B, H, Q, D, T = _shapes(q, k, v, spec)
+    for name, x in (("out", out), ("dout", dout)):
         if x.shape != q.shape:
             raise ValueError(f"{name} {tuple(x.shape)} must have the shape of q {tuple(q.shape)}")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, T):
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H, Q):
+        raise ValueError("lse must be a contiguous float32 [B, H, Q_LEN] tensor")
     _check_mod(mod, H)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, x, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if x.shape != ref.shape:
+            raise ValueError(f"{name} {tuple(x.shape)} must be {tuple(ref.shape)}")
     if workspace is None:
-        workspace = bwd_workspace(B, H, T, D, q.device)
+        workspace = bwd_workspace(B, H, Q, D, q.device)
     ts = [_tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"),
                                      (dq, "dq"), (dk, "dk"), (dv, "dv"))]
     cb = block_mask.c_struct()
@@ -345,7 +468,8 @@ def flex_attention_decode_static(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod
     return out, lse
 
 
-__all__ = ["MaskSpec", "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
+__all__ = ["MaskSpec", "MaskTerm", "CAUSAL", "SAME_DOC", "IN_WINDOW", "SINK", "PREFIX", "and_masks", "or_masks",
+           "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
            "flex_attention_decode", "decode_workspace", "flex_attention_decode_static",
            "bwd_workspace", "block_mask_workspace", "_lib"]

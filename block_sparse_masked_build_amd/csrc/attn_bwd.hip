@@ -77,7 +77,8 @@ struct DqArgs {
     const __bf16 *kb, *vb;
     int64_t k_st, v_st;
     const int32_t *fidx, *pidx, *doc;
-    int nfull, nt, qpos;
+    int nfull, nt, qpos;  // qpos: absolute position of this lane's query
+    int kv_len, npos;
     float scale, scale_log2, slope, cap, inv_cap;
     ModK mk;          // folded score-modification constants
     float l2, delta;  // this lane's query
@@ -114,9 +115,11 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto issue = [&](int t, int key0) {
         const uint32_t bf = t & 1;
-        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0);
-        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st);
-        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st);
+        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, a.npos - key0);
+        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st,
+                                               a.kv_len - key0);
+        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st,
+                                               a.kv_len - key0);
     };
     if (nsteps <= 0) return;
     int key0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt);
@@ -214,17 +217,19 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     int e, rem;
     ord.decode(k, e, rem);
     const WorkRec rec = load_rec(p.kv_order, e);
-    const int64_t row = min(max(rec.packed, 0), p.mask_b * nt - 1);
-    const int bm = (int)(row / nt), i = (int)(row - (int64_t)bm * nt);
+    const int64_t row = min(max(rec.packed, 0), p.mask_b * p.nqt - 1);
+    const int bm = (int)(row / p.nqt), i = (int)(row - (int64_t)bm * p.nqt);
     int b, h;
     head_of(p, rem, bm, b, h);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 31, hl = lane >> 5;
-    const int qpos = i * kTile + wv * 32 + n;
+    const int qidx = i * kTile + wv * 32 + n;      // query index (past Q_LEN on a cut-short row)
+    const int qrow = min(qidx, p.q_len - 1);       // the row this lane loads
+    const int qpos = p.q_off + qrow;               // its absolute position
 
     const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
     const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
-    const __bf16 *obr = static_cast<const __bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qpos * p.o_st;
+    const __bf16 *obr = static_cast<const __bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_st;
 
     DqArgs a;
     a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
@@ -235,16 +240,18 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     const int npart = min(max(rec.npart, 0), nt);
     a.fidx = p.full_kv_idx + row * nt;
     a.pidx = p.kv_idx + row * nt;
-    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.T : nullptr;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.npos : nullptr;
     a.nt = nt;
     a.qpos = qpos;
+    a.kv_len = p.T;
+    a.npos = p.npos;
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
     a.cap = SOFTCAP ? p.softcap : 1.0f;
     a.inv_cap = 1.0f / a.cap;
     a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
-    const int64_t row_bh = ((int64_t)b * p.H + h) * p.T + qpos;
+    const int64_t row_bh = ((int64_t)b * p.H + h) * p.q_len + qrow;
     const float lse = p.lse[row_bh];
     a.l2 = lse == -INFINITY ? 0.0f : lse * kLog2e;
     const int nsteps = 2 * (a.nfull + npart);
@@ -262,8 +269,8 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     u32x4 of[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qpos * p.q_st + st * 16 + hl * 8);
-        gf[st] = *reinterpret_cast<const bf16x8 *>(gb + (int64_t)qpos * p.do_st + st * 16 + hl * 8);
+        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qrow * p.q_st + st * 16 + hl * 8);
+        gf[st] = *reinterpret_cast<const bf16x8 *>(gb + (int64_t)qrow * p.do_st + st * 16 + hl * 8);
         of[st] = *reinterpret_cast<const u32x4 *>(obr + st * 16 + hl * 8);
     }
     // Delta = <dO, out> of this lane's query: each lane half holds half of
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
             for (int e = 0; e < 8; ++e)
                 acc += __builtin_bit_cast(float, u16_at(of[st], e) << 16) * static_cast<float>(gf[st][e]);
         a.delta = acc + __shfl_xor(acc, 32);
-        if (hl == 0) {
+        if (hl == 0 && qidx < p.q_len) {
             p.delta[row_bh] = a.delta;
             p.lse2[row_bh] = a.l2;
         }
@@ -300,22 +307,24 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
         dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
 
     // Slope gradient of the item: wave sums by a fixed butterfly, then the
-    // four waves in order, one partial per (batch, head, query tile).
+    // four waves in order, one partial per (batch, head, query tile); lanes
+    // past Q_LEN (a copy of the last query) do not count.
     if (SGRAD) {
+        if (qidx >= p.q_len) sg = 0.0f;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) sg += __shfl_xor(sg, o);
         if (lane == 0) sm.red[wv] = sg;
         __syncthreads();
         if (threadIdx.x == 0)
-            p.dslope_part[((int64_t)b * p.H + h) * nt + i] = ((sm.red[0] + sm.red[1]) + sm.red[2]) + sm.red[3];
+            p.dslope_part[((int64_t)b * p.H + h) * p.nqt + i] = ((sm.red[0] + sm.red[1]) + sm.red[2]) + sm.red[3];
     }
 
     // dQ rows of the wave, staged through the K buffers once every wave is
     // done with them (dS was accumulated without the scale).
     static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "dQ staging fits the K buffers");
     tile_barrier();
-    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)(qpos - n) * p.dq_st;
-    store_rows_staged<D>(dqp, p.dq_st, dq, p.scale, lds.k + (uint32_t)(wv * 32 * 2 * D));
+    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)(qidx - n) * p.dq_st;
+    store_rows_staged<D>(dqp, p.dq_st, dq, p.scale, lds.k + (uint32_t)(wv * 32 * 2 * D), p.q_len - (qidx - n));
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -332,33 +341,35 @@ struct ColMask {
 };
 
 __device__ inline bool make_col_mask(const AttnParams &p, int bm, int kpos, ColMask &cm) {
-    int ds = 0, de = p.T - 1;
+    // interval in absolute positions first, then in query indices
+    int ds = 0, de = p.npos - 1;
     bool gather = false;
     cm.dock = 0;
     if (p.mask_flags & BSM_MASK_DOCUMENT) {
-        const int32_t *dr = p.doc_range + ((int64_t)bm * p.T + kpos) * 2;
+        const int32_t *dr = p.doc_range + ((int64_t)bm * p.npos + kpos) * 2;
         ds = dr[0];
         de = dr[1];
         gather = ds < 0;  // whole row flagged: every lane agrees
         if (gather) {
             ds = 0;
-            de = p.T - 1;
-            cm.dock = p.doc_ids[(int64_t)bm * p.T + kpos];
+            de = p.npos - 1;
+            cm.dock = p.doc_ids[(int64_t)bm * p.npos + kpos];
         }
     }
     // causal: queries from the key on, except for prefix keys, which every
     // query sees
-    cm.lo = max(((p.mask_flags & BSM_MASK_CAUSAL) && kpos >= p.prefix) ? kpos : 0, ds);
+    const int lo = max(((p.mask_flags & BSM_MASK_CAUSAL) && kpos >= p.prefix) ? kpos : 0, ds);
     int hi = de;
     if (p.mask_flags & BSM_MASK_WINDOW) {
         const bool sink = (p.mask_flags & BSM_MASK_SINKS) && kpos < p.sinks;
         if (!sink) {
             int64_t whi = (int64_t)kpos + (int64_t)(*p.window) - 1;
-            whi = whi < -1 ? -1 : (whi > p.T - 1 ? p.T - 1 : whi);
+            whi = whi < -1 ? -1 : (whi > p.npos - 1 ? p.npos - 1 : whi);
             hi = min(hi, (int)whi);
         }
     }
-    cm.hi = hi;
+    cm.lo = max(lo - p.q_off, 0);
+    cm.hi = min(hi - p.q_off, p.q_len - 1);
     return gather;
 }
 
@@ -366,8 +377,9 @@ struct DkdvArgs {
     const __bf16 *qb, *gb;
     int64_t q_st, do_st;
     const float *l2, *delta;  // this (batch, head)
-    const int32_t *fidx, *pidx, *doc;
-    int nfull, nt, kpos;
+    const int32_t *fidx, *pidx, *doc;  // doc: document ids from query 0's position on
+    int nfull, nt, kpos;      // nt: query tiles; kpos: this lane's key (clamped to KV_LEN - 1)
+    int q_len, q_off;
     float scale, scale_log2, slope, cap, inv_cap;
     ModK mk;  // folded score-modification constants
 };
@@ -427,9 +439,10 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
     int lo_t = cm.hi >= cm.lo ? cm.lo - qbase : 1 << 30;  // empty interval: no offset matches
     const int span = cm.hi >= cm.lo ? cm.hi - cm.lo : 0;
     // ALiBi term of the score at query offset c: -slope_f (q - kpos) =
-    // c ns + n with ns = -slope_f and n = ns (qbase - kpos).
+    // c ns + n with ns = -slope_f and n = ns (qbase + q_off - kpos), the
+    // query's absolute position being q_off + its index.
     float ns = -a.mk.slope_f;
-    float n = ALIBI ? ns * (float)(qbase - a.kpos) : 0.0f;
+    float n = ALIBI ? ns * (float)(qbase + a.q_off - a.kpos) : 0.0f;
     asm volatile("" : "+v"(lo_t), "+v"(n), "+v"(ns));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -531,12 +544,14 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf1
                kTile;
     };
     auto issue = [&](int t, int q0) {
+        // rows past Q_LEN repeat the last query's
         const uint32_t bf = t & 1;
-        issue_ints_to_lds_at<kTile>(lds.l2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0));
-        issue_ints_to_lds_at<kTile>(lds.delta + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0));
-        if (GATHER) issue_ints_to_lds_at<kTile>(lds.doc + bf * kWB, a.doc + q0);
-        issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.q + bf * kTB, a.qb + (int64_t)q0 * a.q_st, a.q_st);
-        issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.g + bf * kTB, a.gb + (int64_t)q0 * a.do_st, a.do_st);
+        const int nq = a.q_len - q0;
+        issue_ints_to_lds_at<kTile>(lds.l2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0), nq);
+        issue_ints_to_lds_at<kTile>(lds.delta + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0), nq);
+        if (GATHER) issue_ints_to_lds_at<kTile>(lds.doc + bf * kWB, a.doc + q0, nq);
+        issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.q + bf * kTB, a.qb + (int64_t)q0 * a.q_st, a.q_st, nq);
+        issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.g + bf * kTB, a.gb + (int64_t)q0 * a.do_st, a.do_st, nq);
     };
     if (ntiles <= 0) return;
     int q0 = tile_q0(0);
@@ -577,7 +592,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     const int b = bh / p.H, h = bh % p.H;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int n = lane & 31, hl = lane >> 5;
-    const int kpos = j * kTile + wv * 32 + n;
+    const int kidx = j * kTile + wv * 32 + n;    // key (past KV_LEN on a cut-short tile)
+    const int kpos = min(kidx, p.T - 1);         // the key this lane loads
 
     const __bf16 *kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
     const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
@@ -589,15 +605,17 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     a.gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
     a.q_st = p.q_st;
     a.do_st = p.do_st;
-    a.l2 = p.lse2 + ((int64_t)b * p.H + h) * p.T;
-    a.delta = p.delta + ((int64_t)b * p.H + h) * p.T;
-    a.nfull = min(max(load_uniform(p.full_q_num + col), 0), nt);
-    const int npart = min(max(load_uniform(p.q_num + col), 0), nt);
-    a.fidx = p.full_q_idx + col * nt;
-    a.pidx = p.q_idx + col * nt;
-    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.T : nullptr;
-    a.nt = nt;
+    a.l2 = p.lse2 + ((int64_t)b * p.H + h) * p.q_len;
+    a.delta = p.delta + ((int64_t)b * p.H + h) * p.q_len;
+    a.nfull = min(max(load_uniform(p.full_q_num + col), 0), p.nqt);
+    const int npart = min(max(load_uniform(p.q_num + col), 0), p.nqt);
+    a.fidx = p.full_q_idx + col * p.nqt;
+    a.pidx = p.q_idx + col * p.nqt;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.npos + p.q_off : nullptr;
+    a.nt = p.nqt;
     a.kpos = kpos;
+    a.q_len = p.q_len;
+    a.q_off = p.q_off;
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
@@ -647,10 +665,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     static_assert(sizeof(sm.g) >= (kThreads / 64) * 32 * 2 * D, "dV staging fits the gradient buffers");
     tile_barrier();
     const uint32_t slice = (uint32_t)(wv * 32 * 2 * D);
-    __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)(kpos - n) * p.dk_st;
-    __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)(kpos - n) * p.dv_st;
-    store_rows_staged<D>(dkp, p.dk_st, dk, p.scale, lds.q + slice);
-    store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice);
+    const int k0w = kidx - n;  // the wave's first key
+    __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)k0w * p.dk_st;
+    __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)k0w * p.dv_st;
+    store_rows_staged<D>(dkp, p.dk_st, dk, p.scale, lds.q + slice, p.T - k0w);
+    store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice, p.T - k0w);
 }
 
 // dL/dslope[h]: the per-(batch, head, query tile) partials of dq_kernel
@@ -689,7 +708,7 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
     if (ALIBI && p.dslopes) {
         hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI>), dq_grid, block, 0, stream, q);
         hipLaunchKernelGGL(slope_reduce_kernel, dim3(p.H), block, 0, stream, p.dslope_part, p.dslopes, p.B, p.H,
-                           p.nt);
+                           p.nqt);
     } else {
         hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false>), dq_grid, block, 0, stream, q);
     }

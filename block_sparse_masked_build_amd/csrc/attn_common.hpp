@@ -216,50 +216,64 @@ __device__ inline void copy4_to_lds(const void *g, uint32_t lds_base) {
 // uniform parts of copy addresses are computed by the scalar unit.
 __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// nvalid: rows g_row0 .. g_row0 + nvalid - 1 exist (wave-uniform; it may be
+// <= 0 for a tile half wholly past the end, as long as row g_row0 + nvalid -
+// 1 lies inside the tensor).  A lane whose row lies past them copies that
+// last row instead, so a cut-short tile is read inside the tensor -- its
+// extra rows are masked by the caller.  Every copy takes the same form: a
+// wave-uniform base (the instruction's first source row, clamped) plus a
+// per-lane offset below kRowsPerInstr rows, so a whole tile costs no branch.
 template <int D, int SWZ, int ROWS>
-__device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_row0, int64_t row_stride) {
+__device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_row0, int64_t row_stride,
+                                            int nvalid = ROWS) {
     using L = TileLayout<D>;
     constexpr int kRowsPerInstr = 1024 / L::kRowBytes;
     constexpr int kInstr = ROWS / kRowsPerInstr / 4;
     static_assert(kInstr >= 1, "at least one copy per wave");
     const int wv = wave_id(), lane = threadIdx.x & 63;
+    const int last = __builtin_amdgcn_readfirstlane((nvalid < ROWS ? nvalid : ROWS) - 1);
     const int64_t row_bytes = row_stride * 2;
-    // The wave's base goes to scalar registers once; the instructions'
-    // bases below it are scalar adds.
-    const uint64_t wbase = uniform_u64((uint64_t)(uintptr_t)(reinterpret_cast<const char *>(g_row0) +
-                                                             (int64_t)(wv * kInstr * kRowsPerInstr) * row_bytes));
+    const uint64_t gbase = uniform_u64((uint64_t)(uintptr_t)g_row0);
     const int q = lane / L::kChunks;  // row inside the instruction's block
 #pragma unroll
     for (int x = 0; x < kInstr; ++x) {
         // (wv * kInstr + x) * kRowsPerInstr is a multiple of 16 plus a
         // function of x only, so the swizzle depends on (x, q) alone.
+        const int xrow0 = (wv * kInstr + x) * kRowsPerInstr;
+        const int xsrc0 = xrow0 < last ? xrow0 : last;  // scalar
+        const int row = xrow0 + q;
+        const int d = (row < last ? row : last) - xsrc0;  // 0 .. kRowsPerInstr - 1
         const int r16 = (x * kRowsPerInstr + q) & 15;
         const int c = (lane % L::kChunks) ^ tile_swizzle<D, SWZ>(r16);
-        const uint32_t voff = (uint32_t)(q * row_bytes) + (uint32_t)(c * 16);
-        const uint64_t xbase = wbase + (uint64_t)((int64_t)(x * kRowsPerInstr) * row_bytes);
-        copy16_to_lds_u(xbase, voff, lds_tile + (uint32_t)((wv * kInstr + x) * kRowsPerInstr * L::kRowBytes));
+        const uint32_t voff = (uint32_t)d * (uint32_t)row_bytes + (uint32_t)(c * 16);
+        const uint64_t xbase = gbase + (uint64_t)((int64_t)xsrc0 * row_bytes);
+        copy16_to_lds_u(xbase, voff, lds_tile + (uint32_t)(xrow0 * L::kRowBytes));
     }
 }
 
 template <int D, int SWZ, int ROWS>
-__device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride) {
-    issue_tile_to_lds_at<D, SWZ, ROWS>(lds_addr(lds_tile), g_row0, row_stride);
+__device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride,
+                                         int nvalid = ROWS) {
+    issue_tile_to_lds_at<D, SWZ, ROWS>(lds_addr(lds_tile), g_row0, row_stride, nvalid);
 }
 
-// N int32 values, N/4 per wave (wave w copies entries w N/4 .. (w+1) N/4 - 1).
+// N int32 values, N/4 per wave (wave w copies entries w N/4 .. (w+1) N/4 - 1);
+// entries at or past nvalid repeat entry nvalid - 1 (which exists).
 template <int N = kTile>
-__device__ inline void issue_ints_to_lds(int32_t *lds, const int32_t *g) {
+__device__ inline void issue_ints_to_lds(int32_t *lds, const int32_t *g, int nvalid = N) {
     constexpr int kPer = N / 4;
     const int wv = wave_id(), lane = threadIdx.x & 63;
-    if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds_addr(lds + wv * kPer));
+    const int e = wv * kPer + lane;
+    if (lane < kPer) copy4_to_lds(g + (e < nvalid ? e : nvalid - 1), lds_addr(lds + wv * kPer));
 }
 
 // Same with the LDS destination given as a byte address.
 template <int N>
-__device__ inline void issue_ints_to_lds_at(uint32_t lds, const int32_t *g) {
+__device__ inline void issue_ints_to_lds_at(uint32_t lds, const int32_t *g, int nvalid = N) {
     constexpr int kPer = N / 4;
     const int wv = wave_id(), lane = threadIdx.x & 63;
-    if (lane < kPer) copy4_to_lds(g + wv * kPer + lane, lds + 4 * wv * kPer);
+    const int e = wv * kPer + lane;
+    if (lane < kPer) copy4_to_lds(g + (e < nvalid ? e : nvalid - 1), lds + 4 * wv * kPer);
 }
 
 // Load of a T from an LDS byte address.
@@ -440,11 +454,13 @@ struct RowMask {
 // conflicts), then each store writes 16 bytes per lane and whole 2D-byte
 // rows, instead of 16-byte pieces of 32 rows.  The exchange stays inside the
 // wave, whose LDS accesses execute in order; the caller makes sure no other
-// wave uses the slice.  dst is row 0 of the block, ld its row stride.
+// wave uses the slice.  dst is row 0 of the block, ld its row stride; only
+// rows below nrows are stored (the block may run past the end of a length
+// that is not a multiple of 128).
 template <int D>
 __device__ __attribute__((always_inline)) inline void store_rows_staged(__bf16 *dst, int64_t ld,
                                                                         const f32x16 (&acc)[D / 32], float mul,
-                                                                        uint32_t stage) {
+                                                                        uint32_t stage, int nrows = 32) {
     constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kRowsPerRead = 64 / kChunks;
     const int lane = threadIdx.x & 63, n = lane & 31, hl = lane >> 5;
 #pragma unroll
@@ -461,7 +477,7 @@ __device__ __attribute__((always_inline)) inline void store_rows_staged(__bf16 *
     for (int i = 0; i < 32 / kRowsPerRead; ++i) {
         const int r = i * kRowsPerRead + lane / kChunks, c = lane % kChunks;
         const u32x4 v = lds_load<u32x4>(stage + r * kRowBytes + ((c ^ (r % kChunks)) * 16));
-        *reinterpret_cast<u32x4 *>(dst + (int64_t)r * ld + c * 8) = v;
+        if (r < nrows) *reinterpret_cast<u32x4 *>(dst + (int64_t)r * ld + c * 8) = v;
     }
 }
 
@@ -642,17 +658,17 @@ __device__ inline int make_row_mask(const AttnParams &p, int bm, int qpos, RowMa
     rm.docq = 0;
     bool gather = false;
     if (doc_on) {
-        const int32_t *dr = p.doc_range + ((int64_t)bm * p.T + qpos) * 2;
+        const int32_t *dr = p.doc_range + ((int64_t)bm * p.npos + qpos) * 2;
         ds = dr[0];
         de = dr[1];
         gather = ds < 0;  // the whole row is marked, so every lane agrees
         if (gather) {
             ds = 0;
             de = p.T - 1;
-            rm.docq = p.doc_ids[(int64_t)bm * p.T + qpos];
+            rm.docq = p.doc_ids[(int64_t)bm * p.npos + qpos];
         }
     }
-    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? max(qpos, p.prefix - 1) : p.T - 1, de);
+    const int hi = min(min((p.mask_flags & BSM_MASK_CAUSAL) ? max(qpos, p.prefix - 1) : p.T - 1, de), p.T - 1);
     int lo = ds;
     bool sinks = false;
     if (p.mask_flags & BSM_MASK_WINDOW) {
@@ -722,12 +738,12 @@ __device__ inline int div_by(int k, int d, uint32_t m) {
 }
 
 struct ItemOrder {
-    int nitems;  // B * H * QT, within int32 (checked on the host)
+    int nitems;  // mask rows x head indices, within int32 (checked on the host)
     int Q, queue, cl;
     const AttnParams &p;
 
     __device__ ItemOrder(const AttnParams &p_, int G) : p(p_) {
-        nitems = p.mask_b * p.nt * p.ord_r;
+        nitems = p.mask_b * p.nqt * p.ord_r;
         Q = G < kQueues ? G : kQueues;
         queue = blockIdx.x % Q;
         cl = p.ord_chunk_log2;
@@ -771,11 +787,11 @@ inline uint32_t div_magic(int64_t d) {
 // batch otherwise), chunks of up to 16 entries, at least four per queue.
 inline unsigned item_order(AttnParams &q) {
     q.ord_r = q.mask_b == 1 ? q.B * q.H : q.H;
-    const int64_t nitems = (int64_t)q.mask_b * q.nt * q.ord_r;
+    const int64_t nitems = (int64_t)q.mask_b * q.nqt * q.ord_r;
     int cl = 4;
     while (cl > 0 && ((int64_t)1 << cl) * 4 * kQueues > nitems) --cl;
     q.ord_chunk_log2 = cl;
-    const int nrows = q.mask_b * q.nt;
+    const int nrows = q.mask_b * q.nqt;
     q.ord_nblk = nrows >> cl;
     q.ord_p = nrows - (q.ord_nblk << cl);
     q.ord_m_cr = div_magic((int64_t)q.ord_r << cl);

@@ -53,7 +53,7 @@ struct DecodeParams {
     int32_t B, H, capacity, D, nslot, nt;
     const int32_t *kv_len;       // device: live length(s)
     int32_t kv_len_stride;       // 0: one value for the batch; 1: one per batch element
-    uint32_t mask_flags;
+    uint32_t mask_flags, table;  // table: truth table of a composed mask (BSM_MASK_TABLE)
     int32_t sinks, prefix;
     float scale, softcap;
     const int32_t *doc_ids;      // [mask_b, capacity] or NULL
@@ -79,6 +79,16 @@ __device__ inline int live_len(const DecodeParams &P, int b) {
 
 // The mask predicate for the query at p and key kv < live length.
 __device__ inline bool dec_visible(const DecodeParams &P, int bm, int p, int kv, int window, int docq) {
+    if (P.mask_flags & BSM_MASK_TABLE) {
+        // composed mask: look the five terms up in its truth table
+        const uint32_t f = P.mask_flags;
+        uint32_t idx = kv <= p ? 1u : 0u;
+        if ((f & BSM_MASK_DOCUMENT) && P.doc_ids[(int64_t)bm * P.capacity + kv] == docq) idx |= 2u;
+        if ((f & BSM_MASK_WINDOW) && (int64_t)p - kv < window) idx |= 4u;
+        if ((f & BSM_MASK_SINKS) && kv < P.sinks) idx |= 8u;
+        if ((f & BSM_MASK_PREFIX) && kv < P.prefix) idx |= 16u;
+        return (P.table >> idx) & 1u;
+    }
     if ((P.mask_flags & BSM_MASK_CAUSAL) && kv > p && !(kv < P.prefix)) return false;
     if ((P.mask_flags & BSM_MASK_DOCUMENT) && P.doc_ids[(int64_t)bm * P.capacity + kv] != docq) return false;
     if (P.mask_flags & BSM_MASK_WINDOW) {
@@ -135,8 +145,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         const int64_t c0 = (int64_t)slot_i * kSlotTiles * kTile;
         const int64_t c1 = min(c0 + kSlotTiles * kTile, (int64_t)L);  // keys [c0, c1)
         bool skip = c0 >= L;
-        // wholly before the window and holding no sink
-        if (!skip && (P.mask_flags & BSM_MASK_WINDOW))
+        // wholly before the window and holding no sink (the standard
+        // combination only: a composed mask may OR the window with more)
+        if (!skip && (P.mask_flags & BSM_MASK_WINDOW) && !(P.mask_flags & BSM_MASK_TABLE))
             skip = (int64_t)p - (c1 - 1) >= window && !((P.mask_flags & BSM_MASK_SINKS) && c0 < P.sinks);
         if (skip) {
             write_empty_slot<D>(P, slot);
@@ -324,6 +335,7 @@ hipError_t launch_attn_decode(const DecodeLaunch &d, float *part, hipStream_t st
     P.kv_len = d.kv_len;
     P.kv_len_stride = d.kv_len_stride;
     P.mask_flags = a.mask_flags;
+    P.table = a.table;
     P.sinks = a.sinks;
     P.prefix = a.prefix;
     P.scale = a.scale;

@@ -162,28 +162,31 @@ struct FwdArgs {
     const __bf16 *kb, *vb;
     const int32_t *doc, *fidx, *pidx;
     int b, h, bm, row;
-    int nfull, ntiles, nt, qpos, first;
+    int nfull, ntiles, nt, first;
+    int qidx;  // this lane's query index (may lie past Q_LEN on the last row)
+    int qpos;  // its absolute position (the last query's for lanes past Q_LEN)
     float scale, scale_log2, slope, cap, inv_cap;
     ModK mk;  // folded score-modification constants
 };
 
 template <bool ALIBI, bool SOFTCAP>
 __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &rec, FwdArgs &a) {
-    const int nt = p.nt;
-    const int packed = min(max(rec.packed, 0), p.mask_b * nt - 1);
-    a.bm = packed / nt;
-    a.row = packed - a.bm * nt;
+    const int nt = p.nt;  // key tiles
+    const int packed = min(max(rec.packed, 0), p.mask_b * p.nqt - 1);
+    a.bm = packed / p.nqt;
+    a.row = packed - a.bm * p.nqt;
     head_of(p, rem, a.bm, a.b, a.h);
     a.kb = static_cast<const __bf16 *>(p.k) + a.b * p.k_sb + a.h * p.k_sh;
     a.vb = static_cast<const __bf16 *>(p.v) + a.b * p.v_sb + a.h * p.v_sh;
     a.fidx = p.full_kv_idx + (int64_t)packed * nt;
     a.pidx = p.kv_idx + (int64_t)packed * nt;
-    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)a.bm * p.T : nullptr;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)a.bm * p.npos : nullptr;
     a.nfull = min(max(rec.nfull, 0), nt);
     a.ntiles = a.nfull + min(max(rec.npart, 0), nt);
     a.first = clamp_tile(rec.first, nt);
     a.nt = nt;
-    a.qpos = a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
+    a.qidx = a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
+    a.qpos = p.q_off + min(a.qidx, p.q_len - 1);
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[a.h] : 0.0f;
@@ -232,7 +235,8 @@ __device__ inline int finish_row_mask(const AttnParams &p, int qpos, const RowLo
         de = p.T - 1;
     }
     rm.docq = rl.docq;
-    const int hi = min((p.mask_flags & BSM_MASK_CAUSAL) ? max(qpos, p.prefix - 1) : p.T - 1, de);
+    // keys past KV_LEN are never visible (the last key tile may be cut short)
+    const int hi = min(min((p.mask_flags & BSM_MASK_CAUSAL) ? max(qpos, p.prefix - 1) : p.T - 1, de), p.T - 1);
     int lo = ds;
     bool sinks = false;
     if (p.mask_flags & BSM_MASK_WINDOW) {
@@ -264,17 +268,20 @@ template <int D>
 __device__ __attribute__((always_inline)) inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, bf16x8 (&qf)[D / 16],
                                   TileList &tl, RowLoad &rl) {
     if (a.ntiles > 0) {
+        // rows past KV_LEN (document ids: past the positions) repeat the last one
         const int k0 = a.first * kTile;
         if (a.doc) {
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0);
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k0 + kHalf);
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0, p.npos - k0);
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k0 + kHalf, p.npos - k0 - kHalf);
         }
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st);
-        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st);
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)(k0 + kHalf) * p.k_st, p.k_st);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st, p.T - k0);
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st, p.T - k0);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)(k0 + kHalf) * p.k_st, p.k_st,
+                                           p.T - k0 - kHalf);
     }
     const int hl = (threadIdx.x & 63) >> 5;
-    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + a.b * p.q_sb + a.h * p.q_sh + (int64_t)a.qpos * p.q_st;
+    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + a.b * p.q_sb + a.h * p.q_sh +
+                         (int64_t)min(a.qidx, p.q_len - 1) * p.q_st;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qrow + st * 16 + hl * 8);
     const int lane = threadIdx.x & 63;
@@ -284,7 +291,7 @@ __device__ __attribute__((always_inline)) inline void item_start(const AttnParam
     rl.de = p.T - 1;
     rl.docq = 0;
     if (a.doc) {
-        const int32_t *dr = p.doc_range + ((int64_t)a.bm * p.T + a.qpos) * 2;
+        const int32_t *dr = p.doc_range + ((int64_t)a.bm * p.npos + a.qpos) * 2;
         rl.ds = dr[0];
         rl.de = dr[1];
         rl.docq = a.doc[a.qpos];
@@ -301,11 +308,11 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
     const int hl = (threadIdx.x & 63) >> 5, wv = wave_id();
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.0f ? fast_rcp(l_tot) : 0.0f;
-    __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh +
-                 (int64_t)(a.row * kTile + wv * 32) * p.o_st;
-    store_rows_staged<D>(ob, p.o_st, o, inv, stage + (uint32_t)(wv * 32 * 2 * D));
-    if (hl == 0)
-        p.lse[((int64_t)a.b * p.H + a.h) * p.T + a.qpos] =
+    const int q0w = a.row * kTile + wv * 32;  // the wave's first query index
+    __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh + (int64_t)q0w * p.o_st;
+    store_rows_staged<D>(ob, p.o_st, o, inv, stage + (uint32_t)(wv * 32 * 2 * D), p.q_len - q0w);
+    if (hl == 0 && a.qidx < p.q_len)
+        p.lse[((int64_t)a.b * p.H + a.h) * p.q_len + a.qidx] =
             l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
@@ -352,11 +359,11 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     }
     auto step_key0 = [&](int t) { return tile_at(tl, a, t >> 1) * kTile + (t & 1) * kHalf; };
     auto issue_k = [&](int t, int key0) {
-        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0);
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st);
+        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, p.npos - key0);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st, p.T - key0);
     };
     auto issue_v = [&](int t, int key0) {
-        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[t & 1], a.vb + (int64_t)key0 * p.v_st, p.v_st);
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[t & 1], a.vb + (int64_t)key0 * p.v_st, p.v_st, p.T - key0);
     };
     // Row maximum of a step in the log2 domain (without score modifications
     // the scale is applied here and folded into the exponentials).

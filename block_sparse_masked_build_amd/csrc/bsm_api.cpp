@@ -29,34 +29,62 @@ bsm_status ok() {
 }
 
 constexpr int32_t kMaxT = 1 << 22;
-constexpr uint32_t kMaskFlagsAll =
-    BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS | BSM_MASK_PREFIX;
+constexpr uint32_t kMaskFlagsAll = BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS |
+                                   BSM_MASK_PREFIX | BSM_MASK_TABLE;
 
-// The widened causal bound kv < prefix the kernels use: 0 when the term is
-// off (no PREFIX, or no causal term for it to widen), at most T.
+// The prefix bound kv < prefix the kernels use, at most KV_LEN: with the
+// standard combination the widened causal bound (0 when the term is off: no
+// PREFIX, or no causal term for it to widen); with a truth table the prefix
+// term's own bound (0 without PREFIX).
 int32_t effective_prefix(const bsm_mask_spec *spec) {
-    if (!(spec->flags & BSM_MASK_CAUSAL) || !(spec->flags & BSM_MASK_PREFIX)) return 0;
+    const bool table = spec->flags & BSM_MASK_TABLE;
+    if (!(spec->flags & BSM_MASK_PREFIX) || (!table && !(spec->flags & BSM_MASK_CAUSAL))) return 0;
     return spec->prefix_len < spec->seq_len ? spec->prefix_len : spec->seq_len;
+}
+
+// Shape of a mask: keys, queries, query offset, document positions, tiles.
+struct MaskDims {
+    int32_t kv_len, q_len, q_off, npos, nqt, nkt;
+};
+
+MaskDims mask_dims(const bsm_mask_spec *spec) {
+    MaskDims m;
+    m.kv_len = spec->seq_len;
+    m.q_len = spec->q_len > 0 ? spec->q_len : spec->seq_len;
+    m.q_off = spec->q_offset;
+    m.npos = m.kv_len > m.q_off + m.q_len ? m.kv_len : m.q_off + m.q_len;
+    m.nqt = (m.q_len + bsm::kTile - 1) / bsm::kTile;
+    m.nkt = (m.kv_len + bsm::kTile - 1) / bsm::kTile;
+    return m;
 }
 constexpr uint32_t kModFlagsAll = BSM_MOD_ALIBI | BSM_MOD_SOFTCAP;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-bool bad_T(int64_t T) { return T <= 0 || T % bsm::kTile != 0 || T > kMaxT; }
+bool bad_len(int64_t T) { return T <= 0 || T > kMaxT; }
 
-int32_t n_chunks(int32_t T) { return (T + 255) / 256; }
+int32_t n_chunks(int32_t n) { return (n + 255) / 256; }
 
-// Blocks of the work orders (kOrderBlock rows of one mask batch each).
-int64_t order_blocks(int32_t T, int32_t mask_b) {
-    return (int64_t)mask_b * ((T / bsm::kTile + bsm::kOrderBlock - 1) / bsm::kOrderBlock);
+// Blocks of a work order (kOrderBlock rows of one mask batch each) over
+// `tiles` rows per mask batch.
+int64_t order_blocks(int32_t tiles, int32_t mask_b) {
+    return (int64_t)mask_b * ((tiles + bsm::kOrderBlock - 1) / bsm::kOrderBlock);
+}
+
+int64_t order_ws_ints(const MaskDims &m, int32_t mask_b) {
+    const int64_t r = order_blocks(m.nqt, mask_b), c = order_blocks(m.nkt, mask_b);
+    return r > c ? r : c;
 }
 
 bsm_status check_spec(const bsm_mask_spec *spec) {
     if (!spec) return fail(BSM_E_INVALID, "mask spec is NULL");
     if (spec->flags & ~kMaskFlagsAll) return fail(BSM_E_INVALID, "unknown mask flag bits 0x%x", spec->flags);
-    if (bad_T(spec->seq_len))
-        return fail(BSM_E_INVALID, "seq_len %d must be a positive multiple of 128 and <= %d",
-                    spec->seq_len, kMaxT);
+    if (bad_len(spec->seq_len))
+        return fail(BSM_E_INVALID, "seq_len %d must be in [1, %d]", spec->seq_len, kMaxT);
+    if (spec->q_len < 0 || spec->q_len > kMaxT)
+        return fail(BSM_E_INVALID, "q_len %d must be in [0, %d] (0: seq_len)", spec->q_len, kMaxT);
+    if (spec->q_offset < 0 || (int64_t)spec->q_offset + (spec->q_len ? spec->q_len : spec->seq_len) > kMaxT)
+        return fail(BSM_E_INVALID, "q_offset %d must be >= 0 with q_offset + Q_LEN <= %d", spec->q_offset, kMaxT);
     if (spec->mask_b < 1) return fail(BSM_E_INVALID, "mask_b %d must be >= 1", spec->mask_b);
     if ((spec->flags & BSM_MASK_DOCUMENT) && !spec->doc_ids)
         return fail(BSM_E_INVALID, "DOCUMENT mask without doc_ids");
@@ -111,14 +139,17 @@ bsm_status check_mod(const bsm_score_mod *mod) {
 bsm_status check_attn_common(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_mask_spec *spec,
                              const bsm_score_mod *mod) {
     if (B < 1 || H < 1) return fail(BSM_E_INVALID, "B=%d and H=%d must be >= 1", B, H);
-    if (bad_T(T)) return fail(BSM_E_INVALID, "T %d must be a positive multiple of 128 and <= %d", T, kMaxT);
+    if (bad_len(T)) return fail(BSM_E_INVALID, "T %d must be in [1, %d]", T, kMaxT);
     if (D != 64 && D != 128) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64 and 128 are built", D);
     bsm_status st = check_spec(spec);
     if (st != BSM_OK) return st;
     if (spec->seq_len != T) return fail(BSM_E_INVALID, "mask seq_len %d != T %d", spec->seq_len, T);
     if (spec->mask_b != 1 && spec->mask_b != B)
         return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
-    if ((int64_t)B * H * (T / bsm::kTile) > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
+    if (spec->flags & BSM_MASK_TABLE)
+        return fail(BSM_E_UNSUPPORTED, "composed (TABLE) masks: block masks and decoding only");
+    const MaskDims m = mask_dims(spec);
+    if ((int64_t)B * H * (m.nqt > m.nkt ? m.nqt : m.nkt) > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
     return check_mod(mod);
 }
 
@@ -133,10 +164,16 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
                  const bsm_block_mask *bm, const bsm_mask_spec *spec, const bsm_score_mod *mod,
                  float scale) {
     p = bsm::AttnParams{};
+    const MaskDims m = mask_dims(spec);
     p.B = B;
     p.H = H;
     p.T = T;
-    p.nt = T / bsm::kTile;
+    p.nt = m.nkt;
+    p.q_len = m.q_len;
+    p.nqt = m.nqt;
+    p.q_off = m.q_off;
+    p.npos = m.npos;
+    p.table = spec->table;
     p.mask_b = spec->mask_b;
     p.mask_flags = spec->flags;
     p.sinks = spec->num_sinks;
@@ -184,9 +221,13 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     if (!spec) return fail(BSM_E_INVALID, "mask spec is NULL");
     if (spec->seq_len != capacity)
         return fail(BSM_E_INVALID, "mask seq_len %d != cache capacity %d", spec->seq_len, capacity);
+    if ((spec->q_len != 0 && spec->q_len != capacity) || spec->q_offset != 0)
+        return fail(BSM_E_INVALID, "a decoding step's mask is square over the cache (q_len 0, q_offset 0)");
     if (bm) {  // a block mask is built for the whole capacity, square
         bsm_status st = check_spec(spec);
         if (st != BSM_OK) return st;
+        if (capacity % bsm::kTile != 0)
+            return fail(BSM_E_INVALID, "with a block mask the capacity %d must be a multiple of 128", capacity);
         if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
             return fail(BSM_E_INVALID, "block mask row arrays must be non-NULL");
     } else {
@@ -221,12 +262,14 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     p.H = H;
     p.T = capacity;
     p.nt = (capacity + bsm::kTile - 1) / bsm::kTile;
+    p.q_len = capacity;
+    p.nqt = p.nt;
+    p.npos = capacity;
+    p.table = spec->table;
     p.mask_b = spec->mask_b;
     p.mask_flags = spec->flags;
     p.sinks = spec->num_sinks;
-    p.prefix = (spec->flags & BSM_MASK_CAUSAL) && (spec->flags & BSM_MASK_PREFIX)
-                   ? (spec->prefix_len < capacity ? spec->prefix_len : capacity)
-                   : 0;
+    p.prefix = effective_prefix(spec);
     p.doc_ids = spec->doc_ids;
     p.window = spec->window;
     p.mod_flags = mod ? mod->flags : 0u;
@@ -297,11 +340,12 @@ bsm_status scratch_address(void *stream, void **out) {
 
 extern "C" {
 
-size_t bsm_block_mask_workspace_bytes(int32_t seq_len, int32_t mask_b) {
-    if (bad_T(seq_len) || mask_b < 1) return 0;
-    const int64_t nt = seq_len / bsm::kTile;
-    return align256((size_t)mask_b * n_chunks(seq_len) * sizeof(int32_t)) +
-           align256((size_t)mask_b * nt * nt) + 2 * align256((size_t)order_blocks(seq_len, mask_b) * sizeof(int32_t));
+size_t bsm_block_mask_workspace_bytes(const bsm_mask_spec *spec) {
+    if (check_spec(spec) != BSM_OK) return 0;
+    const MaskDims m = mask_dims(spec);
+    return align256((size_t)spec->mask_b * n_chunks(m.npos) * sizeof(int32_t)) +
+           align256((size_t)spec->mask_b * m.nqt * m.nkt) +
+           2 * align256((size_t)order_ws_ints(m, spec->mask_b) * sizeof(int32_t));
 }
 
 bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask *out,
@@ -310,9 +354,11 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     if (st != BSM_OK) return st;
     st = check_block_mask(out, true, spec);
     if (st != BSM_OK) return st;
-    if ((int64_t)spec->mask_b * (spec->seq_len / bsm::kTile) > INT32_MAX)
-        return fail(BSM_E_INVALID, "mask_b * T/128 exceeds the int32 work-order range");
-    const size_t need = bsm_block_mask_workspace_bytes(spec->seq_len, spec->mask_b);
+    const MaskDims m = mask_dims(spec);
+    if ((int64_t)spec->mask_b * (m.nqt > m.nkt ? m.nqt : m.nkt) > INT32_MAX ||
+        (int64_t)spec->mask_b * m.npos > INT32_MAX)
+        return fail(BSM_E_INVALID, "mask_b x tiles exceeds the int32 work-order range");
+    const size_t need = bsm_block_mask_workspace_bytes(spec);
     if (!workspace || workspace_bytes < need)
         return fail(BSM_E_WORKSPACE, "block-mask workspace needs %zu bytes, got %zu%s", need,
                     workspace_bytes, workspace ? "" : " (NULL)");
@@ -320,12 +366,17 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
         return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
     bsm::MaskBuildParams p{};
     p.flags = spec->flags;
-    p.T = spec->seq_len;
-    p.nt = spec->seq_len / bsm::kTile;
+    p.T = m.kv_len;
+    p.q_len = m.q_len;
+    p.q_off = m.q_off;
+    p.npos = m.npos;
+    p.nqt = m.nqt;
+    p.nkt = m.nkt;
     p.mask_b = spec->mask_b;
-    p.nchunks = n_chunks(spec->seq_len);
+    p.nchunks = n_chunks(m.npos);
     p.sinks = spec->num_sinks;
     p.prefix = effective_prefix(spec);
+    p.table = spec->table;
     p.doc_ids = spec->doc_ids;
     p.window = spec->window;
     p.out = *out;
@@ -333,10 +384,9 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     p.nonmono = reinterpret_cast<int32_t *>(ws);
     const size_t off_cls = align256((size_t)p.mask_b * p.nchunks * sizeof(int32_t));
     p.cls = reinterpret_cast<uint8_t *>(ws + off_cls);
-    const size_t off_order = off_cls + align256((size_t)p.mask_b * p.nt * p.nt);
+    const size_t off_order = off_cls + align256((size_t)p.mask_b * p.nqt * p.nkt);
     p.order_ws = reinterpret_cast<int32_t *>(ws + off_order);
-    p.order_ws_stride =
-        (int32_t)(align256((size_t)order_blocks(spec->seq_len, spec->mask_b) * sizeof(int32_t)) / sizeof(int32_t));
+    p.order_ws_stride = (int32_t)(align256((size_t)order_ws_ints(m, spec->mask_b) * sizeof(int32_t)) / sizeof(int32_t));
     return hip_status(bsm::launch_build_block_mask(p, static_cast<hipStream_t>(stream)),
                       "bsm_build_block_mask launch");
 }
@@ -367,9 +417,10 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                       "bsm_flex_attention_fwd launch");
 }
 
-size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D) {
-    if (B < 1 || H < 1 || bad_T(T) || (D != 64 && D != 128)) return 0;
-    return 2 * align256((size_t)B * H * T * sizeof(float)) + align256((size_t)B * H * (T / 128) * sizeof(float));
+size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D) {
+    if (B < 1 || H < 1 || bad_len(Q) || (D != 64 && D != 128)) return 0;
+    return 2 * align256((size_t)B * H * Q * sizeof(float)) +
+           align256((size_t)B * H * ((Q + bsm::kTile - 1) / bsm::kTile) * sizeof(float));
 }
 
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_tensor *q,
@@ -391,7 +442,8 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     if ((st = check_tensor(dv, "dv")) != BSM_OK) return st;
     if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
     if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
-    const size_t need = bsm_bwd_workspace_bytes(B, H, T, D);
+    const int32_t Q = mask_dims(spec).q_len;
+    const size_t need = bsm_bwd_workspace_bytes(B, H, Q, D);
     if (!workspace || workspace_bytes < need)
         return fail(BSM_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu%s", need,
                     workspace_bytes, workspace ? "" : " (NULL)");
@@ -414,9 +466,9 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     p.dv = const_cast<void *>(ptr);
     p.lse = const_cast<float *>(lse);
     p.delta = static_cast<float *>(workspace);
-    p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)B * H * T * sizeof(float)));
+    p.lse2 = reinterpret_cast<float *>(static_cast<char *>(workspace) + align256((size_t)B * H * Q * sizeof(float)));
     p.dslope_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                              2 * align256((size_t)B * H * T * sizeof(float)));
+                                              2 * align256((size_t)B * H * Q * sizeof(float)));
     p.dslopes = (mod && (mod->flags & BSM_MOD_ALIBI)) ? mod->alibi_slopes_grad : nullptr;
     return hip_status(bsm::launch_attn_bwd(p, D, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_bwd launch");

@@ -22,23 +22,35 @@ enum : uint8_t { kEmpty = 0, kPartial = 1, kFull = 2 };
 
 struct MaskBuildParams {
     uint32_t flags;
-    int32_t T;
-    int32_t nt;          // tiles per side
+    int32_t T;           // KV_LEN: keys
+    int32_t q_len;       // Q_LEN: queries
+    int32_t q_off;       // absolute position of query 0
+    int32_t npos;        // positions of the document ids: max(T, q_off + q_len)
+    int32_t nqt, nkt;    // query tiles, key tiles
     int32_t mask_b;
-    int32_t nchunks;     // 256-position chunks of the monotonicity check
+    int32_t nchunks;     // 256-position chunks of the monotonicity check (over npos)
     int32_t sinks;
-    int32_t prefix;      // causal term widened to kv < prefix (0: plain causal or no causal term)
+    int32_t prefix;      // standard combination: causal term widened to kv < prefix (0: none);
+                         // TABLE: the prefix term's length (0: term off)
+    uint32_t table;      // TABLE: truth table over the five terms
     const int32_t *doc_ids;
     const int32_t *window;
     bsm_block_mask out;
-    uint8_t *cls;        // [mask_b, nt, nt]
+    uint8_t *cls;        // [mask_b, nqt, nkt]
     int32_t *nonmono;    // [mask_b, nchunks]
     int32_t *order_ws;   // two arrays of order_ws_stride ints: sorted blocks of the row / column orders
     int32_t order_ws_stride;
 };
 
 struct AttnParams {
-    int32_t B, H, T, nt;
+    int32_t B, H;
+    int32_t T;           // KV_LEN: keys
+    int32_t nt;          // key tiles, ceil(T / 128)
+    int32_t q_len;       // Q_LEN: queries
+    int32_t nqt;         // query tiles, ceil(q_len / 128)
+    int32_t q_off;       // absolute position of query 0
+    int32_t npos;        // positions of the document ids / ranges: max(T, q_off + q_len)
+    uint32_t table;      // TABLE masks: truth table over the five terms
     int32_t mask_b;
     uint32_t mask_flags;
     uint32_t mod_flags;
@@ -52,8 +64,8 @@ struct AttnParams {
     // block mask
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
     const int32_t *q_num, *q_idx, *full_q_num, *full_q_idx;
-    const int32_t *doc_range;   // [mask_b, T, 2] (first, last) of each position's document, or NULL
-    const int32_t *kv_order, *q_order;  // work orders [mask_b * nt, 4]: longest rows / columns first
+    const int32_t *doc_range;   // [mask_b, npos, 2] (first, last) of each position's document, or NULL
+    const int32_t *kv_order, *q_order;  // work orders [mask_b * nqt, 4] / [mask_b * nt, 4]: longest first
     // tensors (bf16, strides in elements)
     const void *q; int64_t q_sb, q_sh, q_st;
     const void *k; int64_t k_sb, k_sh, k_st;
@@ -63,10 +75,10 @@ struct AttnParams {
     void *dq; int64_t dq_sb, dq_sh, dq_st;
     void *dk; int64_t dk_sb, dk_sh, dk_st;
     void *dv; int64_t dv_sb, dv_sh, dv_st;
-    float *lse;      // [B, H, T]
-    float *delta;    // [B, H, T] (backward workspace): <dO, out> per query
-    float *lse2;     // [B, H, T] (backward workspace): lse * log2(e), 0 where lse = -inf
-    float *dslope_part;  // [B, H, nt] (backward workspace): slope-gradient partial per query tile
+    float *lse;      // [B, H, q_len]
+    float *delta;    // [B, H, q_len] (backward workspace): <dO, out> per query
+    float *lse2;     // [B, H, q_len] (backward workspace): lse * log2(e), 0 where lse = -inf
+    float *dslope_part;  // [B, H, nqt] (backward workspace): slope-gradient partial per query tile
     float *dslopes;      // [H] backward output dL/dslope, or NULL (not computed)
     // forward item order: items per work-order entry, full blocks, entries in
     // the last block, and division magic numbers (set by the launcher)

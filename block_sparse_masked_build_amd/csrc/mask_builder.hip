@@ -33,6 +33,14 @@
 //    the four waves' row quarters and compact the partial and full lists in
 //    ascending order.  A per-tile class byte is kept in the workspace and a
 //    second kernel compacts it per key-tile column.
+//  * Queries and keys may differ in number (query i at absolute position
+//    q_off + i) and need not fill whole tiles: queries past Q_LEN have no
+//    visible key, keys past KV_LEN are never visible, so a cut-short tile is
+//    never full.
+//  * A composed mask (truth table over the five terms, tutorial, Pattern 3:
+//    and_masks / or_masks) has no interval structure in general: each
+//    query-tile row evaluates every pair of every key tile
+//    (rows_table_kernel), exact by construction.
 #include "bsm_internal.hpp"
 
 namespace bsm {
@@ -95,11 +103,63 @@ __device__ inline int lds_search_doc(const int32_t *a, int lo, int hi, int32_t v
 __global__ __launch_bounds__(kThreads) void check_monotone_kernel(MaskBuildParams p) {
     const int b = blockIdx.y;
     const int t = blockIdx.x * kThreads + threadIdx.x;
-    const int32_t *doc = p.doc_ids + (int64_t)b * p.T;
+    const int32_t *doc = p.doc_ids + (int64_t)b * p.npos;
     int bad = 0;
-    if (t + 1 < p.T) bad = doc[t] > doc[t + 1];
+    if (t + 1 < p.npos) bad = doc[t] > doc[t + 1];
     bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) p.nonmono[(int64_t)b * p.nchunks + blockIdx.x] = bad;
+}
+
+// Whether batch row b's document ids are non-decreasing (every thread of
+// the workgroup gets the answer).
+__device__ inline bool row_monotone(const MaskBuildParams &p, int b) {
+    int bad = 0;
+    for (int c = threadIdx.x; c < p.nchunks; c += kThreads) bad |= p.nonmono[(int64_t)b * p.nchunks + c];
+    return !__syncthreads_or(bad);
+}
+
+// doc_range of every position of a 256-position chunk: the first and last
+// position of the position's document (documents are contiguous runs when
+// the ids are non-decreasing), or (-1, -1) for every position of a row whose
+// ids are not.  The document start of the chunk's first position and the end
+// of its last come from wave searches; every other document of the chunk
+// starts or ends inside it and is found in LDS.
+__global__ __launch_bounds__(kThreads) void ranges_kernel(MaskBuildParams p) {
+    __shared__ int32_t s_doc[kThreads];
+    __shared__ int s_ds0, s_deN;
+    const int b = blockIdx.y;
+    const int c0 = blockIdx.x * kThreads;
+    const int n = min(kThreads, p.npos - c0);  // positions in this chunk
+    const int t = c0 + (int)threadIdx.x;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int32_t *doc = p.doc_ids + (int64_t)b * p.npos;
+    int32_t *dr = p.out.doc_range + (int64_t)b * p.npos * 2;
+    const bool mono = row_monotone(p, b);
+    if (!mono) {
+        if (t < p.npos) {
+            dr[(int64_t)t * 2] = -1;
+            dr[(int64_t)t * 2 + 1] = -1;
+        }
+        return;
+    }
+    const int32_t d = t < p.npos ? doc[t] : 0;
+    if ((int)threadIdx.x < n) s_doc[threadIdx.x] = d;
+    __syncthreads();
+    if (wv == 0) {
+        const int v = wave_search_doc<false>(doc, 0, c0 + 1, s_doc[0]);
+        if (lane == 0) s_ds0 = v;
+    } else if (wv == 1) {
+        const int v = wave_search_doc<true>(doc, c0 + n - 1, p.npos, s_doc[n - 1]) - 1;
+        if (lane == 0) s_deN = v;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < n) {
+        const int r = threadIdx.x;
+        const int ds = d == s_doc[0] ? s_ds0 : c0 + lds_search_doc<false>(s_doc, 1, r, d);
+        const int de = d == s_doc[n - 1] ? s_deN : c0 + lds_search_doc<true>(s_doc, r + 1, n - 1, d) - 1;
+        dr[(int64_t)t * 2] = ds;
+        dr[(int64_t)t * 2 + 1] = de;
+    }
 }
 
 // Compacts one chunk of up to 256 class decisions (one per thread, in
@@ -151,75 +211,53 @@ constexpr int kRowsPerWave = kTile / kWaves;  // 32
 __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
     __shared__ i32x4 s_iv[kTile];
     __shared__ int32_t s_docq[kTile];
-    __shared__ int s_ds0, s_deN;
     __shared__ i32x4 s_ext[kTile / 64];
     __shared__ unsigned long long s_any[2][kWaves], s_all[2][kWaves];
 
     const int i = blockIdx.x;
     const int b = blockIdx.y;
     const int T = p.T;
-    const int nt = p.nt;
+    const int nt = p.nkt;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const bool causal = p.flags & BSM_MASK_CAUSAL;
     const bool document = p.flags & BSM_MASK_DOCUMENT;
     const bool windowed = p.flags & BSM_MASK_WINDOW;
     const bool sinks_on = windowed && (p.flags & BSM_MASK_SINKS) && p.sinks > 0;
-    const int32_t *doc = document ? p.doc_ids + (int64_t)b * T : nullptr;
+    const int32_t *doc = document ? p.doc_ids + (int64_t)b * p.npos : nullptr;
     const int64_t w = windowed ? (int64_t)(*p.window) : 0;
-    const int q0 = i * kTile;
 
-    int bad = 0;
-    int32_t dq = 0;
-    if (document) {
-        for (int c = threadIdx.x; c < p.nchunks; c += kThreads)
-            bad |= p.nonmono[(int64_t)b * p.nchunks + c];
-        if (threadIdx.x < kTile) {
-            dq = doc[q0 + threadIdx.x];
-            s_docq[threadIdx.x] = dq;
-        }
-        // Document of the tile's first and last query, searched before the
-        // monotonicity result is known (in bounds either way; unused if the
-        // ids are not monotone).
-        if (wv == 0) {
-            const int v = wave_search_doc<false>(doc, 0, q0 + 1, __shfl(dq, 0));
-            if (lane == 0) s_ds0 = v;
-        } else if (wv == 1) {
-            const int v = wave_search_doc<true>(doc, q0 + kTile - 1, T, __shfl(dq, 63)) - 1;
-            if (lane == 0) s_deN = v;
-        }
-    }
-    const bool mono = !__syncthreads_or(bad);
+    const bool mono = document ? row_monotone(p, b) : true;
     const bool general = document && !mono;  // per-key document compare
 
     if (threadIdx.x < kTile) {
         const int r = threadIdx.x;
-        const int q = q0 + r;
+        const int qi = i * kTile + r;           // query index
+        const bool valid = qi < p.q_len;
+        const int qa = p.q_off + (valid ? qi : p.q_len - 1);  // absolute position
         int ds = 0, de = T - 1;
-        if (document && mono) {
-            // Rows sharing the first (last) query's document share its start
-            // (end); any other document starts (ends) inside the tile.
-            ds = dq == s_docq[0] ? s_ds0 : q0 + lds_search_doc<false>(s_docq, 1, r, dq);
-            de = dq == s_docq[kTile - 1]
-                     ? s_deN
-                     : q0 + lds_search_doc<true>(s_docq, r + 1, kTile - 1, dq) - 1;
+        int32_t dq = 0;
+        if (document) {
+            dq = doc[qa];
+            if (mono) {
+                const int32_t *dr = p.out.doc_range + ((int64_t)b * p.npos + qa) * 2;
+                ds = dr[0];
+                de = dr[1];
+            }
         }
-        int hi = causal ? (q > p.prefix - 1 ? q : p.prefix - 1) : T - 1;
+        s_docq[r] = dq;
+        int hi = causal ? (qa > p.prefix - 1 ? qa : p.prefix - 1) : T - 1;
         if (de < hi) hi = de;
+        if (T - 1 < hi) hi = T - 1;
         int64_t lo64 = ds;
-        if (windowed && (int64_t)q - w + 1 > lo64) lo64 = (int64_t)q - w + 1;
+        if (windowed && (int64_t)qa - w + 1 > lo64) lo64 = (int64_t)qa - w + 1;
         int lo = lo64 < T ? (int)lo64 : T;
         int blo = kNone, bhi = -1;
         if (sinks_on) {
             blo = ds;
             bhi = p.sinks - 1 < hi ? p.sinks - 1 : hi;
         }
-        if (lo > hi) { lo = kNone; hi = -1; }
-        if (blo > bhi) { blo = kNone; bhi = -1; }
-        if (document) {
-            int32_t *dr = p.out.doc_range + ((int64_t)b * T + q) * 2;
-            dr[0] = mono ? ds : -1;
-            dr[1] = mono ? de : -1;
-        }
+        if (!valid || lo > hi) { lo = kNone; hi = -1; }
+        if (!valid || blo > bhi) { blo = kNone; bhi = -1; }
         // Extents of the main and sink intervals over the wave's rows (empty
         // intervals are (kNone, -1) and drop out of both).
         int e0 = lo, e1 = hi, e2 = blo, e3 = bhi;
@@ -257,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
         jhi = bmax / kTile > jhi ? bmax / kTile : jhi;
     }
 
-    const int64_t row_off = ((int64_t)b * nt + i) * nt;
+    const int64_t row_off = ((int64_t)b * p.nqt + i) * nt;
     int32_t *idx_p = p.out.kv_indices + row_off;
     int32_t *idx_f = p.out.full_kv_indices + row_off;
     uint8_t *cls_row = p.cls + row_off;
@@ -338,8 +376,66 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
     pad_tail(idx_p, run_p, nt);
     pad_tail(idx_f, run_f, nt);
     if (threadIdx.x == 0) {
-        p.out.kv_num_blocks[(int64_t)b * nt + i] = run_p;
-        p.out.full_kv_num_blocks[(int64_t)b * nt + i] = run_f;
+        p.out.kv_num_blocks[(int64_t)b * p.nqt + i] = run_p;
+        p.out.full_kv_num_blocks[(int64_t)b * p.nqt + i] = run_f;
+    }
+}
+
+// A composed mask: one workgroup per query-tile row evaluates every (query,
+// key) pair of every key tile, thread (key kk, row parity rb) taking the 64
+// rows rb, rb + 2, ... of the tile's key kk, and a workgroup vote gives the
+// tile's class.  Pairs outside Q_LEN x KV_LEN are never visible.
+__global__ __launch_bounds__(kThreads) void rows_table_kernel(MaskBuildParams p) {
+    __shared__ int32_t s_docq[kTile];
+    const int i = blockIdx.x, b = blockIdx.y;
+    const int nt = p.nkt;
+    const bool document = p.flags & BSM_MASK_DOCUMENT;
+    const bool windowed = p.flags & BSM_MASK_WINDOW;
+    const int sinks = (p.flags & BSM_MASK_SINKS) ? p.sinks : 0;
+    const int prefix = p.prefix;
+    const int64_t w = windowed ? (int64_t)(*p.window) : 0;
+    const int32_t *doc = document ? p.doc_ids + (int64_t)b * p.npos : nullptr;
+    const int kk = threadIdx.x & (kTile - 1), rb = threadIdx.x >> 7;
+    if (threadIdx.x < kTile) {
+        const int qi = i * kTile + threadIdx.x;
+        s_docq[threadIdx.x] = document ? doc[p.q_off + (qi < p.q_len ? qi : p.q_len - 1)] : 0;
+    }
+    __syncthreads();
+    const int64_t row_off = ((int64_t)b * p.nqt + i) * nt;
+    int32_t *idx_p = p.out.kv_indices + row_off;
+    int32_t *idx_f = p.out.full_kv_indices + row_off;
+    uint8_t *cls_row = p.cls + row_off;
+    int run_p = 0, run_f = 0;
+    for (int j = 0; j < nt; ++j) {
+        const int kv = j * kTile + kk;
+        const bool kvalid = kv < p.T;
+        const int32_t dk = document && kvalid ? doc[kv] : 0;
+        int any = 0, all = kvalid;
+        for (int m = 0; m < kTile / 2; ++m) {
+            const int r = rb + 2 * m;
+            const int qi = i * kTile + r;
+            const int64_t qa = (int64_t)p.q_off + qi;
+            const int c = qa >= kv, d = document && s_docq[r] == dk, wt = windowed && qa - kv < w;
+            const int st = kv < sinks, pt = kv < prefix;
+            const int vis = qi < p.q_len && kvalid && ((p.table >> (c + 2 * d + 4 * wt + 8 * st + 16 * pt)) & 1u);
+            any |= vis;
+            all &= vis;
+        }
+        any = __syncthreads_or(any);
+        all = __syncthreads_and(all);
+        if (threadIdx.x == 0) {
+            cls_row[j] = all ? kFull : (any ? kPartial : kEmpty);
+            if (all) idx_f[run_f] = j;
+            else if (any) idx_p[run_p] = j;
+        }
+        run_f += all ? 1 : 0;
+        run_p += (any && !all) ? 1 : 0;
+    }
+    pad_tail(idx_p, run_p, nt);
+    pad_tail(idx_f, run_f, nt);
+    if (threadIdx.x == 0) {
+        p.out.kv_num_blocks[(int64_t)b * p.nqt + i] = run_p;
+        p.out.full_kv_num_blocks[(int64_t)b * p.nqt + i] = run_f;
     }
 }
 
@@ -347,22 +443,22 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(MaskBuildParams p) {
     __shared__ int s_wp[kWaves], s_wf[kWaves];
     const int j = blockIdx.x;
     const int b = blockIdx.y;
-    const int nt = p.nt;
-    const uint8_t *cls = p.cls + (int64_t)b * nt * nt;
-    const int64_t col_off = ((int64_t)b * nt + j) * nt;
+    const int nq = p.nqt, nk = p.nkt;
+    const uint8_t *cls = p.cls + (int64_t)b * nq * nk;
+    const int64_t col_off = ((int64_t)b * nk + j) * nq;
     int32_t *idx_p = p.out.q_indices + col_off;
     int32_t *idx_f = p.out.full_q_indices + col_off;
     int run_p = 0, run_f = 0;
-    for (int ib = 0; ib < nt; ib += kThreads) {
+    for (int ib = 0; ib < nq; ib += kThreads) {
         const int i = ib + threadIdx.x;
-        const uint8_t c = i < nt ? cls[(int64_t)i * nt + j] : kEmpty;
+        const uint8_t c = i < nq ? cls[(int64_t)i * nk + j] : kEmpty;
         compact_chunk(c == kPartial, c == kFull, i, idx_p, idx_f, run_p, run_f, s_wp, s_wf);
     }
-    pad_tail(idx_p, run_p, nt);
-    pad_tail(idx_f, run_f, nt);
+    pad_tail(idx_p, run_p, nq);
+    pad_tail(idx_f, run_f, nq);
     if (threadIdx.x == 0) {
-        p.out.q_num_blocks[(int64_t)b * nt + j] = run_p;
-        p.out.full_q_num_blocks[(int64_t)b * nt + j] = run_f;
+        p.out.q_num_blocks[(int64_t)b * nk + j] = run_p;
+        p.out.full_q_num_blocks[(int64_t)b * nk + j] = run_f;
     }
 }
 
@@ -418,7 +514,8 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(MaskBuildParams p)
     const int32_t *fidx = cols ? p.out.full_q_indices : p.out.full_kv_indices;
     int32_t *order = cols ? p.out.q_order : p.out.kv_order;
     int32_t *sorted = p.order_ws + (cols ? p.order_ws_stride : 0);  // block at each sorted position
-    const int nt = p.nt;
+    const int nt = cols ? p.nkt : p.nqt;    // rows (columns) per mask batch
+    const int len = cols ? p.nqt : p.nkt;   // list length of a row (column)
     const int bpb = (nt + kOrderBlock - 1) / kOrderBlock;  // blocks per mask batch
     const int nb = p.mask_b * bpb;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -524,8 +621,8 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(MaskBuildParams p)
                 const int e = r0 + (x < n ? x : n - 1);
                 nf[x] = fnum[e];
                 np[x] = num[e];
-                fi[x] = fidx[(int64_t)e * nt];
-                pi[x] = idx[(int64_t)e * nt];
+                fi[x] = fidx[(int64_t)e * len];
+                pi[x] = idx[(int64_t)e * len];
             }
 #pragma unroll
             for (int x = 0; x < kOrderBlock; ++x) {
@@ -547,9 +644,13 @@ hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream)
     if (p.flags & BSM_MASK_DOCUMENT) {
         hipLaunchKernelGGL(check_monotone_kernel, dim3(p.nchunks, p.mask_b), dim3(kThreads), 0,
                            stream, p);
+        hipLaunchKernelGGL(ranges_kernel, dim3(p.nchunks, p.mask_b), dim3(kThreads), 0, stream, p);
     }
-    hipLaunchKernelGGL(rows_kernel, dim3(p.nt, p.mask_b), dim3(kThreads), 0, stream, p);
-    hipLaunchKernelGGL(cols_kernel, dim3(p.nt, p.mask_b), dim3(kThreads), 0, stream, p);
+    if (p.flags & BSM_MASK_TABLE)
+        hipLaunchKernelGGL(rows_table_kernel, dim3(p.nqt, p.mask_b), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(rows_kernel, dim3(p.nqt, p.mask_b), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(cols_kernel, dim3(p.nkt, p.mask_b), dim3(kThreads), 0, stream, p);
     hipLaunchKernelGGL(order_kernel, dim3(2), dim3(kOrderThreads), 0, stream, p);
     return hipGetLastError();
 }

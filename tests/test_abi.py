@@ -52,13 +52,17 @@ def _build(spec, bm=None, ws=FAKE, nbytes=1 << 30):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(seq_len=1000), _lib.BSM_E_INVALID),
     (dict(seq_len=0), _lib.BSM_E_INVALID),
+    (dict(seq_len=-128), _lib.BSM_E_INVALID),
+    (dict(q_len=-1), _lib.BSM_E_INVALID),
+    (dict(q_offset=-1), _lib.BSM_E_INVALID),
+    (dict(q_len=1 << 21, q_offset=(1 << 21) + 1), _lib.BSM_E_INVALID),  # last position past the maximum
     (dict(seq_len=(1 << 22) + 128), _lib.BSM_E_INVALID),
     (dict(mask_b=0), _lib.BSM_E_INVALID),
     (dict(flags=2), _lib.BSM_E_INVALID),          # DOCUMENT without doc_ids
     (dict(flags=4), _lib.BSM_E_INVALID),          # WINDOW without window
     (dict(flags=64), _lib.BSM_E_INVALID),         # unknown bit
+    (dict(flags=32 | 2), _lib.BSM_E_INVALID),     # composed mask with the document term, no doc_ids
     (dict(flags=12, window=FAKE, num_sinks=-1), _lib.BSM_E_INVALID),
 ])
 def test_build_rejects_bad_spec(kw, code):
@@ -72,7 +76,7 @@ def test_build_rejects_null_outputs_and_small_workspace():
     # doc_range is required only with the document term
     assert _build(_spec(flags=3, doc_ids=FAKE), _bm(null=8)) == _lib.BSM_E_INVALID
     assert b"doc_range" in lib.bsm_last_error()
-    need = lib.bsm_block_mask_workspace_bytes(1024, 1)
+    need = lib.bsm_block_mask_workspace_bytes(ctypes.byref(_spec()))
     assert need >= 64  # 8x8 class bytes + flags
     assert _build(_spec(), ws=FAKE, nbytes=need - 1) == _lib.BSM_E_WORKSPACE
     assert _build(_spec(), ws=None, nbytes=need) == _lib.BSM_E_WORKSPACE
@@ -80,10 +84,20 @@ def test_build_rejects_null_outputs_and_small_workspace():
     assert b"workspace" in lib.bsm_last_error()
 
 
+def _ws(**kw):
+    return lib.bsm_block_mask_workspace_bytes(ctypes.byref(_spec(**kw)))
+
+
 def test_workspace_sizes():
-    assert lib.bsm_block_mask_workspace_bytes(100, 1) == 0
-    assert lib.bsm_block_mask_workspace_bytes(65536, 1) >= 512 * 512
-    assert lib.bsm_block_mask_workspace_bytes(65536, 2) >= 2 * 512 * 512
+    assert _ws(seq_len=0) == 0
+    assert lib.bsm_block_mask_workspace_bytes(None) == 0
+    assert _ws(seq_len=100) >= 1                               # one ragged tile
+    assert _ws(seq_len=65536) >= 512 * 512
+    assert _ws(seq_len=65536, mask_b=2, flags=3, doc_ids=FAKE) >= 2 * 512 * 512
+    # rectangular: class bytes for QT x KT tiles
+    assert _ws(seq_len=65536, q_len=128) >= 512
+    assert _ws(seq_len=65536, q_len=128) < _ws(seq_len=65536)
+    assert _ws(seq_len=1000, q_len=300, q_offset=700) >= 3 * 8
     assert lib.bsm_bwd_workspace_bytes(2, 16, 16384, 128) >= 2 * (2 * 16 * 16384 * 4)  # Delta and L per row
     assert lib.bsm_bwd_workspace_bytes(1, 1, 1024, 96) == 0
 
@@ -106,7 +120,7 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
 @pytest.mark.parametrize("kw,code", [
     (dict(D=96), _lib.BSM_E_UNSUPPORTED),
     (dict(D=256), _lib.BSM_E_UNSUPPORTED),
-    (dict(T=1000), _lib.BSM_E_INVALID),
+    (dict(T=0), _lib.BSM_E_INVALID),
     (dict(T=2048), _lib.BSM_E_INVALID),            # != spec seq_len
     (dict(B=0), _lib.BSM_E_INVALID),
     (dict(B=3, spec=_spec(flags=3, mask_b=2, doc_ids=FAKE)), _lib.BSM_E_INVALID),
@@ -123,7 +137,7 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
     (dict(mod=BsmScoreMod(2, None, 1.0, FAKE)), _lib.BSM_E_INVALID),  # slope gradient without ALiBi
     (dict(scale=float("nan")), _lib.BSM_E_INVALID),
     (dict(spec=_spec(flags=1 | 16, prefix_len=-1)), _lib.BSM_E_INVALID),  # negative prefix
-    (dict(spec=_spec(flags=32)), _lib.BSM_E_INVALID),                     # unknown mask flag
+    (dict(spec=_spec(flags=64)), _lib.BSM_E_INVALID),                     # unknown mask flag
 ])
 def test_fwd_rejects(kw, code):
     assert _fwd(**kw) == code
