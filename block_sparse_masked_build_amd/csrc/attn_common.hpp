@@ -218,11 +218,11 @@ __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadId
 
 // nvalid: rows g_row0 .. g_row0 + nvalid - 1 exist (wave-uniform; it may be
 // <= 0 for a tile half wholly past the end, as long as row g_row0 + nvalid -
-// 1 lies inside the tensor).  A lane whose row lies past them copies that
-// last row instead, so a cut-short tile is read inside the tensor -- its
-// extra rows are masked by the caller.  Every copy takes the same form: a
-// wave-uniform base (the instruction's first source row, clamped) plus a
-// per-lane offset below kRowsPerInstr rows, so a whole tile costs no branch.
+// 1 lies inside the tensor).  A whole tile takes the plain copies; in a tile
+// cut short by the length a lane whose row lies past nvalid copies that last
+// row instead, so the tile is read inside the tensor -- its extra rows are
+// masked by the caller.  Both forms address a wave-uniform base plus a
+// per-lane offset below kRowsPerInstr rows.
 template <int D, int SWZ, int ROWS>
 __device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_row0, int64_t row_stride,
                                             int nvalid = ROWS) {
@@ -231,14 +231,30 @@ __device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_r
     constexpr int kInstr = ROWS / kRowsPerInstr / 4;
     static_assert(kInstr >= 1, "at least one copy per wave");
     const int wv = wave_id(), lane = threadIdx.x & 63;
-    const int last = __builtin_amdgcn_readfirstlane((nvalid < ROWS ? nvalid : ROWS) - 1);
     const int64_t row_bytes = row_stride * 2;
-    const uint64_t gbase = uniform_u64((uint64_t)(uintptr_t)g_row0);
     const int q = lane / L::kChunks;  // row inside the instruction's block
+    nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+    if (nvalid >= ROWS) {
+        // The wave's base goes to scalar registers once; the instructions'
+        // bases below it are scalar adds.
+        const uint64_t wbase = uniform_u64((uint64_t)(uintptr_t)(reinterpret_cast<const char *>(g_row0) +
+                                                                 (int64_t)(wv * kInstr * kRowsPerInstr) * row_bytes));
+#pragma unroll
+        for (int x = 0; x < kInstr; ++x) {
+            // (wv * kInstr + x) * kRowsPerInstr is a multiple of 16 plus a
+            // function of x only, so the swizzle depends on (x, q) alone.
+            const int r16 = (x * kRowsPerInstr + q) & 15;
+            const int c = (lane % L::kChunks) ^ tile_swizzle<D, SWZ>(r16);
+            const uint32_t voff = (uint32_t)(q * row_bytes) + (uint32_t)(c * 16);
+            const uint64_t xbase = wbase + (uint64_t)((int64_t)(x * kRowsPerInstr) * row_bytes);
+            copy16_to_lds_u(xbase, voff, lds_tile + (uint32_t)((wv * kInstr + x) * kRowsPerInstr * L::kRowBytes));
+        }
+        return;
+    }
+    const int last = nvalid - 1;
+    const uint64_t gbase = uniform_u64((uint64_t)(uintptr_t)g_row0);
 #pragma unroll
     for (int x = 0; x < kInstr; ++x) {
-        // (wv * kInstr + x) * kRowsPerInstr is a multiple of 16 plus a
-        // function of x only, so the swizzle depends on (x, q) alone.
         const int xrow0 = (wv * kInstr + x) * kRowsPerInstr;
         const int xsrc0 = xrow0 < last ? xrow0 : last;  // scalar
         const int row = xrow0 + q;
