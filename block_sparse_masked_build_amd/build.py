@@ -20,7 +20,15 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbsm.so")
 
-SOURCES = ["mask_builder.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "bsm_api.cpp"]
+# (source, object, extra flags): the attention passes are compiled once per
+# head dimension so that the halves build in parallel
+SOURCES = [("mask_builder.hip", "mask_builder.o", []),
+           ("attn_fwd.hip", "attn_fwd_d64.o", ["-DBSM_HEAD_DIM=64"]),
+           ("attn_fwd.hip", "attn_fwd_d128.o", ["-DBSM_HEAD_DIM=128"]),
+           ("attn_bwd.hip", "attn_bwd_d64.o", ["-DBSM_HEAD_DIM=64"]),
+           ("attn_bwd.hip", "attn_bwd_d128.o", ["-DBSM_HEAD_DIM=128"]),
+           ("attn_decode.hip", "attn_decode.o", []),
+           ("bsm_api.cpp", "bsm_api.o", [])]
 ARCH = "gfx950"
 
 
@@ -40,9 +48,10 @@ def compile_flags():
             "-I", os.path.join(HERE, "..", "include")]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *compile_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(entry, verbose: bool) -> str:
+    src, obj_name, extra = entry
+    obj = os.path.join(BUILD_DIR, obj_name)
+    cmd = [hipcc(), *compile_flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -115,7 +115,8 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto issue = [&](int t, int key0) {
         const uint32_t bf = t & 1;
-        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, a.npos - key0);
+        if (MODE == kGather || (MODE == kTable && a.doc))
+            issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, a.npos - key0);
         issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st,
                                                a.kv_len - key0);
         issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st,
@@ -169,7 +170,8 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
                 dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, st), gf[st], dp[kb]);
             }
         }
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial);
+        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial,
+                                           MODE == kTable && a.doc);
         bf16x8 dsb[2][2];
         float sg_c = 0.0f, sg_s = 0.0f;  // SGRAD: sum ds c and sum ds over the step
 #pragma unroll
@@ -299,7 +301,9 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     // first pipeline step waits for everything.
 
     float sg = 0.0f;
-    if (mode == kGather)
+    if (mode == kTable)
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+    else if (mode == kGather)
         dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else if (mode == kSinks)
         dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
@@ -338,9 +342,33 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
 // compare.
 struct ColMask {
     int32_t lo, hi, dock;
+    // composed mask (kTable): query indices from which the causal term holds
+    // (q >= kpos) and below which the window term holds (q - kpos < window),
+    // and the truth table shifted by the key's own sink and prefix bits, so
+    // that bit (C + 2 Dc + 4 W) of it decides the pair
+    int32_t cq0, wq1;
+    uint32_t table;
 };
 
+// Column view of a composed mask for key kpos: [lo, hi] holds the queries
+// that exist.
+__device__ inline void make_col_table(const AttnParams &p, int bm, int kpos, int window, ColMask &cm) {
+    cm.lo = 0;
+    cm.hi = p.q_len - 1;
+    cm.dock = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids[(int64_t)bm * p.npos + kpos] : 0;
+    const int64_t c0 = (int64_t)kpos - p.q_off;
+    cm.cq0 = (int)(c0 < -(1 << 30) ? -(1 << 30) : c0);
+    int64_t w1 = (p.mask_flags & BSM_MASK_WINDOW) ? (int64_t)kpos + window - p.q_off : -((int64_t)1 << 30);
+    cm.wq1 = w1 < -(1 << 30) ? -(1 << 30) : (w1 > (1 << 30) ? (1 << 30) : (int)w1);
+    const bool sink = (p.mask_flags & BSM_MASK_SINKS) && kpos < p.sinks;
+    const bool pre = kpos < p.prefix;
+    cm.table = p.table >> ((sink ? 8u : 0u) | (pre ? 16u : 0u));
+}
+
 __device__ inline bool make_col_mask(const AttnParams &p, int bm, int kpos, ColMask &cm) {
+    cm.cq0 = 0;
+    cm.wq1 = 0;
+    cm.table = 0;
     // interval in absolute positions first, then in query indices
     int ds = 0, de = p.npos - 1;
     bool gather = false;
@@ -377,7 +405,7 @@ struct DkdvArgs {
     const __bf16 *qb, *gb;
     int64_t q_st, do_st;
     const float *l2, *delta;  // this (batch, head)
-    const int32_t *fidx, *pidx, *doc;  // doc: document ids from query 0's position on
+    const int32_t *fidx, *pidx, *doc;  // doc: document ids from query 0's position on (NULL: none)
     int nfull, nt, kpos;      // nt: query tiles; kpos: this lane's key (clamped to KV_LEN - 1)
     int q_len, q_off;
     float scale, scale_log2, slope, cap, inv_cap;
@@ -429,7 +457,9 @@ __device__ inline void dkdv_sdp(const bf16x8 (&rq)[D / 16], const bf16x8 (&rg)[D
 
 // p and dS / scale of query block b (queries q0 + 32 b + 4 hl + 8 (r/4) + r%4
 // in register r) as the bf16 B operands of the dV and dK products.
-template <bool ALIBI, bool SOFTCAP, bool GATHER, bool MASKED>
+// CMODE: kPlain (the interval), kGather (interval and a per-query document
+// compare) or kTable (a composed mask, [lo, hi] the queries that exist).
+template <bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
 __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t sl2, uint32_t sdl,
                                   uint32_t sdoc, int b, int q0, const f32x16 &s, const f32x16 &dp,
                                   bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
@@ -444,13 +474,21 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
     float ns = -a.mk.slope_f;
     float n = ALIBI ? ns * (float)(qbase + a.q_off - a.kpos) : 0.0f;
     asm volatile("" : "+v"(lo_t), "+v"(n), "+v"(ns));
+    // composed mask, query offset c: causal for c >= tc, window for c < tw
+    int tc = 0, tw = 0;
+    if (CMODE == kTable && MASKED) {
+        tc = cm.cq0 - qbase;
+        tw = cm.wq1 - qbase;
+        asm volatile("" : "+v"(tc), "+v"(tw));
+    }
+    const bool docs = CMODE == kGather || (CMODE == kTable && a.doc);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int ql4 = b * 32 + g * 8 + hl * 4;
         const f32x4 L = lds_load<f32x4>(sl2 + 4 * ql4);
         const f32x4 Dl = lds_load<f32x4>(sdl + 4 * ql4);
         i32x4 dq4 = {0, 0, 0, 0};
-        if (GATHER && MASKED) dq4 = lds_load<i32x4>(sdoc + 4 * ql4);
+        if (docs && MASKED) dq4 = lds_load<i32x4>(sdoc + 4 * ql4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = g * 4 + e;
@@ -465,8 +503,11 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
             }
             if (MASKED) {
                 bool vis = (uint32_t)(c - lo_t) <= (uint32_t)span;
-                if (GATHER) {
-                    const int dqv = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
+                const int dqv = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
+                if (CMODE == kTable) {
+                    const uint32_t idx = (c >= tc ? 1u : 0u) | (docs && dqv == cm.dock ? 2u : 0u) | (c < tw ? 4u : 0u);
+                    vis = vis && ((cm.table >> idx) & 1u);
+                } else if (CMODE == kGather) {
                     vis = vis && dqv == cm.dock;
                 }
                 pv = vis ? pv : 0.0f;
@@ -508,7 +549,7 @@ __device__ inline void dkdv_acc(const bf16x8 (&tq)[2][D / 32], const bf16x8 (&tg
 // four 32-query blocks: the S / dP products of block b+1 are issued next to
 // the gradient arithmetic of block b, and the row operands of block b+2 are
 // read during the dV / dK products of block b.
-template <int D, bool ALIBI, bool SOFTCAP, bool GATHER, bool MASKED>
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
 __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
                                  const bf16x8 (&vf)[D / 16], const KvOffsets &oq, const KvOffsets &og,
                                  uint32_t sl2, uint32_t sdl, uint32_t sdoc, int q0,
@@ -524,7 +565,7 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf1
         const int cur = b & 1;
         if (b + 1 < NB) dkdv_sdp<D>(rq, rg, kf, vf, s[cur ^ 1], dp[cur ^ 1]);
         bf16x8 pb[2], dsb[2];
-        dkdv_grads<ALIBI, SOFTCAP, GATHER, MASKED>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb);
+        dkdv_grads<ALIBI, SOFTCAP, CMODE, MASKED>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb);
         bf16x8 tq[2][D / 32], tg[2][D / 32];
         dkdv_read_cols<D>(oq, og, b, tq, tg);
         if (b + 2 < NB) dkdv_read_rows<D>(oq, og, b + 2, rq, rg);
@@ -533,7 +574,7 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf1
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, bool GATHER>
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE>
 __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
                                  const bf16x8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
                                  int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
@@ -549,7 +590,8 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf1
         const int nq = a.q_len - q0;
         issue_ints_to_lds_at<kTile>(lds.l2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0), nq);
         issue_ints_to_lds_at<kTile>(lds.delta + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0), nq);
-        if (GATHER) issue_ints_to_lds_at<kTile>(lds.doc + bf * kWB, a.doc + q0, nq);
+        if (CMODE == kGather || (CMODE == kTable && a.doc))
+            issue_ints_to_lds_at<kTile>(lds.doc + bf * kWB, a.doc + q0, nq);
         issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.q + bf * kTB, a.qb + (int64_t)q0 * a.q_st, a.q_st, nq);
         issue_tile_to_lds_at<D, kSwzKV, kTile>(lds.g + bf * kTB, a.gb + (int64_t)q0 * a.do_st, a.do_st, nq);
     };
@@ -571,7 +613,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf1
         // Tile base and buffer enter through the lane offsets (see dq_main):
         // the second tile's base lies beyond a read's 16-bit offset field.
         const KvOffsets oq = step_offsets(off, lds.q + bf * kTB), og = step_offsets(off, lds.g + bf * kTB);
-        dkdv_tile<D, ALIBI, SOFTCAP, GATHER, decltype(masked)::value>(
+        dkdv_tile<D, ALIBI, SOFTCAP, CMODE, decltype(masked)::value>(
             a, cm, kf, vf, oq, og, lds.l2 + bf * kWB, lds.delta + bf * kWB, lds.doc + bf * kWB, q0, dk, dv);
         wait_lds_reads();  // this wave's reads of tile t are done before the next barrier
         q0 = q_next;
@@ -625,7 +667,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     const int ntiles = a.nfull + npart;
 
     ColMask cm;
-    const bool gather = make_col_mask(p, bm, kpos, cm);
+    const bool table = p.mask_flags & BSM_MASK_TABLE;
+    bool gather = false;
+    if (table)
+        make_col_table(p, bm, kpos, (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0, cm);
+    else
+        gather = make_col_mask(p, bm, kpos, cm);
     // LDS is addressed by byte address, taken here from the shared object.
     DkdvLds<D> lds;
     lds.q = lds_addr(&sm.q[0][0]);
@@ -653,10 +700,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     // No wait here: the first tile copies are issued while the key rows
     // load (see dq_kernel).
 
-    if (gather)
-        dkdv_main<D, ALIBI, SOFTCAP, true>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+    if (table)
+        dkdv_main<D, ALIBI, SOFTCAP, kTable>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+    else if (gather)
+        dkdv_main<D, ALIBI, SOFTCAP, kGather>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
     else
-        dkdv_main<D, ALIBI, SOFTCAP, false>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kPlain>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
 
     // dK and dV rows of the wave, staged through the query and output-gradient
     // buffers once every wave is done with them (dS was accumulated without
@@ -732,9 +781,13 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attn_bwd(const AttnParams &p, int D, hipStream_t stream) {
-    if (D == 64) return launch_d<64>(p, stream);
-    return launch_d<128>(p, stream);
-}
+// The build compiles this source once per head dimension (BSM_HEAD_DIM),
+// so that the two halves compile in parallel; without it both are built.
+#if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 64
+hipError_t launch_attn_bwd_d64(const AttnParams &p, hipStream_t stream) { return launch_d<64>(p, stream); }
+#endif
+#if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 128
+hipError_t launch_attn_bwd_d128(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
+#endif
 
 }  // namespace bsm

@@ -453,14 +453,98 @@ __device__ inline void store_transposed_4x8(__bf16 *dst, int ld, int r0, int c0,
 //              (causal, window and, with contiguous documents, the document);
 //   kSinks  -- plus the sink interval [slo, shi];
 //   kGather -- document ids are not contiguous runs: interval terms without
-//              the document, then a per-key document id compare.
-enum MaskMode { kPlain = 0, kSinks = 1, kGather = 2 };
+//              the document, then a per-key document id compare;
+//   kTable  -- a composed mask: the five terms of every score index its
+//              truth table; [lo, hi] holds the keys that exist.
+enum MaskMode { kPlain = 0, kSinks = 1, kGather = 2, kTable = 3 };
 
 struct RowMask {
     int32_t lo, hi;     // main visible interval of keys (inclusive)
     int32_t slo, shi;   // sink interval (empty when slo > shi)
-    int32_t docq;       // document id of the query (kGather only)
+    int32_t docq;       // document id of the query (kGather, kTable)
+    // kTable only: key bounds of the terms -- causal key <= qpos, window
+    // key >= wlo, sink key < sinks, prefix key < prefix (0: term off) -- and
+    // the truth table (bit C + 2 Dc + 4 W + 8 S + 16 P)
+    int32_t qpos, wlo, sinks, prefix;
+    uint32_t table;
 };
+
+// Row view of a composed mask.  A lane's 32 keys of a step are kbase + c,
+// c = 32 kb + 8 g + e (e < 4), numbered j = 16 kb + 4 g + e; each term, as
+// a function of the key, is a threshold, so over the lane's keys it is a
+// 32-bit mask with bit j for key j.  The truth table then combines the five
+// masks bitwise (a tree of 31 two-way selects), and a score is kept or set
+// to -inf by its bit.
+//
+// Number of the lane's offsets c below t (t clamped to [0, 64]).
+__device__ inline int owned_below(int t) {
+    t = min(max(t, 0), 64);
+    return 4 * (t >> 3) + min(t & 7, 4);
+}
+
+// Bits j of the lane's keys with offset c < t.
+__device__ inline uint32_t bits_below(int t) {
+    const int n = owned_below(t);
+    return n >= 32 ? ~0u : (1u << n) - 1u;
+}
+
+// (sel & a) | (~sel & b), bit by bit.
+__device__ inline uint32_t bit_select(uint32_t sel, uint32_t a, uint32_t b) { return (sel & a) | (~sel & b); }
+
+// The truth table (bit C + 2 Dc + 4 W + 8 S + 16 P) applied bitwise to the
+// term masks.
+__device__ inline uint32_t table_combine(uint32_t table, uint32_t c, uint32_t d, uint32_t w, uint32_t s,
+                                         uint32_t p) {
+    uint32_t l1[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const uint32_t t0 = ((table >> (2 * k)) & 1u) ? ~0u : 0u;
+        const uint32_t t1 = ((table >> (2 * k + 1)) & 1u) ? ~0u : 0u;
+        l1[k] = bit_select(c, t1, t0);
+    }
+    uint32_t l2[8], l3[4], l4[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) l2[k] = bit_select(d, l1[2 * k + 1], l1[2 * k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) l3[k] = bit_select(w, l2[2 * k + 1], l2[2 * k]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) l4[k] = bit_select(s, l3[2 * k + 1], l3[2 * k]);
+    return bit_select(p, l4[1], l4[0]);
+}
+
+// Visible keys of the lane for the step starting at key0, as bits j; sdoc
+// is the LDS byte address of the step's key document ids, read when docs.
+__device__ inline uint32_t table_row_bits(const RowMask &rm, uint32_t sdoc, int key0, bool docs) {
+    const int hl = (threadIdx.x & 63) >> 5;
+    const int kbase = key0 + hl * 4;
+    const uint32_t c = bits_below(rm.qpos + 1 - kbase);  // key <= qpos
+    const uint32_t w = ~bits_below(rm.wlo - kbase);      // key >= wlo
+    const uint32_t s = bits_below(rm.sinks - kbase);     // key < sinks
+    const uint32_t p = bits_below(rm.prefix - kbase);    // key < prefix
+    const uint32_t v = bits_below(rm.hi + 1 - kbase);    // the key exists
+    uint32_t d = 0;
+    if (docs) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const i32x4 dk = lds_load<i32x4>(sdoc + 4 * (kb * 32 + g * 8 + hl * 4));
+                const int j = kb * 16 + g * 4;
+                d |= (dk.x == rm.docq ? 1u : 0u) << j;
+                d |= (dk.y == rm.docq ? 2u : 0u) << j;
+                d |= (dk.z == rm.docq ? 4u : 0u) << j;
+                d |= (dk.w == rm.docq ? 8u : 0u) << j;
+            }
+    }
+    return table_combine(rm.table, c, d, w, s, p) & v;
+}
+
+// Score kept when bit j of bits is set, -inf otherwise (a sign-extended bit
+// field as the select mask).
+__device__ inline float keep_if_bit(float x, uint32_t bits, int j) {
+    const uint32_t m = (uint32_t)((int32_t)(bits << (31 - j)) >> 31);
+    return __builtin_bit_cast(float, (__builtin_bit_cast(uint32_t, x) & m) | (~m & 0xff800000u));
+}
 
 // Stores a wave's 32 x D block of fp32 accumulators as bf16 rows, times mul
 // (per lane, i.e. per row).  Accumulator layout: lane (row n, half hl) holds
@@ -533,7 +617,7 @@ __device__ inline void row_mods(f32x16 (&s)[2], int key0, int qpos, const ModK &
 
 template <bool ALIBI, bool SOFTCAP, int MODE>
 __device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int qpos, const ModK &mk,
-                                    const RowMask &rm, bool partial) {
+                                    const RowMask &rm, bool partial, bool table_docs = false) {
     const int hl = (threadIdx.x & 63) >> 5;
     const int kbase = key0 + hl * 4;
     row_mods<ALIBI, SOFTCAP>(s, key0, qpos, mk);
@@ -547,6 +631,17 @@ __device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int
     int slo_t = rm.shi >= rm.slo ? rm.slo - kbase : 1 << 30;
     const int sspan = rm.shi >= rm.slo ? rm.shi - rm.slo : 0;
     asm volatile("" : "+v"(lo_t), "+v"(slo_t));
+    if (MODE == kTable) {
+        const uint32_t bits = table_row_bits(rm, sdoc, key0, table_docs);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint32_t half = (bits >> (16 * kb)) & 0xffffu;
+            if (__all(half == 0xffffu)) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = keep_if_bit(s[kb][r], bits, kb * 16 + r);
+        }
+        return;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         // The wave's 32 queries x these 32 keys: skip the elementwise test
@@ -585,7 +680,8 @@ __device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int
 // every score is tested, hidden ones become -inf.  sdoc is the LDS byte
 // address of the step's key document ids (kGather only).
 template <int MODE>
-__device__ inline void row_mask_flat(uint32_t sdoc, f32x16 (&s)[2], int key0, const RowMask &rm) {
+__device__ inline void row_mask_flat(uint32_t sdoc, f32x16 (&s)[2], int key0, const RowMask &rm,
+                                     bool table_docs = false) {
     const int hl = (threadIdx.x & 63) >> 5;
     const int kbase = key0 + hl * 4;
     // Bounds relative to this lane's first key, opaque so that the compiler
@@ -596,6 +692,14 @@ __device__ inline void row_mask_flat(uint32_t sdoc, f32x16 (&s)[2], int key0, co
     int slo_t = rm.shi >= rm.slo ? rm.slo - kbase : 1 << 30;
     const int sspan = rm.shi >= rm.slo ? rm.shi - rm.slo : 0;
     asm volatile("" : "+v"(lo_t), "+v"(slo_t));
+    if (MODE == kTable) {
+        const uint32_t bits = table_row_bits(rm, sdoc, key0, table_docs);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = keep_if_bit(s[kb][r], bits, kb * 16 + r);
+        return;
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -668,7 +772,29 @@ __device__ inline float row_max(const f32x16 (&s)[2]) {
 // range; a row whose documents are not contiguous is flagged (-1) there, and
 // then the interval terms exclude the document and docq holds the query's id
 // for a per-key compare.  Returns the mode the row needs.
+// Composed mask: every key that exists, the term bounds and the truth table
+// (window: the int32 scalar read at run time).
+__device__ inline void make_table_mask(const AttnParams &p, int qpos, int window, int32_t docq, RowMask &rm) {
+    rm.lo = 0;
+    rm.hi = p.T - 1;
+    rm.slo = 0;
+    rm.shi = -1;
+    rm.docq = docq;
+    rm.qpos = qpos;
+    int64_t wlo = (int64_t)qpos - (int64_t)window + 1;
+    if (!(p.mask_flags & BSM_MASK_WINDOW)) wlo = (int64_t)1 << 30;  // no key is in an absent window
+    rm.wlo = wlo < -(1 << 30) ? -(1 << 30) : (wlo > (1 << 30) ? (1 << 30) : (int)wlo);
+    rm.sinks = (p.mask_flags & BSM_MASK_SINKS) ? min(max(p.sinks, 0), p.T) : 0;
+    rm.prefix = p.prefix;
+    rm.table = p.table;
+}
+
 __device__ inline int make_row_mask(const AttnParams &p, int bm, int qpos, RowMask &rm) {
+    if (p.mask_flags & BSM_MASK_TABLE) {
+        make_table_mask(p, qpos, (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0,
+                        (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids[(int64_t)bm * p.npos + qpos] : 0, rm);
+        return kTable;
+    }
     const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
     int ds = 0, de = p.T - 1;
     rm.docq = 0;

@@ -228,6 +228,10 @@ struct RowLoad {
 // the mode the row needs (uniform over the workgroup: the document-range
 // sentinel marks whole mask rows).
 __device__ inline int finish_row_mask(const AttnParams &p, int qpos, const RowLoad &rl, int window, RowMask &rm) {
+    if (p.mask_flags & BSM_MASK_TABLE) {
+        make_table_mask(p, qpos, window, rl.docq, rm);
+        return kTable;
+    }
     int ds = rl.ds, de = rl.de;
     const bool gather = ds < 0;
     if (gather) {
@@ -359,7 +363,8 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     }
     auto step_key0 = [&](int t) { return tile_at(tl, a, t >> 1) * kTile + (t & 1) * kHalf; };
     auto issue_k = [&](int t, int key0) {
-        if (MODE == kGather) issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, p.npos - key0);
+        if (MODE == kGather || (MODE == kTable && a.doc))
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, p.npos - key0);
         issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st, p.T - key0);
     };
     auto issue_v = [&](int t, int key0) {
@@ -394,7 +399,8 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     int key_ahead = k0 + kHalf;  // first key of step t+1 at the top of step t
     fwd_qk<D>(sm.k[0], off, qf, sa);
     row_mods<ALIBI, SOFTCAP>(sa, k0, a.qpos, a.mk);
-    if (a.nfull == 0) row_mask_flat<MODE>(lds_addr(sm.doc[0]), sa, k0, rm);
+    const bool table_docs = MODE == kTable && a.doc;
+    if (a.nfull == 0) row_mask_flat<MODE>(lds_addr(sm.doc[0]), sa, k0, rm, table_docs);
     mx = step_max(sa);
 
     auto step = [&](f32x16 (&sc)[2], f32x16 (&sn)[2], int t, auto next_masked, auto first_step) {
@@ -415,7 +421,8 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
         fwd_exp(sc, pb, l, c_mul, m_use);
         fwd_pv<D>(sm.v[t & 1], offt, pb, o);
         row_mods<ALIBI, SOFTCAP>(sn, key_next, a.qpos, a.mk);
-        if (decltype(next_masked)::value) row_mask_flat<MODE>(lds_addr(sm.doc[(t + 1) & 1]), sn, key_next, rm);
+        if (decltype(next_masked)::value)
+            row_mask_flat<MODE>(lds_addr(sm.doc[(t + 1) & 1]), sn, key_next, rm, table_docs);
         mx = step_max(sn);
         wait_lds_reads();  // this wave's reads of step t are done before the next barrier
     };
@@ -477,7 +484,9 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd
     tile_barrier();
     RowMask rm;
     const int mode = finish_row_mask(p, cur.qpos, rl, window, rm);
-    if (mode == kGather)
+    if (mode == kTable)
+        item_run<D, ALIBI, SOFTCAP, kTable>(p, cur, tl, rm, qf, off, sm, o, m, l);
+    else if (mode == kGather)
         item_run<D, ALIBI, SOFTCAP, kGather>(p, cur, tl, rm, qf, off, sm, o, m, l);
     else if (mode == kSinks)
         item_run<D, ALIBI, SOFTCAP, kSinks>(p, cur, tl, rm, qf, off, sm, o, m, l);
@@ -504,9 +513,13 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const AttnParams &p, int D, hipStream_t stream) {
-    if (D == 64) return launch_d<64>(p, stream);
-    return launch_d<128>(p, stream);
-}
+// The build compiles this source once per head dimension (BSM_HEAD_DIM),
+// so that the two halves compile in parallel; without it both are built.
+#if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 64
+hipError_t launch_attn_fwd_d64(const AttnParams &p, hipStream_t stream) { return launch_d<64>(p, stream); }
+#endif
+#if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 128
+hipError_t launch_attn_fwd_d128(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
+#endif
 
 }  // namespace bsm

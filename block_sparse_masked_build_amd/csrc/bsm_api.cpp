@@ -146,8 +146,6 @@ bsm_status check_attn_common(int32_t B, int32_t H, int32_t T, int32_t D, const b
     if (spec->seq_len != T) return fail(BSM_E_INVALID, "mask seq_len %d != T %d", spec->seq_len, T);
     if (spec->mask_b != 1 && spec->mask_b != B)
         return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
-    if (spec->flags & BSM_MASK_TABLE)
-        return fail(BSM_E_UNSUPPORTED, "composed (TABLE) masks: block masks and decoding only");
     const MaskDims m = mask_dims(spec);
     if ((int64_t)B * H * (m.nqt > m.nkt ? m.nqt : m.nkt) > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
     return check_mod(mod);
@@ -413,7 +411,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     fill_tensor(out, optr, p.o_sb, p.o_sh, p.o_st);
     p.o = const_cast<void *>(optr);
     p.lse = lse;
-    return hip_status(bsm::launch_attn_fwd(p, D, static_cast<hipStream_t>(stream)),
+    return hip_status((D == 64 ? bsm::launch_attn_fwd_d64 : bsm::launch_attn_fwd_d128)(p, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_fwd launch");
 }
 
@@ -470,7 +468,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     p.dslope_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                               2 * align256((size_t)B * H * Q * sizeof(float)));
     p.dslopes = (mod && (mod->flags & BSM_MOD_ALIBI)) ? mod->alibi_slopes_grad : nullptr;
-    return hip_status(bsm::launch_attn_bwd(p, D, static_cast<hipStream_t>(stream)),
+    return hip_status((D == 64 ? bsm::launch_attn_bwd_d64 : bsm::launch_attn_bwd_d128)(p, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_bwd launch");
 }
 

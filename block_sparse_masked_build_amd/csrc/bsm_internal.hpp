@@ -87,8 +87,10 @@ struct AttnParams {
 };
 
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);
-hipError_t launch_attn_fwd(const AttnParams &p, int D, hipStream_t stream);
-hipError_t launch_attn_bwd(const AttnParams &p, int D, hipStream_t stream);
+hipError_t launch_attn_fwd_d64(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_fwd_d128(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d64(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d128(const AttnParams &p, hipStream_t stream);
 // Decoding step: one query per (b, h) at the last live position of a cache
 // of p.T (capacity) positions; the block-mask row arrays of `a` are the
 // optional block mask (kv_num NULL: none).  part = B*H*slots*(D + 2) floats.

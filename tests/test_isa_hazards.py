@@ -82,22 +82,35 @@ the block that follows it."""
 _ASM = {}
 
 
+ATTN_OBJECTS = ["attn_fwd.hip@64", "attn_fwd.hip@128", "attn_bwd.hip@64", "attn_bwd.hip@128"]
+ALL_OBJECTS = ATTN_OBJECTS + ["mask_builder.hip", "attn_decode.hip"]
+
+
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    """Device assembly of a source, compiled once per test module."""
-    def get(src):
-        if src not in _ASM:
-            out = tmp_path_factory.mktemp("isa") / (src + ".s")
+    """Device assembly of a source (name, or "name@D" for the attention
+    passes' objects of head dimension D, as the build compiles them).  The
+    first use compiles every object the tests read, concurrently."""
+    if not _ASM:
+        tmp = tmp_path_factory.mktemp("isa")
+        procs = {}
+        for key in ALL_OBJECTS:
+            src, _, d = key.partition("@")
+            out = tmp / (src + d + ".s")
             cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
                    "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
+                   *([f"-DBSM_HEAD_DIM={d}"] if d else []),
                    "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
-            subprocess.run(cmd, check=True, capture_output=True)
-            _ASM[src] = out.read_text()
-        return _ASM[src]
-    return get
+            procs[key] = (subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE), out)
+        for key, (proc, out) in procs.items():
+            _, err = proc.communicate()
+            assert proc.returncode == 0, (key, err.decode()[-2000:])
+            _ASM[key] = out.read_text()
+    return lambda key: _ASM[key]
 
 
-@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip"])
+
+@pytest.mark.parametrize("src", ATTN_OBJECTS)
 def test_no_inline_assembly_reads_of_pending_matrix_results(src, asm):
     text = asm(src)
     kernels = re.findall(r"^(_Z\S*kernel\S*):", text, re.M)
@@ -113,7 +126,7 @@ def test_no_inline_assembly_reads_of_pending_matrix_results(src, asm):
 
 
 
-@pytest.mark.parametrize("src", ["attn_fwd.hip", "attn_bwd.hip", "mask_builder.hip", "attn_decode.hip"])
+@pytest.mark.parametrize("src", ALL_OBJECTS)
 def test_m0_is_only_written_by_the_lds_copies(src, asm):
     """The asynchronous LDS copies set M0 (the LDS destination) in inline
     assembly and list it as clobbered, but M0 is a register the compiler
