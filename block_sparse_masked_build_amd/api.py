@@ -435,6 +435,44 @@ def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = Non
     return out, lse
 
 
+def decode_multi_spec(spec: MaskSpec, kv_len: int, n: int) -> MaskSpec:
+    """The mask of a block of n queries at positions kv_len - n .. kv_len - 1
+    against the first kv_len positions of a cache described by spec (whose T
+    is the cache capacity): KV_LEN = kv_len, Q_LEN = n, q_offset = kv_len - n.
+    Document ids are restricted to the live positions (a copy when the mask
+    batch has several rows)."""
+    if not 1 <= n <= kv_len <= spec.T:
+        raise ValueError(f"need 1 <= n={n} <= kv_len={kv_len} <= capacity={spec.T}")
+    docs = spec.doc_ids[:, :kv_len].contiguous() if spec.doc_ids is not None else None
+    return MaskSpec(int(kv_len), spec.causal, docs, spec.window, spec.sinks, spec.prefix, int(n),
+                    int(kv_len - n), spec.composed)
+
+
+def flex_attention_decode_multi(q, k, v, spec: MaskSpec, kv_len: int, mod: Optional[ScoreMod] = None,
+                                scale: Optional[float] = None, step_spec: Optional[MaskSpec] = None,
+                                block_mask: Optional[BlockMask] = None, out=None, lse=None):
+    """A block of n = q.shape[2] new queries (speculative or chunked decoding)
+    at positions kv_len - n .. kv_len - 1 of the cache k, v [B, H, capacity,
+    D], on the matrix cores: the rectangular forward over the live keys
+    (views of the cache, no copy).  kv_len is a host int here, since the
+    block mask of the step is built for it: pass step_spec =
+    decode_multi_spec(spec, kv_len, n) and its block mask to reuse them,
+    otherwise both are built on this call.  Returns (out [B, H, n, D], lse
+    [B, H, n])."""
+    B, H, n, D = q.shape
+    if k.dim() != 4 or k.shape[0] != B or k.shape[1] != H or k.shape[3] != D or v.shape != k.shape:
+        raise ValueError(f"k, v must be [B, H, capacity, D] matching q {tuple(q.shape)}")
+    if spec.T != k.shape[2]:
+        raise ValueError(f"mask spec length {spec.T} != cache capacity {k.shape[2]}")
+    if step_spec is None:
+        step_spec = decode_multi_spec(spec, kv_len, n)
+    elif (step_spec.T, step_spec.Q, step_spec.q_offset) != (kv_len, n, kv_len - n):
+        raise ValueError("step_spec was built for another live length or query count")
+    if block_mask is None:
+        block_mask = build_block_mask(step_spec)
+    return flex_attention_fwd(q, k[:, :, :kv_len], v[:, :, :kv_len], block_mask, step_spec, mod, scale, out, lse)
+
+
 def flex_attention_decode_static(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod], scale: Optional[float],
                                  kv_len: torch.Tensor, block_mask: Optional[BlockMask], out: torch.Tensor,
                                  lse: torch.Tensor):
@@ -472,4 +510,5 @@ __all__ = ["MaskSpec", "MaskTerm", "CAUSAL", "SAME_DOC", "IN_WINDOW", "SINK", "P
            "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
            "flex_attention_decode", "decode_workspace", "flex_attention_decode_static",
+           "decode_multi_spec", "flex_attention_decode_multi",
            "bwd_workspace", "block_mask_workspace", "_lib"]

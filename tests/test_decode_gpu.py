@@ -186,3 +186,36 @@ def test_graph_replay_as_the_cache_grows():
         ref = api.flex_attention_decode(q, k, v, spec, None, kv_len=kvl.clone(), block_mask=bm)
         torch.cuda.synchronize()
         assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), L0
+
+
+@pytest.mark.parametrize("n,L", [(1, 1), (1, 1000), (4, 4), (4, 4096), (16, 2049), (130, 3000)])
+def test_multi_query_decode_on_the_matrix_cores(n, L):
+    """A block of n new queries at the end of a live cache (speculative or
+    chunked decoding) runs as the rectangular forward over the live keys:
+    parity with the oracle's rows L - n .. L - 1, documents + window 700,
+    ALiBi + soft-cap 30, capacity 4,096."""
+    from block_sparse_masked_build_amd import api
+    cap, B, H, D = 4096, 2, 2, 128
+    rng = np.random.default_rng(70 + n)
+    docs = np.stack([np.cumsum(rng.random(cap) < 1 / 600).astype(np.int32) for _ in range(B)])
+    spec = MaskSpecData(cap, causal=True, document=True, doc_ids=docs, window=700)
+    mod = ScoreModData(alibi_slopes=alibi_slopes(H), softcap=30.0)
+    log(f"[decode multi] n={n} L={L} cap {cap} B{B} H{H} D{D}")
+    g = torch.Generator("cpu").manual_seed(80 + n)
+    q = random_bf16((B, H, n, D), g)
+    k = random_bf16((B, H, cap, D), g)
+    v = random_bf16((B, H, cap, D), g)
+    s = api.from_spec_data(spec)
+    m = api.score_mod(mod.alibi_slopes, mod.softcap)
+    out, lse = api.flex_attention_decode_multi(q.cuda(), k.cuda(), v.cuda(), s, L, m)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    rows = np.arange(L - n, L)
+    for b in range(B):
+        for h in range(H):
+            Qf = np.zeros((L, D))
+            Qf[rows] = q[b, h].double().numpy()
+            ro, rl = oracle.forward_rows(Qf, k[b, h, :L].double().numpy(), v[b, h, :L].double().numpy(),
+                                         _live_spec(spec, L), mod, b, h, rows)
+            assert_close(f64(out[b, h]), ro, f"multi n{n} L{L} b{b} h{h}")
+            assert_lse_close(lse[b, h].double().numpy(), rl, f"multi n{n} L{L} b{b} h{h}")
