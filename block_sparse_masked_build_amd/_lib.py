@@ -24,6 +24,7 @@ STATUS_NAMES = {0: "BSM_OK", 1: "BSM_E_INVALID", 2: "BSM_E_UNSUPPORTED",
 BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX = 1, 2, 4, 8, 16
 BSM_MASK_TABLE = 32
 BSM_MOD_ALIBI, BSM_MOD_SOFTCAP = 1, 2
+BSM_DTYPE_BF16, BSM_DTYPE_F16 = 0, 1
 
 
 class BsmMaskSpec(ctypes.Structure):
@@ -48,7 +49,8 @@ class BsmScoreMod(ctypes.Structure):
 
 class BsmTensor(ctypes.Structure):
     _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
-                ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64)]
+                ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64),
+                ("dtype", ctypes.c_int32)]
 
 
 # Every symbol include/bsm.h declares, with its ctypes signature.

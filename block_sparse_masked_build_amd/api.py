@@ -265,15 +265,18 @@ def build_block_mask(spec: MaskSpec, out: Optional[BlockMask] = None,
     return out
 
 
+_DTYPES = {torch.bfloat16: _lib.BSM_DTYPE_BF16, torch.float16: _lib.BSM_DTYPE_F16}
+
+
 def _tensor(t: torch.Tensor, name: str) -> BsmTensor:
-    if t.dtype != torch.bfloat16:
-        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
     if t.dim() != 4:
         raise ValueError(f"{name} must be [B, H, T, D]")
     if t.stride(3) != 1:
         raise ValueError(f"{name}: last dimension must be contiguous")
     sb, sh, st, _ = t.stride()
-    return BsmTensor(t.data_ptr(), sb, sh, st)
+    return BsmTensor(t.data_ptr(), sb, sh, st, _DTYPES[t.dtype])
 
 
 def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,

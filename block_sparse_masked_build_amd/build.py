@@ -9,6 +9,7 @@ verifier runs on every build.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -22,13 +23,15 @@ LIB_PATH = os.path.join(HERE, "libbsm.so")
 
 # (source, object, extra flags): the attention passes are compiled once per
 # head dimension so that the halves build in parallel
-SOURCES = [("mask_builder.hip", "mask_builder.o", []),
-           ("attn_fwd.hip", "attn_fwd_d64.o", ["-DBSM_HEAD_DIM=64"]),
-           ("attn_fwd.hip", "attn_fwd_d128.o", ["-DBSM_HEAD_DIM=128"]),
-           ("attn_bwd.hip", "attn_bwd_d64.o", ["-DBSM_HEAD_DIM=64"]),
-           ("attn_bwd.hip", "attn_bwd_d128.o", ["-DBSM_HEAD_DIM=128"]),
-           ("attn_decode.hip", "attn_decode.o", []),
-           ("bsm_api.cpp", "bsm_api.o", [])]
+# (source, object, extra flags): the attention sources are compiled once
+# per element type (bf16, fp16) and, for the forward and backward, once per
+# head dimension, so that the pieces build in parallel
+ELEM_FLAGS = {"bf16": [], "f16": ["-DBSM_ELEM_FP16"]}
+# (longest first)
+SOURCES = ([(f"attn_{p}.hip", f"attn_{p}_d{d}_{e}.o", [f"-DBSM_HEAD_DIM={d}", *ef])
+            for p in ("fwd", "bwd") for d in (128, 64) for e, ef in ELEM_FLAGS.items()] +
+           [("attn_decode.hip", f"attn_decode_{e}.o", ef) for e, ef in ELEM_FLAGS.items()] +
+           [("mask_builder.hip", "mask_builder.o", []), ("bsm_api.cpp", "bsm_api.o", [])])
 ARCH = "gfx950"
 
 
@@ -48,10 +51,39 @@ def compile_flags():
             "-I", os.path.join(HERE, "..", "include")]
 
 
+def source_stamp(extra) -> str:
+    """Hash of every source and header the objects are built from, the
+    compiler flags and the object's own flags."""
+    h = hashlib.sha256()
+    for d in (CSRC, os.path.join(HERE, "..", "include")):
+        for name in sorted(os.listdir(d)):
+            path = os.path.join(d, name)
+            if os.path.isfile(path):
+                h.update(name.encode())
+                with open(path, "rb") as f:
+                    h.update(f.read())
+    h.update(" ".join(compile_flags() + list(extra)).encode())
+    return h.hexdigest()
+
+
+def object_dir(obj_name: str) -> str:
+    """Each object is built in a folder of its own, beside its temporary
+    files: the device assembly (*-gfx950.s, with inline assembly marked)
+    that the machine-code checks of the test suite read, and a stamp of
+    the sources it came from."""
+    return os.path.join(BUILD_DIR, os.path.splitext(obj_name)[0])
+
+
 def _compile(entry, verbose: bool) -> str:
     src, obj_name, extra = entry
-    obj = os.path.join(BUILD_DIR, obj_name)
-    cmd = [hipcc(), *compile_flags(), *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    d = object_dir(obj_name)
+    os.makedirs(d, exist_ok=True)
+    obj = os.path.join(d, obj_name)
+    stamp = os.path.join(d, "stamp.txt")
+    if os.path.exists(stamp):
+        os.remove(stamp)
+    cmd = [hipcc(), *compile_flags(), *extra, "-save-temps=obj", "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,6 +93,8 @@ def _compile(entry, verbose: bool) -> str:
         lines = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln]
         if lines:
             print("\n".join(lines), flush=True)
+    with open(stamp, "w") as f:
+        f.write(source_stamp(extra))
     return obj
 
 

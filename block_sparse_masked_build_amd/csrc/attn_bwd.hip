@@ -74,7 +74,7 @@ __device__ inline int step_row0(int t, int nfull, const int32_t *fidx, const int
 // ---------------------------------------------------------------- dQ
 
 struct DqArgs {
-    const __bf16 *kb, *vb;
+    const elem_t *kb, *vb;
     int64_t k_st, v_st;
     const int32_t *fidx, *pidx, *doc;
     int nfull, nt, qpos;  // qpos: absolute position of this lane's query
@@ -88,8 +88,8 @@ struct DqArgs {
 // document ids, addressed by byte address from the shared object.
 template <int D>
 struct DqSmem {
-    __bf16 k[2][kHalf * D];  // fkv swizzle
-    __bf16 v[2][kHalf * D];  // fkv swizzle
+    elem_t k[2][kHalf * D];  // fkv swizzle
+    elem_t v[2][kHalf * D];  // fkv swizzle
     int32_t doc[2][kHalf];
     float red[kThreads / 64];  // per-wave sums of the slope gradient
 };
@@ -106,8 +106,8 @@ struct DqLds {
 // is added to).  Per step, with the score at key key0 + 4 hl + c:
 //   sum g (k - q) = sum g c + (key0 + 4 hl - q) sum g.
 template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE>
-__device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 (&qf)[D / 16],
-                               const bf16x8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
+__device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (&qf)[D / 16],
+                               const elem8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
                                f32x16 (&dq)[D / 32], float &sg) {
     static_assert(!SGRAD || ALIBI, "the slope gradient needs the ALiBi term");
     constexpr bool kMods = ALIBI || SOFTCAP;
@@ -172,7 +172,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
         }
         row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial,
                                            MODE == kTable && a.doc);
-        bf16x8 dsb[2][2];
+        elem8 dsb[2][2];
         float sg_c = 0.0f, sg_s = 0.0f;  // SGRAD: sum ds c and sum ds over the step
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -182,7 +182,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const bf16x8 
                 const float pv = fast_exp2(kMods ? tl - a.l2 : __builtin_fmaf(tl, a.scale_log2, -a.l2));
                 float ds = pv * (dp[kb][r] - a.delta);
                 if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
-                dsb[kb][r >> 3][r & 7] = static_cast<__bf16>(ds);
+                dsb[kb][r >> 3][r & 7] = static_cast<elem_t>(ds);
                 if (SGRAD) {
                     sg_c = __builtin_fmaf(ds, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), sg_c);
                     sg_s += ds;
@@ -229,13 +229,13 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     const int qrow = min(qidx, p.q_len - 1);       // the row this lane loads
     const int qpos = p.q_off + qrow;               // its absolute position
 
-    const __bf16 *qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
-    const __bf16 *gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
-    const __bf16 *obr = static_cast<const __bf16 *>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_st;
+    const elem_t *qb = static_cast<const elem_t *>(p.q) + b * p.q_sb + h * p.q_sh;
+    const elem_t *gb = static_cast<const elem_t *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    const elem_t *obr = static_cast<const elem_t *>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)qrow * p.o_st;
 
     DqArgs a;
-    a.kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
-    a.vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
+    a.kb = static_cast<const elem_t *>(p.k) + b * p.k_sb + h * p.k_sh;
+    a.vb = static_cast<const elem_t *>(p.v) + b * p.v_sb + h * p.v_sh;
     a.k_st = p.k_st;
     a.v_st = p.v_st;
     a.nfull = min(max(rec.nfull, 0), nt);
@@ -267,12 +267,12 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     lds.v = lds_addr(&sm.v[0][0]);
     lds.doc = lds_addr(&sm.doc[0][0]);
 
-    bf16x8 qf[D / 16], gf[D / 16];
+    elem8 qf[D / 16], gf[D / 16];
     u32x4 of[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        qf[st] = *reinterpret_cast<const bf16x8 *>(qb + (int64_t)qrow * p.q_st + st * 16 + hl * 8);
-        gf[st] = *reinterpret_cast<const bf16x8 *>(gb + (int64_t)qrow * p.do_st + st * 16 + hl * 8);
+        qf[st] = *reinterpret_cast<const elem8 *>(qb + (int64_t)qrow * p.q_st + st * 16 + hl * 8);
+        gf[st] = *reinterpret_cast<const elem8 *>(gb + (int64_t)qrow * p.do_st + st * 16 + hl * 8);
         of[st] = *reinterpret_cast<const u32x4 *>(obr + st * 16 + hl * 8);
     }
     // Delta = <dO, out> of this lane's query: each lane half holds half of
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
         for (int st = 0; st < D / 16; ++st)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                acc += __builtin_bit_cast(float, u16_at(of[st], e) << 16) * static_cast<float>(gf[st][e]);
+                acc += elem_bits_to_float(u16_at(of[st], e)) * static_cast<float>(gf[st][e]);
         a.delta = acc + __shfl_xor(acc, 32);
         if (hl == 0 && qidx < p.q_len) {
             p.delta[row_bh] = a.delta;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     // done with them (dS was accumulated without the scale).
     static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "dQ staging fits the K buffers");
     tile_barrier();
-    __bf16 *dqp = static_cast<__bf16 *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)(qidx - n) * p.dq_st;
+    elem_t *dqp = static_cast<elem_t *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)(qidx - n) * p.dq_st;
     store_rows_staged<D>(dqp, p.dq_st, dq, p.scale, lds.k + (uint32_t)(wv * 32 * 2 * D), p.q_len - (qidx - n));
 }
 
@@ -402,7 +402,7 @@ __device__ inline bool make_col_mask(const AttnParams &p, int bm, int kpos, ColM
 }
 
 struct DkdvArgs {
-    const __bf16 *qb, *gb;
+    const elem_t *qb, *gb;
     int64_t q_st, do_st;
     const float *l2, *delta;  // this (batch, head)
     const int32_t *fidx, *pidx, *doc;  // doc: document ids from query 0's position on (NULL: none)
@@ -415,8 +415,8 @@ struct DkdvArgs {
 // One pipeline step of dkdv is one listed 128-query tile.
 template <int D>
 struct DkdvSmem {
-    __bf16 q[2][kTile * D];   // queries (fkv swizzle)
-    __bf16 g[2][kTile * D];   // output gradients (fkv swizzle)
+    elem_t q[2][kTile * D];   // queries (fkv swizzle)
+    elem_t g[2][kTile * D];   // output gradients (fkv swizzle)
     float l2[2][kTile];
     float delta[2][kTile];
     int32_t doc[2][kTile];
@@ -431,8 +431,8 @@ struct DkdvLds {
 
 // Row operands (A of S = Q K^T and dP = dO V^T) of query block b.
 template <int D>
-__device__ inline void dkdv_read_rows(const KvOffsets &oq, const KvOffsets &og, int b, bf16x8 (&rq)[D / 16],
-                                      bf16x8 (&rg)[D / 16]) {
+__device__ inline void dkdv_read_rows(const KvOffsets &oq, const KvOffsets &og, int b, elem8 (&rq)[D / 16],
+                                      elem8 (&rg)[D / 16]) {
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
         rq[st] = read_rows_operand<D>(0, oq, b, st);
@@ -441,8 +441,8 @@ __device__ inline void dkdv_read_rows(const KvOffsets &oq, const KvOffsets &og, 
 }
 
 template <int D>
-__device__ inline void dkdv_sdp(const bf16x8 (&rq)[D / 16], const bf16x8 (&rg)[D / 16], const bf16x8 (&kf)[D / 16],
-                                const bf16x8 (&vf)[D / 16], f32x16 &s, f32x16 &dp) {
+__device__ inline void dkdv_sdp(const elem8 (&rq)[D / 16], const elem8 (&rg)[D / 16], const elem8 (&kf)[D / 16],
+                                const elem8 (&vf)[D / 16], f32x16 &s, f32x16 &dp) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         s[r] = 0.0f;
@@ -462,7 +462,7 @@ __device__ inline void dkdv_sdp(const bf16x8 (&rq)[D / 16], const bf16x8 (&rg)[D
 template <bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
 __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t sl2, uint32_t sdl,
                                   uint32_t sdoc, int b, int q0, const f32x16 &s, const f32x16 &dp,
-                                  bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) {
+                                  elem8 (&pb)[2], elem8 (&dsb)[2]) {
     constexpr bool kMods = ALIBI || SOFTCAP;
     const int hl = (threadIdx.x & 63) >> 5;
     const int qbase = q0 + b * 32 + 4 * hl;
@@ -514,16 +514,16 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
             }
             float ds = pv * (dp[r] - Dl[e]);
             if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
-            pb[r >> 3][r & 7] = static_cast<__bf16>(pv);
-            dsb[r >> 3][r & 7] = static_cast<__bf16>(ds);
+            pb[r >> 3][r & 7] = static_cast<elem_t>(pv);
+            dsb[r >> 3][r & 7] = static_cast<elem_t>(ds);
         }
     }
 }
 
 // Transposed operands (A of dV^T += dO^T P and dK^T += Q^T dS) of block b.
 template <int D>
-__device__ inline void dkdv_read_cols(const KvOffsets &oq, const KvOffsets &og, int b, bf16x8 (&tq)[2][D / 32],
-                                      bf16x8 (&tg)[2][D / 32]) {
+__device__ inline void dkdv_read_cols(const KvOffsets &oq, const KvOffsets &og, int b, elem8 (&tq)[2][D / 32],
+                                      elem8 (&tg)[2][D / 32]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -534,8 +534,8 @@ __device__ inline void dkdv_read_cols(const KvOffsets &oq, const KvOffsets &og, 
 }
 
 template <int D>
-__device__ inline void dkdv_acc(const bf16x8 (&tq)[2][D / 32], const bf16x8 (&tg)[2][D / 32], const bf16x8 (&pb)[2],
-                                const bf16x8 (&dsb)[2], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+__device__ inline void dkdv_acc(const elem8 (&tq)[2][D / 32], const elem8 (&tg)[2][D / 32], const elem8 (&pb)[2],
+                                const elem8 (&dsb)[2], f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -550,12 +550,12 @@ __device__ inline void dkdv_acc(const bf16x8 (&tq)[2][D / 32], const bf16x8 (&tg
 // the gradient arithmetic of block b, and the row operands of block b+2 are
 // read during the dV / dK products of block b.
 template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
-__device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
-                                 const bf16x8 (&vf)[D / 16], const KvOffsets &oq, const KvOffsets &og,
+__device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 16],
+                                 const elem8 (&vf)[D / 16], const KvOffsets &oq, const KvOffsets &og,
                                  uint32_t sl2, uint32_t sdl, uint32_t sdoc, int q0,
                                  f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
     constexpr int NB = kTile / 32;
-    bf16x8 rq[D / 16], rg[D / 16];
+    elem8 rq[D / 16], rg[D / 16];
     f32x16 s[2], dp[2];
     dkdv_read_rows<D>(oq, og, 0, rq, rg);
     dkdv_sdp<D>(rq, rg, kf, vf, s[0], dp[0]);
@@ -564,9 +564,9 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf1
     for (int b = 0; b < NB; ++b) {
         const int cur = b & 1;
         if (b + 1 < NB) dkdv_sdp<D>(rq, rg, kf, vf, s[cur ^ 1], dp[cur ^ 1]);
-        bf16x8 pb[2], dsb[2];
+        elem8 pb[2], dsb[2];
         dkdv_grads<ALIBI, SOFTCAP, CMODE, MASKED>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb);
-        bf16x8 tq[2][D / 32], tg[2][D / 32];
+        elem8 tq[2][D / 32], tg[2][D / 32];
         dkdv_read_cols<D>(oq, og, b, tq, tg);
         if (b + 2 < NB) dkdv_read_rows<D>(oq, og, b + 2, rq, rg);
         dkdv_acc<D>(tq, tg, pb, dsb, dk, dv);
@@ -575,8 +575,8 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const bf1
 }
 
 template <int D, bool ALIBI, bool SOFTCAP, int CMODE>
-__device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const bf16x8 (&kf)[D / 16],
-                                 const bf16x8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
+__device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 16],
+                                 const elem8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
                                  int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
     constexpr uint32_t kTB = DkdvLds<D>::kTileBytes, kWB = kTile * 4;
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
@@ -637,14 +637,14 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     const int kidx = j * kTile + wv * 32 + n;    // key (past KV_LEN on a cut-short tile)
     const int kpos = min(kidx, p.T - 1);         // the key this lane loads
 
-    const __bf16 *kb = static_cast<const __bf16 *>(p.k) + b * p.k_sb + h * p.k_sh;
-    const __bf16 *vb = static_cast<const __bf16 *>(p.v) + b * p.v_sb + h * p.v_sh;
+    const elem_t *kb = static_cast<const elem_t *>(p.k) + b * p.k_sb + h * p.k_sh;
+    const elem_t *vb = static_cast<const elem_t *>(p.v) + b * p.v_sb + h * p.v_sh;
     const int bm = p.mask_b == 1 ? 0 : b;
     const int64_t col = (int64_t)bm * nt + j;
 
     DkdvArgs a;
-    a.qb = static_cast<const __bf16 *>(p.q) + b * p.q_sb + h * p.q_sh;
-    a.gb = static_cast<const __bf16 *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    a.qb = static_cast<const elem_t *>(p.q) + b * p.q_sb + h * p.q_sh;
+    a.gb = static_cast<const elem_t *>(p.dout) + b * p.do_sb + h * p.do_sh;
     a.q_st = p.q_st;
     a.do_st = p.do_st;
     a.l2 = p.lse2 + ((int64_t)b * p.H + h) * p.q_len;
@@ -683,11 +683,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     KvOffsets off;
     kv_offsets<D>(off);
 
-    bf16x8 kf[D / 16], vf[D / 16];
+    elem8 kf[D / 16], vf[D / 16];
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-        kf[st] = *reinterpret_cast<const bf16x8 *>(kb + (int64_t)kpos * p.k_st + st * 16 + hl * 8);
-        vf[st] = *reinterpret_cast<const bf16x8 *>(vb + (int64_t)kpos * p.v_st + st * 16 + hl * 8);
+        kf[st] = *reinterpret_cast<const elem8 *>(kb + (int64_t)kpos * p.k_st + st * 16 + hl * 8);
+        vf[st] = *reinterpret_cast<const elem8 *>(vb + (int64_t)kpos * p.v_st + st * 16 + hl * 8);
     }
     f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -715,8 +715,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     tile_barrier();
     const uint32_t slice = (uint32_t)(wv * 32 * 2 * D);
     const int k0w = kidx - n;  // the wave's first key
-    __bf16 *dkp = static_cast<__bf16 *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)k0w * p.dk_st;
-    __bf16 *dvp = static_cast<__bf16 *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)k0w * p.dv_st;
+    elem_t *dkp = static_cast<elem_t *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)k0w * p.dk_st;
+    elem_t *dvp = static_cast<elem_t *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)k0w * p.dv_st;
     store_rows_staged<D>(dkp, p.dk_st, dk, p.scale, lds.q + slice, p.T - k0w);
     store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice, p.T - k0w);
 }
@@ -784,10 +784,10 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
 // The build compiles this source once per head dimension (BSM_HEAD_DIM),
 // so that the two halves compile in parallel; without it both are built.
 #if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 64
-hipError_t launch_attn_bwd_d64(const AttnParams &p, hipStream_t stream) { return launch_d<64>(p, stream); }
+hipError_t BSM_ELEM_FN(launch_attn_bwd_d64)(const AttnParams &p, hipStream_t stream) { return launch_d<64>(p, stream); }
 #endif
 #if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 128
-hipError_t launch_attn_bwd_d128(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
+hipError_t BSM_ELEM_FN(launch_attn_bwd_d128)(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
 #endif
 
 }  // namespace bsm

@@ -5,8 +5,23 @@
 
 namespace bsm {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// Element type of q, k, v, out and the gradients, and of the matrix-core
+// operands formed from them: bf16, or fp16 when the source is compiled with
+// BSM_ELEM_FP16.  Each attention source is compiled once per type; the
+// launchers it exports carry the type in their names (BSM_ELEM_FN).
+#ifdef BSM_ELEM_FP16
+typedef _Float16 elem_t;
+#define BSM_ELEM_SUFFIX f16
+#else
+typedef __bf16 elem_t;
+#define BSM_ELEM_SUFFIX bf16
+#endif
+#define BSM_CAT2(a, b) a##_##b
+#define BSM_CAT(a, b) BSM_CAT2(a, b)
+#define BSM_ELEM_FN(name) BSM_CAT(name, BSM_ELEM_SUFFIX)
+
+typedef elem_t elem8 __attribute__((ext_vector_type(8)));
+typedef elem_t elem4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -16,12 +31,26 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// D[32x32] += A[32x16] * B[16x32] on the bf16 matrix cores.
+// D[32x32] += A[32x16] * B[16x32] on the matrix cores (bf16 or fp16
+// operands, fp32 accumulation).
 // Operand layout (wave64): A row i, k-slot kk sits in lane i + 32*(kk/8),
 // element kk%8; B column j, k-slot kk in lane j + 32*(kk/8), element kk%8;
 // D row i, column j in lane j + 32*((i/4)%2), register (i%4) + 4*(i/8).
-__device__ inline f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+__device__ inline f32x16 mfma32(const elem8 &a, const elem8 &b, const f32x16 &c) {
+#ifdef BSM_ELEM_FP16
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+#else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+#endif
+}
+
+// An element given by its 16 bits, as fp32.
+__device__ inline float elem_bits_to_float(uint32_t bits) {
+#ifdef BSM_ELEM_FP16
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+#else
+    return __builtin_bit_cast(float, bits << 16);
+#endif
 }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -56,9 +85,9 @@ __device__ inline float mod_apply(float s, float b, const ModK &k) {
     return __builtin_fmaf(-k.c2, fast_rcp(fast_exp2(u) + 1.0f), k.c1);
 }
 
-__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = static_cast<__bf16>(lo);
-    const __bf16 b = static_cast<__bf16>(hi);
+__device__ inline uint32_t pack_elem2(float lo, float hi) {
+    const elem_t a = static_cast<elem_t>(lo);
+    const elem_t b = static_cast<elem_t>(hi);
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
@@ -224,7 +253,7 @@ __device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadId
 // masked by the caller.  Both forms address a wave-uniform base plus a
 // per-lane offset below kRowsPerInstr rows.
 template <int D, int SWZ, int ROWS>
-__device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_row0, int64_t row_stride,
+__device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const elem_t *g_row0, int64_t row_stride,
                                             int nvalid = ROWS) {
     using L = TileLayout<D>;
     constexpr int kRowsPerInstr = 1024 / L::kRowBytes;
@@ -268,7 +297,7 @@ __device__ inline void issue_tile_to_lds_at(uint32_t lds_tile, const __bf16 *g_r
 }
 
 template <int D, int SWZ, int ROWS>
-__device__ inline void issue_tile_to_lds(__bf16 *lds_tile, const __bf16 *g_row0, int64_t row_stride,
+__device__ inline void issue_tile_to_lds(elem_t *lds_tile, const elem_t *g_row0, int64_t row_stride,
                                          int nvalid = ROWS) {
     issue_tile_to_lds_at<D, SWZ, ROWS>(lds_addr(lds_tile), g_row0, row_stride, nvalid);
 }
@@ -319,7 +348,7 @@ __device__ inline void wait_vmcnt() {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-__device__ inline i16x4 ds_read_tr16(const __bf16 *p) {
+__device__ inline i16x4 ds_read_tr16(const elem_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(p));
 }
 
@@ -401,19 +430,19 @@ __device__ inline void kv_offsets(KvOffsets &off) {
 // A operand [32 rows][16 columns] at row block rb, column step st of an fkv
 // tile at LDS byte address `tile` (lane = row, 8 consecutive columns).
 template <int D>
-__device__ inline bf16x8 read_rows_operand(uint32_t tile, const KvOffsets &off, int rb, int st) {
-    return lds_load<bf16x8>(tile + rb * 32 * TileLayout<D>::kRowBytes + (off.row ^ (st << 5)));
+__device__ inline elem8 read_rows_operand(uint32_t tile, const KvOffsets &off, int rb, int st) {
+    return lds_load<elem8>(tile + rb * 32 * TileLayout<D>::kRowBytes + (off.row ^ (st << 5)));
 }
 
 // A operand [32 columns][16 rows] of an fkv tile transposed: columns
 // 32 db + lane%32, rows 16 g16 + {4 hl..4 hl+3, 8+4 hl..8+4 hl+3} with hl the
 // lane half (the k-slot order of a 32x32 score block's registers).
 template <int D>
-__device__ inline bf16x8 read_cols_operand(uint32_t tile, const KvOffsets &off, int g16, int db) {
+__device__ inline elem8 read_cols_operand(uint32_t tile, const KvOffsets &off, int g16, int db) {
     const uint32_t base = tile + g16 * 16 * TileLayout<D>::kRowBytes;
     const i16x4 lo = ds_read_tr16_at(base + (off.tr ^ (db << 6)));
     const i16x4 hi = ds_read_tr16_at(base + 8 * TileLayout<D>::kRowBytes + (off.tr ^ ((db << 6) | 32)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(elem8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ inline int clamp_tile(int j, int nt) { return j < 0 ? 0 : (j >= nt ? nt - 1 : j); }
@@ -436,7 +465,7 @@ __device__ inline uint32_t u16_at(const u32x4 &x, int i) {
 // 16-byte vector each, columns c0..c0+7) into a [column][row] LDS array with
 // row stride `ld`: column c gets the 4 values as one 8-byte store at the
 // permuted slot vt_slot(r0) (r0 a multiple of 4).
-__device__ inline void store_transposed_4x8(__bf16 *dst, int ld, int r0, int c0, const u32x4 (&v)[4]) {
+__device__ inline void store_transposed_4x8(elem_t *dst, int ld, int r0, int c0, const u32x4 (&v)[4]) {
     const int slot = vt_slot(r0);
 #pragma unroll
     for (int dd = 0; dd < 8; ++dd) {
@@ -558,7 +587,7 @@ __device__ inline float keep_if_bit(float x, uint32_t bits, int j) {
 // rows below nrows are stored (the block may run past the end of a length
 // that is not a multiple of 128).
 template <int D>
-__device__ __attribute__((always_inline)) inline void store_rows_staged(__bf16 *dst, int64_t ld,
+__device__ __attribute__((always_inline)) inline void store_rows_staged(elem_t *dst, int64_t ld,
                                                                         const f32x16 (&acc)[D / 32], float mul,
                                                                         uint32_t stage, int nrows = 32) {
     constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kRowsPerRead = 64 / kChunks;
@@ -568,8 +597,8 @@ __device__ __attribute__((always_inline)) inline void store_rows_staged(__bf16 *
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             u32x2 w;  // columns 32 db + 8 g + 4 hl + 0..3: chunk 4 db + g, half hl
-            w.x = pack_bf16x2(acc[db][g * 4 + 0] * mul, acc[db][g * 4 + 1] * mul);
-            w.y = pack_bf16x2(acc[db][g * 4 + 2] * mul, acc[db][g * 4 + 3] * mul);
+            w.x = pack_elem2(acc[db][g * 4 + 0] * mul, acc[db][g * 4 + 1] * mul);
+            w.y = pack_elem2(acc[db][g * 4 + 2] * mul, acc[db][g * 4 + 3] * mul);
             lds_store<u32x2>(stage + n * kRowBytes + (((db * 4 + g) ^ (n % kChunks)) * 16) + hl * 8, w);
         }
     }

@@ -42,11 +42,11 @@
 namespace bsm {
 namespace {
 
-typedef __bf16 dec_bf16x8 __attribute__((ext_vector_type(8)));
+typedef elem_t dec_elem8 __attribute__((ext_vector_type(8)));
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kSlotTiles = 8;                      // 128-key tiles per workgroup
+constexpr int kSlotTiles = kDecodeSlotTiles;       // 128-key tiles per workgroup
 constexpr int kWaveTiles = kSlotTiles / kDecWaves; // 2 per wave
 
 struct DecodeParams {
@@ -62,10 +62,10 @@ struct DecodeParams {
     const float *alibi_slopes;   // [H] or NULL
     // block mask rows (NULL kv_num: no block mask)
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
-    const __bf16 *q; int64_t q_sb, q_sh;
-    const __bf16 *k; int64_t k_sb, k_sh, k_st;
-    const __bf16 *v; int64_t v_sb, v_sh, v_st;
-    __bf16 *o; int64_t o_sb, o_sh;
+    const elem_t *q; int64_t q_sb, q_sh;
+    const elem_t *k; int64_t k_sb, k_sh, k_st;
+    const elem_t *v; int64_t v_sb, v_sh, v_st;
+    elem_t *o; int64_t o_sb, o_sh;
     float *lse;                  // [B, H]
     float *part_o;               // [B*H, nslot, D]
     float *part_ml;              // [B*H, nslot, 2]: running max (log2 domain) and sum
@@ -160,12 +160,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     const float slope = ALIBI ? P.alibi_slopes[h] : 0.0f;
     const ModK mk = mod_k<SOFTCAP>(P.scale, slope, SOFTCAP ? P.softcap : 1.0f);
 
-    const __bf16 *qrow = P.q + b * P.q_sb + h * P.q_sh;
+    const elem_t *qrow = P.q + b * P.q_sb + h * P.q_sh;
     for (int d = threadIdx.x; d < D; d += kDecThreads) sq[d] = static_cast<float>(qrow[d]);
     __syncthreads();
 
-    const __bf16 *kb = P.k + b * P.k_sb + h * P.k_sh;
-    const __bf16 *vb = P.v + b * P.v_sb + h * P.v_sh;
+    const elem_t *kb = P.k + b * P.k_sb + h * P.k_sh;
+    const elem_t *vb = P.v + b * P.v_sb + h * P.v_sh;
     float m = -INFINITY, l = 0.0f;
     float o[kDimsPerLane];
 #pragma unroll
@@ -189,11 +189,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         const int kv = key0 + lane;
         float t = -INFINITY;
         if (kv < L && dec_visible(P, bm, p, kv, window, docq)) {
-            const __bf16 *krow = kb + (int64_t)kv * P.k_st;
+            const elem_t *krow = kb + (int64_t)kv * P.k_st;
             float acc = 0.0f;
 #pragma unroll
             for (int d0 = 0; d0 < D; d0 += 8) {
-                const dec_bf16x8 kk = *reinterpret_cast<const dec_bf16x8 *>(krow + d0);
+                const dec_elem8 kk = *reinterpret_cast<const dec_elem8 *>(krow + d0);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(sq[d0 + e], static_cast<float>(kk[e]), acc);
             }
@@ -220,14 +220,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
             // issued together (keys past the live length have p = 0 and read
             // a row inside the cache instead)
             const int nk = min(64, L - key0);
-            const __bf16 *vbase = vb + lane * kDimsPerLane;
+            const elem_t *vbase = vb + lane * kDimsPerLane;
 #pragma unroll 1
             for (int j0 = 0; j0 < 64; j0 += 16) {
                 float vv[16][kDimsPerLane];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = min(key0 + j0 + j, L - 1);
-                    const __bf16 *vrow = vbase + (int64_t)key * P.v_st;
+                    const elem_t *vrow = vbase + (int64_t)key * P.v_st;
 #pragma unroll
                     for (int i = 0; i < kDimsPerLane; ++i) vv[j][i] = static_cast<float>(vrow[i]);
                 }
@@ -289,9 +289,9 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams P) {
         for (int i = 0; i < kDimsPerLane; ++i) acc[i] += P.part_o[slot * D + lane * kDimsPerLane + i] * f;
     }
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-    __bf16 *orow = P.o + b * P.o_sb + h * P.o_sh;
+    elem_t *orow = P.o + b * P.o_sb + h * P.o_sh;
 #pragma unroll
-    for (int i = 0; i < kDimsPerLane; ++i) orow[lane * kDimsPerLane + i] = static_cast<__bf16>(acc[i] * inv);
+    for (int i = 0; i < kDimsPerLane; ++i) orow[lane * kDimsPerLane + i] = static_cast<elem_t>(acc[i] * inv);
     if (lane == 0) P.lse[bh] = Ls > 0.0f ? (M + log2f(Ls)) * kLn2 : -INFINITY;
 }
 
@@ -321,9 +321,7 @@ hipError_t launch_d(const DecodeParams &P, uint32_t mod_flags, hipStream_t strea
 
 }  // namespace
 
-int decode_slots(int capacity) { return (capacity + kSlotTiles * kTile - 1) / (kSlotTiles * kTile); }
-
-hipError_t launch_attn_decode(const DecodeLaunch &d, float *part, hipStream_t stream) {
+hipError_t BSM_ELEM_FN(launch_attn_decode)(const DecodeLaunch &d, float *part, hipStream_t stream) {
     const AttnParams &a = d.a;
     DecodeParams P{};
     P.B = a.B;
@@ -348,18 +346,18 @@ hipError_t launch_attn_decode(const DecodeLaunch &d, float *part, hipStream_t st
     P.kv_idx = a.kv_idx;
     P.full_kv_num = a.full_kv_num;
     P.full_kv_idx = a.full_kv_idx;
-    P.q = static_cast<const __bf16 *>(a.q);
+    P.q = static_cast<const elem_t *>(a.q);
     P.q_sb = a.q_sb;
     P.q_sh = a.q_sh;
-    P.k = static_cast<const __bf16 *>(a.k);
+    P.k = static_cast<const elem_t *>(a.k);
     P.k_sb = a.k_sb;
     P.k_sh = a.k_sh;
     P.k_st = a.k_st;
-    P.v = static_cast<const __bf16 *>(a.v);
+    P.v = static_cast<const elem_t *>(a.v);
     P.v_sb = a.v_sb;
     P.v_sh = a.v_sh;
     P.v_st = a.v_st;
-    P.o = static_cast<__bf16 *>(a.o);
+    P.o = static_cast<elem_t *>(a.o);
     P.o_sb = a.o_sb;
     P.o_sh = a.o_sh;
     P.lse = a.lse;

@@ -96,7 +96,7 @@ __device__ inline int v_operand_offset(const OperandOffsets<D> &off, int u, int 
 // S^T = K Q^T for one half tile: lane (query n, half hl) gets, for key block
 // kb (32 keys), the 16 scores of keys 32 kb + 8 (r/4) + 4 hl + r%4.
 template <int D>
-__device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, const bf16x8 (&qf)[D / 16],
+__device__ inline void fwd_qk(const elem_t *sk, const OperandOffsets<D> &off, const elem8 (&qf)[D / 16],
                               f32x16 (&s)[2]) {
     const char *kbytes = reinterpret_cast<const char *>(sk);
 #pragma unroll
@@ -107,7 +107,7 @@ __device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, co
     for (int st = 0; st < D / 16; ++st) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbytes + kb * 32 * TileLayout<D>::kRowBytes +
+            const elem8 a = *reinterpret_cast<const elem8 *>(kbytes + kb * 32 * TileLayout<D>::kRowBytes +
                                                                 k_operand_offset(off, st));
             s[kb] = mfma32(a, qf[st], s[kb]);
         }
@@ -116,7 +116,7 @@ __device__ inline void fwd_qk(const __bf16 *sk, const OperandOffsets<D> &off, co
 
 // p = 2^(s c - m) as bf16 (the B operand of the PV products), summed into l
 // in fp32 before rounding (so lse keeps fp32 accuracy).
-__device__ inline void fwd_exp(const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float &l, float c_mul, float m_use) {
+__device__ inline void fwd_exp(const f32x16 (&s)[2], elem8 (&pb)[2][2], float &l, float c_mul, float m_use) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -125,12 +125,12 @@ __device__ inline void fwd_exp(const f32x16 (&s)[2], bf16x8 (&pb)[2][2], float &
             for (int e = 0; e < 8; ++e) {
                 const float pv = fast_exp2(__builtin_fmaf(s[kb][s2 * 8 + e], c_mul, -m_use));
                 l += pv;
-                pb[kb][s2][e] = static_cast<__bf16>(pv);
+                pb[kb][s2][e] = static_cast<elem_t>(pv);
             }
 }
 
 template <int D>
-__device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, const bf16x8 (&pb)[2][2],
+__device__ inline void fwd_pv(const elem_t *sv, const OperandOffsets<D> &off, const elem8 (&pb)[2][2],
                               f32x16 (&o)[D / 32]) {
     const char *vbytes = reinterpret_cast<const char *>(sv);
 #pragma unroll
@@ -140,9 +140,9 @@ __device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, co
             const int rowbase = (kb * 32 + s2 * 16) * TileLayout<D>::kRowBytes;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const i16x4 lo = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + v_operand_offset(off, 0, db)));
-                const i16x4 hi = ds_read_tr16(reinterpret_cast<const __bf16 *>(vbytes + rowbase + v_operand_offset(off, 1, db)));
-                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                const i16x4 lo = ds_read_tr16(reinterpret_cast<const elem_t *>(vbytes + rowbase + v_operand_offset(off, 0, db)));
+                const i16x4 hi = ds_read_tr16(reinterpret_cast<const elem_t *>(vbytes + rowbase + v_operand_offset(off, 1, db)));
+                const elem8 a = __builtin_bit_cast(elem8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 o[db] = mfma32(a, pb[kb][s2], o[db]);
             }
         }
@@ -159,7 +159,7 @@ __device__ inline void fwd_pv(const __bf16 *sv, const OperandOffsets<D> &off, co
 
 // Wave-uniform values of the item being worked on.
 struct FwdArgs {
-    const __bf16 *kb, *vb;
+    const elem_t *kb, *vb;
     const int32_t *doc, *fidx, *pidx;
     int b, h, bm, row;
     int nfull, ntiles, nt, first;
@@ -176,8 +176,8 @@ __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &re
     a.bm = packed / p.nqt;
     a.row = packed - a.bm * p.nqt;
     head_of(p, rem, a.bm, a.b, a.h);
-    a.kb = static_cast<const __bf16 *>(p.k) + a.b * p.k_sb + a.h * p.k_sh;
-    a.vb = static_cast<const __bf16 *>(p.v) + a.b * p.v_sb + a.h * p.v_sh;
+    a.kb = static_cast<const elem_t *>(p.k) + a.b * p.k_sb + a.h * p.k_sh;
+    a.vb = static_cast<const elem_t *>(p.v) + a.b * p.v_sb + a.h * p.v_sh;
     a.fidx = p.full_kv_idx + (int64_t)packed * nt;
     a.pidx = p.kv_idx + (int64_t)packed * nt;
     a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)a.bm * p.npos : nullptr;
@@ -259,8 +259,8 @@ __device__ inline int finish_row_mask(const AttnParams &p, int qpos, const RowLo
 // keys' document ids.
 template <int D>
 struct FwdSmem {
-    __bf16 k[2][kHalf * D];  // keys, rows swizzled by fk
-    __bf16 v[2][kHalf * D];  // values, rows swizzled by fv
+    elem_t k[2][kHalf * D];  // keys, rows swizzled by fk
+    elem_t v[2][kHalf * D];  // values, rows swizzled by fv
     int32_t doc[2][kHalf];   // document ids of the keys
 };
 
@@ -269,7 +269,7 @@ struct FwdSmem {
 // query rows, the tile list and the row data.  Every item has an even
 // number of steps, so each item starts on buffer 0.
 template <int D>
-__device__ __attribute__((always_inline)) inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, bf16x8 (&qf)[D / 16],
+__device__ __attribute__((always_inline)) inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, elem8 (&qf)[D / 16],
                                   TileList &tl, RowLoad &rl) {
     if (a.ntiles > 0) {
         // rows past KV_LEN (document ids: past the positions) repeat the last one
@@ -284,10 +284,10 @@ __device__ __attribute__((always_inline)) inline void item_start(const AttnParam
                                            p.T - k0 - kHalf);
     }
     const int hl = (threadIdx.x & 63) >> 5;
-    const __bf16 *qrow = static_cast<const __bf16 *>(p.q) + a.b * p.q_sb + a.h * p.q_sh +
+    const elem_t *qrow = static_cast<const elem_t *>(p.q) + a.b * p.q_sb + a.h * p.q_sh +
                          (int64_t)min(a.qidx, p.q_len - 1) * p.q_st;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const bf16x8 *>(qrow + st * 16 + hl * 8);
+    for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const elem8 *>(qrow + st * 16 + hl * 8);
     const int lane = threadIdx.x & 63;
     tl.lo = list_entry(a, lane);
     tl.hi = a.ntiles > 64 ? list_entry(a, 64 + lane) : 0;
@@ -313,7 +313,7 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
     const float l_tot = l + __shfl_xor(l, 32);
     const float inv = l_tot > 0.0f ? fast_rcp(l_tot) : 0.0f;
     const int q0w = a.row * kTile + wv * 32;  // the wave's first query index
-    __bf16 *ob = static_cast<__bf16 *>(p.o) + a.b * p.o_sb + a.h * p.o_sh + (int64_t)q0w * p.o_st;
+    elem_t *ob = static_cast<elem_t *>(p.o) + a.b * p.o_sb + a.h * p.o_sh + (int64_t)q0w * p.o_st;
     store_rows_staged<D>(ob, p.o_st, o, inv, stage + (uint32_t)(wv * 32 * 2 * D), p.q_len - q0w);
     if (hl == 0 && a.qidx < p.q_len)
         p.lse[((int64_t)a.b * p.H + a.h) * p.q_len + a.qidx] =
@@ -342,7 +342,7 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
 // which no wave reads during the last step.
 template <int D, bool ALIBI, bool SOFTCAP, int MODE>
 __device__ __attribute__((always_inline)) inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
-                                const bf16x8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
+                                const elem8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
                                 f32x16 (&o)[D / 32], float &m, float &l) {
     constexpr bool kMods = ALIBI || SOFTCAP;
     static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "output staging fits the K buffers");
@@ -416,7 +416,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
         if (decltype(first_step)::value) reset();
         const float m_use = settle(mx);
 
-        bf16x8 pb[2][2];
+        elem8 pb[2][2];
         fwd_qk<D>(sm.k[(t + 1) & 1], offt, qf, sn);
         fwd_exp(sc, pb, l, c_mul, m_use);
         fwd_pv<D>(sm.v[t & 1], offt, pb, o);
@@ -454,7 +454,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     wait_vmcnt<0>();
     tile_barrier();
     const float m_use = settle(mx);
-    bf16x8 pb[2][2];
+    elem8 pb[2][2];
     fwd_exp(sa, pb, l, c_mul, m_use);
     fwd_pv<D>(sm.v[1], off, pb, o);
     store_item<D>(p, a, o, m, l, lds_addr(sm.k[0]));
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd
     item_args<ALIBI, SOFTCAP>(p, rem, load_rec(p.kv_order, e), cur);
     OperandOffsets<D> off;
     operand_offsets<D>(off);
-    bf16x8 qf[D / 16];
+    elem8 qf[D / 16];
     TileList tl;
     RowLoad rl;
     item_start<D>(p, sm, cur, qf, tl, rl);
@@ -516,10 +516,10 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
 // The build compiles this source once per head dimension (BSM_HEAD_DIM),
 // so that the two halves compile in parallel; without it both are built.
 #if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 64
-hipError_t launch_attn_fwd_d64(const AttnParams &p, hipStream_t stream) { return launch_d<64>(p, stream); }
+hipError_t BSM_ELEM_FN(launch_attn_fwd_d64)(const AttnParams &p, hipStream_t stream) { return launch_d<64>(p, stream); }
 #endif
 #if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 128
-hipError_t launch_attn_fwd_d128(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
+hipError_t BSM_ELEM_FN(launch_attn_fwd_d128)(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
 #endif
 
 }  // namespace bsm

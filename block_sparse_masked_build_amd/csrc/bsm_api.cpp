@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 
@@ -115,6 +116,8 @@ bsm_status check_block_mask(const bsm_block_mask *bm, bool need_transposed, cons
 
 bsm_status check_tensor(const bsm_tensor *t, const char *name) {
     if (!t || !t->ptr) return fail(BSM_E_INVALID, "tensor %s is NULL", name);
+    if (t->dtype != BSM_DTYPE_BF16 && t->dtype != BSM_DTYPE_F16)
+        return fail(BSM_E_INVALID, "tensor %s has unknown dtype %d", name, t->dtype);
     if (reinterpret_cast<uintptr_t>(t->ptr) % 16 != 0)
         return fail(BSM_E_INVALID, "tensor %s must be 16-byte aligned", name);
     if (t->stride_b % 8 || t->stride_h % 8 || t->stride_t % 8)
@@ -149,6 +152,31 @@ bsm_status check_attn_common(int32_t B, int32_t H, int32_t T, int32_t D, const b
     const MaskDims m = mask_dims(spec);
     if ((int64_t)B * H * (m.nqt > m.nkt ? m.nqt : m.nkt) > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
     return check_mod(mod);
+}
+
+// Every tensor of a call has the type of the first (already checked).
+bsm_status check_same_dtype(std::initializer_list<const bsm_tensor *> ts) {
+    const int32_t dt = (*ts.begin())->dtype;
+    for (const bsm_tensor *t : ts)
+        if (t->dtype != dt) return fail(BSM_E_INVALID, "tensors of one call must share one dtype");
+    return BSM_OK;
+}
+
+using AttnLauncher = hipError_t (*)(const bsm::AttnParams &, hipStream_t);
+
+AttnLauncher fwd_launcher(int D, int32_t dtype) {
+    if (dtype == BSM_DTYPE_F16) return D == 64 ? bsm::launch_attn_fwd_d64_f16 : bsm::launch_attn_fwd_d128_f16;
+    return D == 64 ? bsm::launch_attn_fwd_d64_bf16 : bsm::launch_attn_fwd_d128_bf16;
+}
+
+AttnLauncher bwd_launcher(int D, int32_t dtype) {
+    if (dtype == BSM_DTYPE_F16) return D == 64 ? bsm::launch_attn_bwd_d64_f16 : bsm::launch_attn_bwd_d128_f16;
+    return D == 64 ? bsm::launch_attn_bwd_d64_bf16 : bsm::launch_attn_bwd_d128_bf16;
+}
+
+hipError_t launch_decode(const bsm::DecodeLaunch &d, float *part, hipStream_t stream) {
+    return d.dtype == BSM_DTYPE_F16 ? bsm::launch_attn_decode_f16(d, part, stream)
+                                    : bsm::launch_attn_decode_bf16(d, part, stream);
 }
 
 void fill_tensor(const bsm_tensor *t, const void *&ptr, int64_t &sb, int64_t &sh, int64_t &st) {
@@ -252,8 +280,10 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;
     if ((st = check_tensor(v, "v")) != BSM_OK) return st;
     if ((st = check_tensor(out, "out")) != BSM_OK) return st;
+    if ((st = check_same_dtype({q, k, v, out})) != BSM_OK) return st;
     if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
     if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
+    d.dtype = q->dtype;
     bsm::AttnParams &p = d.a;
     p = bsm::AttnParams{};
     p.B = B;
@@ -400,6 +430,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;
     if ((st = check_tensor(v, "v")) != BSM_OK) return st;
     if ((st = check_tensor(out, "out")) != BSM_OK) return st;
+    if ((st = check_same_dtype({q, k, v, out})) != BSM_OK) return st;
     if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
     if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
     bsm::AttnParams p;
@@ -411,7 +442,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     fill_tensor(out, optr, p.o_sb, p.o_sh, p.o_st);
     p.o = const_cast<void *>(optr);
     p.lse = lse;
-    return hip_status((D == 64 ? bsm::launch_attn_fwd_d64 : bsm::launch_attn_fwd_d128)(p, static_cast<hipStream_t>(stream)),
+    return hip_status(fwd_launcher(D, q->dtype)(p, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_fwd launch");
 }
 
@@ -438,6 +469,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     if ((st = check_tensor(dq, "dq")) != BSM_OK) return st;
     if ((st = check_tensor(dk, "dk")) != BSM_OK) return st;
     if ((st = check_tensor(dv, "dv")) != BSM_OK) return st;
+    if ((st = check_same_dtype({q, k, v, out, dout, dq, dk, dv})) != BSM_OK) return st;
     if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
     if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
     const int32_t Q = mask_dims(spec).q_len;
@@ -468,7 +500,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     p.dslope_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                               2 * align256((size_t)B * H * Q * sizeof(float)));
     p.dslopes = (mod && (mod->flags & BSM_MOD_ALIBI)) ? mod->alibi_slopes_grad : nullptr;
-    return hip_status((D == 64 ? bsm::launch_attn_bwd_d64 : bsm::launch_attn_bwd_d128)(p, static_cast<hipStream_t>(stream)),
+    return hip_status(bwd_launcher(D, q->dtype)(p, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_bwd launch");
 }
 
@@ -492,7 +524,7 @@ bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int
                     workspace ? "" : " (NULL)");
     if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
         return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
-    return hip_status(bsm::launch_attn_decode(d, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
+    return hip_status(launch_decode(d, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_decode launch");
 }
 
@@ -517,7 +549,7 @@ bsm_status bsm_flex_attention_decode_static(int32_t B, int32_t H, int32_t capaci
     if ((st = scratch_address(stream, &ptr)) != BSM_OK) return st;
     // Every slot of the partials is written before the combine reads it, so
     // nothing in the scratch needs clearing.
-    return hip_status(bsm::launch_attn_decode(d, static_cast<float *>(ptr), static_cast<hipStream_t>(stream)),
+    return hip_status(launch_decode(d, static_cast<float *>(ptr), static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_decode_static launch");
 }
 

@@ -66,7 +66,7 @@ struct AttnParams {
     const int32_t *q_num, *q_idx, *full_q_num, *full_q_idx;
     const int32_t *doc_range;   // [mask_b, npos, 2] (first, last) of each position's document, or NULL
     const int32_t *kv_order, *q_order;  // work orders [mask_b * nqt, 4] / [mask_b * nt, 4]: longest first
-    // tensors (bf16, strides in elements)
+    // tensors (bf16 or fp16 by the launcher called, strides in elements)
     const void *q; int64_t q_sb, q_sh, q_st;
     const void *k; int64_t k_sb, k_sh, k_st;
     const void *v; int64_t v_sb, v_sh, v_st;
@@ -87,20 +87,31 @@ struct AttnParams {
 };
 
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);
-hipError_t launch_attn_fwd_d64(const AttnParams &p, hipStream_t stream);
-hipError_t launch_attn_fwd_d128(const AttnParams &p, hipStream_t stream);
-hipError_t launch_attn_bwd_d64(const AttnParams &p, hipStream_t stream);
-hipError_t launch_attn_bwd_d128(const AttnParams &p, hipStream_t stream);
+// Attention launchers, one per head dimension and element type (bf16 / f16).
+hipError_t launch_attn_fwd_d64_bf16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_fwd_d128_bf16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d64_bf16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d128_bf16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_fwd_d64_f16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_fwd_d128_f16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d64_f16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d128_f16(const AttnParams &p, hipStream_t stream);
 // Decoding step: one query per (b, h) at the last live position of a cache
 // of p.T (capacity) positions; the block-mask row arrays of `a` are the
 // optional block mask (kv_num NULL: none).  part = B*H*slots*(D + 2) floats.
 struct DecodeLaunch {
     AttnParams a;
     int D;
+    int32_t dtype;           // BSM_DTYPE_*
     const int32_t *kv_len;   // device live length(s)
     int32_t kv_len_stride;   // 0: one value; 1: one per batch element
 };
-int decode_slots(int capacity);
-hipError_t launch_attn_decode(const DecodeLaunch &d, float *part, hipStream_t stream);
+// A decoding workgroup ("slot") covers kDecodeSlotTiles 128-key tiles.
+constexpr int kDecodeSlotTiles = 8;
+inline int decode_slots(int capacity) {
+    return (capacity + kDecodeSlotTiles * kTile - 1) / (kDecodeSlotTiles * kTile);
+}
+hipError_t launch_attn_decode_bf16(const DecodeLaunch &d, float *part, hipStream_t stream);
+hipError_t launch_attn_decode_f16(const DecodeLaunch &d, float *part, hipStream_t stream);
 
 }  // namespace bsm

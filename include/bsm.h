@@ -30,9 +30,14 @@
  *    cache.  Tiles are 128 x 128: QT = ceil(Q_LEN / 128) query tiles and
  *    KT = ceil(KV_LEN / 128) key tiles; a tile cut short by a length that is
  *    not a multiple of 128 is never full.
- *  - bf16 tensors are [B, H, T, D] with the last dimension contiguous and
- *    the other three strides given in elements (bsm_tensor).  Base pointers
- *    must be 16-byte aligned and strides multiples of 8 elements.
+ *  - Tensors are [B, H, T, D] of bf16 or fp16 elements (bsm_tensor.dtype;
+ *    every tensor of one call has the same type) with the last dimension
+ *    contiguous and the other three strides given in elements.  Base
+ *    pointers must be 16-byte aligned and strides multiples of 8 elements.
+ *    The matrix-core products take their operands in the tensors' type
+ *    (including the probabilities and score gradients formed on the way)
+ *    and accumulate in fp32 (tutorial "FlexAttention in PyTorch", "What to
+ *    expect, and the sharp edges": bf16 and fp16 inputs).
  */
 #ifndef BSM_H
 #define BSM_H
@@ -178,13 +183,21 @@ typedef struct {
                                     ignores it.                        */
 } bsm_score_mod;
 
-/* bf16 tensor [B, H, T, D]; element (b,h,t,d) lives at
+/* Element types of bsm_tensor.dtype (0, the zero-initialised value, is
+ * bf16). */
+enum {
+    BSM_DTYPE_BF16 = 0,
+    BSM_DTYPE_F16 = 1
+};
+
+/* Tensor [B, H, T, D]; element (b,h,t,d) lives at
  * ptr + b*stride_b + h*stride_h + t*stride_t + d  (strides in elements). */
 typedef struct {
     void *ptr;
     int64_t stride_b;
     int64_t stride_h;
     int64_t stride_t;
+    int32_t dtype;           /* BSM_DTYPE_*                                        */
 } bsm_tensor;
 
 /* Bytes of device workspace bsm_build_block_mask needs for `spec` (per-tile

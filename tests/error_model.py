@@ -1,5 +1,6 @@
-"""A numpy emulation of where a bf16 implementation of the attention path
-must round, used to check the parity bound (test infrastructure; CPU).
+"""A numpy emulation of where a bf16 (or fp16) implementation of the
+attention path must round, used to check the parity bound (test
+infrastructure; CPU).
 
 The interface fixes three roundings: the forward's output is bf16, so the
 backward forms Delta = <dO, out> from the bf16 out; and a bf16 matrix-core
@@ -20,7 +21,12 @@ def bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)).to(torch.bfloat16).double().numpy()
 
 
-def _emulated_rows(Q, K, V, spec, mod, b, h, rows, sc):
+def f16(x):
+    """Round to nearest-even fp16, returned as float64."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64)).to(torch.float16).double().numpy()
+
+
+def _emulated_rows(Q, K, V, spec, mod, b, h, rows, sc, rnd=bf16):
     """bf16 out of the forward for `rows` with bf16 probabilities in the PV
     product and the fp64 row sum, and the exact lse."""
     out = np.zeros((len(rows), V.shape[1]))
@@ -36,12 +42,12 @@ def _emulated_rows(Q, K, V, spec, mod, b, h, rows, sc):
         with np.errstate(invalid="ignore"):
             p = np.where(m, np.exp(s - mx0[:, None]), 0.0)
         ell = np.where(live, p.sum(axis=1), 1.0)
-        out[a:a + len(r)] = np.where(live[:, None], bf16(bf16(p) @ V[cols] / ell[:, None]), 0.0)
+        out[a:a + len(r)] = np.where(live[:, None], rnd(rnd(p) @ V[cols] / ell[:, None]), 0.0)
         lse[a:a + len(r)] = np.where(live, mx0 + np.log(ell), -np.inf)
     return out, lse
 
 
-def emulate_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None):
+def emulate_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None, rnd=bf16):
     """dK, dV [C, D] for the key positions `cols` with the bf16 rounding
     points of the interface: Delta from the bf16 out, dS and P rounded to
     bf16 before their products, outputs rounded to bf16."""
@@ -53,10 +59,10 @@ def emulate_dkdv_cols(Q, K, V, dO, spec, mod, b, h, cols, scale=None):
     dV = np.zeros((len(cols), V.shape[1]))
     if len(rows) == 0:
         return dK, dV
-    out_e, lse = _emulated_rows(Q, K, V, spec, mod, b, h, rows, sc)
+    out_e, lse = _emulated_rows(Q, K, V, spec, mod, b, h, rows, sc, rnd)
     for a in range(0, len(rows), oa.ROW_CHUNK):
         r = rows[a:a + oa.ROW_CHUNK]
         g, p = oa._grad_block(Q, K, V, dO, spec, mod, b, h, r, cols, out_e[a:a + len(r)], lse[a:a + len(r)], sc)
-        dK += sc * (bf16(g).T @ Q[r])
-        dV += bf16(p).T @ dO[r]
-    return bf16(dK), bf16(dV)
+        dK += sc * (rnd(g).T @ Q[r])
+        dV += rnd(p).T @ dO[r]
+    return rnd(dK), rnd(dV)

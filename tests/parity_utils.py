@@ -74,6 +74,12 @@ def f64(t):
 
 
 BF16_U = 2.0 ** -8  # unit roundoff of bf16 (8 significant bits, round to nearest)
+F16_U = 2.0 ** -11  # unit roundoff of fp16 (11 significant bits)
+# fp16 outputs: the fixed part of the bound.  fp16 carries three more bits
+# than bf16 and the fp32 arithmetic around the products is far below either,
+# so a tenth of the bf16 bar is still generous; a path that rounded its
+# operands to bf16 would miss it.
+F16_MAX_ABS = 2e-3
 
 
 def half_ulp_bf16(x):
@@ -83,15 +89,28 @@ def half_ulp_bf16(x):
     return np.where(x > 0, np.ldexp(1.0, E - 9), 0.0)
 
 
-def operand_bound(ref, mass, max_abs=MAX_ABS):
-    """Per-element bound: max_abs + half_ulp_bf16(|ref|) + u * mass."""
-    return max_abs + half_ulp_bf16(ref) + BF16_U * np.asarray(mass, dtype=np.float64)
+def half_ulp_f16(x):
+    """Half the fp16 spacing at |x|: 2^(e - 11) for |x| in [2^e, 2^(e+1)),
+    and 2^-25 below 2^-14 (subnormals)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, E = np.frexp(x)
+    return np.where(x > 0, np.maximum(np.ldexp(1.0, E - 12), 2.0 ** -25), 0.0)
 
 
-def assert_within_bound(gpu, ref, mass, ctx="", mean_abs=MEAN_ABS):
+FORMATS = {"bf16": (BF16_U, half_ulp_bf16, MAX_ABS), "f16": (F16_U, half_ulp_f16, F16_MAX_ABS)}
+
+
+def operand_bound(ref, mass, max_abs=None, fmt="bf16"):
+    """Per-element bound: max_abs + half_ulp(|ref|) + u * mass for the
+    output format fmt (bf16 or f16), max_abs by default that format's."""
+    u, half_ulp, fixed = FORMATS[fmt]
+    return (fixed if max_abs is None else max_abs) + half_ulp(ref) + u * np.asarray(mass, dtype=np.float64)
+
+
+def assert_within_bound(gpu, ref, mass, ctx="", mean_abs=MEAN_ABS, fmt="bf16"):
     """Every element within operand_bound, and mean-abs within
     mean_abs / MAX_ABS of the mean of that bound (mean_abs for outputs of
-    unit scale)."""
+    unit scale in bf16)."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert gpu.shape == ref.shape == np.shape(mass), (ctx, gpu.shape, ref.shape, np.shape(mass))
@@ -99,7 +118,7 @@ def assert_within_bound(gpu, ref, mass, ctx="", mean_abs=MEAN_ABS):
     err = np.abs(gpu - ref)
     if not err.size:
         return 0.0, 0.0
-    bound = operand_bound(ref, mass)
+    bound = operand_bound(ref, mass, fmt=fmt)
     worst = int(np.argmax(err - bound))
     mx, mn = float(err.max()), float(err.mean())
     mean_bar = float(bound.mean()) * (mean_abs / MAX_ABS)

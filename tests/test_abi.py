@@ -102,8 +102,8 @@ def test_workspace_sizes():
     assert lib.bsm_bwd_workspace_bytes(1, 1, 1024, 96) == 0
 
 
-def _t(ptr=FAKE, sb=8 * 1024 * 64, sh=1024 * 64, st=64):
-    return BsmTensor(ptr, sb, sh, st)
+def _t(ptr=FAKE, sb=8 * 1024 * 64, sh=1024 * 64, st=64, dtype=0):
+    return BsmTensor(ptr, sb, sh, st, dtype)
 
 
 def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=None, lse=FAKE,
@@ -127,6 +127,8 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
     (dict(q=_t(ptr=FAKE + 8)), _lib.BSM_E_INVALID),  # misaligned
     (dict(k=_t(st=60)), _lib.BSM_E_INVALID),        # stride not a multiple of 8
     (dict(v=_t(ptr=0)), _lib.BSM_E_INVALID),
+    (dict(k=_t(dtype=1)), _lib.BSM_E_INVALID),      # fp16 k with bf16 q, v, out
+    (dict(q=_t(dtype=2), k=_t(dtype=2), v=_t(dtype=2), o=_t(dtype=2)), _lib.BSM_E_INVALID),  # unknown dtype
     (dict(lse=None), _lib.BSM_E_INVALID),
     (dict(bm=_bm(null=0)), _lib.BSM_E_INVALID),
     (dict(bm=_bm(null=9)), _lib.BSM_E_INVALID),     # work order

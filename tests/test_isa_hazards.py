@@ -82,32 +82,43 @@ the block that follows it."""
 _ASM = {}
 
 
-ATTN_OBJECTS = ["attn_fwd.hip@64", "attn_fwd.hip@128", "attn_bwd.hip@64", "attn_bwd.hip@128"]
-ALL_OBJECTS = ATTN_OBJECTS + ["mask_builder.hip", "attn_decode.hip"]
+def _objects():
+    from block_sparse_masked_build_amd import build
+    return build
+
+
+BUILD = _objects()
+# the objects the build compiles: (source, object name, flags)
+ATTN_OBJECTS = [e[1] for e in BUILD.SOURCES if e[0] in ("attn_fwd.hip", "attn_bwd.hip")]
+ALL_OBJECTS = [e[1] for e in BUILD.SOURCES if e[0].endswith(".hip")]
 
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
-    """Device assembly of a source (name, or "name@D" for the attention
-    passes' objects of head dimension D, as the build compiles them).  The
-    first use compiles every object the tests read, concurrently."""
+    """Device assembly of each object the build compiles, with its own
+    flags: the build's saved copy when its stamp matches the current
+    sources, else compiled here (all missing ones concurrently)."""
     if not _ASM:
         tmp = tmp_path_factory.mktemp("isa")
         procs = {}
-        for key in ALL_OBJECTS:
-            src, _, d = key.partition("@")
-            out = tmp / (src + d + ".s")
-            cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-                   "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-x", "hip",
-                   *([f"-DBSM_HEAD_DIM={d}"] if d else []),
-                   "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", str(out)]
-            procs[key] = (subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE), out)
-        for key, (proc, out) in procs.items():
+        for src, obj, extra in BUILD.SOURCES:
+            if not src.endswith(".hip"):
+                continue
+            d = BUILD.object_dir(obj)
+            saved = os.path.join(d, os.path.splitext(src)[0] + "-hip-amdgcn-amd-amdhsa-gfx950.s")
+            stamp = os.path.join(d, "stamp.txt")
+            if os.path.exists(saved) and os.path.exists(stamp) and open(stamp).read() == BUILD.source_stamp(extra):
+                _ASM[obj] = open(saved).read()
+                continue
+            out = tmp / (obj + ".s")
+            cmd = [HIPCC, *BUILD.compile_flags(), *extra, "-x", "hip", "--cuda-device-only", "-S",
+                   os.path.join(CSRC, src), "-o", str(out)]
+            procs[obj] = (subprocess.Popen(cmd, stdout=subprocess.DEVNULL, stderr=subprocess.PIPE), out)
+        for obj, (proc, out) in procs.items():
             _, err = proc.communicate()
-            assert proc.returncode == 0, (key, err.decode()[-2000:])
-            _ASM[key] = out.read_text()
+            assert proc.returncode == 0, (obj, err.decode()[-2000:])
+            _ASM[obj] = out.read_text()
     return lambda key: _ASM[key]
-
 
 
 @pytest.mark.parametrize("src", ATTN_OBJECTS)

@@ -14,6 +14,7 @@ from .generators import (  # noqa: F401
     doc_ids_lognormal,
     doc_ids_chunks,
     random_bf16,
+    random_f16,
     alibi_slopes,
     make_config,
     CONFIG_NAMES,

@@ -108,6 +108,11 @@ def random_bf16(shape, generator: torch.Generator) -> torch.Tensor:
     return torch.randn(shape, generator=generator, dtype=torch.float32).to(torch.bfloat16)
 
 
+def random_f16(shape, generator: torch.Generator) -> torch.Tensor:
+    """The same N(0, 1) draws rounded to fp16 (round-to-nearest-even)."""
+    return torch.randn(shape, generator=generator, dtype=torch.float32).to(torch.float16)
+
+
 def doc_ids_from_eot_flags(flags: np.ndarray) -> np.ndarray:
     """Document id of every position: the running count of end-of-text flags
     (the flagged position opens the next document)."""
