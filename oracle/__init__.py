@@ -19,6 +19,8 @@ from .block_mask import (  # noqa: F401
     tile_counts_dense_numpy,
     classify,
     block_mask_lists,
+    spec_block_mask_lists,
+    kv_block,
     EMPTY, PARTIAL, FULL, TILE,
 )
 from .attention import (  # noqa: F401

@@ -8,10 +8,18 @@ Follows:
     is entirely empty, partially masked or full; empty blocks are never
     scheduled, only partial blocks need the elementwise mask.
 
+  * same tutorial, "What to expect, and the sharp edges", item 4: the block
+    size is a tunable (128 x 128 by default); smaller blocks capture more
+    sparsity.  Here the key-block width of the row lists may be 64 (blocks
+    of 128 queries x 64 keys).
+
 Readings taken where the pages are silent:
-  * classes come from the exact number of visible pairs in the tile
-    (0 -> empty, 128*128 -> full, otherwise partial), so a tile at the end
-    of a length that is not a multiple of 128 is never full;
+  * classes come from the exact number of visible pairs in the block
+    (0 -> empty, all of its tile_q x tile_k pairs -> full, otherwise
+    partial), so a block at the end of a length that is not a multiple of
+    its size is never full;
+  * with 64-key blocks the row lists (what the forward visits) are at
+    128 x 64; the column lists stay at 128 x 128 tiles;
   * partial and full tiles are listed separately, each in ascending column
     order, padded with -1 after the count; counts are int32;
   * for the backward pass the same lists are also given per key tile
@@ -32,6 +40,11 @@ from .predicate import visible
 
 TILE = 128
 EMPTY, PARTIAL, FULL = 0, 1, 2
+
+
+def kv_block(spec) -> int:
+    """Key-block width of the spec's row lists (128 by default)."""
+    return int(getattr(spec, "kv_block", TILE) or TILE)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "c", "liboracle_tiles.so")
@@ -57,7 +70,8 @@ def _load():
         lib.oracle_tile_counts.restype = ctypes.c_int
         lib.oracle_tile_counts.argtypes = [
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
-            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p]
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_uint32,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -84,12 +98,12 @@ def _q_len(spec):
     return spec.T if q is None else int(q)
 
 
-def tile_counts(spec) -> np.ndarray:
-    """int32 [mask_b, ceil(Q_LEN/128), ceil(KV_LEN/128)]: visible pairs per
-    tile (brute force)."""
+def tile_counts(spec, tile_q: int = TILE, tile_k: int = TILE) -> np.ndarray:
+    """int32 [mask_b, ceil(Q_LEN/tile_q), ceil(KV_LEN/tile_k)]: visible pairs
+    per block (brute force)."""
     kv_len, q_len, q_off = spec.T, _q_len(spec), int(getattr(spec, "q_offset", 0))
     mb = spec.mask_b
-    nq, nk = -(-q_len // TILE), -(-kv_len // TILE)
+    nq, nk = -(-q_len // tile_q), -(-kv_len // tile_k)
     out = np.zeros((mb, nq, nk), dtype=np.int32)
     docs, npos = None, max(kv_len, q_off + q_len)
     if spec.document:
@@ -102,30 +116,31 @@ def tile_counts(spec) -> np.ndarray:
         docs.ctypes.data if docs is not None else None, npos,
         int(spec.window) if spec.window is not None else 0,
         int(spec.sinks), int(getattr(spec, "prefix", 0)),
-        int(getattr(spec, "table", None) or 0) & 0xFFFFFFFF, out.ctypes.data)
+        int(getattr(spec, "table", None) or 0) & 0xFFFFFFFF, int(tile_q), int(tile_k), out.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_tile_counts rejected the spec")
     return out
 
 
-def tile_counts_dense_numpy(spec) -> np.ndarray:
+def tile_counts_dense_numpy(spec, tile_q: int = TILE, tile_k: int = TILE) -> np.ndarray:
     """Same counts from a dense [Q_LEN, KV_LEN] boolean mask, padded with
-    False to whole tiles (small sizes only)."""
+    False to whole blocks (small sizes only)."""
     kv_len, q_len = spec.T, _q_len(spec)
-    nq, nk = -(-q_len // TILE), -(-kv_len // TILE)
+    nq, nk = -(-q_len // tile_q), -(-kv_len // tile_k)
     res = []
     for b in range(spec.mask_b):
-        m = np.zeros((nq * TILE, nk * TILE), dtype=bool)
+        m = np.zeros((nq * tile_q, nk * tile_k), dtype=bool)
         m[:q_len, :kv_len] = visible(spec, b, np.arange(q_len)[:, None], np.arange(kv_len)[None, :])
-        res.append(m.reshape(nq, TILE, nk, TILE).sum(axis=(1, 3)).astype(np.int32))
+        res.append(m.reshape(nq, tile_q, nk, tile_k).sum(axis=(1, 3)).astype(np.int32))
     return np.stack(res)
 
 
-def classify(counts: np.ndarray) -> np.ndarray:
-    """uint8 class per tile: 0 empty, 1 partial, 2 full."""
+def classify(counts: np.ndarray, tile_q: int = TILE, tile_k: int = TILE) -> np.ndarray:
+    """uint8 class per block of tile_q x tile_k pairs: 0 empty, 1 partial,
+    2 full."""
     cls = np.full(counts.shape, PARTIAL, dtype=np.uint8)
     cls[counts == 0] = EMPTY
-    cls[counts == TILE * TILE] = FULL
+    cls[counts == tile_q * tile_k] = FULL
     return cls
 
 
@@ -142,20 +157,23 @@ def _lists(cls2d: np.ndarray, want: int):
     return num, idx
 
 
-def block_mask_lists(counts: np.ndarray) -> dict:
+def block_mask_lists(counts: np.ndarray, row_counts: np.ndarray = None, row_tile_k: int = TILE) -> dict:
     """The eight tile-list arrays of a block mask, shaped [mask_b, 1, ...]
-    (head dim 1: one mask shared by all heads)."""
+    (head dim 1: one mask shared by all heads).  counts: 128 x 128 tile
+    counts; row_counts (optional): counts at 128 x row_tile_k blocks for the
+    row lists (the column lists always come from counts)."""
     cls = classify(counts)
+    row_cls = cls if row_counts is None else classify(row_counts, TILE, row_tile_k)
     names = {}
     out = {k: [] for k in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
                            "full_kv_indices", "q_num_blocks", "q_indices",
                            "full_q_num_blocks", "full_q_indices")}
     for b in range(cls.shape[0]):
         c = cls[b]
-        n, i = _lists(c, PARTIAL)
+        n, i = _lists(row_cls[b], PARTIAL)
         out["kv_num_blocks"].append(n)
         out["kv_indices"].append(i)
-        n, i = _lists(c, FULL)
+        n, i = _lists(row_cls[b], FULL)
         out["full_kv_num_blocks"].append(n)
         out["full_kv_indices"].append(i)
         n, i = _lists(c.T, PARTIAL)
@@ -167,3 +185,13 @@ def block_mask_lists(counts: np.ndarray) -> dict:
     for k, v in out.items():
         names[k] = np.stack(v)[:, None]
     return names
+
+
+def spec_block_mask_lists(spec) -> dict:
+    """The eight arrays of the spec's block mask: row lists at the spec's
+    key-block width, column lists at 128 x 128."""
+    kb = kv_block(spec)
+    counts = tile_counts(spec)
+    if kb == TILE:
+        return block_mask_lists(counts)
+    return block_mask_lists(counts, tile_counts(spec, TILE, kb), kb)

@@ -1,6 +1,8 @@
 /*
  * Oracle (test infrastructure only): brute-force count of visible (q, kv)
- * pairs in every 128 x 128 tile of the attention grid.
+ * pairs in every tile_q x tile_k block of the attention grid (128 x 128 by
+ * default; the tutorial's sharp edges call the block size a tunable that
+ * captures more sparsity when smaller).
  *
  * Definition followed: a tile's class is decided by how many of its scores
  * the mask predicate lets through -- none (empty), all 128 x 128 (full) or
@@ -27,8 +29,6 @@
 #include <stdint.h>
 #include <string.h>
 
-#define ORACLE_TILE 128
-
 /* flags: bit0 causal, bit1 document, bit2 window, bit3 sinks, bit4 prefix,
  * bit5 truth table (table bit C + 2 Dc + 4 W + 8 S + 16 P) */
 static inline int visible_pair(int64_t q, int64_t kv, int flags,
@@ -53,35 +53,35 @@ static inline int visible_pair(int64_t q, int64_t kv, int flags,
 }
 
 /*
- * counts: int32 [mask_b, ceil(q_len/128), ceil(kv_len/128)];
+ * counts: int32 [mask_b, ceil(q_len/tile_q), ceil(kv_len/tile_k)];
  * counts[b][i][j] = number of visible pairs with query index qi in
- * [128 i, min(128 i + 127, q_len - 1)] (absolute position q_offset + qi) and
- * kv in [128 j, min(128 j + 127, kv_len - 1)].
+ * [tile_q i, min(tile_q (i + 1), q_len) - 1] (absolute position
+ * q_offset + qi) and kv in [tile_k j, min(tile_k (j + 1), kv_len) - 1].
  * docs: int32 [mask_b, positions] (may be NULL when bit1 is clear), indexed by
  * absolute position; positions >= max(kv_len, q_offset + q_len).
  * Returns 0 on success, -1 on a bad size.
  */
 int oracle_tile_counts(int64_t kv_len, int64_t q_len, int64_t q_offset, int mask_b, int flags,
                        const int32_t *docs, int64_t positions, int64_t window, int64_t sinks,
-                       int64_t prefix, uint32_t table, int32_t *counts)
+                       int64_t prefix, uint32_t table, int64_t tile_q, int64_t tile_k, int32_t *counts)
 {
-    if (kv_len <= 0 || q_len <= 0 || q_offset < 0 || mask_b <= 0)
+    if (kv_len <= 0 || q_len <= 0 || q_offset < 0 || mask_b <= 0 || tile_q <= 0 || tile_k <= 0)
         return -1;
     if ((flags & 2) && positions < (kv_len > q_offset + q_len ? kv_len : q_offset + q_len))
         return -1;
-    const int64_t nq = (q_len + ORACLE_TILE - 1) / ORACLE_TILE;
-    const int64_t nk = (kv_len + ORACLE_TILE - 1) / ORACLE_TILE;
+    const int64_t nq = (q_len + tile_q - 1) / tile_q;
+    const int64_t nk = (kv_len + tile_k - 1) / tile_k;
     for (int b = 0; b < mask_b; ++b) {
         const int32_t *d = docs ? docs + (int64_t)b * positions : NULL;
         int32_t *c = counts + (int64_t)b * nq * nk;
         #pragma omp parallel for schedule(dynamic, 1)
         for (int64_t i = 0; i < nq; ++i) {
-            const int64_t q1 = (i + 1) * ORACLE_TILE < q_len ? (i + 1) * ORACLE_TILE : q_len;
+            const int64_t q1 = (i + 1) * tile_q < q_len ? (i + 1) * tile_q : q_len;
             for (int64_t j = 0; j < nk; ++j) {
-                const int64_t k1 = (j + 1) * ORACLE_TILE < kv_len ? (j + 1) * ORACLE_TILE : kv_len;
+                const int64_t k1 = (j + 1) * tile_k < kv_len ? (j + 1) * tile_k : kv_len;
                 int32_t n = 0;
-                for (int64_t qi = i * ORACLE_TILE; qi < q1; ++qi)
-                    for (int64_t kv = j * ORACLE_TILE; kv < k1; ++kv)
+                for (int64_t qi = i * tile_q; qi < q1; ++qi)
+                    for (int64_t kv = j * tile_k; kv < k1; ++kv)
                         n += visible_pair(q_offset + qi, kv, flags, d, window, sinks, prefix, table);
                 c[i * nk + j] = n;
             }

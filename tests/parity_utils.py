@@ -42,7 +42,7 @@ def log(msg):
 
 
 def oracle_block_mask(spec_data):
-    return oracle.block_mask_lists(oracle.tile_counts(spec_data))
+    return oracle.spec_block_mask_lists(spec_data)
 
 
 def gpu_block_mask(spec_data):

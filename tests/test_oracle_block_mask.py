@@ -372,3 +372,112 @@ def test_table_of_the_standard_combination_gives_the_same_counts():
         ref = oracle.tile_counts(spec)
         spec.table = _equivalent_table(spec)
         assert np.array_equal(oracle.tile_counts(spec), ref), spec
+
+
+# ------------------------------------------------ 64-key blocks (tutorial,
+# "What to expect, and the sharp edges", item 4: block size is a tunable)
+
+def _pairs_python_blocks(spec, tq, tk):
+    """Pure-Python loops over every pair of a standard-combination spec,
+    counted into tq x tk blocks (tiny sizes)."""
+    kv_len, q_len, off = spec.T, spec.Q, spec.q_offset
+    res = np.zeros((spec.mask_b, -(-q_len // tq), -(-kv_len // tk)), dtype=np.int64)
+    for b in range(spec.mask_b):
+        docs = None if spec.doc_ids is None else [int(x) for x in spec.doc_ids[b]]
+        for qi in range(q_len):
+            q = off + qi
+            for kv in range(kv_len):
+                ok = ((not spec.causal) or q >= kv or (bool(spec.prefix) and kv < spec.prefix)) and \
+                     ((not spec.document) or docs[q] == docs[kv]) and \
+                     (spec.window is None or (q - kv) < spec.window or (bool(spec.sinks) and kv < spec.sinks))
+                if ok:
+                    res[b, qi // tq, kv // tk] += 1
+    return res
+
+
+def test_64_key_blocks_brute_force_python():
+    rng = np.random.default_rng(640)
+    for it in range(6):
+        T = int(rng.choice([64, 100, 200, 300]))
+        Q = int(rng.choice([T, 1, 77, 150]))
+        off = int(rng.integers(0, T + 1))
+        docs = np.cumsum(rng.random(max(T, off + Q)) < 1 / 30).astype(np.int32)[None]
+        spec = MaskSpecData(T, causal=bool(it % 3), document=bool(it % 2), doc_ids=docs,
+                            window=int(rng.choice([5, 40, 90])) if it % 2 else None, sinks=3 if it == 3 else 0,
+                            prefix=20 if it == 4 else 0, q_len=Q, q_offset=off)
+        got = oracle.tile_counts(spec, 128, 64)
+        assert np.array_equal(got, _pairs_python_blocks(spec, 128, 64)), it
+        assert np.array_equal(got, oracle.tile_counts_dense_numpy(spec, 128, 64)), it
+
+
+@pytest.mark.parametrize("T", [1024, 8192, 8192 + 77])
+def test_64_key_blocks_causal_closed_form(T):
+    """Causal, 128 x 64 blocks, n = T // 128 whole query tiles: row i sees
+    key blocks 0 .. 2i + 1, of which the first 2i are full (every key below
+    the row's first query).  A cut-short last row (T = 128 n + r) sees
+    every key block, ceil(T/64) of them, and holds r < 128 queries, so none
+    of its blocks is full."""
+    n, r = divmod(T, 128)
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True), 128, 64), 128, 64)
+    vis = n * (n + 1)
+    full = n * (n - 1)
+    if r:
+        vis += -(-T // 64)  # the last row sees every key block
+    assert int((cls > 0).sum()) == vis
+    assert int((cls == oracle.FULL).sum()) == full
+
+
+def _window_blocks_closed_form(n, w, tk):
+    """Causal + window w at 128 x tk blocks, T = 128 n: block (i, j) holds
+    differences q - k from 128 i - tk j - tk + 1 to 128 i + 127 - tk j; it
+    is visible iff the largest is >= 0 and the smallest < w, full iff the
+    smallest is >= 0 and the largest < w.  Arithmetic per block, no pairs."""
+    vis = full = 0
+    for i in range(n):
+        for j in range(n * 128 // tk):
+            lo, hi = 128 * i - tk * j - tk + 1, 128 * i + 127 - tk * j
+            if hi >= 0 and lo < w:
+                vis += 1
+                if lo >= 0 and hi < w:
+                    full += 1
+    return vis, full
+
+
+@pytest.mark.parametrize("w", [1, 64, 100, 640, 1024, 1792])
+def test_64_key_blocks_window_closed_form(w):
+    T = 8192
+    cls = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True, window=w), 128, 64), 128, 64)
+    vis, full = _window_blocks_closed_form(T // 128, w, 64)
+    assert int((cls > 0).sum()) == vis
+    assert int((cls == oracle.FULL).sum()) == full
+    # and the same arithmetic gives the 128 x 128 counts
+    cls128 = oracle.classify(oracle.tile_counts(MaskSpecData(T, causal=True, window=w)))
+    assert (int((cls128 > 0).sum()), int((cls128 == oracle.FULL).sum())) == _window_blocks_closed_form(T // 128, w, 128)
+
+
+def test_64_key_blocks_refine_128_tiles():
+    """Counts of the two 64-key halves add up to the 128 x 128 tile's; a
+    tile is full iff both halves are, empty iff both are.  Row lists of a
+    kv_block = 64 spec index 64-key blocks, column lists 128 x 128 tiles."""
+    rng = np.random.default_rng(641)
+    T = 1000
+    docs = np.cumsum(rng.random(T) < 1 / 150).astype(np.int32)[None]
+    spec = MaskSpecData(T, causal=True, document=True, doc_ids=docs, window=300, sinks=4, kv_block=64)
+    c64 = oracle.tile_counts(spec, 128, 64)
+    c128 = oracle.tile_counts(spec)
+    pad = np.zeros(c64.shape[:2] + (2 * c128.shape[2],), dtype=np.int64)
+    pad[..., :c64.shape[2]] = c64
+    assert np.array_equal(pad.reshape(c64.shape[0], c64.shape[1], -1, 2).sum(axis=3), c128)
+    k64 = oracle.classify(c64, 128, 64)
+    k128 = oracle.classify(c128)
+    for j in range(c128.shape[2]):
+        halves = k64[..., 2 * j:2 * j + 2]
+        both_full = np.all(halves == oracle.FULL, axis=-1) & (halves.shape[-1] == 2)
+        assert np.array_equal(k128[..., j] == oracle.FULL, both_full)
+        assert np.array_equal(k128[..., j] == oracle.EMPTY, np.all(halves == oracle.EMPTY, axis=-1))
+    lists = oracle.spec_block_mask_lists(spec)
+    assert lists["kv_indices"].shape == (1, 1, 8, 16)
+    assert lists["q_indices"].shape == (1, 1, 8, 8)
+    ref128 = oracle.block_mask_lists(c128)
+    for n in ("q_num_blocks", "q_indices", "full_q_num_blocks", "full_q_indices"):
+        assert np.array_equal(lists[n], ref128[n]), n

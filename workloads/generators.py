@@ -41,6 +41,8 @@ class MaskSpecData:
     sinks       -- kv < sinks, OR-ed with the window term (0: none)
     prefix      -- kv < prefix, OR-ed with the causal term (prefix-LM: the
                    first `prefix` positions are seen by every query; 0: none)
+    kv_block    -- key-block width of the block mask's row lists: 128, or 64
+                   for finer blocks (128 queries x 64 keys)
     table       -- None: the terms combine as above.  Otherwise a 32-bit truth
                    table over the five terms: the pair is visible iff bit
                    (C + 2 Dc + 4 W + 8 S + 16 P) of it is set, with C = q >= kv,
@@ -59,6 +61,7 @@ class MaskSpecData:
     q_len: Optional[int] = None
     q_offset: int = 0
     table: Optional[int] = None
+    kv_block: int = 128
 
     @property
     def mask_b(self) -> int:
