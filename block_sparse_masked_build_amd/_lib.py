@@ -32,7 +32,8 @@ class BsmMaskSpec(ctypes.Structure):
                 ("mask_b", ctypes.c_int32), ("doc_ids", ctypes.c_void_p),
                 ("window", ctypes.c_void_p), ("num_sinks", ctypes.c_int32),
                 ("prefix_len", ctypes.c_int32), ("q_len", ctypes.c_int32),
-                ("q_offset", ctypes.c_int32), ("table", ctypes.c_uint32)]
+                ("q_offset", ctypes.c_int32), ("table", ctypes.c_uint32),
+                ("kv_block", ctypes.c_int32)]
 
 
 class BsmBlockMask(ctypes.Structure):

@@ -101,6 +101,7 @@ class MaskSpec:
     q_len: int = 0
     q_offset: int = 0
     composed: Optional[MaskTerm] = None      # replaces the standard combination of the terms
+    kv_block: int = 128                      # key-block width of the row lists: 128 or 64
 
     @property
     def Q(self) -> int:
@@ -117,6 +118,11 @@ class MaskSpec:
     @property
     def KT(self) -> int:
         return -(-self.T // TILE)
+
+    @property
+    def KB(self) -> int:
+        """Key blocks of the row lists."""
+        return -(-self.T // self.kv_block)
 
     @property
     def mask_b(self) -> int:
@@ -142,7 +148,7 @@ class MaskSpec:
                            self.doc_ids.data_ptr() if self.doc_ids is not None else None,
                            self.window.data_ptr() if self.window is not None else None,
                            int(self.sinks), int(self.prefix), int(self.q_len), int(self.q_offset),
-                           self.composed.table if self.composed is not None else 0)
+                           self.composed.table if self.composed is not None else 0, int(self.kv_block))
 
     def set_window(self, w: int) -> None:
         """Writes a new window value on the device (stream-ordered)."""
@@ -191,7 +197,7 @@ def _stream() -> int:
 
 def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] = None,
               sinks: int = 0, device="cuda", prefix: int = 0, q_len: int = 0, q_offset: int = 0,
-              composed: Optional[MaskTerm] = None) -> MaskSpec:
+              composed: Optional[MaskTerm] = None, kv_block: int = 128) -> MaskSpec:
     """Device mask spec from host values (numpy / torch / int).  T is KV_LEN;
     doc_ids has one id per absolute position (max(T, q_offset + Q_LEN))."""
     d = None
@@ -205,7 +211,10 @@ def mask_spec(T: int, causal: bool = True, doc_ids=None, window: Optional[int] =
         w = torch.tensor([int(window)], dtype=torch.int32, device=device)
     if composed is not None and not isinstance(composed, MaskTerm):
         composed = MaskTerm(composed)
-    return MaskSpec(int(T), bool(causal), d, w, int(sinks), int(prefix), int(q_len), int(q_offset), composed)
+    if kv_block not in (64, 128):
+        raise ValueError(f"kv_block must be 64 or 128, got {kv_block}")
+    return MaskSpec(int(T), bool(causal), d, w, int(sinks), int(prefix), int(q_len), int(q_offset), composed,
+                    int(kv_block))
 
 
 def from_spec_data(spec_data, device="cuda") -> MaskSpec:
@@ -216,7 +225,8 @@ def from_spec_data(spec_data, device="cuda") -> MaskSpec:
                      spec_data.doc_ids if spec_data.document else None,
                      spec_data.window, spec_data.sinks, device, getattr(spec_data, "prefix", 0),
                      q_len=int(q_len) if q_len else 0, q_offset=int(getattr(spec_data, "q_offset", 0)),
-                     composed=MaskTerm(table) if table is not None else None)
+                     composed=MaskTerm(table) if table is not None else None,
+                     kv_block=int(getattr(spec_data, "kv_block", 128)))
 
 
 def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda") -> ScoreMod:
@@ -230,14 +240,15 @@ def empty_block_mask(spec, mask_b: Optional[int] = None, device="cuda") -> Block
     """Uninitialised block-mask arrays for a MaskSpec (or for a square mask
     of length T = spec and mask_b batch rows)."""
     if isinstance(spec, MaskSpec):
-        Q, T, npos = spec.Q, spec.T, spec.positions
+        Q, T, npos, kbw = spec.Q, spec.T, spec.positions, spec.kv_block
         mask_b = spec.mask_b if mask_b is None else mask_b
     else:
         Q = T = npos = int(spec)
+        kbw = TILE
         mask_b = 1 if mask_b is None else mask_b
-    qt, kt = -(-Q // TILE), -(-T // TILE)
+    qt, kt, nkb = -(-Q // TILE), -(-T // TILE), -(-T // kbw)
     mk = lambda *s: torch.empty(s, dtype=torch.int32, device=device)
-    return BlockMask(mk(mask_b, 1, qt), mk(mask_b, 1, qt, kt), mk(mask_b, 1, qt), mk(mask_b, 1, qt, kt),
+    return BlockMask(mk(mask_b, 1, qt), mk(mask_b, 1, qt, nkb), mk(mask_b, 1, qt), mk(mask_b, 1, qt, nkb),
                      mk(mask_b, 1, kt), mk(mask_b, 1, kt, qt), mk(mask_b, 1, kt), mk(mask_b, 1, kt, qt),
                      mk(mask_b, npos, 2), mk(mask_b * qt, 4), mk(mask_b * kt, 4))
 
@@ -448,7 +459,7 @@ def decode_multi_spec(spec: MaskSpec, kv_len: int, n: int) -> MaskSpec:
         raise ValueError(f"need 1 <= n={n} <= kv_len={kv_len} <= capacity={spec.T}")
     docs = spec.doc_ids[:, :kv_len].contiguous() if spec.doc_ids is not None else None
     return MaskSpec(int(kv_len), spec.causal, docs, spec.window, spec.sinks, spec.prefix, int(n),
-                    int(kv_len - n), spec.composed)
+                    int(kv_len - n), spec.composed, spec.kv_block)
 
 
 def flex_attention_decode_multi(q, k, v, spec: MaskSpec, kv_len: int, mod: Optional[ScoreMod] = None,

@@ -63,12 +63,13 @@ __device__ inline KvOffsets step_offsets(const KvOffsets &off, uint32_t base) {
     return o;
 }
 
-// Start of pipeline step t (64 rows): step t covers half t%2 of listed tile
-// t/2 (full tiles first, then partial ones).
-__device__ inline int step_row0(int t, int nfull, const int32_t *fidx, const int32_t *pidx, int nt) {
-    const int it = t >> 1;
+// Start of pipeline step t (64 keys): with 128-key blocks (spb = 2) step t
+// covers half t%2 of listed block t/2, with 64-key blocks (spb = 1) listed
+// block t (full blocks first, then partial ones).
+__device__ inline int step_row0(int t, int nfull, const int32_t *fidx, const int32_t *pidx, int nt, int spb) {
+    const int it = spb == 2 ? t >> 1 : t;
     const int jj = clamp_tile(it < nfull ? load_uniform(fidx + it) : load_uniform(pidx + it - nfull), nt);
-    return jj * kTile + (t & 1) * kHalf;
+    return spb == 2 ? jj * kTile + (t & 1) * kHalf : jj * kHalf;
 }
 
 // ---------------------------------------------------------------- dQ
@@ -79,6 +80,7 @@ struct DqArgs {
     const int32_t *fidx, *pidx, *doc;
     int nfull, nt, qpos;  // qpos: absolute position of this lane's query
     int kv_len, npos;
+    int spb;              // 64-key steps per listed block: 2 (128-key blocks) or 1
     float scale, scale_log2, slope, cap, inv_cap;
     ModK mk;          // folded score-modification constants
     float l2, delta;  // this lane's query
@@ -123,7 +125,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
                                                a.kv_len - key0);
     };
     if (nsteps <= 0) return;
-    int key0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt);
+    int key0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt, a.spb);
     issue(0, key0);
 #pragma unroll 1
     for (int t = 0; t < nsteps; ++t) {
@@ -131,7 +133,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
         tile_barrier();  // step t's tiles are visible; every wave is done with step t-1's buffers
         int key_next = 0;
         if (t + 1 < nsteps) {
-            key_next = step_row0(t + 1, a.nfull, a.fidx, a.pidx, a.nt);
+            key_next = step_row0(t + 1, a.nfull, a.fidx, a.pidx, a.nt, a.spb);
             issue(t + 1, key_next);
         }
         const uint32_t bf = t & 1;
@@ -140,7 +142,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
         // folds into the instruction's offset field).
         const uint32_t sk = lds.k, sv = lds.v;
         const KvOffsets offt = step_offsets(off, bf * kTB);
-        const bool partial = (t >> 1) >= a.nfull;
+        const bool partial = (a.spb == 2 ? t >> 1 : t) >= a.nfull;
         bool skip[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -210,7 +212,7 @@ template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
-    const int nt = p.nt;
+    const int nt = p.nkb;  // key blocks of the row lists
     // Item: a query-tile row of the row work order (longest first) and a
     // head index, in the forward's item order.
     const ItemOrder ord(p, kQueues);
@@ -247,6 +249,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     a.qpos = qpos;
     a.kv_len = p.T;
     a.npos = p.npos;
+    a.spb = p.kb / kHalf;
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     const int64_t row_bh = ((int64_t)b * p.H + h) * p.q_len + qrow;
     const float lse = p.lse[row_bh];
     a.l2 = lse == -INFINITY ? 0.0f : lse * kLog2e;
-    const int nsteps = 2 * (a.nfull + npart);
+    const int nsteps = a.spb * (a.nfull + npart);
 
     RowMask rm;
     const int mode = make_row_mask(p, bm, qpos, rm);

@@ -162,7 +162,8 @@ struct FwdArgs {
     const elem_t *kb, *vb;
     const int32_t *doc, *fidx, *pidx;
     int b, h, bm, row;
-    int nfull, ntiles, nt, first;
+    int nfull, ntiles, nt, first;  // listed blocks (full, all), blocks per row, first listed block
+    int kblk, spb;                  // block width (128 or 64 keys) and 64-key steps per block
     int qidx;  // this lane's query index (may lie past Q_LEN on the last row)
     int qpos;  // its absolute position (the last query's for lanes past Q_LEN)
     float scale, scale_log2, slope, cap, inv_cap;
@@ -171,7 +172,7 @@ struct FwdArgs {
 
 template <bool ALIBI, bool SOFTCAP>
 __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &rec, FwdArgs &a) {
-    const int nt = p.nt;  // key tiles
+    const int nt = p.nkb;  // key blocks of the row lists
     const int packed = min(max(rec.packed, 0), p.mask_b * p.nqt - 1);
     a.bm = packed / p.nqt;
     a.row = packed - a.bm * p.nqt;
@@ -185,6 +186,8 @@ __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &re
     a.ntiles = a.nfull + min(max(rec.npart, 0), nt);
     a.first = clamp_tile(rec.first, nt);
     a.nt = nt;
+    a.kblk = p.kb;
+    a.spb = p.kb / kHalf;
     a.qidx = a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
     a.qpos = p.q_off + min(a.qidx, p.q_len - 1);
     a.scale = p.scale;
@@ -216,6 +219,21 @@ __device__ inline int tile_at(const TileList &tl, const FwdArgs &a, int it) {
     if (it >= 128)
         return clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull), a.nt);
     return __builtin_amdgcn_readlane(it < 64 ? tl.lo : tl.hi, it & 63);
+}
+
+// First key of the row's 64-key step t: listed block t / spb (full blocks
+// first), and for 128-key blocks its half t % 2.
+__device__ inline int row_step_key0(const TileList &tl, const FwdArgs &a, int t) {
+    return a.spb == 2 ? tile_at(tl, a, t >> 1) * kTile + (t & 1) * kHalf : tile_at(tl, a, t) * kHalf;
+}
+
+// The same for step 1, before the tile list is loaded.  A row of a single
+// 64-key block has no step 1: its key is then the block's own, so that the
+// copy issued for it stays inside the tensor.
+__device__ inline int step1_key0(const FwdArgs &a) {
+    if (a.spb == 2) return a.first * kTile + kHalf;
+    if (a.ntiles < 2) return a.first * kHalf;
+    return clamp_tile(1 < a.nfull ? load_uniform(a.fidx + 1) : load_uniform(a.pidx + 1 - a.nfull), a.nt) * kHalf;
 }
 
 // Per-lane row data loaded at the start of an item: the query's document
@@ -273,15 +291,15 @@ __device__ __attribute__((always_inline)) inline void item_start(const AttnParam
                                   TileList &tl, RowLoad &rl) {
     if (a.ntiles > 0) {
         // rows past KV_LEN (document ids: past the positions) repeat the last one
-        const int k0 = a.first * kTile;
+        const int k0 = a.first * a.kblk;
+        const int k1 = step1_key0(a);
         if (a.doc) {
             issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0, p.npos - k0);
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k0 + kHalf, p.npos - k0 - kHalf);
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k1, p.npos - k1);
         }
         issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st, p.T - k0);
         issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st, p.T - k0);
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)(k0 + kHalf) * p.k_st, p.k_st,
-                                           p.T - k0 - kHalf);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)k1 * p.k_st, p.k_st, p.T - k1);
     }
     const int hl = (threadIdx.x & 63) >> 5;
     const elem_t *qrow = static_cast<const elem_t *>(p.q) + a.b * p.q_sb + a.h * p.q_sh +
@@ -347,7 +365,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     constexpr bool kMods = ALIBI || SOFTCAP;
     static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "output staging fits the K buffers");
     const float c_mul = kMods ? 1.0f : a.scale_log2;
-    const int nsteps = 2 * a.ntiles;
+    const int nsteps = a.spb * a.ntiles;  // 64-key steps
     auto reset = [&]() {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -361,7 +379,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
         store_item<D>(p, a, o, m, l, lds_addr(sm.k[0]));
         return;
     }
-    auto step_key0 = [&](int t) { return tile_at(tl, a, t >> 1) * kTile + (t & 1) * kHalf; };
+    auto step_key0 = [&](int t) { return row_step_key0(tl, a, t); };
     auto issue_k = [&](int t, int key0) {
         if (MODE == kGather || (MODE == kTable && a.doc))
             issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, p.npos - key0);
@@ -395,8 +413,8 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
 
     f32x16 sa[2], sb[2];
     float mx;  // row maximum of the current step's scores
-    const int k0 = a.first * kTile;
-    int key_ahead = k0 + kHalf;  // first key of step t+1 at the top of step t
+    const int k0 = a.first * a.kblk;
+    int key_ahead = step1_key0(a);  // first key of step t+1 at the top of step t
     fwd_qk<D>(sm.k[0], off, qf, sa);
     row_mods<ALIBI, SOFTCAP>(sa, k0, a.qpos, a.mk);
     const bool table_docs = MODE == kTable && a.doc;
@@ -410,7 +428,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
         asm volatile("" : "+v"(offt.k), "+v"(offt.v));
         // first keys of steps t+1 (carried from the previous step) and t+2
         const int key_next = key_ahead;
-        key_ahead = ((t + 2) & 1) ? key_ahead + kHalf : (t + 2 < nsteps ? step_key0(t + 2) : 0);
+        key_ahead = (a.spb == 2 && ((t + 2) & 1)) ? key_ahead + kHalf : (t + 2 < nsteps ? step_key0(t + 2) : 0);
         if (t + 2 < nsteps) issue_k(t + 2, key_ahead);
         issue_v(t + 1, key_next);
         if (decltype(first_step)::value) reset();
@@ -426,15 +444,20 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
         mx = step_max(sn);
         wait_lds_reads();  // this wave's reads of step t are done before the next barrier
     };
-    // step 0; its next step is the second half of the first tile
-    if (a.nfull > 0)
-        step(sa, sb, 0, std::false_type(), std::true_type());
-    else
-        step(sa, sb, 0, std::true_type(), std::true_type());
-    sa[0] = sb[0];  // the current scores live in sa between loops
-    sa[1] = sb[1];
-    // Steps t < t_switch have a full next tile.
-    const int t_switch = min(max(2 * a.nfull - 1, 1), nsteps - 1);
+    // step 0 (unless it is the only one); its next step is the second half
+    // of the first tile, or the second listed 64-key block
+    if (nsteps > 1) {
+        if (a.spb == 2 ? a.nfull > 0 : a.nfull > 1)
+            step(sa, sb, 0, std::false_type(), std::true_type());
+        else
+            step(sa, sb, 0, std::true_type(), std::true_type());
+        sa[0] = sb[0];  // the current scores live in sa between loops
+        sa[1] = sb[1];
+    } else {
+        reset();
+    }
+    // Steps t < t_switch have a full next block.
+    const int t_switch = min(max(a.spb * a.nfull - 1, 1), nsteps - 1);
     int t = 1;
     auto phase = [&](int t_end, auto next_masked) {
         for (; t + 1 < t_end; t += 2) {
@@ -456,7 +479,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     const float m_use = settle(mx);
     elem8 pb[2][2];
     fwd_exp(sa, pb, l, c_mul, m_use);
-    fwd_pv<D>(sm.v[1], off, pb, o);
+    fwd_pv<D>(sm.v[(nsteps - 1) & 1], off, pb, o);
     store_item<D>(p, a, o, m, l, lds_addr(sm.k[0]));
 }
 

@@ -43,9 +43,10 @@ int32_t effective_prefix(const bsm_mask_spec *spec) {
     return spec->prefix_len < spec->seq_len ? spec->prefix_len : spec->seq_len;
 }
 
-// Shape of a mask: keys, queries, query offset, document positions, tiles.
+// Shape of a mask: keys, queries, query offset, document positions, tiles,
+// and the key blocks of the row lists (kb keys each).
 struct MaskDims {
-    int32_t kv_len, q_len, q_off, npos, nqt, nkt;
+    int32_t kv_len, q_len, q_off, npos, nqt, nkt, kb, nkb;
 };
 
 MaskDims mask_dims(const bsm_mask_spec *spec) {
@@ -56,6 +57,8 @@ MaskDims mask_dims(const bsm_mask_spec *spec) {
     m.npos = m.kv_len > m.q_off + m.q_len ? m.kv_len : m.q_off + m.q_len;
     m.nqt = (m.q_len + bsm::kTile - 1) / bsm::kTile;
     m.nkt = (m.kv_len + bsm::kTile - 1) / bsm::kTile;
+    m.kb = spec->kv_block == 64 ? 64 : bsm::kTile;
+    m.nkb = (m.kv_len + m.kb - 1) / m.kb;
     return m;
 }
 constexpr uint32_t kModFlagsAll = BSM_MOD_ALIBI | BSM_MOD_SOFTCAP;
@@ -95,6 +98,8 @@ bsm_status check_spec(const bsm_mask_spec *spec) {
         return fail(BSM_E_INVALID, "num_sinks %d must be >= 0", spec->num_sinks);
     if ((spec->flags & BSM_MASK_PREFIX) && spec->prefix_len < 0)
         return fail(BSM_E_INVALID, "prefix_len %d must be >= 0", spec->prefix_len);
+    if (spec->kv_block != 0 && spec->kv_block != 64 && spec->kv_block != bsm::kTile)
+        return fail(BSM_E_INVALID, "kv_block %d must be 0, 64 or 128", spec->kv_block);
     return BSM_OK;
 }
 
@@ -195,6 +200,8 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
     p.H = H;
     p.T = T;
     p.nt = m.nkt;
+    p.kb = m.kb;
+    p.nkb = m.nkb;
     p.q_len = m.q_len;
     p.nqt = m.nqt;
     p.q_off = m.q_off;
@@ -254,6 +261,8 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
         if (st != BSM_OK) return st;
         if (capacity % bsm::kTile != 0)
             return fail(BSM_E_INVALID, "with a block mask the capacity %d must be a multiple of 128", capacity);
+        if (spec->kv_block == 64)
+            return fail(BSM_E_UNSUPPORTED, "the decoding step reads block masks of 128-key blocks only");
         if (!bm->kv_num_blocks || !bm->kv_indices || !bm->full_kv_num_blocks || !bm->full_kv_indices)
             return fail(BSM_E_INVALID, "block mask row arrays must be non-NULL");
     } else {
@@ -290,6 +299,8 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     p.H = H;
     p.T = capacity;
     p.nt = (capacity + bsm::kTile - 1) / bsm::kTile;
+    p.kb = bsm::kTile;
+    p.nkb = p.nt;
     p.q_len = capacity;
     p.nqt = p.nt;
     p.npos = capacity;
@@ -372,7 +383,7 @@ size_t bsm_block_mask_workspace_bytes(const bsm_mask_spec *spec) {
     if (check_spec(spec) != BSM_OK) return 0;
     const MaskDims m = mask_dims(spec);
     return align256((size_t)spec->mask_b * n_chunks(m.npos) * sizeof(int32_t)) +
-           align256((size_t)spec->mask_b * m.nqt * m.nkt) +
+           align256((size_t)spec->mask_b * m.nqt * m.nkb) +
            2 * align256((size_t)order_ws_ints(m, spec->mask_b) * sizeof(int32_t));
 }
 
@@ -400,6 +411,8 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     p.npos = m.npos;
     p.nqt = m.nqt;
     p.nkt = m.nkt;
+    p.kb = m.kb;
+    p.nkb = m.nkb;
     p.mask_b = spec->mask_b;
     p.nchunks = n_chunks(m.npos);
     p.sinks = spec->num_sinks;
@@ -412,7 +425,7 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
     p.nonmono = reinterpret_cast<int32_t *>(ws);
     const size_t off_cls = align256((size_t)p.mask_b * p.nchunks * sizeof(int32_t));
     p.cls = reinterpret_cast<uint8_t *>(ws + off_cls);
-    const size_t off_order = off_cls + align256((size_t)p.mask_b * p.nqt * p.nkt);
+    const size_t off_order = off_cls + align256((size_t)p.mask_b * p.nqt * p.nkb);
     p.order_ws = reinterpret_cast<int32_t *>(ws + off_order);
     p.order_ws_stride = (int32_t)(align256((size_t)order_ws_ints(m, spec->mask_b) * sizeof(int32_t)) / sizeof(int32_t));
     return hip_status(bsm::launch_build_block_mask(p, static_cast<hipStream_t>(stream)),

@@ -27,6 +27,7 @@ struct MaskBuildParams {
     int32_t q_off;       // absolute position of query 0
     int32_t npos;        // positions of the document ids: max(T, q_off + q_len)
     int32_t nqt, nkt;    // query tiles, key tiles
+    int32_t kb, nkb;     // key-block width of the row lists (128 or 64), key blocks ceil(T / kb)
     int32_t mask_b;
     int32_t nchunks;     // 256-position chunks of the monotonicity check (over npos)
     int32_t sinks;
@@ -36,7 +37,7 @@ struct MaskBuildParams {
     const int32_t *doc_ids;
     const int32_t *window;
     bsm_block_mask out;
-    uint8_t *cls;        // [mask_b, nqt, nkt]
+    uint8_t *cls;        // [mask_b, nqt, nkb]: class of each row-list block
     int32_t *nonmono;    // [mask_b, nchunks]
     int32_t *order_ws;   // two arrays of order_ws_stride ints: sorted blocks of the row / column orders
     int32_t order_ws_stride;
@@ -46,6 +47,7 @@ struct AttnParams {
     int32_t B, H;
     int32_t T;           // KV_LEN: keys
     int32_t nt;          // key tiles, ceil(T / 128)
+    int32_t kb, nkb;     // key-block width of the row lists (128 or 64), key blocks ceil(T / kb)
     int32_t q_len;       // Q_LEN: queries
     int32_t nqt;         // query tiles, ceil(q_len / 128)
     int32_t q_off;       // absolute position of query 0

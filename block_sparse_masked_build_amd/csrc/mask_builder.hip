@@ -217,7 +217,8 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
     const int i = blockIdx.x;
     const int b = blockIdx.y;
     const int T = p.T;
-    const int nt = p.nkt;
+    const int nt = p.nkb;   // key blocks of the row lists
+    const int kb = p.kb;    // their width
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const bool causal = p.flags & BSM_MASK_CAUSAL;
     const bool document = p.flags & BSM_MASK_DOCUMENT;
@@ -287,12 +288,12 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
     const int bmin = min(x0.z, x1.z), bmax = max(x0.w, x1.w);
     int jlo = nt, jhi = -1;  // tiles that can hold a visible pair
     if (amin <= amax) {
-        jlo = amin / kTile;
-        jhi = amax / kTile;
+        jlo = amin / kb;
+        jhi = amax / kb;
     }
     if (bmin <= bmax) {
-        jlo = bmin / kTile < jlo ? bmin / kTile : jlo;
-        jhi = bmax / kTile > jhi ? bmax / kTile : jhi;
+        jlo = bmin / kb < jlo ? bmin / kb : jlo;
+        jhi = bmax / kb > jhi ? bmax / kb : jhi;
     }
 
     const int64_t row_off = ((int64_t)b * p.nqt + i) * nt;
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
     int run_p = 0, run_f = 0, buf = 0;
     for (int jc = jlo; jc <= jhi; jc += W, buf ^= 1) {
         const int j = jc + tl;
-        const int k0 = j * kTile, k1 = k0 + kTile - 1;
+        const int k0 = j * kb, k1 = k0 + kb - 1;
         bool any = false, all = false;
         if (j <= jhi && ((amin <= k1 && amax >= k0) || (bmin <= k1 && bmax >= k0))) {
             if (!general) {
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
                     for (int kv = c0; kv <= c1; ++kv)
                         if (kv < v.x || kv > v.y) n += doc[kv] == d;
                     any |= n > 0;
-                    all &= n == kTile;
+                    all &= n == kb;
                 }
             }
         }
@@ -382,20 +383,21 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(MaskBuildParams p) {
 }
 
 // A composed mask: one workgroup per query-tile row evaluates every (query,
-// key) pair of every key tile, thread (key kk, row parity rb) taking the 64
-// rows rb, rb + 2, ... of the tile's key kk, and a workgroup vote gives the
-// tile's class.  Pairs outside Q_LEN x KV_LEN are never visible.
+// key) pair of every key block, thread (key kk, row group rb) taking the
+// rows rb, rb + groups, ... of the block's key kk, and a workgroup vote
+// gives the block's class.  Pairs outside Q_LEN x KV_LEN are never visible.
 __global__ __launch_bounds__(kThreads) void rows_table_kernel(MaskBuildParams p) {
     __shared__ int32_t s_docq[kTile];
     const int i = blockIdx.x, b = blockIdx.y;
-    const int nt = p.nkt;
+    const int nt = p.nkb, kb = p.kb;   // key blocks of the row lists and their width
+    const int groups = kThreads / kb;  // row groups: 2 (128-key blocks) or 4 (64-key blocks)
     const bool document = p.flags & BSM_MASK_DOCUMENT;
     const bool windowed = p.flags & BSM_MASK_WINDOW;
     const int sinks = (p.flags & BSM_MASK_SINKS) ? p.sinks : 0;
     const int prefix = p.prefix;
     const int64_t w = windowed ? (int64_t)(*p.window) : 0;
     const int32_t *doc = document ? p.doc_ids + (int64_t)b * p.npos : nullptr;
-    const int kk = threadIdx.x & (kTile - 1), rb = threadIdx.x >> 7;
+    const int kk = threadIdx.x % kb, rb = threadIdx.x / kb;
     if (threadIdx.x < kTile) {
         const int qi = i * kTile + threadIdx.x;
         s_docq[threadIdx.x] = document ? doc[p.q_off + (qi < p.q_len ? qi : p.q_len - 1)] : 0;
@@ -407,12 +409,12 @@ __global__ __launch_bounds__(kThreads) void rows_table_kernel(MaskBuildParams p)
     uint8_t *cls_row = p.cls + row_off;
     int run_p = 0, run_f = 0;
     for (int j = 0; j < nt; ++j) {
-        const int kv = j * kTile + kk;
+        const int kv = j * kb + kk;
         const bool kvalid = kv < p.T;
         const int32_t dk = document && kvalid ? doc[kv] : 0;
         int any = 0, all = kvalid;
-        for (int m = 0; m < kTile / 2; ++m) {
-            const int r = rb + 2 * m;
+        for (int m = 0; m < kTile / groups; ++m) {
+            const int r = rb + groups * m;
             const int qi = i * kTile + r;
             const int64_t qa = (int64_t)p.q_off + qi;
             const int c = qa >= kv, d = document && s_docq[r] == dk, wt = windowed && qa - kv < w;
@@ -443,15 +445,26 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(MaskBuildParams p) {
     __shared__ int s_wp[kWaves], s_wf[kWaves];
     const int j = blockIdx.x;
     const int b = blockIdx.y;
-    const int nq = p.nqt, nk = p.nkt;
-    const uint8_t *cls = p.cls + (int64_t)b * nq * nk;
+    const int nq = p.nqt, nk = p.nkt, nkb = p.nkb;
+    const uint8_t *cls = p.cls + (int64_t)b * nq * nkb;
     const int64_t col_off = ((int64_t)b * nk + j) * nq;
     int32_t *idx_p = p.out.q_indices + col_off;
     int32_t *idx_f = p.out.full_q_indices + col_off;
     int run_p = 0, run_f = 0;
     for (int ib = 0; ib < nq; ib += kThreads) {
         const int i = ib + threadIdx.x;
-        const uint8_t c = i < nq ? cls[(int64_t)i * nk + j] : kEmpty;
+        uint8_t c = kEmpty;
+        if (i < nq) {
+            const uint8_t *row = cls + (int64_t)i * nkb;
+            if (p.kb == kTile) {
+                c = row[j];
+            } else {
+                // a 128 x 128 tile from its two 64-key blocks (the second
+                // may lie past KV_LEN): full iff both are, empty iff both are
+                const uint8_t c0 = row[2 * j], c1 = 2 * j + 1 < nkb ? row[2 * j + 1] : kEmpty;
+                c = (c0 == kFull && c1 == kFull) ? kFull : (c0 == kEmpty && c1 == kEmpty) ? kEmpty : kPartial;
+            }
+        }
         compact_chunk(c == kPartial, c == kFull, i, idx_p, idx_f, run_p, run_f, s_wp, s_wf);
     }
     pad_tail(idx_p, run_p, nq);
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_kernel(MaskBuildParams p)
     int32_t *order = cols ? p.out.q_order : p.out.kv_order;
     int32_t *sorted = p.order_ws + (cols ? p.order_ws_stride : 0);  // block at each sorted position
     const int nt = cols ? p.nkt : p.nqt;    // rows (columns) per mask batch
-    const int len = cols ? p.nqt : p.nkt;   // list length of a row (column)
+    const int len = cols ? p.nqt : p.nkb;   // list length of a row (column)
     const int bpb = (nt + kOrderBlock - 1) / kOrderBlock;  // blocks per mask batch
     const int nb = p.mask_b * bpb;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;

@@ -110,18 +110,27 @@ typedef struct {
     int32_t q_len;           /* Q_LEN; 0: equal to seq_len                         */
     int32_t q_offset;        /* absolute position of query 0 (>= 0)                */
     uint32_t table;          /* TABLE: truth table over the five terms             */
+    int32_t kv_block;        /* key-block width of the row lists: 128 (0 means
+                                128) or 64, i.e. blocks of 128 queries x 64 keys
+                                (tutorial "FlexAttention in PyTorch", "What to
+                                expect, and the sharp edges", item 4: the block
+                                size is a tunable; smaller blocks capture more
+                                sparsity).  The forward and dQ then visit only
+                                the listed 64-key blocks; the column lists stay
+                                128 x 128.                                    */
 } bsm_mask_spec;
 
 /* A block mask: the tile-level summary of a mask predicate (speedrun notes
  * "FlexAttention", tile-summary paragraph: per row of query tiles, the number
  * of tiles that are not fully masked and their column indices; tutorial,
  * "The two hooks": blocks are empty, partial or full).
- * Layout, all device int32, head dimension 1 (shared by every head):
- *   kv_num_blocks       [mask_b, 1, QT]      partial tiles per query-tile row
- *   kv_indices          [mask_b, 1, QT, KT]  their key-tile indices, ascending,
+ * Layout, all device int32, head dimension 1 (shared by every head); KB =
+ * ceil(KV_LEN / kv_block) key blocks (KB = KT for 128-key blocks):
+ *   kv_num_blocks       [mask_b, 1, QT]      partial blocks per query-tile row
+ *   kv_indices          [mask_b, 1, QT, KB]  their key-block indices, ascending,
  *                                            slots >= count hold -1
- *   full_kv_num_blocks  [mask_b, 1, QT]      full tiles per row
- *   full_kv_indices     [mask_b, 1, QT, KT]
+ *   full_kv_num_blocks  [mask_b, 1, QT]      full blocks per row
+ *   full_kv_indices     [mask_b, 1, QT, KB]
  *   q_num_blocks        [mask_b, 1, KT]      transposed view (per key tile,
  *   q_indices           [mask_b, 1, KT, QT]   the query tiles), used by the
  *   full_q_num_blocks   [mask_b, 1, KT]       backward pass
@@ -144,7 +153,7 @@ typedef struct {
  *                                            min(kv_num + full_kv_num, 8191),
  *                                            ties in ascending bm * QT + i, as
  *                                            (bm * QT + i, full_kv_num,
- *                                            kv_num, first listed key tile:
+ *                                            kv_num, first listed key block:
  *                                            the first full one if any, else
  *                                            the first partial one, else 0)
  *   q_order             [mask_b * KT, 4]     the same for the key-tile columns
@@ -287,13 +296,15 @@ size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t capacity, int32_
  * (kv_len[b] - 1, kv); its scores take the score modifications of the
  * forward.
  * bm (optional, may be NULL): the block mask of spec built once for the
- * whole capacity (so capacity is then a multiple of 128).  The step reads
+ * whole capacity (so capacity is then a multiple of 128, and kv_block 128:
+ * 64-key blocks are BSM_E_UNSUPPORTED here).  The step reads
  * only the key tiles listed in the row of query tiles holding the query
  * (every tile some query of that row sees), so a document-masked step reads
  * its document's tiles only; the mask stays valid while the cache grows
  * within the capacity.  Without it every key below the live length is
  * visited, except 1024-key chunks wholly before the window.
- * out: bf16 [B, H, 1, D] (stride_t unused); lse: fp32 [B, H], natural log.
+ * out: [B, H, 1, D] of q's type (stride_t unused); lse: fp32 [B, H],
+ * natural log.
  * workspace: device, >= bsm_decode_workspace_bytes(), 256-byte aligned.
  * Errors: BSM_E_INVALID, BSM_E_UNSUPPORTED (D), BSM_E_WORKSPACE, BSM_E_HIP. */
 bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int32_t D,

@@ -63,6 +63,7 @@ def _build(spec, bm=None, ws=FAKE, nbytes=1 << 30):
     (dict(flags=4), _lib.BSM_E_INVALID),          # WINDOW without window
     (dict(flags=64), _lib.BSM_E_INVALID),         # unknown bit
     (dict(flags=32 | 2), _lib.BSM_E_INVALID),     # composed mask with the document term, no doc_ids
+    (dict(kv_block=32), _lib.BSM_E_INVALID),      # block width other than 64 / 128
     (dict(flags=12, window=FAKE, num_sinks=-1), _lib.BSM_E_INVALID),
 ])
 def test_build_rejects_bad_spec(kw, code):
@@ -201,6 +202,11 @@ def test_decode_rejects_bad_arguments():
     # (fails only at the workspace check here), not with one
     assert call(cap=1000, s=_spec(seq_len=1000), ws=None) == _lib.BSM_E_WORKSPACE
     assert call(cap=1000, s=_spec(seq_len=1000), bm=_bm()) == _lib.BSM_E_INVALID
+    # the decoding step reads block masks of 128-key blocks only
+    assert call(s=_spec(kv_block=64), bm=_bm()) == _lib.BSM_E_UNSUPPORTED
+    assert call(s=_spec(kv_block=64), ws=None) == _lib.BSM_E_WORKSPACE  # fine without a block mask
+    # a workspace for 64-key blocks holds twice the class bytes
+    assert lib.bsm_block_mask_workspace_bytes(ctypes.byref(_spec(seq_len=65536, kv_block=64))) >= 512 * 1024
 
 
 def _cpu(shape, dtype=None):
