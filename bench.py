@@ -270,7 +270,7 @@ class Path:
         self.mod = None
         if w.mod.alibi_slopes is not None or w.mod.softcap is not None:
             self.mod = api.score_mod(w.mod.alibi_slopes, w.mod.softcap)
-        self.bm = api.empty_block_mask(w.T, self.spec.mask_b)
+        self.bm = api.empty_block_mask(self.spec)
         self.ws = api.block_mask_workspace(self.spec)
         self.out = torch.empty_like(self.dev["q"])
         self.lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
@@ -298,11 +298,20 @@ class Path:
 
 def config_detail(api, key, reps):
     """Cold timings of one other workload: mask build, forward and (with a
-    backward) backward medians, and the throughput over visible tiles."""
+    backward) backward medians, and the throughput over visible tiles.  A
+    key ending in "-block64" is that workload with 128 x 64 blocks: its
+    throughput counts the listed 64-key blocks (4 * 128 * 64 * D flops
+    each), the work the kernels do there."""
+    import dataclasses
     import numpy as np
     import torch
     from workloads import make_config
-    w = make_config(key)
+    base, _, variant = key.partition("-block")
+    w = make_config(base if variant else key)
+    kb = TILE
+    if variant:
+        kb = int(variant)
+        w = dataclasses.replace(w, name=w.name + f", 128 x {kb} blocks", spec=dataclasses.replace(w.spec, kv_block=kb))
     path = Path(api, w, w.backward)
     windows = w.windows or [None]
     res = {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D, "mask_b": path.spec.mask_b}
@@ -319,7 +328,7 @@ def config_detail(api, key, reps):
             if w.backward:
                 ev["bwd"].append(timed(path.bwd))
         torch.cuda.synchronize()
-        fl = vis * 4 * TILE * TILE * w.D
+        fl = vis * 4 * TILE * kb * w.D
         r = {"visible_tiles_per_head": vis // w.H, "full_tiles": full, "partial_tiles": part,
              "mask_build_us": round(float(np.median(us(ev["mask"]))), 1),
              "fwd_us": round(float(np.median(us(ev["fwd"]))), 1)}
@@ -476,7 +485,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_configs:
         confs = {}
-        for key in ("1", "2", "2-causal", "2-window", "2-chunks", "3", "4a", "4b", "5"):
+        for key in ("1", "2", "2-block64", "2-causal", "2-window", "2-chunks", "3", "4a", "4b", "5", "5-block64"):
             print(f"[bench] timing workload {key}", file=sys.stderr, flush=True)
             confs[key] = config_detail(api, key, args.config_reps)
         line["detail"]["configs"] = confs
