@@ -107,7 +107,10 @@ struct DqLds {
 // before the scale, the gradient with respect to the score the ALiBi term
 // is added to).  Per step, with the score at key key0 + 4 hl + c:
 //   sum g (k - q) = sum g c + (key0 + 4 hl - q) sum g.
-template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE>
+// RAGGED: the general kernel (see kv_ragged): the last key block's copies
+// are clamped and the block width is read at run time; the other kernel has
+// whole 128-key tiles compiled in (see the forward).
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE, bool RAGGED>
 __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (&qf)[D / 16],
                                const elem8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
                                f32x16 (&dq)[D / 32], float &sg) {
@@ -117,12 +120,11 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto issue = [&](int t, int key0) {
         const uint32_t bf = t & 1;
+        const int nk = RAGGED ? a.kv_len - key0 : kHalf;
         if (MODE == kGather || (MODE == kTable && a.doc))
-            issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, a.npos - key0);
-        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st,
-                                               a.kv_len - key0);
-        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st,
-                                               a.kv_len - key0);
+            issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, RAGGED ? a.npos - key0 : kHalf);
+        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st, nk);
+        issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st, nk);
     };
     if (nsteps <= 0) return;
     int key0 = step_row0(0, a.nfull, a.fidx, a.pidx, a.nt, a.spb);
@@ -208,7 +210,9 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD>
+// TABLE: a composed mask (its own kernel, so that the truth-table
+// evaluation does not take registers from the other masks' kernels).
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, bool TABLE, bool RAGGED>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     a.qpos = qpos;
     a.kv_len = p.T;
     a.npos = p.npos;
-    a.spb = p.kb / kHalf;
+    a.spb = RAGGED ? p.kb / kHalf : 2;  // 128-key tiles in the other kernel (see kv_ragged)
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
@@ -262,7 +266,12 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     const int nsteps = a.spb * (a.nfull + npart);
 
     RowMask rm;
-    const int mode = make_row_mask(p, bm, qpos, rm);
+    int mode = kTable;
+    if (TABLE)
+        make_table_mask(p, qpos, (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0,
+                        (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids[(int64_t)bm * p.npos + qpos] : 0, rm);
+    else
+        mode = make_row_mask(p, bm, qpos, rm);
     KvOffsets off;
     kv_offsets<D>(off);
     DqLds<D> lds;
@@ -304,14 +313,14 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     // first pipeline step waits for everything.
 
     float sg = 0.0f;
-    if (mode == kTable)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+    if (TABLE)
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else if (mode == kGather)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else if (mode == kSinks)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
 
     // Slope gradient of the item: wave sums by a fixed butterfly, then the
     // four waves in order, one partial per (batch, head, query tile); lanes
@@ -577,7 +586,9 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const ele
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, int CMODE>
+// RAGGED: Q_LEN is not a multiple of 128, so the last query tile's copies
+// are clamped (compiled out otherwise).
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool RAGGED>
 __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 16],
                                  const elem8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
                                  int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
@@ -590,7 +601,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const ele
     auto issue = [&](int t, int q0) {
         // rows past Q_LEN repeat the last query's
         const uint32_t bf = t & 1;
-        const int nq = a.q_len - q0;
+        const int nq = RAGGED ? a.q_len - q0 : kTile;
         issue_ints_to_lds_at<kTile>(lds.l2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0), nq);
         issue_ints_to_lds_at<kTile>(lds.delta + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0), nq);
         if (CMODE == kGather || (CMODE == kTable && a.doc))
@@ -627,7 +638,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const ele
     for (int t = a.nfull; t < ntiles; ++t) step(t, std::true_type());
 }
 
-template <int D, bool ALIBI, bool SOFTCAP>
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool RAGGED>
 __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
     const int nt = p.nt;
@@ -670,9 +681,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     const int ntiles = a.nfull + npart;
 
     ColMask cm;
-    const bool table = p.mask_flags & BSM_MASK_TABLE;
     bool gather = false;
-    if (table)
+    if (TABLE)
         make_col_table(p, bm, kpos, (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0, cm);
     else
         gather = make_col_mask(p, bm, kpos, cm);
@@ -703,12 +713,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     // No wait here: the first tile copies are issued while the key rows
     // load (see dq_kernel).
 
-    if (table)
-        dkdv_main<D, ALIBI, SOFTCAP, kTable>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+    if (TABLE)
+        dkdv_main<D, ALIBI, SOFTCAP, kTable, RAGGED>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
     else if (gather)
-        dkdv_main<D, ALIBI, SOFTCAP, kGather>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kGather, RAGGED>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
     else
-        dkdv_main<D, ALIBI, SOFTCAP, kPlain>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kPlain, RAGGED>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
 
     // dK and dV rows of the wave, staged through the query and output-gradient
     // buffers once every wave is done with them (dS was accumulated without
@@ -751,34 +761,57 @@ __global__ __launch_bounds__(kThreads) void slope_reduce_kernel(const float *par
 // the 64K doc+window, causal-in-chunks and ALiBi + soft-cap workloads, the
 // column work order gained for dK/dV only with soft-capped documents and lost
 // elsewhere, while the row order for dQ gained or held everywhere.
-template <int D, bool ALIBI, bool SOFTCAP>
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE>
 void launch_main(const AttnParams &p, hipStream_t stream) {
     AttnParams q = p;
     const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
+    // Composed masks always take the clamped copies; otherwise only a key
+    // (query) length off the block grid makes dQ's (dK/dV's) copies clamped.
+    // (The non-clamped branches name RAGGED = TABLE: with TABLE they are never
+    // taken, and the name then matches the clamped kernel instead of adding
+    // an unused one.)
+    const bool kv_r = TABLE || kv_ragged(p), q_r = TABLE || p.q_len % kTile != 0;
     // dq_kernel writes Delta and L of every query row (every row is one of
     // its items), which dkdv_kernel reads.
     if (ALIBI && p.dslopes) {
-        hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI>), dq_grid, block, 0, stream, q);
+        if (kv_r)
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI, TABLE, true>), dq_grid, block, 0, stream, q);
+        else
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI, TABLE, TABLE>), dq_grid, block, 0, stream, q);
         hipLaunchKernelGGL(slope_reduce_kernel, dim3(p.H), block, 0, stream, p.dslope_part, p.dslopes, p.B, p.H,
                            p.nqt);
     } else {
-        hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false>), dq_grid, block, 0, stream, q);
+        if (kv_r)
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, true>), dq_grid, block, 0, stream, q);
+        else
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, TABLE>), dq_grid, block, 0, stream, q);
     }
-    hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP>), dkdv_grid, block, 0, stream, q);
+    if (q_r)
+        hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, true>), dkdv_grid, block, 0, stream, q);
+    else
+        hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, TABLE>), dkdv_grid, block, 0, stream, q);
+}
+
+template <int D, bool TABLE>
+void launch_mods(const AttnParams &p, hipStream_t stream) {
+    const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
+    const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
+    if (alibi && cap)
+        launch_main<D, true, true, TABLE>(p, stream);
+    else if (alibi)
+        launch_main<D, true, false, TABLE>(p, stream);
+    else if (cap)
+        launch_main<D, false, true, TABLE>(p, stream);
+    else
+        launch_main<D, false, false, TABLE>(p, stream);
 }
 
 template <int D>
 hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
-    const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
-    const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
-    if (alibi && cap)
-        launch_main<D, true, true>(p, stream);
-    else if (alibi)
-        launch_main<D, true, false>(p, stream);
-    else if (cap)
-        launch_main<D, false, true>(p, stream);
+    if (p.mask_flags & BSM_MASK_TABLE)
+        launch_mods<D, true>(p, stream);
     else
-        launch_main<D, false, false>(p, stream);
+        launch_mods<D, false>(p, stream);
     return hipGetLastError();
 }
 

@@ -819,11 +819,6 @@ __device__ inline void make_table_mask(const AttnParams &p, int qpos, int window
 }
 
 __device__ inline int make_row_mask(const AttnParams &p, int bm, int qpos, RowMask &rm) {
-    if (p.mask_flags & BSM_MASK_TABLE) {
-        make_table_mask(p, qpos, (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0,
-                        (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids[(int64_t)bm * p.npos + qpos] : 0, rm);
-        return kTable;
-    }
     const bool doc_on = p.mask_flags & BSM_MASK_DOCUMENT;
     int ds = 0, de = p.T - 1;
     rm.docq = 0;
@@ -862,6 +857,12 @@ __device__ inline bool block_none_visible(const RowMask &rm, int kf, int kl) {
                       (MODE == kPlain || rm.shi < kf || rm.slo > kl || rm.shi < rm.slo);
     return __all(none);
 }
+
+// Whether the row direction (forward, dQ) needs its general kernel: a key
+// length off the 128-key grid (the last tile's copies are clamped; its
+// second half may lie wholly past KV_LEN) or 64-key blocks.  The other
+// kernel has whole 128-key tiles and two 64-key steps per tile compiled in.
+inline bool kv_ragged(const AttnParams &p) { return p.T % kTile != 0 || p.kb != kTile; }
 
 // ---------------------------------------------------------------- item order
 // Both attention directions run one workgroup per item: a row (forward, dQ)

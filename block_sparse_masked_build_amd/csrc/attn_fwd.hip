@@ -164,13 +164,18 @@ struct FwdArgs {
     int b, h, bm, row;
     int nfull, ntiles, nt, first;  // listed blocks (full, all), blocks per row, first listed block
     int kblk, spb;                  // block width (128 or 64 keys) and 64-key steps per block
-    int qidx;  // this lane's query index (may lie past Q_LEN on the last row)
-    int qpos;  // its absolute position (the last query's for lanes past Q_LEN)
+    int qpos;  // this lane's absolute query position (the last query's for lanes past Q_LEN)
     float scale, scale_log2, slope, cap, inv_cap;
     ModK mk;  // folded score-modification constants
 };
 
-template <bool ALIBI, bool SOFTCAP>
+// This lane's query index (past Q_LEN on a cut-short last row), recomputed
+// where needed rather than kept live through the item.
+__device__ inline int lane_query(const FwdArgs &a) {
+    return a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
+}
+
+template <bool ALIBI, bool SOFTCAP, bool RAGGED>
 __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &rec, FwdArgs &a) {
     const int nt = p.nkb;  // key blocks of the row lists
     const int packed = min(max(rec.packed, 0), p.mask_b * p.nqt - 1);
@@ -186,10 +191,9 @@ __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &re
     a.ntiles = a.nfull + min(max(rec.npart, 0), nt);
     a.first = clamp_tile(rec.first, nt);
     a.nt = nt;
-    a.kblk = p.kb;
-    a.spb = p.kb / kHalf;
-    a.qidx = a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
-    a.qpos = p.q_off + min(a.qidx, p.q_len - 1);
+    a.kblk = RAGGED ? p.kb : kTile;  // 128-key tiles in the other kernel (see kv_ragged)
+    a.spb = a.kblk / kHalf;
+    a.qpos = p.q_off + min(lane_query(a), p.q_len - 1);
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[a.h] : 0.0f;
@@ -246,10 +250,6 @@ struct RowLoad {
 // the mode the row needs (uniform over the workgroup: the document-range
 // sentinel marks whole mask rows).
 __device__ inline int finish_row_mask(const AttnParams &p, int qpos, const RowLoad &rl, int window, RowMask &rm) {
-    if (p.mask_flags & BSM_MASK_TABLE) {
-        make_table_mask(p, qpos, window, rl.docq, rm);
-        return kTable;
-    }
     int ds = rl.ds, de = rl.de;
     const bool gather = ds < 0;
     if (gather) {
@@ -286,7 +286,15 @@ struct FwdSmem {
 // halves of the first listed tile) into buffers 0 / 0 / 1, and loads of the
 // query rows, the tile list and the row data.  Every item has an even
 // number of steps, so each item starts on buffer 0.
-template <int D>
+// Rows of a 64-key copy that exist, given n = KV_LEN (or positions) - its
+// first key.  RAGGED (the general kernel, see kv_ragged): the last block may
+// be cut short and its copies are clamped; otherwise every copy is whole and
+// the clamping code is compiled out -- its mere presence in the step loop
+// cost the forward 6-9% on whole-tile shapes.
+template <bool RAGGED>
+__device__ inline int rows_left(int n) { return RAGGED ? n : kHalf; }
+
+template <int D, bool RAGGED>
 __device__ __attribute__((always_inline)) inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, elem8 (&qf)[D / 16],
                                   TileList &tl, RowLoad &rl) {
     if (a.ntiles > 0) {
@@ -294,16 +302,16 @@ __device__ __attribute__((always_inline)) inline void item_start(const AttnParam
         const int k0 = a.first * a.kblk;
         const int k1 = step1_key0(a);
         if (a.doc) {
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0, p.npos - k0);
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k1, p.npos - k1);
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0, rows_left<RAGGED>(p.npos - k0));
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k1, rows_left<RAGGED>(p.npos - k1));
         }
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st, p.T - k0);
-        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st, p.T - k0);
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)k1 * p.k_st, p.k_st, p.T - k1);
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st, rows_left<RAGGED>(p.T - k0));
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st, rows_left<RAGGED>(p.T - k0));
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)k1 * p.k_st, p.k_st, rows_left<RAGGED>(p.T - k1));
     }
     const int hl = (threadIdx.x & 63) >> 5;
     const elem_t *qrow = static_cast<const elem_t *>(p.q) + a.b * p.q_sb + a.h * p.q_sh +
-                         (int64_t)min(a.qidx, p.q_len - 1) * p.q_st;
+                         (int64_t)min(lane_query(a), p.q_len - 1) * p.q_st;
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) qf[st] = *reinterpret_cast<const elem8 *>(qrow + st * 16 + hl * 8);
     const int lane = threadIdx.x & 63;
@@ -333,8 +341,9 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
     const int q0w = a.row * kTile + wv * 32;  // the wave's first query index
     elem_t *ob = static_cast<elem_t *>(p.o) + a.b * p.o_sb + a.h * p.o_sh + (int64_t)q0w * p.o_st;
     store_rows_staged<D>(ob, p.o_st, o, inv, stage + (uint32_t)(wv * 32 * 2 * D), p.q_len - q0w);
-    if (hl == 0 && a.qidx < p.q_len)
-        p.lse[((int64_t)a.b * p.H + a.h) * p.q_len + a.qidx] =
+    const int qidx = lane_query(a);
+    if (hl == 0 && qidx < p.q_len)
+        p.lse[((int64_t)a.b * p.H + a.h) * p.q_len + qidx] =
             l_tot > 0.0f ? (m + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
@@ -358,7 +367,7 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
 //
 // The item's output is written at its end, staged through the K buffers,
 // which no wave reads during the last step.
-template <int D, bool ALIBI, bool SOFTCAP, int MODE>
+template <int D, bool ALIBI, bool SOFTCAP, int MODE, bool RAGGED>
 __device__ __attribute__((always_inline)) inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
                                 const elem8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
                                 f32x16 (&o)[D / 32], float &m, float &l) {
@@ -382,11 +391,13 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     auto step_key0 = [&](int t) { return row_step_key0(tl, a, t); };
     auto issue_k = [&](int t, int key0) {
         if (MODE == kGather || (MODE == kTable && a.doc))
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, p.npos - key0);
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st, p.T - key0);
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, rows_left<RAGGED>(p.npos - key0));
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st,
+                                           rows_left<RAGGED>(p.T - key0));
     };
     auto issue_v = [&](int t, int key0) {
-        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[t & 1], a.vb + (int64_t)key0 * p.v_st, p.v_st, p.T - key0);
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[t & 1], a.vb + (int64_t)key0 * p.v_st, p.v_st,
+                                           rows_left<RAGGED>(p.T - key0));
     };
     // Row maximum of a step in the log2 domain (without score modifications
     // the scale is applied here and folded into the exponentials).
@@ -484,7 +495,9 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
 }
 
 // One item per workgroup (workgroups past the last item exit at once).
-template <int D, bool ALIBI, bool SOFTCAP>
+// TABLE: a composed mask (its own kernel, so that the truth-table
+// evaluation does not take registers from the other masks' kernels).
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool RAGGED>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
     const ItemOrder ord(p, kQueues);
@@ -494,27 +507,44 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd
     int e, rem;
     ord.decode(k, e, rem);
     FwdArgs cur;
-    item_args<ALIBI, SOFTCAP>(p, rem, load_rec(p.kv_order, e), cur);
+    item_args<ALIBI, SOFTCAP, RAGGED>(p, rem, load_rec(p.kv_order, e), cur);
     OperandOffsets<D> off;
     operand_offsets<D>(off);
     elem8 qf[D / 16];
     TileList tl;
     RowLoad rl;
-    item_start<D>(p, sm, cur, qf, tl, rl);
+    item_start<D, RAGGED>(p, sm, cur, qf, tl, rl);
     f32x16 o[D / 32];
     float m = -INFINITY, l = 0.0f;
     wait_vmcnt<0>();  // the item's first tiles, query rows, tile list and row data
     tile_barrier();
     RowMask rm;
+    if (TABLE) {
+        make_table_mask(p, cur.qpos, window, rl.docq, rm);
+        item_run<D, ALIBI, SOFTCAP, kTable, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        return;
+    }
     const int mode = finish_row_mask(p, cur.qpos, rl, window, rm);
-    if (mode == kTable)
-        item_run<D, ALIBI, SOFTCAP, kTable>(p, cur, tl, rm, qf, off, sm, o, m, l);
-    else if (mode == kGather)
-        item_run<D, ALIBI, SOFTCAP, kGather>(p, cur, tl, rm, qf, off, sm, o, m, l);
+    if (mode == kGather)
+        item_run<D, ALIBI, SOFTCAP, kGather, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
     else if (mode == kSinks)
-        item_run<D, ALIBI, SOFTCAP, kSinks>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kSinks, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
     else
-        item_run<D, ALIBI, SOFTCAP, kPlain>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kPlain, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
+}
+
+template <int D, bool TABLE, bool RAGGED>
+hipError_t launch_mods(const AttnParams &q, dim3 grid, bool alibi, bool cap, hipStream_t stream) {
+    const dim3 block(kThreads);
+    if (alibi && cap)
+        hipLaunchKernelGGL((fwd_kernel<D, true, true, TABLE, RAGGED>), grid, block, 0, stream, q);
+    else if (alibi)
+        hipLaunchKernelGGL((fwd_kernel<D, true, false, TABLE, RAGGED>), grid, block, 0, stream, q);
+    else if (cap)
+        hipLaunchKernelGGL((fwd_kernel<D, false, true, TABLE, RAGGED>), grid, block, 0, stream, q);
+    else
+        hipLaunchKernelGGL((fwd_kernel<D, false, false, TABLE, RAGGED>), grid, block, 0, stream, q);
+    return hipGetLastError();
 }
 
 template <int D>
@@ -523,15 +553,12 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid(item_order(q)), block(kThreads);  // one workgroup per (queue, grab index) pair
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
-    if (alibi && cap)
-        hipLaunchKernelGGL((fwd_kernel<D, true, true>), grid, block, 0, stream, q);
-    else if (alibi)
-        hipLaunchKernelGGL((fwd_kernel<D, true, false>), grid, block, 0, stream, q);
-    else if (cap)
-        hipLaunchKernelGGL((fwd_kernel<D, false, true>), grid, block, 0, stream, q);
-    else
-        hipLaunchKernelGGL((fwd_kernel<D, false, false>), grid, block, 0, stream, q);
-    return hipGetLastError();
+    // composed masks always take the clamped copies (one kernel per mod)
+    if (p.mask_flags & BSM_MASK_TABLE)
+        return launch_mods<D, true, true>(q, grid, alibi, cap, stream);
+    if (kv_ragged(p))
+        return launch_mods<D, false, true>(q, grid, alibi, cap, stream);
+    return launch_mods<D, false, false>(q, grid, alibi, cap, stream);
 }
 
 }  // namespace
