@@ -467,8 +467,9 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": measured_traffic() if args.workload == "2" else None,
-            "kernel": "fwd_kernel<%d,%s,%s>" % (w.D, str(w.mod.alibi_slopes is not None).lower(),
-                                                str(w.mod.softcap is not None).lower()),
+            "kernel": "fwd_kernel<%d,%s,%s,false,%s>" % (
+                w.D, str(w.mod.alibi_slopes is not None).lower(), str(w.mod.softcap is not None).lower(),
+                str(w.T % TILE != 0).lower()),
         },
         "detail": extra,
     }
