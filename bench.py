@@ -318,9 +318,10 @@ def config_detail(api, key, reps):
     per_win = {}
     for win in windows:
         vis, full, part = tiles_per_bh(api, path.spec, path.bm, path.ws, w, win)
-        path.fwd()
-        if w.backward:
-            path.bwd()
+        for _ in range(3):  # warm-up: a lighter workload just ran, let the clocks settle
+            path.fwd()
+            if w.backward:
+                path.bwd()
         ev = {"mask": [], "fwd": [], "bwd": []}
         for _ in range(reps):
             ev["mask"].append(timed(path.build))

@@ -107,10 +107,10 @@ struct DqLds {
 // before the scale, the gradient with respect to the score the ALiBi term
 // is added to).  Per step, with the score at key key0 + 4 hl + c:
 //   sum g (k - q) = sum g c + (key0 + 4 hl - q) sum g.
-// RAGGED: the general kernel (see kv_ragged): the last key block's copies
+// GENERAL: the general kernel (see kv_ragged): the last key block's copies
 // are clamped and the block width is read at run time; the other kernel has
 // whole 128-key tiles compiled in (see the forward).
-template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE, bool RAGGED>
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE, bool GENERAL>
 __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (&qf)[D / 16],
                                const elem8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
                                f32x16 (&dq)[D / 32], float &sg) {
@@ -120,9 +120,9 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto issue = [&](int t, int key0) {
         const uint32_t bf = t & 1;
-        const int nk = RAGGED ? a.kv_len - key0 : kHalf;
+        const int nk = GENERAL ? a.kv_len - key0 : kHalf;
         if (MODE == kGather || (MODE == kTable && a.doc))
-            issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, RAGGED ? a.npos - key0 : kHalf);
+            issue_ints_to_lds_at<kHalf>(lds.doc + bf * kHalf * 4, a.doc + key0, GENERAL ? a.npos - key0 : kHalf);
         issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.k + bf * kTB, a.kb + (int64_t)key0 * a.k_st, a.k_st, nk);
         issue_tile_to_lds_at<D, kSwzKV, kHalf>(lds.v + bf * kTB, a.vb + (int64_t)key0 * a.v_st, a.v_st, nk);
     };
@@ -212,7 +212,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
 
 // TABLE: a composed mask (its own kernel, so that the truth-table
 // evaluation does not take registers from the other masks' kernels).
-template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, bool TABLE, bool RAGGED>
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, bool TABLE, bool GENERAL>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
 
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     a.qpos = qpos;
     a.kv_len = p.T;
     a.npos = p.npos;
-    a.spb = RAGGED ? p.kb / kHalf : 2;  // 128-key tiles in the other kernel (see kv_ragged)
+    a.spb = GENERAL ? p.kb / kHalf : 2;  // 128-key tiles in the other kernel (see kv_ragged)
     a.scale = p.scale;
     a.scale_log2 = p.scale * kLog2e;
     a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
@@ -314,13 +314,13 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
 
     float sg = 0.0f;
     if (TABLE)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else if (mode == kGather)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else if (mode == kSinks)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
     else
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, RAGGED>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
 
     // Slope gradient of the item: wave sums by a fixed butterfly, then the
     // four waves in order, one partial per (batch, head, query tile); lanes
@@ -586,9 +586,9 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const ele
     }
 }
 
-// RAGGED: Q_LEN is not a multiple of 128, so the last query tile's copies
+// GENERAL: Q_LEN is not a multiple of 128, so the last query tile's copies
 // are clamped (compiled out otherwise).
-template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool RAGGED>
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool GENERAL>
 __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 16],
                                  const elem8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
                                  int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
@@ -601,7 +601,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const ele
     auto issue = [&](int t, int q0) {
         // rows past Q_LEN repeat the last query's
         const uint32_t bf = t & 1;
-        const int nq = RAGGED ? a.q_len - q0 : kTile;
+        const int nq = GENERAL ? a.q_len - q0 : kTile;
         issue_ints_to_lds_at<kTile>(lds.l2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0), nq);
         issue_ints_to_lds_at<kTile>(lds.delta + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0), nq);
         if (CMODE == kGather || (CMODE == kTable && a.doc))
@@ -638,7 +638,7 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const ele
     for (int t = a.nfull; t < ntiles; ++t) step(t, std::true_type());
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool RAGGED>
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL>
 __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
     const int nt = p.nt;
@@ -714,11 +714,11 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     // load (see dq_kernel).
 
     if (TABLE)
-        dkdv_main<D, ALIBI, SOFTCAP, kTable, RAGGED>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kTable, GENERAL>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
     else if (gather)
-        dkdv_main<D, ALIBI, SOFTCAP, kGather, RAGGED>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kGather, GENERAL>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
     else
-        dkdv_main<D, ALIBI, SOFTCAP, kPlain, RAGGED>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kPlain, GENERAL>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
 
     // dK and dV rows of the wave, staged through the query and output-gradient
     // buffers once every wave is done with them (dS was accumulated without
@@ -767,7 +767,7 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
     const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
     // Composed masks always take the clamped copies; otherwise only a key
     // (query) length off the block grid makes dQ's (dK/dV's) copies clamped.
-    // (The non-clamped branches name RAGGED = TABLE: with TABLE they are never
+    // (The non-clamped branches name GENERAL = TABLE: with TABLE they are never
     // taken, and the name then matches the clamped kernel instead of adding
     // an unused one.)
     const bool kv_r = TABLE || kv_ragged(p), q_r = TABLE || p.q_len % kTile != 0;

@@ -175,7 +175,7 @@ __device__ inline int lane_query(const FwdArgs &a) {
     return a.row * kTile + (threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
 }
 
-template <bool ALIBI, bool SOFTCAP, bool RAGGED>
+template <bool ALIBI, bool SOFTCAP, bool GENERAL>
 __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &rec, FwdArgs &a) {
     const int nt = p.nkb;  // key blocks of the row lists
     const int packed = min(max(rec.packed, 0), p.mask_b * p.nqt - 1);
@@ -191,7 +191,7 @@ __device__ inline void item_args(const AttnParams &p, int rem, const WorkRec &re
     a.ntiles = a.nfull + min(max(rec.npart, 0), nt);
     a.first = clamp_tile(rec.first, nt);
     a.nt = nt;
-    a.kblk = RAGGED ? p.kb : kTile;  // 128-key tiles in the other kernel (see kv_ragged)
+    a.kblk = GENERAL ? p.kb : kTile;  // 128-key tiles in the other kernel (see kv_ragged)
     a.spb = a.kblk / kHalf;
     a.qpos = p.q_off + min(lane_query(a), p.q_len - 1);
     a.scale = p.scale;
@@ -287,14 +287,14 @@ struct FwdSmem {
 // query rows, the tile list and the row data.  Every item has an even
 // number of steps, so each item starts on buffer 0.
 // Rows of a 64-key copy that exist, given n = KV_LEN (or positions) - its
-// first key.  RAGGED (the general kernel, see kv_ragged): the last block may
+// first key.  GENERAL (the general kernel, see kv_ragged): the last block may
 // be cut short and its copies are clamped; otherwise every copy is whole and
 // the clamping code is compiled out -- its mere presence in the step loop
 // cost the forward 6-9% on whole-tile shapes.
-template <bool RAGGED>
-__device__ inline int rows_left(int n) { return RAGGED ? n : kHalf; }
+template <bool GENERAL>
+__device__ inline int rows_left(int n) { return GENERAL ? n : kHalf; }
 
-template <int D, bool RAGGED>
+template <int D, bool GENERAL>
 __device__ __attribute__((always_inline)) inline void item_start(const AttnParams &p, FwdSmem<D> &sm, const FwdArgs &a, elem8 (&qf)[D / 16],
                                   TileList &tl, RowLoad &rl) {
     if (a.ntiles > 0) {
@@ -302,12 +302,12 @@ __device__ __attribute__((always_inline)) inline void item_start(const AttnParam
         const int k0 = a.first * a.kblk;
         const int k1 = step1_key0(a);
         if (a.doc) {
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0, rows_left<RAGGED>(p.npos - k0));
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k1, rows_left<RAGGED>(p.npos - k1));
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[0]), a.doc + k0, rows_left<GENERAL>(p.npos - k0));
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[1]), a.doc + k1, rows_left<GENERAL>(p.npos - k1));
         }
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st, rows_left<RAGGED>(p.T - k0));
-        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st, rows_left<RAGGED>(p.T - k0));
-        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)k1 * p.k_st, p.k_st, rows_left<RAGGED>(p.T - k1));
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[0], a.kb + (int64_t)k0 * p.k_st, p.k_st, rows_left<GENERAL>(p.T - k0));
+        issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[0], a.vb + (int64_t)k0 * p.v_st, p.v_st, rows_left<GENERAL>(p.T - k0));
+        issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[1], a.kb + (int64_t)k1 * p.k_st, p.k_st, rows_left<GENERAL>(p.T - k1));
     }
     const int hl = (threadIdx.x & 63) >> 5;
     const elem_t *qrow = static_cast<const elem_t *>(p.q) + a.b * p.q_sb + a.h * p.q_sh +
@@ -367,7 +367,7 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
 //
 // The item's output is written at its end, staged through the K buffers,
 // which no wave reads during the last step.
-template <int D, bool ALIBI, bool SOFTCAP, int MODE, bool RAGGED>
+template <int D, bool ALIBI, bool SOFTCAP, int MODE, bool GENERAL>
 __device__ __attribute__((always_inline)) inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
                                 const elem8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
                                 f32x16 (&o)[D / 32], float &m, float &l) {
@@ -391,13 +391,13 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     auto step_key0 = [&](int t) { return row_step_key0(tl, a, t); };
     auto issue_k = [&](int t, int key0) {
         if (MODE == kGather || (MODE == kTable && a.doc))
-            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, rows_left<RAGGED>(p.npos - key0));
+            issue_ints_to_lds_at<kHalf>(lds_addr(sm.doc[t & 1]), a.doc + key0, rows_left<GENERAL>(p.npos - key0));
         issue_tile_to_lds<D, kSwzK, kHalf>(sm.k[t & 1], a.kb + (int64_t)key0 * p.k_st, p.k_st,
-                                           rows_left<RAGGED>(p.T - key0));
+                                           rows_left<GENERAL>(p.T - key0));
     };
     auto issue_v = [&](int t, int key0) {
         issue_tile_to_lds<D, kSwzV, kHalf>(sm.v[t & 1], a.vb + (int64_t)key0 * p.v_st, p.v_st,
-                                           rows_left<RAGGED>(p.T - key0));
+                                           rows_left<GENERAL>(p.T - key0));
     };
     // Row maximum of a step in the log2 domain (without score modifications
     // the scale is applied here and folded into the exponentials).
@@ -497,7 +497,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
 // One item per workgroup (workgroups past the last item exit at once).
 // TABLE: a composed mask (its own kernel, so that the truth-table
 // evaluation does not take registers from the other masks' kernels).
-template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool RAGGED>
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL>
 __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
     const ItemOrder ord(p, kQueues);
@@ -507,13 +507,13 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd
     int e, rem;
     ord.decode(k, e, rem);
     FwdArgs cur;
-    item_args<ALIBI, SOFTCAP, RAGGED>(p, rem, load_rec(p.kv_order, e), cur);
+    item_args<ALIBI, SOFTCAP, GENERAL>(p, rem, load_rec(p.kv_order, e), cur);
     OperandOffsets<D> off;
     operand_offsets<D>(off);
     elem8 qf[D / 16];
     TileList tl;
     RowLoad rl;
-    item_start<D, RAGGED>(p, sm, cur, qf, tl, rl);
+    item_start<D, GENERAL>(p, sm, cur, qf, tl, rl);
     f32x16 o[D / 32];
     float m = -INFINITY, l = 0.0f;
     wait_vmcnt<0>();  // the item's first tiles, query rows, tile list and row data
@@ -521,29 +521,29 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd
     RowMask rm;
     if (TABLE) {
         make_table_mask(p, cur.qpos, window, rl.docq, rm);
-        item_run<D, ALIBI, SOFTCAP, kTable, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kTable, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
         return;
     }
     const int mode = finish_row_mask(p, cur.qpos, rl, window, rm);
     if (mode == kGather)
-        item_run<D, ALIBI, SOFTCAP, kGather, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kGather, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
     else if (mode == kSinks)
-        item_run<D, ALIBI, SOFTCAP, kSinks, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kSinks, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
     else
-        item_run<D, ALIBI, SOFTCAP, kPlain, RAGGED>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kPlain, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
 }
 
-template <int D, bool TABLE, bool RAGGED>
+template <int D, bool TABLE, bool GENERAL>
 hipError_t launch_mods(const AttnParams &q, dim3 grid, bool alibi, bool cap, hipStream_t stream) {
     const dim3 block(kThreads);
     if (alibi && cap)
-        hipLaunchKernelGGL((fwd_kernel<D, true, true, TABLE, RAGGED>), grid, block, 0, stream, q);
+        hipLaunchKernelGGL((fwd_kernel<D, true, true, TABLE, GENERAL>), grid, block, 0, stream, q);
     else if (alibi)
-        hipLaunchKernelGGL((fwd_kernel<D, true, false, TABLE, RAGGED>), grid, block, 0, stream, q);
+        hipLaunchKernelGGL((fwd_kernel<D, true, false, TABLE, GENERAL>), grid, block, 0, stream, q);
     else if (cap)
-        hipLaunchKernelGGL((fwd_kernel<D, false, true, TABLE, RAGGED>), grid, block, 0, stream, q);
+        hipLaunchKernelGGL((fwd_kernel<D, false, true, TABLE, GENERAL>), grid, block, 0, stream, q);
     else
-        hipLaunchKernelGGL((fwd_kernel<D, false, false, TABLE, RAGGED>), grid, block, 0, stream, q);
+        hipLaunchKernelGGL((fwd_kernel<D, false, false, TABLE, GENERAL>), grid, block, 0, stream, q);
     return hipGetLastError();
 }
 
