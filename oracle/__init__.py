@@ -30,4 +30,7 @@ from .attention import (  # noqa: F401
     backward_dq_rows,
     backward_dkdv_cols,
     slope_grad_dense,
+    bias_grad_dense,
+    bias_index,
+    bias_radius,
 )

@@ -9,6 +9,10 @@ What is computed, per batch element b, head h and query position q
                                                    PyTorch", Pattern 3; q the
                                                    query's absolute position,
                                                    q_offset + its index)
+  bias:    s_j <- s_j + bias[h, R + clip(q - j, -R, R)]
+                                                 (a learned relative-position
+                                                   bias, same section; reading
+                                                   below)
   cap:     s_j <- c * tanh(s_j / c)              (same section, c = 30 there)
   out_q  = sum_{j in V_q} softmax(s)_j v_j        over visible keys only
   lse_q  = log sum_{j in V_q} exp(s_j)            natural log
@@ -19,7 +23,11 @@ removes pairs) and the exact, fused softmax attention they feed (speedrun
 notes "FlexAttention", Context paragraph).  Readings taken where they are
 silent: the scale is applied before any score modification; ALiBi comes
 before the soft-cap when both are on; ALiBi uses absolute positions; a query
-with no visible key gives out = 0 and lse = -inf.
+with no visible key gives out = 0 and lse = -inf.  The pages name a learned
+relative-position bias without fixing its form; the reading here is the
+clipped relative position of Shaw, Uszkoreit and Vaswani (2018) with one
+scalar per head: a table of 2R + 1 entries per head indexed by the
+query-key distance clipped to [-R, R], added like ALiBi before the cap.
 
 Backward, with upstream gradient dO (the pages state that the score
 modifications are differentiable and get a fused backward pass -- tutorial,
@@ -38,6 +46,11 @@ tutorial, Pattern 3).  The slope enters every visible score through
 u_qj = ... - slope[h] (q - j), so
   dL/dslope[h] = sum over b and visible (q, j) of g_qj (j - q)
 with g as above (the gradient with respect to u).
+
+The same for the bias table: every visible pair adds g_qj to the entry it
+reads, so
+  dL/dbias[h, R + r] = sum over b and visible (q, j) with clip(q - j, -R, R) = r
+                       of g_qj.
 
 Operand masses (for the parity bound of a bf16 implementation).  Each
 output element is a sum of products; its "mass" is the same sum with every
@@ -88,11 +101,29 @@ def _scores(Qr, Kc, rows, cols, h, scale, mod, q_offset=0):
     if mod is not None and mod.alibi_slopes is not None:
         slope = float(mod.alibi_slopes[h])
         s = s - slope * ((rows[:, None] + q_offset) - cols[None, :]).astype(np.float64)
+    if mod is not None and getattr(mod, "bias_table", None) is not None:
+        s = s + np.asarray(mod.bias_table, dtype=np.float64)[h][bias_index(mod, rows + q_offset, cols)]
     u = s
     if mod is not None and mod.softcap is not None:
         c = float(mod.softcap)
         s = c * np.tanh(u / c)
     return u, s
+
+
+def bias_radius(mod):
+    """R of a bias table with 2R + 1 entries per head."""
+    n = np.asarray(mod.bias_table).shape[1]
+    assert n % 2 == 1, "a bias table has 2R + 1 entries per head"
+    return (n - 1) // 2
+
+
+def bias_index(mod, qpos, cols):
+    """Table entry of every (query position, key) pair, [len(qpos), len(cols)]:
+    R + the distance q - kv clipped to [-R, R] (one learned scalar per head
+    and clipped relative distance)."""
+    R = bias_radius(mod)
+    d = np.asarray(qpos, dtype=np.int64)[:, None] - np.asarray(cols, dtype=np.int64)[None, :]
+    return np.clip(d, -R, R) + R
 
 
 def _row_block(Q, K, V, spec, mod, b, h, rows, scale, restrict):
@@ -278,3 +309,24 @@ def slope_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=Non
         total += float(term.sum())
         mass += float(np.abs(term).sum())
     return total, mass
+
+
+def bias_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=None):
+    """(dL/dbias[h, :] for batch element b, the same sums of |g|), float64
+    [2R + 1] each, over every visible pair (small T).  out, lse: as for
+    slope_grad_dense."""
+    T, D = Q.shape
+    sc = _scale(D, scale)
+    R = bias_radius(mod)
+    if out is None or lse is None:
+        out, lse = forward_dense(Q, K, V, spec, mod, b, h, scale)
+    allcols = np.arange(K.shape[0])
+    grad = np.zeros(2 * R + 1, dtype=np.float64)
+    mass = np.zeros(2 * R + 1, dtype=np.float64)
+    for a in range(0, T, ROW_CHUNK):
+        r = np.arange(a, min(T, a + ROW_CHUNK))
+        g, _ = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc)
+        idx = bias_index(mod, r + _qoff(spec), allcols)
+        grad += np.bincount(idx.ravel(), weights=g.ravel(), minlength=2 * R + 1)
+        mass += np.bincount(idx.ravel(), weights=np.abs(g).ravel(), minlength=2 * R + 1)
+    return grad, mass

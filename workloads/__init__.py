@@ -16,6 +16,7 @@ from .generators import (  # noqa: F401
     random_bf16,
     random_f16,
     alibi_slopes,
+    bias_table,
     make_config,
     CONFIG_NAMES,
 )

@@ -80,9 +80,12 @@ class MaskSpecData:
 
 @dataclasses.dataclass
 class ScoreModData:
-    """ALiBi slopes (float32 [H]) and a soft-cap value (None: off)."""
+    """ALiBi slopes (float32 [H]), a soft-cap value (None: off) and a
+    relative-position bias table (float32 [H, 2R + 1], entry R + d for the
+    query-key distance d in [-R, R]; None: off)."""
     alibi_slopes: Optional[np.ndarray] = None
     softcap: Optional[float] = None
+    bias_table: Optional[np.ndarray] = None
 
 
 @dataclasses.dataclass
@@ -147,6 +150,12 @@ def doc_ids_lognormal(T: int, median: float, sigma: float, lo: int, hi: int,
 def doc_ids_chunks(T: int, chunk: int) -> np.ndarray:
     """Independent fixed-size chunks: position i belongs to chunk i // chunk."""
     return (np.arange(T, dtype=np.int64) // chunk).astype(np.int32)
+
+
+def bias_table(H: int, R: int, seed: int, sd: float = 1.0) -> np.ndarray:
+    """A synthetic learned relative-position bias: float32 [H, 2R + 1] of
+    N(0, sd^2) draws from numpy's default_rng(seed)."""
+    return (np.random.default_rng(seed).standard_normal((H, 2 * R + 1)) * sd).astype(np.float32)
 
 
 def alibi_slopes(H: int) -> np.ndarray:
