@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "BSM_OK", 1: "BSM_E_INVALID", 2: "BSM_E_UNSUPPORTED",
 
 BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX = 1, 2, 4, 8, 16
 BSM_MASK_TABLE = 32
-BSM_MOD_ALIBI, BSM_MOD_SOFTCAP = 1, 2
+BSM_MOD_ALIBI, BSM_MOD_SOFTCAP, BSM_MOD_BIAS = 1, 2, 4
+BSM_BIAS_MAX_RADIUS = 1024
 BSM_DTYPE_BF16, BSM_DTYPE_F16 = 0, 1
 
 
@@ -45,7 +46,8 @@ class BsmBlockMask(ctypes.Structure):
 
 class BsmScoreMod(ctypes.Structure):
     _fields_ = [("flags", ctypes.c_uint32), ("alibi_slopes", ctypes.c_void_p),
-                ("softcap", ctypes.c_float), ("alibi_slopes_grad", ctypes.c_void_p)]
+                ("softcap", ctypes.c_float), ("alibi_slopes_grad", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("bias_radius", ctypes.c_int32), ("bias_grad", ctypes.c_void_p)]
 
 
 class BsmTensor(ctypes.Structure):
@@ -65,6 +67,7 @@ SIGNATURES = {
         _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), _P(BsmBlockMask), _P(BsmMaskSpec),
         _P(BsmScoreMod), ctypes.c_float, _P(BsmTensor), ctypes.c_void_p, ctypes.c_void_p]),
     "bsm_bwd_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32] * 4),
+    "bsm_bwd_workspace_bytes_mod": (ctypes.c_size_t, [ctypes.c_int32] * 4 + [_P(BsmScoreMod)]),
     "bsm_flex_attention_bwd": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), ctypes.c_void_p,

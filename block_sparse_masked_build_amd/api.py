@@ -26,7 +26,7 @@ import torch
 from . import _lib
 from ._lib import (BsmBlockMask, BsmMaskSpec, BsmScoreMod, BsmTensor, check, lib,
                    BSM_MASK_CAUSAL, BSM_MASK_DOCUMENT, BSM_MASK_WINDOW, BSM_MASK_SINKS, BSM_MASK_PREFIX,
-                   BSM_MASK_TABLE, BSM_MOD_ALIBI, BSM_MOD_SOFTCAP)
+                   BSM_MASK_TABLE, BSM_MOD_ALIBI, BSM_MOD_SOFTCAP, BSM_MOD_BIAS)
 
 TILE = 128
 
@@ -159,6 +159,11 @@ class MaskSpec:
 class ScoreMod:
     alibi_slopes: Optional[torch.Tensor] = None  # float32 [H] on the device
     softcap: Optional[float] = None
+    bias: Optional[torch.Tensor] = None          # float32 [H, 2R + 1] on the device: relative-position bias
+
+    @property
+    def bias_radius(self) -> int:
+        return (self.bias.shape[-1] - 1) // 2 if self.bias is not None else 0
 
     def c_struct(self) -> BsmScoreMod:
         f = 0
@@ -166,8 +171,11 @@ class ScoreMod:
             f |= BSM_MOD_ALIBI
         if self.softcap is not None:
             f |= BSM_MOD_SOFTCAP
+        if self.bias is not None:
+            f |= BSM_MOD_BIAS
         return BsmScoreMod(f, self.alibi_slopes.data_ptr() if self.alibi_slopes is not None else None,
-                           float(self.softcap) if self.softcap is not None else 0.0, None)
+                           float(self.softcap) if self.softcap is not None else 0.0, None,
+                           self.bias.data_ptr() if self.bias is not None else None, self.bias_radius, None)
 
 
 class BlockMask(NamedTuple):
@@ -229,11 +237,18 @@ def from_spec_data(spec_data, device="cuda") -> MaskSpec:
                      kv_block=int(getattr(spec_data, "kv_block", 128)))
 
 
-def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda") -> ScoreMod:
+def score_mod(alibi_slopes=None, softcap: Optional[float] = None, device="cuda", bias=None) -> ScoreMod:
+    """Score modifications: ALiBi slopes [H], a soft-cap value, and a
+    relative-position bias table [H, 2R + 1] (entry R + d for the distance
+    q - kv = d, distances beyond R clipped)."""
     s = None
     if alibi_slopes is not None:
         s = torch.as_tensor(np.asarray(alibi_slopes), dtype=torch.float32).to(device).contiguous()
-    return ScoreMod(s, softcap)
+    t = None
+    if bias is not None:
+        t = torch.as_tensor(np.asarray(bias) if not isinstance(bias, torch.Tensor) else bias,
+                            dtype=torch.float32).to(device).contiguous()
+    return ScoreMod(s, softcap, t)
 
 
 def empty_block_mask(spec, mask_b: Optional[int] = None, device="cuda") -> BlockMask:
@@ -330,19 +345,25 @@ def _shapes(q, k, v, spec: MaskSpec):
     return B, H, Q, D, T
 
 
-def bwd_workspace(B: int, H: int, Q: int, D: int, device="cuda") -> torch.Tensor:
-    """Workspace of the backward for Q = Q_LEN queries."""
-    n = lib.bsm_bwd_workspace_bytes(B, H, Q, D)
+def bwd_workspace(B: int, H: int, Q: int, D: int, device="cuda", mod: Optional[ScoreMod] = None) -> torch.Tensor:
+    """Workspace of the backward for Q = Q_LEN queries (and the score
+    modifications mod: a bias table adds its gradient partials)."""
+    if mod is None:
+        n = lib.bsm_bwd_workspace_bytes(B, H, Q, D)
+    else:
+        cm = mod.c_struct()
+        n = lib.bsm_bwd_workspace_bytes_mod(B, H, Q, D, ctypes.byref(cm))
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
 def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: MaskSpec,
                        mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
                        dq=None, dk=None, dv=None, workspace: Optional[torch.Tensor] = None,
-                       dslopes: Optional[torch.Tensor] = None):
+                       dslopes: Optional[torch.Tensor] = None, dbias: Optional[torch.Tensor] = None):
     """Returns (dq bf16 [B, H, Q_LEN, D], dk and dv bf16 [B, H, KV_LEN, D]).
     With ALiBi, a float32 [H] device tensor passed as dslopes receives
-    dL/dslope (summed over the batch)."""
+    dL/dslope (summed over the batch); with a bias table, a float32
+    [H, 2R + 1] device tensor passed as dbias receives dL/dbias."""
     B, H, Q, D, T = _shapes(q, k, v, spec)
     for name, x in (("out", out), ("dout", dout)):
         if x.shape != q.shape:
@@ -357,7 +378,7 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
         if x.shape != ref.shape:
             raise ValueError(f"{name} {tuple(x.shape)} must be {tuple(ref.shape)}")
     if workspace is None:
-        workspace = bwd_workspace(B, H, Q, D, q.device)
+        workspace = bwd_workspace(B, H, Q, D, q.device, mod)
     ts = [_tensor(x, n) for x, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout"),
                                      (dq, "dq"), (dk, "dk"), (dv, "dv"))]
     cb = block_mask.c_struct()
@@ -369,6 +390,12 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
         if dslopes.dtype != torch.float32 or dslopes.numel() != H or not dslopes.is_contiguous():
             raise ValueError("dslopes must be a contiguous float32 tensor of H elements")
         cm.alibi_slopes_grad = dslopes.data_ptr()
+    if dbias is not None:
+        if cm is None or mod.bias is None:
+            raise ValueError("dbias needs a score_mod with a bias table")
+        if dbias.dtype != torch.float32 or dbias.shape != mod.bias.shape or not dbias.is_contiguous():
+            raise ValueError("dbias must be a contiguous float32 tensor shaped like the bias table")
+        cm.bias_grad = dbias.data_ptr()
     check(lib.bsm_flex_attention_bwd(
         B, H, T, D, *[ctypes.byref(t) for t in ts[:4]], lse.data_ptr(), ctypes.byref(ts[4]),
         ctypes.byref(cb), ctypes.byref(cs), ctypes.byref(cm) if cm is not None else None,
@@ -378,11 +405,16 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
 
 
 def _check_mod(mod: Optional[ScoreMod], H: int) -> None:
-    """The slopes tensor the kernels read H entries of."""
+    """The slopes tensor the kernels read H entries of, and the bias table
+    they read H rows of 2R + 1 entries of."""
     if mod is not None and mod.alibi_slopes is not None:
         sl = mod.alibi_slopes
         if sl.dtype != torch.float32 or not sl.is_contiguous() or sl.numel() < H:
             raise ValueError(f"alibi_slopes must be a contiguous float32 tensor of at least H={H} elements")
+    if mod is not None and mod.bias is not None:
+        t = mod.bias
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2 or t.shape[0] < H or t.shape[1] % 2 != 1:
+            raise ValueError(f"bias must be a contiguous float32 [H={H}, 2R + 1] tensor")
 
 
 def _kv_len_tensor(kv_len, B: int, capacity: int, device) -> tuple:

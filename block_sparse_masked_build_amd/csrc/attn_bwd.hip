@@ -102,6 +102,61 @@ struct DqLds {
     uint32_t k, v, doc;  // buffer 0; buffer 1 follows
 };
 
+// Bias-gradient sums of one wave (BIAS).  Every wave owns two LDS arrays of
+// kBiasAccStride floats, one per lane half, at bacc (this lane's half):
+// entries 0..2R sum g over the pairs of each clipped distance; the 32 after
+// them sum each lane's pairs beyond +R, the next 32 those beyond -R.  Within
+// one add instruction the lanes of a half have 32 distinct distances, so no
+// two lanes of an instruction touch one address, and a wave's LDS operations
+// complete in order: every sum is formed in program order, and the item's
+// partial row (bias_grad_flush) is identical from run to run.
+constexpr int kBiasAccStride = kBiasMaxEntries + 64;
+
+__device__ inline void bias_grad_add(const float (&dsv)[2][16], int key0, int qpos, int R, uint32_t bacc) {
+    const int hl = (threadIdx.x & 63) >> 5, n = threadIdx.x & 31;
+    const int t = qpos - (key0 + 4 * hl);  // distance at register offset c: t - c
+    if (__all(t - kRowMaxOffset >= -R && t <= R)) {
+        const uint32_t a0 = bacc + 4u * (uint32_t)(t - kRowMaxOffset + R);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+                lds_add(a0 + 4u * (uint32_t)(kRowMaxOffset - c), dsv[kb][r]);
+            }
+    } else {
+        const int hi_slot = 2 * R + 1 + n, lo_slot = 2 * R + 33 + n;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+                const int d = t - c;
+                const int idx = d > R ? hi_slot : d < -R ? lo_slot : d + R;
+                lds_add(bacc + 4u * (uint32_t)idx, dsv[kb][r]);
+            }
+    }
+}
+
+// The item's partial row: entry j summed over the four waves and both lane
+// halves in a fixed order, the overflow slots into the end entries.
+__device__ inline void bias_grad_flush(uint32_t acc0, int R, float *row) {
+    const int nb = 2 * R + 1;
+    for (int j = threadIdx.x; j < nb; j += kThreads) {
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 2 * (kThreads / 64); ++w) v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + j));
+        if (j == nb - 1)
+            for (int w = 0; w < 2 * (kThreads / 64); ++w)
+                for (int k = 0; k < 32; ++k) v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + nb + k));
+        if (j == 0)
+            for (int w = 0; w < 2 * (kThreads / 64); ++w)
+                for (int k = 0; k < 32; ++k)
+                    v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + nb + 32 + k));
+        row[j] = v;
+    }
+}
+
 // SGRAD (with ALiBi only): also sums g_qk (k - q) over the visible keys of
 // this lane's query into sg, the lane's share of dL/dslope[h] (g is dS
 // before the scale, the gradient with respect to the score the ALiBi term
@@ -110,12 +165,12 @@ struct DqLds {
 // GENERAL: the general kernel (see kv_ragged): the last key block's copies
 // are clamped and the block width is read at run time; the other kernel has
 // whole 128-key tiles compiled in (see the forward).
-template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE, bool GENERAL>
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE, bool GENERAL, bool BIAS = false>
 __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (&qf)[D / 16],
                                const elem8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
-                               f32x16 (&dq)[D / 32], float &sg) {
+                               f32x16 (&dq)[D / 32], float &sg, const BiasLds &bl = {}, uint32_t bacc = 0) {
     static_assert(!SGRAD || ALIBI, "the slope gradient needs the ALiBi term");
-    constexpr bool kMods = ALIBI || SOFTCAP;
+    constexpr bool kMods = ALIBI || SOFTCAP || BIAS;
     constexpr uint32_t kTB = DqLds<D>::kTileBytes;
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto issue = [&](int t, int key0) {
@@ -174,9 +229,10 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
                 dp[kb] = mfma32(read_rows_operand<D>(sv, offt, kb, st), gf[st], dp[kb]);
             }
         }
-        row_mod_mask<ALIBI, SOFTCAP, MODE>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial,
-                                           MODE == kTable && a.doc);
+        row_mod_mask<ALIBI, SOFTCAP, MODE, BIAS>(lds.doc + bf * kHalf * 4, s, key0, a.qpos, a.mk, rm, partial,
+                                                 MODE == kTable && a.doc, bl);
         elem8 dsb[2][2];
+        float dsv[2][16];                // BIAS: the step's ds, added to the bias-gradient sums
         float sg_c = 0.0f, sg_s = 0.0f;  // SGRAD: sum ds c and sum ds over the step
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -187,6 +243,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
                 float ds = pv * (dp[kb][r] - a.delta);
                 if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
                 dsb[kb][r >> 3][r & 7] = static_cast<elem_t>(ds);
+                if (BIAS) dsv[kb][r] = ds;
                 if (SGRAD) {
                     sg_c = __builtin_fmaf(ds, (float)(kb * 32 + (r >> 2) * 8 + (r & 3)), sg_c);
                     sg_s += ds;
@@ -196,6 +253,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
             const int hl = (threadIdx.x & 63) >> 5;
             sg = __builtin_fmaf((float)(key0 + 4 * hl - a.qpos), sg_s, sg + sg_c);
         }
+        if (BIAS) bias_grad_add(dsv, key0, a.qpos, bl.R, bacc);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (skip[kb]) continue;
@@ -212,9 +270,23 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
 
 // TABLE: a composed mask (its own kernel, so that the truth-table
 // evaluation does not take registers from the other masks' kernels).
-template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, bool TABLE, bool GENERAL>
-__global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
+// BIAS: a relative-position bias table (no ALiBi; general path only),
+// staged in LDS, with the per-wave bias-gradient sums (see bias_grad_add).
+// The table and the eight gradient arrays take 74 KB of LDS, so the BIAS
+// kernels run one workgroup per CU.  (One kernel template: routing the
+// kernel through a shared device-function body changed the register
+// allocation of the other instances.)
+template <int D, bool BIAS>
+struct DqBiasSmem {
+    float tab[BIAS ? kBiasMaxEntries : 1];
+    float acc[BIAS ? 2 * (kThreads / 64) * kBiasAccStride : 1];
+};
+
+template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, bool TABLE, bool GENERAL, bool BIAS>
+__global__ __launch_bounds__(kThreads, (BIAS ? 1 : kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
+    __shared__ DqBiasSmem<D, BIAS> bsm;
+    const uint32_t btab = lds_addr(bsm.tab), bacc = lds_addr(bsm.acc);
 
     const int nt = p.nkb;  // key blocks of the row lists
     // Item: a query-tile row of the row work order (longest first) and a
@@ -261,6 +333,9 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     a.inv_cap = 1.0f / a.cap;
     a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
     const int64_t row_bh = ((int64_t)b * p.H + h) * p.q_len + qrow;
+    const int nb = 2 * p.bias_r + 1;
+    float bstage[kBiasPerThread];
+    if (BIAS) stage_bias_load(p.bias + (int64_t)h * nb, nb, bstage);
     const float lse = p.lse[row_bh];
     a.l2 = lse == -INFINITY ? 0.0f : lse * kLog2e;
     const int nsteps = a.spb * (a.nfull + npart);
@@ -302,6 +377,18 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
             p.lse2[row_bh] = a.l2;
         }
     }
+    // BIAS: lanes past Q_LEN (a copy of the last query) get p = 0, so that
+    // they add nothing to the bias gradient; the table goes to LDS and this
+    // wave's gradient sums start at zero (the wave's own LDS operations stay
+    // in order, the table is read after the first step's barrier).
+    const uint32_t bacc_w = bacc + 4u * (uint32_t)((wv * 2 + hl) * kBiasAccStride);
+    if (BIAS) {
+        if (qidx >= p.q_len) a.l2 = INFINITY;
+        stage_bias_store(bstage, nb, mod_f<SOFTCAP>(a.cap), btab);
+        for (int j = n; j < kBiasAccStride; j += 32) lds_store<float>(bacc_w + 4u * (uint32_t)j, 0.0f);
+        wait_lds_reads();  // (and writes)
+    }
+    const BiasLds bl = {btab, p.bias_r};
     f32x16 dq[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -314,13 +401,17 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
 
     float sg = 0.0f;
     if (TABLE)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
     else if (mode == kGather)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
     else if (mode == kSinks)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
     else
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, GENERAL>(a, rm, qf, gf, off, lds, nsteps, dq, sg);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
+    if (BIAS) {
+        __syncthreads();  // every wave's sums are complete
+        bias_grad_flush(bacc, p.bias_r, p.dbias_part + (((int64_t)b * p.H + h) * p.nqt + i) * nb);
+    }
 
     // Slope gradient of the item: wave sums by a fixed butterfly, then the
     // four waves in order, one partial per (batch, head, query tile); lanes
@@ -342,6 +433,7 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_
     elem_t *dqp = static_cast<elem_t *>(p.dq) + b * p.dq_sb + h * p.dq_sh + (int64_t)(qidx - n) * p.dq_st;
     store_rows_staged<D>(dqp, p.dq_st, dq, p.scale, lds.k + (uint32_t)(wv * 32 * 2 * D), p.q_len - (qidx - n));
 }
+
 
 // ---------------------------------------------------------------- dK, dV
 
@@ -467,15 +559,36 @@ __device__ inline void dkdv_sdp(const elem8 (&rq)[D / 16], const elem8 (&rg)[D /
     }
 }
 
+// Bias terms of the column view (BIAS): query offset c = 8 (r/4) + r%4 <= 27
+// of the block at distance t0 + c (t0 = the block's first query position in
+// this lane half minus the key); one LDS read per term at a fixed offset
+// when the wave's distances lie inside [-R, R], clipped per score otherwise.
+constexpr int kColMaxOffset = 27;  // 3 * 8 + 3
+
+__device__ inline void col_bias(float (&bt)[16], int t0, const BiasLds &bl) {
+    if (__all(t0 >= -bl.R && t0 + kColMaxOffset <= bl.R)) {
+        const uint32_t a0 = bl.tab + 4u * (uint32_t)(t0 + bl.R);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bt[r] = lds_load<float>(a0 + 4u * (uint32_t)((r >> 2) * 8 + (r & 3)));
+    } else {
+        const uint32_t a0 = bl.tab + 4u * (uint32_t)bl.R;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int d = min(max(t0 + (r >> 2) * 8 + (r & 3), -bl.R), bl.R);
+            bt[r] = lds_load<float>(a0 + 4u * (uint32_t)d);  // d < 0 wraps back below a0
+        }
+    }
+}
+
 // p and dS / scale of query block b (queries q0 + 32 b + 4 hl + 8 (r/4) + r%4
 // in register r) as the bf16 B operands of the dV and dK products.
 // CMODE: kPlain (the interval), kGather (interval and a per-query document
 // compare) or kTable (a composed mask, [lo, hi] the queries that exist).
-template <bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
+template <bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED, bool BIAS>
 __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t sl2, uint32_t sdl,
                                   uint32_t sdoc, int b, int q0, const f32x16 &s, const f32x16 &dp,
-                                  elem8 (&pb)[2], elem8 (&dsb)[2]) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
+                                  elem8 (&pb)[2], elem8 (&dsb)[2], const BiasLds &bl) {
+    constexpr bool kMods = ALIBI || SOFTCAP || BIAS;
     const int hl = (threadIdx.x & 63) >> 5;
     const int qbase = q0 + b * 32 + 4 * hl;
     int lo_t = cm.hi >= cm.lo ? cm.lo - qbase : 1 << 30;  // empty interval: no offset matches
@@ -494,6 +607,8 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
         asm volatile("" : "+v"(tc), "+v"(tw));
     }
     const bool docs = CMODE == kGather || (CMODE == kTable && a.doc);
+    float bt[16];
+    if (BIAS) col_bias(bt, qbase + a.q_off - a.kpos, bl);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const int ql4 = b * 32 + g * 8 + hl * 4;
@@ -507,8 +622,8 @@ __device__ inline void dkdv_grads(const DkdvArgs &a, const ColMask &cm, uint32_t
             const int c = g * 8 + e;
             float pv, tl = 0.0f;
             if (kMods) {
-                const float bias = ALIBI ? __builtin_fmaf((float)c, ns, n) : 0.0f;
-                tl = mod_apply<ALIBI, SOFTCAP>(s[r], bias, a.mk);
+                const float bias = ALIBI ? __builtin_fmaf((float)c, ns, n) : BIAS ? bt[r] : 0.0f;
+                tl = mod_apply<ALIBI || BIAS, SOFTCAP>(s[r], bias, a.mk);
                 pv = fast_exp2(tl - L[e]);
             } else {
                 pv = fast_exp2(__builtin_fmaf(s[r], a.scale_log2, -L[e]));
@@ -561,11 +676,11 @@ __device__ inline void dkdv_acc(const elem8 (&tq)[2][D / 32], const elem8 (&tg)[
 // four 32-query blocks: the S / dP products of block b+1 are issued next to
 // the gradient arithmetic of block b, and the row operands of block b+2 are
 // read during the dV / dK products of block b.
-template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED, bool BIAS>
 __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 16],
                                  const elem8 (&vf)[D / 16], const KvOffsets &oq, const KvOffsets &og,
                                  uint32_t sl2, uint32_t sdl, uint32_t sdoc, int q0,
-                                 f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+                                 f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const BiasLds &bl) {
     constexpr int NB = kTile / 32;
     elem8 rq[D / 16], rg[D / 16];
     f32x16 s[2], dp[2];
@@ -577,7 +692,7 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const ele
         const int cur = b & 1;
         if (b + 1 < NB) dkdv_sdp<D>(rq, rg, kf, vf, s[cur ^ 1], dp[cur ^ 1]);
         elem8 pb[2], dsb[2];
-        dkdv_grads<ALIBI, SOFTCAP, CMODE, MASKED>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb);
+        dkdv_grads<ALIBI, SOFTCAP, CMODE, MASKED, BIAS>(a, cm, sl2, sdl, sdoc, b, q0, s[cur], dp[cur], pb, dsb, bl);
         elem8 tq[2][D / 32], tg[2][D / 32];
         dkdv_read_cols<D>(oq, og, b, tq, tg);
         if (b + 2 < NB) dkdv_read_rows<D>(oq, og, b + 2, rq, rg);
@@ -588,10 +703,10 @@ __device__ inline void dkdv_tile(const DkdvArgs &a, const ColMask &cm, const ele
 
 // GENERAL: Q_LEN is not a multiple of 128, so the last query tile's copies
 // are clamped (compiled out otherwise).
-template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool GENERAL>
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool GENERAL, bool BIAS = false>
 __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 16],
                                  const elem8 (&vf)[D / 16], const KvOffsets &off, const DkdvLds<D> &lds,
-                                 int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32]) {
+                                 int ntiles, f32x16 (&dk)[D / 32], f32x16 (&dv)[D / 32], const BiasLds &bl = {}) {
     constexpr uint32_t kTB = DkdvLds<D>::kTileBytes, kWB = kTile * 4;
     static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
     auto tile_q0 = [&](int it) {
@@ -627,8 +742,8 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const ele
         // Tile base and buffer enter through the lane offsets (see dq_main):
         // the second tile's base lies beyond a read's 16-bit offset field.
         const KvOffsets oq = step_offsets(off, lds.q + bf * kTB), og = step_offsets(off, lds.g + bf * kTB);
-        dkdv_tile<D, ALIBI, SOFTCAP, CMODE, decltype(masked)::value>(
-            a, cm, kf, vf, oq, og, lds.l2 + bf * kWB, lds.delta + bf * kWB, lds.doc + bf * kWB, q0, dk, dv);
+        dkdv_tile<D, ALIBI, SOFTCAP, CMODE, decltype(masked)::value, BIAS>(
+            a, cm, kf, vf, oq, og, lds.l2 + bf * kWB, lds.delta + bf * kWB, lds.doc + bf * kWB, q0, dk, dv, bl);
         wait_lds_reads();  // this wave's reads of tile t are done before the next barrier
         q0 = q_next;
     };
@@ -638,9 +753,10 @@ __device__ inline void dkdv_main(const DkdvArgs &a, const ColMask &cm, const ele
     for (int t = a.nfull; t < ntiles; ++t) step(t, std::true_type());
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
+// BIAS: a relative-position bias table (no ALiBi), staged in LDS at btab.
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL, bool BIAS>
+__device__ __attribute__((always_inline)) inline void dkdv_body(const AttnParams &p, DkdvSmem<D> &sm,
+                                                                uint32_t btab) {
     const int nt = p.nt;
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int bh = wg / nt;
@@ -655,6 +771,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     const elem_t *vb = static_cast<const elem_t *>(p.v) + b * p.v_sb + h * p.v_sh;
     const int bm = p.mask_b == 1 ? 0 : b;
     const int64_t col = (int64_t)bm * nt + j;
+    const int nb = 2 * p.bias_r + 1;
+    float bstage[kBiasPerThread];
+    if (BIAS) stage_bias_load(p.bias + (int64_t)h * nb, nb, bstage);
 
     DkdvArgs a;
     a.qb = static_cast<const elem_t *>(p.q) + b * p.q_sb + h * p.q_sh;
@@ -711,14 +830,19 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
             dv[db][r] = 0.0f;
         }
     // No wait here: the first tile copies are issued while the key rows
-    // load (see dq_kernel).
-
+    // load (see dq_kernel).  BIAS: the table's LDS writes are done before
+    // the first step's barrier, after which it is read.
+    if (BIAS) {
+        stage_bias_store(bstage, nb, mod_f<SOFTCAP>(a.cap), btab);
+        wait_lds_reads();  // (and writes)
+    }
+    const BiasLds bl = {btab, p.bias_r};
     if (TABLE)
-        dkdv_main<D, ALIBI, SOFTCAP, kTable, GENERAL>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kTable, GENERAL, BIAS>(a, cm, kf, vf, off, lds, ntiles, dk, dv, bl);
     else if (gather)
-        dkdv_main<D, ALIBI, SOFTCAP, kGather, GENERAL>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kGather, GENERAL, BIAS>(a, cm, kf, vf, off, lds, ntiles, dk, dv, bl);
     else
-        dkdv_main<D, ALIBI, SOFTCAP, kPlain, GENERAL>(a, cm, kf, vf, off, lds, ntiles, dk, dv);
+        dkdv_main<D, ALIBI, SOFTCAP, kPlain, GENERAL, BIAS>(a, cm, kf, vf, off, lds, ntiles, dk, dv, bl);
 
     // dK and dV rows of the wave, staged through the query and output-gradient
     // buffers once every wave is done with them (dS was accumulated without
@@ -732,6 +856,32 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnP
     elem_t *dvp = static_cast<elem_t *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)k0w * p.dv_st;
     store_rows_staged<D>(dkp, p.dk_st, dk, p.scale, lds.q + slice, p.T - k0w);
     store_rows_staged<D>(dvp, p.dv_st, dv, 1.0f, lds.g + slice, p.T - k0w);
+}
+
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL>
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
+    dkdv_body<D, ALIBI, SOFTCAP, TABLE, GENERAL, false>(p, sm, 0);
+}
+
+template <int D, bool SOFTCAP, bool TABLE>
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_bias_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) DkdvSmem<D> sm;
+    __shared__ float btab[kBiasMaxEntries];
+    dkdv_body<D, false, SOFTCAP, TABLE, true, true>(p, sm, lds_addr(btab));
+}
+
+// dL/dbias: the per-(batch, head, query tile) partial rows of the BIAS dq_kernel
+// summed over the batch and the query tiles in a fixed order; one thread per
+// (head, entry), coalesced over the entries.
+__global__ __launch_bounds__(kThreads) void bias_reduce_kernel(const float *part, float *dbias, int B, int H,
+                                                                 int nqt, int nb) {
+    const int h = blockIdx.y, j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= nb) return;
+    float acc = 0.0f;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < nqt; ++i) acc += part[(((int64_t)b * H + h) * nqt + i) * nb + j];
+    dbias[(int64_t)h * nb + j] = acc;
 }
 
 // dL/dslope[h]: the per-(batch, head, query tile) partials of dq_kernel
@@ -775,16 +925,16 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
     // its items), which dkdv_kernel reads.
     if (ALIBI && p.dslopes) {
         if (kv_r)
-            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI, TABLE, true>), dq_grid, block, 0, stream, q);
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI, TABLE, true, false>), dq_grid, block, 0, stream, q);
         else
-            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI, TABLE, TABLE>), dq_grid, block, 0, stream, q);
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, ALIBI, TABLE, TABLE, false>), dq_grid, block, 0, stream, q);
         hipLaunchKernelGGL(slope_reduce_kernel, dim3(p.H), block, 0, stream, p.dslope_part, p.dslopes, p.B, p.H,
                            p.nqt);
     } else {
         if (kv_r)
-            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, true>), dq_grid, block, 0, stream, q);
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, true, false>), dq_grid, block, 0, stream, q);
         else
-            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, TABLE>), dq_grid, block, 0, stream, q);
+            hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, TABLE, false>), dq_grid, block, 0, stream, q);
     }
     if (q_r)
         hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, true>), dkdv_grid, block, 0, stream, q);
@@ -792,10 +942,32 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
         hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, TABLE>), dkdv_grid, block, 0, stream, q);
 }
 
+// With a bias table: the bias kernels (general path), then the reduction of
+// the bias-gradient partials when the caller asked for the gradient.
+template <int D, bool SOFTCAP, bool TABLE>
+void launch_bias(const AttnParams &p, hipStream_t stream) {
+    AttnParams q = p;
+    const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
+    hipLaunchKernelGGL((dq_kernel<D, false, SOFTCAP, false, TABLE, true, true>), dq_grid, block, 0, stream, q);
+    if (p.dbias) {
+        const int nb = 2 * p.bias_r + 1;
+        hipLaunchKernelGGL(bias_reduce_kernel, dim3((nb + kThreads - 1) / kThreads, p.H), block, 0, stream,
+                           p.dbias_part, p.dbias, p.B, p.H, p.nqt, nb);
+    }
+    hipLaunchKernelGGL((dkdv_bias_kernel<D, SOFTCAP, TABLE>), dkdv_grid, block, 0, stream, q);
+}
+
 template <int D, bool TABLE>
 void launch_mods(const AttnParams &p, hipStream_t stream) {
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
+    if (p.mod_flags & BSM_MOD_BIAS) {
+        if (cap)
+            launch_bias<D, true, TABLE>(p, stream);
+        else
+            launch_bias<D, false, TABLE>(p, stream);
+        return;
+    }
     if (alibi && cap)
         launch_main<D, true, true, TABLE>(p, stream);
     else if (alibi)

@@ -71,9 +71,13 @@ struct ModK {
     float c1, c2;      // soft-cap constants
 };
 
+// The domain factor f (an additive term b enters as b f).
+template <bool SOFTCAP>
+__device__ inline float mod_f(float cap) { return SOFTCAP ? 2.0f * kLog2e / cap : kLog2e; }
+
 template <bool SOFTCAP>
 __device__ inline ModK mod_k(float scale, float slope, float cap) {
-    const float f = SOFTCAP ? 2.0f * kLog2e / cap : kLog2e;
+    const float f = mod_f<SOFTCAP>(cap);
     return {scale * f, slope * f, cap * kLog2e, 2.0f * cap * kLog2e};
 }
 
@@ -331,6 +335,13 @@ __device__ inline T lds_load(uint32_t addr) {
 template <typename T>
 __device__ inline void lds_store(uint32_t addr, T v) {
     *reinterpret_cast<__attribute__((address_space(3))) T *>((uintptr_t)addr) = v;
+}
+
+// Atomic add of v to the float at an LDS byte address (ds_add_f32, no
+// return value).
+__device__ inline void lds_add(uint32_t addr, float v) {
+    __hip_atomic_fetch_add(reinterpret_cast<__attribute__((address_space(3))) float *>((uintptr_t)addr), v,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Same for N 4-byte words of any type.
@@ -620,36 +631,102 @@ __device__ inline bool in_range(int c, int lo_t, int span) {
     return (uint32_t)(c - lo_t) <= (uint32_t)span;  // lo_t <= c <= lo_t + span, span >= 0
 }
 
+// Relative-position bias table (one scalar per clipped distance q - kv in
+// [-R, R]) of a head, staged in LDS (stage_bias_load / stage_bias_store)
+// already multiplied by the log2-domain factor of mod_k.
+struct BiasLds {
+    uint32_t tab;  // LDS byte address of entry 0 (distance -R)
+    int R;
+};
+
+// Bias terms of one step of the row view: key kbase + c at the register
+// offsets c <= 59, distance t - c with t = qpos - kbase.  When every
+// distance of the wave's step lies inside [-R, R] each term is one LDS read
+// at a fixed offset from a per-lane base (no clip); otherwise the distance
+// is clipped per score.
+constexpr int kRowMaxOffset = 59;  // 32 + 3 * 8 + 3
+
+__device__ inline void row_bias(float (&bt)[2][16], int kbase, int qpos, const BiasLds &bl) {
+    const int t = qpos - kbase;
+    if (__all(t - kRowMaxOffset >= -bl.R && t <= bl.R)) {
+        const uint32_t a0 = bl.tab + 4u * (uint32_t)(t - kRowMaxOffset + bl.R);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+                bt[kb][r] = lds_load<float>(a0 + 4u * (uint32_t)(kRowMaxOffset - c));
+            }
+    } else {
+        const uint32_t a0 = bl.tab + 4u * (uint32_t)bl.R;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
+                const int d = min(max(t - c, -bl.R), bl.R);
+                bt[kb][r] = lds_load<float>(a0 + 4u * (uint32_t)d);  // d < 0 wraps back below a0
+            }
+    }
+}
+
+// Copies a head's 2R + 1 bias entries, times f, into LDS at `tab`: the
+// loads happen here, the LDS writes in stage_bias_store after the caller's
+// wait for its loads, so that no wait for them stalls the tile copies
+// issued in between.  Up to kBiasPerThread entries per thread.
+constexpr int kBiasMaxEntries = 2 * BSM_BIAS_MAX_RADIUS + 1;
+constexpr int kBiasPerThread = (kBiasMaxEntries + 255) / 256;
+
+__device__ inline void stage_bias_load(const float *row, int n, float (&v)[kBiasPerThread]) {
+#pragma unroll
+    for (int j = 0; j < kBiasPerThread; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        v[j] = i < n ? row[i] : 0.0f;
+    }
+}
+
+__device__ inline void stage_bias_store(const float (&v)[kBiasPerThread], int n, float f, uint32_t tab) {
+#pragma unroll
+    for (int j = 0; j < kBiasPerThread; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        if (i < n) lds_store<float>(tab + 4u * (uint32_t)i, v[j] * f);
+    }
+}
+
 // Score modifications alone (row view, step starting at key0): the scores
 // leave in the log2 domain.  Without modifications nothing is done here; the
 // scale is folded into the exponential instead.  The ALiBi term of the
 // score at key offset c (key - key0 - 4 hl) is slope_f c + n with
-// n = -slope_f (q - key0 - 4 hl).
-template <bool ALIBI, bool SOFTCAP>
-__device__ inline void row_mods(f32x16 (&s)[2], int key0, int qpos, const ModK &mk) {
-    if (!(ALIBI || SOFTCAP)) return;
+// n = -slope_f (q - key0 - 4 hl); a bias table's term (BIAS) takes its place.
+template <bool ALIBI, bool SOFTCAP, bool BIAS = false>
+__device__ inline void row_mods(f32x16 (&s)[2], int key0, int qpos, const ModK &mk, const BiasLds &bl = {}) {
+    static_assert(!(ALIBI && BIAS), "one additive term at a time");
+    if (!(ALIBI || SOFTCAP || BIAS)) return;
     const int hl = (threadIdx.x & 63) >> 5;
     float n = 0.0f, sf = mk.slope_f;
     if (ALIBI) {
         n = -mk.slope_f * (float)(qpos - (key0 + hl * 4));
         asm volatile("" : "+v"(n), "+v"(sf));  // per step: keeps the per-register terms from being hoisted
     }
+    float bt[2][16];
+    if (BIAS) row_bias(bt, key0 + hl * 4, qpos, bl);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-            const float b = ALIBI ? __builtin_fmaf((float)c, sf, n) : 0.0f;
-            s[kb][r] = mod_apply<ALIBI, SOFTCAP>(s[kb][r], b, mk);
+            const float b = ALIBI ? __builtin_fmaf((float)c, sf, n) : BIAS ? bt[kb][r] : 0.0f;
+            s[kb][r] = mod_apply<ALIBI || BIAS, SOFTCAP>(s[kb][r], b, mk);
         }
 }
 
-template <bool ALIBI, bool SOFTCAP, int MODE>
+template <bool ALIBI, bool SOFTCAP, int MODE, bool BIAS = false>
 __device__ inline void row_mod_mask(uint32_t sdoc, f32x16 (&s)[2], int key0, int qpos, const ModK &mk,
-                                    const RowMask &rm, bool partial, bool table_docs = false) {
+                                    const RowMask &rm, bool partial, bool table_docs = false,
+                                    const BiasLds &bl = {}) {
     const int hl = (threadIdx.x & 63) >> 5;
     const int kbase = key0 + hl * 4;
-    row_mods<ALIBI, SOFTCAP>(s, key0, qpos, mk);
+    row_mods<ALIBI, SOFTCAP, BIAS>(s, key0, qpos, mk, bl);
     if (!partial) return;  // full tile: every pair is visible
     // Bounds relative to this step, kept opaque so that the compiler compares
     // them with the per-register key offsets instead of hoisting 64

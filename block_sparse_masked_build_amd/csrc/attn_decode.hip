@@ -12,7 +12,8 @@
 // query of batch element b sits at position p = kv_len[b] - 1 and sees key kv
 // when kv < kv_len[b] and the mask predicate holds for (p, kv); its scores go
 // through the score modifications in the forward's own formulation
-// (mod_apply: ALiBi, then the exp2-based tanh soft-cap).
+// (mod_apply: ALiBi or a relative-position bias table, then the exp2-based
+// tanh soft-cap).
 //
 // Which keys are read:
 //  * with a block mask (built once for the whole capacity, square), the
@@ -60,6 +61,8 @@ struct DecodeParams {
     const int32_t *window;       // device scalar or NULL
     int32_t mask_b;
     const float *alibi_slopes;   // [H] or NULL
+    const float *bias;           // [H, 2 bias_r + 1] relative-position bias table or NULL (then ADD is ALiBi)
+    int32_t bias_r;
     // block mask rows (NULL kv_num: no block mask)
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
     const elem_t *q; int64_t q_sb, q_sh;
@@ -108,7 +111,10 @@ __device__ inline void write_empty_slot(const DecodeParams &P, int64_t slot) {
     }
 }
 
-template <int D, bool ALIBI, bool SOFTCAP, bool LISTED>
+// ADD: an additive position term -- the ALiBi slope, or with P.bias the bias
+// table (one wave-uniform branch per key block; the decoding step is bound
+// by its HBM reads, not by this arithmetic).
+template <int D, bool ADD, bool SOFTCAP, bool LISTED>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
     constexpr int kDimsPerLane = D / 64;  // output dims per lane: lane * kDimsPerLane + i
     __shared__ float sq[D];               // the query row, fp32
@@ -157,8 +163,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 
     int docq = 0;
     if (P.mask_flags & BSM_MASK_DOCUMENT) docq = P.doc_ids[(int64_t)bm * P.capacity + p];
-    const float slope = ALIBI ? P.alibi_slopes[h] : 0.0f;
+    const bool table = ADD && P.bias;
+    const float slope = ADD && !table ? P.alibi_slopes[h] : 0.0f;
     const ModK mk = mod_k<SOFTCAP>(P.scale, slope, SOFTCAP ? P.softcap : 1.0f);
+    const float bias_f = mod_f<SOFTCAP>(SOFTCAP ? P.softcap : 1.0f);
+    const float *brow = table ? P.bias + (int64_t)h * (2 * P.bias_r + 1) + P.bias_r : nullptr;  // entry of distance 0
 
     const elem_t *qrow = P.q + b * P.q_sb + h * P.q_sh;
     for (int d = threadIdx.x; d < D; d += kDecThreads) sq[d] = static_cast<float>(qrow[d]);
@@ -198,7 +207,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
                 for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(sq[d0 + e], static_cast<float>(kk[e]), acc);
             }
             // log2-domain modified score, as in the forward
-            t = mod_apply<ALIBI, SOFTCAP>(acc, -mk.slope_f * (float)(p - kv), mk);
+            float add = -mk.slope_f * (float)(p - kv);
+            if (table) add = bias_f * brow[min(max(p - kv, -P.bias_r), P.bias_r)];
+            t = mod_apply<ADD, SOFTCAP>(acc, add, mk);
         }
         // online softmax over this wave's 64 keys (log2 domain)
         float mx = t;
@@ -306,7 +317,8 @@ void launch_mods(const DecodeParams &P, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams &P, uint32_t mod_flags, hipStream_t stream) {
-    const bool alibi = mod_flags & BSM_MOD_ALIBI, cap = mod_flags & BSM_MOD_SOFTCAP;
+    // the bias table takes the ALiBi instances (see decode_partial_kernel)
+    const bool alibi = mod_flags & (BSM_MOD_ALIBI | BSM_MOD_BIAS), cap = mod_flags & BSM_MOD_SOFTCAP;
     if (alibi && cap)
         launch_mods<D, true, true>(P, stream);
     else if (alibi)
@@ -342,6 +354,8 @@ hipError_t BSM_ELEM_FN(launch_attn_decode)(const DecodeLaunch &d, float *part, h
     P.window = a.window;
     P.mask_b = a.mask_b;
     P.alibi_slopes = a.alibi_slopes;
+    P.bias = a.bias;
+    P.bias_r = a.bias_r;
     P.kv_num = a.kv_num;
     P.kv_idx = a.kv_idx;
     P.full_kv_num = a.full_kv_num;

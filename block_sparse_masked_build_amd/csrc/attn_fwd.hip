@@ -367,11 +367,11 @@ __device__ __attribute__((always_inline)) inline void store_item(const AttnParam
 //
 // The item's output is written at its end, staged through the K buffers,
 // which no wave reads during the last step.
-template <int D, bool ALIBI, bool SOFTCAP, int MODE, bool GENERAL>
+template <int D, bool ALIBI, bool SOFTCAP, int MODE, bool GENERAL, bool BIAS>
 __device__ __attribute__((always_inline)) inline void item_run(const AttnParams &p, const FwdArgs &a, const TileList &tl, const RowMask &rm,
                                 const elem8 (&qf)[D / 16], const OperandOffsets<D> &off, FwdSmem<D> &sm,
-                                f32x16 (&o)[D / 32], float &m, float &l) {
-    constexpr bool kMods = ALIBI || SOFTCAP;
+                                f32x16 (&o)[D / 32], float &m, float &l, const BiasLds &bl) {
+    constexpr bool kMods = ALIBI || SOFTCAP || BIAS;
     static_assert(sizeof(sm.k) >= (kThreads / 64) * 32 * 2 * D, "output staging fits the K buffers");
     const float c_mul = kMods ? 1.0f : a.scale_log2;
     const int nsteps = a.spb * a.ntiles;  // 64-key steps
@@ -427,7 +427,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
     const int k0 = a.first * a.kblk;
     int key_ahead = step1_key0(a);  // first key of step t+1 at the top of step t
     fwd_qk<D>(sm.k[0], off, qf, sa);
-    row_mods<ALIBI, SOFTCAP>(sa, k0, a.qpos, a.mk);
+    row_mods<ALIBI, SOFTCAP, BIAS>(sa, k0, a.qpos, a.mk, bl);
     const bool table_docs = MODE == kTable && a.doc;
     if (a.nfull == 0) row_mask_flat<MODE>(lds_addr(sm.doc[0]), sa, k0, rm, table_docs);
     mx = step_max(sa);
@@ -449,7 +449,7 @@ __device__ __attribute__((always_inline)) inline void item_run(const AttnParams 
         fwd_qk<D>(sm.k[(t + 1) & 1], offt, qf, sn);
         fwd_exp(sc, pb, l, c_mul, m_use);
         fwd_pv<D>(sm.v[t & 1], offt, pb, o);
-        row_mods<ALIBI, SOFTCAP>(sn, key_next, a.qpos, a.mk);
+        row_mods<ALIBI, SOFTCAP, BIAS>(sn, key_next, a.qpos, a.mk, bl);
         if (decltype(next_masked)::value)
             row_mask_flat<MODE>(lds_addr(sm.doc[(t + 1) & 1]), sn, key_next, rm, table_docs);
         mx = step_max(sn);
@@ -519,18 +519,68 @@ __global__ __launch_bounds__(kThreads, (kWgPerCu<D, ALIBI || SOFTCAP>)) void fwd
     wait_vmcnt<0>();  // the item's first tiles, query rows, tile list and row data
     tile_barrier();
     RowMask rm;
+    const BiasLds none = {};
     if (TABLE) {
         make_table_mask(p, cur.qpos, window, rl.docq, rm);
-        item_run<D, ALIBI, SOFTCAP, kTable, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kTable, GENERAL, false>(p, cur, tl, rm, qf, off, sm, o, m, l, none);
         return;
     }
     const int mode = finish_row_mask(p, cur.qpos, rl, window, rm);
     if (mode == kGather)
-        item_run<D, ALIBI, SOFTCAP, kGather, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kGather, GENERAL, false>(p, cur, tl, rm, qf, off, sm, o, m, l, none);
     else if (mode == kSinks)
-        item_run<D, ALIBI, SOFTCAP, kSinks, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kSinks, GENERAL, false>(p, cur, tl, rm, qf, off, sm, o, m, l, none);
     else
-        item_run<D, ALIBI, SOFTCAP, kPlain, GENERAL>(p, cur, tl, rm, qf, off, sm, o, m, l);
+        item_run<D, ALIBI, SOFTCAP, kPlain, GENERAL, false>(p, cur, tl, rm, qf, off, sm, o, m, l, none);
+}
+
+// The same with a relative-position bias table (no ALiBi), always on the
+// general (clamped-copy) path.  The head's table goes to LDS: its loads are
+// issued before the item's first tile copies, its LDS writes after the wait
+// for them, before the barrier that starts the loop.  (A separate kernel
+// body: routing fwd_kernel through a shared body changed the register
+// allocation of its ALiBi and soft-cap instances.)
+template <int D, bool SOFTCAP, bool TABLE>
+__global__ __launch_bounds__(kThreads, (kWgPerCu<D, true>)) void fwd_bias_kernel(AttnParams p) {
+    __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
+    __shared__ float btab[kBiasMaxEntries];
+    const ItemOrder ord(p, kQueues);
+    const int k = ord.item(blockIdx.x / ord.Q);
+    if (k >= ord.nitems) return;
+    const int window = (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0;
+    int e, rem;
+    ord.decode(k, e, rem);
+    FwdArgs cur;
+    item_args<false, SOFTCAP, true>(p, rem, load_rec(p.kv_order, e), cur);
+    const int nb = 2 * p.bias_r + 1;
+    float bstage[kBiasPerThread];
+    stage_bias_load(p.bias + (int64_t)cur.h * nb, nb, bstage);
+    OperandOffsets<D> off;
+    operand_offsets<D>(off);
+    elem8 qf[D / 16];
+    TileList tl;
+    RowLoad rl;
+    item_start<D, true>(p, sm, cur, qf, tl, rl);
+    f32x16 o[D / 32];
+    float m = -INFINITY, l = 0.0f;
+    wait_vmcnt<0>();  // the table, the item's first tiles, query rows, tile list and row data
+    stage_bias_store(bstage, nb, mod_f<SOFTCAP>(cur.cap), lds_addr(btab));
+    wait_lds_reads();  // (and writes) before the barrier
+    tile_barrier();
+    const BiasLds bl = {lds_addr(btab), p.bias_r};
+    RowMask rm;
+    if (TABLE) {
+        make_table_mask(p, cur.qpos, window, rl.docq, rm);
+        item_run<D, false, SOFTCAP, kTable, true, true>(p, cur, tl, rm, qf, off, sm, o, m, l, bl);
+        return;
+    }
+    const int mode = finish_row_mask(p, cur.qpos, rl, window, rm);
+    if (mode == kGather)
+        item_run<D, false, SOFTCAP, kGather, true, true>(p, cur, tl, rm, qf, off, sm, o, m, l, bl);
+    else if (mode == kSinks)
+        item_run<D, false, SOFTCAP, kSinks, true, true>(p, cur, tl, rm, qf, off, sm, o, m, l, bl);
+    else
+        item_run<D, false, SOFTCAP, kPlain, true, true>(p, cur, tl, rm, qf, off, sm, o, m, l, bl);
 }
 
 template <int D, bool TABLE, bool GENERAL>
@@ -553,6 +603,18 @@ hipError_t launch_d(const AttnParams &p, hipStream_t stream) {
     const dim3 grid(item_order(q)), block(kThreads);  // one workgroup per (queue, grab index) pair
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
+    if (p.mod_flags & BSM_MOD_BIAS) {
+        const bool table = p.mask_flags & BSM_MASK_TABLE;
+        if (table && cap)
+            hipLaunchKernelGGL((fwd_bias_kernel<D, true, true>), grid, block, 0, stream, q);
+        else if (table)
+            hipLaunchKernelGGL((fwd_bias_kernel<D, false, true>), grid, block, 0, stream, q);
+        else if (cap)
+            hipLaunchKernelGGL((fwd_bias_kernel<D, true, false>), grid, block, 0, stream, q);
+        else
+            hipLaunchKernelGGL((fwd_bias_kernel<D, false, false>), grid, block, 0, stream, q);
+        return hipGetLastError();
+    }
     // composed masks always take the clamped copies (one kernel per mod)
     if (p.mask_flags & BSM_MASK_TABLE)
         return launch_mods<D, true, true>(q, grid, alibi, cap, stream);

@@ -61,7 +61,7 @@ MaskDims mask_dims(const bsm_mask_spec *spec) {
     m.nkb = (m.kv_len + m.kb - 1) / m.kb;
     return m;
 }
-constexpr uint32_t kModFlagsAll = BSM_MOD_ALIBI | BSM_MOD_SOFTCAP;
+constexpr uint32_t kModFlagsAll = BSM_MOD_ALIBI | BSM_MOD_SOFTCAP | BSM_MOD_BIAS;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -141,6 +141,16 @@ bsm_status check_mod(const bsm_score_mod *mod) {
         return fail(BSM_E_INVALID, "SOFTCAP needs a finite cap > 0");
     if (mod->alibi_slopes_grad && !(mod->flags & BSM_MOD_ALIBI))
         return fail(BSM_E_INVALID, "alibi_slopes_grad given without ALIBI");
+    if (mod->flags & BSM_MOD_BIAS) {
+        if (!mod->bias) return fail(BSM_E_INVALID, "BIAS without a table");
+        if (mod->bias_radius < 0 || mod->bias_radius > BSM_BIAS_MAX_RADIUS)
+            return fail(BSM_E_UNSUPPORTED, "bias radius %d must be in [0, %d]", mod->bias_radius,
+                        BSM_BIAS_MAX_RADIUS);
+        if (mod->flags & BSM_MOD_ALIBI)
+            return fail(BSM_E_UNSUPPORTED, "ALIBI and BIAS together are not built (put the slope into the table)");
+    } else if (mod->bias_grad) {
+        return fail(BSM_E_INVALID, "bias_grad given without BIAS");
+    }
     return BSM_OK;
 }
 
@@ -191,6 +201,14 @@ void fill_tensor(const bsm_tensor *t, const void *&ptr, int64_t &sb, int64_t &sh
     st = t->stride_t;
 }
 
+void fill_bias(bsm::AttnParams &p, const bsm_score_mod *mod) {
+    const bool on = mod && (mod->flags & BSM_MOD_BIAS);
+    p.bias = on ? mod->bias : nullptr;
+    p.bias_r = on ? mod->bias_radius : 0;
+    p.dbias_part = nullptr;  // set by the backward only
+    p.dbias = nullptr;
+}
+
 void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
                  const bsm_block_mask *bm, const bsm_mask_spec *spec, const bsm_score_mod *mod,
                  float scale) {
@@ -215,6 +233,7 @@ void fill_common(bsm::AttnParams &p, int32_t B, int32_t H, int32_t T, int32_t D,
     p.window = spec->window;
     p.mod_flags = mod ? mod->flags : 0u;
     p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
+    fill_bias(p, mod);
     p.dslopes = nullptr;  // set by the backward only
     p.dslope_part = nullptr;
     p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
@@ -285,6 +304,7 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     bsm_status st = check_mod(mod);
     if (st != BSM_OK) return st;
     if (mod && mod->alibi_slopes_grad) return fail(BSM_E_INVALID, "alibi_slopes_grad is a backward output");
+    if (mod && mod->bias_grad) return fail(BSM_E_INVALID, "bias_grad is a backward output");
     if ((st = check_tensor(q, "q")) != BSM_OK) return st;
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;
     if ((st = check_tensor(v, "v")) != BSM_OK) return st;
@@ -313,6 +333,7 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     p.window = spec->window;
     p.mod_flags = mod ? mod->flags : 0u;
     p.alibi_slopes = mod ? mod->alibi_slopes : nullptr;
+    fill_bias(p, mod);
     p.softcap = (mod && (mod->flags & BSM_MOD_SOFTCAP)) ? mod->softcap : 0.0f;
     p.scale = scale > 0.0f ? scale : 1.0f / std::sqrt((float)D);
     if (bm) {
@@ -465,6 +486,18 @@ size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D) {
            align256((size_t)B * H * ((Q + bsm::kTile - 1) / bsm::kTile) * sizeof(float));
 }
 
+static size_t bias_part_bytes(int32_t B, int32_t H, int32_t Q, const bsm_score_mod *mod) {
+    if (!mod || !(mod->flags & BSM_MOD_BIAS)) return 0;
+    return align256((size_t)B * H * ((Q + bsm::kTile - 1) / bsm::kTile) * (2 * (size_t)mod->bias_radius + 1) *
+                    sizeof(float));
+}
+
+size_t bsm_bwd_workspace_bytes_mod(int32_t B, int32_t H, int32_t Q, int32_t D, const bsm_score_mod *mod) {
+    const size_t base = bsm_bwd_workspace_bytes(B, H, Q, D);
+    if (base == 0 || check_mod(mod) != BSM_OK) return 0;
+    return base + bias_part_bytes(B, H, Q, mod);
+}
+
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, const bsm_tensor *q,
                                   const bsm_tensor *k, const bsm_tensor *v, const bsm_tensor *out,
                                   const float *lse, const bsm_tensor *dout, const bsm_block_mask *bm,
@@ -486,7 +519,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     if (!lse) return fail(BSM_E_INVALID, "lse is NULL");
     if (!std::isfinite(scale)) return fail(BSM_E_INVALID, "scale must be finite");
     const int32_t Q = mask_dims(spec).q_len;
-    const size_t need = bsm_bwd_workspace_bytes(B, H, Q, D);
+    const size_t need = bsm_bwd_workspace_bytes_mod(B, H, Q, D, mod);
     if (!workspace || workspace_bytes < need)
         return fail(BSM_E_WORKSPACE, "backward workspace needs %zu bytes, got %zu%s", need,
                     workspace_bytes, workspace ? "" : " (NULL)");
@@ -513,6 +546,10 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
     p.dslope_part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
                                               2 * align256((size_t)B * H * Q * sizeof(float)));
     p.dslopes = (mod && (mod->flags & BSM_MOD_ALIBI)) ? mod->alibi_slopes_grad : nullptr;
+    if (p.bias) {
+        p.dbias_part = reinterpret_cast<float *>(static_cast<char *>(workspace) + bsm_bwd_workspace_bytes(B, H, Q, D));
+        p.dbias = mod->bias_grad;
+    }
     return hip_status(bwd_launcher(D, q->dtype)(p, static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_bwd launch");
 }

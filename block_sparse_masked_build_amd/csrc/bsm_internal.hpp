@@ -63,6 +63,8 @@ struct AttnParams {
     const int32_t *doc_ids;
     const int32_t *window;
     const float *alibi_slopes;
+    const float *bias;   // BIAS: [H, 2 bias_r + 1] relative-position bias table
+    int32_t bias_r;      // BIAS: its radius R
     // block mask
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
     const int32_t *q_num, *q_idx, *full_q_num, *full_q_idx;
@@ -82,6 +84,8 @@ struct AttnParams {
     float *lse2;     // [B, H, q_len] (backward workspace): lse * log2(e), 0 where lse = -inf
     float *dslope_part;  // [B, H, nqt] (backward workspace): slope-gradient partial per query tile
     float *dslopes;      // [H] backward output dL/dslope, or NULL (not computed)
+    float *dbias_part;   // BIAS: [B, H, nqt, 2 bias_r + 1] (backward workspace): bias-gradient partials
+    float *dbias;        // BIAS: [H, 2 bias_r + 1] backward output dL/dbias, or NULL (not reduced)
     // forward item order: items per work-order entry, full blocks, entries in
     // the last block, and division magic numbers (set by the launcher)
     int32_t ord_r, ord_chunk_log2, ord_nblk, ord_p;

@@ -86,11 +86,21 @@ enum {
 /* Score modifications (bsm_score_mod.flags), applied to s = scale * q.k in
  * this order (tutorial "FlexAttention in PyTorch", Pattern 3):
  *   ALIBI:   s <- s - alibi_slopes[h] * (q - kv)     (absolute positions)
- *   SOFTCAP: s <- softcap * tanh(s / softcap)                           */
+ *   BIAS:    s <- s + bias[h][R + clip(q - kv, -R, R)]
+ *   SOFTCAP: s <- softcap * tanh(s / softcap)
+ * BIAS is a learned relative-position bias (named in the same section): one
+ * scalar per head and query-key distance, distances beyond R sharing the
+ * end entries (clipped relative positions).  ALIBI and BIAS together are
+ * BSM_E_UNSUPPORTED (within R a slope is a special table).               */
 enum {
     BSM_MOD_ALIBI = 1u,
-    BSM_MOD_SOFTCAP = 2u
+    BSM_MOD_SOFTCAP = 2u,
+    BSM_MOD_BIAS = 4u
 };
+
+/* Largest bias radius R: the kernels keep the head's 2R + 1 entries (and
+ * the backward its per-wave gradient sums) in LDS. */
+#define BSM_BIAS_MAX_RADIUS 1024
 
 typedef struct {
     uint32_t flags;          /* BSM_MASK_* bits                                    */
@@ -190,6 +200,18 @@ typedef struct {
                                     PyTorch", Pattern 3).  Non-NULL without
                                     ALIBI is BSM_E_INVALID; the forward
                                     ignores it.                        */
+    const float *bias;           /* BIAS: device float32 [H, 2 bias_radius + 1],
+                                    rows contiguous; entry R + d holds the bias
+                                    of distance q - kv = d                */
+    int32_t bias_radius;         /* BIAS: R, 0 <= R <= BSM_BIAS_MAX_RADIUS  */
+    float *bias_grad;            /* BIAS, backward only: NULL, or device
+                                    float32 [H, 2R + 1] that
+                                    bsm_flex_attention_bwd overwrites with
+                                    dL/dbias summed over the batch (the sums
+                                    are formed in a fixed order: repeated
+                                    calls give identical bits).  Non-NULL
+                                    without BIAS is BSM_E_INVALID; the forward
+                                    ignores it, a decoding step rejects it. */
 } bsm_score_mod;
 
 /* Element types of bsm_tensor.dtype (0, the zero-initialised value, is
@@ -255,6 +277,12 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D,
  * Q_LEN (the square case: T). */
 size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D);
 
+/* The same for a call with score modifications `mod` (may be NULL): with
+ * BIAS it adds one bias-gradient partial row of 2R + 1 floats per (batch,
+ * head, query tile), B*H*ceil(Q/128)*(2R + 1)*4 bytes rounded up to 256.
+ * Returns 0 for arguments the backward would reject. */
+size_t bsm_bwd_workspace_bytes_mod(int32_t B, int32_t H, int32_t Q, int32_t D, const bsm_score_mod *mod);
+
 /* Backward attention: gradients of sum(out * dout) with respect to q, k, v
  * through the softmax, the mask and the score modifications (tutorial
  * "FlexAttention in PyTorch", Pattern 3: differentiable score mods with a
@@ -265,8 +293,12 @@ size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D);
  * mod->alibi_slopes_grad (optional, ALIBI): dL/dslope[h] = sum over the batch
  * and the visible pairs of g_qk (k - q), with g the gradient with respect to
  * the score the ALiBi term is added to; deterministic (fixed-order sums).
- * workspace: device, >= bsm_bwd_workspace_bytes(B, H, Q_LEN, D), 256-byte
- * aligned.  Errors: as the forward, plus BSM_E_WORKSPACE. */
+ * mod->bias_grad (optional, BIAS): dL/dbias[h][R + r] = sum over the batch
+ * and the visible pairs with clip(q - kv, -R, R) = r of g_qk, the same g;
+ * deterministic as well.  With BIAS the kernels form these sums whether or
+ * not bias_grad is given.
+ * workspace: device, >= bsm_bwd_workspace_bytes_mod(B, H, Q_LEN, D, mod),
+ * 256-byte aligned.  Errors: as the forward, plus BSM_E_WORKSPACE. */
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *q, const bsm_tensor *k,
                                   const bsm_tensor *v, const bsm_tensor *out,

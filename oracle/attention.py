@@ -311,10 +311,13 @@ def slope_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=Non
     return total, mass
 
 
-def bias_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=None):
+def bias_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=None, with_pmass=False):
     """(dL/dbias[h, :] for batch element b, the same sums of |g|), float64
     [2R + 1] each, over every visible pair (small T).  out, lse: as for
-    slope_grad_dense."""
+    slope_grad_dense.  with_pmass also returns, per entry, the sum over its
+    pairs of p c' (sum_d |dO_qd v_jd| + sum_d |dO_qd out_qd|): the size of
+    the dot products dP and Delta that g subtracts, which bounds what
+    rounding them moves g by."""
     T, D = Q.shape
     sc = _scale(D, scale)
     R = bias_radius(mod)
@@ -323,10 +326,16 @@ def bias_grad_dense(Q, K, V, dO, spec, mod, b, h, scale=None, out=None, lse=None
     allcols = np.arange(K.shape[0])
     grad = np.zeros(2 * R + 1, dtype=np.float64)
     mass = np.zeros(2 * R + 1, dtype=np.float64)
+    pmass = np.zeros(2 * R + 1, dtype=np.float64)
     for a in range(0, T, ROW_CHUNK):
         r = np.arange(a, min(T, a + ROW_CHUNK))
-        g, _ = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc)
-        idx = bias_index(mod, r + _qoff(spec), allcols)
-        grad += np.bincount(idx.ravel(), weights=g.ravel(), minlength=2 * R + 1)
-        mass += np.bincount(idx.ravel(), weights=np.abs(g).ravel(), minlength=2 * R + 1)
+        g, p, cp = _grad_block(Q, K, V, dO, spec, mod, b, h, r, allcols, out[r], lse[r], sc, with_cap=True)
+        idx = bias_index(mod, r + _qoff(spec), allcols).ravel()
+        grad += np.bincount(idx, weights=g.ravel(), minlength=2 * R + 1)
+        mass += np.bincount(idx, weights=np.abs(g).ravel(), minlength=2 * R + 1)
+        if with_pmass:
+            dots = np.abs(dO[r]) @ np.abs(V).T + np.sum(np.abs(dO[r] * out[r]), axis=1)[:, None]
+            pmass += np.bincount(idx, weights=(p * cp * dots).ravel(), minlength=2 * R + 1)
+    if with_pmass:
+        return grad, mass, pmass
     return grad, mass

@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -174,6 +174,43 @@ def test_bwd_rejects_slope_gradient_without_alibi():
         ctypes.byref(spec), ctypes.byref(mod), 0.0, *([ctypes.byref(t)] * 3), FAKE, need, None)
     assert rc == _lib.BSM_E_INVALID
     assert "alibi_slopes_grad" in lib.bsm_last_error().decode()
+
+
+def test_bias_table_checks_and_workspace():
+    """Relative-position bias table: a table is required, its radius is at
+    most BSM_BIAS_MAX_RADIUS, ALiBi and a table together are not built, a
+    gradient output needs the table, and the backward workspace grows by one
+    partial row of 2R + 1 floats per (batch, head, query tile)."""
+    R = 100
+    ok = BsmScoreMod(_lib.BSM_MOD_BIAS, None, 0.0, None, FAKE, R, None)
+    assert _fwd(mod=BsmScoreMod(_lib.BSM_MOD_BIAS, None, 0.0, None, None, R, None)) == _lib.BSM_E_INVALID
+    assert _fwd(mod=BsmScoreMod(_lib.BSM_MOD_BIAS, None, 0.0, None, FAKE, -1, None)) == _lib.BSM_E_UNSUPPORTED
+    assert _fwd(mod=BsmScoreMod(_lib.BSM_MOD_BIAS, None, 0.0, None, FAKE, _lib.BSM_BIAS_MAX_RADIUS + 1,
+                                None)) == _lib.BSM_E_UNSUPPORTED
+    assert _fwd(mod=BsmScoreMod(_lib.BSM_MOD_BIAS | _lib.BSM_MOD_ALIBI, FAKE, 0.0, None, FAKE, R,
+                                None)) == _lib.BSM_E_UNSUPPORTED
+    assert _fwd(mod=BsmScoreMod(0, None, 0.0, None, None, 0, FAKE)) == _lib.BSM_E_INVALID  # gradient, no table
+    assert "bias_grad" in lib.bsm_last_error().decode()
+    base = lib.bsm_bwd_workspace_bytes(2, 3, 1000, 64)
+    assert lib.bsm_bwd_workspace_bytes_mod(2, 3, 1000, 64, None) == base
+    need = lib.bsm_bwd_workspace_bytes_mod(2, 3, 1000, 64, ctypes.byref(ok))
+    part = 2 * 3 * 8 * (2 * R + 1) * 4  # 8 query tiles
+    assert need == base + (part + 255) // 256 * 256
+    bad = BsmScoreMod(_lib.BSM_MOD_BIAS, None, 0.0, None, None, R, None)
+    assert lib.bsm_bwd_workspace_bytes_mod(2, 3, 1000, 64, ctypes.byref(bad)) == 0
+    # the backward asks for the larger workspace
+    spec = _spec()
+    t = _t()
+    small = lib.bsm_bwd_workspace_bytes(1, 1, 1024, 64)
+    rc = lib.bsm_flex_attention_bwd(
+        1, 1, 1024, 64, *([ctypes.byref(t)] * 4), FAKE, ctypes.byref(t), ctypes.byref(_bm()),
+        ctypes.byref(spec), ctypes.byref(ok), 0.0, *([ctypes.byref(t)] * 3), FAKE, small, None)
+    assert rc == _lib.BSM_E_WORKSPACE
+    # a decoding step computes no gradient
+    dmod = BsmScoreMod(_lib.BSM_MOD_BIAS, None, 0.0, None, FAKE, R, FAKE)
+    rc = lib.bsm_flex_attention_decode(1, 1, 1024, 64, FAKE, 0, *([ctypes.byref(t)] * 3), ctypes.byref(spec), None,
+                                       ctypes.byref(dmod), 0.0, ctypes.byref(t), FAKE, FAKE, 1 << 20, None)
+    assert rc == _lib.BSM_E_INVALID and "bias_grad" in lib.bsm_last_error().decode()
 
 
 def test_decode_rejects_bad_arguments():
