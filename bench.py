@@ -61,8 +61,15 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="leave out the timing of the other workloads (detail.configs)")
     ap.add_argument("--config-reps", type=int, default=8, help="cold reps per other workload")
+    ap.add_argument("--configs", default=",".join(CONFIG_KEYS),
+                    help="comma-separated workloads timed for detail.configs")
     return ap.parse_args()
 
+
+# Workloads of detail.configs ("-block64": 128 x 64 blocks; "-bias": with a
+# relative-position bias table and its gradient).
+CONFIG_KEYS = ("1", "2", "2-block64", "2-bias", "2-causal", "2-window", "2-chunks", "3", "4a", "4b", "5",
+               "5-block64")
 
 FLUSH_BYTES = 512 << 20
 _flush_buf = None
@@ -268,16 +275,19 @@ class Path:
         self.host = t
         self.spec = api.from_spec_data(w.spec)
         self.mod = None
-        if w.mod.alibi_slopes is not None or w.mod.softcap is not None:
-            self.mod = api.score_mod(w.mod.alibi_slopes, w.mod.softcap)
+        bias = getattr(w.mod, "bias_table", None)
+        if w.mod.alibi_slopes is not None or w.mod.softcap is not None or bias is not None:
+            self.mod = api.score_mod(w.mod.alibi_slopes, w.mod.softcap, bias=bias)
         self.bm = api.empty_block_mask(self.spec)
         self.ws = api.block_mask_workspace(self.spec)
         self.out = torch.empty_like(self.dev["q"])
         self.lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device="cuda")
-        self.dslopes = None
+        self.dslopes = self.dbias = None
         if backward:
             self.grads = [torch.empty_like(self.dev["q"]) for _ in range(3)]
-            self.bws = api.bwd_workspace(w.B, w.H, w.T, w.D)
+            self.bws = api.bwd_workspace(w.B, w.H, w.T, w.D, mod=self.mod)
+            if bias is not None:
+                self.dbias = torch.empty(self.mod.bias.shape, dtype=torch.float32, device="cuda")
             if slopes:
                 self.dslopes = torch.empty(w.H, dtype=torch.float32, device="cuda")
 
@@ -293,7 +303,8 @@ class Path:
         d = self.dev
         dq, dk, dv = self.grads
         self.api.flex_attention_bwd(d["q"], d["k"], d["v"], self.out, self.lse, d["dout"], self.bm, self.spec,
-                                    self.mod, dq=dq, dk=dk, dv=dv, workspace=self.bws, dslopes=self.dslopes)
+                                    self.mod, dq=dq, dk=dk, dv=dv, workspace=self.bws, dslopes=self.dslopes,
+                                    dbias=self.dbias)
 
 
 def config_detail(api, key, reps):
@@ -301,13 +312,21 @@ def config_detail(api, key, reps):
     backward) backward medians, and the throughput over visible tiles.  A
     key ending in "-block64" is that workload with 128 x 64 blocks: its
     throughput counts the listed 64-key blocks (4 * 128 * 64 * D flops
-    each), the work the kernels do there."""
+    each), the work the kernels do there.  A key ending in "-bias" adds a
+    relative-position bias table of radius 1024 (N(0, 0.25) entries) and
+    runs the backward with its gradient."""
     import dataclasses
     import numpy as np
     import torch
-    from workloads import make_config
+    from workloads import bias_table, make_config
+    with_bias = key.endswith("-bias")
+    if with_bias:
+        key = key[:-len("-bias")]
     base, _, variant = key.partition("-block")
     w = make_config(base if variant else key)
+    if with_bias:
+        w = dataclasses.replace(w, name=w.name + ", bias table R 1024", backward=True,
+                                mod=dataclasses.replace(w.mod, bias_table=bias_table(w.H, 1024, seed=2, sd=0.5)))
     kb = TILE
     if variant:
         kb = int(variant)
@@ -487,7 +506,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_configs:
         confs = {}
-        for key in ("1", "2", "2-block64", "2-causal", "2-window", "2-chunks", "3", "4a", "4b", "5", "5-block64"):
+        for key in [k for k in args.configs.split(",") if k]:
+            if key not in CONFIG_KEYS:
+                sys.exit(f"unknown config {key!r}: one of {', '.join(CONFIG_KEYS)}")
             print(f"[bench] timing workload {key}", file=sys.stderr, flush=True)
             confs[key] = config_detail(api, key, args.config_reps)
         line["detail"]["configs"] = confs

@@ -79,6 +79,7 @@ struct DqArgs {
     int64_t k_st, v_st;
     const int32_t *fidx, *pidx, *doc;
     int nfull, nt, qpos;  // qpos: absolute position of this lane's query
+    int qw0;              // absolute position of the wave's first query (BIAS)
     int kv_len, npos;
     int spb;              // 64-key steps per listed block: 2 (128-key blocks) or 1
     float scale, scale_log2, slope, cap, inv_cap;
@@ -102,57 +103,68 @@ struct DqLds {
     uint32_t k, v, doc;  // buffer 0; buffer 1 follows
 };
 
-// Bias-gradient sums of one wave (BIAS).  Every wave owns two LDS arrays of
-// kBiasAccStride floats, one per lane half, at bacc (this lane's half):
-// entries 0..2R sum g over the pairs of each clipped distance; the 32 after
-// them sum each lane's pairs beyond +R, the next 32 those beyond -R.  Within
-// one add instruction the lanes of a half have 32 distinct distances, so no
-// two lanes of an instruction touch one address, and a wave's LDS operations
-// complete in order: every sum is formed in program order, and the item's
-// partial row (bias_grad_flush) is identical from run to run.
-constexpr int kBiasAccStride = kBiasMaxEntries + 64;
+// Bias-gradient sums of one wave (BIAS).  The gradient of table entry
+// R + d sums g over the pairs at clipped distance d, so each step's
+// 32 x 64 block of g is reduced along its diagonals.  Per 32-key block, the
+// wave writes its 32 x 32 values to a private LDS scratch skewed so that
+// each diagonal is one row (pair (query n, key c) at row n - c + 31, column
+// n; positions no pair maps to stay zero), and lane j then sums row j in
+// a fixed order and adds it to the wave's private accumulator: entries
+// 0..2R for the clipped distances, then one slot per lane for distances
+// beyond +R and one beyond -R.  Plain LDS reads and writes: within an
+// instruction every lane has its own address, and a wave's LDS operations
+// complete in order, so every sum is formed in program order and the
+// item's partial row (bias_grad_flush) is identical from run to run.
+constexpr int kDiagRows = 63;        // diagonals of a 32 x 32 block
+constexpr int kDiagStride = 40;      // floats per scratch row: conflict-free skewed writes
+constexpr int kDiagFloats = kDiagRows * kDiagStride;
+constexpr int kBiasAccStride = kBiasMaxEntries + 128;
 
-__device__ inline void bias_grad_add(const float (&dsv)[2][16], int key0, int qpos, int R, uint32_t bacc) {
-    const int hl = (threadIdx.x & 63) >> 5, n = threadIdx.x & 31;
-    const int t = qpos - (key0 + 4 * hl);  // distance at register offset c: t - c
-    if (__all(t - kRowMaxOffset >= -R && t <= R)) {
-        const uint32_t a0 = bacc + 4u * (uint32_t)(t - kRowMaxOffset + R);
+// qw0: absolute position of the wave's first query (lanes past Q_LEN carry
+// g = 0, so their positions only decide where zeros are added).
+__device__ inline void bias_grad_add(const float (&dsv)[2][16], int key0, int qw0, int R, uint32_t scr,
+                                     uint32_t acc) {
+    const int lane = threadIdx.x & 63, n = lane & 31, hl = lane >> 5;
+    constexpr int kMaxC = 27;  // largest in-block key offset 8 g + e of a lane half
+    // pair (n, c = 8 g + 4 hl + e) -> row n - c + 31, column n
+    const uint32_t wbase = scr + 4u * (uint32_t)((n - 4 * hl - kMaxC + 31) * kDiagStride + n);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-                lds_add(a0 + 4u * (uint32_t)(kRowMaxOffset - c), dsv[kb][r]);
+        for (int r = 0; r < 16; ++r) {
+            const int c = (r >> 2) * 8 + (r & 3);
+            lds_store<float>(wbase + 4u * (uint32_t)((kMaxC - c) * kDiagStride), dsv[kb][r]);
+        }
+        if (lane < kDiagRows) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 32 / 4; ++k) {
+                const f32x4 v = lds_load<f32x4>(scr + 4u * (uint32_t)(lane * kDiagStride + 4 * k));
+                sum += ((v[0] + v[1]) + v[2]) + v[3];
             }
-    } else {
-        const int hi_slot = 2 * R + 1 + n, lo_slot = 2 * R + 33 + n;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int c = kb * 32 + (r >> 2) * 8 + (r & 3);
-                const int d = t - c;
-                const int idx = d > R ? hi_slot : d < -R ? lo_slot : d + R;
-                lds_add(bacc + 4u * (uint32_t)idx, dsv[kb][r]);
-            }
+            const int d = qw0 - key0 - 32 * kb + lane - 31;  // the row's distance q - kv
+            const int idx = d > R ? 2 * R + 1 + lane : d < -R ? 2 * R + 65 + lane : d + R;
+            const uint32_t a = acc + 4u * (uint32_t)idx;
+            lds_store<float>(a, lds_load<float>(a) + sum);
+        }
     }
 }
 
-// The item's partial row: entry j summed over the four waves and both lane
-// halves in a fixed order, the overflow slots into the end entries.
+// The item's partial row: entry j summed over the four waves in a fixed
+// order, the overflow slots into the end entries.
 __device__ inline void bias_grad_flush(uint32_t acc0, int R, float *row) {
     const int nb = 2 * R + 1;
     for (int j = threadIdx.x; j < nb; j += kThreads) {
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 2 * (kThreads / 64); ++w) v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + j));
+        for (int w = 0; w < kThreads / 64; ++w) v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + j));
         if (j == nb - 1)
-            for (int w = 0; w < 2 * (kThreads / 64); ++w)
-                for (int k = 0; k < 32; ++k) v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + nb + k));
+            for (int w = 0; w < kThreads / 64; ++w)
+                for (int k = 0; k < 64; ++k) v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + nb + k));
         if (j == 0)
-            for (int w = 0; w < 2 * (kThreads / 64); ++w)
-                for (int k = 0; k < 32; ++k)
-                    v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + nb + 32 + k));
+            for (int w = 0; w < kThreads / 64; ++w)
+                for (int k = 0; k < 64; ++k)
+                    v += lds_load<float>(acc0 + 4u * (uint32_t)(w * kBiasAccStride + nb + 64 + k));
         row[j] = v;
     }
 }
@@ -168,7 +180,8 @@ __device__ inline void bias_grad_flush(uint32_t acc0, int R, float *row) {
 template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, int MODE, bool GENERAL, bool BIAS = false>
 __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (&qf)[D / 16],
                                const elem8 (&gf)[D / 16], const KvOffsets &off, const DqLds<D> &lds, int nsteps,
-                               f32x16 (&dq)[D / 32], float &sg, const BiasLds &bl = {}, uint32_t bacc = 0) {
+                               f32x16 (&dq)[D / 32], float &sg, const BiasLds &bl = {}, uint32_t bscr = 0,
+                               uint32_t bacc = 0) {
     static_assert(!SGRAD || ALIBI, "the slope gradient needs the ALiBi term");
     constexpr bool kMods = ALIBI || SOFTCAP || BIAS;
     constexpr uint32_t kTB = DqLds<D>::kTileBytes;
@@ -253,7 +266,7 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
             const int hl = (threadIdx.x & 63) >> 5;
             sg = __builtin_fmaf((float)(key0 + 4 * hl - a.qpos), sg_s, sg + sg_c);
         }
-        if (BIAS) bias_grad_add(dsv, key0, a.qpos, bl.R, bacc);
+        if (BIAS) bias_grad_add(dsv, key0, a.qw0, bl.R, bscr, bacc);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             if (skip[kb]) continue;
@@ -272,21 +285,23 @@ __device__ inline void dq_main(const DqArgs &a, const RowMask &rm, const elem8 (
 // evaluation does not take registers from the other masks' kernels).
 // BIAS: a relative-position bias table (no ALiBi; general path only),
 // staged in LDS, with the per-wave bias-gradient sums (see bias_grad_add).
-// The table and the eight gradient arrays take 74 KB of LDS, so the BIAS
+// The table, the four per-wave gradient arrays and diagonal scratches take
+// 81 KB of LDS, so the BIAS
 // kernels run one workgroup per CU.  (One kernel template: routing the
 // kernel through a shared device-function body changed the register
 // allocation of the other instances.)
 template <int D, bool BIAS>
 struct DqBiasSmem {
     float tab[BIAS ? kBiasMaxEntries : 1];
-    float acc[BIAS ? 2 * (kThreads / 64) * kBiasAccStride : 1];
+    float acc[BIAS ? (kThreads / 64) * kBiasAccStride : 1];
+    float scr[BIAS ? (kThreads / 64) * kDiagFloats : 1];
 };
 
 template <int D, bool ALIBI, bool SOFTCAP, bool SGRAD, bool TABLE, bool GENERAL, bool BIAS>
 __global__ __launch_bounds__(kThreads, (BIAS ? 1 : kWgPerCu<D, ALIBI || SOFTCAP>)) void dq_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(1024))) DqSmem<D> sm;
     __shared__ DqBiasSmem<D, BIAS> bsm;
-    const uint32_t btab = lds_addr(bsm.tab), bacc = lds_addr(bsm.acc);
+    const uint32_t btab = lds_addr(bsm.tab), bacc = lds_addr(bsm.acc), bscr = lds_addr(bsm.scr);
 
     const int nt = p.nkb;  // key blocks of the row lists
     // Item: a query-tile row of the row work order (longest first) and a
@@ -378,14 +393,18 @@ __global__ __launch_bounds__(kThreads, (BIAS ? 1 : kWgPerCu<D, ALIBI || SOFTCAP>
         }
     }
     // BIAS: lanes past Q_LEN (a copy of the last query) get p = 0, so that
-    // they add nothing to the bias gradient; the table goes to LDS and this
-    // wave's gradient sums start at zero (the wave's own LDS operations stay
-    // in order, the table is read after the first step's barrier).
-    const uint32_t bacc_w = bacc + 4u * (uint32_t)((wv * 2 + hl) * kBiasAccStride);
+    // they add nothing to the bias gradient; the table goes to LDS, and this
+    // wave's gradient sums and diagonal scratch start at zero (the wave's
+    // own LDS operations stay in order, the table is read after the first
+    // step's barrier).
+    const uint32_t bacc_w = bacc + 4u * (uint32_t)(wv * kBiasAccStride);
+    const uint32_t bscr_w = bscr + 4u * (uint32_t)(wv * kDiagFloats);
     if (BIAS) {
+        a.qw0 = p.q_off + i * kTile + wv * 32;
         if (qidx >= p.q_len) a.l2 = INFINITY;
         stage_bias_store(bstage, nb, mod_f<SOFTCAP>(a.cap), btab);
-        for (int j = n; j < kBiasAccStride; j += 32) lds_store<float>(bacc_w + 4u * (uint32_t)j, 0.0f);
+        for (int j = lane; j < kBiasAccStride; j += 64) lds_store<float>(bacc_w + 4u * (uint32_t)j, 0.0f);
+        for (int j = lane; j < kDiagFloats; j += 64) lds_store<float>(bscr_w + 4u * (uint32_t)j, 0.0f);
         wait_lds_reads();  // (and writes)
     }
     const BiasLds bl = {btab, p.bias_r};
@@ -401,13 +420,13 @@ __global__ __launch_bounds__(kThreads, (BIAS ? 1 : kWgPerCu<D, ALIBI || SOFTCAP>
 
     float sg = 0.0f;
     if (TABLE)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kTable, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bscr_w, bacc_w);
     else if (mode == kGather)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kGather, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bscr_w, bacc_w);
     else if (mode == kSinks)
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kSinks, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bscr_w, bacc_w);
     else
-        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bacc_w);
+        dq_main<D, ALIBI, SOFTCAP, SGRAD, kPlain, GENERAL, BIAS>(a, rm, qf, gf, off, lds, nsteps, dq, sg, bl, bscr_w, bacc_w);
     if (BIAS) {
         __syncthreads();  // every wave's sums are complete
         bias_grad_flush(bacc, p.bias_r, p.dbias_part + (((int64_t)b * p.H + h) * p.nqt + i) * nb);
@@ -871,17 +890,29 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_bias_kernel(
     dkdv_body<D, false, SOFTCAP, TABLE, true, true>(p, sm, lds_addr(btab));
 }
 
-// dL/dbias: the per-(batch, head, query tile) partial rows of the BIAS dq_kernel
-// summed over the batch and the query tiles in a fixed order; one thread per
-// (head, entry), coalesced over the entries.
+// dL/dbias: the per-(batch, head, query tile) partial rows of the BIAS
+// dq_kernel summed over the batch and the query tiles in a fixed order: a
+// workgroup takes 32 entries of one head, its 8 row groups sum the rows
+// g, g + 8, ... in turn, and the groups are added in order.
 __global__ __launch_bounds__(kThreads) void bias_reduce_kernel(const float *part, float *dbias, int B, int H,
                                                                  int nqt, int nb) {
-    const int h = blockIdx.y, j = blockIdx.x * kThreads + threadIdx.x;
-    if (j >= nb) return;
+    constexpr int kGroups = kThreads / 32;
+    __shared__ float red[kGroups][32];
+    const int h = blockIdx.y, e = threadIdx.x & 31, g = threadIdx.x >> 5;
+    const int j = blockIdx.x * 32 + e;
     float acc = 0.0f;
-    for (int b = 0; b < B; ++b)
-        for (int i = 0; i < nqt; ++i) acc += part[(((int64_t)b * H + h) * nqt + i) * nb + j];
-    dbias[(int64_t)h * nb + j] = acc;
+    if (j < nb)
+        for (int r = g; r < B * nqt; r += kGroups) {
+            const int b = r / nqt, i = r - b * nqt;
+            acc += part[(((int64_t)b * H + h) * nqt + i) * nb + j];
+        }
+    red[g][e] = acc;
+    __syncthreads();
+    if (g == 0 && j < nb) {
+        float v = 0.0f;
+        for (int k = 0; k < kGroups; ++k) v += red[k][e];
+        dbias[(int64_t)h * nb + j] = v;
+    }
 }
 
 // dL/dslope[h]: the per-(batch, head, query tile) partials of dq_kernel
@@ -951,7 +982,7 @@ void launch_bias(const AttnParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((dq_kernel<D, false, SOFTCAP, false, TABLE, true, true>), dq_grid, block, 0, stream, q);
     if (p.dbias) {
         const int nb = 2 * p.bias_r + 1;
-        hipLaunchKernelGGL(bias_reduce_kernel, dim3((nb + kThreads - 1) / kThreads, p.H), block, 0, stream,
+        hipLaunchKernelGGL(bias_reduce_kernel, dim3((nb + 31) / 32, p.H), block, 0, stream,
                            p.dbias_part, p.dbias, p.B, p.H, p.nqt, nb);
     }
     hipLaunchKernelGGL((dkdv_bias_kernel<D, SOFTCAP, TABLE>), dkdv_grid, block, 0, stream, q);
