@@ -100,14 +100,17 @@ class Workload:
     seed: int
     backward: bool = False
     windows: Optional[list] = None  # window sweep (config 3)
+    dtype: str = "bf16"             # element type of q, k, v, dout: "bf16" or "f16"
 
     def tensors(self, with_dout: Optional[bool] = None) -> dict:
-        """q, k, v (and dout) as bfloat16 CPU tensors [B, H, T, D]."""
+        """q, k, v (and dout) as CPU tensors [B, H, T, D] of the workload's
+        element type (bfloat16 unless dtype says float16)."""
         if with_dout is None:
             with_dout = self.backward
         g = torch.Generator("cpu").manual_seed(self.seed)
         names = ["q", "k", "v"] + (["dout"] if with_dout else [])
-        return {n: random_bf16((self.B, self.H, self.T, self.D), g) for n in names}
+        rand = random_f16 if self.dtype == "f16" else random_bf16
+        return {n: rand((self.B, self.H, self.T, self.D), g) for n in names}
 
 
 def random_bf16(shape, generator: torch.Generator) -> torch.Tensor:
