@@ -177,6 +177,17 @@ struct TileLayout<64> {
     __device__ static int fkv(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 };
 
+// D = 256: 512-byte rows start on the same bank, as the 256-byte ones do,
+// so the D = 128 patterns (four row bits into the chunk index) serve.
+template <>
+struct TileLayout<256> {
+    static constexpr int kRowBytes = 512;
+    static constexpr int kChunks = 32;
+    __device__ static int fk(int r) { return r & 15; }
+    __device__ static int fv(int r) { return (r & 3) << 2; }
+    __device__ static int fkv(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+};
+
 template <int D, int SWZ>
 __device__ inline int tile_swizzle(int r) {
     using L = TileLayout<D>;
@@ -973,8 +984,10 @@ constexpr int kQueues = 8;
 // without score modifications the loops fit 168 registers with no spill
 // inside them, and the LDS (33 KB) allows three: 12 waves per CU instead of
 // 8.  With score modifications at 168 registers the loops would spill.
+// At D = 256 the K/V buffers alone take 128 KB: one per CU, with up to 512
+// registers per lane.
 template <int D, bool MODS>
-constexpr int kWgPerCu = (D == 64 && !MODS) ? 3 : 2;
+constexpr int kWgPerCu = D == 256 ? 1 : (D == 64 && !MODS) ? 3 : 2;
 
 // Quotient k / d for 0 <= k < 2^31 and d >= 1, with m = ceil(2^32 / d)
 // computed on the host (d >= 2; d = 1 is passed through): the estimate is

@@ -378,6 +378,7 @@ hipError_t BSM_ELEM_FN(launch_attn_decode)(const DecodeLaunch &d, float *part, h
     P.part_o = part;
     P.part_ml = part + (int64_t)a.B * a.H * P.nslot * d.D;
     if (d.D == 64) return launch_d<64>(P, a.mod_flags, stream);
+    if (d.D == 256) return launch_d<256>(P, a.mod_flags, stream);
     return launch_d<128>(P, a.mod_flags, stream);
 }
 

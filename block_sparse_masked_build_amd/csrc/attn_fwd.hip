@@ -633,5 +633,8 @@ hipError_t BSM_ELEM_FN(launch_attn_fwd_d64)(const AttnParams &p, hipStream_t str
 #if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 128
 hipError_t BSM_ELEM_FN(launch_attn_fwd_d128)(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
 #endif
+#if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 256
+hipError_t BSM_ELEM_FN(launch_attn_fwd_d256)(const AttnParams &p, hipStream_t stream) { return launch_d<256>(p, stream); }
+#endif
 
 }  // namespace bsm

@@ -30,6 +30,11 @@ bsm_status ok() {
 }
 
 constexpr int32_t kMaxT = 1 << 22;
+
+// Head dimensions the forward and decoding kernels are built for (the
+// backward: 64 and 128, see bwd_head_dim).
+bool built_head_dim(int32_t D) { return D == 64 || D == 128 || D == 256; }
+bool bwd_head_dim(int32_t D) { return D == 64 || D == 128; }
 constexpr uint32_t kMaskFlagsAll = BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS |
                                    BSM_MASK_PREFIX | BSM_MASK_TABLE;
 
@@ -158,7 +163,7 @@ bsm_status check_attn_common(int32_t B, int32_t H, int32_t T, int32_t D, const b
                              const bsm_score_mod *mod) {
     if (B < 1 || H < 1) return fail(BSM_E_INVALID, "B=%d and H=%d must be >= 1", B, H);
     if (bad_len(T)) return fail(BSM_E_INVALID, "T %d must be in [1, %d]", T, kMaxT);
-    if (D != 64 && D != 128) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64 and 128 are built", D);
+    if (!built_head_dim(D)) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64, 128 and 256 are built", D);
     bsm_status st = check_spec(spec);
     if (st != BSM_OK) return st;
     if (spec->seq_len != T) return fail(BSM_E_INVALID, "mask seq_len %d != T %d", spec->seq_len, T);
@@ -180,8 +185,11 @@ bsm_status check_same_dtype(std::initializer_list<const bsm_tensor *> ts) {
 using AttnLauncher = hipError_t (*)(const bsm::AttnParams &, hipStream_t);
 
 AttnLauncher fwd_launcher(int D, int32_t dtype) {
-    if (dtype == BSM_DTYPE_F16) return D == 64 ? bsm::launch_attn_fwd_d64_f16 : bsm::launch_attn_fwd_d128_f16;
-    return D == 64 ? bsm::launch_attn_fwd_d64_bf16 : bsm::launch_attn_fwd_d128_bf16;
+    if (dtype == BSM_DTYPE_F16)
+        return D == 64 ? bsm::launch_attn_fwd_d64_f16 : D == 256 ? bsm::launch_attn_fwd_d256_f16
+                                                               : bsm::launch_attn_fwd_d128_f16;
+    return D == 64 ? bsm::launch_attn_fwd_d64_bf16 : D == 256 ? bsm::launch_attn_fwd_d256_bf16
+                                                            : bsm::launch_attn_fwd_d128_bf16;
 }
 
 AttnLauncher bwd_launcher(int D, int32_t dtype) {
@@ -269,7 +277,7 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     if (B < 1 || H < 1) return fail(BSM_E_INVALID, "B=%d and H=%d must be >= 1", B, H);
     if (capacity < 1 || capacity > kMaxT)
         return fail(BSM_E_INVALID, "capacity %d must be in [1, %d]", capacity, kMaxT);
-    if (D != 64 && D != 128) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64 and 128 are built", D);
+    if (!built_head_dim(D)) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64, 128 and 256 are built", D);
     if (!spec) return fail(BSM_E_INVALID, "mask spec is NULL");
     if (spec->seq_len != capacity)
         return fail(BSM_E_INVALID, "mask seq_len %d != cache capacity %d", spec->seq_len, capacity);
@@ -481,7 +489,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
 }
 
 size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D) {
-    if (B < 1 || H < 1 || bad_len(Q) || (D != 64 && D != 128)) return 0;
+    if (B < 1 || H < 1 || bad_len(Q) || !bwd_head_dim(D)) return 0;
     return 2 * align256((size_t)B * H * Q * sizeof(float)) +
            align256((size_t)B * H * ((Q + bsm::kTile - 1) / bsm::kTile) * sizeof(float));
 }
@@ -506,6 +514,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                                   void *workspace, size_t workspace_bytes, void *stream) {
     bsm_status st = check_attn_common(B, H, T, D, spec, mod);
     if (st != BSM_OK) return st;
+    if (!bwd_head_dim(D)) return fail(BSM_E_UNSUPPORTED, "head dim %d: the backward is built for 64 and 128", D);
     if ((st = check_block_mask(bm, true, spec)) != BSM_OK) return st;
     if ((st = check_tensor(q, "q")) != BSM_OK) return st;
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;
@@ -555,7 +564,7 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
 }
 
 size_t bsm_decode_workspace_bytes(int32_t B, int32_t H, int32_t capacity, int32_t D) {
-    if (B < 1 || H < 1 || capacity < 1 || capacity > kMaxT || (D != 64 && D != 128)) return 0;
+    if (B < 1 || H < 1 || capacity < 1 || capacity > kMaxT || !built_head_dim(D)) return 0;
     return decode_part_bytes(B, H, capacity, D);
 }
 

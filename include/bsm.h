@@ -258,12 +258,13 @@ bsm_status bsm_build_block_mask(const bsm_mask_spec *spec, const bsm_block_mask 
  *   lse[b,h,i]   = log sum_{kv visible} exp(s[kv])   (natural log; -inf and
  *                  out = 0 for a query with no visible key)
  * q, out: [B, H, Q_LEN, D]; k, v: [B, H, KV_LEN, D] (T = KV_LEN =
- * spec->seq_len, Q_LEN from spec->q_len).  D in {64, 128}.  scale <= 0
+ * spec->seq_len, Q_LEN from spec->q_len).  D in {64, 128, 256} (that
+ * tutorial's sharp edges: head dims that are multiples of 64).  scale <= 0
  * selects 1/sqrt(D).  mod may be NULL.  ALiBi uses absolute positions.
  * bm must be the block mask of `spec` (as built by bsm_build_block_mask);
  * the mask batch index is b when spec->mask_b == B, else 0.
  * lse: device float32 [B, H, Q_LEN], contiguous.
- * Errors: BSM_E_INVALID, BSM_E_UNSUPPORTED (D not 64/128), BSM_E_HIP. */
+ * Errors: BSM_E_INVALID, BSM_E_UNSUPPORTED (D not 64/128/256), BSM_E_HIP. */
 bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *q, const bsm_tensor *k,
                                   const bsm_tensor *v, const bsm_block_mask *bm,
@@ -298,7 +299,8 @@ size_t bsm_bwd_workspace_bytes_mod(int32_t B, int32_t H, int32_t Q, int32_t D, c
  * deterministic as well.  With BIAS the kernels form these sums whether or
  * not bias_grad is given.
  * workspace: device, >= bsm_bwd_workspace_bytes_mod(B, H, Q_LEN, D, mod),
- * 256-byte aligned.  Errors: as the forward, plus BSM_E_WORKSPACE. */
+ * 256-byte aligned.  D in {64, 128}.  Errors: as the forward, plus
+ * BSM_E_WORKSPACE. */
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *q, const bsm_tensor *k,
                                   const bsm_tensor *v, const bsm_tensor *out,

@@ -120,7 +120,7 @@ def _fwd(B=1, H=1, T=1024, D=64, spec=None, mod=None, q=None, k=None, v=None, o=
 
 @pytest.mark.parametrize("kw,code", [
     (dict(D=96), _lib.BSM_E_UNSUPPORTED),
-    (dict(D=256), _lib.BSM_E_UNSUPPORTED),
+    (dict(D=192), _lib.BSM_E_UNSUPPORTED),
     (dict(T=0), _lib.BSM_E_INVALID),
     (dict(T=2048), _lib.BSM_E_INVALID),            # != spec seq_len
     (dict(B=0), _lib.BSM_E_INVALID),
