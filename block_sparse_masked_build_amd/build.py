@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(HERE, "libbsm.so")
 # head dimension, so that the pieces build in parallel
 ELEM_FLAGS = {"bf16": [], "f16": ["-DBSM_ELEM_FP16"]}
 # (longest first)
-HEAD_DIMS = {"fwd": (128, 64, 256), "bwd": (128, 64)}
+HEAD_DIMS = {"fwd": (256, 128, 64), "bwd": (128, 256, 64)}
 SOURCES = ([(f"attn_{p}.hip", f"attn_{p}_d{d}_{e}.o", [f"-DBSM_HEAD_DIM={d}", *ef])
             for p in ("fwd", "bwd") for d in HEAD_DIMS[p] for e, ef in ELEM_FLAGS.items()] +
            [("attn_decode.hip", f"attn_decode_{e}.o", ef) for e, ef in ELEM_FLAGS.items()] +

@@ -890,6 +890,347 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void dkdv_bias_kernel(
     dkdv_body<D, false, SOFTCAP, TABLE, true, true>(p, sm, lds_addr(btab));
 }
 
+// ---------------------------------------------------------------- dK, dV at D = 256
+//
+// At D = 256 the 32-key layout of dkdv_kernel would need about 900 registers
+// (dK, dV and the K/V operands alone take 640) and 256 KB of LDS for its
+// 128-query double buffers.  dkdv256_kernel instead gives each of four waves
+// 16 keys (a workgroup takes half a 128-key tile, 64 keys, and reads that
+// tile's column lists) and works in v_mfma_f32_16x16x32 blocks:
+//  * S = Q K^T and dP = dO V^T per 16 queries x the wave's 16 keys, with the
+//    K and V rows as B operands (lane = key l%16); lane l gets queries
+//    4 (l/16) + 0..3 of the block in its four result registers;
+//  * two such blocks give the eight query values a lane feeds as the B
+//    operand (k slots) of dV^T += dO^T P and dK^T += Q^T dS over 32
+//    queries: queries 4G..4G+3 and 16+4G..16+4G+3 for lane group
+//    G = l/16, the order the transposing reads of dO and Q produce;
+//  * each listed 128-query tile is taken in two 64-query steps through
+//    double-buffered LDS (128 KB): one workgroup per CU, one wave per SIMD,
+//    about 300 registers.
+// 16x16x32 operand layout (wave64): A row i, k-slot kk in lane i + 16 (kk/8),
+// element kk%8; B column j, k-slot kk in lane j + 16 (kk/8); D row i, column
+// j in lane j + 16 (i/4), register i%4.
+constexpr int kQStep = 64;  // queries per pipeline step
+
+__device__ inline f32x4 mfma16(const elem8 &a, const elem8 &b, const f32x4 &c) {
+#ifdef BSM_ELEM_FP16
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+#else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+#endif
+}
+
+// Per-lane LDS byte offsets of the 16x16x32 operands of an fkv tile (fkv
+// swizzles the 16-byte chunk index by the row's low four bits):
+//   row: A operand [16 rows][32 columns]: row 16 rb + l%16, columns
+//        32 st + 8 (l/16) .. +7, logical chunk (l/16) + 4 st; the XOR with
+//        fkv commutes with the 4 st bits: rb 16 rows + (row ^ (st << 6));
+//   tr:  A operand [16 columns][32 rows] of the tile transposed, columns
+//        16 db + l%16, rows 4G..4G+3 (+16: 16+4G..) of a 32-row block with
+//        ds_read_tr16_b64: lane j of a 16-lane group G addresses row
+//        4G + j/4, columns 16 db + 4 (j%4) .. +3, i.e. logical chunk
+//        2 db + (j%4)/2, half j%2; the db part is an XOR of bits 5 and up.
+struct Kv16Offsets {
+    int row;
+    int tr;
+};
+
+template <int D>
+__device__ inline void kv16_offsets(Kv16Offsets &off) {
+    using L = TileLayout<D>;
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    off.row = r * L::kRowBytes + ((g ^ L::fkv(r)) << 4);
+    const int tr_r = 4 * g + (r >> 2);
+    off.tr = tr_r * L::kRowBytes + ((((r & 3) >> 1) ^ L::fkv(tr_r)) << 4) + ((r & 1) << 3);
+}
+
+__device__ inline Kv16Offsets step_offsets16(const Kv16Offsets &off, uint32_t base) {
+    Kv16Offsets o;
+    o.row = off.row + (int)base;
+    o.tr = off.tr + (int)base;
+    asm volatile("" : "+v"(o.row), "+v"(o.tr));
+    return o;
+}
+
+template <int D>
+__device__ inline elem8 read_rows16(const Kv16Offsets &off, int rb, int st) {
+    return lds_load<elem8>((uint32_t)(rb * 16 * TileLayout<D>::kRowBytes + (off.row ^ (st << 6))));
+}
+
+template <int D>
+__device__ inline elem8 read_cols16(const Kv16Offsets &off, int qb, int db) {
+    constexpr int kRB = TileLayout<D>::kRowBytes;
+    const uint32_t a = (uint32_t)(qb * 32 * kRB + (off.tr ^ (db << 5)));
+    const i16x4 lo = ds_read_tr16_at(a);
+    const i16x4 hi = ds_read_tr16_at(a + 16 * kRB);
+    return __builtin_bit_cast(elem8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// p and dS / scale of 16-query block b16 of the step (queries
+// q0 + 16 b16 + 4 G + e in register e): as dkdv_grads, for four registers.
+template <bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
+__device__ inline void dkdv16_grads(const DkdvArgs &a, const ColMask &cm, uint32_t sl2, uint32_t sdl,
+                                    uint32_t sdoc, int b16, int q0, const f32x4 &s, const f32x4 &dp,
+                                    float (&pv_out)[4], float (&ds_out)[4]) {
+    constexpr bool kMods = ALIBI || SOFTCAP;
+    const int G = (threadIdx.x & 63) >> 4;
+    const int qbase = q0 + b16 * 16 + 4 * G;
+    int lo_t = cm.hi >= cm.lo ? cm.lo - qbase : 1 << 30;  // empty interval: no offset matches
+    const int span = cm.hi >= cm.lo ? cm.hi - cm.lo : 0;
+    float ns = -a.mk.slope_f;
+    float n = ALIBI ? ns * (float)(qbase + a.q_off - a.kpos) : 0.0f;
+    asm volatile("" : "+v"(lo_t), "+v"(n), "+v"(ns));
+    int tc = 0, tw = 0;
+    if (CMODE == kTable && MASKED) {
+        tc = cm.cq0 - qbase;
+        tw = cm.wq1 - qbase;
+        asm volatile("" : "+v"(tc), "+v"(tw));
+    }
+    const bool docs = CMODE == kGather || (CMODE == kTable && a.doc);
+    const int ql4 = b16 * 16 + 4 * G;
+    const f32x4 L = lds_load<f32x4>(sl2 + 4 * ql4);
+    const f32x4 Dl = lds_load<f32x4>(sdl + 4 * ql4);
+    i32x4 dq4 = {0, 0, 0, 0};
+    if (docs && MASKED) dq4 = lds_load<i32x4>(sdoc + 4 * ql4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float pv, tl = 0.0f;
+        if (kMods) {
+            const float bias = ALIBI ? __builtin_fmaf((float)e, ns, n) : 0.0f;
+            tl = mod_apply<ALIBI, SOFTCAP>(s[e], bias, a.mk);
+            pv = fast_exp2(tl - L[e]);
+        } else {
+            pv = fast_exp2(__builtin_fmaf(s[e], a.scale_log2, -L[e]));
+        }
+        if (MASKED) {
+            bool vis = (uint32_t)(e - lo_t) <= (uint32_t)span;
+            const int dqv = e == 0 ? dq4.x : e == 1 ? dq4.y : e == 2 ? dq4.z : dq4.w;
+            if (CMODE == kTable) {
+                const uint32_t idx = (e >= tc ? 1u : 0u) | (docs && dqv == cm.dock ? 2u : 0u) | (e < tw ? 4u : 0u);
+                vis = vis && ((cm.table >> idx) & 1u);
+            } else if (CMODE == kGather) {
+                vis = vis && dqv == cm.dock;
+            }
+            pv = vis ? pv : 0.0f;
+        }
+        float ds = pv * (dp[e] - Dl[e]);
+        if (SOFTCAP) ds *= softcap_grad(tl, a.inv_cap);
+        pv_out[e] = pv;
+        ds_out[e] = ds;
+    }
+}
+
+// One 64-query step against the wave's 16 keys, in two 32-query blocks.
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool MASKED>
+__device__ inline void dkdv16_step(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 32],
+                                   const elem8 (&vf)[D / 32], const Kv16Offsets &oq, const Kv16Offsets &og,
+                                   uint32_t sl2, uint32_t sdl, uint32_t sdoc, int q0, f32x4 (&dk)[D / 16],
+                                   f32x4 (&dv)[D / 16]) {
+#pragma unroll
+    for (int qb = 0; qb < kQStep / 32; ++qb) {
+        float pv[2][4], dsv[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int b16 = qb * 2 + h;
+            f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f}, dp = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < D / 32; ++st) {
+                s = mfma16(read_rows16<D>(oq, b16, st), kf[st], s);
+                dp = mfma16(read_rows16<D>(og, b16, st), vf[st], dp);
+            }
+            dkdv16_grads<ALIBI, SOFTCAP, CMODE, MASKED>(a, cm, sl2, sdl, sdoc, b16, q0, s, dp, pv[h], dsv[h]);
+        }
+        elem8 pb, dsb;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            pb[e] = static_cast<elem_t>(pv[0][e]);
+            pb[4 + e] = static_cast<elem_t>(pv[1][e]);
+            dsb[e] = static_cast<elem_t>(dsv[0][e]);
+            dsb[4 + e] = static_cast<elem_t>(dsv[1][e]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            dv[db] = mfma16(read_cols16<D>(og, qb, db), pb, dv[db]);
+            dk[db] = mfma16(read_cols16<D>(oq, qb, db), dsb, dk[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep each block's reads and products in their own window
+    }
+}
+
+// LDS of dkdv256_kernel: double-buffered 64-query halves of the listed query
+// tiles (queries and output gradients) and their L, Delta and document ids.
+template <int D>
+struct Dkdv16Smem {
+    elem_t q[2][kQStep * D];  // fkv swizzle
+    elem_t g[2][kQStep * D];
+    float l2[2][kQStep];
+    float delta[2][kQStep];
+    int32_t doc[2][kQStep];
+};
+
+// The step loop: two 64-query steps per listed 128-query tile (full tiles
+// first), copies issued one step ahead, one barrier per step.
+template <int D, bool ALIBI, bool SOFTCAP, int CMODE, bool GENERAL>
+__device__ inline void dkdv16_main(const DkdvArgs &a, const ColMask &cm, const elem8 (&kf)[D / 32],
+                                   const elem8 (&vf)[D / 32], const Kv16Offsets &off, Dkdv16Smem<D> &sm,
+                                   int ntiles, f32x4 (&dk)[D / 16], f32x4 (&dv)[D / 16]) {
+    constexpr uint32_t kTB = kQStep * D * 2, kWB = kQStep * 4;
+    static_assert(kTB % 256 == 0, "buffer stride commutes with the swizzle");
+    const uint32_t lq = lds_addr(&sm.q[0][0]), lg = lds_addr(&sm.g[0][0]);
+    const uint32_t ll2 = lds_addr(&sm.l2[0][0]), ldl = lds_addr(&sm.delta[0][0]), ldoc = lds_addr(&sm.doc[0][0]);
+    auto step_q0 = [&](int t) {
+        const int it = t >> 1;
+        return clamp_tile(it < a.nfull ? load_uniform(a.fidx + it) : load_uniform(a.pidx + it - a.nfull), a.nt) *
+                   kTile + (t & 1) * kQStep;
+    };
+    auto issue = [&](int t, int q0) {
+        // rows past Q_LEN repeat the last query's
+        const uint32_t bf = t & 1;
+        const int nq = GENERAL ? a.q_len - q0 : kQStep;
+        issue_ints_to_lds_at<kQStep>(ll2 + bf * kWB, reinterpret_cast<const int32_t *>(a.l2 + q0), nq);
+        issue_ints_to_lds_at<kQStep>(ldl + bf * kWB, reinterpret_cast<const int32_t *>(a.delta + q0), nq);
+        if (CMODE == kGather || (CMODE == kTable && a.doc))
+            issue_ints_to_lds_at<kQStep>(ldoc + bf * kWB, a.doc + q0, nq);
+        issue_tile_to_lds_at<D, kSwzKV, kQStep>(lq + bf * kTB, a.qb + (int64_t)q0 * a.q_st, a.q_st, nq);
+        issue_tile_to_lds_at<D, kSwzKV, kQStep>(lg + bf * kTB, a.gb + (int64_t)q0 * a.do_st, a.do_st, nq);
+    };
+    const int nsteps = 2 * ntiles;
+    if (nsteps <= 0) return;
+    int q0 = step_q0(0);
+    issue(0, q0);
+    auto step = [&](int t, auto masked) {
+        wait_vmcnt<0>();
+        tile_barrier();  // step t is visible; every wave is done with step t-1's buffers
+        int q_next = 0;
+        if (t + 1 < nsteps) {
+            q_next = step_q0(t + 1);
+            issue(t + 1, q_next);
+        }
+        const uint32_t bf = t & 1;
+        const Kv16Offsets oq = step_offsets16(off, lq + bf * kTB), og = step_offsets16(off, lg + bf * kTB);
+        dkdv16_step<D, ALIBI, SOFTCAP, CMODE, decltype(masked)::value>(
+            a, cm, kf, vf, oq, og, ll2 + bf * kWB, ldl + bf * kWB, ldoc + bf * kWB, q0, dk, dv);
+        wait_lds_reads();  // this wave's reads of step t are done before the next barrier
+        q0 = q_next;
+    };
+#pragma unroll 1
+    for (int t = 0; t < 2 * a.nfull; ++t) step(t, std::false_type());
+#pragma unroll 1
+    for (int t = 2 * a.nfull; t < nsteps; ++t) step(t, std::true_type());
+}
+
+// dK (times mul) or dV rows of the wave's 16 keys from the 16x16 blocks
+// (lane: key l%16, d = 16 db + 4 (l/16) + 0..3 in block db), staged through
+// the wave's slice of LDS at `stage` (16-byte chunks XOR-swizzled by the
+// row) and stored as whole rows; rows below nrows are stored.
+template <int D>
+__device__ inline void store16_staged(elem_t *dst, int64_t ld, const f32x4 (&acc)[D / 16], float mul,
+                                      uint32_t stage, int nrows) {
+    constexpr int kRowBytes = 2 * D, kChunks = kRowBytes / 16, kPerLane = 16 * kChunks / 64;
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        u32x2 w;  // columns 16 db + 4 g + 0..3: chunk 2 db + g/2, half g%2
+        w.x = pack_elem2(acc[db][0] * mul, acc[db][1] * mul);
+        w.y = pack_elem2(acc[db][2] * mul, acc[db][3] * mul);
+        lds_store<u32x2>(stage + r * kRowBytes + (((2 * db + (g >> 1)) ^ r) * 16) + (g & 1) * 8, w);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+        const int row = lane >> 2, c = kPerLane * (lane & 3) + i;  // 16 rows, kPerLane chunks per lane
+        const u32x4 v = lds_load<u32x4>(stage + row * kRowBytes + ((c ^ row) * 16));
+        if (row < nrows) *reinterpret_cast<u32x4 *>(dst + (int64_t)row * ld + c * 8) = v;
+    }
+}
+
+template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL>
+__global__ __launch_bounds__(kThreads, 1) void dkdv256_kernel(AttnParams p) {
+    static_assert(D == 256, "the 16-key layout serves D = 256");
+    __shared__ __attribute__((aligned(1024))) Dkdv16Smem<D> sm;
+    const int nt = p.nt;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = wg / (2 * nt);
+    const int jh = wg % (2 * nt);  // early key tiles first
+    const int j = jh >> 1, half = jh & 1;
+    const int b = bh / p.H, h = bh % p.H;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int kidx = j * kTile + half * kQStep + wv * 16 + n;  // key (past KV_LEN on a cut-short tile)
+    const int kpos = min(kidx, p.T - 1);                         // the key this lane loads
+
+    const elem_t *kb = static_cast<const elem_t *>(p.k) + b * p.k_sb + h * p.k_sh;
+    const elem_t *vb = static_cast<const elem_t *>(p.v) + b * p.v_sb + h * p.v_sh;
+    const int bm = p.mask_b == 1 ? 0 : b;
+    const int64_t col = (int64_t)bm * nt + j;
+
+    DkdvArgs a;
+    a.qb = static_cast<const elem_t *>(p.q) + b * p.q_sb + h * p.q_sh;
+    a.gb = static_cast<const elem_t *>(p.dout) + b * p.do_sb + h * p.do_sh;
+    a.q_st = p.q_st;
+    a.do_st = p.do_st;
+    a.l2 = p.lse2 + ((int64_t)b * p.H + h) * p.q_len;
+    a.delta = p.delta + ((int64_t)b * p.H + h) * p.q_len;
+    a.nfull = min(max(load_uniform(p.full_q_num + col), 0), p.nqt);
+    const int npart = min(max(load_uniform(p.q_num + col), 0), p.nqt);
+    a.fidx = p.full_q_idx + col * p.nqt;
+    a.pidx = p.q_idx + col * p.nqt;
+    a.doc = (p.mask_flags & BSM_MASK_DOCUMENT) ? p.doc_ids + (int64_t)bm * p.npos + p.q_off : nullptr;
+    a.nt = p.nqt;
+    a.kpos = kpos;
+    a.q_len = p.q_len;
+    a.q_off = p.q_off;
+    a.scale = p.scale;
+    a.scale_log2 = p.scale * kLog2e;
+    a.slope = ALIBI ? p.alibi_slopes[h] : 0.0f;
+    a.cap = SOFTCAP ? p.softcap : 1.0f;
+    a.inv_cap = 1.0f / a.cap;
+    a.mk = mod_k<SOFTCAP>(a.scale, a.slope, a.cap);
+    const int ntiles = a.nfull + npart;
+
+    ColMask cm;
+    bool gather = false;
+    if (TABLE)
+        make_col_table(p, bm, kpos, (p.mask_flags & BSM_MASK_WINDOW) ? load_uniform(p.window) : 0, cm);
+    else
+        gather = make_col_mask(p, bm, kpos, cm);
+    Kv16Offsets off;
+    kv16_offsets<D>(off);
+
+    // K and V rows of the lane's key as B operands: d = 32 st + 8 g .. +7
+    elem8 kf[D / 32], vf[D / 32];
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+        kf[st] = *reinterpret_cast<const elem8 *>(kb + (int64_t)kpos * p.k_st + st * 32 + g * 8);
+        vf[st] = *reinterpret_cast<const elem8 *>(vb + (int64_t)kpos * p.v_st + st * 32 + g * 8);
+    }
+    f32x4 dk[D / 16], dv[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+        dk[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        dv[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // No wait here: the first copies are issued while the key rows load.
+    if (TABLE)
+        dkdv16_main<D, ALIBI, SOFTCAP, kTable, GENERAL>(a, cm, kf, vf, off, sm, ntiles, dk, dv);
+    else if (gather)
+        dkdv16_main<D, ALIBI, SOFTCAP, kGather, GENERAL>(a, cm, kf, vf, off, sm, ntiles, dk, dv);
+    else
+        dkdv16_main<D, ALIBI, SOFTCAP, kPlain, GENERAL>(a, cm, kf, vf, off, sm, ntiles, dk, dv);
+
+    // dK and dV rows of the wave (8 KB each per wave), staged through the
+    // query and output-gradient buffers once every wave is done with them.
+    static_assert(sizeof(sm.q) >= (kThreads / 64) * 16 * 2 * D, "dK staging fits the query buffers");
+    static_assert(sizeof(sm.g) >= (kThreads / 64) * 16 * 2 * D, "dV staging fits the gradient buffers");
+    tile_barrier();
+    const uint32_t slice = (uint32_t)(wv * 16 * 2 * D);
+    const int k0w = kidx - n;  // the wave's first key
+    elem_t *dkp = static_cast<elem_t *>(p.dk) + b * p.dk_sb + h * p.dk_sh + (int64_t)k0w * p.dk_st;
+    elem_t *dvp = static_cast<elem_t *>(p.dv) + b * p.dv_sb + h * p.dv_sh + (int64_t)k0w * p.dv_st;
+    store16_staged<D>(dkp, p.dk_st, dk, p.scale, lds_addr(&sm.q[0][0]) + slice, p.T - k0w);
+    store16_staged<D>(dvp, p.dv_st, dv, 1.0f, lds_addr(&sm.g[0][0]) + slice, p.T - k0w);
+}
+
 // dL/dbias: the per-(batch, head, query tile) partial rows of the BIAS
 // dq_kernel summed over the batch and the query tiles in a fixed order: a
 // workgroup takes 32 entries of one head, its 8 row groups sum the rows
@@ -967,10 +1308,18 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
         else
             hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, TABLE, false>), dq_grid, block, 0, stream, q);
     }
-    if (q_r)
-        hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, true>), dkdv_grid, block, 0, stream, q);
-    else
-        hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, TABLE>), dkdv_grid, block, 0, stream, q);
+    if constexpr (D == 256) {  // 16 keys per wave, half a key tile per workgroup
+        const dim3 grid256(2 * p.B * p.H * p.nt);
+        if (q_r)
+            hipLaunchKernelGGL((dkdv256_kernel<D, ALIBI, SOFTCAP, TABLE, true>), grid256, block, 0, stream, q);
+        else
+            hipLaunchKernelGGL((dkdv256_kernel<D, ALIBI, SOFTCAP, TABLE, TABLE>), grid256, block, 0, stream, q);
+    } else {
+        if (q_r)
+            hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, true>), dkdv_grid, block, 0, stream, q);
+        else
+            hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, TABLE>), dkdv_grid, block, 0, stream, q);
+    }
 }
 
 // With a bias table: the bias kernels (general path), then the reduction of
@@ -993,10 +1342,12 @@ void launch_mods(const AttnParams &p, hipStream_t stream) {
     const bool alibi = p.mod_flags & BSM_MOD_ALIBI;
     const bool cap = p.mod_flags & BSM_MOD_SOFTCAP;
     if (p.mod_flags & BSM_MOD_BIAS) {
-        if (cap)
-            launch_bias<D, true, TABLE>(p, stream);
-        else
-            launch_bias<D, false, TABLE>(p, stream);
+        if constexpr (D != 256) {  // the host rejects a bias table at D = 256
+            if (cap)
+                launch_bias<D, true, TABLE>(p, stream);
+            else
+                launch_bias<D, false, TABLE>(p, stream);
+        }
         return;
     }
     if (alibi && cap)
@@ -1027,6 +1378,9 @@ hipError_t BSM_ELEM_FN(launch_attn_bwd_d64)(const AttnParams &p, hipStream_t str
 #endif
 #if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 128
 hipError_t BSM_ELEM_FN(launch_attn_bwd_d128)(const AttnParams &p, hipStream_t stream) { return launch_d<128>(p, stream); }
+#endif
+#if !defined(BSM_HEAD_DIM) || BSM_HEAD_DIM == 256
+hipError_t BSM_ELEM_FN(launch_attn_bwd_d256)(const AttnParams &p, hipStream_t stream) { return launch_d<256>(p, stream); }
 #endif
 
 }  // namespace bsm

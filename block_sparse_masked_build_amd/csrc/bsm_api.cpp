@@ -31,10 +31,8 @@ bsm_status ok() {
 
 constexpr int32_t kMaxT = 1 << 22;
 
-// Head dimensions the forward and decoding kernels are built for (the
-// backward: 64 and 128, see bwd_head_dim).
+// Head dimensions the kernels are built for.
 bool built_head_dim(int32_t D) { return D == 64 || D == 128 || D == 256; }
-bool bwd_head_dim(int32_t D) { return D == 64 || D == 128; }
 constexpr uint32_t kMaskFlagsAll = BSM_MASK_CAUSAL | BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_SINKS |
                                    BSM_MASK_PREFIX | BSM_MASK_TABLE;
 
@@ -193,8 +191,11 @@ AttnLauncher fwd_launcher(int D, int32_t dtype) {
 }
 
 AttnLauncher bwd_launcher(int D, int32_t dtype) {
-    if (dtype == BSM_DTYPE_F16) return D == 64 ? bsm::launch_attn_bwd_d64_f16 : bsm::launch_attn_bwd_d128_f16;
-    return D == 64 ? bsm::launch_attn_bwd_d64_bf16 : bsm::launch_attn_bwd_d128_bf16;
+    if (dtype == BSM_DTYPE_F16)
+        return D == 64 ? bsm::launch_attn_bwd_d64_f16 : D == 256 ? bsm::launch_attn_bwd_d256_f16
+                                                               : bsm::launch_attn_bwd_d128_f16;
+    return D == 64 ? bsm::launch_attn_bwd_d64_bf16 : D == 256 ? bsm::launch_attn_bwd_d256_bf16
+                                                            : bsm::launch_attn_bwd_d128_bf16;
 }
 
 hipError_t launch_decode(const bsm::DecodeLaunch &d, float *part, hipStream_t stream) {
@@ -489,7 +490,7 @@ bsm_status bsm_flex_attention_fwd(int32_t B, int32_t H, int32_t T, int32_t D, co
 }
 
 size_t bsm_bwd_workspace_bytes(int32_t B, int32_t H, int32_t Q, int32_t D) {
-    if (B < 1 || H < 1 || bad_len(Q) || !bwd_head_dim(D)) return 0;
+    if (B < 1 || H < 1 || bad_len(Q) || !built_head_dim(D)) return 0;
     return 2 * align256((size_t)B * H * Q * sizeof(float)) +
            align256((size_t)B * H * ((Q + bsm::kTile - 1) / bsm::kTile) * sizeof(float));
 }
@@ -514,7 +515,8 @@ bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D, co
                                   void *workspace, size_t workspace_bytes, void *stream) {
     bsm_status st = check_attn_common(B, H, T, D, spec, mod);
     if (st != BSM_OK) return st;
-    if (!bwd_head_dim(D)) return fail(BSM_E_UNSUPPORTED, "head dim %d: the backward is built for 64 and 128", D);
+    if (D == 256 && mod && (mod->flags & BSM_MOD_BIAS))
+        return fail(BSM_E_UNSUPPORTED, "a bias table's backward is built for head dims 64 and 128");
     if ((st = check_block_mask(bm, true, spec)) != BSM_OK) return st;
     if ((st = check_tensor(q, "q")) != BSM_OK) return st;
     if ((st = check_tensor(k, "k")) != BSM_OK) return st;

@@ -102,6 +102,8 @@ hipError_t launch_attn_fwd_d64_f16(const AttnParams &p, hipStream_t stream);
 hipError_t launch_attn_fwd_d128_f16(const AttnParams &p, hipStream_t stream);
 hipError_t launch_attn_fwd_d256_bf16(const AttnParams &p, hipStream_t stream);
 hipError_t launch_attn_fwd_d256_f16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d256_bf16(const AttnParams &p, hipStream_t stream);
+hipError_t launch_attn_bwd_d256_f16(const AttnParams &p, hipStream_t stream);
 hipError_t launch_attn_bwd_d64_f16(const AttnParams &p, hipStream_t stream);
 hipError_t launch_attn_bwd_d128_f16(const AttnParams &p, hipStream_t stream);
 // Decoding step: one query per (b, h) at the last live position of a cache

@@ -299,8 +299,8 @@ size_t bsm_bwd_workspace_bytes_mod(int32_t B, int32_t H, int32_t Q, int32_t D, c
  * deterministic as well.  With BIAS the kernels form these sums whether or
  * not bias_grad is given.
  * workspace: device, >= bsm_bwd_workspace_bytes_mod(B, H, Q_LEN, D, mod),
- * 256-byte aligned.  D in {64, 128}.  Errors: as the forward, plus
- * BSM_E_WORKSPACE. */
+ * 256-byte aligned.  With BIAS, D in {64, 128} (BSM_E_UNSUPPORTED at 256).
+ * Errors: as the forward, plus BSM_E_WORKSPACE. */
 bsm_status bsm_flex_attention_bwd(int32_t B, int32_t H, int32_t T, int32_t D,
                                   const bsm_tensor *q, const bsm_tensor *k,
                                   const bsm_tensor *v, const bsm_tensor *out,

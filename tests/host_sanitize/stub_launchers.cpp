@@ -33,6 +33,8 @@ hipError_t launch_attn_fwd_d64_f16(const AttnParams &p, hipStream_t) { return re
 hipError_t launch_attn_fwd_d128_f16(const AttnParams &p, hipStream_t) { return record(p); }
 hipError_t launch_attn_fwd_d256_bf16(const AttnParams &p, hipStream_t) { return record(p); }
 hipError_t launch_attn_fwd_d256_f16(const AttnParams &p, hipStream_t) { return record(p); }
+hipError_t launch_attn_bwd_d256_bf16(const AttnParams &p, hipStream_t) { return record(p); }
+hipError_t launch_attn_bwd_d256_f16(const AttnParams &p, hipStream_t) { return record(p); }
 hipError_t launch_attn_bwd_d64_f16(const AttnParams &p, hipStream_t) { return record(p); }
 hipError_t launch_attn_bwd_d128_f16(const AttnParams &p, hipStream_t) { return record(p); }
 

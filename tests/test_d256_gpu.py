@@ -8,8 +8,9 @@ against the fp64 oracle, which takes any D.
     operand bound of parity_utils, lse within 1e-3;
   * the decoding step at several live lengths, with and without a block
     mask;
-  * the backward is built for D = 64 and 128: at D = 256 it returns
-    BSM_E_UNSUPPORTED before anything is enqueued.
+  * the backward (dkdv256_kernel for dK/dV) on the same random shapes and
+    a 2K document + window mask, bit-identical over two calls; a bias
+    table's backward returns BSM_E_UNSUPPORTED at D = 256.
 Inputs: N(0, 1) draws rounded to the tensor type, seeded per case."""
 import dataclasses
 
@@ -149,7 +150,64 @@ def test_d256_decode(listed):
                 assert_lse_close(lse[b, h:h + 1].double().numpy(), rl, f"decode b{b} h{h} L{L}")
 
 
-def test_d256_backward_is_unsupported():
+@pytest.mark.parametrize("it", range(16))
+def test_d256_backward(it):
+    """dQ, dK and dV at D = 256 (dkdv256_kernel: 16 keys per wave in
+    16x16x32 blocks, 64-query steps) on the forward cases' shapes and masks
+    (no bias table: its backward is built for D = 64 and 128)."""
+    from block_sparse_masked_build_amd import api
+    B, H, Q, T, spec, mod, tensors, fmt = _case(100 + it)
+    mod = dataclasses.replace(mod, bias_table=None)
+    ctx = (f"[d256 bwd {it}] B{B} H{H} Q{Q} KV{T} off{spec.q_offset} {fmt} causal={spec.causal} "
+           f"docs={spec.document} window={spec.window} sinks={spec.sinks} table={spec.table} "
+           f"kv_block={spec.kv_block} alibi={mod.alibi_slopes is not None} cap={mod.softcap}")
+    log(ctx)
+    g = torch.Generator("cpu").manual_seed(17900 + it)
+    rand = random_f16 if fmt == "f16" else random_bf16
+    tensors["dout"] = rand((B, H, Q, D), g)
+    s = api.from_spec_data(spec)
+    bm = api.build_block_mask(s)
+    m = _mod(api, mod)
+    q, k, v, do = (tensors[n].cuda() for n in ("q", "k", "v", "dout"))
+    out, lse = api.flex_attention_fwd(q, k, v, bm, s, m)
+    dq, dk, dv = api.flex_attention_bwd(q, k, v, out, lse, do, bm, s, m)
+    torch.cuda.synchronize()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    for b in range(B):
+        for h in range(H):
+            Qm, K, V, dO = (per_head_f64(tensors[n], b, h) for n in ("q", "k", "v", "dout"))
+            rq, rk, rv, mq, mk, mv = oracle.backward_dense(Qm, K, V, dO, spec, mod, b, h, with_mass=True)
+            for name, x, ref, mass in (("dq", dq, rq, mq), ("dk", dk, rk, mk), ("dv", dv, rv, mv)):
+                assert_within_bound(f64(x[b, h]), ref, mass, f"{ctx} b{b} h{h} {name}", fmt=fmt)
+
+
+def test_d256_backward_doc_window_2k_deterministic():
+    """Causal + documents + window at T = 2048: parity of every element and
+    two calls bit-identical."""
+    from block_sparse_masked_build_amd import api
+    T, H = 2048, 2
+    rng = np.random.default_rng(17800)
+    docs = np.cumsum(rng.random(T) < 1 / 400).astype(np.int32)[None]
+    spec = MaskSpecData(T, causal=True, document=True, doc_ids=docs, window=700)
+    g = torch.Generator("cpu").manual_seed(17800)
+    tensors = {n: random_bf16((1, H, T, D), g) for n in ("q", "k", "v", "dout")}
+    log("[d256 bwd 2k] causal+docs+window 700")
+    s = api.from_spec_data(spec)
+    bm = api.build_block_mask(s)
+    q, k, v, do = (tensors[n].cuda() for n in ("q", "k", "v", "dout"))
+    out, lse = api.flex_attention_fwd(q, k, v, bm, s)
+    r1 = [x.cpu() for x in api.flex_attention_bwd(q, k, v, out, lse, do, bm, s)]
+    r2 = [x.cpu() for x in api.flex_attention_bwd(q, k, v, out, lse, do, bm, s)]
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    for h in range(H):
+        Qm, K, V, dO = (per_head_f64(tensors[n], 0, h) for n in ("q", "k", "v", "dout"))
+        rq, rk, rv, mq, mk, mv = oracle.backward_dense(Qm, K, V, dO, spec, None, 0, h, with_mass=True)
+        for name, x, ref, mass in (("dq", r1[0], rq, mq), ("dk", r1[1], rk, mk), ("dv", r1[2], rv, mv)):
+            assert_within_bound(f64(x[0, h]), ref, mass, f"2k h{h} {name}")
+
+
+def test_d256_bias_backward_is_unsupported():
     from block_sparse_masked_build_amd import _lib, api
     T, H = 256, 1
     spec = MaskSpecData(T, causal=True)
@@ -157,8 +215,9 @@ def test_d256_backward_is_unsupported():
     q, k, v, do = (random_bf16((1, H, T, D), g).cuda() for _ in range(4))
     s = api.from_spec_data(spec)
     bm = api.build_block_mask(s)
-    out, lse = api.flex_attention_fwd(q, k, v, bm, s)
+    m = api.score_mod(bias=bias_table(H, 16, seed=1))
+    out, lse = api.flex_attention_fwd(q, k, v, bm, s, m)
     with pytest.raises(RuntimeError) as e:
-        api.flex_attention_bwd(q, k, v, out, lse, do, bm, s, workspace=torch.empty(1 << 20, dtype=torch.uint8,
-                                                                                      device="cuda"))
-    assert e.value.status == _lib.BSM_E_UNSUPPORTED and "head dim 256" in str(e.value)
+        api.flex_attention_bwd(q, k, v, out, lse, do, bm, s, m,
+                               workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == _lib.BSM_E_UNSUPPORTED and "bias" in str(e.value)
