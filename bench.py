@@ -67,9 +67,10 @@ def parse():
 
 
 # Workloads of detail.configs ("-block64": 128 x 64 blocks; "-bias": with a
-# relative-position bias table and its gradient; "-f16": fp16 tensors).
-CONFIG_KEYS = ("1", "2", "2-block64", "2-bias", "2-f16", "2-causal", "2-window", "2-chunks", "3", "4a", "4b",
-               "5", "5-block64")
+# relative-position bias table and its gradient; "-f16": fp16 tensors;
+# "-d256": head dimension 256).
+CONFIG_KEYS = ("1", "2", "2-block64", "2-bias", "2-f16", "2-d256", "2-causal", "2-window", "2-chunks", "3", "4a",
+               "4b", "5", "5-block64")
 
 FLUSH_BYTES = 512 << 20
 _flush_buf = None
@@ -315,7 +316,7 @@ def config_detail(api, key, reps):
     each), the work the kernels do there.  A key ending in "-bias" adds a
     relative-position bias table of radius 1024 (N(0, 0.25) entries) and
     runs the backward with its gradient; "-f16" runs the workload on fp16
-    tensors, forward and backward."""
+    tensors, forward and backward; "-d256" at head dimension 256."""
     import dataclasses
     import numpy as np
     import torch
@@ -326,10 +327,15 @@ def config_detail(api, key, reps):
     f16 = key.endswith("-f16")
     if f16:
         key = key[:-len("-f16")]
+    d256 = key.endswith("-d256")
+    if d256:
+        key = key[:-len("-d256")]
     base, _, variant = key.partition("-block")
     w = make_config(base if variant else key)
     if f16:
         w = dataclasses.replace(w, name=w.name + ", fp16", backward=True, dtype="f16")
+    if d256:
+        w = dataclasses.replace(w, name=w.name.replace("D128", "D256"), D=256, backward=True)
     if with_bias:
         w = dataclasses.replace(w, name=w.name + ", bias table R 1024", backward=True,
                                 mod=dataclasses.replace(w.mod, bias_table=bias_table(w.H, 1024, seed=2, sd=0.5)))
