@@ -49,8 +49,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="2",
-                    help="1, 2, 2-causal, 2-window, 2-chunks, 3, 4a, 4b, 5, decode")
+                    help="1, 2, 2-causal, 2-window, 2-chunks, 3, 4a, 4b, 5, decode, decode-docs")
     ap.add_argument("--fwd-only", action="store_true", help="leave the backward out of the step")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="decode workload: read K/V from a shuffled pool of pages of this many keys "
+                         "through a block table (0: one contiguous cache)")
     ap.add_argument("--slopes", action="store_true",
                     help="the backward also returns dL/dslope (workloads with ALiBi)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,9 +214,44 @@ def decode_bench(args, w):
     ws = api.decode_workspace(w.B, w.H, w.T, w.D)
     kvl = torch.tensor([w.T], dtype=torch.int32, device="cuda")  # live length: the whole cache
     import numpy as np
+    page = args.page_size
+    # with documents the step reads the tiles its block-mask row lists: K and
+    # V of those tiles are the algorithmic bytes (every tile is below the
+    # live length, the whole cache)
+    bm = api.build_block_mask(spec) if w.spec.document else None
+    if bm is not None:
+        nt, row = w.T // 128, (w.T - 1) // 128
+        tiles = (bm.kv_num_blocks + bm.full_kv_num_blocks).view(-1, nt)[:, row].cpu().numpy()
+        tiles = np.broadcast_to(tiles, (w.B,)) if tiles.size == 1 else tiles
+        kv_bytes = int(tiles.sum()) * w.H * 128 * w.D * 2 * 2
+    else:
+        kv_bytes = 2 * w.B * w.H * w.T * w.D * 2
 
-    def call():
-        api.flex_attention_decode(q, k, v, spec, None, kv_len=kvl, out=out, lse=lse, workspace=ws)
+    if page:
+        # the same cache as pages of `page` keys in a shuffled pool, one
+        # block-table row per batch element
+        if page % 64 or w.T % page:
+            sys.exit(f"--page-size {page} must be a multiple of 64 that divides {w.T}")
+        nl = w.T // page
+        gen = torch.Generator("cpu").manual_seed(w.seed)
+        table = torch.randperm(w.B * nl, generator=gen).to(torch.int32).view(w.B, nl).cuda()
+
+        def to_pages(x):
+            blocks = x.view(w.B, w.H, nl, page, w.D).permute(0, 2, 1, 3, 4).reshape(w.B * nl, w.H, page, w.D)
+            pool = torch.empty_like(blocks)
+            pool[table.flatten().long()] = blocks
+            return pool
+
+        kp, vp = to_pages(k), to_pages(v)
+        del k, v
+
+        def call():
+            api.flex_attention_decode_paged(q, kp, vp, table, spec, None, kv_len=kvl, block_mask=bm, out=out,
+                                            lse=lse, workspace=ws)
+    else:
+        def call():
+            api.flex_attention_decode(q, k, v, spec, None, kv_len=kvl, block_mask=bm, out=out, lse=lse,
+                                      workspace=ws)
 
     for _ in range(args.warmup):
         call()
@@ -226,16 +264,17 @@ def decode_bench(args, w):
     warm = [timed(call, flush=False) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_us = float(np.median(us(evs)))
-    kv_bytes = 2 * w.B * w.H * w.T * w.D * 2
     gbs = kv_bytes / (t_us * 1e-6) / 1e9
+    what = "the tiles of the query's document" if bm is not None else "whole cache"
     print(json.dumps({
-        "metric": "decode K/V GB/s (one query per batch and head, whole cache)", "value": round(gbs, 1),
+        "metric": f"decode K/V GB/s (one query per batch and head, {what})", "value": round(gbs, 1),
         "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall * 1e3 / args.steps, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D},
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "D": w.D, "page_size": page or None},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": decode_traffic(),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None if page or bm is not None else decode_traffic(),
                      "kernel": "decode_partial_kernel<%d> + decode_combine_kernel" % w.D},
         "detail": {"decode_us_median_cold": t_us, "decode_us_min_cold": float(us(evs).min()),
                    "decode_us_median_warm": float(np.median(us(warm))), "kv_bytes": kv_bytes,
@@ -404,7 +443,7 @@ def main():
         return 1
 
     w = make_config(args.workload)
-    if str(args.workload) == "decode":
+    if str(args.workload) in ("decode", "decode-docs"):
         return decode_bench(args, w)
     backward = w.backward or (str(args.workload) == "2" and not args.fwd_only)
     if args.fwd_only:

@@ -481,6 +481,54 @@ def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = Non
     return out, lse
 
 
+def flex_attention_decode_paged(q, k_pages, v_pages, block_table, spec: MaskSpec,
+                                mod: Optional[ScoreMod] = None, scale: Optional[float] = None, kv_len=None,
+                                block_mask: Optional[BlockMask] = None, out=None, lse=None,
+                                workspace: Optional[torch.Tensor] = None):
+    """The decoding step of flex_attention_decode over a paged cache: k_pages,
+    v_pages [num_pages, H, page_size, D] hold the pages of every sequence and
+    block_table, a device int32 [B, n_logical] tensor, maps logical page j of
+    batch element b to its physical page (key kv sits at row kv % page_size
+    of page block_table[b, kv // page_size]).  The logical capacity is
+    n_logical * page_size: spec, block_mask and kv_len refer to it.
+    page_size is a positive multiple of 64.  Returns (out, lse) as
+    flex_attention_decode, which gives the same bits on the gathered cache."""
+    num_pages, H, page_size, D = k_pages.shape
+    if v_pages.shape != k_pages.shape:
+        raise ValueError(f"v_pages {tuple(v_pages.shape)} must have the shape of k_pages {tuple(k_pages.shape)}")
+    if (block_table.dim() != 2 or block_table.dtype != torch.int32 or not block_table.is_contiguous()
+            or block_table.device != q.device):
+        raise ValueError("block_table must be a contiguous int32 [B, n_logical] tensor on q's device")
+    B, n_logical = block_table.shape
+    capacity = n_logical * page_size
+    if q.shape != (B, H, 1, D):
+        raise ValueError(f"q must be [B, H, 1, D] = {(B, H, 1, D)}, got {tuple(q.shape)}")
+    if spec.T != capacity:
+        raise ValueError(f"mask spec length {spec.T} != logical capacity {capacity}")
+    _check_mod(mod, H)
+    out = torch.empty_like(q) if out is None else out
+    if out.shape != (B, H, 1, D):
+        raise ValueError(f"out must be [B, H, 1, D] = {(B, H, 1, D)}")
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (B, H):
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    kvl, stride = _kv_len_tensor(kv_len, B, capacity, q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, H, capacity, D, q.device)
+    ts = [_tensor(x, n) for x, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (out, "out"))]
+    cs = spec.c_struct()
+    cb = block_mask.c_struct() if block_mask is not None else None
+    cm = mod.c_struct() if mod is not None else None
+    check(lib.bsm_flex_attention_decode_paged(
+        B, H, D, page_size, num_pages, block_table.data_ptr(), n_logical, kvl.data_ptr(), stride,
+        ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
+        ctypes.byref(cs), ctypes.byref(cb) if cb is not None else None,
+        ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
+        ctypes.byref(ts[3]), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
+    return out, lse
+
+
 def decode_multi_spec(spec: MaskSpec, kv_len: int, n: int) -> MaskSpec:
     """The mask of a block of n queries at positions kv_len - n .. kv_len - 1
     against the first kv_len positions of a cache described by spec (whose T
@@ -556,5 +604,6 @@ __all__ = ["MaskSpec", "MaskTerm", "CAUSAL", "SAME_DOC", "IN_WINDOW", "SINK", "P
            "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
            "flex_attention_decode", "decode_workspace", "flex_attention_decode_static",
+           "flex_attention_decode_paged",
            "decode_multi_spec", "flex_attention_decode_multi",
            "bwd_workspace", "block_mask_workspace", "_lib"]

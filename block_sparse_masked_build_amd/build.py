@@ -21,8 +21,6 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libbsm.so")
 
-# (source, object, extra flags): the attention passes are compiled once per
-# head dimension so that the halves build in parallel
 # (source, object, extra flags): the attention sources are compiled once
 # per element type (bf16, fp16) and, for the forward and backward, once per
 # head dimension, so that the pieces build in parallel

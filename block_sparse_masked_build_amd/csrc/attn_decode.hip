@@ -26,13 +26,17 @@
 //
 // Mapping to CDNA4: a single query has no matrix-product shape, and K and V
 // are streamed once, so the path is HBM-bound and runs on the vector units:
-//  * decode_partial_kernel: one workgroup of 4 waves per (slot of up to
-//    eight 128-key tiles, batch x head).  Each wave takes two tiles, in
-//    64-key blocks: lane = key for the scores (the query row is broadcast
-//    from LDS), then lane = head dimension for the value sum (value rows
-//    read as coalesced lines, 16 rows in flight).  fp32 online softmax in
-//    the log2 domain per wave, waves merged through LDS; the slot's (max,
-//    sum, unnormalised output) go to the workspace.
+//  * decode_partial_kernel: one workgroup of 4 waves per (batch x head,
+//    slot of up to eight 128-key tiles), batch x head fastest so that the
+//    busy slots of short caches spread over the XCDs.  Each wave takes two
+//    tiles, in 64-key blocks whose list entries and page-table entries are
+//    looked up while the query row loads.  For D <= 128 a load instruction
+//    covers whole rows (16 bytes per lane, D / 8 lanes per row), K and V of
+//    a block are requested together, and the scores' partial dot products
+//    are summed across each row's lanes; for D = 256 lane = key for the
+//    scores and lane = head dimension for the value sum.  fp32 online
+//    softmax in the log2 domain per wave, waves merged through LDS; the
+//    slot's (max, sum, unnormalised output) go to the workspace.
 //  * decode_combine_kernel: one workgroup per (batch, head) merges the slots
 //    through their log-sum-exps and writes out (bf16) and lse (fp32, natural
 //    log; -inf and out = 0 when no key is visible).
@@ -65,6 +69,11 @@ struct DecodeParams {
     int32_t bias_r;
     // block mask rows (NULL kv_num: no block mask)
     const int32_t *kv_num, *kv_idx, *full_kv_num, *full_kv_idx;
+    // paged K/V (NULL block_table: one contiguous cache per (b, h)): key kv of
+    // batch element b sits in page block_table[b * table_stride + kv / page_size]
+    // at row kv % page_size; k_sb / v_sb are then the page strides
+    const int32_t *block_table;
+    int32_t table_stride, page_size, num_pages;
     const elem_t *q; int64_t q_sb, q_sh;
     const elem_t *k; int64_t k_sb, k_sh, k_st;
     const elem_t *v; int64_t v_sb, v_sh, v_st;
@@ -111,9 +120,17 @@ __device__ inline void write_empty_slot(const DecodeParams &P, int64_t slot) {
     }
 }
 
+// lane l's value of a 64-bit integer, for a wave-uniform l
+__device__ inline int64_t readlane64(int64_t v, int l) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // ADD: an additive position term -- the ALiBi slope, or with P.bias the bias
 // table (one wave-uniform branch per key block; the decoding step is bound
 // by its HBM reads, not by this arithmetic).
+
 template <int D, bool ADD, bool SOFTCAP, bool LISTED>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
     constexpr int kDimsPerLane = D / 64;  // output dims per lane: lane * kDimsPerLane + i
@@ -122,7 +139,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     __shared__ float sm[kDecWaves], sl[kDecWaves];
     __shared__ float so[kDecWaves][D];
 
-    const int slot_i = blockIdx.x, bh = blockIdx.y;
+    const int slot_i = blockIdx.y, bh = blockIdx.x;
     const int b = bh / P.H, h = bh - b * P.H;
     const int bm = P.mask_b == 1 ? 0 : b;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -169,95 +186,234 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     const float bias_f = mod_f<SOFTCAP>(SOFTCAP ? P.softcap : 1.0f);
     const float *brow = table ? P.bias + (int64_t)h * (2 * P.bias_r + 1) + P.bias_r : nullptr;  // entry of distance 0
 
-    const elem_t *qrow = P.q + b * P.q_sb + h * P.q_sh;
-    for (int d = threadIdx.x; d < D; d += kDecThreads) sq[d] = static_cast<float>(qrow[d]);
-    __syncthreads();
-
-    const elem_t *kb = P.k + b * P.k_sb + h * P.k_sh;
-    const elem_t *vb = P.v + b * P.v_sb + h * P.v_sh;
-    float m = -INFINITY, l = 0.0f;
-    float o[kDimsPerLane];
-#pragma unroll
-    for (int i = 0; i < kDimsPerLane; ++i) o[i] = 0.0f;
-
-#pragma unroll 1
-    for (int sub = 0; sub < 2 * kWaveTiles; ++sub) {
-        // first key of this 64-key block (-1: no block)
-        const int te = kSlotTiles * slot_i + kWaveTiles * wv + (sub >> 1);
+    // The wave's 64-key blocks, looked up before the query row is loaded so
+    // that the list and page-table reads overlap it: lane s < 2 kWaveTiles
+    // holds block s's first key (-1: no block) and the offsets of its first
+    // K and V rows.  A paged block lies in one page (page sizes are
+    // multiples of 64); an out-of-range table entry is clamped, so a bad
+    // table reads a wrong page, never outside the pool.
+    int blk_key0 = -1;
+    int64_t blk_koff = 0, blk_voff = 0;
+    if (lane < 2 * kWaveTiles) {
+        const int te = kSlotTiles * slot_i + kWaveTiles * wv + (lane >> 1);
         int key0 = -1;
         if (LISTED) {
             if (te < nlist) {
                 const int j = te < nfull ? P.full_kv_idx[(int64_t)row * P.nt + te]
                                          : P.kv_idx[(int64_t)row * P.nt + te - nfull];
-                key0 = clamp_tile(j, P.nt) * kTile + (sub & 1) * 64;
+                key0 = clamp_tile(j, P.nt) * kTile + (lane & 1) * 64;
             }
         } else {
-            key0 = te * kTile + (sub & 1) * 64;
+            key0 = te * kTile + (lane & 1) * 64;
         }
-        if (key0 < 0 || key0 >= L) continue;  // wave-uniform
-        const int kv = key0 + lane;
-        float t = -INFINITY;
-        if (kv < L && dec_visible(P, bm, p, kv, window, docq)) {
-            const elem_t *krow = kb + (int64_t)kv * P.k_st;
-            float acc = 0.0f;
-#pragma unroll
-            for (int d0 = 0; d0 < D; d0 += 8) {
-                const dec_elem8 kk = *reinterpret_cast<const dec_elem8 *>(krow + d0);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(sq[d0 + e], static_cast<float>(kk[e]), acc);
-            }
-            // log2-domain modified score, as in the forward
-            float add = -mk.slope_f * (float)(p - kv);
-            if (table) add = bias_f * brow[min(max(p - kv, -P.bias_r), P.bias_r)];
-            t = mod_apply<ADD, SOFTCAP>(acc, add, mk);
-        }
-        // online softmax over this wave's 64 keys (log2 domain)
-        float mx = t;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        const float m_new = fmaxf(m, mx);
-        const float pk = m_new == -INFINITY ? 0.0f : fast_exp2(t - m_new);
-        const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m - m_new);
-        float ps = pk;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
-        l = l * alpha + ps;
-        m = m_new;
-        sp[wv][lane] = pk;  // read back by every lane of this wave (LDS operations stay in order)
-#pragma unroll
-        for (int i = 0; i < kDimsPerLane; ++i) o[i] *= alpha;
-        if (mx != -INFINITY) {
-            // value rows of the block's keys, 16 at a time with their loads
-            // issued together (keys past the live length have p = 0 and read
-            // a row inside the cache instead)
-            const int nk = min(64, L - key0);
-            const elem_t *vbase = vb + lane * kDimsPerLane;
-#pragma unroll 1
-            for (int j0 = 0; j0 < 64; j0 += 16) {
-                float vv[16][kDimsPerLane];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int key = min(key0 + j0 + j, L - 1);
-                    const elem_t *vrow = vbase + (int64_t)key * P.v_st;
-#pragma unroll
-                    for (int i = 0; i < kDimsPerLane; ++i) vv[j][i] = static_cast<float>(vrow[i]);
-                }
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float pj = j0 + j < nk ? sp[wv][j0 + j] : 0.0f;
-#pragma unroll
-                    for (int i = 0; i < kDimsPerLane; ++i) o[i] = __builtin_fmaf(pj, vv[j][i], o[i]);
-                }
+        if (key0 >= 0 && key0 < L) {
+            blk_key0 = key0;
+            if (P.block_table) {
+                const int pg = min(max(P.block_table[(int64_t)b * P.table_stride + key0 / P.page_size], 0),
+                                   P.num_pages - 1);
+                const int64_t r = key0 % P.page_size;
+                blk_koff = pg * P.k_sb + r * P.k_st;
+                blk_voff = pg * P.v_sb + r * P.v_st;
+            } else {
+                blk_koff = b * P.k_sb + (int64_t)key0 * P.k_st;
+                blk_voff = b * P.v_sb + (int64_t)key0 * P.v_st;
             }
         }
     }
-    // merge the four waves
+
+    const elem_t *qrow = P.q + b * P.q_sb + h * P.q_sh;
+    for (int d = threadIdx.x; d < D; d += kDecThreads) sq[d] = static_cast<float>(qrow[d]);
+    __syncthreads();
+
+    const elem_t *kb = P.k + h * P.k_sh;
+    const elem_t *vb = P.v + h * P.v_sh;
+    float m = -INFINITY, l = 0.0f;  // running max (log2 domain) and sum of the wave
+    if constexpr (D <= 128) {
+        // Lane l reads 16-byte pieces of rows: chunk c = l % kG (head
+        // dims 8c .. 8c + 7) of row g = l / kG of each group of kKpi rows,
+        // so one load instruction covers kKpi whole rows.  The query chunk
+        // stays in registers.
+        constexpr int kG = D / 8, kKpi = 64 / kG;
+        const int c = lane % kG, g = lane / kG;
+        float qc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qc[e] = sq[c * 8 + e];
+        // after the reduction of the scores lane l holds the score of key
+        // (l % kG) kKpi + l / kG of the block
+        const int my_key = c * kKpi + g;
+        float o[8];  // head dims 8c .. 8c + 7 over the rows g, g + kKpi, ...
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+
+#pragma unroll 1
+        for (int sub = 0; sub < 2 * kWaveTiles; ++sub) {
+            const int key0 = __builtin_amdgcn_readlane(blk_key0, sub);
+            if (key0 < 0) continue;  // no block
+            // rows key0 .. key0 + 63 of K and V
+            const elem_t *kblk = kb + readlane64(blk_koff, sub), *vblk = vb + readlane64(blk_voff, sub);
+            const uint64_t vis = __ballot(key0 + lane < L && dec_visible(P, bm, p, key0 + lane, window, docq));
+            if (vis == 0) continue;  // nothing visible: the running state is unchanged
+            // rows of invisible keys are replaced by the first visible one (a
+            // cache hit), so every load stays in bounds and reads no extra line
+            const int fv = __builtin_ctzll(vis);
+            // every K and V piece of the block is requested before any is
+            // used: the value rows do not depend on the scores, so both
+            // stream at once
+            dec_elem8 kk[kG], vv[kG];
+#pragma unroll
+            for (int i = 0; i < kG; ++i) {
+                const int r = i * kKpi + g;
+                const int re = (vis >> r) & 1 ? r : fv;
+                kk[i] = *reinterpret_cast<const dec_elem8 *>(kblk + (int64_t)re * P.k_st + c * 8);
+            }
+#pragma unroll
+            for (int i = 0; i < kG; ++i) {
+                const int r = i * kKpi + g;
+                const int re = (vis >> r) & 1 ? r : fv;
+                vv[i] = *reinterpret_cast<const dec_elem8 *>(vblk + (int64_t)re * P.v_st + c * 8);
+            }
+            float part[kG];
+#pragma unroll
+            for (int i = 0; i < kG; ++i) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(qc[e], static_cast<float>(kk[i][e]), acc);
+                part[i] = acc;
+            }
+            // sum the kG partial dot products of each row across its kG lanes:
+            // each halving step keeps the half of the rows selected by one lane
+            // bit (highest first), so lane l ends with row index l % kG
+#pragma unroll
+            for (int n = kG; n > 1; n >>= 1) {
+                const int half = n >> 1;
+                const bool up = (c & half) != 0;
+#pragma unroll
+                for (int j = 0; j < half; ++j) {
+                    const float send = up ? part[j] : part[j + half];
+                    const float keep = up ? part[j + half] : part[j];
+                    part[j] = keep + __shfl_xor(send, half);
+                }
+            }
+            const int kv = key0 + my_key;
+            float t = -INFINITY;
+            if ((vis >> my_key) & 1) {
+                // log2-domain modified score, as in the forward
+                float add = -mk.slope_f * (float)(p - kv);
+                if (table) add = bias_f * brow[min(max(p - kv, -P.bias_r), P.bias_r)];
+                t = mod_apply<ADD, SOFTCAP>(part[0], add, mk);
+            }
+            // online softmax over this wave's 64 keys (log2 domain)
+            float mx = t;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float m_new = fmaxf(m, mx);  // finite: some key is visible
+            const float pk = fast_exp2(t - m_new);
+            const float alpha = fast_exp2(m - m_new);
+            float ps = pk;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+            l = l * alpha + ps;
+            m = m_new;
+            sp[wv][my_key] = pk;  // read back by every lane of this wave (LDS operations stay in order)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= alpha;
+            // value rows (invisible keys have p = 0 and hold the first visible row)
+#pragma unroll
+            for (int i = 0; i < kG; ++i) {
+                const float pj = sp[wv][i * kKpi + g];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pj, static_cast<float>(vv[i][e]), o[e]);
+            }
+        }
+        // sum the output pieces of the kKpi row groups: lanes l < kG then hold
+        // head dims 8l .. 8l + 7
+#pragma unroll
+        for (int off = kG; off < 64; off <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], off);
+        }
+        if (lane < kG) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) so[wv][lane * 8 + e] = o[e];
+        }
+    } else {
+        // D = 256: lane = key for the scores (the query row broadcast from
+        // LDS), then lane = head dimensions for the value sum, 16 value rows
+        // in flight (the row-piece layout above measured slower here)
+        float o[kDimsPerLane];
+#pragma unroll
+        for (int i = 0; i < kDimsPerLane; ++i) o[i] = 0.0f;
+
+#pragma unroll 1
+        for (int sub = 0; sub < 2 * kWaveTiles; ++sub) {
+            const int key0 = __builtin_amdgcn_readlane(blk_key0, sub);
+            if (key0 < 0) continue;  // no block
+            // rows key0 .. key0 + 63 of K and V
+            const elem_t *kblk = kb + readlane64(blk_koff, sub), *vblk = vb + readlane64(blk_voff, sub);
+            const int kv = key0 + lane;
+            float t = -INFINITY;
+            if (kv < L && dec_visible(P, bm, p, kv, window, docq)) {
+                const elem_t *krow = kblk + (int64_t)lane * P.k_st;
+                float acc = 0.0f;
+#pragma unroll
+                for (int d0 = 0; d0 < D; d0 += 8) {
+                    const dec_elem8 kk = *reinterpret_cast<const dec_elem8 *>(krow + d0);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(sq[d0 + e], static_cast<float>(kk[e]), acc);
+                }
+                // log2-domain modified score, as in the forward
+                float add = -mk.slope_f * (float)(p - kv);
+                if (table) add = bias_f * brow[min(max(p - kv, -P.bias_r), P.bias_r)];
+                t = mod_apply<ADD, SOFTCAP>(acc, add, mk);
+            }
+            // online softmax over this wave's 64 keys (log2 domain)
+            float mx = t;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float m_new = fmaxf(m, mx);
+            const float pk = m_new == -INFINITY ? 0.0f : fast_exp2(t - m_new);
+            const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2(m - m_new);
+            float ps = pk;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+            l = l * alpha + ps;
+            m = m_new;
+            sp[wv][lane] = pk;  // read back by every lane of this wave (LDS operations stay in order)
+#pragma unroll
+            for (int i = 0; i < kDimsPerLane; ++i) o[i] *= alpha;
+            if (mx != -INFINITY) {
+                // value rows of the block's keys, 16 at a time with their loads
+                // issued together (keys past the live length have p = 0 and read
+                // a row inside the cache instead)
+                const int nk = min(64, L - key0);
+                const elem_t *vbase = vblk + lane * kDimsPerLane;
+#pragma unroll 1
+                for (int j0 = 0; j0 < 64; j0 += 16) {
+                    float vv[16][kDimsPerLane];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const int key = min(j0 + j, nk - 1);  // offset in the block
+                        const elem_t *vrow = vbase + (int64_t)key * P.v_st;
+#pragma unroll
+                        for (int i = 0; i < kDimsPerLane; ++i) vv[j][i] = static_cast<float>(vrow[i]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        const float pj = j0 + j < nk ? sp[wv][j0 + j] : 0.0f;
+#pragma unroll
+                        for (int i = 0; i < kDimsPerLane; ++i) o[i] = __builtin_fmaf(pj, vv[j][i], o[i]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kDimsPerLane; ++i) so[wv][lane * kDimsPerLane + i] = o[i];
+    }
+    // merge the four waves (their outputs are in so)
     if (lane == 0) {
         sm[wv] = m;
         sl[wv] = l;
     }
-#pragma unroll
-    for (int i = 0; i < kDimsPerLane; ++i) so[wv][lane * kDimsPerLane + i] = o[i];
     __syncthreads();
     if (wv == 0) {
         float M = sm[0];
@@ -308,7 +464,10 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeParams P) {
 
 template <int D, bool ALIBI, bool SOFTCAP>
 void launch_mods(const DecodeParams &P, hipStream_t stream) {
-    const dim3 grid(P.nslot, P.B * P.H), block(kDecThreads);
+    // (batch, head) fastest: consecutive workgroups go to different XCDs, so
+    // the slots that hold keys -- the first ones at short live lengths --
+    // spread over the whole chip instead of landing on one XCD
+    const dim3 grid(P.B * P.H, P.nslot), block(kDecThreads);
     if (P.kv_num)
         hipLaunchKernelGGL((decode_partial_kernel<D, ALIBI, SOFTCAP, true>), grid, block, 0, stream, P);
     else
@@ -360,6 +519,10 @@ hipError_t BSM_ELEM_FN(launch_attn_decode)(const DecodeLaunch &d, float *part, h
     P.kv_idx = a.kv_idx;
     P.full_kv_num = a.full_kv_num;
     P.full_kv_idx = a.full_kv_idx;
+    P.block_table = d.block_table;
+    P.table_stride = d.table_stride;
+    P.page_size = d.page_size;
+    P.num_pages = d.num_pages;
     P.q = static_cast<const elem_t *>(a.q);
     P.q_sb = a.q_sb;
     P.q_sh = a.q_sh;

@@ -361,6 +361,10 @@ bsm_status prepare_decode(int32_t B, int32_t H, int32_t capacity, int32_t D, con
     d.D = D;
     d.kv_len = kv_len;
     d.kv_len_stride = kv_len_stride;
+    d.block_table = nullptr;  // contiguous cache (the paged entry point sets these)
+    d.table_stride = 0;
+    d.page_size = 0;
+    d.num_pages = 0;
     return BSM_OK;
 }
 
@@ -587,6 +591,39 @@ bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int
         return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
     return hip_status(launch_decode(d, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
                       "bsm_flex_attention_decode launch");
+}
+
+bsm_status bsm_flex_attention_decode_paged(int32_t B, int32_t H, int32_t D, int32_t page_size, int32_t num_pages,
+                                           const int32_t *block_table, int32_t table_stride, const int32_t *kv_len,
+                                           int32_t kv_len_stride, const bsm_tensor *q, const bsm_tensor *k_pages,
+                                           const bsm_tensor *v_pages, const bsm_mask_spec *spec,
+                                           const bsm_block_mask *bm, const bsm_score_mod *mod, float scale,
+                                           const bsm_tensor *out, float *lse, void *workspace, size_t workspace_bytes,
+                                           void *stream) {
+    if (page_size < 64 || page_size % 64 != 0)
+        return fail(BSM_E_INVALID, "page_size %d must be a positive multiple of 64", page_size);
+    if (num_pages < 1) return fail(BSM_E_INVALID, "num_pages %d must be >= 1", num_pages);
+    if (!block_table) return fail(BSM_E_INVALID, "block_table is NULL");
+    if (table_stride < 1 || (int64_t)table_stride * page_size > kMaxT)
+        return fail(BSM_E_INVALID, "table_stride %d x page_size %d must give a capacity in [1, %d]", table_stride,
+                    page_size, kMaxT);
+    const int32_t capacity = table_stride * page_size;
+    bsm::DecodeLaunch d;
+    bsm_status st = prepare_decode(B, H, capacity, D, kv_len, kv_len_stride, q, k_pages, v_pages, spec, bm, mod,
+                                   scale, out, lse, d);
+    if (st != BSM_OK) return st;
+    const size_t need = decode_part_bytes(B, H, capacity, D);
+    if (!workspace || workspace_bytes < need)
+        return fail(BSM_E_WORKSPACE, "decode workspace needs %zu bytes, got %zu%s", need, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+        return fail(BSM_E_WORKSPACE, "workspace must be 256-byte aligned");
+    d.block_table = block_table;
+    d.table_stride = table_stride;
+    d.page_size = page_size;
+    d.num_pages = num_pages;
+    return hip_status(launch_decode(d, static_cast<float *>(workspace), static_cast<hipStream_t>(stream)),
+                      "bsm_flex_attention_decode_paged launch");
 }
 
 size_t bsm_decode_static_max_bytes(void) { return kScratchBytes; }

@@ -115,6 +115,9 @@ struct DecodeLaunch {
     int32_t dtype;           // BSM_DTYPE_*
     const int32_t *kv_len;   // device live length(s)
     int32_t kv_len_stride;   // 0: one value; 1: one per batch element
+    // paged K/V, or NULL block_table: see bsm_flex_attention_decode_paged
+    const int32_t *block_table;
+    int32_t table_stride, page_size, num_pages;
 };
 // A decoding workgroup ("slot") covers kDecodeSlotTiles 128-key tiles.
 constexpr int kDecodeSlotTiles = 8;

@@ -349,6 +349,31 @@ bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int
                                      const bsm_tensor *out, float *lse, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* The decoding step over a paged key/value cache (tutorial "FlexAttention in
+ * PyTorch", "Decoding and paged KV caches": the cache is held in fixed-size
+ * pages that a block table maps to each sequence's logical key blocks).
+ * k_pages, v_pages: pools of num_pages pages, each [H, page_size, D]; the
+ * tensors' stride_b is the page stride, stride_h and stride_t as usual.
+ * block_table: device int32 [B, table_stride]: key kv of batch element b
+ * sits at row kv % page_size of page block_table[b][kv / page_size].  The
+ * logical capacity is table_stride * page_size (spec->seq_len and any block
+ * mask are for it); entries for pages at or past the live length are never
+ * read; entries outside [0, num_pages) are clamped into it (a wrong page,
+ * never a read outside the pools).  page_size: a positive multiple of 64.
+ * Otherwise as bsm_flex_attention_decode, whose workspace size it shares
+ * (bsm_decode_workspace_bytes(B, H, table_stride * page_size, D)); the
+ * results equal those of that call on the gathered contiguous cache bit for
+ * bit.  Errors: as bsm_flex_attention_decode. */
+bsm_status bsm_flex_attention_decode_paged(int32_t B, int32_t H, int32_t D, int32_t page_size,
+                                           int32_t num_pages, const int32_t *block_table,
+                                           int32_t table_stride, const int32_t *kv_len,
+                                           int32_t kv_len_stride, const bsm_tensor *q,
+                                           const bsm_tensor *k_pages, const bsm_tensor *v_pages,
+                                           const bsm_mask_spec *spec, const bsm_block_mask *bm,
+                                           const bsm_score_mod *mod, float scale,
+                                           const bsm_tensor *out, float *lse, void *workspace,
+                                           size_t workspace_bytes, void *stream);
+
 /* Allocation-free decoding step, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  The same step as bsm_flex_attention_decode, with the

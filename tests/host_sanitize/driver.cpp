@@ -211,6 +211,24 @@ static void decoding() {
                                      nullptr));
     CHECK(stub::last_decode_part == reinterpret_cast<float *>(ws));
     CHECK(stub::last_decode.kv_len_stride == 1 && stub::last_decode.D == D);
+    CHECK(stub::last_decode.block_table == nullptr);
+    // paged: 16 logical pages of 256 keys over a pool of 40
+    int32_t *table = reinterpret_cast<int32_t *>(arena(1 << 20));
+    bsm_tensor kp = tensor_of(arena(20 << 20), H, 256, D);
+    REJECT(bsm_flex_attention_decode_paged(B, H, D, 96, 40, table, 16, kv_len, 1, &q, &kp, &kp, &s, nullptr, nullptr,
+                                           0.0f, &o, lse, ws, need, nullptr),
+           BSM_E_INVALID);
+    REJECT(bsm_flex_attention_decode_paged(B, H, D, 256, 40, nullptr, 16, kv_len, 1, &q, &kp, &kp, &s, nullptr,
+                                           nullptr, 0.0f, &o, lse, ws, need, nullptr),
+           BSM_E_INVALID);
+    REJECT(bsm_flex_attention_decode_paged(B, H, D, 256, 40, table, 8, kv_len, 1, &q, &kp, &kp, &s, nullptr, nullptr,
+                                           0.0f, &o, lse, ws, need, nullptr),
+           BSM_E_INVALID);  // 8 x 256 != the mask's 4096
+    ACCEPT(bsm_flex_attention_decode_paged(B, H, D, 256, 40, table, 16, kv_len, 1, &q, &kp, &kp, &s, nullptr, nullptr,
+                                           0.0f, &o, lse, ws, need, nullptr));
+    CHECK(stub::last_decode.block_table == table && stub::last_decode.table_stride == 16);
+    CHECK(stub::last_decode.page_size == 256 && stub::last_decode.num_pages == 40);
+    CHECK(stub::last_decode.a.k_sb == kp.stride_b);
     // the allocation-free variant looks up its static array on the current
     // device first: with no device that is a HIP error, never a launch
     const int before = stub::calls;

@@ -23,7 +23,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -307,3 +307,45 @@ def test_static_decode_rejects_oversize_on_the_host():
                                               ctypes.byref(spec), None, None, 0.0, ctypes.byref(t), FAKE, None)
     assert rc == _lib.BSM_E_WORKSPACE
     assert b"static scratch" in lib.bsm_last_error()
+
+
+def test_paged_decode_rejects_bad_arguments():
+    """Host checks of the paged decoding step: page size, pool, table and
+    capacity, then the decoding step's own checks on the logical capacity."""
+    t = _t()
+    spec = _spec(seq_len=1024)
+    need = lib.bsm_decode_workspace_bytes(1, 1, 1024, 64)
+
+    def call(page=256, pages=8, table=FAKE, tstride=4, s=spec, ws=FAKE, n=need, D=64):
+        return lib.bsm_flex_attention_decode_paged(1, 1, D, page, pages, table, tstride, FAKE, 0,
+                                                   *([ctypes.byref(t)] * 3), ctypes.byref(s), None, None, 0.0,
+                                                   ctypes.byref(t), FAKE, ws, n, None)
+
+    assert call(page=0) == _lib.BSM_E_INVALID
+    assert call(page=96) == _lib.BSM_E_INVALID        # not a multiple of 64
+    assert call(pages=0) == _lib.BSM_E_INVALID
+    assert call(table=None) == _lib.BSM_E_INVALID
+    assert call(tstride=0) == _lib.BSM_E_INVALID
+    assert call(page=1 << 16, tstride=1 << 7) == _lib.BSM_E_INVALID  # capacity past 2^22
+    assert call(s=_spec(seq_len=2048)) == _lib.BSM_E_INVALID          # spec must be the logical capacity
+    assert call(D=96) == _lib.BSM_E_UNSUPPORTED
+    assert call(n=need - 4) == _lib.BSM_E_WORKSPACE
+    assert call(ws=None) == _lib.BSM_E_WORKSPACE
+    assert call(page=64, tstride=16, ws=None) == _lib.BSM_E_WORKSPACE
+
+
+def test_python_paged_decode_checks_shapes_before_launch():
+    import torch
+    from block_sparse_masked_build_amd import api
+    B, H, P, D, npg = 2, 3, 128, 64, 5
+    kp, vp = _cpu((npg, H, P, D)), _cpu((npg, H, P, D))
+    table = torch.zeros((B, 4), dtype=torch.int32)
+    spec = api.MaskSpec(4 * P)
+    with pytest.raises(ValueError, match="v_pages"):
+        api.flex_attention_decode_paged(_cpu((B, H, 1, D)), kp, _cpu((npg, H, 2 * P, D)), table, spec)
+    with pytest.raises(ValueError, match="block_table"):
+        api.flex_attention_decode_paged(_cpu((B, H, 1, D)), kp, vp, table.long(), spec)
+    with pytest.raises(ValueError, match="q must be"):
+        api.flex_attention_decode_paged(_cpu((B + 1, H, 1, D)), kp, vp, table, spec)
+    with pytest.raises(ValueError, match="logical capacity"):
+        api.flex_attention_decode_paged(_cpu((B, H, 1, D)), kp, vp, table, api.MaskSpec(3 * P))

@@ -178,6 +178,7 @@ CONFIG_NAMES = {
     "4b": "B1 H16 S32768 D64 causal+(window 1024 | 4 sinks)",
     5: "B2 H16 S16384 D128 causal+document(Geometric 1024) ALiBi+softcap 30, fwd+bwd",
     "decode": "decoding step: B8 H32 cache 32768 D128 causal, one query per (b, h)",
+    "decode-docs": "decoding step: B8 H32 cache 32768 D128 causal+document(log-normal 500) with the block mask",
 }
 
 
@@ -187,7 +188,7 @@ def make_config(key, *, seed: Optional[int] = None, T: Optional[int] = None,
     smaller instance with the same structure (used by tests)."""
     k = str(key)
     base_seed = {"1": 1, "2": 2, "2-causal": 2, "2-window": 2, "2-chunks": 2,
-                 "3": 3, "4a": 4, "4b": 4, "5": 5, "decode": 6}[k]
+                 "3": 3, "4a": 4, "4b": 4, "5": 5, "decode": 6, "decode-docs": 6}[k]
     seed = base_seed if seed is None else seed
     rng = np.random.default_rng(seed)
     if k == "1":
@@ -231,6 +232,11 @@ def make_config(key, *, seed: Optional[int] = None, T: Optional[int] = None,
         T_ = T or 32768
         return Workload(CONFIG_NAMES[k], B or 8, H or 32, T_, 128, MaskSpecData(T_, causal=True),
                         ScoreModData(), seed)
+    if k == "decode-docs":
+        B_, T_ = B or 8, T or 32768
+        docs = np.stack([doc_ids_lognormal(T_, 500.0, 1.0, 16, 65536, rng) for _ in range(B_)])
+        return Workload(CONFIG_NAMES[k], B_, H or 32, T_, 128,
+                        MaskSpecData(T_, causal=True, document=True, doc_ids=docs), ScoreModData(), seed)
     if k == "5":
         B_, H_, T_, D = 2, 16, 16384, 128
         B_ = B or B_
