@@ -143,3 +143,71 @@ def test_single_page_pool_and_empty_live_length():
     out, lse = api.flex_attention_decode_paged(q, kp, vp, table, spec, kv_len=0)
     torch.cuda.synchronize()
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_graph_replay_serving_loop():
+    """A serving loop: the paged step captured once in a HIP graph; between
+    replays new tokens are written into their pages, a page is taken from a
+    free list whenever a sequence enters a new one (its table entry written
+    in device memory), and the live lengths grow.  Every replay equals the
+    eager contiguous step on the same keys bit for bit."""
+    from block_sparse_masked_build_amd import api
+    B, H, D, page, nl, npool = 2, 4, 128, 64, 16, 40
+    cap = page * nl
+    g = torch.Generator("cpu").manual_seed(78)
+    q = random_bf16((B, H, 1, D), g).cuda()
+    k_full = random_bf16((B, H, cap, D), g).cuda()
+    v_full = random_bf16((B, H, cap, D), g).cuda()
+    kp = torch.zeros((npool, H, page, D), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    table = torch.full((B, nl), -1, dtype=torch.int32, device="cuda")
+    free = [int(x) for x in np.random.default_rng(78).permutation(npool)]
+    kvl = torch.ones(B, dtype=torch.int32, device="cuda")
+    spec = api.mask_spec(cap, causal=True, window=300, sinks=4)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    ws = api.decode_workspace(B, H, cap, D)
+    host_table = [[-1] * nl for _ in range(B)]
+    filled = [0] * B
+
+    def append(b, upto):
+        # write keys filled[b] .. upto - 1 of sequence b into its pages
+        while filled[b] < upto:
+            pos = filled[b]
+            j, r = divmod(pos, page)
+            if host_table[b][j] < 0:
+                host_table[b][j] = free.pop()
+                table[b, j] = host_table[b][j]
+            n = min(page - r, upto - pos)
+            kp[host_table[b][j], :, r:r + n] = k_full[b, :, pos:pos + n]
+            vp[host_table[b][j], :, r:r + n] = v_full[b, :, pos:pos + n]
+            filled[b] += n
+
+    def step():
+        api.flex_attention_decode_paged(q, kp, vp, table, spec, None, kv_len=kvl, out=out, lse=lse, workspace=ws)
+
+    for b in range(B):
+        append(b, 1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for L0 in (1, 63, 64, 65, 300, 777, 1024):
+        lens = [L0, max(1, L0 - 30)]
+        log(f"[paged decode] graph replay at live lengths {lens}")
+        for b in range(B):
+            append(b, lens[b])
+        kvl.copy_(torch.tensor(lens, dtype=torch.int32))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (out.clone(), lse.clone())
+        ref = api.flex_attention_decode(q, k_full, v_full, spec, None, kv_len=kvl.clone())
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), lens
+    assert len(free) == npool - sum(-(-n // page) for n in filled)
