@@ -1,0 +1,140 @@
+"""The largest sequence the library accepts, T = 2^22 = 4,194,304 positions
+(32,768 x 32,768 tiles of 128), with the causal sliding-window mask of the
+speedrun notes ("FlexAttention", Record #12: a 1024-key window).
+
+The predicate depends only on q - kv and every tile is whole, so tile (i, j)
+has the class of the distance i - j, and a row (column) far from the start
+(end) of the sequence is a shifted copy of any other.  The oracle supplies
+that class table from a 65,536-position instance; the 2^22 block mask is
+checked against it exactly on every count and on sampled rows and columns
+entry by entry, and on every row by its padding.
+
+Attention outputs and gradients are checked on sampled positions against
+the oracle on a window of the sequence that holds everything the sampled
+position depends on, shifted to start at 0 (the same predicate holds there,
+since it depends only on q - kv)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_utils import assert_lse_close, assert_within_bound, f64, log, needs_gpu
+from workloads import MaskSpecData, random_bf16
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+T = 1 << 22
+NT = T // 128
+W = 1024
+
+
+def _offsets():
+    """Distances i - j of the full and of the partial tiles, from the oracle's
+    65,536-position block mask (row 511 is past the sequence start)."""
+    ref = oracle.spec_block_mask_lists(MaskSpecData(65536, causal=True, window=W))
+    r = 511
+    full = ref["full_kv_indices"].reshape(512, 512)[r]
+    part = ref["kv_indices"].reshape(512, 512)[r]
+    nf = int(ref["full_kv_num_blocks"].reshape(-1)[r])
+    npart = int(ref["kv_num_blocks"].reshape(-1)[r])
+    return r - full[:nf].astype(np.int64), r - part[:npart].astype(np.int64), ref
+
+
+def _expected_row(i, offs):
+    j = i - offs
+    return np.sort(j[j >= 0])
+
+
+def _expected_col(j, offs):
+    i = j + offs
+    return np.sort(i[i < NT])
+
+
+def test_block_mask_at_the_maximum_length():
+    from block_sparse_masked_build_amd import api
+    full_off, part_off, ref = _offsets()
+    log(f"[max size] block mask T={T}: full distances {sorted(full_off.tolist())}, "
+        f"partial distances {sorted(part_off.tolist())}")
+    spec = api.mask_spec(T, causal=True, window=W)
+    bm = api.build_block_mask(spec)
+    torch.cuda.synchronize()
+    i = np.arange(NT)
+    # every count, rows and columns
+    exp_fr = np.array([(i_ - full_off >= 0).sum() for i_ in i])
+    exp_pr = np.array([(i_ - part_off >= 0).sum() for i_ in i])
+    exp_fc = np.array([(j_ + full_off < NT).sum() for j_ in i])
+    exp_pc = np.array([(j_ + part_off < NT).sum() for j_ in i])
+    got = {n: getattr(bm, n).view(-1).cpu().numpy() for n in
+           ("full_kv_num_blocks", "kv_num_blocks", "full_q_num_blocks", "q_num_blocks")}
+    for n, e in (("full_kv_num_blocks", exp_fr), ("kv_num_blocks", exp_pr),
+                 ("full_q_num_blocks", exp_fc), ("q_num_blocks", exp_pc)):
+        assert np.array_equal(got[n], e), (n, np.argwhere(got[n] != e)[:5].tolist())
+    # the first rows equal the 65,536-position oracle's
+    assert np.array_equal(got["kv_num_blocks"][:512], ref["kv_num_blocks"].reshape(-1))
+    assert np.array_equal(got["full_kv_num_blocks"][:512], ref["full_kv_num_blocks"].reshape(-1))
+    # sampled rows and columns entry by entry, -1 after the count
+    rows = [0, 1, 7, 8, 9, 511, 512, 12345, NT // 2, NT - 9, NT - 2, NT - 1]
+    for name, exp_fn, offs in (("full_kv_indices", _expected_row, full_off), ("kv_indices", _expected_row, part_off),
+                               ("full_q_indices", _expected_col, full_off), ("q_indices", _expected_col, part_off)):
+        arr = getattr(bm, name).view(NT, NT)
+        for r in rows:
+            row = arr[r].cpu().numpy()
+            e = exp_fn(r, offs)
+            assert np.array_equal(row[:len(e)], e), (name, r, row[:len(e) + 2], e)
+            assert np.all(row[len(e):] == -1), (name, r)
+    # every row's padding: exactly count entries differ from -1
+    for name, cnt in (("full_kv_indices", "full_kv_num_blocks"), ("kv_indices", "kv_num_blocks"),
+                      ("full_q_indices", "full_q_num_blocks"), ("q_indices", "q_num_blocks")):
+        arr = getattr(bm, name).view(NT, NT)
+        c = getattr(bm, cnt).view(-1)
+        for a in range(0, NT, 4096):
+            live = (arr[a:a + 4096] != -1).sum(dim=1, dtype=torch.int32)
+            assert torch.equal(live, c[a:a + 4096]), (name, a)
+            head = arr[a:a + 4096, :1]
+            assert bool(((head >= 0) | (c[a:a + 4096, None] == 0)).all()), (name, a)
+    log("  ok")
+
+
+def _sub(x, lo, hi):
+    return x[lo:hi].double().numpy()
+
+
+def test_forward_and_backward_at_the_maximum_length():
+    from block_sparse_masked_build_amd import api
+    B, H, D = 1, 1, 64
+    log(f"[max size] forward + backward B{B} H{H} T={T} D{D}, causal + window {W}")
+    g = torch.Generator("cpu").manual_seed(4242)
+    q, k, v, do = (random_bf16((B, H, T, D), g) for _ in range(4))
+    spec = api.mask_spec(T, causal=True, window=W)
+    bm = api.build_block_mask(spec)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = api.flex_attention_fwd(qd, kd, vd, bm, spec)
+    dq, dk, dv = api.flex_attention_bwd(qd, kd, vd, out, lse, dod, bm, spec)
+    torch.cuda.synchronize()
+    for name, x in (("out", out), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert bool(torch.isfinite(x).all()), name
+    out_c, lse_c, dq_c, dk_c, dv_c = (x[0, 0].cpu() for x in (out, lse, dq, dk, dv))
+    Q, K, V, dO = (x[0, 0] for x in (q, k, v, do))
+    # query rows: everything they depend on lies in [qp - W + 1, qp]
+    for qp in (0, 1, 127, 128, W - 1, W, 1 << 21, (1 << 21) + 77, T - 129, T - 1):
+        lo = max(0, qp - W + 1)
+        sub = MaskSpecData(qp + 1 - lo, causal=True, window=W)
+        r = np.array([qp - lo])
+        ro, rl, rm = oracle.forward_rows(_sub(Q, lo, qp + 1), _sub(K, lo, qp + 1), _sub(V, lo, qp + 1),
+                                         sub, None, 0, 0, r, with_mass=True)
+        assert_within_bound(f64(out_c[qp:qp + 1]), ro, rm, f"out row {qp}")
+        assert_lse_close(lse_c[qp:qp + 1].double().numpy(), rl, f"lse row {qp}")
+        rdq, mdq = oracle.backward_dq_rows(_sub(Q, lo, qp + 1), _sub(K, lo, qp + 1), _sub(V, lo, qp + 1),
+                                           _sub(dO, lo, qp + 1), sub, None, 0, 0, r, with_mass=True)
+        assert_within_bound(f64(dq_c[qp:qp + 1]), rdq, mdq, f"dq row {qp}")
+    # key columns: the queries that see kp are [kp, kp + W - 1], and each of
+    # those sees keys from kp - W + 1 on
+    for kp in (0, 1, 128, W, 1 << 21, T - W - 1, T - 2, T - 1):
+        lo, hi = max(0, kp - W + 1), min(T, kp + W)
+        sub = MaskSpecData(hi - lo, causal=True, window=W)
+        c = np.array([kp - lo])
+        rdk, rdv, mdk, mdv = oracle.backward_dkdv_cols(_sub(Q, lo, hi), _sub(K, lo, hi), _sub(V, lo, hi),
+                                                       _sub(dO, lo, hi), sub, None, 0, 0, c, with_mass=True)
+        assert_within_bound(f64(dk_c[kp:kp + 1]), rdk, mdk, f"dk col {kp}")
+        assert_within_bound(f64(dv_c[kp:kp + 1]), rdv, mdv, f"dv col {kp}")
+    log("  ok")
