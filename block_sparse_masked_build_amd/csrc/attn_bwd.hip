@@ -777,7 +777,8 @@ template <int D, bool ALIBI, bool SOFTCAP, bool TABLE, bool GENERAL, bool BIAS>
 __device__ __attribute__((always_inline)) inline void dkdv_body(const AttnParams &p, DkdvSmem<D> &sm,
                                                                 uint32_t btab) {
     const int nt = p.nt;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int wg = p.col_chunked ? col_remap(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (wg >= p.B * p.H * nt) return;  // past the work (chunked placement; whole workgroup)
     const int bh = wg / nt;
     const int j = wg % nt;  // early key tiles first: under a causal mask they carry the most tiles
     const int b = bh / p.H, h = bh % p.H;
@@ -1149,7 +1150,8 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv256_kernel(AttnParams p) {
     static_assert(D == 256, "the 16-key layout serves D = 256");
     __shared__ __attribute__((aligned(1024))) Dkdv16Smem<D> sm;
     const int nt = p.nt;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    const int wg = p.col_chunked ? col_remap(blockIdx.x) : xcd_remap(blockIdx.x, gridDim.x);
+    if (wg >= 2 * p.B * p.H * nt) return;  // past the work (chunked placement; whole workgroup)
     const int bh = wg / (2 * nt);
     const int jh = wg % (2 * nt);  // early key tiles first
     const int j = jh >> 1, half = jh & 1;
@@ -1283,10 +1285,29 @@ __global__ __launch_bounds__(kThreads) void slope_reduce_kernel(const float *par
 // the 64K doc+window, causal-in-chunks and ALiBi + soft-cap workloads, the
 // column work order gained for dK/dV only with soft-capped documents and lost
 // elsewhere, while the row order for dQ gained or held everywhere.
+//
+// dK/dV placement.  The workgroups of the key tiles go to the XCDs in
+// contiguous ranges, so neighbouring tiles share their query tiles in one
+// L2.  Under a plain causal mask (no document, window or composed table) a
+// head's early tiles carry the most work, and when the ranges do not hold
+// whole heads the XCDs get unequal shares (1.66x between the heaviest and
+// the lightest at B1 H6 T65536); there the tiles go out in chunks dealt to
+// the XCDs in alternating rounds instead (col_remap).  Measured at B1 H6
+// T65536: causal 25.1 -> 21.4 ms; the chunked placement was 3.8% slower on
+// the doc+window workload and 6% slower with ALiBi + soft-capped documents,
+// which keep the ranges.
+inline unsigned dkdv_grid_of(AttnParams &q, int per_head) {
+    const int64_t n = (int64_t)q.B * q.H * per_head;
+    const uint32_t f = q.mask_flags;
+    const bool plain_causal = (f & BSM_MASK_CAUSAL) && !(f & (BSM_MASK_DOCUMENT | BSM_MASK_WINDOW | BSM_MASK_TABLE));
+    q.col_chunked = plain_causal && n % (8 * (int64_t)per_head) != 0;
+    return q.col_chunked ? col_grid(n) : (unsigned)n;
+}
+
 template <int D, bool ALIBI, bool SOFTCAP, bool TABLE>
 void launch_main(const AttnParams &p, hipStream_t stream) {
     AttnParams q = p;
-    const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
+    const dim3 dq_grid(item_order(q)), block(kThreads);
     // Composed masks always take the clamped copies; otherwise only a key
     // (query) length off the block grid makes dQ's (dK/dV's) copies clamped.
     // (The non-clamped branches name GENERAL = TABLE: with TABLE they are never
@@ -1309,12 +1330,13 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
             hipLaunchKernelGGL((dq_kernel<D, ALIBI, SOFTCAP, false, TABLE, TABLE, false>), dq_grid, block, 0, stream, q);
     }
     if constexpr (D == 256) {  // 16 keys per wave, half a key tile per workgroup
-        const dim3 grid256(2 * p.B * p.H * p.nt);
+        const dim3 grid256(dkdv_grid_of(q, 2 * p.nt));
         if (q_r)
             hipLaunchKernelGGL((dkdv256_kernel<D, ALIBI, SOFTCAP, TABLE, true>), grid256, block, 0, stream, q);
         else
             hipLaunchKernelGGL((dkdv256_kernel<D, ALIBI, SOFTCAP, TABLE, TABLE>), grid256, block, 0, stream, q);
     } else {
+        const dim3 dkdv_grid(dkdv_grid_of(q, p.nt));
         if (q_r)
             hipLaunchKernelGGL((dkdv_kernel<D, ALIBI, SOFTCAP, TABLE, true>), dkdv_grid, block, 0, stream, q);
         else
@@ -1327,13 +1349,14 @@ void launch_main(const AttnParams &p, hipStream_t stream) {
 template <int D, bool SOFTCAP, bool TABLE>
 void launch_bias(const AttnParams &p, hipStream_t stream) {
     AttnParams q = p;
-    const dim3 dq_grid(item_order(q)), dkdv_grid(p.B * p.H * p.nt), block(kThreads);
+    const dim3 dq_grid(item_order(q)), block(kThreads);
     hipLaunchKernelGGL((dq_kernel<D, false, SOFTCAP, false, TABLE, true, true>), dq_grid, block, 0, stream, q);
     if (p.dbias) {
         const int nb = 2 * p.bias_r + 1;
         hipLaunchKernelGGL(bias_reduce_kernel, dim3((nb + 31) / 32, p.H), block, 0, stream,
                            p.dbias_part, p.dbias, p.B, p.H, p.nqt, nb);
     }
+    const dim3 dkdv_grid(dkdv_grid_of(q, p.nt));
     hipLaunchKernelGGL((dkdv_bias_kernel<D, SOFTCAP, TABLE>), dkdv_grid, block, 0, stream, q);
 }
 

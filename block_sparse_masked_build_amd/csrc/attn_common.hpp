@@ -106,6 +106,26 @@ __device__ inline int xcd_remap(int L, int N) {
     return (x < rem) ? x * (per + 1) + slot : rem * (per + 1) + (x - rem) * per + slot;
 }
 
+// Key-tile workgroup -> work index for the column kernels in chunked
+// placement.  Workgroup L runs on XCD L % 8 and is that XCD's (L / 8)-th.
+// Work indices go out in chunks of kColChunk consecutive ones (neighbouring
+// key tiles read the same query tiles, so a chunk shares one L2), dealt to
+// the 8 XCDs in rounds whose direction alternates (0..7, then 7..0): under a
+// causal mask a head's early tiles carry the most work and it falls
+// steadily, so each XCD gets an even share.  The grid is rounded up to whole
+// rounds (col_grid); indices past the work exit at once.  A bijection of
+// [0, col_grid(n)).
+constexpr int kColChunk = 16;
+inline unsigned col_grid(int64_t n) {
+    const int64_t r = 8 * kColChunk;
+    return (unsigned)((n + r - 1) / r * r);
+}
+__device__ inline int col_remap(int L) {
+    const int x = L % 8, s = L / 8, round = s / kColChunk;
+    const int xcd_pos = (round & 1) ? 7 - x : x;
+    return (8 * round + xcd_pos) * kColChunk + s % kColChunk;
+}
+
 // Scheduling hints for a straight-line block of N (LDS read -> MFMA) pairs:
 // issue `ahead` reads first, then alternate one product and one read, then
 // drain the last products.

@@ -338,8 +338,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
         }
     } else {
         // D = 256: lane = key for the scores (the query row broadcast from
-        // LDS), then lane = head dimensions for the value sum, 16 value rows
-        // in flight (the row-piece layout above measured slower here)
+        // LDS), then lane = head dimensions for the value sum, all 64 value
+        // rows in flight (the row-piece layout above measured slower here)
         float o[kDimsPerLane];
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; ++i) o[i] = 0.0f;
@@ -382,27 +382,24 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 #pragma unroll
             for (int i = 0; i < kDimsPerLane; ++i) o[i] *= alpha;
             if (mx != -INFINITY) {
-                // value rows of the block's keys, 16 at a time with their loads
-                // issued together (keys past the live length have p = 0 and read
-                // a row inside the cache instead)
+                // the block's 64 value rows, their loads issued together
+                // (keys past the live length have p = 0 and read a row
+                // inside the cache instead)
                 const int nk = min(64, L - key0);
                 const elem_t *vbase = vblk + lane * kDimsPerLane;
-#pragma unroll 1
-                for (int j0 = 0; j0 < 64; j0 += 16) {
-                    float vv[16][kDimsPerLane];
+                float vv[64][kDimsPerLane];
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = min(j0 + j, nk - 1);  // offset in the block
-                        const elem_t *vrow = vbase + (int64_t)key * P.v_st;
+                for (int j = 0; j < 64; ++j) {
+                    const int key = min(j, nk - 1);  // offset in the block
+                    const elem_t *vrow = vbase + (int64_t)key * P.v_st;
 #pragma unroll
-                        for (int i = 0; i < kDimsPerLane; ++i) vv[j][i] = static_cast<float>(vrow[i]);
-                    }
+                    for (int i = 0; i < kDimsPerLane; ++i) vv[j][i] = static_cast<float>(vrow[i]);
+                }
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const float pj = j0 + j < nk ? sp[wv][j0 + j] : 0.0f;
+                for (int j = 0; j < 64; ++j) {
+                    const float pj = j < nk ? sp[wv][j] : 0.0f;
 #pragma unroll
-                        for (int i = 0; i < kDimsPerLane; ++i) o[i] = __builtin_fmaf(pj, vv[j][i], o[i]);
-                    }
+                    for (int i = 0; i < kDimsPerLane; ++i) o[i] = __builtin_fmaf(pj, vv[j][i], o[i]);
                 }
             }
         }

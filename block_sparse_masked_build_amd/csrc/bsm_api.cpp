@@ -168,7 +168,10 @@ bsm_status check_attn_common(int32_t B, int32_t H, int32_t T, int32_t D, const b
     if (spec->mask_b != 1 && spec->mask_b != B)
         return fail(BSM_E_INVALID, "mask_b %d must be 1 or B=%d", spec->mask_b, B);
     const MaskDims m = mask_dims(spec);
-    if ((int64_t)B * H * (m.nqt > m.nkt ? m.nqt : m.nkt) > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
+    // the D = 256 backward runs two workgroups per key tile, and a chunked
+    // dK/dV grid is rounded up to 128 workgroups
+    if ((int64_t)B * H * (m.nqt > m.nkt ? m.nqt : m.nkt) > (INT32_MAX - 1024) / 2)
+        return fail(BSM_E_INVALID, "grid too large");
     return check_mod(mod);
 }
 

@@ -90,6 +90,9 @@ struct AttnParams {
     // the last block, and division magic numbers (set by the launcher)
     int32_t ord_r, ord_chunk_log2, ord_nblk, ord_p;
     uint32_t ord_m_cr, ord_m_p;
+    // dK/dV workgroup placement: 0 contiguous ranges per XCD, 1 chunks dealt
+    // to the XCDs in alternating rounds (set by the backward's launcher)
+    int32_t col_chunked;
 };
 
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t stream);

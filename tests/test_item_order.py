@@ -117,3 +117,69 @@ def test_random_small_shapes():
             continue
         for ipw in (1, 2):
             emulate(mask_b, nt, B, H, ipw)
+
+
+# dK/dV workgroup placement (the backward's column kernels), written out as
+# the launcher and kernels compute it.
+COL_CHUNK = 16
+
+
+def xcd_remap(L, N):
+    per, rem = N // 8, N % 8
+    x, slot = L % 8, L // 8
+    return x * (per + 1) + slot if x < rem else rem * (per + 1) + (x - rem) * per + slot
+
+
+def col_grid(n):
+    r = 8 * COL_CHUNK
+    return (n + r - 1) // r * r
+
+
+def col_remap(L):
+    x, s = L % 8, L // 8
+    rnd = s // COL_CHUNK
+    pos = 7 - x if rnd & 1 else x
+    return (8 * rnd + pos) * COL_CHUNK + s % COL_CHUNK
+
+
+def dkdv_grid_of(B, H, per_head, plain_causal):
+    n = B * H * per_head
+    chunked = plain_causal and n % (8 * per_head) != 0
+    return (col_grid(n) if chunked else n), chunked
+
+
+def _placement(B, H, per_head, plain_causal):
+    n = B * H * per_head
+    grid, chunked = dkdv_grid_of(B, H, per_head, plain_causal)
+    wgs = [col_remap(L) if chunked else xcd_remap(L, grid) for L in range(grid)]
+    return n, grid, chunked, wgs
+
+
+@pytest.mark.parametrize("B,H,nt", [(1, 1, 1), (1, 1, 7), (1, 6, 512), (1, 1, 512), (2, 3, 129), (3, 5, 64),
+                                    (4, 16, 64), (1, 16, 256), (2, 16, 128)])
+@pytest.mark.parametrize("per_tile", [1, 2])  # D = 256 runs two workgroups per key tile
+@pytest.mark.parametrize("plain_causal", [False, True])
+def test_dkdv_placement_covers_every_tile_once(B, H, nt, per_tile, plain_causal):
+    n, grid, chunked, wgs = _placement(B, H, nt * per_tile, plain_causal)
+    assert sorted(wgs) == list(range(grid))        # a bijection of the grid
+    assert sorted(w for w in wgs if w < n) == list(range(n))  # every tile once; the rest exit
+    assert grid - n < 8 * COL_CHUNK
+
+
+@pytest.mark.parametrize("B,H,nt", [(1, 6, 512), (1, 1, 512), (1, 3, 256), (2, 3, 129), (1, 6, 128)])
+def test_dkdv_placement_balances_causal_work_over_xcds(B, H, nt):
+    """Under a causal mask key tile j of a head has nt - j query tiles.  The
+    placement used for a plain causal mask gives the XCDs equal work when a
+    head's tiles fill whole chunks, and within 25% otherwise, where
+    contiguous ranges differed by 1.6x and more."""
+    n, grid, chunked, wgs = _placement(B, H, nt, True)
+    assert chunked
+    work = [0] * 8
+    for L, w in enumerate(wgs):
+        if w < n:
+            work[L % 8] += nt - w % nt
+    ranges = [0] * 8
+    for L in range(n):
+        ranges[L % 8] += nt - xcd_remap(L, n) % nt
+    assert max(work) / min(work) < (1.0001 if nt % COL_CHUNK == 0 else 1.25), work
+    assert max(ranges) / min(ranges) > 1.6, ranges
