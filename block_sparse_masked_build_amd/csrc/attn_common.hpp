@@ -991,7 +991,10 @@ __device__ inline WorkRec load_rec(const int32_t *order, int e) {
 // Item order.  Item k is work-order entry e for head (and, with a shared
 // mask, batch entry) rem.  Items come in chunks of 2^ord_chunk_log2
 // consecutive entries of one head -- rows that mostly share key and value
-// tiles -- and chunk c is served by queue c % Q: workgroup b takes the
+// tiles -- dealt to the Q queues in rounds of Q chunks whose direction
+// alternates (chunk Q r + j goes to queue j in even rounds r and to queue
+// Q - 1 - j in odd ones): the work order runs from the longest rows down,
+// so alternating evens out the queues' work.  Workgroup b takes the
 // (b / Q)-th item of queue b % Q.  Workgroups are dispatched round-robin
 // over the XCDs, so with Q = 8 each queue runs on one XCD and the rows
 // running at the same time there share tiles through its L2; items leave
@@ -1032,7 +1035,9 @@ struct ItemOrder {
     }
     // Item of this queue's i-th grab (>= nitems: the queue is empty).
     __device__ int item(int i) const {
-        const int64_t k = (((int64_t)queue + (int64_t)Q * (i >> cl)) << cl) + (i & ((1 << cl) - 1));
+        const int r = i >> cl;
+        const int pos = (r & 1) ? Q - 1 - queue : queue;  // this queue's chunk in round r
+        const int64_t k = (((int64_t)pos + (int64_t)Q * r) << cl) + (i & ((1 << cl) - 1));
         return k < nitems ? (int)k : nitems;
     }
     // Blocks of 2^cl entries times R heads, head-major inside a block; the

@@ -1,7 +1,7 @@
 """Host emulation of the attention kernels' item order (CPU only): the grid
-size, the queue / grab arithmetic and the decode of an item into (work-order
-entry, head index), written out exactly as the forward and dQ kernels
-compute them (including the division by magic numbers), one item per
+size, the queue / grab arithmetic (chunks dealt to the queues in rounds of
+alternating direction) and the decode of an item into (work-order entry,
+head index), written out exactly as the forward and dQ kernels compute them (including the division by magic numbers), one item per
 workgroup.  For many shapes every item must be taken exactly once, and every
 index the kernels form from it -- the record they load, the batch and head --
 must lie inside its array.  The emulation also takes several consecutive
@@ -49,7 +49,9 @@ def item_order(mask_b, nt, B, H):
 
 def item(f, queue, i):
     cl = f["cl"]
-    k = ((queue + QUEUES * (i >> cl)) << cl) + (i & ((1 << cl) - 1))
+    r = i >> cl
+    pos = QUEUES - 1 - queue if r & 1 else queue
+    k = ((pos + QUEUES * r) << cl) + (i & ((1 << cl) - 1))
     return k if k < f["nitems"] else f["nitems"]
 
 
@@ -183,3 +185,26 @@ def test_dkdv_placement_balances_causal_work_over_xcds(B, H, nt):
         ranges[L % 8] += nt - xcd_remap(L, n) % nt
     assert max(work) / min(work) < (1.0001 if nt % COL_CHUNK == 0 else 1.25), work
     assert max(ranges) / min(ranges) > 1.6, ranges
+
+
+def _queue_tiles(nt, R, counts_by_entry):
+    """Visible tiles each queue (XCD) runs for one mask batch whose work-order
+    entry e has counts_by_entry[e] tiles, R heads."""
+    f, grid = item_order(1, nt, 1, R)
+    work = [0] * QUEUES
+    for wg in range(grid):
+        k = item(f, wg % QUEUES, wg // QUEUES)
+        if k < f["nitems"]:
+            e, _ = decode(f, k)
+            work[wg % QUEUES] += counts_by_entry[e]
+    return work
+
+
+@pytest.mark.parametrize("nt,R", [(512, 6), (512, 1), (128, 3), (64, 64)])
+def test_queues_share_causal_rows_evenly(nt, R):
+    """Causal rows sorted longest first (entry e has nt - e tiles): the
+    alternating rounds give every queue the same tiles within 1%; dealing
+    every round in the same direction gave the first queue up to 1.56x the
+    last one's."""
+    work = _queue_tiles(nt, R, [nt - e for e in range(nt)])
+    assert max(work) / min(work) < 1.01, work
