@@ -363,7 +363,14 @@ bsm_status bsm_flex_attention_decode(int32_t B, int32_t H, int32_t capacity, int
  * Otherwise as bsm_flex_attention_decode, whose workspace size it shares
  * (bsm_decode_workspace_bytes(B, H, table_stride * page_size, D)); the
  * results equal those of that call on the gathered contiguous cache bit for
- * bit.  Errors: as bsm_flex_attention_decode. */
+ * bit.  The pools, the table and every output stay the caller's; the table
+ * is read by the kernels on `stream`, so it may change between steps (and
+ * between replays of a captured graph) like kv_len.
+ * Errors: BSM_E_INVALID for page_size < 64 or not a multiple of 64,
+ * num_pages < 1, a NULL block_table, table_stride < 1 or a logical capacity
+ * past 2^22, and then every error of bsm_flex_attention_decode for the
+ * logical capacity (BSM_E_INVALID, BSM_E_UNSUPPORTED for D, BSM_E_WORKSPACE,
+ * BSM_E_HIP on a failed launch). */
 bsm_status bsm_flex_attention_decode_paged(int32_t B, int32_t H, int32_t D, int32_t page_size,
                                            int32_t num_pages, const int32_t *block_table,
                                            int32_t table_stride, const int32_t *kv_len,
