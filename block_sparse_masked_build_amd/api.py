@@ -86,6 +86,18 @@ def or_masks(*terms: MaskTerm) -> MaskTerm:
     return out
 
 
+def _ptr(t: torch.Tensor, name: str) -> int:
+    """Device address of a tensor the kernels read or write: it must live on
+    the current GPU (a host or other-device address would be read by the
+    kernels as if it were theirs)."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a tensor on the GPU, got "
+                         f"{t.device if isinstance(t, torch.Tensor) else type(t).__name__}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device cuda:{torch.cuda.current_device()}")
+    return t.data_ptr()
+
+
 @dataclasses.dataclass
 class MaskSpec:
     """Device-side mask description.  `window` is a device int32 tensor of
@@ -145,8 +157,8 @@ class MaskSpec:
 
     def c_struct(self) -> BsmMaskSpec:
         return BsmMaskSpec(self.flags, self.T, self.mask_b,
-                           self.doc_ids.data_ptr() if self.doc_ids is not None else None,
-                           self.window.data_ptr() if self.window is not None else None,
+                           _ptr(self.doc_ids, "doc_ids") if self.doc_ids is not None else None,
+                           _ptr(self.window, "window") if self.window is not None else None,
                            int(self.sinks), int(self.prefix), int(self.q_len), int(self.q_offset),
                            self.composed.table if self.composed is not None else 0, int(self.kv_block))
 
@@ -173,9 +185,9 @@ class ScoreMod:
             f |= BSM_MOD_SOFTCAP
         if self.bias is not None:
             f |= BSM_MOD_BIAS
-        return BsmScoreMod(f, self.alibi_slopes.data_ptr() if self.alibi_slopes is not None else None,
+        return BsmScoreMod(f, _ptr(self.alibi_slopes, "alibi_slopes") if self.alibi_slopes is not None else None,
                            float(self.softcap) if self.softcap is not None else 0.0, None,
-                           self.bias.data_ptr() if self.bias is not None else None, self.bias_radius, None)
+                           _ptr(self.bias, "bias") if self.bias is not None else None, self.bias_radius, None)
 
 
 class BlockMask(NamedTuple):
@@ -192,7 +204,7 @@ class BlockMask(NamedTuple):
     q_order: torch.Tensor     # int32 [mask_b * KT, 4]: columns, most tiles first (same layout)
 
     def c_struct(self) -> BsmBlockMask:
-        return BsmBlockMask(*[t.data_ptr() for t in self])
+        return BsmBlockMask(*[_ptr(t, n) for n, t in zip(self._fields, self)])
 
     def visible_tiles(self) -> int:
         """Non-empty tiles (partial + full) over the mask batch."""
@@ -286,7 +298,7 @@ def build_block_mask(spec: MaskSpec, out: Optional[BlockMask] = None,
         workspace = block_mask_workspace(spec)
     cs = spec.c_struct()
     cb = out.c_struct()
-    check(lib.bsm_build_block_mask(ctypes.byref(cs), ctypes.byref(cb), workspace.data_ptr(),
+    check(lib.bsm_build_block_mask(ctypes.byref(cs), ctypes.byref(cb), _ptr(workspace, "workspace"),
                                    workspace.numel(), _stream()))
     return out
 
@@ -302,7 +314,7 @@ def _tensor(t: torch.Tensor, name: str) -> BsmTensor:
     if t.stride(3) != 1:
         raise ValueError(f"{name}: last dimension must be contiguous")
     sb, sh, st, _ = t.stride()
-    return BsmTensor(t.data_ptr(), sb, sh, st, _DTYPES[t.dtype])
+    return BsmTensor(_ptr(t, name), sb, sh, st, _DTYPES[t.dtype])
 
 
 def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,
@@ -327,7 +339,7 @@ def flex_attention_fwd(q, k, v, block_mask: BlockMask, spec: MaskSpec,
     check(lib.bsm_flex_attention_fwd(
         B, H, T, D, ctypes.byref(tq), ctypes.byref(tk), ctypes.byref(tv), ctypes.byref(cb),
         ctypes.byref(cs), ctypes.byref(cm) if cm is not None else None,
-        float(scale) if scale is not None else 0.0, ctypes.byref(to), lse.data_ptr(), _stream()))
+        float(scale) if scale is not None else 0.0, ctypes.byref(to), _ptr(lse, "lse"), _stream()))
     return out, lse
 
 
@@ -389,18 +401,18 @@ def flex_attention_bwd(q, k, v, out, lse, dout, block_mask: BlockMask, spec: Mas
             raise ValueError("dslopes needs a score_mod with ALiBi slopes")
         if dslopes.dtype != torch.float32 or dslopes.numel() != H or not dslopes.is_contiguous():
             raise ValueError("dslopes must be a contiguous float32 tensor of H elements")
-        cm.alibi_slopes_grad = dslopes.data_ptr()
+        cm.alibi_slopes_grad = _ptr(dslopes, "dslopes")
     if dbias is not None:
         if cm is None or mod.bias is None:
             raise ValueError("dbias needs a score_mod with a bias table")
         if dbias.dtype != torch.float32 or dbias.shape != mod.bias.shape or not dbias.is_contiguous():
             raise ValueError("dbias must be a contiguous float32 tensor shaped like the bias table")
-        cm.bias_grad = dbias.data_ptr()
+        cm.bias_grad = _ptr(dbias, "dbias")
     check(lib.bsm_flex_attention_bwd(
-        B, H, T, D, *[ctypes.byref(t) for t in ts[:4]], lse.data_ptr(), ctypes.byref(ts[4]),
+        B, H, T, D, *[ctypes.byref(t) for t in ts[:4]], _ptr(lse, "lse"), ctypes.byref(ts[4]),
         ctypes.byref(cb), ctypes.byref(cs), ctypes.byref(cm) if cm is not None else None,
         float(scale) if scale is not None else 0.0, *[ctypes.byref(t) for t in ts[5:]],
-        workspace.data_ptr(), workspace.numel(), _stream()))
+        _ptr(workspace, "workspace"), workspace.numel(), _stream()))
     return dq, dk, dv
 
 
@@ -474,10 +486,10 @@ def flex_attention_decode(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod] = Non
     cb = block_mask.c_struct() if block_mask is not None else None
     cm = mod.c_struct() if mod is not None else None
     check(lib.bsm_flex_attention_decode(
-        B, H, capacity, D, kvl.data_ptr(), stride, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
+        B, H, capacity, D, _ptr(kvl, "kv_len"), stride, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
         ctypes.byref(cs), ctypes.byref(cb) if cb is not None else None,
         ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
-        ctypes.byref(ts[3]), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
+        ctypes.byref(ts[3]), _ptr(lse, "lse"), _ptr(workspace, "workspace"), workspace.numel(), _stream()))
     return out, lse
 
 
@@ -521,11 +533,11 @@ def flex_attention_decode_paged(q, k_pages, v_pages, block_table, spec: MaskSpec
     cb = block_mask.c_struct() if block_mask is not None else None
     cm = mod.c_struct() if mod is not None else None
     check(lib.bsm_flex_attention_decode_paged(
-        B, H, D, page_size, num_pages, block_table.data_ptr(), n_logical, kvl.data_ptr(), stride,
+        B, H, D, page_size, num_pages, _ptr(block_table, "block_table"), n_logical, _ptr(kvl, "kv_len"), stride,
         ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
         ctypes.byref(cs), ctypes.byref(cb) if cb is not None else None,
         ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
-        ctypes.byref(ts[3]), lse.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
+        ctypes.byref(ts[3]), _ptr(lse, "lse"), _ptr(workspace, "workspace"), workspace.numel(), _stream()))
     return out, lse
 
 
@@ -593,10 +605,10 @@ def flex_attention_decode_static(q, k, v, spec: MaskSpec, mod: Optional[ScoreMod
     cb = block_mask.c_struct() if block_mask is not None else None
     cm = mod.c_struct() if mod is not None else None
     check(lib.bsm_flex_attention_decode_static(
-        B, H, capacity, D, kvl.data_ptr(), stride, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
+        B, H, capacity, D, _ptr(kvl, "kv_len"), stride, ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]),
         ctypes.byref(cs), ctypes.byref(cb) if cb is not None else None,
         ctypes.byref(cm) if cm is not None else None, float(scale) if scale is not None else 0.0,
-        ctypes.byref(ts[3]), lse.data_ptr(), _stream()))
+        ctypes.byref(ts[3]), _ptr(lse, "lse"), _stream()))
     return out, lse
 
 

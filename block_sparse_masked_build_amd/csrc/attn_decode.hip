@@ -130,7 +130,6 @@ __device__ inline int64_t readlane64(int64_t v, int l) {
 // ADD: an additive position term -- the ALiBi slope, or with P.bias the bias
 // table (one wave-uniform branch per key block; the decoding step is bound
 // by its HBM reads, not by this arithmetic).
-
 template <int D, bool ADD, bool SOFTCAP, bool LISTED>
 __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
     constexpr int kDimsPerLane = D / 64;  // output dims per lane: lane * kDimsPerLane + i
@@ -148,8 +147,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
     const int p = L - 1;
     const int window = (P.mask_flags & BSM_MASK_WINDOW) ? *P.window : 0;
 
-    // Tiles of this slot: listed ones (block mask row of p), or the slot's
-    // eight consecutive tiles.  ntl = number of tiles the slot covers.
+    // Tiles of this slot: entries 8 slot_i .. 8 slot_i + 7 of the block-mask
+    // row of p (full tiles first), or the slot's eight consecutive tiles; a
+    // slot with none of them below the live length writes an empty partial.
     int row = 0, nfull = 0, nlist = 0;
     if (L == 0) {
         write_empty_slot<D>(P, slot);

@@ -349,3 +349,25 @@ def test_python_paged_decode_checks_shapes_before_launch():
         api.flex_attention_decode_paged(_cpu((B + 1, H, 1, D)), kp, vp, table, spec)
     with pytest.raises(ValueError, match="logical capacity"):
         api.flex_attention_decode_paged(_cpu((B, H, 1, D)), kp, vp, table, api.MaskSpec(3 * P))
+
+
+def test_python_binding_rejects_host_tensors():
+    """Every address handed to the library must be device memory: host
+    tensors of the right shapes are refused before any call."""
+    import torch
+    from block_sparse_masked_build_amd import api
+    B, H, T, D = 1, 2, 256, 64
+    q = _cpu((B, H, T, D))
+    spec = api.MaskSpec(T)
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.flex_attention_fwd(q, q, q, None, spec, out=_cpu((B, H, T, D)),
+                               lse=_cpu((B, H, T), torch.float32))
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.flex_attention_decode(_cpu((B, H, 1, D)), q, q, spec)
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.flex_attention_decode_paged(_cpu((B, H, 1, D)), q, q, torch.zeros((B, 1), dtype=torch.int32),
+                                        api.MaskSpec(T))
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.ScoreMod(alibi_slopes=_cpu((H,), torch.float32)).c_struct()
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.MaskSpec(T, doc_ids=torch.zeros((1, T), dtype=torch.int32)).c_struct()
