@@ -219,3 +219,24 @@ def test_multi_query_decode_on_the_matrix_cores(n, L):
                                          _live_spec(spec, L), mod, b, h, rows)
             assert_close(f64(out[b, h]), ro, f"multi n{n} L{L} b{b} h{h}")
             assert_lse_close(lse[b, h].double().numpy(), rl, f"multi n{n} L{L} b{b} h{h}")
+
+
+def test_more_than_65535_batch_heads():
+    """B x H = 66,000 (batch and head index the grid's first dimension, which
+    takes more than 65,535 workgroups): sampled heads against the oracle."""
+    from block_sparse_masked_build_amd import api
+    B, H, cap, D, L = 2, 33000, 128, 64, 100
+    log(f"[decode] B{B} H{H} cap {cap} D{D}, live length {L}")
+    g = torch.Generator("cpu").manual_seed(61)
+    q = random_bf16((B, H, 1, D), g)
+    k = random_bf16((B, H, cap, D), g)
+    v = random_bf16((B, H, cap, D), g)
+    spec = MaskSpecData(cap, causal=True)
+    out, lse = api.flex_attention_decode(q.cuda(), k.cuda(), v.cuda(), api.from_spec_data(spec), None, kv_len=L)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    for b, h in ((0, 0), (0, 32999), (1, 0), (1, 17001), (1, 32999)):
+        ro, rl = _oracle_row(q, k, v, spec, None, b, h, L)
+        assert_close(f64(out[b, h]), ro, f"b{b} h{h}")
+        assert_lse_close(lse[b, h:h + 1].double().numpy(), rl, f"b{b} h{h}")
