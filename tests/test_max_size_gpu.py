@@ -138,3 +138,34 @@ def test_forward_and_backward_at_the_maximum_length():
         assert_within_bound(f64(dk_c[kp:kp + 1]), rdk, mdk, f"dk col {kp}")
         assert_within_bound(f64(dv_c[kp:kp + 1]), rdv, mdv, f"dv col {kp}")
     log("  ok")
+
+
+def test_forward_and_backward_with_more_than_65535_heads():
+    """B x H = 66,000 (B2 H33000), T = 200 (a cut-short second tile), D64,
+    causal: every kernel's grid takes the heads in its first dimension.
+    Sampled heads against the oracle."""
+    from block_sparse_masked_build_amd import api
+    B, H, Tn, D = 2, 33000, 200, 64
+    log(f"[max size] forward + backward B{B} H{H} T={Tn} D{D}, causal")
+    g = torch.Generator("cpu").manual_seed(4343)
+    q, k, v, do = (random_bf16((B, H, Tn, D), g) for _ in range(4))
+    spec_d = MaskSpecData(Tn, causal=True)
+    spec = api.from_spec_data(spec_d)
+    bm = api.build_block_mask(spec)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = api.flex_attention_fwd(qd, kd, vd, bm, spec)
+    dq, dk, dv = api.flex_attention_bwd(qd, kd, vd, out, lse, dod, bm, spec)
+    torch.cuda.synchronize()
+    out, lse, dq, dk, dv = (x.cpu() for x in (out, lse, dq, dk, dv))
+    rows = np.array([0, 1, 127, 128, 199])
+    for b, h in ((0, 0), (0, 32999), (1, 12345), (1, 32999)):
+        Q, K, V, dO = (x[b, h].double().numpy() for x in (q, k, v, do))
+        ro, rl, rm = oracle.forward_rows(Q, K, V, spec_d, None, b, h, rows, with_mass=True)
+        assert_within_bound(f64(out[b, h, rows]), ro, rm, f"out b{b} h{h}")
+        assert_lse_close(lse[b, h, rows].double().numpy(), rl, f"lse b{b} h{h}")
+        rdq, mdq = oracle.backward_dq_rows(Q, K, V, dO, spec_d, None, b, h, rows, with_mass=True)
+        assert_within_bound(f64(dq[b, h, rows]), rdq, mdq, f"dq b{b} h{h}")
+        rdk, rdv, mdk, mdv = oracle.backward_dkdv_cols(Q, K, V, dO, spec_d, None, b, h, rows, with_mass=True)
+        assert_within_bound(f64(dk[b, h, rows]), rdk, mdk, f"dk b{b} h{h}")
+        assert_within_bound(f64(dv[b, h, rows]), rdv, mdv, f"dv b{b} h{h}")
+    log("  ok")
