@@ -10,6 +10,7 @@ _API_NAMES = {"MaskSpec", "MaskTerm", "CAUSAL", "SAME_DOC", "IN_WINDOW", "SINK",
               "empty_block_mask", "build_block_mask", "flex_attention_fwd",
               "flex_attention_bwd", "bwd_workspace", "block_mask_workspace",
               "flex_attention_decode", "flex_attention_decode_static", "flex_attention_decode_paged",
+              "gather_kv_pages", "flex_attention_decode_multi_paged",
               "decode_workspace",
               "decode_multi_spec", "flex_attention_decode_multi"}
 

@@ -84,6 +84,10 @@ SIGNATURES = {
         ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
         _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), _P(BsmMaskSpec), _P(BsmBlockMask), _P(BsmScoreMod),
         ctypes.c_float, _P(BsmTensor), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "bsm_gather_kv_pages": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_int32, ctypes.c_int32, _P(BsmTensor), _P(BsmTensor), _P(BsmTensor), _P(BsmTensor),
+        ctypes.c_void_p]),
     "bsm_decode_static_max_bytes": (ctypes.c_size_t, []),
     "bsm_flex_attention_decode_static": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,

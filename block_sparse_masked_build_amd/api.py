@@ -541,6 +541,54 @@ def flex_attention_decode_paged(q, k_pages, v_pages, block_table, spec: MaskSpec
     return out, lse
 
 
+def gather_kv_pages(k_pages, v_pages, block_table, n_keys: int, k_out=None, v_out=None):
+    """The first n_keys keys and values of every sequence of a paged cache
+    (pools [num_pages, H, page_size, D], block_table int32 [B, n_logical] on
+    the device) copied into contiguous [B, H, n_keys, D] tensors by the
+    library's gather kernel.  Returns (k_out, v_out)."""
+    num_pages, H, page_size, D = k_pages.shape
+    if v_pages.shape != k_pages.shape:
+        raise ValueError(f"v_pages {tuple(v_pages.shape)} must have the shape of k_pages {tuple(k_pages.shape)}")
+    if block_table.dim() != 2 or block_table.dtype != torch.int32 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [B, n_logical] tensor")
+    B, n_logical = block_table.shape
+    if not 1 <= n_keys <= n_logical * page_size:
+        raise ValueError(f"n_keys {n_keys} must be in [1, {n_logical * page_size}]")
+    shape = (B, H, n_keys, D)
+    k_out = torch.empty(shape, dtype=k_pages.dtype, device=k_pages.device) if k_out is None else k_out
+    v_out = torch.empty(shape, dtype=v_pages.dtype, device=v_pages.device) if v_out is None else v_out
+    if k_out.shape != shape or v_out.shape != shape:
+        raise ValueError(f"k_out and v_out must be {shape}")
+    ts = [_tensor(x, n) for x, n in ((k_pages, "k_pages"), (v_pages, "v_pages"), (k_out, "k_out"), (v_out, "v_out"))]
+    check(lib.bsm_gather_kv_pages(B, H, D, page_size, num_pages, _ptr(block_table, "block_table"), n_logical,
+                                  int(n_keys), *[ctypes.byref(t) for t in ts], _stream()))
+    return k_out, v_out
+
+
+def flex_attention_decode_multi_paged(q, k_pages, v_pages, block_table, spec: MaskSpec, kv_len: int,
+                                      mod: Optional[ScoreMod] = None, scale: Optional[float] = None,
+                                      step_spec: Optional[MaskSpec] = None,
+                                      block_mask: Optional[BlockMask] = None, out=None, lse=None):
+    """flex_attention_decode_multi over a paged cache (spec.T = the logical
+    capacity n_logical * page_size): the live keys are gathered into
+    contiguous rows (gather_kv_pages), then the rectangular forward runs over
+    them.  Returns (out [B, H, n, D], lse [B, H, n])."""
+    B, H, n, D = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[1] != H or k_pages.shape[3] != D or block_table.shape[0] != B:
+        raise ValueError(f"k_pages [num_pages, H, page_size, D] and block_table [B, n_logical] must match q "
+                         f"{tuple(q.shape)}")
+    if spec.T != block_table.shape[1] * k_pages.shape[2]:
+        raise ValueError(f"mask spec length {spec.T} != logical capacity {block_table.shape[1] * k_pages.shape[2]}")
+    if step_spec is None:
+        step_spec = decode_multi_spec(spec, kv_len, n)
+    elif (step_spec.T, step_spec.Q, step_spec.q_offset) != (kv_len, n, kv_len - n):
+        raise ValueError("step_spec was built for another live length or query count")
+    if block_mask is None:
+        block_mask = build_block_mask(step_spec)
+    k, v = gather_kv_pages(k_pages, v_pages, block_table, kv_len)
+    return flex_attention_fwd(q, k, v, block_mask, step_spec, mod, scale, out, lse)
+
+
 def decode_multi_spec(spec: MaskSpec, kv_len: int, n: int) -> MaskSpec:
     """The mask of a block of n queries at positions kv_len - n .. kv_len - 1
     against the first kv_len positions of a cache described by spec (whose T
@@ -616,6 +664,6 @@ __all__ = ["MaskSpec", "MaskTerm", "CAUSAL", "SAME_DOC", "IN_WINDOW", "SINK", "P
            "ScoreMod", "BlockMask", "mask_spec", "from_spec_data", "score_mod",
            "empty_block_mask", "build_block_mask", "flex_attention_fwd", "flex_attention_bwd",
            "flex_attention_decode", "decode_workspace", "flex_attention_decode_static",
-           "flex_attention_decode_paged",
+           "flex_attention_decode_paged", "gather_kv_pages", "flex_attention_decode_multi_paged",
            "decode_multi_spec", "flex_attention_decode_multi",
            "bwd_workspace", "block_mask_workspace", "_lib"]

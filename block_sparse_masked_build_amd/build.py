@@ -30,7 +30,8 @@ HEAD_DIMS = {"fwd": (256, 128, 64), "bwd": (128, 256, 64)}
 SOURCES = ([(f"attn_{p}.hip", f"attn_{p}_d{d}_{e}.o", [f"-DBSM_HEAD_DIM={d}", *ef])
             for p in ("fwd", "bwd") for d in HEAD_DIMS[p] for e, ef in ELEM_FLAGS.items()] +
            [("attn_decode.hip", f"attn_decode_{e}.o", ef) for e, ef in ELEM_FLAGS.items()] +
-           [("mask_builder.hip", "mask_builder.o", []), ("bsm_api.cpp", "bsm_api.o", [])])
+           [("mask_builder.hip", "mask_builder.o", []), ("gather_pages.hip", "gather_pages.o", []),
+            ("bsm_api.cpp", "bsm_api.o", [])])
 ARCH = "gfx950"
 
 

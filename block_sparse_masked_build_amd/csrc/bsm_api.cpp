@@ -629,6 +629,49 @@ bsm_status bsm_flex_attention_decode_paged(int32_t B, int32_t H, int32_t D, int3
                       "bsm_flex_attention_decode_paged launch");
 }
 
+bsm_status bsm_gather_kv_pages(int32_t B, int32_t H, int32_t D, int32_t page_size, int32_t num_pages,
+                               const int32_t *block_table, int32_t table_stride, int32_t n_keys,
+                               const bsm_tensor *k_pages, const bsm_tensor *v_pages, const bsm_tensor *k_out,
+                               const bsm_tensor *v_out, void *stream) {
+    if (B < 1 || H < 1) return fail(BSM_E_INVALID, "B=%d and H=%d must be >= 1", B, H);
+    if ((int64_t)B * H > INT32_MAX) return fail(BSM_E_INVALID, "grid too large");
+    if (!built_head_dim(D)) return fail(BSM_E_UNSUPPORTED, "head dim %d: only 64, 128 and 256 are built", D);
+    if (page_size < 64 || page_size % 64 != 0)
+        return fail(BSM_E_INVALID, "page_size %d must be a positive multiple of 64", page_size);
+    if (num_pages < 1) return fail(BSM_E_INVALID, "num_pages %d must be >= 1", num_pages);
+    if (!block_table) return fail(BSM_E_INVALID, "block_table is NULL");
+    if (table_stride < 1 || (int64_t)table_stride * page_size > kMaxT)
+        return fail(BSM_E_INVALID, "table_stride %d x page_size %d must give a capacity in [1, %d]", table_stride,
+                    page_size, kMaxT);
+    if (n_keys < 1 || n_keys > table_stride * page_size)
+        return fail(BSM_E_INVALID, "n_keys %d must be in [1, %d]", n_keys, table_stride * page_size);
+    bsm_status st;
+    if ((st = check_tensor(k_pages, "k_pages")) != BSM_OK) return st;
+    if ((st = check_tensor(v_pages, "v_pages")) != BSM_OK) return st;
+    if ((st = check_tensor(k_out, "k_out")) != BSM_OK) return st;
+    if ((st = check_tensor(v_out, "v_out")) != BSM_OK) return st;
+    if ((st = check_same_dtype({k_pages, v_pages, k_out, v_out})) != BSM_OK) return st;
+    constexpr int64_t kElem = 2;  // bf16 and fp16
+    bsm::GatherLaunch g;
+    g.B = B;
+    g.H = H;
+    g.row_bytes = D * (int32_t)kElem;
+    g.page_size = page_size;
+    g.num_pages = num_pages;
+    g.table_stride = table_stride;
+    g.n_keys = n_keys;
+    g.table = block_table;
+    g.k_src = static_cast<const char *>(k_pages->ptr);
+    g.v_src = static_cast<const char *>(v_pages->ptr);
+    g.ks_b = k_pages->stride_b * kElem, g.ks_h = k_pages->stride_h * kElem, g.ks_t = k_pages->stride_t * kElem;
+    g.vs_b = v_pages->stride_b * kElem, g.vs_h = v_pages->stride_h * kElem, g.vs_t = v_pages->stride_t * kElem;
+    g.k_dst = static_cast<char *>(const_cast<void *>(k_out->ptr));
+    g.v_dst = static_cast<char *>(const_cast<void *>(v_out->ptr));
+    g.kd_b = k_out->stride_b * kElem, g.kd_h = k_out->stride_h * kElem, g.kd_t = k_out->stride_t * kElem;
+    g.vd_b = v_out->stride_b * kElem, g.vd_h = v_out->stride_h * kElem, g.vd_t = v_out->stride_t * kElem;
+    return hip_status(bsm::launch_gather_pages(g, static_cast<hipStream_t>(stream)), "bsm_gather_kv_pages launch");
+}
+
 size_t bsm_decode_static_max_bytes(void) { return kScratchBytes; }
 
 bsm_status bsm_flex_attention_decode_static(int32_t B, int32_t H, int32_t capacity, int32_t D,

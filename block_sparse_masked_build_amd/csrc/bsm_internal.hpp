@@ -130,4 +130,17 @@ inline int decode_slots(int capacity) {
 hipError_t launch_attn_decode_bf16(const DecodeLaunch &d, float *part, hipStream_t stream);
 hipError_t launch_attn_decode_f16(const DecodeLaunch &d, float *part, hipStream_t stream);
 
+// Copy of the first n_keys keys of each (b, h) of a paged K/V cache into
+// contiguous rows (see bsm_gather_kv_pages).  Strides in bytes; sources are
+// page-major ([page, head, row]), destinations [b, head, key].
+struct GatherLaunch {
+    int32_t B, H, row_bytes, page_size, num_pages, table_stride, n_keys;
+    const int32_t *table;
+    const char *k_src, *v_src;
+    int64_t ks_b, ks_h, ks_t, vs_b, vs_h, vs_t;
+    char *k_dst, *v_dst;
+    int64_t kd_b, kd_h, kd_t, vd_b, vd_h, vd_t;
+};
+hipError_t launch_gather_pages(const GatherLaunch &g, hipStream_t stream);
+
 }  // namespace bsm

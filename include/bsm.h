@@ -381,6 +381,25 @@ bsm_status bsm_flex_attention_decode_paged(int32_t B, int32_t H, int32_t D, int3
                                            const bsm_tensor *out, float *lse, void *workspace,
                                            size_t workspace_bytes, void *stream);
 
+/* Copies the first n_keys keys and values of every sequence of a paged
+ * cache into contiguous rows (tutorial "FlexAttention in PyTorch",
+ * "Decoding and paged KV caches"), for the calls that take contiguous K and
+ * V: a block of several new queries runs the rectangular forward over them.
+ * k_pages, v_pages, block_table, table_stride, page_size, num_pages: as in
+ * bsm_flex_attention_decode_paged.  k_out, v_out: device tensors
+ * [B, H, n_keys, D] of the pools' element type, written (key kv of batch
+ * element b, head h at k_out + b stride_b + h stride_h + kv stride_t).
+ * Table entries outside [0, num_pages) are clamped into it.  Enqueued on
+ * `stream`; nothing is allocated.  Errors: BSM_E_INVALID for B or H < 1,
+ * page_size not a positive multiple of 64, num_pages < 1, a NULL table,
+ * table_stride < 1, n_keys outside [1, table_stride * page_size], or a bad
+ * tensor (NULL, unaligned, mixed element types); BSM_E_UNSUPPORTED for D
+ * outside {64, 128, 256}; BSM_E_HIP on a failed launch. */
+bsm_status bsm_gather_kv_pages(int32_t B, int32_t H, int32_t D, int32_t page_size, int32_t num_pages,
+                               const int32_t *block_table, int32_t table_stride, int32_t n_keys,
+                               const bsm_tensor *k_pages, const bsm_tensor *v_pages,
+                               const bsm_tensor *k_out, const bsm_tensor *v_out, void *stream);
+
 /* Allocation-free decoding step, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  The same step as bsm_flex_attention_decode, with the

@@ -229,6 +229,14 @@ static void decoding() {
     CHECK(stub::last_decode.block_table == table && stub::last_decode.table_stride == 16);
     CHECK(stub::last_decode.page_size == 256 && stub::last_decode.num_pages == 40);
     CHECK(stub::last_decode.a.k_sb == kp.stride_b);
+    // gathering the live keys of the pages into contiguous rows
+    bsm_tensor kc = tensor_of(arena(24 << 20), H, 1000, D);
+    REJECT(bsm_gather_kv_pages(B, H, D, 256, 40, table, 16, 0, &kp, &kp, &kc, &kc, nullptr), BSM_E_INVALID);
+    REJECT(bsm_gather_kv_pages(B, H, D, 256, 40, table, 16, 4097, &kp, &kp, &kc, &kc, nullptr), BSM_E_INVALID);
+    REJECT(bsm_gather_kv_pages(B, H, 96, 256, 40, table, 16, 1000, &kp, &kp, &kc, &kc, nullptr), BSM_E_UNSUPPORTED);
+    ACCEPT(bsm_gather_kv_pages(B, H, D, 256, 40, table, 16, 1000, &kp, &kp, &kc, &kc, nullptr));
+    CHECK(stub::last_gather.n_keys == 1000 && stub::last_gather.row_bytes == 2 * D);
+    CHECK(stub::last_gather.ks_b == 2 * kp.stride_b && stub::last_gather.kd_t == 2 * kc.stride_t);
     // the allocation-free variant looks up its static array on the current
     // device first: with no device that is a HIP error, never a launch
     const int before = stub::calls;

@@ -9,6 +9,7 @@ int calls = 0;
 bsm::AttnParams last_attn{};
 bsm::MaskBuildParams last_build{};
 bsm::DecodeLaunch last_decode{};
+bsm::GatherLaunch last_gather{};
 float *last_decode_part = nullptr;
 }  // namespace stub
 
@@ -20,6 +21,11 @@ static hipError_t record(const AttnParams &p) {
     return hipSuccess;
 }
 
+hipError_t launch_gather_pages(const GatherLaunch &g, hipStream_t) {
+    ++stub::calls;
+    stub::last_gather = g;
+    return hipSuccess;
+}
 hipError_t launch_build_block_mask(const MaskBuildParams &p, hipStream_t) {
     ++stub::calls;
     stub::last_build = p;

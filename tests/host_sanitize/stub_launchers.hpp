@@ -7,5 +7,6 @@ extern int calls;
 extern bsm::AttnParams last_attn;
 extern bsm::MaskBuildParams last_build;
 extern bsm::DecodeLaunch last_decode;
+extern bsm::GatherLaunch last_gather;
 extern float *last_decode_part;
 }  // namespace stub

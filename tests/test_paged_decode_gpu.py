@@ -211,3 +211,59 @@ def test_graph_replay_serving_loop():
         torch.cuda.synchronize()
         assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), lens
     assert len(free) == npool - sum(-(-n // page) for n in filled)
+
+
+@pytest.mark.parametrize("D,page,n_keys,dtype", [(64, 64, 1, "bf16"), (128, 192, 1000, "f16"), (128, 256, 4096, "bf16"),
+                                                 (256, 128, 777, "bf16")])
+def test_gather_pages_copies_exactly(D, page, n_keys, dtype):
+    """The gather kernel's contiguous rows equal the keys and values they came
+    from, bit for bit (ragged last block, table entries past n_keys out of
+    range)."""
+    from block_sparse_masked_build_amd import api
+    B, H, cap = 3, 2, 4096 if page != 192 else 3840
+    log(f"[gather] B{B} H{H} cap {cap} D{D} page {page} n_keys {n_keys} {dtype}")
+    rand = random_f16 if dtype == "f16" else random_bf16
+    g = torch.Generator("cpu").manual_seed(79 + D + page)
+    k = rand((B, H, cap, D), g)
+    v = rand((B, H, cap, D), g)
+    kp, vp, table = _page(k, v, page, n_keys, spare=2, seed=80)
+    kc, vc = api.gather_kv_pages(kp.cuda(), vp.cuda(), table.cuda(), n_keys)
+    torch.cuda.synchronize()
+    assert torch.equal(kc.cpu(), k[:, :, :n_keys]) and torch.equal(vc.cpu(), v[:, :, :n_keys])
+
+
+@pytest.mark.parametrize("n,L", [(1, 1), (4, 777), (130, 3000)])
+def test_multi_query_decode_over_pages(n, L):
+    """A block of n new queries over a paged cache (gather, then the
+    rectangular forward) equals the same block over the contiguous cache bit
+    for bit, and the oracle on its first and last rows."""
+    from block_sparse_masked_build_amd import api
+    B, H, cap, D, page = 2, 2, 4096, 128, 128
+    log(f"[paged multi-query decode] n {n} live {L}")
+    rng = np.random.default_rng(81)
+    docs = np.stack([np.cumsum(rng.random(cap) < 1 / 600).astype(np.int32) for _ in range(B)])
+    spec_d = MaskSpecData(cap, causal=True, document=True, doc_ids=docs, window=700)
+    mod_d = ScoreModData(alibi_slopes=alibi_slopes(H), softcap=30.0)
+    g = torch.Generator("cpu").manual_seed(82 + n)
+    q = random_bf16((B, H, n, D), g)
+    k = random_bf16((B, H, cap, D), g)
+    v = random_bf16((B, H, cap, D), g)
+    kp, vp, table = _page(k, v, page, L, spare=3, seed=83)
+    spec = api.from_spec_data(spec_d)
+    m = api.score_mod(mod_d.alibi_slopes, mod_d.softcap)
+    ref_o, ref_l = api.flex_attention_decode_multi(q.cuda(), k.cuda(), v.cuda(), spec, L, m)
+    out, lse = api.flex_attention_decode_multi_paged(q.cuda(), kp.cuda(), vp.cuda(), table.cuda(), spec, L, m)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), ref_o.cpu()) and torch.equal(lse.cpu(), ref_l.cpu())
+    out, lse = out.cpu(), lse.cpu()
+    live = dataclasses.replace(spec_d, T=L, doc_ids=docs[:, :L])  # queries at positions L - n .. L - 1
+    sel = np.unique([0, n - 1])
+    rows = L - n + sel
+    for b in range(B):
+        for h in range(H):
+            Qf = np.zeros((L, D))
+            Qf[rows] = q[b, h, sel].double().numpy()
+            ro, rl, rm = oracle.forward_rows(Qf, k[b, h, :L].double().numpy(), v[b, h, :L].double().numpy(),
+                                             live, mod_d, b, h, rows, with_mass=True)
+            assert_within_bound(f64(out[b, h, sel]), ro, rm, f"b{b} h{h}")
+            assert_lse_close(lse[b, h, sel].double().numpy(), rl, f"b{b} h{h}")
