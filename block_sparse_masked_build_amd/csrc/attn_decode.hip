@@ -26,11 +26,12 @@
 //
 // Mapping to CDNA4: a single query has no matrix-product shape, and K and V
 // are streamed once, so the path is HBM-bound and runs on the vector units:
-//  * decode_partial_kernel: one workgroup of 4 waves per (batch x head,
-//    slot of up to eight 128-key tiles), batch x head fastest so that the
-//    busy slots of short caches spread over the XCDs.  Each wave takes two
-//    tiles, in 64-key blocks whose list entries and page-table entries are
-//    looked up while the query row loads.  For D <= 128 a load instruction
+//  * decode_partial_kernel: one workgroup per (batch x head, slot of up to
+//    eight 128-key tiles), batch x head fastest so that the busy slots of
+//    short caches spread over the XCDs: 8 waves of one tile each for
+//    D <= 128, 4 waves of two tiles at D = 256.  A wave takes its tiles in
+//    64-key blocks whose list entries and page-table entries are looked up
+//    while the query row loads.  For D <= 128 a load instruction
 //    covers whole rows (16 bytes per lane, D / 8 lanes per row), K and V of
 //    a block are requested together, and the scores' partial dot products
 //    are summed across each row's lanes; for D = 256 lane = key for the
@@ -49,10 +50,12 @@ namespace {
 
 typedef elem_t dec_elem8 __attribute__((ext_vector_type(8)));
 
-constexpr int kDecThreads = 256;
-constexpr int kDecWaves = kDecThreads / 64;
+// threads per decoding workgroup: 8 waves of one tile each for D <= 128, 4
+// waves of two tiles at D = 256 (whose registers allow one wave per SIMD)
+template <int D>
+constexpr int kDecThreadsOf = D == 256 ? 256 : 512;
 constexpr int kSlotTiles = kDecodeSlotTiles;       // 128-key tiles per workgroup
-constexpr int kWaveTiles = kSlotTiles / kDecWaves; // 2 per wave
+
 
 struct DecodeParams {
     int32_t B, H, capacity, D, nslot, nt;
@@ -113,7 +116,7 @@ __device__ inline bool dec_visible(const DecodeParams &P, int bm, int p, int kv,
 
 template <int D>
 __device__ inline void write_empty_slot(const DecodeParams &P, int64_t slot) {
-    for (int d = threadIdx.x; d < D; d += kDecThreads) P.part_o[slot * D + d] = 0.0f;
+    for (int d = threadIdx.x; d < D; d += (int)blockDim.x) P.part_o[slot * D + d] = 0.0f;
     if (threadIdx.x == 0) {
         P.part_ml[slot * 2] = -INFINITY;
         P.part_ml[slot * 2 + 1] = 0.0f;
@@ -131,7 +134,9 @@ __device__ inline int64_t readlane64(int64_t v, int l) {
 // table (one wave-uniform branch per key block; the decoding step is bound
 // by its HBM reads, not by this arithmetic).
 template <int D, bool ADD, bool SOFTCAP, bool LISTED>
-__global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParams P) {
+__global__ __launch_bounds__(kDecThreadsOf<D>) void decode_partial_kernel(DecodeParams P) {
+    constexpr int kDecThreads = kDecThreadsOf<D>, kDecWaves = kDecThreads / 64;
+    constexpr int kWaveTiles = kSlotTiles / kDecWaves;  // tiles per wave
     constexpr int kDimsPerLane = D / 64;  // output dims per lane: lane * kDimsPerLane + i
     __shared__ float sq[D];               // the query row, fp32
     __shared__ float sp[kDecWaves][64];   // probabilities of a wave's 64 keys
@@ -406,7 +411,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_partial_kernel(DecodeParam
 #pragma unroll
         for (int i = 0; i < kDimsPerLane; ++i) so[wv][lane * kDimsPerLane + i] = o[i];
     }
-    // merge the four waves (their outputs are in so)
+    // merge the waves (their outputs are in so)
     if (lane == 0) {
         sm[wv] = m;
         sl[wv] = l;
@@ -464,7 +469,7 @@ void launch_mods(const DecodeParams &P, hipStream_t stream) {
     // (batch, head) fastest: consecutive workgroups go to different XCDs, so
     // the slots that hold keys -- the first ones at short live lengths --
     // spread over the whole chip instead of landing on one XCD
-    const dim3 grid(P.B * P.H, P.nslot), block(kDecThreads);
+    const dim3 grid(P.B * P.H, P.nslot), block(kDecThreadsOf<D>);
     if (P.kv_num)
         hipLaunchKernelGGL((decode_partial_kernel<D, ALIBI, SOFTCAP, true>), grid, block, 0, stream, P);
     else
